@@ -1,0 +1,482 @@
+"""CPU oracle for the MoE-layer hot path -- TEST INFRASTRUCTURE ONLY.
+
+This module is the plain, slow, obviously correct statement of what the GPU
+path computes.  Only the tests, the smoke check in the repository's graft
+entry and the benchmark's CPU-baseline leg may import it; the product path
+never does.  It shares no code with the HIP library.
+
+Arithmetic is numpy float64 throughout.  Inputs arrive as float32 arrays whose
+values are exactly representable (bf16-rounded where the workload stores bf16)
+and are upcast without change.  Per-expert matrix products use numpy's matmul;
+everything else is written out step by step in the order the pages describe.
+
+Sources (page title -- place on the page):
+  [LAYOUT] "MoE Pretraining: Parallelism Layout Changes the Model, Not Quality"
+           -- Methodology (Models and Data table), Two Kinds of Layout Effects,
+           Finding 3 (routing margin and near-ties), Practical Implications.
+  [COUPLING] "Expert Coupling in MoE Pretraining: Reducing All-to-All Overhead
+           with Correlated Placement and Token Shuffling" -- Abstract, Fig. 2,
+           Table I, Fig. 3, Fig. 5, Table III (notation t, T, E, k, S(t), W).
+  [REVISIT] "Revisiting MoE and Dense Speed-Accuracy Comparisons for LLM
+           Training" -- Sec. 2.1 (SwiGLU, Top-K routing, load-balancing loss),
+           Sec. 2.2 (GShard gating/dispatch/combine, outer batches), Sec. 3.6
+           (naive second-expert routing).
+  [LOADING] "Why does expert-parallel loading matter so much in MoE training?"
+           -- What to verify before trusting an MoE checkpoint load.
+
+Readings where the pages are silent or garbled (listed with reasons in the
+design notes of the repository):
+  * no router bias; logits l = X Wr^T with Wr stored [E, d];
+  * top-k by descending logit, lower expert id first on exact ties;
+  * gates: softmax renormalised over the k chosen logits;
+  * margin: raw gap between the k-th and (k+1)-th largest logits, near-tie when
+    it is below eps (default 1e-3); the normalised margin of [LAYOUT] Finding 3
+    (gap / spread of the token's logits) is reported beside it;
+  * SwiGLU: h = silu(x W1^T) * (x W3^T), y = h W2^T, weights [E, out, in];
+  * dropless routing (no capacity);
+  * LB statistics per contiguous token block: f = count / (block tokens * k),
+    P = mean full-softmax probability, aux = E * sum_e f_e P_e;
+  * dedup plan rows ordered by (group, token); all destinations count,
+    including the token's home block.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a):
+    return np.asarray(a, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# Router: logits, top-k, gates, margins  ([COUPLING] Abstract: each token is
+# routed to k of E experts; [REVISIT] Sec. 2.1 Top-K routing, Table 1 router
+# weight "ME" with no bias; [REVISIT] Sec. 3.6 the second expert is simply the
+# second best; [LAYOUT] Finding 3 margin and near-ties)
+# ---------------------------------------------------------------------------
+
+def router_logits(x, wr):
+    """l[t, e] = sum_i x[t, i] * wr[e, i]."""
+    return _f64(x) @ _f64(wr).T
+
+
+def topk_select(logits, k):
+    """Experts ordered by descending logit, lower id first on exact ties.
+
+    Returns (idx [T,k] int32, margin [T] f64).  margin[t] is the gap between
+    the k-th and the (k+1)-th largest logits (+inf when k == E).
+    """
+    logits = _f64(logits)
+    T, E = logits.shape
+    order = np.argsort(-logits, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    if k < E:
+        kth = np.take_along_axis(logits, order[:, k - 1:k], axis=1)[:, 0]
+        nxt = np.take_along_axis(logits, order[:, k:k + 1], axis=1)[:, 0]
+        margin = kth - nxt
+    else:
+        margin = np.full(T, np.inf)
+    return idx, margin
+
+
+def chosen_gates(logits, idx):
+    """Softmax over the chosen k logits only: g_j = exp(l_j) / sum_i exp(l_i)."""
+    logits = _f64(logits)
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def full_softmax(logits):
+    logits = _f64(logits)
+    z = np.exp(logits - logits.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def normalized_margin(logits, margin):
+    """[LAYOUT] Finding 3: the margin divided by the spread of the token's scores."""
+    logits = _f64(logits)
+    spread = logits.max(axis=1) - logits.min(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(spread > 0, margin / spread, np.inf)
+
+
+def route(x, wr, k, near_tie_eps=1e-3):
+    """Router forward: logits, top-k, renormalised gates, margins, near-tie count."""
+    logits = router_logits(x, wr)
+    idx, margin = topk_select(logits, k)
+    gates = chosen_gates(logits, idx)
+    near = margin < near_tie_eps
+    return {
+        "logits": logits,
+        "topk_idx": idx,
+        "gates": gates,
+        "margin": margin,
+        "near_tie": near,
+        "near_tie_count": int(near.sum()),
+        "norm_margin": normalized_margin(logits, margin),
+    }
+
+
+def lb_stats(logits, idx, E, G):
+    """Load-balancing statistics per contiguous block of T/G tokens.
+
+    [LAYOUT] Key Insight and Two Kinds of Layout Effects: balancing statistics
+    computed per machine; [REVISIT] Sec. 2.2: tokens split into O outer batches;
+    [REVISIT] Sec. 2.1: GShard load-balancing loss.
+    Returns count [G,E] int64, f [G,E], P [G,E], aux [G].
+    """
+    logits = _f64(logits)
+    T, k = idx.shape
+    if T % G:
+        raise ValueError("G must divide T")
+    n = T // G
+    p = full_softmax(logits)
+    count = np.zeros((G, E), dtype=np.int64)
+    P = np.zeros((G, E))
+    for r in range(G):
+        for t in range(r * n, (r + 1) * n):
+            for j in range(k):
+                count[r, idx[t, j]] += 1
+        P[r] = p[r * n:(r + 1) * n].mean(axis=0)
+    f = count / float(n * k)
+    aux = E * (f * P).sum(axis=1)
+    return {"count": count, "f": f, "P": P, "aux": aux}
+
+
+# ---------------------------------------------------------------------------
+# Permutation into expert-contiguous rows ([COUPLING] Abstract and Fig. 5 step
+# 3: dispatch tokens to their experts; [REVISIT] Sec. 2.2 GShard dispatch)
+# ---------------------------------------------------------------------------
+
+def permute_plan(idx, E):
+    """Stable counting sort of the T*k (token, slot) assignments by expert.
+
+    Inside one expert's segment the rows are in ascending token id.
+    Returns counts [E], offsets [E+1], pos [T,k] (row of assignment (t, j)),
+    src [T*k] (token of each row), all int64.
+    """
+    T, k = idx.shape
+    counts = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            counts[idx[t, j]] += 1
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:-1].copy()
+    pos = np.zeros((T, k), dtype=np.int64)
+    src = np.zeros(T * k, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            pos[t, j] = fill[e]
+            src[fill[e]] = t
+            fill[e] += 1
+    return {"counts": counts, "offsets": offsets, "pos": pos, "src": src}
+
+
+def gather_rows(x, src):
+    """x_perm[p] = x[src[p]]."""
+    return _f64(x)[np.asarray(src, dtype=np.int64)]
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU experts ([REVISIT] Sec. 2.1: SwiGLU activation; [LAYOUT] Methodology:
+# SwiGLU experts; [COUPLING] Fig. 5 step 4: expert computation)
+# ---------------------------------------------------------------------------
+
+def _sigmoid(a):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def silu(a):
+    return a * _sigmoid(a)
+
+
+def swiglu_experts(x_perm, offsets, w1, w3, w2):
+    """Per expert e over rows [offsets[e], offsets[e+1]):
+    a = X W1[e]^T, b = X W3[e]^T, h = silu(a) * b, y = h W2[e]^T."""
+    x_perm = _f64(x_perm)
+    w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
+    R = x_perm.shape[0]
+    E, f, d = w1.shape
+    a = np.zeros((R, f))
+    b = np.zeros((R, f))
+    h = np.zeros((R, f))
+    y = np.zeros((R, d))
+    for e in range(E):
+        s = slice(int(offsets[e]), int(offsets[e + 1]))
+        xe = x_perm[s]
+        a[s] = xe @ w1[e].T
+        b[s] = xe @ w3[e].T
+        h[s] = silu(a[s]) * b[s]
+        y[s] = h[s] @ w2[e].T
+    return {"a": a, "b": b, "h": h, "y_perm": y}
+
+
+def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm):
+    """Backward of swiglu_experts for the upstream gradient dy_perm [R, d].
+
+    dh = dy W2[e]; da = dh * b * silu'(a); db = dh * silu(a);
+    dx = da W1[e] + db W3[e]; dW2[e] = dy^T h; dW1[e] = da^T x; dW3[e] = db^T x,
+    with silu'(a) = s (1 + a (1 - s)), s = sigmoid(a).
+    """
+    x_perm, dy_perm = _f64(x_perm), _f64(dy_perm)
+    a, b = _f64(a), _f64(b)
+    w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
+    E, f, d = w1.shape
+    R = x_perm.shape[0]
+    dx = np.zeros((R, d))
+    dh = np.zeros((R, f))
+    da = np.zeros((R, f))
+    db = np.zeros((R, f))
+    dw1 = np.zeros_like(w1)
+    dw3 = np.zeros_like(w3)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        s = slice(int(offsets[e]), int(offsets[e + 1]))
+        sg = _sigmoid(a[s])
+        act = a[s] * sg
+        dact = sg * (1.0 + a[s] * (1.0 - sg))
+        dh[s] = dy_perm[s] @ w2[e]
+        da[s] = dh[s] * b[s] * dact
+        db[s] = dh[s] * act
+        dx[s] = da[s] @ w1[e] + db[s] @ w3[e]
+        dw2[e] = dy_perm[s].T @ (act * b[s])
+        dw1[e] = da[s].T @ x_perm[s]
+        dw3[e] = db[s].T @ x_perm[s]
+    return {"dx_perm": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2,
+            "dh": dh, "da": da, "db": db}
+
+
+# ---------------------------------------------------------------------------
+# Combine and its adjoint ([COUPLING] Abstract and Fig. 5 step 5: combine the
+# results; [REVISIT] Sec. 2.2 GShard combine)
+# ---------------------------------------------------------------------------
+
+def combine(rows, pos, gates=None):
+    """y[t] = sum_j g[t, j] * rows[pos[t, j]]  (unit weights when gates is None)."""
+    rows = _f64(rows)
+    T, k = pos.shape
+    y = np.zeros((T, rows.shape[1]))
+    for j in range(k):
+        w = 1.0 if gates is None else _f64(gates)[:, j:j + 1]
+        y += w * rows[np.asarray(pos[:, j], dtype=np.int64)]
+    return y
+
+
+def combine_bwd(dy, y_perm, pos, gates):
+    """dy_perm[pos[t,j]] = g[t,j] dY[t];  dgate[t,j] = <dY[t], y_perm[pos[t,j]]>."""
+    dy, y_perm, gates = _f64(dy), _f64(y_perm), _f64(gates)
+    T, k = pos.shape
+    dy_perm = np.zeros((T * k, dy.shape[1]))
+    dgate = np.zeros((T, k))
+    for j in range(k):
+        p = np.asarray(pos[:, j], dtype=np.int64)
+        dy_perm[p] = gates[:, j:j + 1] * dy
+        dgate[:, j] = (dy * y_perm[p]).sum(axis=1)
+    return dy_perm, dgate
+
+
+# ---------------------------------------------------------------------------
+# Router backward (adjoint of logits -> top-k -> renormalised softmax)
+# ---------------------------------------------------------------------------
+
+def route_bwd(x, wr, idx, gates, dgate):
+    """dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i), zero for unchosen experts;
+    dX_router = dl Wr;  dWr = dl^T X."""
+    x, wr, gates, dgate = _f64(x), _f64(wr), _f64(gates), _f64(dgate)
+    T, k = idx.shape
+    E = wr.shape[0]
+    inner = (gates * dgate).sum(axis=1, keepdims=True)
+    dsel = gates * (dgate - inner)
+    dl = np.zeros((T, E))
+    for j in range(k):
+        dl[np.arange(T), idx[:, j]] += dsel[:, j]
+    return {"dlogits": dl, "dx_router": dl @ wr, "dwr": dl.T @ x}
+
+
+# ---------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------
+
+def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None):
+    """Router -> permute -> SwiGLU experts -> combine.
+
+    routing, when given, is a (topk_idx, gates) pair that replaces the router's
+    own decision (the logits, margins and near-ties are still reported).
+    """
+    E = np.asarray(wr).shape[0]
+    r = route(x, wr, k, near_tie_eps)
+    if routing is not None:
+        idx, gates = routing
+        idx = np.asarray(idx, dtype=np.int32)
+        gates = _f64(gates)
+    else:
+        idx, gates = r["topk_idx"], r["gates"]
+    plan = permute_plan(idx, E)
+    x_perm = gather_rows(x, plan["src"])
+    ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2)
+    y = combine(ex["y_perm"], plan["pos"], gates)
+    out = dict(r)
+    out.update(plan)
+    out.update(ex)
+    out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y})
+    return out
+
+
+def layer_backward(x, wr, w1, w3, w2, fwd, dy):
+    """Backward of layer_forward for the upstream gradient dy [T, d]."""
+    dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"])
+    eb = swiglu_experts_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2,
+                            fwd["a"], fwd["b"], dy_perm)
+    dx_exp = combine(eb["dx_perm"], fwd["pos"], None)
+    rb = route_bwd(x, wr, fwd["topk_idx"], fwd["gates"], dgate)
+    return {
+        "dy_perm": dy_perm, "dgate": dgate,
+        "dx_perm": eb["dx_perm"], "dh": eb["dh"], "da": eb["da"], "db": eb["db"],
+        "dw1": eb["dw1"], "dw3": eb["dw3"], "dw2": eb["dw2"],
+        "dx_expert": dx_exp, "dlogits": rb["dlogits"],
+        "dx": dx_exp + rb["dx_router"], "dwr": rb["dwr"],
+    }
+
+
+# ---------------------------------------------------------------------------
+# Index products for expert-parallel layouts ([COUPLING] Table III notation,
+# Fig. 2 co-selection, Fig. 3 correlated placement, Abstract: a dispatcher that
+# sends each token to each GPU once, Table I statistics)
+# ---------------------------------------------------------------------------
+
+def coselect(idx, E):
+    """W[e, e'] = number of tokens that select both e and e' (diagonal zero)."""
+    T, k = idx.shape
+    W = np.zeros((E, E), dtype=np.int64)
+    for t in range(T):
+        for i in range(k):
+            for j in range(k):
+                if i != j:
+                    W[idx[t, i], idx[t, j]] += 1
+    return W
+
+
+def placement_contiguous(E, G):
+    """Expert e lives in group floor(e / (E/G))."""
+    if E % G:
+        raise ValueError("G must divide E")
+    return np.arange(E, dtype=np.int64) // (E // G)
+
+
+def check_placement(placement, E, G):
+    """[LOADING] What to verify: every expert owned by exactly one group, and
+    equal expert counts per group.  Raises ValueError otherwise."""
+    placement = np.asarray(placement)
+    if placement.shape != (E,) or E % G:
+        raise ValueError("placement must have E entries and G must divide E")
+    if placement.min() < 0 or placement.max() >= G:
+        raise ValueError("placement entries must lie in [0, G)")
+    per = np.bincount(placement, minlength=G)
+    if not np.all(per == E // G):
+        raise ValueError("placement must put E/G experts in every group")
+
+
+def placement_greedy(W, G):
+    """Correlated placement: fill one group at a time with experts that are
+    often selected together ([COUPLING] Abstract and Fig. 3).
+
+    The pages do not print the fitting algorithm; this is a plain greedy
+    reading, in integer arithmetic:
+      1. seed the group with the unassigned expert of largest co-selection mass
+         to the other unassigned experts (ties: lowest id);
+      2. repeatedly add the unassigned expert with the largest co-selection
+         count to the group's members (ties: larger mass to the unassigned
+         experts, then lowest id) until the group holds E/G experts.
+    """
+    W = np.asarray(W, dtype=np.int64)
+    E = W.shape[0]
+    if E % G:
+        raise ValueError("G must divide E")
+    cap = E // G
+    placement = np.full(E, -1, dtype=np.int64)
+    unassigned = list(range(E))
+    for g in range(G):
+        def mass(e):
+            return sum(int(W[e, o]) for o in unassigned if o != e)
+        seed = unassigned[0]
+        best = mass(seed)
+        for e in unassigned[1:]:
+            m = mass(e)
+            if m > best:
+                seed, best = e, m
+        members = [seed]
+        unassigned.remove(seed)
+        while len(members) < cap:
+            pick, key = None, None
+            for e in unassigned:
+                cand = (sum(int(W[e, m]) for m in members), mass(e))
+                if key is None or cand > key:
+                    pick, key = e, cand
+            members.append(pick)
+            unassigned.remove(pick)
+        for e in members:
+            placement[e] = g
+    return placement
+
+
+def dispatch_plan(idx, placement, G):
+    """Deduplicated dispatch: each token is sent to each group once.
+
+    D_t = the distinct groups of the token's chosen experts; one row per
+    (g, t) with g in D_t, rows ordered by (g, t).  assign_row[t, j] is the row
+    that carries expert slot j of token t.  Table I statistics of [COUPLING]:
+    share of tokens whose experts share one group, distinct destinations per
+    token, and rows removed as duplicates.  home(t) = t // (T/G).
+    """
+    idx = np.asarray(idx)
+    placement = np.asarray(placement, dtype=np.int64)
+    T, k = idx.shape
+    n_dest = np.zeros(T, dtype=np.int64)
+    dest = []
+    for t in range(T):
+        groups = sorted({int(placement[idx[t, j]]) for j in range(k)})
+        dest.append(groups)
+        n_dest[t] = len(groups)
+    group_rows = np.zeros(G, dtype=np.int64)
+    for t in range(T):
+        for g in dest[t]:
+            group_rows[g] += 1
+    group_offsets = np.zeros(G + 1, dtype=np.int64)
+    for g in range(G):
+        group_offsets[g + 1] = group_offsets[g] + group_rows[g]
+    fill = group_offsets[:-1].copy()
+    row_of = {}
+    row_token = np.zeros(int(group_offsets[G]), dtype=np.int64)
+    for t in range(T):
+        for g in dest[t]:
+            row_of[(g, t)] = fill[g]
+            row_token[fill[g]] = t
+            fill[g] += 1
+    assign_row = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            assign_row[t, j] = row_of[(int(placement[idx[t, j]]), t)]
+    rows_total = int(group_offsets[G])
+    per_home = T // G if T % G == 0 else None
+    off_home = 0
+    if per_home:
+        for t in range(T):
+            for g in dest[t]:
+                if g != t // per_home:
+                    off_home += 1
+    return {
+        "n_dest": n_dest, "group_rows": group_rows, "group_offsets": group_offsets,
+        "row_token": row_token, "assign_row": assign_row,
+        "rows_total": rows_total, "rows_removed": T * k - rows_total,
+        "tokens_single_group": int((n_dest == 1).sum()), "rows_off_home": off_home,
+        "same_group_share": float((n_dest == 1).mean()),
+        "mean_destinations": rows_total / T,
+        "dedup_fraction": (T * k - rows_total) / (T * k),
+    }
