@@ -1,0 +1,282 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the hot path of one Mixture-of-Experts layer on
+ * one GPU's share of tokens, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (router -> top-k gating -> permutation into expert-contiguous rows
+ * -> SwiGLU experts -> gate-weighted combine, and its backward) follows:
+ *   [COUPLING] "Expert Coupling in MoE Pretraining: Reducing All-to-All
+ *              Overhead with Correlated Placement and Token Shuffling":
+ *              Abstract (each token routed to k of E experts; dispatch and
+ *              combine in the forward and backward passes; a dispatcher that
+ *              sends each token to each GPU once), Fig. 5 (steps 3-5: dispatch,
+ *              expert computation, combine), Table I (placement statistics),
+ *              Table III (notation t, T, E, k, S(t), W[e,e']).
+ *   [REVISIT]  "Revisiting MoE and Dense Speed-Accuracy Comparisons for LLM
+ *              Training": Sec. 2.1 (SwiGLU, Top-K routing, load-balancing
+ *              loss), Sec. 2.2 (GShard gating/dispatch/combine, outer batches),
+ *              Sec. 3.6 (the second expert is simply the second best).
+ *   [LAYOUT]   "MoE Pretraining: Parallelism Layout Changes the Model, Not
+ *              Quality": Finding 3 (routing margin, near-ties), Two Kinds of
+ *              Layout Effects (per-machine balancing statistics), Correctness
+ *              Checks (bit-identical reruns).
+ *   [LOADING]  "Why does expert-parallel loading matter so much in MoE
+ *              training?": What to verify (each expert owned by exactly one
+ *              shard, equal expert counts per shard).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked [host].  Tensors are dense,
+ *    row-major and 16-byte aligned.  Shapes are given in brackets.
+ *  - "act" tensors (X, W1, W3, W2, Y, dY, dX, x_perm, y_perm, a, b, h, the
+ *    weight gradients) are fp32 when dims->act == MOE_F32 and bfloat16 when
+ *    dims->act == MOE_BF16.  The router weight, logits, gates, margins and
+ *    router gradients are always fp32.  Accumulation is always fp32.
+ *  - Weights are stored [expert, out, in]: W1, W3 [E, f, d]; W2 [E, d, f];
+ *    Wr [E, d].
+ *  - The caller owns all memory: outputs and the workspace are allocated by
+ *    the caller; the library allocates and frees nothing and never
+ *    synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream).  Outputs are fully overwritten.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    an error nothing is enqueued, outputs are untouched, and
+ *    moe_last_error() describes the problem.  Faults inside kernels surface
+ *    at the caller's next synchronisation.
+ *  - Results are bitwise reproducible from run to run: no floating-point
+ *    atomics, every reduction has a fixed order.
+ *  - Supported envelope (else MOE_ERR_UNSUPPORTED): 1 <= k <= min(E, 16),
+ *    E <= 256, d % 64 == 0, f % 64 == 0, T * k < 2^31, act in {F32, BF16}.
+ *  - topk_idx inputs must hold expert ids in [0, E) with no repeats within a
+ *    token (moe_route produces such tables).  Out-of-range ids are ignored by
+ *    the index kernels rather than written out of bounds.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, G not dividing T */
+  MOE_ERR_UNSUPPORTED = 2,       /* outside the supported envelope above */
+  MOE_ERR_WORKSPACE = 3,         /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_INVALID_PLACEMENT = 4, /* placement is not a balanced partition */
+  MOE_ERR_HIP = 5                /* a HIP launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct moe_dims {
+  int64_t T;    /* tokens */
+  int32_t d;    /* model width */
+  int32_t E;    /* experts */
+  int32_t f;    /* expert FFN width */
+  int32_t k;    /* experts per token */
+  int32_t act;  /* moe_dtype of the act tensors */
+} moe_dims;
+
+/* [host] Static string naming a status code. */
+const char* moe_status_string(int32_t status);
+
+/* [host] Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* [host] Workspace bytes that every entry point below needs for these dims
+ * (the maximum over the entry points; n_groups is the largest LB-statistics
+ * or dispatch-plan group count the caller will use).  Returns 0 when the dims
+ * are invalid. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups);
+
+/*
+ * moe_route -- router logits, top-k gating, margins, near-ties and
+ * per-block load-balancing statistics.
+ *   [COUPLING] Abstract / Table III: S(t) = the k experts selected for token t;
+ *   [REVISIT] Sec. 2.1 Top-K routing, Sec. 3.6 naive second expert;
+ *   [LAYOUT] Finding 3: margin between the k-th and (k+1)-th scores;
+ *   [LAYOUT] Two Kinds of Layout Effects and [REVISIT] Sec. 2.2 (outer
+ *   batches): balancing statistics per contiguous block of tokens.
+ *
+ * x [T,d] act; w_router [E,d] fp32.
+ * logits [T,E] fp32: l[t,e] = sum_i x[t,i] w_router[e,i] (no bias).
+ * topk_idx [T,k] int32: experts by descending logit, lower id first on ties.
+ * topk_gate [T,k] fp32: softmax over the k chosen logits.
+ * margin [T] fp32: l_(k) - l_(k+1) (the k-th minus the (k+1)-th largest
+ *   logit; +inf when k == E).
+ * near_tie_count [1] int32: number of tokens with margin < near_tie_eps.
+ * n_groups: G >= 1 dividing T (G = 1 for whole-batch statistics).
+ * group_count [G,E] int32: assignments of block r's tokens to expert e.
+ * group_mean_prob [G,E] fp32: mean over block r of the full softmax p[t,e].
+ * group_aux [G] fp32: E * sum_e (count[r,e] / (T/G * k)) * mean_prob[r,e].
+ * group_count, group_mean_prob and group_aux may each be NULL.
+ */
+moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
+                     float* logits, int32_t* topk_idx, float* topk_gate, float* margin,
+                     float near_tie_eps, int32_t* near_tie_count, int32_t n_groups,
+                     int32_t* group_count, float* group_mean_prob, float* group_aux,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_permute -- stable counting sort of the T*k (token, slot) assignments by
+ * expert, and the row gather into expert-contiguous order.
+ *   [COUPLING] Abstract and Fig. 5 step 3 (dispatch tokens to their experts);
+ *   [REVISIT] Sec. 2.2 (GShard dispatch: a token's position inside its expert
+ *   is the running count of earlier tokens that chose that expert).
+ *
+ * topk_idx [T,k] int32 in.
+ * expert_counts [E], expert_offsets [E+1] (exclusive scan; offsets[E] = T*k).
+ * pos [T,k]: row of assignment (t, j) in the permuted order; rows of one
+ *   expert are in ascending token id.
+ * src_token [T*k]: token of each permuted row.
+ * x [T,d] act and x_perm [T*k,d] act: x_perm[pos[t,j]] = x[t].  Pass both
+ *   NULL to build the plan only.
+ */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                       int32_t* src_token, const void* x, void* x_perm,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_swiglu_fwd -- the E SwiGLU experts as one grouped GEMM pair.
+ *   [REVISIT] Sec. 2.1 (SwiGLU activation); [LAYOUT] Methodology (SwiGLU
+ *   experts); [COUPLING] Fig. 5 step 4 (expert computation).
+ *
+ * For each expert e over rows p in [expert_offsets[e], expert_offsets[e+1]):
+ *   a[p] = x_perm[p] W1[e]^T,  b[p] = x_perm[p] W3[e]^T,
+ *   h[p] = silu(a[p]) * b[p]   (silu(z) = z / (1 + exp(-z))),
+ *   y_perm[p] = h[p] W2[e]^T.
+ * x_perm [T*k,d] act; expert_offsets [E+1] int32 (from moe_permute);
+ * w1, w3 [E,f,d] act; w2 [E,d,f] act.
+ * a_save, b_save, h_save [T*k,f] act: saved for the backward (required).
+ * y_perm [T*k,d] act.
+ */
+moe_status moe_grouped_swiglu_fwd(const moe_dims* dims, const void* x_perm,
+                                  const int32_t* expert_offsets, const void* w1,
+                                  const void* w3, const void* w2, void* a_save, void* b_save,
+                                  void* h_save, void* y_perm, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * moe_combine -- gate-weighted sum of each token's k expert rows.
+ *   [COUPLING] Abstract and Fig. 5 step 5 (combine the results);
+ *   [REVISIT] Sec. 2.2 (GShard combine).
+ *
+ * out[t] = sum_{j<k} gate[t,j] * rows[pos[t,j]], accumulated in fp32 in slot
+ * order j = 0..k-1, then stored as act.  gate == NULL means unit weights
+ * (the plain unpermute-and-sum used for the input gradient).
+ * rows [T*k,d] act; pos [T,k]; gate [T,k] fp32 or NULL; out [T,d] act.
+ */
+moe_status moe_combine(const moe_dims* dims, const void* rows, const int32_t* pos,
+                       const float* gate, void* out, void* stream);
+
+/*
+ * moe_combine_bwd -- adjoint of moe_combine with respect to rows and gates
+ * ("routed gradients" in the backward pass, [COUPLING] Abstract).
+ *
+ * dy_perm[pos[t,j]] = gate[t,j] * dy[t]           (act)
+ * dgate[t,j]        = <dy[t], y_perm[pos[t,j]]>   (fp32 dot over d)
+ * dy [T,d] act; y_perm [T*k,d] act; pos [T,k]; gate [T,k] fp32;
+ * dy_perm [T*k,d] act; dgate [T,k] fp32.
+ */
+moe_status moe_combine_bwd(const moe_dims* dims, const void* dy, const void* y_perm,
+                           const int32_t* pos, const float* gate, void* dy_perm,
+                           float* dgate, void* stream);
+
+/*
+ * moe_grouped_swiglu_bwd -- dgrad and wgrad grouped GEMMs of the experts.
+ *
+ * For each expert e over its rows p:
+ *   dh = dy_perm W2[e];  da = dh * b * silu'(a);  db = dh * silu(a)
+ *   dx_perm = da W1[e] + db W3[e]
+ *   dW2[e] = dy_perm^T h;  dW1[e] = da^T x_perm;  dW3[e] = db^T x_perm
+ * with silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + exp(-z)).
+ * Inputs: x_perm [T*k,d], a_save, b_save, h_save [T*k,f], dy_perm [T*k,d]
+ * (act); expert_offsets [E+1]; w1, w3 [E,f,d]; w2 [E,d,f] (act).
+ * Outputs: dx_perm [T*k,d] act; dw1, dw3 [E,f,d] act; dw2 [E,d,f] act.
+ * Each weight gradient is accumulated in fp32 over all rows of its expert in
+ * a fixed order and rounded to act once.  Experts with no rows get zeros.
+ */
+moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
+                                  const int32_t* expert_offsets, const void* w1,
+                                  const void* w3, const void* w2, const void* a_save,
+                                  const void* b_save, const void* h_save, const void* dy_perm,
+                                  void* dx_perm, void* dw1, void* dw3, void* dw2,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_bwd -- adjoint of the router (logits -> top-k -> renormalised
+ * softmax), fused with the unpermute-and-sum of the expert input gradient.
+ *
+ * dl[t, S_j(t)] = g_j (dg_j - sum_i g_i dg_i), zero for unchosen experts;
+ * dx[t]  = sum_j dx_perm[pos[t,j]] + sum_j dl[t,S_j(t)] w_router[S_j(t)]
+ *          (fp32, rounded once to act; the first sum is skipped when
+ *          dx_perm == NULL);
+ * dw_router[e] = sum over the rows p of expert e (ascending token order) of
+ *          dl[src_token[p], e] * x[src_token[p]]   (fp32).
+ * x [T,d] act; w_router [E,d]; topk_idx, topk_gate, dgate [T,k];
+ * expert_offsets [E+1], pos [T,k], src_token [T*k] from moe_permute;
+ * dx_perm [T*k,d] act or NULL; dx [T,d] act; dw_router [E,d] fp32.
+ */
+moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_router,
+                         const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                         const int32_t* expert_offsets, const int32_t* pos,
+                         const int32_t* src_token, const void* dx_perm, void* dx,
+                         float* dw_router, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * moe_coselect -- co-selection counts ([COUPLING] Table III, Fig. 2):
+ * W[e,e'] = number of tokens whose chosen set contains both e and e' (e != e'),
+ * diagonal zero.  topk_idx [T,k]; coselect [E,E] int32.
+ */
+moe_status moe_coselect(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx,
+                        int32_t* coselect, void* stream);
+
+/*
+ * moe_dispatch_plan -- the deduplicated dispatch row map: each token is sent
+ * to each group once ([COUPLING] Abstract; Table I statistics).
+ *
+ * placement [host] [E]: group of each expert.  It must be a balanced
+ *   partition (every entry in [0,G), exactly E/G experts per group), else
+ *   MOE_ERR_INVALID_PLACEMENT ([LOADING] What to verify).  1 <= G <= 64,
+ *   G divides E and T.
+ * D_t = the distinct groups of token t's experts.  One row per (g, t) with g
+ * in D_t, rows ordered by (g, t).
+ * n_dest [T] int32 = |D_t|; group_rows [G]; group_offsets [G+1];
+ * row_token [T*k] (first group_offsets[G] entries used): token of each row;
+ * assign_row [T,k]: the row that carries expert slot j of token t;
+ * stats [4] int32: rows_total = sum |D_t|, rows_removed = T*k - rows_total,
+ *   tokens_single_group = #{t : |D_t| = 1},
+ *   rows_off_home = #{rows (g,t) : g != t / (T/G)}.
+ */
+moe_status moe_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G,
+                             const int32_t* topk_idx, const int32_t* placement,
+                             int32_t* n_dest, int32_t* group_rows, int32_t* group_offsets,
+                             int32_t* row_token, int32_t* assign_row, int32_t* stats,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_placement_greedy -- [host] correlated expert placement ([COUPLING]
+ * Abstract and Fig. 3: experts that are often selected together go to the
+ * same GPU).  Deterministic, integer arithmetic only.  Fills one group at a
+ * time: seed = the unassigned expert with the largest co-selection mass to
+ * the other unassigned experts (ties: lowest id); then repeatedly add the
+ * unassigned expert with the largest co-selection count to the group's
+ * members (ties: larger mass to the unassigned experts, then lowest id)
+ * until the group holds E/G experts.
+ * coselect [host] [E,E] int64 (symmetric); placement [host] [E] int32 out.
+ */
+moe_status moe_placement_greedy(int32_t E, int32_t G, const int64_t* coselect,
+                                int32_t* placement);
+
+/* [host] 0 when placement [host][E] is a balanced partition over G groups,
+ * else MOE_ERR_INVALID_PLACEMENT (or MOE_ERR_INVALID_ARGUMENT). */
+moe_status moe_check_placement(int32_t E, int32_t G, const int32_t* placement);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -51,6 +51,34 @@ def _f64(a):
 
 
 # ---------------------------------------------------------------------------
+# Storage precision of activations.  The bf16 workloads store weights and
+# activations in bfloat16 and accumulate in higher precision.  With
+# act="bf16" every activation or activation-gradient tensor that a step of the
+# layer produces (a, b, h, y_perm, y, dy_perm, dh, da, db, dx_perm, dx) and the
+# expert weight gradients are rounded to bfloat16 when they are formed; all
+# sums are still carried out in float64.  act="f64" stores nothing rounded.
+# The router (logits, gates, its gradients) is fp32 in every workload and is
+# never rounded here.
+# ---------------------------------------------------------------------------
+
+def to_bf16(v):
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
+    Written from the definition: v = m * 2**e with 0.5 <= |m| < 1, so m * 2**8
+    holds the 8 kept bits in its integer part."""
+    v = _f64(v)
+    m, e = np.frexp(v)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def storage(act):
+    if act in ("f64", "f32", None):
+        return lambda v: _f64(v)
+    if act == "bf16":
+        return to_bf16
+    raise ValueError(act)
+
+
+# ---------------------------------------------------------------------------
 # Router: logits, top-k, gates, margins  ([COUPLING] Abstract: each token is
 # routed to k of E experts; [REVISIT] Sec. 2.1 Top-K routing, Table 1 router
 # weight "ME" with no bias; [REVISIT] Sec. 3.6 the second expert is simply the
@@ -197,9 +225,11 @@ def silu(a):
     return a * _sigmoid(a)
 
 
-def swiglu_experts(x_perm, offsets, w1, w3, w2):
+def swiglu_experts(x_perm, offsets, w1, w3, w2, act="f64"):
     """Per expert e over rows [offsets[e], offsets[e+1]):
-    a = X W1[e]^T, b = X W3[e]^T, h = silu(a) * b, y = h W2[e]^T."""
+    a = X W1[e]^T, b = X W3[e]^T, h = silu(a) * b, y = h W2[e]^T.
+    (act="bf16": a, b, h and y are stored as bfloat16 values.)"""
+    st = storage(act)
     x_perm = _f64(x_perm)
     w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
     R = x_perm.shape[0]
@@ -211,20 +241,22 @@ def swiglu_experts(x_perm, offsets, w1, w3, w2):
     for e in range(E):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         xe = x_perm[s]
-        a[s] = xe @ w1[e].T
-        b[s] = xe @ w3[e].T
-        h[s] = silu(a[s]) * b[s]
-        y[s] = h[s] @ w2[e].T
+        a[s] = st(xe @ w1[e].T)
+        b[s] = st(xe @ w3[e].T)
+        h[s] = st(silu(a[s]) * b[s])
+        y[s] = st(h[s] @ w2[e].T)
     return {"a": a, "b": b, "h": h, "y_perm": y}
 
 
-def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm):
+def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm, act="f64"):
     """Backward of swiglu_experts for the upstream gradient dy_perm [R, d].
 
     dh = dy W2[e]; da = dh * b * silu'(a); db = dh * silu(a);
     dx = da W1[e] + db W3[e]; dW2[e] = dy^T h; dW1[e] = da^T x; dW3[e] = db^T x,
-    with silu'(a) = s (1 + a (1 - s)), s = sigmoid(a).
+    with silu'(a) = s (1 + a (1 - s)), s = sigmoid(a) and h = silu(a) * b.
+    (act="bf16": dh, da, db, dx and the weight gradients are stored as bfloat16.)
     """
+    st = storage(act)
     x_perm, dy_perm = _f64(x_perm), _f64(dy_perm)
     a, b = _f64(a), _f64(b)
     w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
@@ -240,15 +272,15 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm):
     for e in range(E):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         sg = _sigmoid(a[s])
-        act = a[s] * sg
+        act_s = a[s] * sg
         dact = sg * (1.0 + a[s] * (1.0 - sg))
-        dh[s] = dy_perm[s] @ w2[e]
-        da[s] = dh[s] * b[s] * dact
-        db[s] = dh[s] * act
-        dx[s] = da[s] @ w1[e] + db[s] @ w3[e]
-        dw2[e] = dy_perm[s].T @ (act * b[s])
-        dw1[e] = da[s].T @ x_perm[s]
-        dw3[e] = db[s].T @ x_perm[s]
+        dh[s] = st(dy_perm[s] @ w2[e])
+        da[s] = st(dh[s] * b[s] * dact)
+        db[s] = st(dh[s] * act_s)
+        dx[s] = st(da[s] @ w1[e] + db[s] @ w3[e])
+        dw2[e] = st(dy_perm[s].T @ st(act_s * b[s]))
+        dw1[e] = st(da[s].T @ x_perm[s])
+        dw3[e] = st(db[s].T @ x_perm[s])
     return {"dx_perm": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2,
             "dh": dh, "da": da, "db": db}
 
@@ -258,7 +290,7 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm):
 # results; [REVISIT] Sec. 2.2 GShard combine)
 # ---------------------------------------------------------------------------
 
-def combine(rows, pos, gates=None):
+def combine(rows, pos, gates=None, act="f64"):
     """y[t] = sum_j g[t, j] * rows[pos[t, j]]  (unit weights when gates is None)."""
     rows = _f64(rows)
     T, k = pos.shape
@@ -266,18 +298,20 @@ def combine(rows, pos, gates=None):
     for j in range(k):
         w = 1.0 if gates is None else _f64(gates)[:, j:j + 1]
         y += w * rows[np.asarray(pos[:, j], dtype=np.int64)]
-    return y
+    return storage(act)(y)
 
 
-def combine_bwd(dy, y_perm, pos, gates):
-    """dy_perm[pos[t,j]] = g[t,j] dY[t];  dgate[t,j] = <dY[t], y_perm[pos[t,j]]>."""
+def combine_bwd(dy, y_perm, pos, gates, act="f64"):
+    """dy_perm[pos[t,j]] = g[t,j] dY[t];  dgate[t,j] = <dY[t], y_perm[pos[t,j]]>.
+    (act="bf16": dy_perm is stored as bfloat16; dgate is a router quantity.)"""
+    st = storage(act)
     dy, y_perm, gates = _f64(dy), _f64(y_perm), _f64(gates)
     T, k = pos.shape
     dy_perm = np.zeros((T * k, dy.shape[1]))
     dgate = np.zeros((T, k))
     for j in range(k):
         p = np.asarray(pos[:, j], dtype=np.int64)
-        dy_perm[p] = gates[:, j:j + 1] * dy
+        dy_perm[p] = st(gates[:, j:j + 1] * dy)
         dgate[:, j] = (dy * y_perm[p]).sum(axis=1)
     return dy_perm, dgate
 
@@ -304,11 +338,12 @@ def route_bwd(x, wr, idx, gates, dgate):
 # Whole layer
 # ---------------------------------------------------------------------------
 
-def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None):
+def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f64"):
     """Router -> permute -> SwiGLU experts -> combine.
 
     routing, when given, is a (topk_idx, gates) pair that replaces the router's
     own decision (the logits, margins and near-ties are still reported).
+    act: storage precision of the activations ("f64" or "bf16").
     """
     E = np.asarray(wr).shape[0]
     r = route(x, wr, k, near_tie_eps)
@@ -320,20 +355,22 @@ def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None):
         idx, gates = r["topk_idx"], r["gates"]
     plan = permute_plan(idx, E)
     x_perm = gather_rows(x, plan["src"])
-    ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2)
-    y = combine(ex["y_perm"], plan["pos"], gates)
+    ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2, act)
+    y = combine(ex["y_perm"], plan["pos"], gates, act)
     out = dict(r)
     out.update(plan)
     out.update(ex)
-    out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y})
+    out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y, "act": act})
     return out
 
 
 def layer_backward(x, wr, w1, w3, w2, fwd, dy):
-    """Backward of layer_forward for the upstream gradient dy [T, d]."""
-    dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"])
+    """Backward of layer_forward for the upstream gradient dy [T, d], in the
+    forward's storage precision."""
+    act = fwd.get("act", "f64")
+    dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"], act)
     eb = swiglu_experts_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2,
-                            fwd["a"], fwd["b"], dy_perm)
+                            fwd["a"], fwd["b"], dy_perm, act)
     dx_exp = combine(eb["dx_perm"], fwd["pos"], None)
     rb = route_bwd(x, wr, fwd["topk_idx"], fwd["gates"], dgate)
     return {
@@ -341,7 +378,7 @@ def layer_backward(x, wr, w1, w3, w2, fwd, dy):
         "dx_perm": eb["dx_perm"], "dh": eb["dh"], "da": eb["da"], "db": eb["db"],
         "dw1": eb["dw1"], "dw3": eb["dw3"], "dw2": eb["dw2"],
         "dx_expert": dx_exp, "dlogits": rb["dlogits"],
-        "dx": dx_exp + rb["dx_router"], "dwr": rb["dwr"],
+        "dx": storage(act)(dx_exp + rb["dx_router"]), "dwr": rb["dwr"],
     }
 
 

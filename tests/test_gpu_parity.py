@@ -1,0 +1,350 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Rules (per output tensor):
+  * integer and index outputs (routing outside near-ties, counts, offsets,
+    permutation, dispatch plan, co-selection): bit-exact;
+  * routing: identical expert sets wherever the oracle's top-k margin is at
+    least 1e-3; where it is smaller (a near-tie) the GPU's set must still be a
+    valid top-k of the oracle's logits to within fp32 resolution;
+  * floats: max_i |g - o| / max(|o|, rms(o)) <= 1e-4 for fp32 workloads and
+    for the router's fp32 outputs, <= 2e-2 for bf16 workloads.
+Downstream of the router, both sides run on the oracle's routing decision
+(uploaded to the GPU), so float parity is judged on identical routing.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import get_config, make_layer_inputs, stream
+from top_routing_grouped_router_amd import MoELayer
+import top_routing_grouped_router_amd as M
+
+from _util import TOL, TOL_ROUTER, act_torch, dev, host, per_slice_err, rel_err
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-3
+
+
+def _announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+# ---------------------------------------------------------------- route
+
+def check_route(layer, x, wr, k, G=1, eps=EPS):
+    """Run moe_route and hold it to the routing rules.  Returns the oracle route."""
+    E = wr.shape[0]
+    o = O.route(x, wr, k, eps)
+    act = layer.act
+    layer.route(dev(x, act), dev(wr, torch.float32))
+    torch.cuda.synchronize()
+    lg, idx = host(layer.logits), host(layer.topk_idx)
+    gate, margin = host(layer.topk_gate), host(layer.margin)
+    T = x.shape[0]
+    if T == 0:
+        assert int(host(layer.near_tie_count)[0]) == 0
+        return o, np.zeros(0, bool)
+    assert rel_err(lg, o["logits"]) <= TOL_ROUTER
+    scale = float(np.sqrt(np.mean(o["logits"] ** 2))) or 1.0
+    tol = 1e-5 * scale
+    assert idx.min() >= 0 and idx.max() < E
+    assert np.all(np.sort(idx, 1)[:, 1:] != np.sort(idx, 1)[:, :-1])  # no repeats
+    same = np.all(np.sort(idx, 1) == np.sort(o["topk_idx"], 1), axis=1)
+    clear = o["margin"] >= eps
+    assert same[clear].all(), f"{(~same[clear]).sum()} clear-margin tokens routed differently"
+    lo = o["logits"]
+    for t in np.where(~same)[0]:
+        chosen = idx[t]
+        others = np.setdiff1d(np.arange(E), chosen)
+        assert lo[t, chosen].min() >= lo[t, others].max() - tol, t
+    # slot order: non-increasing oracle logits (within fp32 resolution)
+    ordered = np.take_along_axis(lo, idx.astype(np.int64), 1)
+    assert np.all(np.diff(ordered, axis=1) <= tol)
+    # gates compared per expert id, on tokens with the same set
+    gd = np.zeros((T, E))
+    go = np.zeros((T, E))
+    np.put_along_axis(gd, idx.astype(np.int64), gate, 1)
+    np.put_along_axis(go, o["topk_idx"].astype(np.int64), o["gates"], 1)
+    assert rel_err(gd[same], go[same]) <= TOL_ROUTER
+    if k < E:
+        assert np.abs(margin[same] - o["margin"][same]).max() <= tol
+    else:
+        assert np.all(np.isinf(margin))
+    ambiguous = int((np.abs(o["margin"] - eps) < tol).sum())
+    assert abs(int(host(layer.near_tie_count)[0]) - o["near_tie_count"]) <= ambiguous
+    # load-balancing statistics per contiguous block
+    s = O.lb_stats(lo, o["topk_idx"], E, G)
+    n = T // G
+    mism = [(~same[r * n:(r + 1) * n]).sum() for r in range(G)]
+    cnt = host(layer.group_count)
+    for r in range(G):
+        assert np.abs(cnt[r] - s["count"][r]).sum() <= 2 * mism[r]
+    assert rel_err(host(layer.group_mean_prob), s["P"]) <= TOL_ROUTER
+    if sum(mism) == 0:
+        assert np.array_equal(cnt, s["count"])
+        assert rel_err(host(layer.group_aux), s["aux"]) <= TOL_ROUTER
+    return o, same
+
+
+# ---------------------------------------------------------------- whole layer
+
+def run_layer(cfg, inp, G=1, backward=True, routing=None):
+    """Forward (and backward) on the GPU with the given routing injected."""
+    act = act_torch(cfg.act)
+    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G)
+    t = {k: dev(v, act) for k, v in inp.items() if k != "wr"}
+    t["wr"] = dev(inp["wr"], torch.float32)
+    layer.forward(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], routing=routing)
+    if backward:
+        layer.backward(t["dy"], t["x"], t["wr"], t["w1"], t["w3"], t["w2"])
+    torch.cuda.synchronize()
+    return layer
+
+
+def store(cfg):
+    """The oracle's storage precision for a workload: bf16 workloads store
+    activations as bfloat16 (sums in float64); fp32 workloads are compared
+    with the unrounded float64 oracle."""
+    return "bf16" if cfg.act == "bf16" else "f64"
+
+
+def compare_exact(cfg, inp, layer, k, routing):
+    """The layer's outputs Y and dX against the unrounded float64 oracle: the
+    bf16 storage of activations stays within the bf16 tolerance there too."""
+    o_f = O.layer_forward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], k,
+                          routing=routing)
+    o_b = O.layer_backward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], o_f, inp["dy"])
+    tol = TOL[cfg.act]
+    for key, ref in (("y", o_f["y"]), ("dx", o_b["dx"])):
+        err = rel_err(host(getattr(layer, key)), ref)
+        print(f"[exact] {key} {err:.2e}", flush=True)
+        assert err <= tol, (key, err)
+
+
+def oracle_routing(o):
+    return (dev(o["topk_idx"], torch.int32), dev(o["gates"].astype(np.float32), torch.float32))
+
+
+def compare_layer(cfg, inp, layer, o_f, o_b=None):
+    tol = TOL[cfg.act]
+    assert np.array_equal(host(layer.expert_counts), o_f["counts"])
+    assert np.array_equal(host(layer.expert_offsets), o_f["offsets"])
+    assert np.array_equal(host(layer.pos), o_f["pos"])
+    assert np.array_equal(host(layer.src_token), o_f["src"])
+    # the permutation moves bits: x_perm[p] == x[src[p]] exactly
+    assert np.array_equal(host(layer.x_perm), inp["x"][o_f["src"]])
+    for key in ("a", "b", "h", "y_perm", "y"):
+        err = rel_err(host(getattr(layer, key)), o_f[key])
+        assert err <= tol, (key, err)
+    if o_b is None:
+        return
+    for key in ("dy_perm", "dgate", "dx_perm", "dx"):
+        err = rel_err(host(getattr(layer, key)), o_b[key])
+        assert err <= tol, (key, err)
+    for key in ("dw1", "dw3", "dw2"):
+        err = per_slice_err(host(getattr(layer, key)), o_b[key])
+        assert err <= tol, (key, err)
+    err = per_slice_err(host(layer.dwr), o_b["dwr"])
+    assert err <= tol, ("dwr", err)
+
+
+SMALL_CASES = {
+    # name: (T, d, E, f, k, act)   -- several tiles, ragged rows and columns
+    "ragged_bf16": (1000, 256, 8, 192, 3, "bf16"),
+    "ragged_f32": (777, 128, 6, 128, 2, "f32"),
+    "k_equals_E": (37, 64, 4, 64, 4, "bf16"),
+    "single_expert_dense": (300, 64, 1, 64, 1, "f32"),
+    "max_experts_max_k": (260, 64, 256, 64, 16, "bf16"),
+    "wide_f_bf16": (513, 128, 5, 320, 2, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_layer_small_cases(name):
+    _announce(name)
+    T, d, E, f, k, act = SMALL_CASES[name]
+    cfg = get_config("c2", T=T, d=d, E=E, f=f, k=k, act=act, x_kind="normal", backward=True)
+    inp = make_layer_inputs(cfg, seed=100 + list(SMALL_CASES).index(name))
+    layer0 = MoELayer(T, d, E, f, k, act_torch(act))
+    o_route, _ = check_route(layer0, inp["x"], inp["wr"], k)
+    o_f = O.layer_forward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], k, act=store(cfg))
+    o_b = O.layer_backward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], o_f, inp["dy"])
+    layer = run_layer(cfg, inp, routing=oracle_routing(o_f))
+    compare_layer(cfg, inp, layer, o_f, o_b)
+    compare_exact(cfg, inp, layer, k, (o_f["topk_idx"], o_f["gates"]))
+    if E == 1:
+        assert np.all(host(layer.dwr) == 0.0)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_layer_full_config(name):
+    """Element-by-element parity at the workload's full size."""
+    _announce(name)
+    cfg = get_config(name)
+    inp = make_layer_inputs(cfg, with_dy=True)
+    G = max(cfg.lb_groups)
+    layer0 = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act_torch(cfg.act), n_groups=G)
+    check_route(layer0, inp["x"], inp["wr"], cfg.k, G=G)
+    o_f = O.layer_forward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], cfg.k,
+                          act=store(cfg))
+    o_b = O.layer_backward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], o_f, inp["dy"])
+    layer = run_layer(cfg, inp, G=G, routing=oracle_routing(o_f))
+    compare_layer(cfg, inp, layer, o_f, o_b)
+    compare_exact(cfg, inp, layer, cfg.k, (o_f["topk_idx"], o_f["gates"]))
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_layer_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration: the router
+    and the permutation are compared in full; outputs that the oracle can
+    compute one at a time are compared on samples (tokens for Y, dX, dgate;
+    whole experts for dW1, dW3, dW2); dWr by a property that holds at any size
+    (every token's router gradients sum to zero over the experts)."""
+    _announce(name)
+    cfg = get_config(name)
+    inp = make_layer_inputs(cfg)
+    tol = TOL[cfg.act]
+    layer0 = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act_torch(cfg.act))
+    o_r, same = check_route(layer0, inp["x"], inp["wr"], cfg.k)
+    del layer0
+    print(f"[{name}] near-ties {o_r['near_tie_count']} / {cfg.T}, routing mismatches "
+          f"{int((~same).sum())}", flush=True)
+    idx, gates = o_r["topk_idx"], o_r["gates"]
+    layer = run_layer(cfg, inp, routing=oracle_routing(o_r))
+    plan = O.permute_plan(idx, cfg.E)
+    for key, lk in (("counts", "expert_counts"), ("offsets", "expert_offsets"), ("pos", "pos"),
+                    ("src", "src_token")):
+        assert np.array_equal(host(getattr(layer, lk)), plan[key]), key
+    # sampled tokens: every token's forward and input gradient are its own
+    S = np.sort(stream(7, 7).choice(cfg.T, size=48, replace=False))
+    sub_f = O.layer_forward(inp["x"][S], inp["wr"], inp["w1"], inp["w3"], inp["w2"], cfg.k,
+                            routing=(idx[S], gates[S]), act=store(cfg))
+    sub_b = O.layer_backward(inp["x"][S], inp["wr"], inp["w1"], inp["w3"], inp["w2"], sub_f,
+                             inp["dy"][S])
+    assert rel_err(host(layer.y)[S], sub_f["y"]) <= tol
+    assert rel_err(host(layer.dgate)[S], sub_b["dgate"]) <= tol
+    assert rel_err(host(layer.dx)[S], sub_b["dx"]) <= tol
+    # sampled experts: dW over all of the expert's rows
+    counts = plan["counts"]
+    nz = np.where(counts > 0)[0]
+    experts = sorted({int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])]),
+                      int(nz[len(nz) // 2])})
+    dw1, dw3, dw2 = host(layer.dw1), host(layer.dw3), host(layer.dw2)
+    for e in experts:
+        rows = plan["src"][plan["offsets"][e]:plan["offsets"][e + 1]]
+        slot = np.array([int(np.where(idx[t] == e)[0][0]) for t in rows])
+        xe = inp["x"][rows]
+        dye = O.storage(store(cfg))(gates[rows, slot][:, None] * inp["dy"][rows])
+        off = np.array([0, len(rows)])
+        ex = O.swiglu_experts(xe, off, inp["w1"][e:e + 1], inp["w3"][e:e + 1], inp["w2"][e:e + 1],
+                              act=store(cfg))
+        eb = O.swiglu_experts_bwd(xe, off, inp["w1"][e:e + 1], inp["w3"][e:e + 1],
+                                  inp["w2"][e:e + 1], ex["a"], ex["b"], dye, act=store(cfg))
+        for key, got in (("dw1", dw1), ("dw3", dw3), ("dw2", dw2)):
+            err = rel_err(got[e], eb[key][0])
+            assert err <= tol, (name, e, key, err)
+    dwr = host(layer.dwr).astype(np.float64)
+    rms = float(np.sqrt(np.mean(dwr ** 2)))
+    assert rms > 0
+    assert np.abs(dwr.sum(0)).max() <= 1e-4 * rms * np.sqrt(cfg.E)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_route_exact_ties_pick_lower_id():
+    _announce("exact ties")
+    T, d, E, k = 256, 64, 8, 3
+    g = stream(31, 1)
+    wr = g.standard_normal((E, d)).astype(np.float32)
+    wr[5] = wr[2]          # experts 2 and 5 always tie exactly
+    wr[7] = wr[0]
+    x = g.standard_normal((T, d)).astype(np.float32)
+    layer = MoELayer(T, d, E, 64, k, torch.float32)
+    o, same = check_route(layer, x, wr, k)
+    idx = host(layer.topk_idx)
+    assert np.array_equal(idx, o["topk_idx"])
+    for t in range(T):
+        row = list(idx[t])
+        if 5 in row:
+            assert 2 in row and row.index(2) < row.index(5)
+
+
+def test_bitwise_rerun_and_layout_invariance():
+    """Two runs give identical bytes; the LB-statistics grouping does not
+    change any layer output (only the per-group statistics)."""
+    _announce("determinism")
+    cfg = get_config("c2", T=4096)
+    inp = make_layer_inputs(cfg)
+    outs = []
+    for G in (1, 1, 8):
+        layer = run_layer(cfg, inp, G=G)
+        outs.append({k: host(getattr(layer, k)).copy() for k in
+                     ("logits", "topk_idx", "topk_gate", "y", "dx", "dw1", "dw3", "dw2", "dwr",
+                      "dgate")})
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[1][k].view(np.uint8)), k
+        assert np.array_equal(outs[0][k].view(np.uint8), outs[2][k].view(np.uint8)), k
+
+
+def test_empty_batch():
+    _announce("T=0")
+    cfg = get_config("c2", T=0, d=64, E=4, f=64, k=2)
+    layer = MoELayer(0, 64, 4, 64, 2, torch.bfloat16)
+    z = torch.zeros(1, 64, dtype=torch.bfloat16, device="cuda")[:0]
+    w = torch.ones(4, 64, 64, dtype=torch.bfloat16, device="cuda")
+    wr = torch.ones(4, 64, dtype=torch.float32, device="cuda")
+    layer.dw1.fill_(7)
+    layer.dwr.fill_(7)
+    layer.step(z, wr, w, w, w, z)
+    torch.cuda.synchronize()
+    assert int(host(layer.near_tie_count)[0]) == 0
+    assert np.all(host(layer.expert_counts) == 0) and np.all(host(layer.expert_offsets) == 0)
+    assert np.all(host(layer.dw1) == 0) and np.all(host(layer.dwr) == 0)
+    assert np.all(host(layer.group_count) == 0)
+
+
+# ---------------------------------------------------------------- index products
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_dispatch_plan_and_coselect(name):
+    _announce(f"plan {name}")
+    cfg = get_config(name)
+    inp = make_layer_inputs(cfg, parts=("x", "wr"))
+    fit = make_layer_inputs(cfg, batch_seed=1, parts=("x",))
+    idx = O.route(inp["x"], inp["wr"], cfg.k)["topk_idx"]
+    idx_fit = O.route(fit["x"], inp["wr"], cfg.k)["topk_idx"]
+    d_idx = dev(idx, torch.int32)
+    W = torch.empty(cfg.E, cfg.E, dtype=torch.int32, device="cuda")
+    M.moe_coselect(cfg.T, cfg.k, cfg.E, d_idx, W)
+    torch.cuda.synchronize()
+    W_o = O.coselect(idx, cfg.E)
+    assert np.array_equal(host(W), W_o)
+    W_fit = O.coselect(idx_fit, cfg.E)
+    for G in cfg.plan_groups:
+        greedy = M.moe_placement_greedy(cfg.E, G, W_fit)
+        assert greedy == [int(v) for v in O.placement_greedy(W_fit, G)]
+        for kind, pl in (("contiguous", O.placement_contiguous(cfg.E, G)), ("correlated", greedy)):
+            T, k = cfg.T, cfg.k
+            out = {n: torch.empty(s, dtype=torch.int32, device="cuda") for n, s in
+                   (("n_dest", T), ("group_rows", G), ("group_offsets", G + 1),
+                    ("row_token", T * k), ("assign_row", (T, k)), ("stats", 4))}
+            ws = torch.empty(M.workspace_bytes(M.make_dims(T, 64, cfg.E, 64, k, 1), G),
+                             dtype=torch.uint8, device="cuda")
+            M.moe_dispatch_plan(T, k, cfg.E, G, d_idx, pl, out["n_dest"], out["group_rows"],
+                                out["group_offsets"], out["row_token"], out["assign_row"],
+                                out["stats"], ws)
+            torch.cuda.synchronize()
+            o = O.dispatch_plan(idx, pl, G)
+            R = o["rows_total"]
+            assert np.array_equal(host(out["n_dest"]), o["n_dest"])
+            assert np.array_equal(host(out["group_rows"]), o["group_rows"])
+            assert np.array_equal(host(out["group_offsets"]), o["group_offsets"])
+            assert np.array_equal(host(out["row_token"])[:R], o["row_token"])
+            assert np.array_equal(host(out["assign_row"]), o["assign_row"])
+            assert list(host(out["stats"])) == [R, o["rows_removed"], o["tokens_single_group"],
+                                                o["rows_off_home"]]
+            print(f"[{name} G={G} {kind}] same-group {o['same_group_share']:.3f} "
+                  f"destinations {o['mean_destinations']:.3f} dedup {o['dedup_fraction']:.3f}",
+                  flush=True)

@@ -19,6 +19,37 @@ from synth import make_routing, stream
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+# ---------------------------------------------------------------- storage precision
+
+def test_bf16_storage_rounding_agrees_with_torch():
+    """The oracle's bf16 rounding (from the frexp definition) equals torch's
+    float32 -> bfloat16 conversion, ties to even included."""
+    import torch
+    g = stream(2, 2)
+    v = np.concatenate([g.standard_normal(50000) * 10.0 ** g.integers(-6, 6, 50000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, 3.0]])
+    v32 = v.astype(np.float32)
+    ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.to_bf16(v32.astype(np.float64)), ref)
+    assert O.to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0          # tie -> even
+    assert O.to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+def test_bf16_storage_layer_stays_close_to_exact():
+    """Storing activations as bf16 moves the layer output by bf16-sized amounts
+    only (well-conditioned outputs on Gaussian data)."""
+    x, wr, w1, w3, w2, dy, k = _tiny_problem(9, T=64, d=32, E=4, f=32, k=2)
+    ex = O.layer_forward(x, wr, w1, w3, w2, k)
+    bf = O.layer_forward(x, wr, w1, w3, w2, k, act="bf16")
+    assert np.array_equal(ex["topk_idx"], bf["topk_idx"])
+    rel = np.abs(bf["y"] - ex["y"]).max() / np.abs(ex["y"]).max()
+    assert 0 < rel < 2e-2
+    assert np.array_equal(O.to_bf16(bf["y"]), bf["y"])
+    bb = O.layer_backward(x, wr, w1, w3, w2, bf, dy)
+    for key in ("dx", "dw1", "dw2", "dx_perm", "dh", "da"):
+        assert np.array_equal(O.to_bf16(bb[key]), bb[key]), key
+
+
 # ---------------------------------------------------------------- top-k (D1)
 
 def brute_topk(row, k):

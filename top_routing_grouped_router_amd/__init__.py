@@ -1,0 +1,30 @@
+"""MI355X (gfx950) hot path of one Mixture-of-Experts layer.
+
+The computation lives in libmoe.so (hand-written HIP kernels behind the C ABI
+of include/moe.h); this package holds its sources (csrc/), the build step
+(build.py), a ctypes binding with the same names as the C entry points
+(_lib.py) and the layer's call sequence (layer.py).
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MOE_BF16,
+    MOE_F32,
+    MoEError,
+    alloc_workspace,
+    lib,
+    make_dims,
+    moe_check_placement,
+    moe_combine,
+    moe_combine_bwd,
+    moe_coselect,
+    moe_dispatch_plan,
+    moe_grouped_swiglu_bwd,
+    moe_grouped_swiglu_fwd,
+    moe_permute,
+    moe_placement_greedy,
+    moe_route,
+    moe_route_bwd,
+    workspace_bytes,
+)
+from .layer import MoELayer  # noqa: F401

@@ -1,0 +1,268 @@
+"""ctypes binding of libmoe.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every function here checks tensor placement and
+dtypes, turns torch tensors into device pointers, passes torch's current HIP
+stream, and raises MoEError when the library returns a non-zero status.  All
+computation happens in the library's HIP kernels.  There is no fallback: if
+the library is missing, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_F32 = 0
+MOE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "MOE_OK",
+    1: "MOE_ERR_INVALID_ARGUMENT",
+    2: "MOE_ERR_UNSUPPORTED",
+    3: "MOE_ERR_WORKSPACE",
+    4: "MOE_ERR_INVALID_PLACEMENT",
+    5: "MOE_ERR_HIP",
+}
+
+EXPORTED = (
+    "moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
+    "moe_grouped_swiglu_fwd", "moe_combine", "moe_combine_bwd", "moe_grouped_swiglu_bwd",
+    "moe_route_bwd", "moe_coselect", "moe_dispatch_plan", "moe_placement_greedy",
+    "moe_check_placement",
+)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        self.name = STATUS_NAMES.get(status, f"status {status}")
+        super().__init__(f"{func}: {self.name}: {detail}")
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("f", ctypes.c_int32), ("k", ctypes.c_int32), ("act", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+_DIMS = ctypes.POINTER(moe_dims)
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_I32]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_workspace_bytes": (_SZ, [_DIMS, _I32]),
+    "moe_route": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_swiglu_fwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_combine": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
+    "moe_combine_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_grouped_swiglu_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _SZ, _P]),
+    "moe_route_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_coselect": (_I32, [_I64, _I32, _I32, _P, _P, _P]),
+    "moe_dispatch_plan": (_I32, [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _SZ, _P]),
+    "moe_placement_greedy": (_I32, [_I32, _I32, _P, _P]),
+    "moe_check_placement": (_I32, [_I32, _I32, _P]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m top_routing_grouped_router_amd.build` (no CPU fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise MoEError(status, func, last_error())
+
+
+def make_dims(T: int, d: int, E: int, f: int, k: int, act) -> moe_dims:
+    if isinstance(act, torch.dtype):
+        act = MOE_BF16 if act == torch.bfloat16 else MOE_F32
+    return moe_dims(int(T), int(d), int(E), int(f), int(k), int(act))
+
+
+def act_dtype(dims: moe_dims) -> torch.dtype:
+    return torch.bfloat16 if dims.act == MOE_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace_bytes(dims: moe_dims, n_groups: int = 1) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(dims), int(n_groups)))
+
+
+def alloc_workspace(dims: moe_dims, n_groups: int = 1, device="cuda") -> torch.Tensor:
+    n = max(workspace_bytes(dims, n_groups), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def moe_route(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_eps,
+              near_tie_count, n_groups, group_count, group_mean_prob, group_aux, workspace,
+              stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_route(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(w_router, "w_router", torch.float32),
+        _ptr(logits, "logits", torch.float32), _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(topk_gate, "topk_gate", torch.float32), _ptr(margin, "margin", torch.float32),
+        float(near_tie_eps), _ptr(near_tie_count, "near_tie_count", torch.int32), int(n_groups),
+        _ptr(group_count, "group_count", torch.int32),
+        _ptr(group_mean_prob, "group_mean_prob", torch.float32),
+        _ptr(group_aux, "group_aux", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_route")
+
+
+def moe_permute(dims, topk_idx, expert_counts, expert_offsets, pos, src_token, x, x_perm,
+                workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_permute(
+        ctypes.byref(dims), _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(expert_counts, "expert_counts", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(pos, "pos", torch.int32),
+        _ptr(src_token, "src_token", torch.int32), _ptr(x, "x", act), _ptr(x_perm, "x_perm", act),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_permute")
+
+
+def moe_grouped_swiglu_fwd(dims, x_perm, expert_offsets, w1, w3, w2, a_save, b_save, h_save,
+                           y_perm, workspace=None, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_grouped_swiglu_fwd(
+        ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
+        _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
+        _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(y_perm, "y_perm", act),
+        _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_grouped_swiglu_fwd")
+
+
+def moe_combine(dims, rows, pos, gate, out, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_combine(ctypes.byref(dims), _ptr(rows, "rows", act),
+                           _ptr(pos, "pos", torch.int32), _ptr(gate, "gate", torch.float32),
+                           _ptr(out, "out", act), _stream(stream))
+    _check(st, "moe_combine")
+
+
+def moe_combine_bwd(dims, dy, y_perm, pos, gate, dy_perm, dgate, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_combine_bwd(ctypes.byref(dims), _ptr(dy, "dy", act),
+                               _ptr(y_perm, "y_perm", act), _ptr(pos, "pos", torch.int32),
+                               _ptr(gate, "gate", torch.float32), _ptr(dy_perm, "dy_perm", act),
+                               _ptr(dgate, "dgate", torch.float32), _stream(stream))
+    _check(st, "moe_combine_bwd")
+
+
+def moe_grouped_swiglu_bwd(dims, x_perm, expert_offsets, w1, w3, w2, a_save, b_save, h_save,
+                           dy_perm, dx_perm, dw1, dw3, dw2, workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_grouped_swiglu_bwd(
+        ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
+        _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
+        _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(dy_perm, "dy_perm", act),
+        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act),
+        _ptr(dw2, "dw2", act), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_grouped_swiglu_bwd")
+
+
+def moe_route_bwd(dims, x, w_router, topk_idx, topk_gate, dgate, expert_offsets, pos, src_token,
+                  dx_perm, dx, dw_router, workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_route_bwd(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(w_router, "w_router", torch.float32),
+        _ptr(topk_idx, "topk_idx", torch.int32), _ptr(topk_gate, "topk_gate", torch.float32),
+        _ptr(dgate, "dgate", torch.float32), _ptr(expert_offsets, "expert_offsets", torch.int32),
+        _ptr(pos, "pos", torch.int32), _ptr(src_token, "src_token", torch.int32),
+        _ptr(dx_perm, "dx_perm", act), _ptr(dx, "dx", act),
+        _ptr(dw_router, "dw_router", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_route_bwd")
+
+
+def moe_coselect(T, k, E, topk_idx, coselect, stream=None):
+    st = lib().moe_coselect(int(T), int(k), int(E), _ptr(topk_idx, "topk_idx", torch.int32),
+                            _ptr(coselect, "coselect", torch.int32), _stream(stream))
+    _check(st, "moe_coselect")
+
+
+def moe_dispatch_plan(T, k, E, G, topk_idx, placement, n_dest, group_rows, group_offsets,
+                      row_token, assign_row, stats, workspace, stream=None):
+    pl = (ctypes.c_int32 * E)(*[int(v) for v in placement])
+    st = lib().moe_dispatch_plan(
+        int(T), int(k), int(E), int(G), _ptr(topk_idx, "topk_idx", torch.int32),
+        ctypes.cast(pl, ctypes.c_void_p), _ptr(n_dest, "n_dest", torch.int32),
+        _ptr(group_rows, "group_rows", torch.int32),
+        _ptr(group_offsets, "group_offsets", torch.int32),
+        _ptr(row_token, "row_token", torch.int32), _ptr(assign_row, "assign_row", torch.int32),
+        _ptr(stats, "stats", torch.int32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_dispatch_plan")
+
+
+def moe_placement_greedy(E, G, coselect) -> list:
+    import numpy as np
+    W = np.ascontiguousarray(np.asarray(coselect, dtype=np.int64))
+    if W.shape != (E, E):
+        raise ValueError("coselect must be [E, E]")
+    out = (ctypes.c_int32 * E)()
+    st = lib().moe_placement_greedy(int(E), int(G), W.ctypes.data_as(ctypes.c_void_p),
+                                    ctypes.cast(out, ctypes.c_void_p))
+    _check(st, "moe_placement_greedy")
+    return list(out)
+
+
+def moe_check_placement(E, G, placement) -> None:
+    pl = (ctypes.c_int32 * E)(*[int(v) for v in placement])
+    st = lib().moe_check_placement(int(E), int(G), ctypes.cast(pl, ctypes.c_void_p))
+    _check(st, "moe_check_placement")

@@ -1,0 +1,143 @@
+// Gate-weighted combine of each token's k expert rows, and its adjoint.
+//
+// Method sources: "Expert Coupling in MoE Pretraining" (Abstract and Fig. 5
+// step 5: combine the expert results; the backward pass routes the gradients
+// the same way); "Revisiting MoE and Dense Speed-Accuracy Comparisons"
+// (Sec. 2.2: GShard combine).
+//
+// Both kernels are gathers keyed by the token, so no two threads ever write
+// the same output and no atomics are needed: the sum over the k slots runs in
+// slot order in fp32, which makes the result bitwise reproducible.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+// out[t] = sum_j gate[t,j] * rows[pos[t,j]]; one thread per 16-byte piece.
+template <typename TA>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ rows,
+                                                           const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ gate,
+                                                           uint4* __restrict__ out, int64_t T,
+                                                           int32_t vpr, int32_t k) {
+  constexpr int kPer = Act<TA>::kPer16B;
+  const int64_t total = T * vpr;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total;
+       v += stride) {
+    const int64_t t = v / vpr;
+    const int32_t c = static_cast<int32_t>(v - t * vpr);
+    float acc[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = pos[t * k + j];
+      if (p < 0) continue;
+      const float g = gate ? gate[t * k + j] : 1.0f;
+      float r[kPer];
+      unpack16(rows[p * vpr + c], r, TA{});
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(g, r[i], acc[i]);
+    }
+    out[v] = pack16(acc, TA{});
+  }
+}
+
+// dy_perm[pos[t,j]] = gate[t,j] * dy[t];  dgate[t,j] = <dy[t], y_perm[pos[t,j]]>
+// A group of L lanes (a power of two <= 64) owns one token; the dot product is
+// reduced across the group with xor shuffles in a fixed pattern.
+template <typename TA, int L>
+__global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
+    const uint4* __restrict__ dy, const uint4* __restrict__ yp, const int32_t* __restrict__ pos,
+    const float* __restrict__ gate, uint4* __restrict__ dyp, float* __restrict__ dgate,
+    int64_t T, int32_t vpr, int32_t k) {
+  constexpr int kPer = Act<TA>::kPer16B;
+  const int lane_in = threadIdx.x % L;
+  const int64_t groups_per_block = kThreads / L;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * groups_per_block + threadIdx.x / L;
+  const bool live = t < T;
+  for (int j = 0; j < k; ++j) {
+    const int64_t p = live ? pos[t * k + j] : -1;
+    const float g = live ? gate[t * k + j] : 0.f;
+    float dot = 0.f;
+    if (p >= 0) {
+      for (int c = lane_in; c < vpr; c += L) {
+        float a[kPer], b[kPer];
+        unpack16(dy[t * vpr + c], a, TA{});
+        unpack16(yp[p * vpr + c], b, TA{});
+        float s[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          dot = fmaf(a[i], b[i], dot);
+          s[i] = g * a[i];
+        }
+        dyp[p * vpr + c] = pack16(s, TA{});
+      }
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (live && lane_in == 0) dgate[t * k + j] = (p >= 0) ? dot : 0.f;
+  }
+}
+
+template <typename TA>
+hipError_t combine_bwd_dispatch(int L, dim3 grid, hipStream_t s, const uint4* dy,
+                                const uint4* yp, const int32_t* pos, const float* gate,
+                                uint4* dyp, float* dgate, int64_t T, int32_t vpr, int32_t k) {
+#define MOE_CB(LL)                                                                         \
+  case LL:                                                                                 \
+    hipLaunchKernelGGL((combine_bwd_kernel<TA, LL>), grid, dim3(kThreads), 0, s, dy, yp, pos, \
+                       gate, dyp, dgate, T, vpr, k);                                       \
+    break;
+  switch (L) {
+    MOE_CB(8)
+    MOE_CB(16)
+    MOE_CB(32)
+    default: MOE_CB(64)
+  }
+#undef MOE_CB
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* pos,
+                          const float* gate, void* out, hipStream_t s) {
+  if (dm.T == 0) return hipSuccess;
+  const int elem = (dm.act == MOE_BF16) ? 2 : 4;
+  const int32_t vpr = dm.d * elem / 16;
+  const int64_t total = dm.T * vpr;
+  const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
+  if (dm.act == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(rows), pos, gate, static_cast<uint4*>(out),
+                       dm.T, vpr, dm.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(rows), pos, gate, static_cast<uint4*>(out),
+                       dm.T, vpr, dm.k);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(const moe_dims& dm, const void* dy, const void* y_perm,
+                              const int32_t* pos, const float* gate, void* dy_perm,
+                              float* dgate, hipStream_t s) {
+  if (dm.T == 0) return hipSuccess;
+  const int elem = (dm.act == MOE_BF16) ? 2 : 4;
+  const int32_t vpr = dm.d * elem / 16;
+  int L = 8;
+  while (L < 64 && L < vpr) L <<= 1;
+  const int64_t per_block = kThreads / L;
+  const dim3 grid((dm.T + per_block - 1) / per_block);
+  if (dm.act == MOE_BF16)
+    return combine_bwd_dispatch<bf16_t>(L, grid, s, static_cast<const uint4*>(dy),
+                                        static_cast<const uint4*>(y_perm), pos, gate,
+                                        static_cast<uint4*>(dy_perm), dgate, dm.T, vpr, dm.k);
+  return combine_bwd_dispatch<float>(L, grid, s, static_cast<const uint4*>(dy),
+                                     static_cast<const uint4*>(y_perm), pos, gate,
+                                     static_cast<uint4*>(dy_perm), dgate, dm.T, vpr, dm.k);
+}
+
+}  // namespace moe

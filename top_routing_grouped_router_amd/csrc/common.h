@@ -1,0 +1,133 @@
+// Shared device helpers and launcher declarations of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16 helpers
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// round to nearest, ties to even (finite inputs)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Act;
+template <> struct Act<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float v) { return v; }
+  static __device__ __forceinline__ float from_f32(float v) { return v; }
+  static constexpr int kPer16B = 4;
+};
+template <> struct Act<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ float to_f32(bf16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ bf16_t from_f32(float v) { return f32_to_bf16(v); }
+  static constexpr int kPer16B = 8;
+};
+
+// unpack a 16-byte vector of act values into fp32
+__device__ __forceinline__ void unpack16(const uint4& v, float* out, float) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack16(const uint4& v, float* out, bf16_t) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack16(const float* in, float) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]),
+                    __float_as_uint(in[2]), __float_as_uint(in[3]));
+}
+__device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) |
+           (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// ---------------------------------------------------------------- workspace
+
+inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+// ---------------------------------------------------------------- launchers
+// All launchers enqueue on `stream` and return hipSuccess or the launch error.
+
+// route
+constexpr int kRouteTileMax = 32;   // tokens per route workgroup (upper bound)
+hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
+                        int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
+                        int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
+                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie, hipStream_t s);
+
+// permutation (also used by the dispatch plan with "groups" as keys)
+constexpr int kPermBlock = 256;     // tokens per permutation block
+hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* pos, int32_t* src, const void* x,
+                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s);
+
+// shared by the permutation and the dispatch plan
+__global__ void key_scan_kernel(const int32_t* hist, int32_t nb, int32_t nkeys, int32_t* base,
+                                int32_t* counts, int32_t* offsets);
+
+// grouped GEMMs
+hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, void* a, void* b,
+                             void* h, void* y, hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                             const void* w1, const void* w3, const void* w2, const void* a,
+                             const void* b, const void* h, const void* dy_perm, void* dx_perm,
+                             void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
+                             hipStream_t s);
+
+// combine
+hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* pos,
+                          const float* gate, void* out, hipStream_t s);
+hipError_t launch_combine_bwd(const moe_dims& dm, const void* dy, const void* y_perm,
+                              const int32_t* pos, const float* gate, void* dy_perm,
+                              float* dgate, hipStream_t s);
+
+// router backward
+hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
+                            const int32_t* idx, const float* gate, const float* dgate,
+                            const int32_t* offsets, const int32_t* pos, const int32_t* src,
+                            const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
+                            float* ws_dl_sel, float* ws_partial, hipStream_t s);
+constexpr int kRouteBwdSplits = 8;   // row splits per expert in the router weight gradient
+
+// index products
+hipError_t launch_coselect(int64_t T, int32_t k, int32_t E, const int32_t* idx, int32_t* W,
+                           hipStream_t s);
+
+struct PlacementArg {
+  int32_t group_of[256];
+};
+hipError_t launch_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G,
+                                const int32_t* idx, const PlacementArg& pl, int32_t* n_dest,
+                                int32_t* group_rows, int32_t* group_offsets, int32_t* row_token,
+                                int32_t* assign_row, int32_t* stats, uint64_t* ws_mask,
+                                int32_t* ws_hist, int32_t* ws_base, int32_t* ws_stat,
+                                hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,516 @@
+// Host side of libmoe: argument validation, workspace carving, kernel launch
+// and error reporting behind the C ABI declared in moe.h.
+//
+// Nothing here allocates device memory or synchronises: every entry point
+// validates its arguments, then enqueues kernels on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status ok() {
+  g_last_error[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A required pointer may be NULL only when the tensor it addresses is empty.
+#define MOE_REQUIRE_PTR(p, n)                                                                \
+  do {                                                                                       \
+    if (!(p) && (n) > 0)                                                                     \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is NULL", __func__, #p);               \
+    if (!aligned16(p))                                                                       \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+#define MOE_OPTIONAL_PTR(p)                                                                  \
+  do {                                                                                       \
+    if ((p) && !aligned16(p))                                                                \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is not 16-byte aligned", __func__, #p); \
+  } while (0)
+
+moe_status check_dims(const moe_dims* dm, const char* fn) {
+  if (!dm) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: dims is NULL", fn);
+  if (dm->T < 0 || dm->d <= 0 || dm->E <= 0 || dm->f <= 0 || dm->k <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need T >= 0 and d, E, f, k > 0 (T=%lld d=%d E=%d f=%d k=%d)",
+                fn, static_cast<long long>(dm->T), dm->d, dm->E, dm->f, dm->k);
+  if (dm->E > 256) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d > 256", fn, dm->E);
+  if (dm->k > dm->E || dm->k > 16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: k=%d must be <= min(E, 16)", fn, dm->k);
+  if (dm->d % 64 || dm->f % 64)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: d=%d and f=%d must be multiples of 64", fn, dm->d, dm->f);
+  if (dm->T * static_cast<int64_t>(dm->k) >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k must be < 2^31", fn);
+  if (dm->act != MOE_F32 && dm->act != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: act=%d is neither MOE_F32 nor MOE_BF16", fn, dm->act);
+  return MOE_OK;
+}
+
+size_t elem_size(const moe_dims& dm) { return dm.act == MOE_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- workspace layout
+// Each entry point carves the caller's workspace from offset 0; the required
+// size is the maximum over entry points.
+struct Carver {
+  size_t off = 0;
+  template <typename T>
+  T* take(void* base, size_t count) {
+    T* p = base ? reinterpret_cast<T*>(static_cast<char*>(base) + off) : nullptr;
+    off += moe::align256(count * sizeof(T));
+    return p;
+  }
+};
+
+int route_tile(int64_t T, int32_t G) {
+  if (G <= 1) return moe::kRouteTileMax;
+  const int64_t per = T / G;
+  int tile = moe::kRouteTileMax;
+  while (tile > 1 && per % tile) tile >>= 1;
+  return tile;
+}
+
+struct RouteWs {
+  float* psum;
+  int32_t* pcnt;
+  int32_t* ptie;
+  size_t bytes;
+};
+RouteWs route_ws(const moe_dims& dm, int tile, void* ws) {
+  const int64_t n_tiles = (dm.T + tile - 1) / tile;
+  Carver c;
+  RouteWs r;
+  r.psum = c.take<float>(ws, n_tiles * dm.E);
+  r.pcnt = c.take<int32_t>(ws, n_tiles * dm.E);
+  r.ptie = c.take<int32_t>(ws, std::max<int64_t>(n_tiles, 1));
+  r.bytes = c.off;
+  return r;
+}
+
+struct PermWs {
+  int32_t* hist;
+  int32_t* base;
+  size_t bytes;
+};
+PermWs perm_ws(int64_t T, int32_t keys, void* ws) {
+  const int64_t nb = std::max<int64_t>((T + moe::kPermBlock - 1) / moe::kPermBlock, 1);
+  Carver c;
+  PermWs r;
+  r.hist = c.take<int32_t>(ws, nb * keys);
+  r.base = c.take<int32_t>(ws, nb * keys);
+  r.bytes = c.off;
+  return r;
+}
+
+struct BwdWs {
+  void* da;
+  void* db;
+  size_t bytes;
+};
+BwdWs bwd_ws(const moe_dims& dm, void* ws) {
+  const int64_t R = dm.T * dm.k;
+  Carver c;
+  BwdWs r;
+  r.da = c.take<char>(ws, R * dm.f * elem_size(dm));
+  r.db = c.take<char>(ws, R * dm.f * elem_size(dm));
+  r.bytes = c.off;
+  return r;
+}
+
+struct RouteBwdWs {
+  float* dl_perm;
+  float* dl_sel;
+  float* partial;
+  size_t bytes;
+};
+RouteBwdWs route_bwd_ws(const moe_dims& dm, void* ws) {
+  const int64_t R = dm.T * dm.k;
+  Carver c;
+  RouteBwdWs r;
+  r.dl_perm = c.take<float>(ws, std::max<int64_t>(R, 1));
+  r.dl_sel = c.take<float>(ws, std::max<int64_t>(R, 1));
+  r.partial = c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::kRouteBwdSplits * dm.d);
+  r.bytes = c.off;
+  return r;
+}
+
+struct PlanWs {
+  uint64_t* mask;
+  int32_t* hist;
+  int32_t* base;
+  int32_t* stat;
+  size_t bytes;
+};
+PlanWs plan_ws(int64_t T, int32_t G, void* ws) {
+  const int64_t nb = std::max<int64_t>((T + moe::kPermBlock - 1) / moe::kPermBlock, 1);
+  Carver c;
+  PlanWs r;
+  r.mask = c.take<uint64_t>(ws, std::max<int64_t>(T, 1));
+  r.hist = c.take<int32_t>(ws, nb * G);
+  r.base = c.take<int32_t>(ws, nb * G);
+  r.stat = c.take<int32_t>(ws, nb * 3);
+  r.bytes = c.off;
+  return r;
+}
+
+size_t workspace_needed(const moe_dims& dm, int32_t n_groups) {
+  const int32_t G = std::max(n_groups, 1);
+  size_t need = route_ws(dm, 1, nullptr).bytes;  // tile 1 is the largest layout
+  need = std::max(need, perm_ws(dm.T, dm.E, nullptr).bytes);
+  need = std::max(need, bwd_ws(dm, nullptr).bytes);
+  need = std::max(need, route_bwd_ws(dm, nullptr).bytes);
+  need = std::max(need, plan_ws(dm.T, std::max(G, 64), nullptr).bytes);
+  return need;
+}
+
+moe_status check_ws(void* ws, size_t have, size_t need, const char* fn) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+  if (!aligned16(ws)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: workspace is not 16-byte aligned", fn);
+  if (have < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", fn, have, need);
+  return MOE_OK;
+}
+
+moe_status check_placement_impl(int32_t E, int32_t G, const int32_t* placement, const char* fn) {
+  if (!placement) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: placement is NULL", fn);
+  if (E <= 0 || G <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need E, G > 0", fn);
+  if (E % G) return fail(MOE_ERR_INVALID_PLACEMENT, "%s: G=%d does not divide E=%d", fn, G, E);
+  std::vector<int32_t> per(G, 0);
+  for (int32_t e = 0; e < E; ++e) {
+    const int32_t g = placement[e];
+    if (g < 0 || g >= G)
+      return fail(MOE_ERR_INVALID_PLACEMENT, "%s: expert %d placed in group %d outside [0, %d)",
+                  fn, e, g, G);
+    per[g] += 1;
+  }
+  for (int32_t g = 0; g < G; ++g)
+    if (per[g] != E / G)
+      return fail(MOE_ERR_INVALID_PLACEMENT, "%s: group %d owns %d experts, expected %d", fn, g,
+                  per[g], E / G);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_INVALID_PLACEMENT: return "MOE_ERR_INVALID_PLACEMENT";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups) {
+  if (check_dims(dims, __func__) != MOE_OK) return 0;
+  return workspace_needed(*dims, n_groups);
+}
+
+moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router, float* logits,
+                     int32_t* topk_idx, float* topk_gate, float* margin, float near_tie_eps,
+                     int32_t* near_tie_count, int32_t n_groups, int32_t* group_count,
+                     float* group_mean_prob, float* group_aux, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x, dm.T * dm.d);
+  MOE_REQUIRE_PTR(w_router, int64_t(dm.E) * dm.d);
+  MOE_REQUIRE_PTR(logits, dm.T * dm.E);
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(margin, dm.T);
+  MOE_REQUIRE_PTR(near_tie_count, 1);
+  MOE_OPTIONAL_PTR(group_count);
+  MOE_OPTIONAL_PTR(group_mean_prob);
+  MOE_OPTIONAL_PTR(group_aux);
+  if (n_groups < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d must be >= 1", __func__, n_groups);
+  if (dm.T % n_groups)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d does not divide T=%lld", __func__,
+                n_groups, static_cast<long long>(dm.T));
+  if (!std::isfinite(near_tie_eps))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: near_tie_eps is not finite", __func__);
+  const int tile = route_tile(dm.T, n_groups);
+  const RouteWs need = route_ws(dm, tile, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const RouteWs w = route_ws(dm, tile, workspace);
+  return hip_status(moe::launch_route(dm, x, w_router, logits, topk_idx, topk_gate, margin,
+                                      near_tie_eps, near_tie_count, n_groups, group_count,
+                                      group_mean_prob, group_aux, tile, w.psum, w.pcnt, w.ptie,
+                                      static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* pos, int32_t* src_token, const void* x,
+                       void* x_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(expert_counts, dm.E);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(src_token, dm.T * dm.k);
+  if ((x == nullptr) != (x_perm == nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: pass both x and x_perm, or neither", __func__);
+  MOE_OPTIONAL_PTR(x);
+  MOE_OPTIONAL_PTR(x_perm);
+  const PermWs need = perm_ws(dm.T, dm.E, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const PermWs w = perm_ws(dm.T, dm.E, workspace);
+  return hip_status(moe::launch_permute(dm, topk_idx, expert_counts, expert_offsets, pos,
+                                        src_token, x, x_perm, w.hist, w.base,
+                                        static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_grouped_swiglu_fwd(const moe_dims* dims, const void* x_perm,
+                                  const int32_t* expert_offsets, const void* w1, const void* w3,
+                                  const void* w2, void* a_save, void* b_save, void* h_save,
+                                  void* y_perm, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(y_perm, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_swiglu_fwd(dm, x_perm, expert_offsets, w1, w3, w2, a_save,
+                                           b_save, h_save, y_perm,
+                                           static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_combine(const moe_dims* dims, const void* rows, const int32_t* pos,
+                       const float* gate, void* out, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(rows, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_OPTIONAL_PTR(gate);
+  MOE_REQUIRE_PTR(out, dm.T * dm.d);
+  return hip_status(moe::launch_combine(*dims, rows, pos, gate, out,
+                                        static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_combine_bwd(const moe_dims* dims, const void* dy, const void* y_perm,
+                           const int32_t* pos, const float* gate, void* dy_perm, float* dgate,
+                           void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(dy, dm.T * dm.d);
+  MOE_REQUIRE_PTR(y_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(dgate, dm.T * dm.k);
+  return hip_status(moe::launch_combine_bwd(*dims, dy, y_perm, pos, gate, dy_perm, dgate,
+                                            static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
+                                  const int32_t* expert_offsets, const void* w1, const void* w3,
+                                  const void* w2, const void* a_save, const void* b_save,
+                                  const void* h_save, const void* dy_perm, void* dx_perm,
+                                  void* dw1, void* dw3, void* dw2, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(dx_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
+  const BwdWs need = bwd_ws(dm, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const BwdWs w = bwd_ws(dm, workspace);
+  return hip_status(moe::launch_swiglu_bwd(dm, x_perm, expert_offsets, w1, w3, w2, a_save, b_save,
+                                           h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da, w.db,
+                                           static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_router,
+                         const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                         const int32_t* expert_offsets, const int32_t* pos,
+                         const int32_t* src_token, const void* dx_perm, void* dx,
+                         float* dw_router, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x, dm.T * dm.d);
+  MOE_REQUIRE_PTR(w_router, int64_t(dm.E) * dm.d);
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dgate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(src_token, dm.T * dm.k);
+  MOE_OPTIONAL_PTR(dx_perm);
+  MOE_REQUIRE_PTR(dx, dm.T * dm.d);
+  MOE_REQUIRE_PTR(dw_router, int64_t(dm.E) * dm.d);
+  const RouteBwdWs need = route_bwd_ws(dm, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const RouteBwdWs w = route_bwd_ws(dm, workspace);
+  return hip_status(moe::launch_route_bwd(dm, x, w_router, topk_idx, topk_gate, dgate,
+                                          expert_offsets, pos, src_token, dx_perm, dx, dw_router,
+                                          w.dl_perm, w.dl_sel, w.partial,
+                                          static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_coselect(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx,
+                        int32_t* coselect, void* stream) {
+  if (T < 0 || k <= 0 || E <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need T >= 0 and k, E > 0", __func__);
+  if (E > 256 || k > E || k > 16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: need E <= 256 and k <= min(E, 16)", __func__);
+  if (T * k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k must be < 2^31", __func__);
+  MOE_REQUIRE_PTR(topk_idx, T * k);
+  MOE_REQUIRE_PTR(coselect, int64_t(E) * E);
+  return hip_status(moe::launch_coselect(T, k, E, topk_idx, coselect,
+                                         static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_check_placement(int32_t E, int32_t G, const int32_t* placement) {
+  const moe_status st = check_placement_impl(E, G, placement, __func__);
+  return st == MOE_OK ? ok() : st;
+}
+
+moe_status moe_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G, const int32_t* topk_idx,
+                             const int32_t* placement, int32_t* n_dest, int32_t* group_rows,
+                             int32_t* group_offsets, int32_t* row_token, int32_t* assign_row,
+                             int32_t* stats, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (T < 0 || k <= 0 || E <= 0 || G <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need T >= 0 and k, E, G > 0", __func__);
+  if (E > 256 || k > E || k > 16 || G > 64)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: need E <= 256, k <= min(E, 16), G <= 64", __func__);
+  if (T * k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k must be < 2^31", __func__);
+  if (T % G)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: G=%d does not divide T=%lld", __func__, G,
+                static_cast<long long>(T));
+  moe_status st = check_placement_impl(E, G, placement, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(topk_idx, T * k);
+  MOE_REQUIRE_PTR(n_dest, T);
+  MOE_REQUIRE_PTR(group_rows, G);
+  MOE_REQUIRE_PTR(group_offsets, G + 1);
+  MOE_REQUIRE_PTR(row_token, T * k);
+  MOE_REQUIRE_PTR(assign_row, T * k);
+  MOE_REQUIRE_PTR(stats, 4);
+  const PlanWs need = plan_ws(T, G, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const PlanWs w = plan_ws(T, G, workspace);
+  moe::PlacementArg pl{};
+  for (int32_t e = 0; e < E; ++e) pl.group_of[e] = placement[e];
+  return hip_status(moe::launch_dispatch_plan(T, k, E, G, topk_idx, pl, n_dest, group_rows,
+                                              group_offsets, row_token, assign_row, stats, w.mask,
+                                              w.hist, w.base, w.stat,
+                                              static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_placement_greedy(int32_t E, int32_t G, const int64_t* coselect,
+                                int32_t* placement) {
+  if (!coselect || !placement)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: NULL argument", __func__);
+  if (E <= 0 || G <= 0 || E > 256)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need 0 < E <= 256 and G > 0", __func__);
+  if (E % G) return fail(MOE_ERR_INVALID_PLACEMENT, "%s: G=%d does not divide E=%d", __func__, G, E);
+  const int32_t cap = E / G;
+  std::vector<char> free_(E, 1);
+  std::vector<int64_t> mass(E, 0);   // co-selection count to the still-unassigned experts
+  for (int32_t e = 0; e < E; ++e)
+    for (int32_t o = 0; o < E; ++o)
+      if (o != e) mass[e] += coselect[static_cast<int64_t>(e) * E + o];
+  auto take = [&](int32_t e) {
+    free_[e] = 0;
+    for (int32_t o = 0; o < E; ++o)
+      if (free_[o]) mass[o] -= coselect[static_cast<int64_t>(o) * E + e];
+  };
+  std::vector<int64_t> link(E, 0);   // co-selection count to the current group's members
+  for (int32_t g = 0; g < G; ++g) {
+    int32_t seed = -1;
+    for (int32_t e = 0; e < E; ++e)
+      if (free_[e] && (seed < 0 || mass[e] > mass[seed])) seed = e;
+    std::fill(link.begin(), link.end(), 0);
+    int32_t members = 0;
+    int32_t pick = seed;
+    while (true) {
+      placement[pick] = g;
+      take(pick);
+      ++members;
+      for (int32_t o = 0; o < E; ++o) link[o] += coselect[static_cast<int64_t>(o) * E + pick];
+      if (members == cap) break;
+      pick = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (!free_[e]) continue;
+        if (pick < 0 || link[e] > link[pick] || (link[e] == link[pick] && mass[e] > mass[pick]))
+          pick = e;
+      }
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

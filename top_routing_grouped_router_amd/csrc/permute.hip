@@ -1,0 +1,169 @@
+// Permutation of the T*k (token, slot) assignments into expert-contiguous rows.
+//
+// Method sources: "Expert Coupling in MoE Pretraining" (Abstract and Fig. 5
+// step 3: dispatch of tokens to their experts); "Revisiting MoE and Dense
+// Speed-Accuracy Comparisons" (Sec. 2.2: GShard dispatch, where a token's slot
+// inside an expert is the running count of earlier tokens that chose it).
+//
+// A stable counting sort in three small kernels plus one row mover:
+//   1. hist:    block b (256 tokens) counts its assignments per expert (LDS
+//               integer atomics, exact);
+//   2. scan:    one workgroup turns the [blocks, E] counts into expert counts,
+//               expert offsets and each block's base row per expert;
+//   3. scatter: block b marks, per expert, which of its tokens chose it in an
+//               LDS bitmap (one bit per token); the rank of token t inside
+//               expert e is the popcount of the bits below t, so rows of one
+//               expert come out in ascending token id;
+//   4. gather:  each 16-byte piece of X is read once and written to the k
+//               rows of its token (coalesced row moves).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxKeys = 256;
+constexpr int kWords = kPermBlock / 64;
+
+__global__ __launch_bounds__(kThreads) void perm_hist_kernel(const int32_t* __restrict__ idx,
+                                                             int64_t T, int32_t k, int32_t E,
+                                                             int32_t* __restrict__ hist) {
+  __shared__ int32_t h[kMaxKeys];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + tid;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
+}
+
+}  // namespace
+
+// Shared with the dispatch plan: nb blocks of per-key counts -> key counts,
+// exclusive key offsets (offsets[nkeys] = total) and per-block base rows.
+__global__ __launch_bounds__(256) void key_scan_kernel(const int32_t* __restrict__ hist,
+                                                       int32_t nb, int32_t nkeys,
+                                                       int32_t* __restrict__ base,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ offsets) {
+  __shared__ int32_t excl[kMaxKeys + 1];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < nkeys) {
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i = static_cast<int64_t>(b) * nkeys + e;
+      const int32_t c = hist[i];
+      base[i] = run;
+      run += c;
+    }
+    if (counts) counts[e] = run;
+  }
+  excl[e] = (e < nkeys) ? run : 0;
+  __syncthreads();
+  if (e == 0) {
+    int32_t s = 0;
+    for (int i = 0; i < nkeys; ++i) {
+      const int32_t c = excl[i];
+      excl[i] = s;
+      s += c;
+    }
+    excl[nkeys] = s;
+  }
+  __syncthreads();
+  if (e < nkeys) {
+    offsets[e] = excl[e];
+    for (int b = 0; b < nb; ++b) base[static_cast<int64_t>(b) * nkeys + e] += excl[e];
+  }
+  if (e == 0) offsets[nkeys] = excl[nkeys];
+}
+
+namespace {
+
+__global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
+    const int32_t* __restrict__ base, int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+  __shared__ unsigned long long bits[kMaxKeys][kWords];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kThreads) bits[i / kWords][i % kWords] = 0ull;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + tid;
+  const int w = tid >> 6, lane = tid & 63;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicOr(&bits[e][w], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      if (e < 0 || e >= E) {
+        pos[t * k + j] = -1;
+        continue;
+      }
+      int32_t rank = __popcll(bits[e][w] & below);
+      for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+      const int32_t p = base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+      pos[t * k + j] = p;
+      src[p] = static_cast<int32_t>(t);
+    }
+  }
+}
+
+// x_perm[pos[t, j]] = x[t], moved as 16-byte pieces
+__global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                               const int32_t* __restrict__ pos,
+                                                               uint4* __restrict__ xp,
+                                                               int64_t T, int32_t vec_per_row,
+                                                               int32_t k) {
+  const int64_t total = T * vec_per_row;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total;
+       v += stride) {
+    const int64_t t = v / vec_per_row;
+    const int32_t c = static_cast<int32_t>(v - t * vec_per_row);
+    const uint4 val = x[v];
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = pos[t * k + j];
+      if (p >= 0) xp[p * vec_per_row + c] = val;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* counts,
+                          int32_t* offsets, int32_t* pos, int32_t* src, const void* x,
+                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s) {
+  const int64_t nb = (dm.T + kPermBlock - 1) / kPermBlock;
+  if (nb > 0) {
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
+                       ws_hist);
+  }
+  hipLaunchKernelGGL(key_scan_kernel, dim3(1), dim3(256), 0, s, ws_hist,
+                     static_cast<int32_t>(nb), dm.E, ws_base, counts, offsets);
+  if (nb > 0) {
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k,
+                       dm.E, ws_base, pos, src);
+  }
+  if (x && x_perm && dm.T > 0) {
+    const int elem = (dm.act == MOE_BF16) ? 2 : 4;
+    const int32_t vpr = dm.d * elem / 16;
+    const int64_t total = dm.T * vpr;
+    const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(x), pos, static_cast<uint4*>(x_perm), dm.T,
+                       vpr, dm.k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

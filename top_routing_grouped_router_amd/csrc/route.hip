@@ -1,0 +1,280 @@
+// Router: logits, wavefront top-k, renormalised gates, margins, near-ties and
+// per-block load-balancing partial sums.
+//
+// Method sources: "Expert Coupling in MoE Pretraining" (Abstract: each token
+// is routed to k of E experts); "Revisiting MoE and Dense Speed-Accuracy
+// Comparisons" (Sec. 2.1 Top-K routing and the GShard balancing loss, Sec. 3.6
+// the second expert is the second best, Sec. 2.2 outer batches); "MoE
+// Pretraining: Parallelism Layout Changes the Model" (Finding 3: the margin
+// between the k-th and (k+1)-th scores; balancing statistics per machine).
+//
+// One workgroup owns `tile` consecutive tokens (tile divides T/G, so a tile
+// never straddles two balancing blocks).  Phase 1 computes the tile's logits
+// with fp32 FMAs from LDS-staged chunks of X and Wr.  Phase 2 gives each token
+// to one wavefront: the E logits sit in registers (lane e holds experts e,
+// e+64, ...) and k+1 rounds of a wave-wide (value, lowest id) arg-max pick the
+// experts in order and the runner-up for the margin.  Per-tile partial sums of
+// the full softmax and the per-expert counts go to the workspace; a second
+// kernel reduces them per block in a fixed order (no floating-point atomics).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kDChunk = 32;
+constexpr int kMaxE = 256;
+constexpr int kOutPerThread = kRouteTileMax * kMaxE / kThreads;  // 32
+
+struct RouteArgs {
+  const void* x;
+  const float* wr;
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  float* margin;
+  float* psum;      // [tiles, E]
+  int32_t* pcnt;    // [tiles, E]
+  int32_t* ptie;    // [tiles]
+  int64_t T;
+  int32_t d, E, k, tile;
+  float eps;
+};
+
+struct Key {
+  float v;
+  int32_t i;
+};
+
+// (v, i) beats (w, j) when v > w, or v == w and i < j
+__device__ __forceinline__ bool better(float v, int32_t i, float w, int32_t j) {
+  return v > w || (v == w && i < j);
+}
+
+__device__ __forceinline__ Key wave_argmax(Key k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float v = __shfl_xor(k.v, off, 64);
+    int32_t i = __shfl_xor(k.i, off, 64);
+    if (better(v, i, k.v, k.i)) { k.v = v; k.i = i; }
+  }
+  return k;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <typename TX>
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
+  __shared__ float xs[kRouteTileMax][kDChunk + 1];
+  __shared__ float wsh[kMaxE][kDChunk + 1];
+  __shared__ float ls[kRouteTileMax][kMaxE + 1];
+  __shared__ float psum_w[4][kMaxE];
+  __shared__ int32_t pcnt_w[4][kMaxE];
+  __shared__ int32_t tie_w[4];
+
+  const int tid = threadIdx.x;
+  const int E = a.E, d = a.d, k = a.k, tile = a.tile;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * tile;
+  const int ntok = static_cast<int>(min<int64_t>(tile, a.T - t0));
+  const int nout = ntok * E;
+  const TX* x = static_cast<const TX*>(a.x);
+
+  // ---------------- phase 1: logits of the tile
+  float acc[kOutPerThread];
+#pragma unroll
+  for (int i = 0; i < kOutPerThread; ++i) acc[i] = 0.f;
+
+  for (int c0 = 0; c0 < d; c0 += kDChunk) {
+    for (int v = tid; v < tile * kDChunk; v += kThreads) {
+      const int t = v / kDChunk, c = v % kDChunk;
+      xs[t][c] = (t < ntok) ? Act<TX>::load(x + (t0 + t) * d + c0 + c) : 0.f;
+    }
+    for (int v = tid; v < E * kDChunk; v += kThreads) {
+      const int e = v / kDChunk, c = v % kDChunk;
+      wsh[e][c] = a.wr[static_cast<int64_t>(e) * d + c0 + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kOutPerThread; ++i) {
+      const int o = tid + i * kThreads;
+      if (o < nout) {
+        const int t = o / E, e = o % E;
+        float s = acc[i];
+#pragma unroll 8
+        for (int c = 0; c < kDChunk; ++c) s = fmaf(xs[t][c], wsh[e][c], s);
+        acc[i] = s;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < kOutPerThread; ++i) {
+    const int o = tid + i * kThreads;
+    if (o < nout) {
+      const int t = o / E, e = o % E;
+      ls[t][e] = acc[i];
+      a.logits[(t0 + t) * E + e] = acc[i];
+    }
+  }
+  __syncthreads();
+
+  // ---------------- phase 2: one wavefront per token
+  const int wave = tid >> 6, lane = tid & 63;
+  float my_psum[kMaxE / 64];
+  int32_t my_cnt[kMaxE / 64];
+#pragma unroll
+  for (int s = 0; s < kMaxE / 64; ++s) { my_psum[s] = 0.f; my_cnt[s] = 0; }
+  int32_t ties = 0;
+
+  for (int t = wave; t < ntok; t += 4) {
+    float v[kMaxE / 64];
+    uint32_t taken = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxE / 64; ++s) {
+      const int e = lane + 64 * s;
+      v[s] = (e < E) ? ls[t][e] : -INFINITY;
+    }
+    // round r's winner is known to every lane; lane r keeps it
+    float my_v = -INFINITY, v_top = -INFINITY, v_km1 = 0.f, v_k = 0.f;
+    int32_t my_i = 0;
+    const int rounds = (k < E) ? k + 1 : k;
+    for (int r = 0; r < rounds; ++r) {
+      Key best{-INFINITY, 0x7fffffff};
+#pragma unroll
+      for (int s = 0; s < kMaxE / 64; ++s) {
+        const int e = lane + 64 * s;
+        if (e < E && !(taken & (1u << s)) && better(v[s], e, best.v, best.i)) {
+          best.v = v[s];
+          best.i = e;
+        }
+      }
+      best = wave_argmax(best);
+      if (r == 0) v_top = best.v;
+      if (r == k - 1) v_km1 = best.v;
+      if (r == k) v_k = best.v;
+      if (lane == r) { my_v = best.v; my_i = best.i; }
+      // the (k+1)-th round only reads the runner-up: it is not chosen
+      if (r < k && (best.i & 63) == lane) taken |= 1u << (best.i >> 6);
+    }
+    // full softmax for the balancing statistics
+    float ex[kMaxE / 64];
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxE / 64; ++s) {
+      const int e = lane + 64 * s;
+      ex[s] = (e < E) ? __expf(v[s] - v_top) : 0.f;
+      part += ex[s];
+    }
+    const float inv = 1.0f / wave_sum(part);
+#pragma unroll
+    for (int s = 0; s < kMaxE / 64; ++s) {
+      my_psum[s] += ex[s] * inv;
+      if (taken & (1u << s)) my_cnt[s] += 1;
+    }
+    // gates: softmax over the k chosen logits (lane j holds choice j)
+    const float my_e = (lane < k) ? __expf(my_v - v_top) : 0.f;
+    const float z = wave_sum(my_e);
+    const int64_t tg = t0 + t;
+    if (lane < k) {
+      a.idx[tg * k + lane] = my_i;
+      a.gate[tg * k + lane] = my_e / z;
+    }
+    const float m = (k < E) ? v_km1 - v_k : INFINITY;
+    if (lane == 0) {
+      a.margin[tg] = m;
+      ties += (m < a.eps) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kMaxE / 64; ++s) {
+    const int e = lane + 64 * s;
+    if (e < E) {
+      psum_w[wave][e] = my_psum[s];
+      pcnt_w[wave][e] = my_cnt[s];
+    }
+  }
+  if (lane == 0) tie_w[wave] = ties;
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    float s = psum_w[0][e];
+    int32_t c = pcnt_w[0][e];
+    for (int w = 1; w < 4; ++w) {
+      s += psum_w[w][e];
+      c += pcnt_w[w][e];
+    }
+    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
+    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+  }
+  if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+}
+
+// One workgroup per balancing block r (grid G).  Thread e sums the tiles of
+// block r in tile order.  Block 0 also totals the near-tie counts.
+__global__ __launch_bounds__(kThreads) void route_finalize_kernel(
+    const float* psum, const int32_t* pcnt, const int32_t* ptie, int32_t n_tiles,
+    int32_t tiles_per_group, int64_t T, int32_t E, int32_t k, int32_t* gcount, float* gprob,
+    float* gaux, int32_t* tie_count) {
+  __shared__ float fp[kMaxE];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t G = gridDim.x;
+  const double per_group = static_cast<double>(T) / static_cast<double>(G);
+  for (int e = tid; e < kMaxE; e += kThreads) fp[e] = 0.f;
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    float s = 0.f;
+    int32_t c = 0;
+    for (int i = 0; i < tiles_per_group; ++i) {
+      const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
+      s += psum[tile * E + e];
+      c += pcnt[tile * E + e];
+    }
+    const float P = (per_group > 0) ? static_cast<float>(s / per_group) : 0.f;
+    const float fr = (per_group > 0) ? static_cast<float>(c / (per_group * k)) : 0.f;
+    if (gcount) gcount[static_cast<int64_t>(r) * E + e] = c;
+    if (gprob) gprob[static_cast<int64_t>(r) * E + e] = P;
+    fp[e] = fr * P;
+  }
+  __syncthreads();
+  // fixed-order tree over the (zero-padded) 256 products
+  for (int w = kMaxE / 2; w >= 1; w >>= 1) {
+    if (tid < w) fp[tid] += fp[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0 && gaux) gaux[r] = static_cast<float>(E) * fp[0];
+  if (r == 0 && tid == 0 && tie_count) {
+    int32_t s = 0;
+    for (int i = 0; i < n_tiles; ++i) s += ptie[i];
+    *tie_count = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
+                        int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
+                        int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
+                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie, hipStream_t s) {
+  const int64_t n_tiles = (dm.T + tile - 1) / tile;
+  if (n_tiles > 0) {
+    RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie,
+                dm.T, dm.d, dm.E, dm.k, tile, eps};
+    if (dm.act == MOE_BF16)
+      hipLaunchKernelGGL(route_kernel<bf16_t>, dim3(n_tiles), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(route_kernel<float>, dim3(n_tiles), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int32_t tiles_per_group = static_cast<int32_t>(n_tiles / G);
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(G), dim3(kThreads), 0, s, ws_psum, ws_pcnt,
+                     ws_ptie, static_cast<int32_t>(n_tiles), tiles_per_group, dm.T, dm.E, dm.k,
+                     gcount, gprob, gaux, tie_count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,102 @@
+"""One MoE layer's forward and backward as a sequence of C-ABI calls.
+
+Buffers for every intermediate are allocated once (torch device memory) and
+reused by each call, so a step enqueues kernels only.  The sequence is:
+
+  forward:  moe_route -> moe_permute -> moe_grouped_swiglu_fwd -> moe_combine
+  backward: moe_combine_bwd -> moe_grouped_swiglu_bwd -> moe_route_bwd
+
+(moe_route_bwd also unpermutes and sums the expert input gradients).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, T: int, d: int, E: int, f: int, k: int, act: torch.dtype,
+                 n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda"):
+        self.dims = L.make_dims(T, d, E, f, k, act)
+        self.act = act
+        self.n_groups = n_groups
+        self.eps = near_tie_eps
+        R = T * k
+        dev = torch.device(device)
+        e32 = dict(dtype=torch.float32, device=dev)
+        i32 = dict(dtype=torch.int32, device=dev)
+        ea = dict(dtype=act, device=dev)
+
+        def empty(*shape, **kw):
+            # never a NULL pointer, even for an empty batch (T = 0)
+            t = torch.empty(max(shape[0], 1), *shape[1:], **kw)
+            return t[:shape[0]]
+
+        self.logits = empty(T, E, **e32)
+        self.topk_idx = empty(T, k, **i32)
+        self.topk_gate = empty(T, k, **e32)
+        self.margin = empty(T, **e32)
+        self.near_tie_count = empty(1, **i32)
+        self.group_count = empty(n_groups, E, **i32)
+        self.group_mean_prob = empty(n_groups, E, **e32)
+        self.group_aux = empty(n_groups, **e32)
+        self.expert_counts = empty(E, **i32)
+        self.expert_offsets = empty(E + 1, **i32)
+        self.pos = empty(T, k, **i32)
+        self.src_token = empty(R, **i32)
+        self.x_perm = empty(R, d, **ea)
+        self.a = empty(R, f, **ea)
+        self.b = empty(R, f, **ea)
+        self.h = empty(R, f, **ea)
+        self.y_perm = empty(R, d, **ea)
+        self.y = empty(T, d, **ea)
+        self.dy_perm = empty(R, d, **ea)
+        self.dgate = empty(T, k, **e32)
+        self.dx_perm = empty(R, d, **ea)
+        self.dw1 = empty(E, f, d, **ea)
+        self.dw3 = empty(E, f, d, **ea)
+        self.dw2 = empty(E, d, f, **ea)
+        self.dx = empty(T, d, **ea)
+        self.dwr = empty(E, d, **e32)
+        self.workspace = L.alloc_workspace(self.dims, n_groups, dev)
+
+    # ------------------------------------------------------------------ forward
+    def route(self, x, wr):
+        L.moe_route(self.dims, x, wr, self.logits, self.topk_idx, self.topk_gate, self.margin,
+                    self.eps, self.near_tie_count, self.n_groups, self.group_count,
+                    self.group_mean_prob, self.group_aux, self.workspace)
+
+    def forward_experts(self, x, w1, w3, w2):
+        L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
+                      self.pos, self.src_token, x, self.x_perm, self.workspace)
+        L.moe_grouped_swiglu_fwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
+                                 self.a, self.b, self.h, self.y_perm)
+        L.moe_combine(self.dims, self.y_perm, self.pos, self.topk_gate, self.y)
+
+    def forward(self, x, wr, w1, w3, w2, routing=None):
+        """routing: optional (topk_idx, topk_gate) device tensors that replace the
+        router's decision after it has run (used to compare the downstream
+        steps on a routing fixed from outside)."""
+        self.route(x, wr)
+        if routing is not None:
+            self.topk_idx.copy_(routing[0])
+            self.topk_gate.copy_(routing[1])
+        self.forward_experts(x, w1, w3, w2)
+        return self.y
+
+    # ------------------------------------------------------------------ backward
+    def backward(self, dy, x, wr, w1, w3, w2):
+        L.moe_combine_bwd(self.dims, dy, self.y_perm, self.pos, self.topk_gate, self.dy_perm,
+                          self.dgate)
+        L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
+                                 self.a, self.b, self.h, self.dy_perm, self.dx_perm, self.dw1,
+                                 self.dw3, self.dw2, self.workspace)
+        L.moe_route_bwd(self.dims, x, wr, self.topk_idx, self.topk_gate, self.dgate,
+                        self.expert_offsets, self.pos, self.src_token, self.dx_perm, self.dx,
+                        self.dwr, self.workspace)
+        return self.dx
+
+    def step(self, x, wr, w1, w3, w2, dy):
+        self.forward(x, wr, w1, w3, w2)
+        self.backward(dy, x, wr, w1, w3, w2)
