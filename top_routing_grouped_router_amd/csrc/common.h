@@ -99,7 +99,19 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
-                             hipStream_t s);
+                             float* ws_partial, hipStream_t s);
+
+// bf16 matrix-core implementations (gemm_bf16.hip)
+hipError_t launch_swiglu_fwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, void* a,
+                                  void* b, void* h, void* y, hipStream_t s);
+hipError_t launch_swiglu_bwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, const void* a,
+                                  const void* b, const void* h, const void* dy_perm,
+                                  void* dx_perm, void* dw1, void* dw3, void* dw2, void* ws_da,
+                                  void* ws_db, float* ws_partial, hipStream_t s);
+int wgrad_splits_bf16(const moe_dims& dm);           // split-K count of the weight gradients
+size_t wgrad_partial_bytes_bf16(const moe_dims& dm); // fp32 partial tiles it needs
 
 // combine
 hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* pos,
@@ -114,7 +126,7 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const int32_t* offsets, const int32_t* pos, const int32_t* src,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
                             float* ws_dl_sel, float* ws_partial, hipStream_t s);
-constexpr int kRouteBwdSplits = 8;   // row splits per expert in the router weight gradient
+int route_bwd_splits(const moe_dims& dm);   // row splits per expert for the router weight gradient
 
 // index products
 hipError_t launch_coselect(int64_t T, int32_t k, int32_t E, const int32_t* idx, int32_t* W,

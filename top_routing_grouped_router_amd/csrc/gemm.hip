@@ -498,7 +498,8 @@ hipError_t bwd_impl(const moe_dims& dm, const void* x_perm, const int32_t* offse
 hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, void* a, void* b,
                              void* h, void* y, hipStream_t s) {
-  if (dm.act == MOE_BF16) return fwd_impl<bf16_t>(dm, x_perm, offsets, w1, w3, w2, a, b, h, y, s);
+  if (dm.act == MOE_BF16)
+    return launch_swiglu_fwd_bf16(dm, x_perm, offsets, w1, w3, w2, a, b, h, y, s);
   return fwd_impl<float>(dm, x_perm, offsets, w1, w3, w2, a, b, h, y, s);
 }
 
@@ -506,10 +507,10 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
-                             hipStream_t s) {
+                             float* ws_partial, hipStream_t s) {
   if (dm.act == MOE_BF16)
-    return bwd_impl<bf16_t>(dm, x_perm, offsets, w1, w3, w2, a, b, h, dy_perm, dx_perm, dw1,
-                            dw3, dw2, ws_da, ws_db, s);
+    return launch_swiglu_bwd_bf16(dm, x_perm, offsets, w1, w3, w2, a, b, h, dy_perm, dx_perm,
+                                  dw1, dw3, dw2, ws_da, ws_db, ws_partial, s);
   return bwd_impl<float>(dm, x_perm, offsets, w1, w3, w2, a, b, h, dy_perm, dx_perm, dw1, dw3,
                          dw2, ws_da, ws_db, s);
 }

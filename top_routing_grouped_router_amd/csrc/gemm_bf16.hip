@@ -1,0 +1,685 @@
+// Grouped GEMMs of the SwiGLU experts in bf16 on CDNA4 matrix cores.
+//
+// Method sources: "Revisiting MoE and Dense Speed-Accuracy Comparisons for LLM
+// Training" (Sec. 2.1: SwiGLU activation in a LLaMA2-style block); "Expert
+// Coupling in MoE Pretraining" (Fig. 5 step 4: the expert computation, run in
+// the forward and backward passes); "MoE Pretraining: Parallelism Layout
+// Changes the Model" (Methodology: SwiGLU experts).
+//
+// Every product is C[m][n] = sum_k A(m,k) B(n,k) over one expert's rows, in
+// one of five modes (see grouped GEMM modes in gemm.hip):
+//   UP          [a | b] = x_perm [W1 | W3]^T; epilogue h = silu(a) b
+//   DOWN        y_perm = h W2^T
+//   DGRAD_DOWN  dh = dy_perm W2; epilogue da = dh b silu'(a), db = dh silu(a)
+//   DGRAD_UP    dx_perm = da W1 + db W3   (one K loop over 2f)
+//   WGRAD       dW2 = dy^T h, dW1 = da^T x, dW3 = db^T x   (K = the expert's rows)
+//
+// Kernel structure (256 threads = 4 wavefronts, 128 x 128 output tile, K step 64):
+//  * LDS holds both operand tiles k-contiguous, 16-byte chunks XOR-swizzled by
+//    row (see swz), double-buffered: global loads of step k+1 are in flight
+//    while step k runs on the matrix cores.
+//  * Operands stored m- or n-contiguous in HBM (W in dgrad, both operands of
+//    wgrad) are loaded as 4 x 8 blocks (four 16-byte rows per thread) and
+//    transposed in registers before the LDS store, so the matrix-core loop is
+//    the same in every mode.
+//  * v_mfma_f32_16x16x32_bf16 with the B fragment as the first source: each
+//    lane then owns 4 consecutive output columns of one row, which the
+//    epilogue writes to LDS as 8-byte pieces and stores to HBM in coalesced
+//    16-byte chunks (with the mode's elementwise work applied on the way).
+//  * Row tiles come from the expert offsets on the device; the flat tile
+//    index is remapped so that each XCD (workgroups are dealt round-robin to
+//    the 8 XCDs) works through a contiguous run of tiles, n fastest, which
+//    keeps a row tile's A panel and the expert's B panel in that XCD's L2.
+// Each output element is produced by one workgroup in a fixed k order, so
+// results are bitwise reproducible.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BM = 128;
+constexpr int BN = 128;
+constexpr int BK = 64;
+constexpr int kTile = 128 * BK;       // bf16 elements per operand tile
+constexpr int kOutLd = BN + 8;        // epilogue LDS row stride (elements)
+constexpr int kXcd = 8;
+
+enum Mode { UP = 0, DOWN = 1, DGRAD_DOWN = 2, DGRAD_UP = 3, WGRAD = 4 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Args {
+  const bf16_t* a0;
+  const bf16_t* a1;
+  const bf16_t* b0;
+  const bf16_t* b1;
+  const bf16_t* aux0;
+  const bf16_t* aux1;
+  bf16_t* c0;
+  bf16_t* c1;
+  bf16_t* c2;
+  const int32_t* offsets;
+  int32_t E, d, f;
+  int32_t n_tiles_n;     // row modes: tiles along n
+  int32_t grid_pad;      // flat grid size (multiple of 8)
+};
+
+// LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r.  The
+// chunk is XORed with S(r) = (r & 7) ^ (bit 3 of r moved to bit 2): 8
+// consecutive rows read at one logical chunk hit 8 different chunk slots, and
+// the transposed stores below (two rows 8 apart per group of 16 lanes) do too.
+__device__ __forceinline__ int swz(int r, int chunk) {
+  return r * BK + ((chunk ^ (r & 7) ^ ((r >> 1) & 4)) << 3);
+}
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+// ------------------------------------------------------------------ staging
+// k-contiguous operand: 128 rows x 64 k = 1024 chunks, 4 per thread.
+struct KPart {
+  uint4 v[4];
+};
+
+template <typename RowPtr>
+__device__ __forceinline__ void kload(KPart& p, RowPtr row_ptr, int valid, int k0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = threadIdx.x + kThreads * i;
+    const int r = v >> 3, c = v & 7;
+    p.v[i] = (r < valid) ? *reinterpret_cast<const uint4*>(row_ptr(r) + k0 + c * 8) : zero4();
+  }
+}
+
+__device__ __forceinline__ void kstore(const KPart& p, bf16_t* lds) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = threadIdx.x + kThreads * i;
+    const int r = v >> 3, c = v & 7;
+    *reinterpret_cast<uint4*>(lds + swz(r, c)) = p.v[i];
+  }
+}
+
+// m/n-contiguous operand: element (k, j) at base[k * ld + j]; the 64 k x 128 j
+// tile is cut into 16 x 16 blocks of 4 k x 8 j, one block per thread.  Within
+// a wavefront, lane bits 0-2 pick the k quad and bits 3-5 the j block, so a
+// load instruction reads 128 contiguous bytes of each of 8 k rows, and each
+// group of 16 lanes stores to 16 distinct bank slots after the transpose.
+struct MPart {
+  uint4 v[4];
+};
+
+__device__ __forceinline__ void mblock(int* jb, int* kq) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  *kq = (wave & 1) * 8 + (lane & 7);
+  *jb = (wave >> 1) * 8 + (lane >> 3);
+}
+
+__device__ __forceinline__ void mload(MPart& p, const bf16_t* base, int64_t ld, int kvalid,
+                                      int jvalid) {
+  int jb, kq;
+  mblock(&jb, &kq);
+  const int j = jb * 8;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int k = kq * 4 + r;
+    p.v[r] = (k < kvalid && j < jvalid) ? *reinterpret_cast<const uint4*>(base + k * ld + j)
+                                        : zero4();
+  }
+}
+
+// transpose the 4 x 8 block in registers: LDS row j receives its 4 k values
+// as one 8-byte piece (half of the swizzled 16-byte chunk kq / 2)
+__device__ __forceinline__ void mstore(const MPart& p, bf16_t* lds) {
+  int jb, kq;
+  mblock(&jb, &kq);
+  const uint32_t in[4][4] = {{p.v[0].x, p.v[0].y, p.v[0].z, p.v[0].w},
+                             {p.v[1].x, p.v[1].y, p.v[1].z, p.v[1].w},
+                             {p.v[2].x, p.v[2].y, p.v[2].z, p.v[2].w},
+                             {p.v[3].x, p.v[3].y, p.v[3].z, p.v[3].w}};
+#pragma unroll
+  for (int c2 = 0; c2 < 4; ++c2) {
+    const uint32_t A0 = in[0][c2], A1 = in[1][c2], A2 = in[2][c2], A3 = in[3][c2];
+    const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
+    const uint2 odd = make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
+    const int row = jb * 8 + 2 * c2;
+    *reinterpret_cast<uint2*>(lds + swz(row, kq >> 1) + 4 * (kq & 1)) = even;
+    *reinterpret_cast<uint2*>(lds + swz(row + 1, kq >> 1) + 4 * (kq & 1)) = odd;
+  }
+}
+
+// ------------------------------------------------------------------ matrix-core step
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[4][4], const bf16_t* As, const bf16_t* Bs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < BK / 8; kk += 4) {
+    const int chunk = kk + g;
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 64 + i * 16 + r, chunk));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * 64 + j * 16 + r, chunk));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// accumulators -> LDS tile [128][kOutLd] of bf16 (rounded once)
+__device__ __forceinline__ void stage_out(const f32x4 (&acc)[4][4], bf16_t* out) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = wm * 64 + i * 16 + (lane & 15);
+      const int n = wn * 64 + j * 16 + (lane >> 4) * 4;
+      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[i][j][0])) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
+      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[i][j][2])) |
+                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
+      *reinterpret_cast<uint2*>(out + m * kOutLd + n) = make_uint2(lo, hi);
+    }
+}
+
+// ------------------------------------------------------------------ tile lookup
+__device__ __forceinline__ int flat_tile() {
+  const int per = gridDim.x / kXcd;            // grid_pad is a multiple of 8
+  return (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
+}
+
+// expert and first row of row tile `tile` (prefix sum of per-expert tile
+// counts across wave 0, 4 experts per lane); false when there is no such tile
+__device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_out, int* m0_out,
+                              int* mend_out) {
+  __shared__ int s_e, s_m0, s_mend;
+  if (threadIdx.x == 0) s_e = -1;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int tiles[4], sum = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = lane * 4 + s;
+      const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+      tiles[s] = (cnt + BM - 1) / BM;
+      sum += tiles[s];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - sum;
+    if (tile >= excl && tile < incl) {
+      int rem = tile - excl;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (rem >= 0 && rem < tiles[s]) {
+          const int e = lane * 4 + s;
+          s_e = e;
+          s_m0 = offsets[e] + rem * BM;
+          s_mend = offsets[e + 1];
+        }
+        rem -= tiles[s];
+      }
+    }
+  }
+  __syncthreads();
+  *e_out = s_e;
+  *m0_out = s_m0;
+  *mend_out = s_mend;
+  return s_e >= 0;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ------------------------------------------------------------------ kernels
+// Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP).
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * kTile];
+  bf16_t* As0 = lds;
+  bf16_t* Bs0 = lds + kTile;
+  bf16_t* As1 = lds + 2 * kTile;
+  bf16_t* Bs1 = lds + 3 * kTile;
+
+  const int flat = flat_tile();
+  const int row_tile = flat / g.n_tiles_n;
+  const int nt = flat - row_tile * g.n_tiles_n;
+  int e, m0, mend;
+  if (!find_row_tile(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  const int rows = min(BM, mend - m0);
+  const int d = g.d, f = g.f;
+  // UP covers 64 f columns of a and the same 64 of b per tile
+  const int n0 = nt * ((MODE == UP) ? 64 : BN);
+  const int Ndim = (MODE == DOWN || MODE == DGRAD_UP) ? d : f;
+  const int nvalid = (MODE == UP) ? BN : min(BN, Ndim - n0);
+  const int K = (MODE == UP || MODE == DGRAD_DOWN) ? d : (MODE == DOWN ? f : 2 * f);
+  const int nk = K / BK;
+
+  const int64_t E_fd = static_cast<int64_t>(f) * d;
+  // A rows (k-contiguous)
+  const bf16_t* A0 = g.a0;
+  const int lda = (MODE == UP || MODE == DGRAD_DOWN) ? d : f;
+  auto a_row = [&](int half) {
+    const bf16_t* base = (MODE == DGRAD_UP && half) ? g.a1 : A0;
+    return base + static_cast<int64_t>(m0) * lda;
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  KPart pa;
+  KPart pb;   // k-contiguous B (UP, DOWN)
+  MPart pm;   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
+
+  auto load = [&](int kt) {
+    int k0 = kt * BK;
+    int half = 0;
+    if (MODE == DGRAD_UP && k0 >= f) {
+      half = 1;
+      k0 -= f;
+    }
+    const bf16_t* ab = a_row(half);
+    kload(pa, [&](int r) { return ab + static_cast<int64_t>(r) * lda; }, rows, k0);
+    if constexpr (MODE == UP) {
+      const bf16_t* w1 = g.b0 + e * E_fd;
+      const bf16_t* w3 = g.b1 + e * E_fd;
+      kload(pb, [&](int r) {
+        return (r < 64 ? w1 + static_cast<int64_t>(n0 + r) * d
+                       : w3 + static_cast<int64_t>(n0 + r - 64) * d);
+      }, BN, k0);
+    } else if constexpr (MODE == DOWN) {
+      const bf16_t* w2 = g.b0 + e * E_fd;
+      kload(pb, [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; }, nvalid, k0);
+    } else if constexpr (MODE == DGRAD_DOWN) {
+      // W2[e] is [d][f]: element (k, n) at k * f + n
+      mload(pm, g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0, f, BK, nvalid);
+    } else {
+      // W1/W3[e] are [f][d]: element (k, n) at k * d + n
+      const bf16_t* w = (half ? g.b1 : g.b0) + e * E_fd;
+      mload(pm, w + static_cast<int64_t>(k0) * d + n0, d, BK, nvalid);
+    }
+  };
+  auto store = [&](bf16_t* As, bf16_t* Bs) {
+    kstore(pa, As);
+    if constexpr (MODE == UP || MODE == DOWN) {
+      kstore(pb, Bs);
+    } else {
+      mstore(pm, Bs);
+    }
+  };
+
+  load(0);
+  store(As0, Bs0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    if (more) load(kt + 1);
+    if (kt & 1)
+      mma_step(acc, As1, Bs1);
+    else
+      mma_step(acc, As0, Bs0);
+    if (more) {
+      if (kt & 1)
+        store(As0, Bs0);
+      else
+        store(As1, Bs1);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: tile through LDS, then coalesced 16-byte chunks
+  bf16_t* out = lds;
+  stage_out(acc, out);
+  __syncthreads();
+  if constexpr (MODE == UP) {
+    // LDS columns [0, 64) hold a, [64, 128) hold b for f columns n0 + c
+    for (int v = threadIdx.x; v < BM * 8; v += kThreads) {
+      const int r = v >> 3, c = (v & 7) * 8;
+      if (r >= rows) continue;
+      const uint4 av = *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+      const uint4 bv = *reinterpret_cast<const uint4*>(out + r * kOutLd + 64 + c);
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t hw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a_lo = bf_lo(aw[q]), a_hi = bf_hi(aw[q]);
+        hw[q] = bf_pack(silu_f(a_lo) * bf_lo(bw[q]), silu_f(a_hi) * bf_hi(bw[q]));
+      }
+      const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c;
+      *reinterpret_cast<uint4*>(g.c0 + o) = av;
+      *reinterpret_cast<uint4*>(g.c1 + o) = bv;
+      *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+  } else if constexpr (MODE == DGRAD_DOWN) {
+    // dh (rounded) in LDS; da = dh b silu'(a), db = dh silu(a)
+    for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
+      const int r = v >> 4, c = (v & 15) * 8;
+      if (r >= rows || c >= nvalid) continue;
+      const uint4 hv = *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+      const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c;
+      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
+      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t daw[4], dbw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float da2[2], db2[2];
+        const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
+        const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+        const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float s = sigmoid_f(aa[u]);
+          da2[u] = hh[u] * bb[u] * (s * (1.0f + aa[u] * (1.0f - s)));
+          db2[u] = hh[u] * (aa[u] * s);
+        }
+        daw[q] = bf_pack(da2[0], da2[1]);
+        dbw[q] = bf_pack(db2[0], db2[1]);
+      }
+      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+    }
+  } else {
+    // DOWN -> y_perm [R][d]; DGRAD_UP -> dx_perm [R][d]
+    for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
+      const int r = v >> 4, c = (v & 15) * 8;
+      if (r >= rows || c >= nvalid) continue;
+      *reinterpret_cast<uint4*>(g.c0 + static_cast<int64_t>(m0 + r) * d + n0 + c) =
+          *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+    }
+  }
+}
+
+// Weight gradients: tile (e, m, n) of dW_z[e] = sum over the expert's rows p of
+// A[p][m] B[p][n]; z = 0: dW2 (A = dy, B = h), 1: dW1 (A = da, B = x),
+// 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
+// `splits` contiguous runs; each workgroup writes its fp32 partial tile and
+// wgrad_reduce_kernel adds the runs in order (deterministic split-K).
+__global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(Args g, int32_t tiles_per_expert,
+                                                            int32_t splits, float* partial) {
+  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * kTile];
+  bf16_t* As0 = lds;
+  bf16_t* Bs0 = lds + kTile;
+  bf16_t* As1 = lds + 2 * kTile;
+  bf16_t* Bs1 = lds + 3 * kTile;
+
+  const int flat = flat_tile();
+  const int per_z = g.E * tiles_per_expert * splits;
+  const int z = flat / per_z;
+  if (z >= 3) return;
+  int rem = flat - z * per_z;
+  const int e = rem / (tiles_per_expert * splits);
+  rem -= e * tiles_per_expert * splits;
+  const int t = rem / splits;
+  const int sp = rem - t * splits;
+  const int d = g.d, f = g.f;
+  const int Mdim = (z == 0) ? d : f;
+  const int Ndim = (z == 0) ? f : d;
+  const int tiles_n = (Ndim + BN - 1) / BN;
+  const int m0 = (t / tiles_n) * BM;
+  const int n0 = (t % tiles_n) * BN;
+  if (m0 >= Mdim) return;
+  const bf16_t* Asrc = (z == 0) ? g.a0 : (z == 1 ? g.a1 : g.aux0);
+  const bf16_t* Bsrc = (z == 0) ? g.b0 : g.b1;
+  const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
+  const int nk_all = (p1 - p0 + BK - 1) / BK;
+  const int per_split = (nk_all + splits - 1) / splits;
+  const int kt0 = min(nk_all, sp * per_split);
+  const int kt1 = min(nk_all, kt0 + per_split);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  MPart pa, pb;
+  auto load = [&](int kt) {
+    const int p = p0 + kt * BK;
+    const int kvalid = min(BK, p1 - p);
+    mload(pa, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kvalid, Mdim - m0);
+    mload(pb, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kvalid, Ndim - n0);
+  };
+  auto store = [&](bf16_t* As, bf16_t* Bs) {
+    mstore(pa, As);
+    mstore(pb, Bs);
+  };
+
+  if (kt0 < kt1) {
+    load(kt0);
+    store(As0, Bs0);
+  }
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const bool more = kt + 1 < kt1;
+    const bool odd = (kt - kt0) & 1;
+    if (more) load(kt + 1);
+    if (odd)
+      mma_step(acc, As1, Bs1);
+    else
+      mma_step(acc, As0, Bs0);
+    if (more) {
+      if (odd)
+        store(As0, Bs0);
+      else
+        store(As1, Bs1);
+    }
+    __syncthreads();
+  }
+  const int nvalid = min(BN, Ndim - n0), mvalid = min(BM, Mdim - m0);
+  if (splits > 1) {
+    // fp32 partial tile [128][128], n contiguous; each lane owns 4 consecutive n
+    float* dst = partial + ((static_cast<int64_t>(z) * g.E + e) * tiles_per_expert + t) *
+                               static_cast<int64_t>(splits) * (BM * BN) +
+                 static_cast<int64_t>(sp) * (BM * BN);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = wm * 64 + i * 16 + (lane & 15);
+        const int n = wn * 64 + j * 16 + (lane >> 4) * 4;
+        *reinterpret_cast<float4*>(dst + m * BN + n) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      }
+    return;
+  }
+  bf16_t* out = lds;
+  stage_out(acc, out);
+  __syncthreads();
+  bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
+  for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
+    const int r = v >> 4, c = (v & 15) * 8;
+    if (r >= mvalid || c >= nvalid) continue;
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c) =
+        *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+  }
+}
+
+// Adds the split-K partial tiles in split order and rounds once to bf16.
+// One thread per 8 consecutive outputs of a tile row.
+__global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t tiles_per_expert,
+                                                                int32_t splits,
+                                                                const float* partial) {
+  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t per_tile = BM * BN / 8;
+  const int64_t tile_id = chunk / per_tile;
+  if (tile_id >= 3LL * g.E * tiles_per_expert) return;
+  const int within = static_cast<int>(chunk - tile_id * per_tile);
+  const int r = within / (BN / 8), c = (within % (BN / 8)) * 8;
+  const int z = static_cast<int>(tile_id / (static_cast<int64_t>(g.E) * tiles_per_expert));
+  const int rem = static_cast<int>(tile_id - static_cast<int64_t>(z) * g.E * tiles_per_expert);
+  const int e = rem / tiles_per_expert, t = rem % tiles_per_expert;
+  const int d = g.d, f = g.f;
+  const int Mdim = (z == 0) ? d : f;
+  const int Ndim = (z == 0) ? f : d;
+  const int tiles_n = (Ndim + BN - 1) / BN;
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  if (m0 + r >= Mdim || n0 + c >= Ndim) return;
+  const float* src = partial + tile_id * splits * static_cast<int64_t>(BM * BN) + r * BN + c;
+  float v[8];
+  {
+    const float4 a = *reinterpret_cast<const float4*>(src);
+    const float4 b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  for (int s = 1; s < splits; ++s) {
+    const float* q = src + static_cast<int64_t>(s) * (BM * BN);
+    const float4 a = *reinterpret_cast<const float4*>(q);
+    const float4 b = *reinterpret_cast<const float4*>(q + 4);
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
+  bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f +
+                static_cast<int64_t>(m0 + r) * Ndim + n0 + c;
+  *reinterpret_cast<uint4*>(dst) =
+      make_uint4(bf_pack(v[0], v[1]), bf_pack(v[2], v[3]), bf_pack(v[4], v[5]), bf_pack(v[6], v[7]));
+}
+
+int wgrad_tiles_per_expert(const moe_dims& dm) {
+  const int tiles = ((dm.d + BM - 1) / BM) * ((dm.f + BN - 1) / BN);
+  const int tiles_t = ((dm.f + BM - 1) / BM) * ((dm.d + BN - 1) / BN);
+  return std::max(tiles, tiles_t);
+}
+
+unsigned pad8(int64_t n) { return static_cast<unsigned>((n + kXcd - 1) / kXcd * kXcd); }
+
+template <int MODE>
+hipError_t launch_rows(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
+  Args g = base;
+  g.n_tiles_n = n_tiles_n;
+  const int64_t row_tiles = (R + BM - 1) / BM + E;   // upper bound of sum_e ceil(M_e / BM)
+  const unsigned grid = pad8(row_tiles * n_tiles_n);
+  g.grid_pad = static_cast<int32_t>(grid);
+  hipLaunchKernelGGL(rows_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_fwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, void* a,
+                                  void* b, void* h, void* y, hipStream_t s) {
+  const int64_t R = dm.T * dm.k;
+  if (R == 0) return hipSuccess;
+  Args g{};
+  g.offsets = offsets;
+  g.E = dm.E;
+  g.d = dm.d;
+  g.f = dm.f;
+  g.a0 = static_cast<const bf16_t*>(x_perm);
+  g.b0 = static_cast<const bf16_t*>(w1);
+  g.b1 = static_cast<const bf16_t*>(w3);
+  g.c0 = static_cast<bf16_t*>(a);
+  g.c1 = static_cast<bf16_t*>(b);
+  g.c2 = static_cast<bf16_t*>(h);
+  hipError_t err = launch_rows<UP>(g, R, dm.E, dm.f / 64, s);
+  if (err != hipSuccess) return err;
+  Args g2{};
+  g2.offsets = offsets;
+  g2.E = dm.E;
+  g2.d = dm.d;
+  g2.f = dm.f;
+  g2.a0 = static_cast<const bf16_t*>(h);
+  g2.b0 = static_cast<const bf16_t*>(w2);
+  g2.c0 = static_cast<bf16_t*>(y);
+  return launch_rows<DOWN>(g2, R, dm.E, (dm.d + BN - 1) / BN, s);
+}
+
+hipError_t launch_swiglu_bwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                                  const void* w1, const void* w3, const void* w2, const void* a,
+                                  const void* b, const void* h, const void* dy_perm,
+                                  void* dx_perm, void* dw1, void* dw3, void* dw2, void* ws_da,
+                                  void* ws_db, float* ws_partial, hipStream_t s) {
+  const int64_t R = dm.T * dm.k;
+  hipError_t err;
+  if (R > 0) {
+    Args g{};
+    g.offsets = offsets;
+    g.E = dm.E;
+    g.d = dm.d;
+    g.f = dm.f;
+    g.a0 = static_cast<const bf16_t*>(dy_perm);
+    g.b0 = static_cast<const bf16_t*>(w2);
+    g.aux0 = static_cast<const bf16_t*>(a);
+    g.aux1 = static_cast<const bf16_t*>(b);
+    g.c0 = static_cast<bf16_t*>(ws_da);
+    g.c1 = static_cast<bf16_t*>(ws_db);
+    err = launch_rows<DGRAD_DOWN>(g, R, dm.E, (dm.f + BN - 1) / BN, s);
+    if (err != hipSuccess) return err;
+    Args g2{};
+    g2.offsets = offsets;
+    g2.E = dm.E;
+    g2.d = dm.d;
+    g2.f = dm.f;
+    g2.a0 = static_cast<const bf16_t*>(ws_da);
+    g2.a1 = static_cast<const bf16_t*>(ws_db);
+    g2.b0 = static_cast<const bf16_t*>(w1);
+    g2.b1 = static_cast<const bf16_t*>(w3);
+    g2.c0 = static_cast<bf16_t*>(dx_perm);
+    err = launch_rows<DGRAD_UP>(g2, R, dm.E, (dm.d + BN - 1) / BN, s);
+    if (err != hipSuccess) return err;
+  }
+  Args g3{};
+  g3.offsets = offsets;
+  g3.E = dm.E;
+  g3.d = dm.d;
+  g3.f = dm.f;
+  g3.a0 = static_cast<const bf16_t*>(dy_perm);   // z = 0: A = dy (m over d), B = h (n over f)
+  g3.b0 = static_cast<const bf16_t*>(h);
+  g3.a1 = static_cast<const bf16_t*>(ws_da);     // z = 1: A = da (m over f), B = x (n over d)
+  g3.aux0 = static_cast<const bf16_t*>(ws_db);   // z = 2: A = db (m over f), B = x (n over d)
+  g3.b1 = static_cast<const bf16_t*>(x_perm);
+  g3.c0 = static_cast<bf16_t*>(dw2);
+  g3.c1 = static_cast<bf16_t*>(dw1);
+  g3.c2 = static_cast<bf16_t*>(dw3);
+  const int tpe = wgrad_tiles_per_expert(dm);
+  const int splits = wgrad_splits_bf16(dm);
+  const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe * splits);
+  g3.grid_pad = static_cast<int32_t>(grid);
+  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kThreads), 0, s, g3, tpe, splits, ws_partial);
+  if (splits > 1) {
+    const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (BM * BN / 8);
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((chunks + kThreads - 1) / kThreads),
+                       dim3(kThreads), 0, s, g3, tpe, splits, ws_partial);
+  }
+  return hipGetLastError();
+}
+
+// Split-K count for the weight gradients: enough workgroups to fill the chip
+// (about 4 per CU) when E x tiles alone would not, at most 8.
+int wgrad_splits_bf16(const moe_dims& dm) {
+  const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert(dm);
+  const int64_t want = 1024;
+  int s = static_cast<int>((want + base - 1) / base);
+  return std::max(1, std::min(s, 8));
+}
+
+size_t wgrad_partial_bytes_bf16(const moe_dims& dm) {
+  const int s = wgrad_splits_bf16(dm);
+  if (s <= 1) return 0;
+  return static_cast<size_t>(3) * dm.E * wgrad_tiles_per_expert(dm) * s * (BM * BN) * sizeof(float);
+}
+
+}  // namespace moe

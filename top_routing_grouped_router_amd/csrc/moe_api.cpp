@@ -126,6 +126,7 @@ PermWs perm_ws(int64_t T, int32_t keys, void* ws) {
 struct BwdWs {
   void* da;
   void* db;
+  float* partial;
   size_t bytes;
 };
 BwdWs bwd_ws(const moe_dims& dm, void* ws) {
@@ -134,6 +135,8 @@ BwdWs bwd_ws(const moe_dims& dm, void* ws) {
   BwdWs r;
   r.da = c.take<char>(ws, R * dm.f * elem_size(dm));
   r.db = c.take<char>(ws, R * dm.f * elem_size(dm));
+  const size_t pbytes = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
+  r.partial = c.take<float>(ws, pbytes / sizeof(float));
   r.bytes = c.off;
   return r;
 }
@@ -150,7 +153,7 @@ RouteBwdWs route_bwd_ws(const moe_dims& dm, void* ws) {
   RouteBwdWs r;
   r.dl_perm = c.take<float>(ws, std::max<int64_t>(R, 1));
   r.dl_sel = c.take<float>(ws, std::max<int64_t>(R, 1));
-  r.partial = c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::kRouteBwdSplits * dm.d);
+  r.partial = c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::route_bwd_splits(dm) * dm.d);
   r.bytes = c.off;
   return r;
 }
@@ -381,7 +384,7 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
   const BwdWs w = bwd_ws(dm, workspace);
   return hip_status(moe::launch_swiglu_bwd(dm, x_perm, expert_offsets, w1, w3, w2, a_save, b_save,
                                            h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da, w.db,
-                                           static_cast<hipStream_t>(stream)),
+                                           w.partial, static_cast<hipStream_t>(stream)),
                     __func__);
 }
 

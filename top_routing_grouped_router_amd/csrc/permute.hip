@@ -47,24 +47,28 @@ __global__ __launch_bounds__(kThreads) void perm_hist_kernel(const int32_t* __re
 
 // Shared with the dispatch plan: nb blocks of per-key counts -> key counts,
 // exclusive key offsets (offsets[nkeys] = total) and per-block base rows.
+// Thread e walks its key's column in chunks of 16 independent loads.
 __global__ __launch_bounds__(256) void key_scan_kernel(const int32_t* __restrict__ hist,
                                                        int32_t nb, int32_t nkeys,
                                                        int32_t* __restrict__ base,
                                                        int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ offsets) {
+  constexpr int kChunk = 16;
   __shared__ int32_t excl[kMaxKeys + 1];
   const int e = threadIdx.x;
-  int32_t run = 0;
+  int32_t total = 0;
   if (e < nkeys) {
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * nkeys + e;
-      const int32_t c = hist[i];
-      base[i] = run;
-      run += c;
+    for (int b0 = 0; b0 < nb; b0 += kChunk) {
+      int32_t v[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        v[i] = (b0 + i < nb) ? hist[static_cast<int64_t>(b0 + i) * nkeys + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) total += v[i];
     }
-    if (counts) counts[e] = run;
+    if (counts) counts[e] = total;
   }
-  excl[e] = (e < nkeys) ? run : 0;
+  excl[e] = (e < nkeys) ? total : 0;
   __syncthreads();
   if (e == 0) {
     int32_t s = 0;
@@ -78,7 +82,18 @@ __global__ __launch_bounds__(256) void key_scan_kernel(const int32_t* __restrict
   __syncthreads();
   if (e < nkeys) {
     offsets[e] = excl[e];
-    for (int b = 0; b < nb; ++b) base[static_cast<int64_t>(b) * nkeys + e] += excl[e];
+    int32_t run = excl[e];
+    for (int b0 = 0; b0 < nb; b0 += kChunk) {
+      int32_t v[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        v[i] = (b0 + i < nb) ? hist[static_cast<int64_t>(b0 + i) * nkeys + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (b0 + i < nb) base[static_cast<int64_t>(b0 + i) * nkeys + e] = run;
+        run += v[i];
+      }
+    }
   }
   if (e == 0) offsets[nkeys] = excl[nkeys];
 }

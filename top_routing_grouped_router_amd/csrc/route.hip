@@ -212,44 +212,70 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
 }
 
-// One workgroup per balancing block r (grid G).  Thread e sums the tiles of
-// block r in tile order.  Block 0 also totals the near-tie counts.
+// One workgroup per balancing block r (grid G).  Per pass, 16 experts x 16
+// tile slices: thread (slice, e) sums tiles slice, slice + 16, ... of block r,
+// then the 16 slice sums are added in slice order.  Block 0 also totals the
+// near-tie counts (strided per thread, then a fixed tree).
 __global__ __launch_bounds__(kThreads) void route_finalize_kernel(
     const float* psum, const int32_t* pcnt, const int32_t* ptie, int32_t n_tiles,
     int32_t tiles_per_group, int64_t T, int32_t E, int32_t k, int32_t* gcount, float* gprob,
     float* gaux, int32_t* tie_count) {
+  __shared__ float sp[16][17];
+  __shared__ int32_t sc[16][17];
   __shared__ float fp[kMaxE];
+  __shared__ int32_t st[kThreads];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int slice = tid >> 4, el = tid & 15;
   const int64_t G = gridDim.x;
   const double per_group = static_cast<double>(T) / static_cast<double>(G);
   for (int e = tid; e < kMaxE; e += kThreads) fp[e] = 0.f;
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
+  for (int e0 = 0; e0 < E; e0 += 16) {
+    const int e = e0 + el;
     float s = 0.f;
     int32_t c = 0;
-    for (int i = 0; i < tiles_per_group; ++i) {
-      const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
-      s += psum[tile * E + e];
-      c += pcnt[tile * E + e];
+    if (e < E) {
+      for (int i = slice; i < tiles_per_group; i += 16) {
+        const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
+        s += psum[tile * E + e];
+        c += pcnt[tile * E + e];
+      }
     }
-    const float P = (per_group > 0) ? static_cast<float>(s / per_group) : 0.f;
-    const float fr = (per_group > 0) ? static_cast<float>(c / (per_group * k)) : 0.f;
-    if (gcount) gcount[static_cast<int64_t>(r) * E + e] = c;
-    if (gprob) gprob[static_cast<int64_t>(r) * E + e] = P;
-    fp[e] = fr * P;
+    sp[slice][el] = s;
+    sc[slice][el] = c;
+    __syncthreads();
+    if (tid < 16 && e0 + tid < E) {
+      float S = 0.f;
+      int32_t C = 0;
+      for (int q = 0; q < 16; ++q) {
+        S += sp[q][tid];
+        C += sc[q][tid];
+      }
+      const int ee = e0 + tid;
+      const float P = (per_group > 0) ? static_cast<float>(S / per_group) : 0.f;
+      const float fr = (per_group > 0) ? static_cast<float>(C / (per_group * k)) : 0.f;
+      if (gcount) gcount[static_cast<int64_t>(r) * E + ee] = C;
+      if (gprob) gprob[static_cast<int64_t>(r) * E + ee] = P;
+      fp[ee] = fr * P;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   // fixed-order tree over the (zero-padded) 256 products
   for (int w = kMaxE / 2; w >= 1; w >>= 1) {
     if (tid < w) fp[tid] += fp[tid + w];
     __syncthreads();
   }
   if (tid == 0 && gaux) gaux[r] = static_cast<float>(E) * fp[0];
-  if (r == 0 && tid == 0 && tie_count) {
+  if (r == 0 && tie_count) {
     int32_t s = 0;
-    for (int i = 0; i < n_tiles; ++i) s += ptie[i];
-    *tie_count = s;
+    for (int i = tid; i < n_tiles; i += kThreads) s += ptie[i];
+    st[tid] = s;
+    __syncthreads();
+    for (int w = kThreads / 2; w >= 1; w >>= 1) {
+      if (tid < w) st[tid] += st[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) *tie_count = st[0];
   }
 }
 

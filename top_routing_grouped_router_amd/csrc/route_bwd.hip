@@ -75,11 +75,10 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
 }
 
 // dWr[e] = sum over rows p of expert e (ascending token order) of
-// dl_perm[p] * x[src[p]].  The expert's rows are cut into kSplits contiguous
+// dl_perm[p] * x[src[p]].  The expert's rows are cut into `splits` contiguous
 // parts; workgroup (col block, split, e) sums its part (wave w takes rows
-// w, w+4, ...; the four waves are combined in order), and a second kernel adds
-// the parts in split order.  Each lane owns 4 consecutive columns.
-constexpr int kSplits = kRouteBwdSplits;
+// w, w+4, ..., four rows in flight; the four waves are combined in order), and
+// a second kernel adds the parts in split order.  Each lane owns 4 columns.
 
 __device__ __forceinline__ void load4(const float* p, float* v) {
   const float4 q = *reinterpret_cast<const float4*>(p);
@@ -95,17 +94,30 @@ template <typename TA>
 __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
     const TA* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ src, const float* __restrict__ dl_perm,
-    float* __restrict__ partial, int32_t d) {
+    float* __restrict__ partial, int32_t d, int32_t splits) {
   __shared__ float red[4][256];
   const int e = blockIdx.z, sp = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col0 = blockIdx.x * 256 + lane * 4;
   const int32_t p0 = offsets[e], n = offsets[e + 1] - p0;
-  const int32_t lo = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * sp) / kSplits);
-  const int32_t hi = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * (sp + 1)) / kSplits);
+  const int32_t lo = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * sp) / splits);
+  const int32_t hi = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * (sp + 1)) / splits);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (col0 < d) {
-    for (int32_t p = lo + wave; p < hi; p += 4) {
+    int32_t p = lo + wave;
+    for (; p + 12 < hi; p += 16) {
+      float g[4], v[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        g[u] = dl_perm[p + 4 * u];
+        load4(x + static_cast<int64_t>(src[p + 4 * u]) * d + col0, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
+    }
+    for (; p < hi; p += 4) {
       const float g = dl_perm[p];
       float v[4];
       load4(x + static_cast<int64_t>(src[p]) * d + col0, v);
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
   for (int i = 0; i < 4; ++i) red[wave][lane * 4 + i] = acc[i];
   __syncthreads();
   if (wave == 0 && col0 < d) {
-    float* out = partial + (static_cast<int64_t>(e) * kSplits + sp) * d + col0;
+    float* out = partial + (static_cast<int64_t>(e) * splits + sp) * d + col0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       out[i] = ((red[0][lane * 4 + i] + red[1][lane * 4 + i]) + red[2][lane * 4 + i]) +
@@ -126,17 +138,25 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void router_dwr_reduce_kernel(
-    const float* __restrict__ partial, float* __restrict__ dwr, int32_t E, int32_t d) {
+    const float* __restrict__ partial, float* __restrict__ dwr, int32_t E, int32_t d,
+    int32_t splits) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= static_cast<int64_t>(E) * d) return;
   const int64_t e = i / d, col = i - e * d;
-  const float* p = partial + e * kSplits * d + col;
+  const float* p = partial + e * splits * d + col;
   float s = p[0];
-  for (int k = 1; k < kSplits; ++k) s += p[static_cast<int64_t>(k) * d];
+  for (int k = 1; k < splits; ++k) s += p[static_cast<int64_t>(k) * d];
   dwr[i] = s;
 }
 
 }  // namespace
+
+// row splits per expert for the router weight gradient: about 2048 workgroups
+int route_bwd_splits(const moe_dims& dm) {
+  const int64_t base = static_cast<int64_t>(dm.E) * ((dm.d + 255) / 256);
+  const int64_t s = (2048 + base - 1) / base;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+}
 
 hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const int32_t* idx, const float* gate, const float* dgate,
@@ -159,16 +179,19 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                          static_cast<const uint4*>(dx_perm), pos, idx, ws_dl_sel, wr,
                          static_cast<uint4*>(dx), dm.T, vpr, dm.d, dm.k, dm.E);
   }
-  const dim3 grid((dm.d + 255) / 256, kSplits, dm.E);
+  const int splits = route_bwd_splits(dm);
+  const dim3 grid((dm.d + 255) / 256, splits, dm.E);
   if (dm.act == MOE_BF16)
     hipLaunchKernelGGL(router_dwr_partial_kernel<bf16_t>, grid, dim3(kThreads), 0, s,
-                       static_cast<const bf16_t*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d);
+                       static_cast<const bf16_t*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d,
+                       splits);
   else
     hipLaunchKernelGGL(router_dwr_partial_kernel<float>, grid, dim3(kThreads), 0, s,
-                       static_cast<const float*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d);
+                       static_cast<const float*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d,
+                       splits);
   const int64_t n = static_cast<int64_t>(dm.E) * dm.d;
   hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((n + kThreads - 1) / kThreads),
-                     dim3(kThreads), 0, s, ws_partial, dwr, dm.E, dm.d);
+                     dim3(kThreads), 0, s, ws_partial, dwr, dm.E, dm.d, splits);
   return hipGetLastError();
 }
 
