@@ -3,9 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
 
 One step is one full pass of the layer's hot path over one batch of synthetic
-tokens: moe_route -> moe_permute -> moe_grouped_swiglu_fwd -> moe_combine ->
-moe_combine_bwd -> moe_grouped_swiglu_bwd -> moe_route_bwd.  Inputs and weights
-are resident in HBM before timing starts.  Prints one JSON line.
+tokens: moe_route -> moe_permute -> moe_expert_up -> moe_expert_down ->
+moe_combine -> moe_combine_bwd -> moe_expert_dgrad_down -> moe_expert_dgrad_up
+-> moe_expert_wgrad -> moe_route_bwd (the kernel-level phases of
+moe_grouped_swiglu_fwd/bwd, so each GEMM kernel can be timed on its own).
+Inputs and weights are resident in HBM before timing starts.  Prints one JSON
+line.
 
 Per-call durations are taken live with HIP events on the stream the library
 launches on; the dominant call's algorithmic bytes (or flops) per launch over
@@ -31,25 +34,45 @@ PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix peaks (fp32: vect
 
 
 def algorithmic_work(cfg):
-    """Per-call algorithmic (flops, bytes): what each call must compute and move
-    (inputs read once, outputs written once, as its C-ABI contract states)."""
+    """Per-call algorithmic (flops, bytes, kernels): what each call must compute
+    and move by its C-ABI contract (inputs read once, outputs written once)."""
     T, d, E, f, k = cfg.T, cfg.d, cfg.E, cfg.f, cfg.k
     R = T * k
     s = 2 if cfg.act == "bf16" else 4
     i4 = 4
-    W = 3 * E * d * f * s
+    Wf = E * d * f * s          # one of W1, W3, W2
     return {
         "moe_route": (2 * T * d * E,
-                      T * d * s + E * d * 4 + T * E * 4 + T * k * (i4 + 4) + T * 4),
-        "moe_permute": (0, T * k * i4 + T * d * s + R * d * s + 2 * R * i4 + (2 * E + 1) * i4),
-        "moe_grouped_swiglu_fwd": (6 * R * d * f, R * d * s + W + 3 * R * f * s + R * d * s),
-        "moe_combine": (2 * R * d, R * d * s + T * d * s + T * k * (i4 + 4)),
-        "moe_combine_bwd": (2 * R * d, T * d * s + 2 * R * d * s + T * k * (i4 + 8)),
-        "moe_grouped_swiglu_bwd": (12 * R * d * f,
-                                   2 * R * d * s + 3 * R * f * s + W + R * d * s + W),
+                      T * d * s + E * d * 4 + T * E * 4 + T * k * (i4 + 4) + T * 4, 2),
+        "moe_permute": (0, T * k * i4 + T * d * s + R * d * s + 2 * R * i4 + (2 * E + 1) * i4, 4),
+        "moe_expert_up": (4 * R * d * f, R * d * s + 2 * Wf + 3 * R * f * s, 1),
+        "moe_expert_down": (2 * R * d * f, R * f * s + Wf + R * d * s, 1),
+        "moe_combine": (2 * R * d, R * d * s + T * d * s + T * k * (i4 + 4), 1),
+        "moe_combine_bwd": (2 * R * d, T * d * s + 2 * R * d * s + T * k * (i4 + 8), 1),
+        "moe_expert_dgrad_down": (2 * R * d * f, R * d * s + Wf + 4 * R * f * s, 1),
+        "moe_expert_dgrad_up": (4 * R * d * f, 2 * R * f * s + 2 * Wf + R * d * s, 1),
+        "moe_expert_wgrad": (6 * R * d * f, 2 * R * d * s + 3 * R * f * s + 3 * Wf, None),
         "moe_route_bwd": (4 * R * d, T * d * s + E * d * 4 + R * d * s + T * d * s + E * d * 4
-                          + T * k * 12 + R * 8),
+                          + T * k * 12 + R * 8, 4),
     }
+
+
+GEMM_CALLS = ("moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
+              "moe_expert_dgrad_up", "moe_expert_wgrad")
+
+
+def wgrad_kernels(dm):
+    """moe_expert_wgrad is one kernel unless it splits K (then it adds a reduce)."""
+    return 1 if wgrad_split_k(dm) <= 1 else 2
+
+
+def wgrad_split_k(dm):
+    # mirrors the library's split rule: ceil(1024 / (3 E tiles)), 1..8, bf16 only
+    if dm.act != 1:
+        return 1
+    tiles = ((dm.d + 127) // 128) * ((dm.f + 127) // 128)
+    base = 3 * dm.E * tiles
+    return max(1, min((1024 + base - 1) // base, 8))
 
 
 def roofline_entry(flops, nbytes, seconds, act):
@@ -64,26 +87,42 @@ def roofline_entry(flops, nbytes, seconds, act):
 
 
 def cpu_baseline(cfg, inp, budget_s=20.0):
-    """The oracle as it stands (fp64 numpy), on the same workload, timed on the
-    host cores.  Runs whole steps of the full workload until budget_s is spent
-    (at least one)."""
+    """The oracle as it stands (fp64 numpy), timed on the host cores on the same
+    workload.  Whole steps of the full batch when one step takes under ~budget/2
+    seconds; otherwise the first `n` tokens of the batch (same weights), n sized
+    from a short probe.  Repeats until budget_s is spent (at least once)."""
     import threadpoolctl
     from oracle import moe_oracle as O
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+
+    def step(n):
+        sl = slice(0, n)
+        fwd = O.layer_forward(inp["x"][sl], inp["wr"], inp["w1"], inp["w3"], inp["w2"], cfg.k)
+        if cfg.backward:
+            O.layer_backward(inp["x"][sl], inp["wr"], inp["w1"], inp["w3"], inp["w2"], fwd,
+                             inp["dy"][sl])
+
+    n = cfg.T
+    probe = min(cfg.T, 512)
+    t0 = time.perf_counter()
+    step(probe)
+    per_token = (time.perf_counter() - t0) / probe
+    if per_token * cfg.T > budget_s / 2:
+        n = max(probe, int(budget_s / 3 / per_token) // 256 * 256)
+        n = min(n, cfg.T)
     t0 = time.perf_counter()
     steps = 0
     while True:
-        fwd = O.layer_forward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], cfg.k)
-        if cfg.backward:
-            O.layer_backward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], fwd, inp["dy"])
+        step(n)
         steps += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or el * (steps + 1) / steps > 3 * budget_s:
+        if el >= budget_s or el * (steps + 1) / steps > 1.5 * budget_s:
             break
-    return {"value": round(cfg.T * steps / el, 1), "unit": "tokens/s", "cores": threads,
+    what = "full batch" if n == cfg.T else f"first {n} of {cfg.T} tokens"
+    return {"value": round(n * steps / el, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{steps} full step(s) of {cfg.name} ({cfg.T} tokens, fwd"
+            "sample": f"{steps} step(s) of {cfg.name} over the {what} (fwd"
                       f"{'+bwd' if cfg.backward else ''}), fp64 numpy, {el:.1f} s"}
 
 
@@ -122,29 +161,36 @@ def main():
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G)
     dm = layer.dims
 
+    da = torch.empty_like(layer.a)
+    db = torch.empty_like(layer.b)
     calls = [
         ("moe_route", lambda: layer.route(x, wr)),
         ("moe_permute", lambda: L.moe_permute(dm, layer.topk_idx, layer.expert_counts,
                                               layer.expert_offsets, layer.pos, layer.src_token,
                                               x, layer.x_perm, layer.workspace)),
-        ("moe_grouped_swiglu_fwd", lambda: L.moe_grouped_swiglu_fwd(
-            dm, layer.x_perm, layer.expert_offsets, w1, w3, w2, layer.a, layer.b, layer.h,
-            layer.y_perm)),
+        ("moe_expert_up", lambda: L.moe_expert_up(dm, layer.x_perm, layer.expert_offsets, w1, w3,
+                                                  layer.a, layer.b, layer.h)),
+        ("moe_expert_down", lambda: L.moe_expert_down(dm, layer.h, layer.expert_offsets, w2,
+                                                      layer.y_perm)),
         ("moe_combine", lambda: L.moe_combine(dm, layer.y_perm, layer.pos, layer.topk_gate,
                                               layer.y)),
         ("moe_combine_bwd", lambda: L.moe_combine_bwd(dm, dy, layer.y_perm, layer.pos,
                                                       layer.topk_gate, layer.dy_perm,
                                                       layer.dgate)),
-        ("moe_grouped_swiglu_bwd", lambda: L.moe_grouped_swiglu_bwd(
-            dm, layer.x_perm, layer.expert_offsets, w1, w3, w2, layer.a, layer.b, layer.h,
-            layer.dy_perm, layer.dx_perm, layer.dw1, layer.dw3, layer.dw2, layer.workspace)),
+        ("moe_expert_dgrad_down", lambda: L.moe_expert_dgrad_down(
+            dm, layer.dy_perm, layer.expert_offsets, w2, layer.a, layer.b, da, db)),
+        ("moe_expert_dgrad_up", lambda: L.moe_expert_dgrad_up(
+            dm, da, db, layer.expert_offsets, w1, w3, layer.dx_perm)),
+        ("moe_expert_wgrad", lambda: L.moe_expert_wgrad(
+            dm, layer.x_perm, layer.expert_offsets, layer.h, layer.dy_perm, da, db, layer.dw1,
+            layer.dw3, layer.dw2, layer.workspace)),
         ("moe_route_bwd", lambda: L.moe_route_bwd(dm, x, wr, layer.topk_idx, layer.topk_gate,
                                                   layer.dgate, layer.expert_offsets, layer.pos,
                                                   layer.src_token, layer.dx_perm, layer.dx,
                                                   layer.dwr, layer.workspace)),
     ]
     if not cfg.backward:
-        calls = calls[:4]
+        calls = calls[:5]
 
     for _ in range(args.warmup):
         for _, fn in calls:
@@ -173,13 +219,15 @@ def main():
                 for i, (name, _) in enumerate(calls)}
 
     work = algorithmic_work(cfg)
-    dominant = max(per_call, key=per_call.get)
-    fl, by = work[dominant]
+    # the dominant single-kernel call carries the roofline
+    single = {n: t for n, t in per_call.items() if work[n][2] == 1 or
+              (n == "moe_expert_wgrad" and wgrad_kernels(dm) == 1)}
+    dominant = max(single, key=single.get)
+    fl, by, _ = work[dominant]
     roof = roofline_entry(fl, by, per_call[dominant] * 1e-3, cfg.act)
     roof.update({"kernel": dominant, "traffic": None})
-    gemm_ms = per_call["moe_grouped_swiglu_fwd"] + per_call.get("moe_grouped_swiglu_bwd", 0.0)
-    gemm_flops = work["moe_grouped_swiglu_fwd"][0] + (
-        work["moe_grouped_swiglu_bwd"][0] if cfg.backward else 0)
+    gemm_ms = sum(per_call[n] for n in GEMM_CALLS if n in per_call)
+    gemm_flops = sum(work[n][0] for n in GEMM_CALLS if n in per_call)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
 
     out = {

@@ -206,6 +206,41 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Kernel-level phases of the two calls above, for callers that schedule the
+ * expert GEMMs themselves (e.g. to overlap them with other work or to time
+ * them one by one).  moe_grouped_swiglu_fwd = moe_expert_up + moe_expert_down;
+ * moe_grouped_swiglu_bwd = moe_expert_dgrad_down + moe_expert_dgrad_up +
+ * moe_expert_wgrad, with da and db held in its workspace.  Each phase is one
+ * GEMM kernel (moe_expert_wgrad adds an ordered split-K reduction kernel when
+ * E x output tiles alone cannot fill the GPU).  Same layouts, formulas and
+ * precision as the calls above; da, db [T*k,f] act are caller buffers here.
+ *   moe_expert_up:         a, b, h from x_perm, W1, W3
+ *   moe_expert_down:       y_perm = h W2^T
+ *   moe_expert_dgrad_down: dh = dy_perm W2 (stored precision), da, db
+ *   moe_expert_dgrad_up:   dx_perm = da W1 + db W3
+ *   moe_expert_wgrad:      dW2 = dy_perm^T h, dW1 = da^T x_perm, dW3 = db^T x_perm
+ * moe_expert_wgrad's workspace: at least moe_workspace_bytes() bytes.
+ */
+moe_status moe_expert_up(const moe_dims* dims, const void* x_perm,
+                         const int32_t* expert_offsets, const void* w1, const void* w3,
+                         void* a_save, void* b_save, void* h_save, void* stream);
+moe_status moe_expert_down(const moe_dims* dims, const void* h_save,
+                           const int32_t* expert_offsets, const void* w2, void* y_perm,
+                           void* stream);
+moe_status moe_expert_dgrad_down(const moe_dims* dims, const void* dy_perm,
+                                 const int32_t* expert_offsets, const void* w2,
+                                 const void* a_save, const void* b_save, void* da, void* db,
+                                 void* stream);
+moe_status moe_expert_dgrad_up(const moe_dims* dims, const void* da, const void* db,
+                               const int32_t* expert_offsets, const void* w1, const void* w3,
+                               void* dx_perm, void* stream);
+moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
+                            const int32_t* expert_offsets, const void* h_save,
+                            const void* dy_perm, const void* da, const void* db, void* dw1,
+                            void* dw3, void* dw2, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * moe_route_bwd -- adjoint of the router (logits -> top-k -> renormalised
  * softmax), fused with the unpermute-and-sum of the expert input gradient.
  *

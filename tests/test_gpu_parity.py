@@ -288,6 +288,33 @@ def test_bitwise_rerun_and_layout_invariance():
         assert np.array_equal(outs[0][k].view(np.uint8), outs[2][k].view(np.uint8)), k
 
 
+def test_kernel_phases_match_coarse_calls():
+    """moe_expert_* phases give the same bytes as moe_grouped_swiglu_fwd/bwd."""
+    _announce("phases")
+    for name in ("c2", "c3"):
+        cfg = get_config(name, T=2048)
+        inp = make_layer_inputs(cfg)
+        layer = run_layer(cfg, inp)
+        dm, act = layer.dims, act_torch(cfg.act)
+        w1, w3, w2 = (dev(inp[k], act) for k in ("w1", "w3", "w2"))
+        a, b, h = (torch.empty_like(layer.a) for _ in range(3))
+        y = torch.empty_like(layer.y_perm)
+        M.moe_expert_up(dm, layer.x_perm, layer.expert_offsets, w1, w3, a, b, h)
+        M.moe_expert_down(dm, h, layer.expert_offsets, w2, y)
+        da, db = torch.empty_like(layer.a), torch.empty_like(layer.a)
+        dxp = torch.empty_like(layer.dx_perm)
+        dw1, dw3, dw2 = (torch.empty_like(t) for t in (layer.dw1, layer.dw3, layer.dw2))
+        M.moe_expert_dgrad_down(dm, layer.dy_perm, layer.expert_offsets, w2, a, b, da, db)
+        M.moe_expert_dgrad_up(dm, da, db, layer.expert_offsets, w1, w3, dxp)
+        M.moe_expert_wgrad(dm, layer.x_perm, layer.expert_offsets, h, layer.dy_perm, da, db,
+                           dw1, dw3, dw2, layer.workspace)
+        torch.cuda.synchronize()
+        for got, ref in ((a, layer.a), (b, layer.b), (h, layer.h), (y, layer.y_perm),
+                         (dxp, layer.dx_perm), (dw1, layer.dw1), (dw3, layer.dw3),
+                         (dw2, layer.dw2)):
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def test_empty_batch():
     _announce("T=0")
     cfg = get_config("c2", T=0, d=64, E=4, f=64, k=2)

@@ -19,6 +19,11 @@ from ._lib import (  # noqa: F401
     moe_combine_bwd,
     moe_coselect,
     moe_dispatch_plan,
+    moe_expert_dgrad_down,
+    moe_expert_dgrad_up,
+    moe_expert_down,
+    moe_expert_up,
+    moe_expert_wgrad,
     moe_grouped_swiglu_bwd,
     moe_grouped_swiglu_fwd,
     moe_permute,

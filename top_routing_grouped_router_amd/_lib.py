@@ -33,7 +33,8 @@ EXPORTED = (
     "moe_status_string", "moe_last_error", "moe_workspace_bytes", "moe_route", "moe_permute",
     "moe_grouped_swiglu_fwd", "moe_combine", "moe_combine_bwd", "moe_grouped_swiglu_bwd",
     "moe_route_bwd", "moe_coselect", "moe_dispatch_plan", "moe_placement_greedy",
-    "moe_check_placement",
+    "moe_check_placement", "moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
+    "moe_expert_dgrad_up", "moe_expert_wgrad",
 )
 
 
@@ -72,6 +73,11 @@ _SIGNATURES = {
     "moe_dispatch_plan": (_I32, [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _SZ, _P]),
     "moe_placement_greedy": (_I32, [_I32, _I32, _P, _P]),
+    "moe_expert_up": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_down": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
+    "moe_expert_dgrad_down": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_dgrad_up": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_wgrad": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
 }
 
@@ -228,6 +234,57 @@ def moe_route_bwd(dims, x, w_router, topk_idx, topk_gate, dgate, expert_offsets,
         _ptr(dw_router, "dw_router", torch.float32), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_route_bwd")
+
+
+def moe_expert_up(dims, x_perm, expert_offsets, w1, w3, a_save, b_save, h_save, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_up(ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
+                             _ptr(expert_offsets, "expert_offsets", torch.int32),
+                             _ptr(w1, "w1", act), _ptr(w3, "w3", act),
+                             _ptr(a_save, "a_save", act), _ptr(b_save, "b_save", act),
+                             _ptr(h_save, "h_save", act), _stream(stream))
+    _check(st, "moe_expert_up")
+
+
+def moe_expert_down(dims, h_save, expert_offsets, w2, y_perm, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_down(ctypes.byref(dims), _ptr(h_save, "h_save", act),
+                               _ptr(expert_offsets, "expert_offsets", torch.int32),
+                               _ptr(w2, "w2", act), _ptr(y_perm, "y_perm", act), _stream(stream))
+    _check(st, "moe_expert_down")
+
+
+def moe_expert_dgrad_down(dims, dy_perm, expert_offsets, w2, a_save, b_save, da, db,
+                          stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_dgrad_down(ctypes.byref(dims), _ptr(dy_perm, "dy_perm", act),
+                                     _ptr(expert_offsets, "expert_offsets", torch.int32),
+                                     _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
+                                     _ptr(b_save, "b_save", act), _ptr(da, "da", act),
+                                     _ptr(db, "db", act), _stream(stream))
+    _check(st, "moe_expert_dgrad_down")
+
+
+def moe_expert_dgrad_up(dims, da, db, expert_offsets, w1, w3, dx_perm, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_dgrad_up(ctypes.byref(dims), _ptr(da, "da", act), _ptr(db, "db", act),
+                                   _ptr(expert_offsets, "expert_offsets", torch.int32),
+                                   _ptr(w1, "w1", act), _ptr(w3, "w3", act),
+                                   _ptr(dx_perm, "dx_perm", act), _stream(stream))
+    _check(st, "moe_expert_dgrad_up")
+
+
+def moe_expert_wgrad(dims, x_perm, expert_offsets, h_save, dy_perm, da, db, dw1, dw3, dw2,
+                     workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_wgrad(
+        ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(h_save, "h_save", act),
+        _ptr(dy_perm, "dy_perm", act), _ptr(da, "da", act), _ptr(db, "db", act),
+        _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act), _ptr(dw2, "dw2", act),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_expert_wgrad")
 
 
 def moe_coselect(T, k, E, topk_idx, coselect, stream=None):

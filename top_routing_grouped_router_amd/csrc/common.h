@@ -101,15 +101,38 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
                              float* ws_partial, hipStream_t s);
 
+// kernel-level phases of the expert GEMMs (dispatch on the activation type)
+hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                            const void* w1, const void* w3, void* a, void* b, void* h,
+                            hipStream_t s);
+hipError_t launch_expert_down(const moe_dims& dm, const void* h, const int32_t* offsets,
+                              const void* w2, void* y, hipStream_t s);
+hipError_t launch_expert_dgrad_down(const moe_dims& dm, const void* dy_perm,
+                                    const int32_t* offsets, const void* w2, const void* a,
+                                    const void* b, void* da, void* db, hipStream_t s);
+hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void* db,
+                                  const int32_t* offsets, const void* w1, const void* w3,
+                                  void* dx_perm, hipStream_t s);
+hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                               const void* h, const void* dy_perm, const void* da,
+                               const void* db, void* dw1, void* dw3, void* dw2, float* partial,
+                               hipStream_t s);
+
 // bf16 matrix-core implementations (gemm_bf16.hip)
-hipError_t launch_swiglu_fwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                                  const void* w1, const void* w3, const void* w2, void* a,
-                                  void* b, void* h, void* y, hipStream_t s);
-hipError_t launch_swiglu_bwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                                  const void* w1, const void* w3, const void* w2, const void* a,
-                                  const void* b, const void* h, const void* dy_perm,
-                                  void* dx_perm, void* dw1, void* dw3, void* dw2, void* ws_da,
-                                  void* ws_db, float* ws_partial, hipStream_t s);
+hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const void* w3, void* a, void* b, void* h,
+                          hipStream_t s);
+hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* offsets,
+                            const void* w2, void* y, hipStream_t s);
+hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const int32_t* offsets,
+                                  const void* w2, const void* a, const void* b, void* da,
+                                  void* db, hipStream_t s);
+hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
+                                const int32_t* offsets, const void* w1, const void* w3,
+                                void* dx_perm, hipStream_t s);
+hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                             const void* h, const void* dy_perm, const void* da, const void* db,
+                             void* dw1, void* dw3, void* dw2, float* partial, hipStream_t s);
 int wgrad_splits_bf16(const moe_dims& dm);           // split-K count of the weight gradients
 size_t wgrad_partial_bytes_bf16(const moe_dims& dm); // fp32 partial tiles it needs
 

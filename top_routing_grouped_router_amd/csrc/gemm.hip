@@ -401,106 +401,111 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename TA, int MODE>
-hipError_t launch_mode(dim3 grid, const GemmArgs& g, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<TA, MODE>), grid, dim3(kThreads), 0, s, g);
+template <int MODE>
+hipError_t launch_f32(dim3 grid, const GemmArgs& g, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<float, MODE>), grid, dim3(kThreads), 0, s, g);
   return hipGetLastError();
 }
 
-template <typename TA>
-hipError_t fwd_impl(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                    const void* w1, const void* w3, const void* w2, void* a, void* b, void* h,
-                    void* y, hipStream_t s) {
-  const int64_t R = dm.T * dm.k;
-  if (R == 0) return hipSuccess;
-  const unsigned row_tiles = static_cast<unsigned>((R + BM - 1) / BM + dm.E);
+GemmArgs base_args(const moe_dims& dm, const int32_t* offsets) {
   GemmArgs g{};
   g.offsets = offsets;
   g.E = dm.E;
   g.d = dm.d;
   g.f = dm.f;
+  return g;
+}
+
+unsigned row_tiles(const moe_dims& dm) {
+  return static_cast<unsigned>((dm.T * dm.k + BM - 1) / BM + dm.E);
+}
+
+}  // namespace
+
+// Each phase dispatches on the activation type: bf16 runs on the matrix cores
+// (gemm_bf16.hip), fp32 on the vector ALUs (the kernel above).
+
+hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                            const void* w1, const void* w3, void* a, void* b, void* h,
+                            hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;
+  if (dm.act == MOE_BF16) return launch_up_bf16(dm, x_perm, offsets, w1, w3, a, b, h, s);
+  GemmArgs g = base_args(dm, offsets);
   g.a0 = x_perm;
   g.b0 = w1;
   g.b1 = w3;
   g.c0 = a;
   g.c1 = b;
   g.c2 = h;
-  hipError_t err = launch_mode<TA, UP>(dim3(row_tiles, dm.f / 64), g, s);
-  if (err != hipSuccess) return err;
-  GemmArgs g2{};
-  g2.offsets = offsets;
-  g2.E = dm.E;
-  g2.d = dm.d;
-  g2.f = dm.f;
-  g2.a0 = h;
-  g2.b0 = w2;
-  g2.c0 = y;
-  return launch_mode<TA, DOWN>(dim3(row_tiles, (dm.d + BN - 1) / BN), g2, s);
+  return launch_f32<UP>(dim3(row_tiles(dm), dm.f / 64), g, s);
 }
 
-template <typename TA>
-hipError_t bwd_impl(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                    const void* w1, const void* w3, const void* w2, const void* a, const void* b,
-                    const void* h, const void* dy_perm, void* dx_perm, void* dw1, void* dw3,
-                    void* dw2, void* ws_da, void* ws_db, hipStream_t s) {
-  const int64_t R = dm.T * dm.k;
-  hipError_t err;
-  if (R > 0) {
-    const unsigned row_tiles = static_cast<unsigned>((R + BM - 1) / BM + dm.E);
-    GemmArgs g{};
-    g.offsets = offsets;
-    g.E = dm.E;
-    g.d = dm.d;
-    g.f = dm.f;
-    g.a0 = dy_perm;
-    g.b0 = w2;
-    g.aux0 = a;
-    g.aux1 = b;
-    g.c0 = ws_da;
-    g.c1 = ws_db;
-    err = launch_mode<TA, DGRAD_DOWN>(dim3(row_tiles, (dm.f + BN - 1) / BN), g, s);
-    if (err != hipSuccess) return err;
-    GemmArgs g2{};
-    g2.offsets = offsets;
-    g2.E = dm.E;
-    g2.d = dm.d;
-    g2.f = dm.f;
-    g2.a0 = ws_da;
-    g2.a1 = ws_db;
-    g2.b0 = w1;
-    g2.b1 = w3;
-    g2.c0 = dx_perm;
-    err = launch_mode<TA, DGRAD_UP>(dim3(row_tiles, (dm.d + BN - 1) / BN), g2, s);
-    if (err != hipSuccess) return err;
-  }
+hipError_t launch_expert_down(const moe_dims& dm, const void* h, const int32_t* offsets,
+                              const void* w2, void* y, hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;
+  if (dm.act == MOE_BF16) return launch_down_bf16(dm, h, offsets, w2, y, s);
+  GemmArgs g = base_args(dm, offsets);
+  g.a0 = h;
+  g.b0 = w2;
+  g.c0 = y;
+  return launch_f32<DOWN>(dim3(row_tiles(dm), (dm.d + BN - 1) / BN), g, s);
+}
+
+hipError_t launch_expert_dgrad_down(const moe_dims& dm, const void* dy_perm,
+                                    const int32_t* offsets, const void* w2, const void* a,
+                                    const void* b, void* da, void* db, hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;
+  if (dm.act == MOE_BF16) return launch_dgrad_down_bf16(dm, dy_perm, offsets, w2, a, b, da, db, s);
+  GemmArgs g = base_args(dm, offsets);
+  g.a0 = dy_perm;
+  g.b0 = w2;
+  g.aux0 = a;
+  g.aux1 = b;
+  g.c0 = da;
+  g.c1 = db;
+  return launch_f32<DGRAD_DOWN>(dim3(row_tiles(dm), (dm.f + BN - 1) / BN), g, s);
+}
+
+hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void* db,
+                                  const int32_t* offsets, const void* w1, const void* w3,
+                                  void* dx_perm, hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;
+  if (dm.act == MOE_BF16) return launch_dgrad_up_bf16(dm, da, db, offsets, w1, w3, dx_perm, s);
+  GemmArgs g = base_args(dm, offsets);
+  g.a0 = da;
+  g.a1 = db;
+  g.b0 = w1;
+  g.b1 = w3;
+  g.c0 = dx_perm;
+  return launch_f32<DGRAD_UP>(dim3(row_tiles(dm), (dm.d + BN - 1) / BN), g, s);
+}
+
+hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                               const void* h, const void* dy_perm, const void* da,
+                               const void* db, void* dw1, void* dw3, void* dw2, float* partial,
+                               hipStream_t s) {
+  if (dm.act == MOE_BF16)
+    return launch_wgrad_bf16(dm, x_perm, offsets, h, dy_perm, da, db, dw1, dw3, dw2, partial, s);
   // weight gradients (also for experts with no rows: they get zeros)
-  GemmArgs g3{};
-  g3.offsets = offsets;
-  g3.E = dm.E;
-  g3.d = dm.d;
-  g3.f = dm.f;
-  g3.a0 = dy_perm;   // z = 0: A = dy (m = d), B = h (n = f)
-  g3.b0 = h;
-  g3.a1 = ws_da;     // z = 1: A = da (m = f), B = x (n = d)
-  g3.aux0 = ws_db;   // z = 2: A = db (m = f), B = x (n = d)
-  g3.b1 = x_perm;
-  g3.c0 = dw2;
-  g3.c1 = dw1;
-  g3.c2 = dw3;
+  GemmArgs g = base_args(dm, offsets);
+  g.a0 = dy_perm;   // z = 0: A = dy (m over d), B = h (n over f)
+  g.b0 = h;
+  g.a1 = da;        // z = 1: A = da (m over f), B = x (n over d)
+  g.aux0 = db;      // z = 2: A = db (m over f), B = x (n over d)
+  g.b1 = x_perm;
+  g.c0 = dw2;
+  g.c1 = dw1;
+  g.c2 = dw3;
   const unsigned tiles = static_cast<unsigned>(((dm.d + BM - 1) / BM) * ((dm.f + BN - 1) / BN));
-  // z = 1, 2 have M = f, N = d: the same count of tiles as z = 0 up to the edge
-  const unsigned tiles_t = static_cast<unsigned>(((dm.f + BM - 1) / BM) * ((dm.d + BN - 1) / BN));
-  return launch_mode<TA, WGRAD>(dim3(std::max(tiles, tiles_t), dm.E, 3), g3, s);
+  return launch_f32<WGRAD>(dim3(tiles, dm.E, 3), g, s);
 }
-
-}  // namespace
 
 hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, void* a, void* b,
                              void* h, void* y, hipStream_t s) {
-  if (dm.act == MOE_BF16)
-    return launch_swiglu_fwd_bf16(dm, x_perm, offsets, w1, w3, w2, a, b, h, y, s);
-  return fwd_impl<float>(dm, x_perm, offsets, w1, w3, w2, a, b, h, y, s);
+  hipError_t e = launch_expert_up(dm, x_perm, offsets, w1, w3, a, b, h, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_down(dm, h, offsets, w2, y, s);
 }
 
 hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
@@ -508,11 +513,12 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
                              float* ws_partial, hipStream_t s) {
-  if (dm.act == MOE_BF16)
-    return launch_swiglu_bwd_bf16(dm, x_perm, offsets, w1, w3, w2, a, b, h, dy_perm, dx_perm,
-                                  dw1, dw3, dw2, ws_da, ws_db, ws_partial, s);
-  return bwd_impl<float>(dm, x_perm, offsets, w1, w3, w2, a, b, h, dy_perm, dx_perm, dw1, dw3,
-                         dw2, ws_da, ws_db, s);
+  hipError_t e = launch_expert_dgrad_down(dm, dy_perm, offsets, w2, a, b, ws_da, ws_db, s);
+  if (e != hipSuccess) return e;
+  e = launch_expert_dgrad_up(dm, ws_da, ws_db, offsets, w1, w3, dx_perm, s);
+  if (e != hipSuccess) return e;
+  return launch_expert_wgrad(dm, x_perm, offsets, h, dy_perm, ws_da, ws_db, dw1, dw3, dw2,
+                             ws_partial, s);
 }
 
 }  // namespace moe

@@ -578,91 +578,85 @@ hipError_t launch_rows(const Args& base, int64_t R, int E, int n_tiles_n, hipStr
 
 }  // namespace
 
-hipError_t launch_swiglu_fwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                                  const void* w1, const void* w3, const void* w2, void* a,
-                                  void* b, void* h, void* y, hipStream_t s) {
-  const int64_t R = dm.T * dm.k;
-  if (R == 0) return hipSuccess;
+namespace {
+Args base_args(const moe_dims& dm, const int32_t* offsets) {
   Args g{};
   g.offsets = offsets;
   g.E = dm.E;
   g.d = dm.d;
   g.f = dm.f;
+  return g;
+}
+}  // namespace
+
+hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                          const void* w1, const void* w3, void* a, void* b, void* h,
+                          hipStream_t s) {
+  Args g = base_args(dm, offsets);
   g.a0 = static_cast<const bf16_t*>(x_perm);
   g.b0 = static_cast<const bf16_t*>(w1);
   g.b1 = static_cast<const bf16_t*>(w3);
   g.c0 = static_cast<bf16_t*>(a);
   g.c1 = static_cast<bf16_t*>(b);
   g.c2 = static_cast<bf16_t*>(h);
-  hipError_t err = launch_rows<UP>(g, R, dm.E, dm.f / 64, s);
-  if (err != hipSuccess) return err;
-  Args g2{};
-  g2.offsets = offsets;
-  g2.E = dm.E;
-  g2.d = dm.d;
-  g2.f = dm.f;
-  g2.a0 = static_cast<const bf16_t*>(h);
-  g2.b0 = static_cast<const bf16_t*>(w2);
-  g2.c0 = static_cast<bf16_t*>(y);
-  return launch_rows<DOWN>(g2, R, dm.E, (dm.d + BN - 1) / BN, s);
+  return launch_rows<UP>(g, dm.T * dm.k, dm.E, dm.f / 64, s);
 }
 
-hipError_t launch_swiglu_bwd_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                                  const void* w1, const void* w3, const void* w2, const void* a,
-                                  const void* b, const void* h, const void* dy_perm,
-                                  void* dx_perm, void* dw1, void* dw3, void* dw2, void* ws_da,
-                                  void* ws_db, float* ws_partial, hipStream_t s) {
-  const int64_t R = dm.T * dm.k;
-  hipError_t err;
-  if (R > 0) {
-    Args g{};
-    g.offsets = offsets;
-    g.E = dm.E;
-    g.d = dm.d;
-    g.f = dm.f;
-    g.a0 = static_cast<const bf16_t*>(dy_perm);
-    g.b0 = static_cast<const bf16_t*>(w2);
-    g.aux0 = static_cast<const bf16_t*>(a);
-    g.aux1 = static_cast<const bf16_t*>(b);
-    g.c0 = static_cast<bf16_t*>(ws_da);
-    g.c1 = static_cast<bf16_t*>(ws_db);
-    err = launch_rows<DGRAD_DOWN>(g, R, dm.E, (dm.f + BN - 1) / BN, s);
-    if (err != hipSuccess) return err;
-    Args g2{};
-    g2.offsets = offsets;
-    g2.E = dm.E;
-    g2.d = dm.d;
-    g2.f = dm.f;
-    g2.a0 = static_cast<const bf16_t*>(ws_da);
-    g2.a1 = static_cast<const bf16_t*>(ws_db);
-    g2.b0 = static_cast<const bf16_t*>(w1);
-    g2.b1 = static_cast<const bf16_t*>(w3);
-    g2.c0 = static_cast<bf16_t*>(dx_perm);
-    err = launch_rows<DGRAD_UP>(g2, R, dm.E, (dm.d + BN - 1) / BN, s);
-    if (err != hipSuccess) return err;
-  }
-  Args g3{};
-  g3.offsets = offsets;
-  g3.E = dm.E;
-  g3.d = dm.d;
-  g3.f = dm.f;
-  g3.a0 = static_cast<const bf16_t*>(dy_perm);   // z = 0: A = dy (m over d), B = h (n over f)
-  g3.b0 = static_cast<const bf16_t*>(h);
-  g3.a1 = static_cast<const bf16_t*>(ws_da);     // z = 1: A = da (m over f), B = x (n over d)
-  g3.aux0 = static_cast<const bf16_t*>(ws_db);   // z = 2: A = db (m over f), B = x (n over d)
-  g3.b1 = static_cast<const bf16_t*>(x_perm);
-  g3.c0 = static_cast<bf16_t*>(dw2);
-  g3.c1 = static_cast<bf16_t*>(dw1);
-  g3.c2 = static_cast<bf16_t*>(dw3);
+hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* offsets,
+                            const void* w2, void* y, hipStream_t s) {
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(h);
+  g.b0 = static_cast<const bf16_t*>(w2);
+  g.c0 = static_cast<bf16_t*>(y);
+  return launch_rows<DOWN>(g, dm.T * dm.k, dm.E, (dm.d + BN - 1) / BN, s);
+}
+
+hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const int32_t* offsets,
+                                  const void* w2, const void* a, const void* b, void* da,
+                                  void* db, hipStream_t s) {
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(dy_perm);
+  g.b0 = static_cast<const bf16_t*>(w2);
+  g.aux0 = static_cast<const bf16_t*>(a);
+  g.aux1 = static_cast<const bf16_t*>(b);
+  g.c0 = static_cast<bf16_t*>(da);
+  g.c1 = static_cast<bf16_t*>(db);
+  return launch_rows<DGRAD_DOWN>(g, dm.T * dm.k, dm.E, (dm.f + BN - 1) / BN, s);
+}
+
+hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
+                                const int32_t* offsets, const void* w1, const void* w3,
+                                void* dx_perm, hipStream_t s) {
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(da);
+  g.a1 = static_cast<const bf16_t*>(db);
+  g.b0 = static_cast<const bf16_t*>(w1);
+  g.b1 = static_cast<const bf16_t*>(w3);
+  g.c0 = static_cast<bf16_t*>(dx_perm);
+  return launch_rows<DGRAD_UP>(g, dm.T * dm.k, dm.E, (dm.d + BN - 1) / BN, s);
+}
+
+hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+                             const void* h, const void* dy_perm, const void* da, const void* db,
+                             void* dw1, void* dw3, void* dw2, float* partial, hipStream_t s) {
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(dy_perm);   // z = 0: A = dy (m over d), B = h (n over f)
+  g.b0 = static_cast<const bf16_t*>(h);
+  g.a1 = static_cast<const bf16_t*>(da);        // z = 1: A = da (m over f), B = x (n over d)
+  g.aux0 = static_cast<const bf16_t*>(db);      // z = 2: A = db (m over f), B = x (n over d)
+  g.b1 = static_cast<const bf16_t*>(x_perm);
+  g.c0 = static_cast<bf16_t*>(dw2);
+  g.c1 = static_cast<bf16_t*>(dw1);
+  g.c2 = static_cast<bf16_t*>(dw3);
   const int tpe = wgrad_tiles_per_expert(dm);
   const int splits = wgrad_splits_bf16(dm);
   const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe * splits);
-  g3.grid_pad = static_cast<int32_t>(grid);
-  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kThreads), 0, s, g3, tpe, splits, ws_partial);
+  g.grid_pad = static_cast<int32_t>(grid);
+  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kThreads), 0, s, g, tpe, splits, partial);
   if (splits > 1) {
     const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (BM * BN / 8);
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((chunks + kThreads - 1) / kThreads),
-                       dim3(kThreads), 0, s, g3, tpe, splits, ws_partial);
+                       dim3(kThreads), 0, s, g, tpe, splits, partial);
   }
   return hipGetLastError();
 }

@@ -388,6 +388,101 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
                     __func__);
 }
 
+moe_status moe_expert_up(const moe_dims* dims, const void* x_perm,
+                         const int32_t* expert_offsets, const void* w1, const void* w3,
+                         void* a_save, void* b_save, void* h_save, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  return hip_status(moe::launch_expert_up(dm, x_perm, expert_offsets, w1, w3, a_save, b_save,
+                                          h_save, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_down(const moe_dims* dims, const void* h_save,
+                           const int32_t* expert_offsets, const void* w2, void* y_perm,
+                           void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(y_perm, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_expert_down(dm, h_save, expert_offsets, w2, y_perm,
+                                            static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_dgrad_down(const moe_dims* dims, const void* dy_perm,
+                                 const int32_t* expert_offsets, const void* w2,
+                                 const void* a_save, const void* b_save, void* da, void* db,
+                                 void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  return hip_status(moe::launch_expert_dgrad_down(dm, dy_perm, expert_offsets, w2, a_save, b_save,
+                                                  da, db, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_dgrad_up(const moe_dims* dims, const void* da, const void* db,
+                               const int32_t* expert_offsets, const void* w1, const void* w3,
+                               void* dx_perm, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dx_perm, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_expert_dgrad_up(dm, da, db, expert_offsets, w1, w3, dx_perm,
+                                                static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
+                            const int32_t* expert_offsets, const void* h_save,
+                            const void* dy_perm, const void* da, const void* db, void* dw1,
+                            void* dw3, void* dw2, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
+  const size_t need = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
+  st = check_ws(workspace, workspace_bytes, need, __func__);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_expert_wgrad(dm, x_perm, expert_offsets, h_save, dy_perm, da, db,
+                                             dw1, dw3, dw2, static_cast<float*>(workspace),
+                                             static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
 moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_router,
                          const int32_t* topk_idx, const float* topk_gate, const float* dgate,
                          const int32_t* expert_offsets, const int32_t* pos,
