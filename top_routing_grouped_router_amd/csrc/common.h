@@ -64,8 +64,11 @@ __device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// v_rcp_f32 instead of a full division (about 1 ulp); exp(-z) = inf gives 0
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 // ---------------------------------------------------------------- workspace
 
@@ -75,7 +78,8 @@ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255);
 // All launchers enqueue on `stream` and return hipSuccess or the launch error.
 
 // route
-constexpr int kRouteTileMax = 32;   // tokens per route workgroup (upper bound)
+constexpr int kRouteTileMax = 32;   // tokens per workgroup of the vector-ALU router
+constexpr int kRouteMfmaTile = 64;  // tokens per workgroup of the matrix-core router (bf16 x)
 hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,

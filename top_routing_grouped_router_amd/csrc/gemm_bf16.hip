@@ -14,7 +14,12 @@
 //   DGRAD_UP    dx_perm = da W1 + db W3   (one K loop over 2f)
 //   WGRAD       dW2 = dy^T h, dW1 = da^T x, dW3 = db^T x   (K = the expert's rows)
 //
-// Kernel structure (256 threads = 4 wavefronts, 128 x 128 output tile, K step 64):
+// Kernel structure (K step 64, v_mfma_f32_32x32x16_bf16), in two tile
+// configurations:
+//   small: 128 x 128 tile, 4 wavefronts of 64 x 64 (shapes with few or short
+//          tiles);
+//   big:   256 x 256 tile, 8 wavefronts of 128 x 64, one workgroup per CU
+//          (large expert GEMMs: twice the matrix-core work per LDS byte).
 //  * LDS holds both operand tiles k-contiguous, 16-byte chunks XOR-swizzled by
 //    row (see swz), double-buffered: global loads of step k+1 are in flight
 //    while step k runs on the matrix cores.
@@ -22,10 +27,10 @@
 //    wgrad) are loaded as 4 x 8 blocks (four 16-byte rows per thread) and
 //    transposed in registers before the LDS store, so the matrix-core loop is
 //    the same in every mode.
-//  * v_mfma_f32_16x16x32_bf16 with the B fragment as the first source: each
-//    lane then owns 4 consecutive output columns of one row, which the
-//    epilogue writes to LDS as 8-byte pieces and stores to HBM in coalesced
-//    16-byte chunks (with the mode's elementwise work applied on the way).
+//  * The MFMA takes the B fragment as its first source: each lane then owns
+//    runs of 4 consecutive output columns of one row, which the epilogue
+//    writes to LDS as 8-byte pieces and stores to HBM in coalesced 16-byte
+//    chunks (with the mode's elementwise work applied on the way).
 //  * Row tiles come from the expert offsets on the device; the flat tile
 //    index is remapped so that each XCD (workgroups are dealt round-robin to
 //    the 8 XCDs) works through a contiguous run of tiles, n fastest, which
@@ -37,18 +42,31 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;
-constexpr int BN = 128;
+constexpr int kThreads = 256;   // small kernels (reduce)
 constexpr int BK = 64;
-constexpr int kTile = 128 * BK;       // bf16 elements per operand tile
-constexpr int kOutLd = BN + 8;        // epilogue LDS row stride (elements)
 constexpr int kXcd = 8;
 
 enum Mode { UP = 0, DOWN = 1, DGRAD_DOWN = 2, DGRAD_UP = 3, WGRAD = 4 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Tile configurations.  Both use v_mfma_f32_32x32x16_bf16 fragments (on gfx950
+// this shape sustains about 2.5x the rate of 16x16x32 in a dependency-free
+// stream); wavefronts form a WAVES_M x WAVES_N grid, each owning FM x FN
+// fragments of 32 x 32.
+template <bool BIG> struct Cfg;
+template <> struct Cfg<false> {   // 128 x 128, 4 wavefronts of 64 x 64
+  static constexpr int THREADS = 256, BM = 128, BN = 128, WAVES_N = 2, FM = 2, FN = 2;
+  static constexpr int kOutLd = BN + 8;
+  static constexpr int kLds = 2 * (BM + BN) * 64;
+};
+template <> struct Cfg<true> {    // 256 x 256, 8 wavefronts of 128 x 64
+  static constexpr int THREADS = 512, BM = 256, BN = 256, WAVES_N = 4, FM = 4, FN = 2;
+  static constexpr int kOutLd = BN + 8;
+  static constexpr int kLds = 256 * (BN + 8);   // >= 2 x (A + B) = 4 x 256 x 64
+};
 
 struct Args {
   const bf16_t* a0;
@@ -77,117 +95,179 @@ __device__ __forceinline__ int swz(int r, int chunk) {
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 // ------------------------------------------------------------------ staging
-// k-contiguous operand: 128 rows x 64 k = 1024 chunks, 4 per thread.
+// Loads never branch: an out-of-range row or column is read from a clamped,
+// valid address and zeroed when the registers are written to LDS, so all of a
+// step's global loads are in flight together (a guarded load would end in a
+// wait for the loads issued before it).
+
+// k-contiguous operand: ROWS rows x 64 k = ROWS x 8 chunks, ROWS x 8 / NT per thread.
+template <int ROWS, int NT>
 struct KPart {
-  uint4 v[4];
+  uint4 v[ROWS * 8 / NT];
 };
 
-template <typename RowPtr>
-__device__ __forceinline__ void kload(KPart& p, RowPtr row_ptr, int valid, int k0) {
+template <int ROWS, int NT, typename RowPtr>
+__device__ __forceinline__ void kload(KPart<ROWS, NT>& p, RowPtr row_ptr, int valid, int k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = threadIdx.x + kThreads * i;
-    const int r = v >> 3, c = v & 7;
-    p.v[i] = (r < valid) ? *reinterpret_cast<const uint4*>(row_ptr(r) + k0 + c * 8) : zero4();
+  for (int i = 0; i < ROWS * 8 / NT; ++i) {
+    const int v = threadIdx.x + NT * i;
+    const int r = min(v >> 3, valid - 1), c = v & 7;
+    p.v[i] = *reinterpret_cast<const uint4*>(row_ptr(r) + k0 + c * 8);
   }
 }
 
-__device__ __forceinline__ void kstore(const KPart& p, bf16_t* lds) {
+__device__ __forceinline__ uint4 mask4(const uint4& v, bool keep) {
+  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+template <int ROWS, int NT>
+__device__ __forceinline__ void kstore(const KPart<ROWS, NT>& p, bf16_t* lds, int valid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = threadIdx.x + kThreads * i;
+  for (int i = 0; i < ROWS * 8 / NT; ++i) {
+    const int v = threadIdx.x + NT * i;
     const int r = v >> 3, c = v & 7;
-    *reinterpret_cast<uint4*>(lds + swz(r, c)) = p.v[i];
+    *reinterpret_cast<uint4*>(lds + swz(r, c)) = mask4(p.v[i], r < valid);
   }
 }
 
-// m/n-contiguous operand: element (k, j) at base[k * ld + j]; the 64 k x 128 j
-// tile is cut into 16 x 16 blocks of 4 k x 8 j, one block per thread.  Within
-// a wavefront, lane bits 0-2 pick the k quad and bits 3-5 the j block, so a
-// load instruction reads 128 contiguous bytes of each of 8 k rows, and each
-// group of 16 lanes stores to 16 distinct bank slots after the transpose.
+// m/n-contiguous operand: element (k, j) at base[k * ld + j]; the 64 k x COLS j
+// tile is cut into 16 x (COLS / 8) blocks of 4 k x 8 j, COLS x 2 / NT per
+// thread.  Within a wavefront, lane bits 0-2 pick the k quad and bits 3-5 the
+// j block, so a load instruction reads 128 contiguous bytes of each of 8 k
+// rows, and each group of 16 lanes stores to 16 distinct bank slots after the
+// transpose.
+template <int COLS, int NT>
 struct MPart {
-  uint4 v[4];
+  uint4 v[COLS * 2 / NT][4];
 };
 
-__device__ __forceinline__ void mblock(int* jb, int* kq) {
+template <int NT>
+__device__ __forceinline__ void mblock(int i, int* jb, int* kq) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   *kq = (wave & 1) * 8 + (lane & 7);
-  *jb = (wave >> 1) * 8 + (lane >> 3);
+  *jb = i * (NT / 16) + (wave >> 1) * 8 + (lane >> 3);
 }
 
-__device__ __forceinline__ void mload(MPart& p, const bf16_t* base, int64_t ld, int kvalid,
-                                      int jvalid) {
-  int jb, kq;
-  mblock(&jb, &kq);
-  const int j = jb * 8;
+// kvalid >= 1 and jvalid >= 8 (a multiple of 8) for every tile that runs
+template <int COLS, int NT>
+__device__ __forceinline__ void mload(MPart<COLS, NT>& p, const bf16_t* base, int64_t ld,
+                                      int kvalid, int jvalid) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int k = kq * 4 + r;
-    p.v[r] = (k < kvalid && j < jvalid) ? *reinterpret_cast<const uint4*>(base + k * ld + j)
-                                        : zero4();
+  for (int i = 0; i < COLS * 2 / NT; ++i) {
+    int jb, kq;
+    mblock<NT>(i, &jb, &kq);
+    const int j = min(jb * 8, jvalid - 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int k = min(kq * 4 + r, kvalid - 1);
+      p.v[i][r] = *reinterpret_cast<const uint4*>(base + k * ld + j);
+    }
   }
 }
 
-// transpose the 4 x 8 block in registers: LDS row j receives its 4 k values
+// transpose each 4 x 8 block in registers: LDS row j receives its 4 k values
 // as one 8-byte piece (half of the swizzled 16-byte chunk kq / 2)
-__device__ __forceinline__ void mstore(const MPart& p, bf16_t* lds) {
-  int jb, kq;
-  mblock(&jb, &kq);
-  const uint32_t in[4][4] = {{p.v[0].x, p.v[0].y, p.v[0].z, p.v[0].w},
-                             {p.v[1].x, p.v[1].y, p.v[1].z, p.v[1].w},
-                             {p.v[2].x, p.v[2].y, p.v[2].z, p.v[2].w},
-                             {p.v[3].x, p.v[3].y, p.v[3].z, p.v[3].w}};
+template <int COLS, int NT>
+__device__ __forceinline__ void mstore(const MPart<COLS, NT>& p, bf16_t* lds, int kvalid,
+                                       int jvalid) {
 #pragma unroll
-  for (int c2 = 0; c2 < 4; ++c2) {
-    const uint32_t A0 = in[0][c2], A1 = in[1][c2], A2 = in[2][c2], A3 = in[3][c2];
-    const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
-    const uint2 odd = make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
-    const int row = jb * 8 + 2 * c2;
-    *reinterpret_cast<uint2*>(lds + swz(row, kq >> 1) + 4 * (kq & 1)) = even;
-    *reinterpret_cast<uint2*>(lds + swz(row + 1, kq >> 1) + 4 * (kq & 1)) = odd;
+  for (int i = 0; i < COLS * 2 / NT; ++i) {
+    int jb, kq;
+    mblock<NT>(i, &jb, &kq);
+    const bool jok = jb * 8 < jvalid;
+    uint4 in4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) in4[r] = mask4(p.v[i][r], jok && (kq * 4 + r < kvalid));
+    const uint32_t in[4][4] = {{in4[0].x, in4[0].y, in4[0].z, in4[0].w},
+                               {in4[1].x, in4[1].y, in4[1].z, in4[1].w},
+                               {in4[2].x, in4[2].y, in4[2].z, in4[2].w},
+                               {in4[3].x, in4[3].y, in4[3].z, in4[3].w}};
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const uint32_t A0 = in[0][c2], A1 = in[1][c2], A2 = in[2][c2], A3 = in[3][c2];
+      const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
+      const uint2 odd =
+          make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
+      const int row = jb * 8 + 2 * c2;
+      *reinterpret_cast<uint2*>(lds + swz(row, kq >> 1) + 4 * (kq & 1)) = even;
+      *reinterpret_cast<uint2*>(lds + swz(row + 1, kq >> 1) + 4 * (kq & 1)) = odd;
+    }
   }
 }
 
 // ------------------------------------------------------------------ matrix-core step
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[4][4], const bf16_t* As, const bf16_t* Bs) {
+template <bool BIG>
+using AccT = f32x16[Cfg<BIG>::FM][Cfg<BIG>::FN];
+
+// One K step (64 = 4 x k16) of the wavefront's FM x FN fragments.  The B
+// fragment is the first MFMA source, so lane l ends up owning
+// C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16 of each fragment.
+template <bool BIG>
+__device__ __forceinline__ void mma_step(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs) {
+  typedef Cfg<BIG> C;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int r = lane & 15, g = lane >> 4;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int kk = 0; kk < BK / 8; kk += 4) {
+  for (int kk = 0; kk < BK / 8; kk += 2) {
     const int chunk = kk + g;
-    bf16x8 af[4], bfr[4];
+    bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 64 + i * 16 + r, chunk));
+    for (int i = 0; i < C::FM; ++i)
+      af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 32 * C::FM + i * 32 + r, chunk));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * 64 + j * 16 + r, chunk));
+    for (int j = 0; j < C::FN; ++j)
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * 32 * C::FN + j * 32 + r, chunk));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   }
 }
 
-// accumulators -> LDS tile [128][kOutLd] of bf16 (rounded once)
-__device__ __forceinline__ void stage_out(const f32x4 (&acc)[4][4], bf16_t* out) {
+template <bool BIG>
+__device__ __forceinline__ void zero_acc(AccT<BIG>& acc) {
+#pragma unroll
+  for (int i = 0; i < Cfg<BIG>::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg<BIG>::FN; ++j) acc[i][j] = f32x16{};
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2(static_cast<uint32_t>(f32_to_bf16(a)) |
+                        (static_cast<uint32_t>(f32_to_bf16(b)) << 16),
+                    static_cast<uint32_t>(f32_to_bf16(c)) |
+                        (static_cast<uint32_t>(f32_to_bf16(d)) << 16));
+}
+
+// Visit the accumulators as (row m, first column n of a run of 4, 4 values).
+template <bool BIG, typename F>
+__device__ __forceinline__ void for_each_quad(const AccT<BIG>& acc, F&& fn) {
+  typedef Cfg<BIG> C;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = wm * 64 + i * 16 + (lane & 15);
-      const int n = wn * 64 + j * 16 + (lane >> 4) * 4;
-      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc[i][j][0])) |
-                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc[i][j][2])) |
-                          (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
-      *reinterpret_cast<uint2*>(out + m * kOutLd + n) = make_uint2(lo, hi);
+    for (int j = 0; j < C::FN; ++j) {
+      const int m = wm * 32 * C::FM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        const int n = wn * 32 * C::FN + j * 32 + vb * 8 + (lane >> 5) * 4;
+        fn(m, n, acc[i][j][4 * vb], acc[i][j][4 * vb + 1], acc[i][j][4 * vb + 2],
+           acc[i][j][4 * vb + 3]);
+      }
     }
+}
+
+// accumulators -> LDS tile [BM][kOutLd] of bf16 (rounded once)
+template <bool BIG>
+__device__ __forceinline__ void stage_out(const AccT<BIG>& acc, bf16_t* out) {
+  for_each_quad<BIG>(acc, [&](int m, int n, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(out + m * Cfg<BIG>::kOutLd + n) = pack4(a, b, c, d);
+  });
 }
 
 // ------------------------------------------------------------------ tile lookup
@@ -196,8 +276,10 @@ __device__ __forceinline__ int flat_tile() {
   return (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
 }
 
-// expert and first row of row tile `tile` (prefix sum of per-expert tile
-// counts across wave 0, 4 experts per lane); false when there is no such tile
+// expert and first row of row tile `tile` (tiles of BM rows; prefix sum of
+// per-expert tile counts across wave 0, 4 experts per lane); false when there
+// is no such tile
+template <int BM>
 __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_out, int* m0_out,
                               int* mend_out) {
   __shared__ int s_e, s_m0, s_mend;
@@ -249,46 +331,44 @@ __device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
 
 // ------------------------------------------------------------------ kernels
 // Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP).
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * kTile];
+template <int MODE, bool BIG>
+__global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
+  typedef Cfg<BIG> C;
+  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
   bf16_t* As0 = lds;
-  bf16_t* Bs0 = lds + kTile;
-  bf16_t* As1 = lds + 2 * kTile;
-  bf16_t* Bs1 = lds + 3 * kTile;
+  bf16_t* Bs0 = lds + BM * BK;
+  bf16_t* As1 = lds + (BM + BN) * BK;
+  bf16_t* Bs1 = lds + (2 * BM + BN) * BK;
 
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
   const int nt = flat - row_tile * g.n_tiles_n;
   int e, m0, mend;
-  if (!find_row_tile(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  if (!find_row_tile<BM>(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
   const int rows = min(BM, mend - m0);
   const int d = g.d, f = g.f;
-  // UP covers 64 f columns of a and the same 64 of b per tile
-  const int n0 = nt * ((MODE == UP) ? 64 : BN);
+  // UP covers BN/2 f columns of a and the same BN/2 of b per tile
+  constexpr int kUpHalf = BN / 2;
+  const int n0 = nt * ((MODE == UP) ? kUpHalf : BN);
   const int Ndim = (MODE == DOWN || MODE == DGRAD_UP) ? d : f;
   const int nvalid = (MODE == UP) ? BN : min(BN, Ndim - n0);
   const int K = (MODE == UP || MODE == DGRAD_DOWN) ? d : (MODE == DOWN ? f : 2 * f);
   const int nk = K / BK;
 
   const int64_t E_fd = static_cast<int64_t>(f) * d;
-  // A rows (k-contiguous)
-  const bf16_t* A0 = g.a0;
   const int lda = (MODE == UP || MODE == DGRAD_DOWN) ? d : f;
   auto a_row = [&](int half) {
-    const bf16_t* base = (MODE == DGRAD_UP && half) ? g.a1 : A0;
+    const bf16_t* base = (MODE == DGRAD_UP && half) ? g.a1 : g.a0;
     return base + static_cast<int64_t>(m0) * lda;
   };
 
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  AccT<BIG> acc;
+  zero_acc<BIG>(acc);
 
-  KPart pa;
-  KPart pb;   // k-contiguous B (UP, DOWN)
-  MPart pm;   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
+  KPart<BM, NT> pa;
+  KPart<BN, NT> pb;   // k-contiguous B (UP, DOWN)
+  MPart<BN, NT> pm;   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
 
   auto load = [&](int kt) {
     int k0 = kt * BK;
@@ -298,32 +378,34 @@ __global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
       k0 -= f;
     }
     const bf16_t* ab = a_row(half);
-    kload(pa, [&](int r) { return ab + static_cast<int64_t>(r) * lda; }, rows, k0);
+    kload<BM, NT>(pa, [&](int r) { return ab + static_cast<int64_t>(r) * lda; }, rows, k0);
     if constexpr (MODE == UP) {
       const bf16_t* w1 = g.b0 + e * E_fd;
       const bf16_t* w3 = g.b1 + e * E_fd;
-      kload(pb, [&](int r) {
-        return (r < 64 ? w1 + static_cast<int64_t>(n0 + r) * d
-                       : w3 + static_cast<int64_t>(n0 + r - 64) * d);
+      kload<BN, NT>(pb, [&](int r) {
+        return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
+                            : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
       }, BN, k0);
     } else if constexpr (MODE == DOWN) {
       const bf16_t* w2 = g.b0 + e * E_fd;
-      kload(pb, [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; }, nvalid, k0);
+      kload<BN, NT>(pb, [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; }, nvalid, k0);
     } else if constexpr (MODE == DGRAD_DOWN) {
       // W2[e] is [d][f]: element (k, n) at k * f + n
-      mload(pm, g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0, f, BK, nvalid);
+      mload<BN, NT>(pm, g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0, f, BK, nvalid);
     } else {
       // W1/W3[e] are [f][d]: element (k, n) at k * d + n
       const bf16_t* w = (half ? g.b1 : g.b0) + e * E_fd;
-      mload(pm, w + static_cast<int64_t>(k0) * d + n0, d, BK, nvalid);
+      mload<BN, NT>(pm, w + static_cast<int64_t>(k0) * d + n0, d, BK, nvalid);
     }
   };
   auto store = [&](bf16_t* As, bf16_t* Bs) {
-    kstore(pa, As);
-    if constexpr (MODE == UP || MODE == DOWN) {
-      kstore(pb, Bs);
+    kstore<BM, NT>(pa, As, rows);
+    if constexpr (MODE == UP) {
+      kstore<BN, NT>(pb, Bs, BN);
+    } else if constexpr (MODE == DOWN) {
+      kstore<BN, NT>(pb, Bs, nvalid);
     } else {
-      mstore(pm, Bs);
+      mstore<BN, NT>(pm, Bs, BK, nvalid);
     }
   };
 
@@ -332,31 +414,26 @@ __global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
+    const bool odd = kt & 1;
     if (more) load(kt + 1);
-    if (kt & 1)
-      mma_step(acc, As1, Bs1);
-    else
-      mma_step(acc, As0, Bs0);
-    if (more) {
-      if (kt & 1)
-        store(As0, Bs0);
-      else
-        store(As1, Bs1);
-    }
+    mma_step<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0);
+    if (more) store(odd ? As0 : As1, odd ? Bs0 : Bs1);
     __syncthreads();
   }
 
   // epilogue: tile through LDS, then coalesced 16-byte chunks
+  constexpr int LO = C::kOutLd;
   bf16_t* out = lds;
-  stage_out(acc, out);
+  stage_out<BIG>(acc, out);
   __syncthreads();
   if constexpr (MODE == UP) {
-    // LDS columns [0, 64) hold a, [64, 128) hold b for f columns n0 + c
-    for (int v = threadIdx.x; v < BM * 8; v += kThreads) {
-      const int r = v >> 3, c = (v & 7) * 8;
+    // LDS columns [0, BN/2) hold a, [BN/2, BN) hold b for f columns n0 + c
+    constexpr int kChunks = kUpHalf / 8;
+    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
+      const int r = v / kChunks, c = (v % kChunks) * 8;
       if (r >= rows) continue;
-      const uint4 av = *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
-      const uint4 bv = *reinterpret_cast<const uint4*>(out + r * kOutLd + 64 + c);
+      const uint4 av = *reinterpret_cast<const uint4*>(out + r * LO + c);
+      const uint4 bv = *reinterpret_cast<const uint4*>(out + r * LO + kUpHalf + c);
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
       uint32_t hw[4];
 #pragma unroll
@@ -371,10 +448,11 @@ __global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
     }
   } else if constexpr (MODE == DGRAD_DOWN) {
     // dh (rounded) in LDS; da = dh b silu'(a), db = dh silu(a)
-    for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
-      const int r = v >> 4, c = (v & 15) * 8;
+    constexpr int kChunks = BN / 8;
+    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
+      const int r = v / kChunks, c = (v % kChunks) * 8;
       if (r >= rows || c >= nvalid) continue;
-      const uint4 hv = *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+      const uint4 hv = *reinterpret_cast<const uint4*>(out + r * LO + c);
       const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c;
       const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
       const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
@@ -401,11 +479,12 @@ __global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
     }
   } else {
     // DOWN -> y_perm [R][d]; DGRAD_UP -> dx_perm [R][d]
-    for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
-      const int r = v >> 4, c = (v & 15) * 8;
+    constexpr int kChunks = BN / 8;
+    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
+      const int r = v / kChunks, c = (v % kChunks) * 8;
       if (r >= rows || c >= nvalid) continue;
       *reinterpret_cast<uint4*>(g.c0 + static_cast<int64_t>(m0 + r) * d + n0 + c) =
-          *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+          *reinterpret_cast<const uint4*>(out + r * LO + c);
     }
   }
 }
@@ -415,13 +494,16 @@ __global__ __launch_bounds__(kThreads, 2) void rows_kernel(Args g) {
 // 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
 // `splits` contiguous runs; each workgroup writes its fp32 partial tile and
 // wgrad_reduce_kernel adds the runs in order (deterministic split-K).
-__global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(Args g, int32_t tiles_per_expert,
-                                                            int32_t splits, float* partial) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[4 * kTile];
+template <bool BIG>
+__global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void wgrad_kernel(
+    Args g, int32_t tiles_per_expert, int32_t splits, float* partial) {
+  typedef Cfg<BIG> C;
+  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
   bf16_t* As0 = lds;
-  bf16_t* Bs0 = lds + kTile;
-  bf16_t* As1 = lds + 2 * kTile;
-  bf16_t* Bs1 = lds + 3 * kTile;
+  bf16_t* Bs0 = lds + BM * BK;
+  bf16_t* As1 = lds + (BM + BN) * BK;
+  bf16_t* Bs1 = lds + (2 * BM + BN) * BK;
 
   const int flat = flat_tile();
   const int per_z = g.E * tiles_per_expert * splits;
@@ -447,22 +529,21 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(Args g, int32_t tile
   const int kt0 = min(nk_all, sp * per_split);
   const int kt1 = min(nk_all, kt0 + per_split);
 
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  AccT<BIG> acc;
+  zero_acc<BIG>(acc);
 
-  MPart pa, pb;
+  MPart<BM, NT> pa;
+  MPart<BN, NT> pb;
+  int kv_loaded = 0;
   auto load = [&](int kt) {
     const int p = p0 + kt * BK;
-    const int kvalid = min(BK, p1 - p);
-    mload(pa, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kvalid, Mdim - m0);
-    mload(pb, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kvalid, Ndim - n0);
+    kv_loaded = min(BK, p1 - p);
+    mload<BM, NT>(pa, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kv_loaded, Mdim - m0);
+    mload<BN, NT>(pb, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kv_loaded, Ndim - n0);
   };
   auto store = [&](bf16_t* As, bf16_t* Bs) {
-    mstore(pa, As);
-    mstore(pb, Bs);
+    mstore<BM, NT>(pa, As, kv_loaded, Mdim - m0);
+    mstore<BN, NT>(pb, Bs, kv_loaded, Ndim - n0);
   };
 
   if (kt0 < kt1) {
@@ -474,54 +555,41 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_kernel(Args g, int32_t tile
     const bool more = kt + 1 < kt1;
     const bool odd = (kt - kt0) & 1;
     if (more) load(kt + 1);
-    if (odd)
-      mma_step(acc, As1, Bs1);
-    else
-      mma_step(acc, As0, Bs0);
-    if (more) {
-      if (odd)
-        store(As0, Bs0);
-      else
-        store(As1, Bs1);
-    }
+    mma_step<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0);
+    if (more) store(odd ? As0 : As1, odd ? Bs0 : Bs1);
     __syncthreads();
   }
   const int nvalid = min(BN, Ndim - n0), mvalid = min(BM, Mdim - m0);
   if (splits > 1) {
-    // fp32 partial tile [128][128], n contiguous; each lane owns 4 consecutive n
+    // fp32 partial tile [BM][BN], n contiguous; runs of 4 consecutive n per lane
     float* dst = partial + ((static_cast<int64_t>(z) * g.E + e) * tiles_per_expert + t) *
                                static_cast<int64_t>(splits) * (BM * BN) +
                  static_cast<int64_t>(sp) * (BM * BN);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = wm * 64 + i * 16 + (lane & 15);
-        const int n = wn * 64 + j * 16 + (lane >> 4) * 4;
-        *reinterpret_cast<float4*>(dst + m * BN + n) =
-            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      }
+    for_each_quad<BIG>(acc, [&](int m, int n, float a, float b, float c, float dd) {
+      *reinterpret_cast<float4*>(dst + m * BN + n) = make_float4(a, b, c, dd);
+    });
     return;
   }
+  constexpr int LO = C::kOutLd;
   bf16_t* out = lds;
-  stage_out(acc, out);
+  stage_out<BIG>(acc, out);
   __syncthreads();
   bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
-  for (int v = threadIdx.x; v < BM * (BN / 8); v += kThreads) {
-    const int r = v >> 4, c = (v & 15) * 8;
+  constexpr int kChunks = BN / 8;
+  for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
+    const int r = v / kChunks, c = (v % kChunks) * 8;
     if (r >= mvalid || c >= nvalid) continue;
     *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c) =
-        *reinterpret_cast<const uint4*>(out + r * kOutLd + c);
+        *reinterpret_cast<const uint4*>(out + r * LO + c);
   }
 }
 
 // Adds the split-K partial tiles in split order and rounds once to bf16.
-// One thread per 8 consecutive outputs of a tile row.
+// One thread per 8 consecutive outputs of a tile row (small tiles only).
 __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t tiles_per_expert,
                                                                 int32_t splits,
                                                                 const float* partial) {
+  constexpr int BM = Cfg<false>::BM, BN = Cfg<false>::BN;
   const int64_t chunk = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t per_tile = BM * BN / 8;
   const int64_t tile_id = chunk / per_tile;
@@ -557,7 +625,9 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t 
       make_uint4(bf_pack(v[0], v[1]), bf_pack(v[2], v[3]), bf_pack(v[4], v[5]), bf_pack(v[6], v[7]));
 }
 
+template <bool BIG>
 int wgrad_tiles_per_expert(const moe_dims& dm) {
+  constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
   const int tiles = ((dm.d + BM - 1) / BM) * ((dm.f + BN - 1) / BN);
   const int tiles_t = ((dm.f + BM - 1) / BM) * ((dm.d + BN - 1) / BN);
   return std::max(tiles, tiles_t);
@@ -565,20 +635,39 @@ int wgrad_tiles_per_expert(const moe_dims& dm) {
 
 unsigned pad8(int64_t n) { return static_cast<unsigned>((n + kXcd - 1) / kXcd * kXcd); }
 
-template <int MODE>
-hipError_t launch_rows(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
+constexpr int kCUs = 256;
+
+// Big tiles when they alone give at least two workgroups per CU (and, for
+// UP, f splits into 128-column halves); otherwise the small tile.
+bool use_big_rows(const moe_dims& dm, int n_big) {
+  const int64_t R = dm.T * dm.k;
+  return (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
+}
+bool use_big_wgrad(const moe_dims& dm) {
+  return 3LL * dm.E * wgrad_tiles_per_expert<true>(dm) >= 2 * kCUs;
+}
+
+template <int MODE, bool BIG>
+hipError_t launch_rows_cfg(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
   Args g = base;
   g.n_tiles_n = n_tiles_n;
-  const int64_t row_tiles = (R + BM - 1) / BM + E;   // upper bound of sum_e ceil(M_e / BM)
+  const int64_t row_tiles = (R + Cfg<BIG>::BM - 1) / Cfg<BIG>::BM + E;  // >= sum_e ceil(M_e/BM)
   const unsigned grid = pad8(row_tiles * n_tiles_n);
   g.grid_pad = static_cast<int32_t>(grid);
-  hipLaunchKernelGGL(rows_kernel<MODE>, dim3(grid), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((rows_kernel<MODE, BIG>), dim3(grid), dim3(Cfg<BIG>::THREADS), 0, s, g);
   return hipGetLastError();
 }
 
-}  // namespace
+// n_cols: the N extent of the mode (UP: f, covered in halves of BN/2)
+template <int MODE>
+hipError_t launch_rows(const Args& g, const moe_dims& dm, int n_cols, hipStream_t s) {
+  const int64_t R = dm.T * dm.k;
+  const int n_big = (MODE == UP) ? n_cols / 128 : (n_cols + 255) / 256;
+  if (use_big_rows(dm, n_big)) return launch_rows_cfg<MODE, true>(g, R, dm.E, n_big, s);
+  const int n_small = (MODE == UP) ? n_cols / 64 : (n_cols + 127) / 128;
+  return launch_rows_cfg<MODE, false>(g, R, dm.E, n_small, s);
+}
 
-namespace {
 Args base_args(const moe_dims& dm, const int32_t* offsets) {
   Args g{};
   g.offsets = offsets;
@@ -587,6 +676,7 @@ Args base_args(const moe_dims& dm, const int32_t* offsets) {
   g.f = dm.f;
   return g;
 }
+
 }  // namespace
 
 hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
@@ -599,7 +689,7 @@ hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t*
   g.c0 = static_cast<bf16_t*>(a);
   g.c1 = static_cast<bf16_t*>(b);
   g.c2 = static_cast<bf16_t*>(h);
-  return launch_rows<UP>(g, dm.T * dm.k, dm.E, dm.f / 64, s);
+  return launch_rows<UP>(g, dm, dm.f, s);
 }
 
 hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* offsets,
@@ -608,7 +698,7 @@ hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* of
   g.a0 = static_cast<const bf16_t*>(h);
   g.b0 = static_cast<const bf16_t*>(w2);
   g.c0 = static_cast<bf16_t*>(y);
-  return launch_rows<DOWN>(g, dm.T * dm.k, dm.E, (dm.d + BN - 1) / BN, s);
+  return launch_rows<DOWN>(g, dm, dm.d, s);
 }
 
 hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const int32_t* offsets,
@@ -621,7 +711,7 @@ hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const
   g.aux1 = static_cast<const bf16_t*>(b);
   g.c0 = static_cast<bf16_t*>(da);
   g.c1 = static_cast<bf16_t*>(db);
-  return launch_rows<DGRAD_DOWN>(g, dm.T * dm.k, dm.E, (dm.f + BN - 1) / BN, s);
+  return launch_rows<DGRAD_DOWN>(g, dm, dm.f, s);
 }
 
 hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
@@ -633,7 +723,7 @@ hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* 
   g.b0 = static_cast<const bf16_t*>(w1);
   g.b1 = static_cast<const bf16_t*>(w3);
   g.c0 = static_cast<bf16_t*>(dx_perm);
-  return launch_rows<DGRAD_UP>(g, dm.T * dm.k, dm.E, (dm.d + BN - 1) / BN, s);
+  return launch_rows<DGRAD_UP>(g, dm, dm.d, s);
 }
 
 hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
@@ -648,23 +738,34 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   g.c0 = static_cast<bf16_t*>(dw2);
   g.c1 = static_cast<bf16_t*>(dw1);
   g.c2 = static_cast<bf16_t*>(dw3);
-  const int tpe = wgrad_tiles_per_expert(dm);
+  if (use_big_wgrad(dm)) {
+    const int tpe = wgrad_tiles_per_expert<true>(dm);
+    const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+    g.grid_pad = static_cast<int32_t>(grid);
+    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(Cfg<true>::THREADS), 0, s, g, tpe, 1,
+                       partial);
+    return hipGetLastError();
+  }
+  const int tpe = wgrad_tiles_per_expert<false>(dm);
   const int splits = wgrad_splits_bf16(dm);
   const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe * splits);
   g.grid_pad = static_cast<int32_t>(grid);
-  hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kThreads), 0, s, g, tpe, splits, partial);
+  hipLaunchKernelGGL(wgrad_kernel<false>, dim3(grid), dim3(Cfg<false>::THREADS), 0, s, g, tpe,
+                     splits, partial);
   if (splits > 1) {
-    const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (BM * BN / 8);
+    const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (128 * 128 / 8);
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((chunks + kThreads - 1) / kThreads),
                        dim3(kThreads), 0, s, g, tpe, splits, partial);
   }
   return hipGetLastError();
 }
 
-// Split-K count for the weight gradients: enough workgroups to fill the chip
-// (about 4 per CU) when E x tiles alone would not, at most 8.
+// Split-K count for the (small-tile) weight gradients: enough workgroups to
+// fill the chip (about 4 per CU) when E x tiles alone would not, at most 8.
+// Big tiles never split.
 int wgrad_splits_bf16(const moe_dims& dm) {
-  const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert(dm);
+  if (use_big_wgrad(dm)) return 1;
+  const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm);
   const int64_t want = 1024;
   int s = static_cast<int>((want + base - 1) / base);
   return std::max(1, std::min(s, 8));
@@ -673,7 +774,8 @@ int wgrad_splits_bf16(const moe_dims& dm) {
 size_t wgrad_partial_bytes_bf16(const moe_dims& dm) {
   const int s = wgrad_splits_bf16(dm);
   if (s <= 1) return 0;
-  return static_cast<size_t>(3) * dm.E * wgrad_tiles_per_expert(dm) * s * (BM * BN) * sizeof(float);
+  return static_cast<size_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm) * s * (128 * 128) *
+         sizeof(float);
 }
 
 }  // namespace moe

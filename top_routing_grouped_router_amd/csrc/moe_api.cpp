@@ -83,7 +83,11 @@ struct Carver {
   }
 };
 
-int route_tile(int64_t T, int32_t G) {
+// Tokens per router workgroup.  bf16 hidden states use the matrix-core router
+// (64-token tiles) when those tiles never straddle two balancing blocks.
+int route_tile(int64_t T, int32_t G, int32_t act) {
+  if (act == MOE_BF16 && (G <= 1 || (T / G) % moe::kRouteMfmaTile == 0))
+    return moe::kRouteMfmaTile;
   if (G <= 1) return moe::kRouteTileMax;
   const int64_t per = T / G;
   int tile = moe::kRouteTileMax;
@@ -263,7 +267,7 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
                 n_groups, static_cast<long long>(dm.T));
   if (!std::isfinite(near_tie_eps))
     return fail(MOE_ERR_INVALID_ARGUMENT, "%s: near_tie_eps is not finite", __func__);
-  const int tile = route_tile(dm.T, n_groups);
+  const int tile = route_tile(dm.T, n_groups, dm.act);
   const RouteWs need = route_ws(dm, tile, nullptr);
   st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
   if (st != MOE_OK) return st;

@@ -212,6 +212,236 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core router for bf16 hidden states (tiles of 64 tokens).
+//
+// fp32 router weights are split exactly into three bf16 terms, w = hi + mid +
+// lo (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid); each
+// remainder is exact in fp32).  A bf16 x times a bf16 term is exact in fp32,
+// so three v_mfma_f32_16x16x32_bf16 passes into one fp32 accumulator give an
+// fp32-accumulated dot product with the fp32 weights.  The split happens while
+// a 32-wide chunk of Wr is staged into LDS, shared by the 4 wavefronts; each
+// wavefront owns 16 tokens and reads its x fragments straight from HBM, two
+// chunks ahead.  The accumulators leave lane l holding tokens 4(l/16)+q and
+// experts 16j + l%16, so every token's E logits sit in one 16-lane group:
+// top-k, gates, margin and the full softmax run there with 16-lane shuffles.
+// ---------------------------------------------------------------------------
+constexpr int kMTile = 64;       // tokens per workgroup
+constexpr int kMBK = 32;         // k chunk
+constexpr int kMLd = kMBK + 8;   // LDS row stride (elements)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Key group16_argmax(Key k) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) {
+    float v = __shfl_xor(k.v, off, 64);
+    int32_t i = __shfl_xor(k.i, off, 64);
+    if (better(v, i, k.v, k.i)) { k.v = v; k.i = i; }
+  }
+  return k;
+}
+
+__device__ __forceinline__ float group16_sum(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int NT>   // 16-expert tiles: E <= 16 NT
+__global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t wsh[3][16 * NT][kMLd];
+  __shared__ float psum_w[4][16 * NT];
+  __shared__ int32_t pcnt_w[4][16 * NT];
+  __shared__ int32_t tie_w[4];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int E = a.E, d = a.d, k = a.k;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMTile;
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const int nk = d / kMBK;
+
+  // A fragment source: token row t0 + 16 wave + c, k offset 8 g
+  const int64_t my_row = t0 + wave * 16 + c;
+  const bool row_ok = my_row < a.T;
+  const bf16_t* xrow = x + (row_ok ? my_row : 0) * d + g * 8;
+
+  // Wr staging: NT*16 rows x 32 k fp32 = NT*128 float4; split into 3 bf16 terms
+  constexpr int kWVec = NT * 16 * (kMBK / 4);
+  constexpr int kWPer = (kWVec + kThreads - 1) / kThreads;
+  float4 wv[kWPer];
+  auto wload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int v = tid + i * kThreads;
+      const int e = v / (kMBK / 4), q = v % (kMBK / 4);
+      wv[i] = (v < kWVec && e < E)
+                  ? *reinterpret_cast<const float4*>(a.wr + static_cast<int64_t>(e) * d +
+                                                     kt * kMBK + q * 4)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto wstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int v = tid + i * kThreads;
+      if (v >= kWVec) continue;
+      const int e = v / (kMBK / 4), q = v % (kMBK / 4);
+      const float w[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+      uint32_t hi[2], mi[2], lo[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16_t h2[2], m2[2], l2[2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const float f0 = w[2 * u + z];
+          const bf16_t h = f32_to_bf16(f0);
+          const float r1 = f0 - bf16_to_f32(h);
+          const bf16_t m = f32_to_bf16(r1);
+          const float r2 = r1 - bf16_to_f32(m);
+          h2[z] = h;
+          m2[z] = m;
+          l2[z] = f32_to_bf16(r2);
+        }
+        hi[u] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+        mi[u] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+        lo[u] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+      }
+      *reinterpret_cast<uint2*>(&wsh[0][e][q * 4]) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(&wsh[1][e][q * 4]) = make_uint2(mi[0], mi[1]);
+      *reinterpret_cast<uint2*>(&wsh[2][e][q * 4]) = make_uint2(lo[0], lo[1]);
+    }
+  };
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int kAhead = 2;
+  uint4 xa[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i)
+    xa[i] = (row_ok && i < nk) ? *reinterpret_cast<const uint4*>(xrow + i * kMBK)
+                               : make_uint4(0u, 0u, 0u, 0u);
+  wload(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    wstore();
+    __syncthreads();
+    if (kt + 1 < nk) wload(kt + 1);
+    const uint4 cur = xa[0];
+#pragma unroll
+    for (int i = 0; i + 1 < kAhead; ++i) xa[i] = xa[i + 1];
+    xa[kAhead - 1] = (row_ok && kt + kAhead < nk)
+                         ? *reinterpret_cast<const uint4*>(xrow + (kt + kAhead) * kMBK)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&cur);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(&wsh[sp][16 * j + c][g * 8]);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------- per-token epilogue: lane holds tokens 4g+q, experts 16j+c
+  float my_psum[NT];
+  int32_t my_cnt[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) { my_psum[j] = 0.f; my_cnt[j] = 0; }
+  int32_t ties = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tg = t0 + wave * 16 + g * 4 + q;
+    const bool live = tg < a.T;
+    float v[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + c;
+      v[j] = (e < E) ? acc[j][q] : -INFINITY;
+      if (live && e < E) a.logits[tg * E + e] = acc[j][q];
+    }
+    uint32_t taken = 0;
+    float my_v = -INFINITY, v_top = -INFINITY, v_km1 = 0.f, v_k = 0.f;
+    int32_t my_i = 0;
+    const int rounds = (k < E) ? k + 1 : k;
+    for (int r = 0; r < rounds; ++r) {
+      Key best{-INFINITY, 0x7fffffff};
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int e = 16 * j + c;
+        if (e < E && !(taken & (1u << j)) && better(v[j], e, best.v, best.i)) {
+          best.v = v[j];
+          best.i = e;
+        }
+      }
+      best = group16_argmax(best);
+      if (r == 0) v_top = best.v;
+      if (r == k - 1) v_km1 = best.v;
+      if (r == k) v_k = best.v;
+      if (c == r) { my_v = best.v; my_i = best.i; }
+      if (r < k && (best.i & 15) == c) taken |= 1u << (best.i >> 4);
+    }
+    float ex[NT];
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + c;
+      ex[j] = (e < E) ? __expf(v[j] - v_top) : 0.f;
+      part += ex[j];
+    }
+    const float inv = 1.0f / group16_sum(part);
+    const float my_e = (c < k) ? __expf(my_v - v_top) : 0.f;
+    const float z = group16_sum(my_e);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        my_psum[j] += ex[j] * inv;
+        if (taken & (1u << j)) my_cnt[j] += 1;
+      }
+      if (c < k) {
+        a.idx[tg * k + c] = my_i;
+        a.gate[tg * k + c] = my_e / z;
+      }
+      const float m = (k < E) ? v_km1 - v_k : INFINITY;
+      if (c == 0) {
+        a.margin[tg] = m;
+        ties += (m < a.eps) ? 1 : 0;
+      }
+    }
+  }
+  // fold the 4 lane groups (fixed xor order), then the 4 waves (fixed order)
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    float s = my_psum[j];
+    int32_t n = my_cnt[j];
+    s += __shfl_xor(s, 16, 64);
+    n += __shfl_xor(n, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    n += __shfl_xor(n, 32, 64);
+    if (g == 0) {
+      psum_w[wave][16 * j + c] = s;
+      pcnt_w[wave][16 * j + c] = n;
+    }
+  }
+  ties += __shfl_xor(ties, 16, 64);
+  ties += __shfl_xor(ties, 32, 64);
+  if (lane == 0) tie_w[wave] = ties;
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
+    const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
+    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
+    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = n;
+  }
+  if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+}
+
 // One workgroup per balancing block r (grid G).  Per pass, 16 experts x 16
 // tile slices: thread (slice, e) sums tiles slice, slice + 16, ... of block r,
 // then the 16 slice sums are added in slice order.  Block 0 also totals the
@@ -289,10 +519,25 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
   if (n_tiles > 0) {
     RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie,
                 dm.T, dm.d, dm.E, dm.k, tile, eps};
-    if (dm.act == MOE_BF16)
+    if (tile == kRouteMfmaTile) {
+      const int nt = (dm.E + 15) / 16;
+#define MOE_RM(N)                                                                        \
+  case N:                                                                                \
+    hipLaunchKernelGGL(route_mfma_kernel<N>, dim3(n_tiles), dim3(kThreads), 0, s, a);    \
+    break;
+      switch (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16) {
+        MOE_RM(1)
+        MOE_RM(2)
+        MOE_RM(4)
+        MOE_RM(8)
+        default: MOE_RM(16)
+      }
+#undef MOE_RM
+    } else if (dm.act == MOE_BF16) {
       hipLaunchKernelGGL(route_kernel<bf16_t>, dim3(n_tiles), dim3(kThreads), 0, s, a);
-    else
+    } else {
       hipLaunchKernelGGL(route_kernel<float>, dim3(n_tiles), dim3(kThreads), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
