@@ -215,12 +215,15 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
   __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
+    // five independent clamped loads (offsets[E] repeats past the end, so
+    // those experts count zero rows): one memory latency, no branches
+    int o[5];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) o[s] = offsets[min(lane * 4 + s, E)];
     int tiles[4], sum = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int e = lane * 4 + s;
-      const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-      tiles[s] = (cnt + BM - 1) / BM;
+      tiles[s] = (o[s + 1] - o[s] + BM - 1) / BM;
       sum += tiles[s];
     }
     int incl = sum;
@@ -238,8 +241,8 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
         if (rem >= 0 && rem < tiles[s]) {
           const int e = lane * 4 + s;
           s_e = e;
-          s_m0 = offsets[e] + rem * BM;
-          s_mend = offsets[e + 1];
+          s_m0 = o[s] + rem * BM;
+          s_mend = o[s + 1];
         }
         rem -= tiles[s];
       }

@@ -204,13 +204,14 @@ using AccT = f32x16[Cfg<BIG>::FM][Cfg<BIG>::FN];
 // fragment is the first MFMA source, so lane l ends up owning
 // C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16 of each fragment.
 template <bool BIG>
-__device__ __forceinline__ void mma_step(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs) {
+__device__ __forceinline__ void mma_substeps(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
+                                             int kk0, int kk1) {
   typedef Cfg<BIG> C;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int r = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int kk = 0; kk < BK / 8; kk += 2) {
+  for (int kk = kk0; kk < kk1; kk += 2) {
     const int chunk = kk + g;
     bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
@@ -224,6 +225,70 @@ __device__ __forceinline__ void mma_step(AccT<BIG>& acc, const bf16_t* As, const
 #pragma unroll
       for (int j = 0; j < C::FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One K step (64 = 4 x k16) of the wavefront's FM x FN fragments.  The B
+// fragment is the first MFMA source, so lane l ends up owning
+// C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16 of each fragment.
+// The step runs in two halves so that LDS stores of the next step can sit
+// between them.
+template <bool BIG>
+__device__ __forceinline__ void mma_half(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
+                                         int half) {
+  if (half == 0)
+    mma_substeps<BIG>(acc, As, Bs, 0, 4);
+  else
+    mma_substeps<BIG>(acc, As, Bs, 4, 8);
+}
+
+// Software pipeline shared by the kernels: operand data for step j is loaded
+// into register set j & 1 two steps ahead, stored to LDS buffer j & 1 during
+// step j - 1 (between its two halves), and consumed at step j.  One barrier
+// per step.  `load(kt, set)` and `store(set, buf)` are the kernel's staging.
+template <bool BIG, bool TWO_SETS, typename Load, typename Store>
+__device__ __forceinline__ void run_pipeline(AccT<BIG>& acc, bf16_t* lds, int kt0, int nk,
+                                             Load&& load, Store&& store) {
+  constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
+  bf16_t* As[2] = {lds, lds + (BM + BN) * BK};
+  bf16_t* Bs[2] = {lds + BM * BK, lds + (2 * BM + BN) * BK};
+  if (nk <= 0) return;
+  if constexpr (!TWO_SETS) {
+    // Without registers for a second staging set, loads for step j + 1 are
+    // issued before step j's MFMAs and stored after them.
+    load(kt0, 0);
+    store(0, As[0], Bs[0]);
+    __syncthreads();
+    for (int j = 0; j < nk; ++j) {
+      const int cur = j & 1;
+      if (j + 1 < nk) load(kt0 + j + 1, 0);
+      mma_substeps<BIG>(acc, cur ? As[1] : As[0], cur ? Bs[1] : Bs[0], 0, BK / 8);
+      if (j + 1 < nk) store(0, cur ? As[0] : As[1], cur ? Bs[0] : Bs[1]);
+      __syncthreads();
+    }
+    return;
+  }
+  // Loads are unconditional (a step past the end reloads the last one) so
+  // that the wait before each store covers only the older register set.
+  const int last = kt0 + nk - 1;
+  load(kt0, 0);
+  load(min(kt0 + 1, last), 1);
+  store(0, As[0], Bs[0]);
+  __syncthreads();
+  for (int j = 0; j < nk; j += 2) {
+    // step j (buffer 0); set 0 is free: load step j + 2 into it
+    load(min(kt0 + j + 2, last), 0);
+    mma_half<BIG>(acc, As[0], Bs[0], 0);
+    if (j + 1 < nk) store(1, As[1], Bs[1]);
+    mma_half<BIG>(acc, As[0], Bs[0], 1);
+    __syncthreads();
+    if (j + 1 >= nk) break;
+    // step j + 1 (buffer 1); set 1 is free: load step j + 3 into it
+    load(min(kt0 + j + 3, last), 1);
+    mma_half<BIG>(acc, As[1], Bs[1], 0);
+    if (j + 2 < nk) store(0, As[0], Bs[0]);
+    mma_half<BIG>(acc, As[1], Bs[1], 1);
+    __syncthreads();
   }
 }
 
@@ -287,12 +352,15 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
   __syncthreads();
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
+    // five independent clamped loads (offsets[E] repeats past the end, so
+    // those experts count zero rows): one memory latency, no branches
+    int o[5];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) o[s] = offsets[min(lane * 4 + s, E)];
     int tiles[4], sum = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int e = lane * 4 + s;
-      const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-      tiles[s] = (cnt + BM - 1) / BM;
+      tiles[s] = (o[s + 1] - o[s] + BM - 1) / BM;
       sum += tiles[s];
     }
     int incl = sum;
@@ -309,8 +377,8 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
         if (rem >= 0 && rem < tiles[s]) {
           const int e = lane * 4 + s;
           s_e = e;
-          s_m0 = offsets[e] + rem * BM;
-          s_mend = offsets[e + 1];
+          s_m0 = o[s] + rem * BM;
+          s_mend = o[s + 1];
         }
         rem -= tiles[s];
       }
@@ -336,10 +404,6 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   typedef Cfg<BIG> C;
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
-  bf16_t* As0 = lds;
-  bf16_t* Bs0 = lds + BM * BK;
-  bf16_t* As1 = lds + (BM + BN) * BK;
-  bf16_t* Bs1 = lds + (2 * BM + BN) * BK;
 
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
@@ -366,11 +430,11 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   AccT<BIG> acc;
   zero_acc<BIG>(acc);
 
-  KPart<BM, NT> pa;
-  KPart<BN, NT> pb;   // k-contiguous B (UP, DOWN)
-  MPart<BN, NT> pm;   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
+  KPart<BM, NT> pa[2];
+  KPart<BN, NT> pb[2];   // k-contiguous B (UP, DOWN)
+  MPart<BN, NT> pm[2];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
 
-  auto load = [&](int kt) {
+  auto load = [&](int kt, int set) {
     int k0 = kt * BK;
     int half = 0;
     if (MODE == DGRAD_UP && k0 >= f) {
@@ -378,48 +442,45 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
       k0 -= f;
     }
     const bf16_t* ab = a_row(half);
-    kload<BM, NT>(pa, [&](int r) { return ab + static_cast<int64_t>(r) * lda; }, rows, k0);
+    auto a_ptr = [&](int r) { return ab + static_cast<int64_t>(r) * lda; };
+    if (set) kload<BM, NT>(pa[1], a_ptr, rows, k0); else kload<BM, NT>(pa[0], a_ptr, rows, k0);
     if constexpr (MODE == UP) {
       const bf16_t* w1 = g.b0 + e * E_fd;
       const bf16_t* w3 = g.b1 + e * E_fd;
-      kload<BN, NT>(pb, [&](int r) {
+      auto b_ptr = [&](int r) {
         return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
                             : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
-      }, BN, k0);
+      };
+      if (set) kload<BN, NT>(pb[1], b_ptr, BN, k0); else kload<BN, NT>(pb[0], b_ptr, BN, k0);
     } else if constexpr (MODE == DOWN) {
       const bf16_t* w2 = g.b0 + e * E_fd;
-      kload<BN, NT>(pb, [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; }, nvalid, k0);
+      auto b_ptr = [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; };
+      if (set) kload<BN, NT>(pb[1], b_ptr, nvalid, k0); else kload<BN, NT>(pb[0], b_ptr, nvalid, k0);
     } else if constexpr (MODE == DGRAD_DOWN) {
       // W2[e] is [d][f]: element (k, n) at k * f + n
-      mload<BN, NT>(pm, g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0, f, BK, nvalid);
+      const bf16_t* base = g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0;
+      if (set) mload<BN, NT>(pm[1], base, f, BK, nvalid); else mload<BN, NT>(pm[0], base, f, BK, nvalid);
     } else {
       // W1/W3[e] are [f][d]: element (k, n) at k * d + n
-      const bf16_t* w = (half ? g.b1 : g.b0) + e * E_fd;
-      mload<BN, NT>(pm, w + static_cast<int64_t>(k0) * d + n0, d, BK, nvalid);
+      const bf16_t* base = (half ? g.b1 : g.b0) + e * E_fd + static_cast<int64_t>(k0) * d + n0;
+      if (set) mload<BN, NT>(pm[1], base, d, BK, nvalid); else mload<BN, NT>(pm[0], base, d, BK, nvalid);
     }
   };
-  auto store = [&](bf16_t* As, bf16_t* Bs) {
-    kstore<BM, NT>(pa, As, rows);
+  auto store_set = [&](const KPart<BM, NT>& a, const KPart<BN, NT>& b, const MPart<BN, NT>& m,
+                       bf16_t* As, bf16_t* Bs) {
+    kstore<BM, NT>(a, As, rows);
     if constexpr (MODE == UP) {
-      kstore<BN, NT>(pb, Bs, BN);
+      kstore<BN, NT>(b, Bs, BN);
     } else if constexpr (MODE == DOWN) {
-      kstore<BN, NT>(pb, Bs, nvalid);
+      kstore<BN, NT>(b, Bs, nvalid);
     } else {
-      mstore<BN, NT>(pm, Bs, BK, nvalid);
+      mstore<BN, NT>(m, Bs, BK, nvalid);
     }
   };
-
-  load(0);
-  store(As0, Bs0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    const bool odd = kt & 1;
-    if (more) load(kt + 1);
-    mma_step<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0);
-    if (more) store(odd ? As0 : As1, odd ? Bs0 : Bs1);
-    __syncthreads();
-  }
+  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
+    if (set) store_set(pa[1], pb[1], pm[1], As, Bs); else store_set(pa[0], pb[0], pm[0], As, Bs);
+  };
+  run_pipeline<BIG, !BIG && (MODE == UP || MODE == DOWN)>(acc, lds, 0, nk, load, store);
 
   // epilogue: tile through LDS, then coalesced 16-byte chunks
   constexpr int LO = C::kOutLd;
@@ -500,10 +561,6 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void wgrad_kernel(
   typedef Cfg<BIG> C;
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
-  bf16_t* As0 = lds;
-  bf16_t* Bs0 = lds + BM * BK;
-  bf16_t* As1 = lds + (BM + BN) * BK;
-  bf16_t* Bs1 = lds + (2 * BM + BN) * BK;
 
   const int flat = flat_tile();
   const int per_z = g.E * tiles_per_expert * splits;
@@ -532,33 +589,34 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void wgrad_kernel(
   AccT<BIG> acc;
   zero_acc<BIG>(acc);
 
-  MPart<BM, NT> pa;
-  MPart<BN, NT> pb;
-  int kv_loaded = 0;
-  auto load = [&](int kt) {
+  MPart<BM, NT> pa[2];
+  MPart<BN, NT> pb[2];
+  int kv[2] = {0, 0};
+  auto load = [&](int kt, int set) {
     const int p = p0 + kt * BK;
-    kv_loaded = min(BK, p1 - p);
-    mload<BM, NT>(pa, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kv_loaded, Mdim - m0);
-    mload<BN, NT>(pb, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kv_loaded, Ndim - n0);
+    const int kvalid = min(BK, p1 - p);
+    const bf16_t* a = Asrc + static_cast<int64_t>(p) * Mdim + m0;
+    const bf16_t* b = Bsrc + static_cast<int64_t>(p) * Ndim + n0;
+    if (set) {
+      kv[1] = kvalid;
+      mload<BM, NT>(pa[1], a, Mdim, kvalid, Mdim - m0);
+      mload<BN, NT>(pb[1], b, Ndim, kvalid, Ndim - n0);
+    } else {
+      kv[0] = kvalid;
+      mload<BM, NT>(pa[0], a, Mdim, kvalid, Mdim - m0);
+      mload<BN, NT>(pb[0], b, Ndim, kvalid, Ndim - n0);
+    }
   };
-  auto store = [&](bf16_t* As, bf16_t* Bs) {
-    mstore<BM, NT>(pa, As, kv_loaded, Mdim - m0);
-    mstore<BN, NT>(pb, Bs, kv_loaded, Ndim - n0);
+  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
+    if (set) {
+      mstore<BM, NT>(pa[1], As, kv[1], Mdim - m0);
+      mstore<BN, NT>(pb[1], Bs, kv[1], Ndim - n0);
+    } else {
+      mstore<BM, NT>(pa[0], As, kv[0], Mdim - m0);
+      mstore<BN, NT>(pb[0], Bs, kv[0], Ndim - n0);
+    }
   };
-
-  if (kt0 < kt1) {
-    load(kt0);
-    store(As0, Bs0);
-  }
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const bool more = kt + 1 < kt1;
-    const bool odd = (kt - kt0) & 1;
-    if (more) load(kt + 1);
-    mma_step<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0);
-    if (more) store(odd ? As0 : As1, odd ? Bs0 : Bs1);
-    __syncthreads();
-  }
+  run_pipeline<BIG, !BIG>(acc, lds, kt0, kt1 - kt0, load, store);
   const int nvalid = min(BN, Ndim - n0), mvalid = min(BM, Mdim - m0);
   if (splits > 1) {
     // fp32 partial tile [BM][BN], n contiguous; runs of 4 consecutive n per lane
