@@ -200,9 +200,12 @@ __device__ __forceinline__ void mstore(const MPart<COLS, NT>& p, bf16_t* lds, in
 template <bool BIG>
 using AccT = f32x16[Cfg<BIG>::FM][Cfg<BIG>::FN];
 
-// One K step (64 = 4 x k16) of the wavefront's FM x FN fragments.  The B
-// fragment is the first MFMA source, so lane l ends up owning
-// C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16 of each fragment.
+// K sub-steps [kk0, kk1) (16-wide pairs of chunks) of the wavefront's FM x FN
+// fragments.  Fragment (i, j) of wavefront (wm, wn) covers tile rows
+// wm 32 FM + 32 i + [0, 32) and columns j (BN / FN) + 32 wn + [0, 32), so the
+// FN fragments of a lane sit BN / FN columns apart (in UP: a and b of the same
+// f column).  The B fragment is the first MFMA source, so lane l ends up
+// owning C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16, of each.
 template <bool BIG>
 __device__ __forceinline__ void mma_substeps(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
                                              int kk0, int kk1) {
@@ -219,7 +222,7 @@ __device__ __forceinline__ void mma_substeps(AccT<BIG>& acc, const bf16_t* As, c
       af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 32 * C::FM + i * 32 + r, chunk));
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(wn * 32 * C::FN + j * 32 + r, chunk));
+      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(j * (C::BN / C::FN) + wn * 32 + r, chunk));
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -228,11 +231,8 @@ __device__ __forceinline__ void mma_substeps(AccT<BIG>& acc, const bf16_t* As, c
   }
 }
 
-// One K step (64 = 4 x k16) of the wavefront's FM x FN fragments.  The B
-// fragment is the first MFMA source, so lane l ends up owning
-// C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16 of each fragment.
-// The step runs in two halves so that LDS stores of the next step can sit
-// between them.
+// One K step (64 = 4 x k16) in two halves, so that LDS stores of the next step
+// can sit between them.
 template <bool BIG>
 __device__ __forceinline__ void mma_half(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
                                          int half) {
@@ -320,7 +320,7 @@ __device__ __forceinline__ void for_each_quad(const AccT<BIG>& acc, F&& fn) {
       const int m = wm * 32 * C::FM + i * 32 + (lane & 31);
 #pragma unroll
       for (int vb = 0; vb < 4; ++vb) {
-        const int n = wn * 32 * C::FN + j * 32 + vb * 8 + (lane >> 5) * 4;
+        const int n = j * (C::BN / C::FN) + wn * 32 + vb * 8 + (lane >> 5) * 4;
         fn(m, n, acc[i][j][4 * vb], acc[i][j][4 * vb + 1], acc[i][j][4 * vb + 2],
            acc[i][j][4 * vb + 3]);
       }
@@ -337,8 +337,333 @@ __device__ __forceinline__ void stage_out(const AccT<BIG>& acc, bf16_t* out) {
 
 // ------------------------------------------------------------------ tile lookup
 __device__ __forceinline__ int flat_tile() {
-  const int per = gridDim.x / kXcd;            // grid_pad is a multiple of 8
+  const int per = gridDim.x / kXcd;            // the grid is a multiple of 8
   return (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Work list of a persistent row-mode workgroup.  Row tiles are BM rows of one
+// expert (ceil(M_e / BM) per expert, in expert order); item it is (row tile
+// it / n_tiles_n, column tile it % n_tiles_n).  The workgroup with remapped
+// index flat takes items flat, flat + G, flat + 2 G, ... (G workgroups), so
+// each round of G items is one contiguous run, cut into one contiguous slice
+// per XCD: a row tile's column tiles share that XCD's L2.
+constexpr int kMaxItems = 64;
+struct RowSched {
+  int32_t pref[257];     // row tiles of the experts before e
+  int32_t off[257];      // expert row offsets
+  int4 desc[kMaxItems];  // expert, first row, end row of the expert, column tile
+};
+
+// Builds the prefix of row tiles per expert (wavefront 0: five independent
+// clamped loads per lane, then a lane scan) and the workgroup's item table.
+// Returns the number of items (the host sizes the grid so that it is at most
+// kMaxItems).
+template <int BM, int NT>
+__device__ int build_row_sched(RowSched& S, const int32_t* offsets, int E, int ntn) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int o[5];
+#pragma unroll
+    for (int s = 0; s < 5; ++s) o[s] = offsets[min(lane * 4 + s, E)];
+    int tiles[4], sum = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      tiles[s] = (o[s + 1] - o[s] + BM - 1) / BM;
+      sum += tiles[s];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int run = incl - sum;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = lane * 4 + s;
+      if (e <= E) {
+        S.pref[e] = run;
+        S.off[e] = o[s];
+      }
+      run += tiles[s];
+    }
+    if (lane == 63 && E == 256) {
+      S.pref[256] = incl;
+      S.off[256] = o[4];
+    }
+  }
+  __syncthreads();
+  const int G = gridDim.x, flat = flat_tile();
+  const int total = S.pref[E] * ntn;
+  const int n = flat < total ? min((total - flat + G - 1) / G, kMaxItems) : 0;
+  for (int t = threadIdx.x; t < n; t += NT) {
+    const int it = flat + t * G;
+    const int rt = it / ntn, nt = it - rt * ntn;
+    int lo = 0, hi = E - 1;   // first expert e with pref[e + 1] > rt
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (S.pref[mid + 1] > rt) hi = mid; else lo = mid + 1;
+    }
+    S.desc[t] = make_int4(lo, S.off[lo] + (rt - S.pref[lo]) * BM, S.off[lo + 1], nt);
+  }
+  __syncthreads();
+  return n;
+}
+
+// Persistent software pipeline over a workgroup's items of nk K steps each.
+// The flattened step sequence runs without a break across items: loads for the
+// next item's first steps are in flight while the current item finishes and
+// its epilogue runs.  TWO_SETS: operand data for step j is loaded into
+// register set j & 1 two steps ahead and stored to LDS buffer j & 1 during
+// step j - 1, between its two halves.  One set: loads for step j + 1 are
+// issued before step j's MFMAs and stored after them.  Loads never branch (a
+// step past the end reloads the last one), so the wait before a store covers
+// only the older register set.  One barrier per step.
+//   load(item, kt, set); store(set, As, Bs); epilogue(item, buf) may use the
+//   LDS buffer that step just consumed (it ends with a barrier); the
+//   accumulators are then cleared.
+template <bool BIG, bool TWO_SETS, typename Load, typename Store, typename Epi>
+__device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_items, int nk,
+                                           Load&& load, Store&& store, Epi&& epilogue) {
+  constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
+  bf16_t* const As0 = lds;
+  bf16_t* const Bs0 = lds + BM * BK;
+  bf16_t* const As1 = lds + (BM + BN) * BK;
+  bf16_t* const Bs1 = lds + (2 * BM + BN) * BK;
+  const int S = n_items * nk;
+  int li = 0, lk = 0;   // load cursor
+  auto next_load = [&](int set) {
+    load(li, lk, set);
+    if (++lk == nk) {
+      if (li + 1 < n_items) {
+        ++li;
+        lk = 0;
+      } else {
+        lk = nk - 1;
+      }
+    }
+  };
+  int ci = 0, ck = 0;   // compute cursor
+  auto finish_step = [&](bf16_t* consumed) {
+    if (++ck == nk) {
+      epilogue(ci, consumed);
+      zero_acc<BIG>(acc);
+      ck = 0;
+      ++ci;
+    }
+  };
+  if constexpr (TWO_SETS) {
+    next_load(0);
+    next_load(1);
+    store(0, As0, Bs0);
+    __syncthreads();
+    for (int j = 0; j < S; j += 2) {
+      next_load(0);
+      mma_half<BIG>(acc, As0, Bs0, 0);
+      if (j + 1 < S) store(1, As1, Bs1);
+      mma_half<BIG>(acc, As0, Bs0, 1);
+      __syncthreads();
+      finish_step(As0);
+      if (j + 1 >= S) break;
+      next_load(1);
+      mma_half<BIG>(acc, As1, Bs1, 0);
+      if (j + 2 < S) store(0, As0, Bs0);
+      mma_half<BIG>(acc, As1, Bs1, 1);
+      __syncthreads();
+      finish_step(As1);
+    }
+  } else {
+    next_load(0);
+    store(0, As0, Bs0);
+    __syncthreads();
+    for (int j = 0; j < S; ++j) {
+      const bool odd = j & 1;
+      if (j + 1 < S) next_load(0);
+      mma_substeps<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0, 0, BK / 8);
+      if (j + 1 < S) store(0, odd ? As0 : As1, odd ? Bs0 : Bs1);
+      __syncthreads();
+      finish_step(odd ? As1 : As0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+// Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP), persistent: G workgroups
+// (at most what is resident at once) each run their item list.
+template <int MODE, bool BIG>
+__global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
+  typedef Cfg<BIG> C;
+  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
+  __shared__ RowSched sched;
+
+  const int n_items = build_row_sched<BM, NT>(sched, g.offsets, g.E, g.n_tiles_n);
+  if (n_items == 0) return;
+  const int d = g.d, f = g.f;
+  // UP covers BN/2 f columns of a and the same BN/2 of b per tile
+  constexpr int kUpHalf = BN / 2;
+  const int Ndim = (MODE == DOWN || MODE == DGRAD_UP) ? d : f;
+  const int K = (MODE == UP || MODE == DGRAD_DOWN) ? d : (MODE == DOWN ? f : 2 * f);
+  const int nk = K / BK;
+  const int64_t E_fd = static_cast<int64_t>(f) * d;
+  const int lda = (MODE == UP || MODE == DGRAD_DOWN) ? d : f;
+
+  AccT<BIG> acc;
+  zero_acc<BIG>(acc);
+
+  KPart<BM, NT> pa[2];
+  KPart<BN, NT> pb[2];   // k-contiguous B (UP, DOWN)
+  MPart<BN, NT> pm[2];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
+  int rows_s[2], nval_s[2];
+
+  auto load = [&](int item, int kt, int set) {
+    const int4 ds = sched.desc[item];
+    const int e = ds.x, m0 = ds.y;
+    const int rows = min(BM, ds.z - m0);
+    const int n0 = ds.w * ((MODE == UP) ? kUpHalf : BN);
+    const int nvalid = (MODE == UP) ? BN : min(BN, Ndim - n0);
+    rows_s[set] = rows;
+    nval_s[set] = nvalid;
+    int k0 = kt * BK;
+    int half = 0;
+    if (MODE == DGRAD_UP && k0 >= f) {
+      half = 1;
+      k0 -= f;
+    }
+    const bf16_t* ab = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) + static_cast<int64_t>(m0) * lda;
+    auto a_ptr = [&](int r) { return ab + static_cast<int64_t>(r) * lda; };
+    if (set) kload<BM, NT>(pa[1], a_ptr, rows, k0); else kload<BM, NT>(pa[0], a_ptr, rows, k0);
+    if constexpr (MODE == UP) {
+      const bf16_t* w1 = g.b0 + e * E_fd;
+      const bf16_t* w3 = g.b1 + e * E_fd;
+      auto b_ptr = [&](int r) {
+        return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
+                            : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
+      };
+      if (set) kload<BN, NT>(pb[1], b_ptr, BN, k0); else kload<BN, NT>(pb[0], b_ptr, BN, k0);
+    } else if constexpr (MODE == DOWN) {
+      const bf16_t* w2 = g.b0 + e * E_fd;
+      auto b_ptr = [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; };
+      if (set) kload<BN, NT>(pb[1], b_ptr, nvalid, k0); else kload<BN, NT>(pb[0], b_ptr, nvalid, k0);
+    } else if constexpr (MODE == DGRAD_DOWN) {
+      // W2[e] is [d][f]: element (k, n) at k * f + n
+      const bf16_t* base = g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0;
+      if (set) mload<BN, NT>(pm[1], base, f, BK, nvalid); else mload<BN, NT>(pm[0], base, f, BK, nvalid);
+    } else {
+      // W1/W3[e] are [f][d]: element (k, n) at k * d + n
+      const bf16_t* base = (half ? g.b1 : g.b0) + e * E_fd + static_cast<int64_t>(k0) * d + n0;
+      if (set) mload<BN, NT>(pm[1], base, d, BK, nvalid); else mload<BN, NT>(pm[0], base, d, BK, nvalid);
+    }
+  };
+  auto store_set = [&](const KPart<BM, NT>& a, const KPart<BN, NT>& b, const MPart<BN, NT>& m,
+                       int rows, int nvalid, bf16_t* As, bf16_t* Bs) {
+    kstore<BM, NT>(a, As, rows);
+    if constexpr (MODE == UP) {
+      kstore<BN, NT>(b, Bs, BN);
+    } else if constexpr (MODE == DOWN) {
+      kstore<BN, NT>(b, Bs, nvalid);
+    } else {
+      mstore<BN, NT>(m, Bs, BK, nvalid);
+    }
+  };
+  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
+    if (set) store_set(pa[1], pb[1], pm[1], rows_s[1], nval_s[1], As, Bs);
+    else store_set(pa[0], pb[0], pm[0], rows_s[0], nval_s[0], As, Bs);
+  };
+
+  // Epilogue through the LDS buffer the last step consumed (free until the
+  // next store into it; the final barrier keeps it so): the accumulators are
+  // rounded to bf16 and staged SR rows at a time as [SR][BN] with 16-byte
+  // chunks XOR-swizzled by row, then read back as whole rows and written in
+  // coalesced 16-byte chunks with the mode's elementwise work applied.
+  constexpr int SR = (BM + BN) * BK / BN;   // rows per pass: 128 in both configs
+  constexpr int CH = BN / 8;                // 16-byte chunks per staged row
+  auto epilogue = [&](int item, bf16_t* buf) {
+    const int4 ds = sched.desc[item];
+    const int m0 = ds.y, rows = min(BM, ds.z - m0);
+    // The row swizzle key (r & 15 = lane & 15 for every fragment) goes through
+    // an opaque move so that the staging addresses are formed here rather
+    // than hoisted out of the step loop into registers held across it.
+    int key;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(key) : "v"(static_cast<int>(threadIdx.x & 15)));
+#pragma unroll
+    for (int p = 0; p < BM / SR; ++p) {
+      for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+        if (m / SR != p) return;   // wavefront-uniform
+        const int r = m - p * SR;
+        *reinterpret_cast<uint2*>(buf + r * BN + (((n >> 3) ^ key) << 3) + (n & 4)) =
+            pack4(v0, v1, v2, v3);
+      });
+      __syncthreads();
+      auto chunk = [&](int r, int c) {
+        return *reinterpret_cast<const uint4*>(buf + r * BN + ((c ^ (r & 15)) << 3));
+      };
+      if constexpr (MODE == UP) {
+        // staged columns [0, BN/2) hold a, [BN/2, BN) hold b of f columns n0 + c
+        constexpr int kCh = kUpHalf / 8;
+#pragma unroll(BIG ? 1 : 4)
+        for (int v = threadIdx.x; v < SR * kCh; v += NT) {
+          const int r = v / kCh, c = v % kCh;
+          if (p * SR + r >= rows) continue;
+          const uint4 av = chunk(r, c), bv = chunk(r, c + kCh);
+          const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+          uint32_t hw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+          const int64_t o = static_cast<int64_t>(m0 + p * SR + r) * f + ds.w * kUpHalf + c * 8;
+          *reinterpret_cast<uint4*>(g.c0 + o) = av;
+          *reinterpret_cast<uint4*>(g.c1 + o) = bv;
+          *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+      } else {
+        const int n0 = ds.w * BN;
+        const int nch = min(BN, Ndim - n0) / 8;
+#pragma unroll(BIG ? 1 : 4)
+        for (int v = threadIdx.x; v < SR * CH; v += NT) {
+          const int r = v / CH, c = v % CH;
+          if (p * SR + r >= rows || c >= nch) continue;
+          const uint4 hv = chunk(r, c);
+          const int64_t o = static_cast<int64_t>(m0 + p * SR + r) * Ndim + n0 + c * 8;
+          if constexpr (MODE == DGRAD_DOWN) {
+            // dh (rounded); da = dh b silu'(a), db = dh silu(a)
+            const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
+            const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
+            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+            uint32_t daw[4], dbw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float da2[2], db2[2];
+              const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
+              const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+              const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+              for (int u = 0; u < 2; ++u) {
+                const float sg = sigmoid_f(aa[u]);
+                da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+                db2[u] = hh[u] * (aa[u] * sg);
+              }
+              daw[q] = bf_pack(da2[0], da2[1]);
+              dbw[q] = bf_pack(db2[0], db2[1]);
+            }
+            *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+            *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+          } else {
+            *reinterpret_cast<uint4*>(g.c0 + o) = hv;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  };
+  run_stream<BIG, !BIG>(acc, lds, n_items, nk, load, store, epilogue);
 }
 
 // expert and first row of row tile `tile` (tiles of BM rows; prefix sum of
@@ -391,16 +716,12 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
   return s_e >= 0;
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
-}
-
-// ------------------------------------------------------------------ kernels
-// Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP).
-template <int MODE, bool BIG>
-__global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
+// Row-split modes with the big tile, one tile per workgroup (long K: the
+// tile's own K loop hides the ramp, and the epilogue can stage the whole tile
+// through LDS).
+template <int MODE>
+__global__ __launch_bounds__(Cfg<true>::THREADS, 2) void tile_rows_kernel(Args g) {
+  constexpr bool BIG = true;
   typedef Cfg<BIG> C;
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
   __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
@@ -695,35 +1016,54 @@ unsigned pad8(int64_t n) { return static_cast<unsigned>((n + kXcd - 1) / kXcd * 
 
 constexpr int kCUs = 256;
 
-// Big tiles when they alone give at least two workgroups per CU (and, for
-// UP, f splits into 128-column halves); otherwise the small tile.
-bool use_big_rows(const moe_dims& dm, int n_big) {
+// Big tiles for long reductions (K >= 1024: the matrix cores, not the memory
+// ramp, bound the tile) when they alone give at least two workgroups per CU
+// (and, for UP, f splits into 128-column halves); otherwise the small tile.
+bool use_big_rows(const moe_dims& dm, int n_big, int K) {
   const int64_t R = dm.T * dm.k;
-  return (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
+  return K >= 1024 && (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
 }
 bool use_big_wgrad(const moe_dims& dm) {
   return 3LL * dm.E * wgrad_tiles_per_expert<true>(dm) >= 2 * kCUs;
 }
 
-template <int MODE, bool BIG>
-hipError_t launch_rows_cfg(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
+// Small tile: persistent grid of the workgroups resident at once (two per
+// CU), fewer when there are fewer items, more when a workgroup would otherwise
+// hold over kMaxItems of them.  Big tile: one workgroup per tile.
+template <int MODE>
+hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
   Args g = base;
   g.n_tiles_n = n_tiles_n;
-  const int64_t row_tiles = (R + Cfg<BIG>::BM - 1) / Cfg<BIG>::BM + E;  // >= sum_e ceil(M_e/BM)
-  const unsigned grid = pad8(row_tiles * n_tiles_n);
-  g.grid_pad = static_cast<int32_t>(grid);
-  hipLaunchKernelGGL((rows_kernel<MODE, BIG>), dim3(grid), dim3(Cfg<BIG>::THREADS), 0, s, g);
+  const int64_t row_tiles = (R + Cfg<false>::BM - 1) / Cfg<false>::BM + E;  // >= sum_e ceil(M_e/BM)
+  const int64_t items = row_tiles * n_tiles_n;
+  const int64_t slots = 2 * static_cast<int64_t>(kCUs);
+  const int64_t grid = std::max(std::min(items, slots), (items + kMaxItems - 1) / kMaxItems);
+  g.grid_pad = static_cast<int32_t>(pad8(grid));
+  hipLaunchKernelGGL((rows_kernel<MODE, false>), dim3(g.grid_pad), dim3(Cfg<false>::THREADS), 0,
+                     s, g);
   return hipGetLastError();
 }
 
-// n_cols: the N extent of the mode (UP: f, covered in halves of BN/2)
 template <int MODE>
-hipError_t launch_rows(const Args& g, const moe_dims& dm, int n_cols, hipStream_t s) {
+hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
+  Args g = base;
+  g.n_tiles_n = n_tiles_n;
+  const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
+  g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
+  hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
+                     g);
+  return hipGetLastError();
+}
+
+// n_cols: the N extent of the mode (UP: f, covered in halves of BN/2); K: its
+// reduction length
+template <int MODE>
+hipError_t launch_rows(const Args& g, const moe_dims& dm, int n_cols, int K, hipStream_t s) {
   const int64_t R = dm.T * dm.k;
   const int n_big = (MODE == UP) ? n_cols / 128 : (n_cols + 255) / 256;
-  if (use_big_rows(dm, n_big)) return launch_rows_cfg<MODE, true>(g, R, dm.E, n_big, s);
+  if (use_big_rows(dm, n_big, K)) return launch_rows_big<MODE>(g, R, dm.E, n_big, s);
   const int n_small = (MODE == UP) ? n_cols / 64 : (n_cols + 127) / 128;
-  return launch_rows_cfg<MODE, false>(g, R, dm.E, n_small, s);
+  return launch_rows_small<MODE>(g, R, dm.E, n_small, s);
 }
 
 Args base_args(const moe_dims& dm, const int32_t* offsets) {
@@ -747,7 +1087,7 @@ hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t*
   g.c0 = static_cast<bf16_t*>(a);
   g.c1 = static_cast<bf16_t*>(b);
   g.c2 = static_cast<bf16_t*>(h);
-  return launch_rows<UP>(g, dm, dm.f, s);
+  return launch_rows<UP>(g, dm, dm.f, dm.d, s);
 }
 
 hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* offsets,
@@ -756,7 +1096,7 @@ hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* of
   g.a0 = static_cast<const bf16_t*>(h);
   g.b0 = static_cast<const bf16_t*>(w2);
   g.c0 = static_cast<bf16_t*>(y);
-  return launch_rows<DOWN>(g, dm, dm.d, s);
+  return launch_rows<DOWN>(g, dm, dm.d, dm.f, s);
 }
 
 hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const int32_t* offsets,
@@ -769,7 +1109,7 @@ hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const
   g.aux1 = static_cast<const bf16_t*>(b);
   g.c0 = static_cast<bf16_t*>(da);
   g.c1 = static_cast<bf16_t*>(db);
-  return launch_rows<DGRAD_DOWN>(g, dm, dm.f, s);
+  return launch_rows<DGRAD_DOWN>(g, dm, dm.f, dm.d, s);
 }
 
 hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
@@ -781,7 +1121,7 @@ hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* 
   g.b0 = static_cast<const bf16_t*>(w1);
   g.b1 = static_cast<const bf16_t*>(w3);
   g.c0 = static_cast<bf16_t*>(dx_perm);
-  return launch_rows<DGRAD_UP>(g, dm, dm.d, s);
+  return launch_rows<DGRAD_UP>(g, dm, dm.d, 2 * dm.f, s);
 }
 
 hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
