@@ -86,6 +86,38 @@ def roofline_entry(flops, nbytes, seconds, act):
             "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "moe_expert_up": "gemm_bf16.hip", "moe_expert_down": "gemm_bf16.hip",
+    "moe_expert_dgrad_down": "gemm_bf16.hip", "moe_expert_dgrad_up": "gemm_bf16.hip",
+    "moe_expert_wgrad": "gemm_bf16.hip", "moe_route": "route.hip", "moe_permute": "permute.hip",
+    "moe_combine": "combine.hip", "moe_combine_bwd": "combine.hip",
+    "moe_route_bwd": "route_bwd.hip",
+}
+
+
+def source_digest(name):
+    import hashlib
+    path = os.path.join(ROOT, "top_routing_grouped_router_amd", "csrc", name)
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per launch of `call` at `workload` from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading
+    for a plain copy of known size), or None when there is none or the
+    kernel's source has changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload, {}).get(call)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_digest(KERNEL_SOURCES[call]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(cfg, inp, budget_s=20.0):
     """The oracle as it stands (fp64 numpy), timed on the host cores on the same
     workload.  Whole steps of the full batch when one step takes under ~budget/2
@@ -134,6 +166,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a "
+                         "known-size kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of tokens; --gpus {args.gpus} is not "
@@ -192,28 +227,45 @@ def main():
     if not cfg.backward:
         calls = calls[:5]
 
+    if args.copy_calibration_mb > 0:
+        nbytes = args.copy_calibration_mb << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         for _, fn in calls:
             fn()
     torch.cuda.synchronize()
 
-    n = len(calls)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n)] for _ in range(args.steps)]
+    # Timed region: K whole steps back to back, bracketed by events on the
+    # stream the library launches on (torch's current stream).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for s in range(args.steps):
-        for i, (_, fn) in enumerate(calls):
-            evs[s][i][0].record()
+    for _ in range(args.steps):
+        for _, fn in calls:
             fn()
-            evs[s][i][1].record()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
+
+    # Per-call durations (same stream, events around each call) in a second
+    # pass of the same K steps; they carry the roofline and the breakdown.
+    n = len(calls)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        for i, (_, fn) in enumerate(calls):
+            evs[s][i][0].record()
+            fn()
+            evs[s][i][1].record()
+    torch.cuda.synchronize()
     per_call = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1])
                                      for s in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
@@ -225,7 +277,7 @@ def main():
     dominant = max(single, key=single.get)
     fl, by, _ = work[dominant]
     roof = roofline_entry(fl, by, per_call[dominant] * 1e-3, cfg.act)
-    roof.update({"kernel": dominant, "traffic": None})
+    roof.update({"kernel": dominant, "traffic": measured_traffic(cfg.name, dominant)})
     gemm_ms = sum(per_call[n] for n in GEMM_CALLS if n in per_call)
     gemm_flops = sum(work[n][0] for n in GEMM_CALLS if n in per_call)
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
