@@ -28,6 +28,8 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# extra -D definitions for tuning experiments, e.g. MOE_EXTRA_DEFINES="MOE_ROW_SETS=4"
+CFLAGS += [f"-D{d}" for d in os.environ.get("MOE_EXTRA_DEFINES", "").split()]
 
 
 def sources():

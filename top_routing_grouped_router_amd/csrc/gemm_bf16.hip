@@ -37,6 +37,8 @@
 //    keeps a row tile's A panel and the expert's B panel in that XCD's L2.
 // Each output element is produced by one workgroup in a fixed k order, so
 // results are bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -354,6 +356,10 @@ __device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
 // each round of G items is one contiguous run, cut into one contiguous slice
 // per XCD: a row tile's column tiles share that XCD's L2.
 constexpr int kMaxItems = 64;
+#ifndef MOE_ROW_SETS
+#define MOE_ROW_SETS 3
+#endif
+constexpr int kRowSets = MOE_ROW_SETS;   // register staging sets of the persistent kernel
 struct RowSched {
   int32_t pref[257];     // row tiles of the experts before e
   int32_t off[257];      // expert row offsets
@@ -416,19 +422,22 @@ __device__ int build_row_sched(RowSched& S, const int32_t* offsets, int E, int n
   return n;
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 // Persistent software pipeline over a workgroup's items of nk K steps each.
 // The flattened step sequence runs without a break across items: loads for the
 // next item's first steps are in flight while the current item finishes and
-// its epilogue runs.  TWO_SETS: operand data for step j is loaded into
-// register set j & 1 two steps ahead and stored to LDS buffer j & 1 during
-// step j - 1, between its two halves.  One set: loads for step j + 1 are
-// issued before step j's MFMAs and stored after them.  Loads never branch (a
-// step past the end reloads the last one), so the wait before a store covers
-// only the older register set.  One barrier per step.
-//   load(item, kt, set); store(set, As, Bs); epilogue(item, buf) may use the
-//   LDS buffer that step just consumed (it ends with a barrier); the
+// its epilogue runs.  NSETS register staging sets rotate: step j's operands
+// are loaded into set j % NSETS while step j - NSETS + 1 computes, stored to
+// LDS buffer j & 1 between the two halves of step j - 1, and consumed at step
+// j, so each load has NSETS - 1.5 steps of matrix-core work to land.  Loads
+// never branch (steps past the end reload the last one), so the wait before a
+// store covers only the oldest set.  One barrier per step.
+//   load(item, kt, IC<set>); store(IC<set>, As, Bs); epilogue(item, buf) may
+//   use the LDS buffer the step just consumed (it ends with a barrier); the
 //   accumulators are then cleared.
-template <bool BIG, bool TWO_SETS, typename Load, typename Store, typename Epi>
+template <bool BIG, int NSETS, typename Load, typename Store, typename Epi>
 __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_items, int nk,
                                            Load&& load, Store&& store, Epi&& epilogue) {
   constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
@@ -438,7 +447,7 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
   bf16_t* const Bs1 = lds + (2 * BM + BN) * BK;
   const int S = n_items * nk;
   int li = 0, lk = 0;   // load cursor
-  auto next_load = [&](int set) {
+  auto next_load = [&](auto set) {
     load(li, lk, set);
     if (++lk == nk) {
       if (li + 1 < n_items) {
@@ -450,46 +459,39 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
     }
   };
   int ci = 0, ck = 0;   // compute cursor
-  auto finish_step = [&](bf16_t* consumed) {
+  int j = 0;            // step
+  auto step = [&](auto set) {
+    constexpr int s = decltype(set)::value;
+    const bool odd = j & 1;
+    bf16_t* const ca = odd ? As1 : As0;
+    bf16_t* const cb = odd ? Bs1 : Bs0;
+    next_load(set);   // set s held step j, already in LDS
+    mma_half<BIG>(acc, ca, cb, 0);
+    if (j + 1 < S) store(IC<(s + 1) % NSETS>{}, odd ? As0 : As1, odd ? Bs0 : Bs1);
+    mma_half<BIG>(acc, ca, cb, 1);
+    __syncthreads();
     if (++ck == nk) {
-      epilogue(ci, consumed);
+      epilogue(ci, ca);
       zero_acc<BIG>(acc);
       ck = 0;
       ++ci;
     }
+    return ++j < S;
   };
-  if constexpr (TWO_SETS) {
-    next_load(0);
-    next_load(1);
-    store(0, As0, Bs0);
-    __syncthreads();
-    for (int j = 0; j < S; j += 2) {
-      next_load(0);
-      mma_half<BIG>(acc, As0, Bs0, 0);
-      if (j + 1 < S) store(1, As1, Bs1);
-      mma_half<BIG>(acc, As0, Bs0, 1);
-      __syncthreads();
-      finish_step(As0);
-      if (j + 1 >= S) break;
-      next_load(1);
-      mma_half<BIG>(acc, As1, Bs1, 0);
-      if (j + 2 < S) store(0, As0, Bs0);
-      mma_half<BIG>(acc, As1, Bs1, 1);
-      __syncthreads();
-      finish_step(As1);
-    }
-  } else {
-    next_load(0);
-    store(0, As0, Bs0);
-    __syncthreads();
-    for (int j = 0; j < S; ++j) {
-      const bool odd = j & 1;
-      if (j + 1 < S) next_load(0);
-      mma_substeps<BIG>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0, 0, BK / 8);
-      if (j + 1 < S) store(0, odd ? As0 : As1, odd ? Bs0 : Bs1);
-      __syncthreads();
-      finish_step(odd ? As1 : As0);
-    }
+  next_load(IC<0>{});
+  if constexpr (NSETS > 1) next_load(IC<1>{});
+  if constexpr (NSETS > 2) next_load(IC<2>{});
+  if constexpr (NSETS > 3) next_load(IC<3>{});
+  static_assert(NSETS >= 2 && NSETS <= 4, "2 to 4 staging sets");
+  store(IC<0>{}, As0, Bs0);
+  __syncthreads();
+  while (true) {
+    if (!step(IC<0>{})) break;
+    if (!step(IC<1>{})) break;
+    if constexpr (NSETS > 2)
+      if (!step(IC<2>{})) break;
+    if constexpr (NSETS > 3)
+      if (!step(IC<3>{})) break;
   }
 }
 
@@ -517,12 +519,14 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   AccT<BIG> acc;
   zero_acc<BIG>(acc);
 
-  KPart<BM, NT> pa[2];
-  KPart<BN, NT> pb[2];   // k-contiguous B (UP, DOWN)
-  MPart<BN, NT> pm[2];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
-  int rows_s[2], nval_s[2];
+  constexpr int NSETS = kRowSets;
+  KPart<BM, NT> pa[NSETS];
+  KPart<BN, NT> pb[NSETS];   // k-contiguous B (UP, DOWN)
+  MPart<BN, NT> pm[NSETS];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
+  int rows_s[NSETS], nval_s[NSETS];
 
-  auto load = [&](int item, int kt, int set) {
+  auto load = [&](int item, int kt, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
     const int4 ds = sched.desc[item];
     const int e = ds.x, m0 = ds.y;
     const int rows = min(BM, ds.z - m0);
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
     }
     const bf16_t* ab = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) + static_cast<int64_t>(m0) * lda;
     auto a_ptr = [&](int r) { return ab + static_cast<int64_t>(r) * lda; };
-    if (set) kload<BM, NT>(pa[1], a_ptr, rows, k0); else kload<BM, NT>(pa[0], a_ptr, rows, k0);
+    kload<BM, NT>(pa[set], a_ptr, rows, k0);
     if constexpr (MODE == UP) {
       const bf16_t* w1 = g.b0 + e * E_fd;
       const bf16_t* w3 = g.b1 + e * E_fd;
@@ -546,19 +550,19 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
         return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
                             : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
       };
-      if (set) kload<BN, NT>(pb[1], b_ptr, BN, k0); else kload<BN, NT>(pb[0], b_ptr, BN, k0);
+      kload<BN, NT>(pb[set], b_ptr, BN, k0);
     } else if constexpr (MODE == DOWN) {
       const bf16_t* w2 = g.b0 + e * E_fd;
       auto b_ptr = [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; };
-      if (set) kload<BN, NT>(pb[1], b_ptr, nvalid, k0); else kload<BN, NT>(pb[0], b_ptr, nvalid, k0);
+      kload<BN, NT>(pb[set], b_ptr, nvalid, k0);
     } else if constexpr (MODE == DGRAD_DOWN) {
       // W2[e] is [d][f]: element (k, n) at k * f + n
       const bf16_t* base = g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0;
-      if (set) mload<BN, NT>(pm[1], base, f, BK, nvalid); else mload<BN, NT>(pm[0], base, f, BK, nvalid);
+      mload<BN, NT>(pm[set], base, f, BK, nvalid);
     } else {
       // W1/W3[e] are [f][d]: element (k, n) at k * d + n
       const bf16_t* base = (half ? g.b1 : g.b0) + e * E_fd + static_cast<int64_t>(k0) * d + n0;
-      if (set) mload<BN, NT>(pm[1], base, d, BK, nvalid); else mload<BN, NT>(pm[0], base, d, BK, nvalid);
+      mload<BN, NT>(pm[set], base, d, BK, nvalid);
     }
   };
   auto store_set = [&](const KPart<BM, NT>& a, const KPart<BN, NT>& b, const MPart<BN, NT>& m,
@@ -572,9 +576,9 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
       mstore<BN, NT>(m, Bs, BK, nvalid);
     }
   };
-  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
-    if (set) store_set(pa[1], pb[1], pm[1], rows_s[1], nval_s[1], As, Bs);
-    else store_set(pa[0], pb[0], pm[0], rows_s[0], nval_s[0], As, Bs);
+  auto store = [&](auto set_c, bf16_t* As, bf16_t* Bs) {
+    constexpr int set = decltype(set_c)::value;
+    store_set(pa[set], pb[set], pm[set], rows_s[set], nval_s[set], As, Bs);
   };
 
   // Epilogue through the LDS buffer the last step consumed (free until the
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
       __syncthreads();
     }
   };
-  run_stream<BIG, !BIG>(acc, lds, n_items, nk, load, store, epilogue);
+  run_stream<BIG, NSETS>(acc, lds, n_items, nk, load, store, epilogue);
 }
 
 // expert and first row of row tile `tile` (tiles of BM rows; prefix sum of

@@ -6,10 +6,11 @@
 //   dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i)   (zero for unchosen experts),
 //   dX[t]     += sum_j dl[t, S_j] Wr[S_j],
 //   dWr[e]     = sum_t dl[t, e] X[t].
-// Three kernels: per-token dl (also scattered into permuted row order), the
-// dX rows (k expert-gradient rows plus k router rows, summed in fp32 in slot
-// order and rounded once), and dWr as an ordered sum over each expert's rows
-// (the permutation already lists them in ascending token order).
+// Three kernels: the dX rows (k expert-gradient rows plus k router rows,
+// summed in fp32 in slot order and rounded once; dl computed per token on the
+// way and scattered into permuted row order), dWr partial sums over contiguous
+// parts of each expert's rows (the permutation lists them in ascending token
+// order), and a fixed-order reduction of the parts.
 #include "common.h"
 
 namespace moe {
@@ -17,58 +18,77 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void router_dl_kernel(const float* __restrict__ gate,
-                                                             const float* __restrict__ dgate,
-                                                             const int32_t* __restrict__ pos,
-                                                             float* __restrict__ dl_sel,
-                                                             float* __restrict__ dl_perm,
-                                                             int64_t T, int32_t k) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (t >= T) return;
-  float inner = 0.f;
-  for (int j = 0; j < k; ++j) inner = fmaf(gate[t * k + j], dgate[t * k + j], inner);
-  for (int j = 0; j < k; ++j) {
-    const float dl = gate[t * k + j] * (dgate[t * k + j] - inner);
-    dl_sel[t * k + j] = dl;
-    const int32_t p = pos[t * k + j];
-    if (p >= 0) dl_perm[p] = dl;
-  }
-}
-
-// dX[t] = sum_j dx_perm[pos[t,j]] + sum_j dl[t,j] * wr[idx[t,j]]
-template <typename TA>
+// One thread per 16-byte chunk of a dX row (grid-stride):
+//   dl[t,j] = g_j (dg_j - sum_i g_i dg_i)          (the fp32 sum in slot order)
+//   dX[t]   = sum_j dx_perm[pos[t,j]] + sum_j dl[t,j] wr[idx[t,j]]
+// summed in fp32 in slot order and rounded once.  The thread holding chunk 0
+// of a row also scatters dl into permuted row order for the dWr kernel.  K is
+// the compile-time k (0: runtime k <= 16); every load of a token is issued
+// before any is used (indices clamped, invalid slots masked), so a row costs
+// one memory latency rather than one per slot.
+template <typename TA, int K>
 __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ pos,
-    const int32_t* __restrict__ idx, const float* __restrict__ dl_sel,
-    const float* __restrict__ wr, uint4* __restrict__ dx, int64_t T, int32_t vpr, int32_t d,
-    int32_t k, int32_t E) {
+    const int32_t* __restrict__ idx, const float* __restrict__ gate,
+    const float* __restrict__ dgate, const float* __restrict__ wr, uint4* __restrict__ dx,
+    float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E) {
   constexpr int kPer = Act<TA>::kPer16B;
+  constexpr int KM = K > 0 ? K : 16;
+  const int kk = K > 0 ? K : k;
   const int64_t total = T * vpr;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total;
        v += stride) {
     const int64_t t = v / vpr;
     const int32_t c = static_cast<int32_t>(v - t * vpr);
+    float g[KM], dg[KM];
+    int32_t p[KM], e[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int64_t q = t * kk + min(j, kk - 1);
+      g[j] = gate[q];
+      dg[j] = dgate[q];
+      p[j] = pos[q];
+      e[j] = idx[q];
+    }
+    uint4 rows[KM];
+    float w[KM][kPer];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      rows[j] = dxp ? dxp[static_cast<int64_t>(max(p[j], 0)) * vpr + c] : make_uint4(0u, 0u, 0u, 0u);
+      const float* wp = wr + static_cast<int64_t>(min(max(e[j], 0), E - 1)) * d +
+                        static_cast<int64_t>(c) * kPer;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) w[j][i] = wp[i];
+    }
+    float inner = 0.f;
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < kk) inner = fmaf(g[j], dg[j], inner);
+    float dl[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) dl[j] = g[j] * (dg[j] - inner);
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+        if (j < kk && p[j] >= 0) dl_perm[p[j]] = dl[j];
+    }
     float acc[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
-    if (dxp) {
-      for (int j = 0; j < k; ++j) {
-        const int64_t p = pos[t * k + j];
-        if (p < 0) continue;
-        float r[kPer];
-        unpack16(dxp[p * vpr + c], r, TA{});
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) acc[i] += r[i];
-      }
+    for (int j = 0; j < KM; ++j) {
+      if (j >= kk || !dxp || p[j] < 0) continue;
+      float r[kPer];
+      unpack16(rows[j], r, TA{});
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] += r[i];
     }
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
-      if (e < 0 || e >= E) continue;
-      const float g = dl_sel[t * k + j];
-      const float* w = wr + static_cast<int64_t>(e) * d + static_cast<int64_t>(c) * kPer;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(g, w[i], acc[i]);
+    for (int j = 0; j < KM; ++j) {
+      if (j >= kk || e[j] < 0 || e[j] >= E) continue;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(dl[j], w[j][i], acc[i]);
     }
     dx[v] = pack16(acc, TA{});
   }
@@ -137,16 +157,44 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
   }
 }
 
+// Adds the per-split partial sums of dWr.  Workgroup (column block of 64,
+// expert): thread (split lane sl = t / 16, column group cg = t % 16) adds
+// splits sl, sl + 16, ... in order (all loads issued first), then thread
+// group sl = 0 adds the 16 lane sums in order: a fixed summation order, so
+// the result is reproducible, and one memory latency per thread.
 __global__ __launch_bounds__(kThreads) void router_dwr_reduce_kernel(
     const float* __restrict__ partial, float* __restrict__ dwr, int32_t E, int32_t d,
     int32_t splits) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= static_cast<int64_t>(E) * d) return;
-  const int64_t e = i / d, col = i - e * d;
-  const float* p = partial + e * splits * d + col;
-  float s = p[0];
-  for (int k = 1; k < splits; ++k) s += p[static_cast<int64_t>(k) * d];
-  dwr[i] = s;
+  __shared__ float4 red[16][16];
+  const int e = blockIdx.y;
+  const int sl = threadIdx.x >> 4, cg = threadIdx.x & 15;
+  const int col = blockIdx.x * 64 + cg * 4;
+  const bool ok = col < d;   // d is a multiple of 64; kept for safety
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (ok) {
+    constexpr int kMaxPer = 4;   // splits <= 64
+    float4 v[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int sp = min(sl + 16 * u, splits - 1);
+      v[u] = *reinterpret_cast<const float4*>(partial + (static_cast<int64_t>(e) * splits + sp) * d + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      if (sl + 16 * u >= splits) break;
+      s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+    }
+  }
+  red[sl][cg] = s;
+  __syncthreads();
+  if (sl == 0 && ok) {
+    float4 r = red[0][cg];
+    for (int q = 1; q < 16; ++q) {
+      const float4 o = red[q][cg];
+      r.x += o.x; r.y += o.y; r.z += o.z; r.w += o.w;
+    }
+    *reinterpret_cast<float4*>(dwr + static_cast<int64_t>(e) * d + col) = r;
+  }
 }
 
 }  // namespace
@@ -164,20 +212,35 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
                             float* ws_dl_sel, float* ws_partial, hipStream_t s) {
   if (dm.T > 0) {
-    hipLaunchKernelGGL(router_dl_kernel, dim3((dm.T + kThreads - 1) / kThreads), dim3(kThreads),
-                       0, s, gate, dgate, pos, ws_dl_sel, ws_dl_perm, dm.T, dm.k);
     const int elem = (dm.act == MOE_BF16) ? 2 : 4;
     const int32_t vpr = dm.d * elem / 16;
     const int64_t total = dm.T * vpr;
     const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
-    if (dm.act == MOE_BF16)
-      hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, s,
-                         static_cast<const uint4*>(dx_perm), pos, idx, ws_dl_sel, wr,
-                         static_cast<uint4*>(dx), dm.T, vpr, dm.d, dm.k, dm.E);
-    else
-      hipLaunchKernelGGL(router_dx_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
-                         static_cast<const uint4*>(dx_perm), pos, idx, ws_dl_sel, wr,
-                         static_cast<uint4*>(dx), dm.T, vpr, dm.d, dm.k, dm.E);
+    const uint4* dxp = static_cast<const uint4*>(dx_perm);
+    uint4* dxo = static_cast<uint4*>(dx);
+#define MOE_DX(TA, KC)                                                                        \
+  hipLaunchKernelGGL((router_dx_kernel<TA, KC>), dim3(blocks), dim3(kThreads), 0, s, dxp, pos, \
+                     idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, dm.E)
+    if (dm.act == MOE_BF16) {
+      switch (dm.k) {
+        case 1: MOE_DX(bf16_t, 1); break;
+        case 2: MOE_DX(bf16_t, 2); break;
+        case 4: MOE_DX(bf16_t, 4); break;
+        case 6: MOE_DX(bf16_t, 6); break;
+        case 8: MOE_DX(bf16_t, 8); break;
+        default: MOE_DX(bf16_t, 0); break;
+      }
+    } else {
+      switch (dm.k) {
+        case 1: MOE_DX(float, 1); break;
+        case 2: MOE_DX(float, 2); break;
+        case 4: MOE_DX(float, 4); break;
+        case 6: MOE_DX(float, 6); break;
+        case 8: MOE_DX(float, 8); break;
+        default: MOE_DX(float, 0); break;
+      }
+    }
+#undef MOE_DX
   }
   const int splits = route_bwd_splits(dm);
   const dim3 grid((dm.d + 255) / 256, splits, dm.E);
@@ -189,9 +252,8 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     hipLaunchKernelGGL(router_dwr_partial_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d,
                        splits);
-  const int64_t n = static_cast<int64_t>(dm.E) * dm.d;
-  hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((n + kThreads - 1) / kThreads),
-                     dim3(kThreads), 0, s, ws_partial, dwr, dm.E, dm.d, splits);
+  hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads), 0,
+                     s, ws_partial, dwr, dm.E, dm.d, splits);
   return hipGetLastError();
 }
 
