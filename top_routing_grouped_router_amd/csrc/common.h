@@ -24,6 +24,15 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// two values rounded to nearest even and packed (lo in bits 0-15): one
+// v_cvt_pk_bf16_f32 on gfx950
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+
 template <typename T> struct Act;
 template <> struct Act<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
@@ -56,12 +65,8 @@ __device__ __forceinline__ uint4 pack16(const float* in, float) {
                     __float_as_uint(in[2]), __float_as_uint(in[3]));
 }
 __device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(in[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(in[2 * i + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(bf16x2_rne(in[0], in[1]), bf16x2_rne(in[2], in[3]),
+                    bf16x2_rne(in[4], in[5]), bf16x2_rne(in[6], in[7]));
 }
 
 // v_rcp_f32 instead of a full division (about 1 ulp); exp(-z) = inf gives 0

@@ -86,12 +86,19 @@ struct Args {
   int32_t grid_pad;      // flat grid size (multiple of 8)
 };
 
-// LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r.  The
-// chunk is XORed with S(r) = (r & 7) ^ (bit 3 of r moved to bit 2): 8
-// consecutive rows read at one logical chunk hit 8 different chunk slots, and
-// the transposed stores below (two rows 8 apart per group of 16 lanes) do too.
+// LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r (128
+// bytes per row, so rows 2q and 2q + 1 fill the 64 banks).  The chunk is XORed
+// with S(r) = ((r >> 1) ^ ((r >> 4) << 2)) & 7, chosen for the access
+// patterns of gfx950's 64-bank LDS:
+//  * fragment reads (16 lanes per clock, 16 consecutive rows, one logical
+//    chunk): S is a bijection on each parity class of an aligned 16-row group,
+//    so the 16 lanes hit 16 distinct 16-byte bank groups;
+//  * k-contiguous stores (16 lanes = two whole rows): distinct by construction;
+//  * transposed 8-byte stores (32 lanes per clock = rows 8 j + 2 c + parity of j
+//    for 4 consecutive j, 4 chunks x 2 halves each, see mstore): rows 16
+//    apart get S values 4 apart, so their chunk sets are disjoint.
 __device__ __forceinline__ int swz(int r, int chunk) {
-  return r * BK + ((chunk ^ (r & 7) ^ ((r >> 1) & 4)) << 3);
+  return r * BK + ((chunk ^ (((r >> 1) ^ ((r >> 4) << 2)) & 7)) << 3);
 }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
@@ -191,9 +198,60 @@ __device__ __forceinline__ void mstore(const MPart<COLS, NT>& p, bf16_t* lds, in
       const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
       const uint2 odd =
           make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
+      // lanes of odd j blocks write the odd row first, so each store
+      // instruction covers both bank halves
+      const int p = jb & 1;
       const int row = jb * 8 + 2 * c2;
-      *reinterpret_cast<uint2*>(lds + swz(row, kq >> 1) + 4 * (kq & 1)) = even;
-      *reinterpret_cast<uint2*>(lds + swz(row + 1, kq >> 1) + 4 * (kq & 1)) = odd;
+      *reinterpret_cast<uint2*>(lds + swz(row + p, kq >> 1) + 4 * (kq & 1)) = p ? odd : even;
+      *reinterpret_cast<uint2*>(lds + swz(row + 1 - p, kq >> 1) + 4 * (kq & 1)) = p ? even : odd;
+    }
+  }
+}
+
+// Buffer-resource loads (persistent kernel).  A resource covers
+// [base, base + nbytes); a lane whose byte offset lies at or past nbytes reads
+// zeros, so rows past an expert's end and columns past the matrix edge need no
+// clamp or mask.  Bases and sizes are wavefront-uniform (scalar registers);
+// the per-lane offsets are fixed per tile and the K step only moves the base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const bf16_t* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base), 0, nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 0));
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above every resource size (< 2^31)
+
+template <int ROWS, int NT>
+__device__ __forceinline__ void kstore_raw(const KPart<ROWS, NT>& p, bf16_t* lds) {
+#pragma unroll
+  for (int i = 0; i < ROWS * 8 / NT; ++i) {
+    const int v = threadIdx.x + NT * i;
+    *reinterpret_cast<uint4*>(lds + swz(v >> 3, v & 7)) = p.v[i];
+  }
+}
+
+template <int COLS, int NT>
+__device__ __forceinline__ void mstore_raw(const MPart<COLS, NT>& p, bf16_t* lds) {
+#pragma unroll
+  for (int i = 0; i < COLS * 2 / NT; ++i) {
+    int jb, kq;
+    mblock<NT>(i, &jb, &kq);
+    const uint32_t in[4][4] = {{p.v[i][0].x, p.v[i][0].y, p.v[i][0].z, p.v[i][0].w},
+                               {p.v[i][1].x, p.v[i][1].y, p.v[i][1].z, p.v[i][1].w},
+                               {p.v[i][2].x, p.v[i][2].y, p.v[i][2].z, p.v[i][2].w},
+                               {p.v[i][3].x, p.v[i][3].y, p.v[i][3].z, p.v[i][3].w}};
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2) {
+      const uint32_t A0 = in[0][c2], A1 = in[1][c2], A2 = in[2][c2], A3 = in[3][c2];
+      const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
+      const uint2 odd =
+          make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
+      // lanes of odd j blocks write the odd row first, so each store
+      // instruction covers both bank halves
+      const int p = jb & 1;
+      const int row = jb * 8 + 2 * c2;
+      *reinterpret_cast<uint2*>(lds + swz(row + p, kq >> 1) + 4 * (kq & 1)) = p ? odd : even;
+      *reinterpret_cast<uint2*>(lds + swz(row + 1 - p, kq >> 1) + 4 * (kq & 1)) = p ? even : odd;
     }
   }
 }
@@ -242,6 +300,66 @@ __device__ __forceinline__ void mma_half(AccT<BIG>& acc, const bf16_t* As, const
     mma_substeps<BIG>(acc, As, Bs, 0, 4);
   else
     mma_substeps<BIG>(acc, As, Bs, 4, 8);
+}
+
+// One K step with the fragments of sub-step ss + 1 read from LDS while the
+// MFMAs of sub-step ss run, and `mid` (the LDS store of the next step's
+// operands) placed before sub-step 2.  Scheduling groups then interleave, in
+// one basic block: the step's global loads (issued by the caller just before)
+// with the MFMAs of sub-steps 0-1, and the LDS stores with those of 2-3.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+
+template <bool BIG, int NVMEM, int NDSW, typename Mid>
+__device__ __forceinline__ void mma_step_pipe(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
+                                              Mid&& mid) {
+  typedef Cfg<BIG> C;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int r = lane & 31, g = lane >> 5;
+  bf16x8 af[2][C::FM], bfr[2][C::FN];
+  auto rd = [&](int b, int kk) {
+    const int chunk = kk + g;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      af[b][i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 32 * C::FM + i * 32 + r, chunk));
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      bfr[b][j] =
+          *reinterpret_cast<const bf16x8*>(Bs + swz(j * (C::BN / C::FN) + wn * 32 + r, chunk));
+  };
+  rd(0, 0);
+#pragma unroll
+  for (int ss = 0; ss < BK / 16; ++ss) {
+    if (ss + 1 < BK / 16) rd((ss + 1) & 1, 2 * (ss + 1));
+    if (ss == 2) mid();
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ss & 1][j], af[ss & 1][i],
+                                                            acc[i][j], 0, 0, 0);
+  }
+  constexpr int MF = C::FM * C::FN, DR = C::FM + C::FN;
+  constexpr int VM = (NVMEM + 2 * MF - 1) / (2 * MF), DW = (NDSW + 2 * MF - 1) / (2 * MF);
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, DR, 0);
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, DR, 0);
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, VM, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, DR, 0);
+#pragma unroll
+  for (int ss = 2; ss < 4; ++ss) {
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsWrite, DW, 0);
+    }
+  }
 }
 
 // Software pipeline shared by the kernels: operand data for step j is loaded
@@ -303,10 +421,7 @@ __device__ __forceinline__ void zero_acc(AccT<BIG>& acc) {
 }
 
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-  return make_uint2(static_cast<uint32_t>(f32_to_bf16(a)) |
-                        (static_cast<uint32_t>(f32_to_bf16(b)) << 16),
-                    static_cast<uint32_t>(f32_to_bf16(c)) |
-                        (static_cast<uint32_t>(f32_to_bf16(d)) << 16));
+  return make_uint2(bf16x2_rne(a, b), bf16x2_rne(c, d));
 }
 
 // Visit the accumulators as (row m, first column n of a run of 4, 4 values).
@@ -346,7 +461,7 @@ __device__ __forceinline__ int flat_tile() {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return bf16x2_rne(lo, hi);
 }
 
 // Work list of a persistent row-mode workgroup.  Row tiles are BM rows of one
@@ -360,6 +475,30 @@ constexpr int kMaxItems = 64;
 #define MOE_ROW_SETS 3
 #endif
 constexpr int kRowSets = MOE_ROW_SETS;   // register staging sets of the persistent kernel
+#ifndef MOE_WGRAD_SETS
+#define MOE_WGRAD_SETS 2
+#endif
+constexpr int kWgradSets = MOE_WGRAD_SETS;
+#ifndef MOE_WGRAD_NOSPLIT_ITEMS
+#define MOE_WGRAD_NOSPLIT_ITEMS 160
+#endif
+
+#ifdef MOE_TRACE
+// Timing build only: workgroup timelines of the persistent kernel (thread 0
+// writes the 100 MHz wall clock at its start, after its schedule, after each
+// step and, with the top bit set, after each epilogue).
+constexpr int kTraceSlots = 512;
+constexpr int kTraceBlocks = 1024;
+__device__ uint64_t moe_trace_data[kTraceBlocks * kTraceSlots];
+__device__ __forceinline__ void trace_mark(int& slot, uint64_t flag) {
+  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks && slot < kTraceSlots)
+    moe_trace_data[blockIdx.x * kTraceSlots + slot] = wall_clock64() | flag;
+  ++slot;
+}
+#define MOE_TRACE_MARK(slot, flag) trace_mark(slot, flag)
+#else
+#define MOE_TRACE_MARK(slot, flag) ((void)0)
+#endif
 struct RowSched {
   int32_t pref[257];     // row tiles of the experts before e
   int32_t off[257];      // expert row offsets
@@ -425,7 +564,8 @@ __device__ int build_row_sched(RowSched& S, const int32_t* offsets, int E, int n
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// Persistent software pipeline over a workgroup's items of nk K steps each.
+// Persistent software pipeline over a workgroup's items, item i taking
+// nk_of(i) >= 1 K steps (S steps in all).
 // The flattened step sequence runs without a break across items: loads for the
 // next item's first steps are in flight while the current item finishes and
 // its epilogue runs.  NSETS register staging sets rotate: step j's operands
@@ -437,44 +577,62 @@ using IC = std::integral_constant<int, V>;
 //   load(item, kt, IC<set>); store(IC<set>, As, Bs); epilogue(item, buf) may
 //   use the LDS buffer the step just consumed (it ends with a barrier); the
 //   accumulators are then cleared.
-template <bool BIG, int NSETS, typename Load, typename Store, typename Epi>
-__device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_items, int nk,
-                                           Load&& load, Store&& store, Epi&& epilogue) {
+template <bool BIG, int NSETS, int NVMEM, int NDSW, typename NkOf, typename Prep, typename Load,
+          typename Store, typename Epi>
+__device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_items, int S,
+                                           NkOf&& nk_of, Prep&& prep, Load&& load,
+                                           Store&& store, Epi&& epilogue) {
   constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
   bf16_t* const As0 = lds;
   bf16_t* const Bs0 = lds + BM * BK;
   bf16_t* const As1 = lds + (BM + BN) * BK;
   bf16_t* const Bs1 = lds + (2 * BM + BN) * BK;
-  const int S = n_items * nk;
-  int li = 0, lk = 0;   // load cursor
-  auto next_load = [&](auto set) {
-    load(li, lk, set);
-    if (++lk == nk) {
+  int li = 0, lk = 0, lnk = nk_of(0);   // load cursor (lnk: K steps of item li)
+  auto advance = [&]() {
+    if (++lk == lnk) {
       if (li + 1 < n_items) {
         ++li;
         lk = 0;
+        lnk = nk_of(li);
       } else {
-        lk = nk - 1;
+        --lk;   // past the end: reload the last step
       }
     }
   };
-  int ci = 0, ck = 0;   // compute cursor
-  int j = 0;            // step
+  auto next_load = [&](auto set) {
+    prep(li);
+    load(li, lk, set);
+    advance();
+  };
+  int ci = 0, ck = 0, cnk = lnk;   // compute cursor
+  int j = 0;                       // step
+#ifdef MOE_TRACE
+  int tslot = 2;
+#endif
   auto step = [&](auto set) {
     constexpr int s = decltype(set)::value;
     const bool odd = j & 1;
     bf16_t* const ca = odd ? As1 : As0;
     bf16_t* const cb = odd ? Bs1 : Bs0;
-    next_load(set);   // set s held step j, already in LDS
-    mma_half<BIG>(acc, ca, cb, 0);
-    if (j + 1 < S) store(IC<(s + 1) % NSETS>{}, odd ? As0 : As1, odd ? Bs0 : Bs1);
-    mma_half<BIG>(acc, ca, cb, 1);
+    bf16_t* const na = odd ? As0 : As1;
+    bf16_t* const nb = odd ? Bs0 : Bs1;
+    prep(li);
+    // one basic block from here to the barrier: set s held step j (already
+    // in LDS) and now takes step j + NSETS; the store of step j + 1's set
+    // past the last step writes the idle buffer and is harmless
+    load(li, lk, set);
+    mma_step_pipe<BIG, NVMEM, NDSW>(acc, ca, cb,
+                                    [&] { store(IC<(s + 1) % NSETS>{}, na, nb); });
     __syncthreads();
-    if (++ck == nk) {
+    MOE_TRACE_MARK(tslot, 0);
+    advance();
+    if (++ck == cnk) {
       epilogue(ci, ca);
       zero_acc<BIG>(acc);
       ck = 0;
       ++ci;
+      if (ci < n_items) cnk = nk_of(ci);
+      MOE_TRACE_MARK(tslot, 1ull << 63);
     }
     return ++j < S;
   };
@@ -504,8 +662,14 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
   __shared__ RowSched sched;
-
+#ifdef MOE_TRACE
+  int tslot0 = 0;
+  MOE_TRACE_MARK(tslot0, 0);
+#endif
   const int n_items = build_row_sched<BM, NT>(sched, g.offsets, g.E, g.n_tiles_n);
+#ifdef MOE_TRACE
+  MOE_TRACE_MARK(tslot0, 0);
+#endif
   if (n_items == 0) return;
   const int d = g.d, f = g.f;
   // UP covers BN/2 f columns of a and the same BN/2 of b per tile
@@ -519,155 +683,200 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   AccT<BIG> acc;
   zero_acc<BIG>(acc);
 
-  constexpr int NSETS = kRowSets;
+  constexpr int NSETS = (MODE == DGRAD_DOWN || MODE == DGRAD_UP) ? 2 : kRowSets;
+  constexpr int KA = BM * 8 / NT;   // A chunks per thread
+  constexpr int KB = BN * 8 / NT;   // k-contiguous B chunks per thread (UP, DOWN)
+  constexpr int MB = BN * 2 / NT;   // n-contiguous B blocks per thread (DGRAD modes)
+  static_assert(KB % 2 == 0 && (NT / 8) * (KB / 2) == kUpHalf, "UP: first half of B chunks is W1");
   KPart<BM, NT> pa[NSETS];
   KPart<BN, NT> pb[NSETS];   // k-contiguous B (UP, DOWN)
   MPart<BN, NT> pm[NSETS];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
-  int rows_s[NSETS], nval_s[NSETS];
+  const int ldb = (MODE == DGRAD_DOWN) ? f : d;   // leading dimension of an n-contiguous B
+
+  // per-item lane offsets (bytes from the item's base) and uniform item data
+  uint32_t voff_a[KA], voff_b[KB], voff_m[MB];
+  int p_item = -1, p_e = 0, p_m0 = 0, p_mend = 0, p_n0 = 0;
+  auto prep = [&](int item) {
+    const int4 ds = sched.desc[item];
+    p_e = __builtin_amdgcn_readfirstlane(ds.x);
+    p_m0 = __builtin_amdgcn_readfirstlane(ds.y);
+    p_mend = __builtin_amdgcn_readfirstlane(ds.z);
+    p_n0 = __builtin_amdgcn_readfirstlane(ds.w) * ((MODE == UP) ? kUpHalf : BN);
+    const int t = threadIdx.x, c8 = (t & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < KA; ++i) voff_a[i] = (((t >> 3) + (NT / 8) * i) * lda + c8) * 2;
+    if constexpr (MODE == UP || MODE == DOWN) {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        int r = (t >> 3) + (NT / 8) * i;
+        if (MODE == UP && i >= KB / 2) r -= kUpHalf;
+        voff_b[i] = (r * ((MODE == UP) ? d : f) + c8) * 2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        int jb, kq;
+        mblock<NT>(i, &jb, &kq);
+        voff_m[i] = (p_n0 + jb * 8 < Ndim) ? static_cast<uint32_t>((kq * 4 * ldb + jb * 8) * 2)
+                                           : kOutOfRange;
+      }
+    }
+  };
 
   auto load = [&](int item, int kt, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const int4 ds = sched.desc[item];
-    const int e = ds.x, m0 = ds.y;
-    const int rows = min(BM, ds.z - m0);
-    const int n0 = ds.w * ((MODE == UP) ? kUpHalf : BN);
-    const int nvalid = (MODE == UP) ? BN : min(BN, Ndim - n0);
-    rows_s[set] = rows;
-    nval_s[set] = nvalid;
     int k0 = kt * BK;
     int half = 0;
     if (MODE == DGRAD_UP && k0 >= f) {
       half = 1;
       k0 -= f;
     }
-    const bf16_t* ab = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) + static_cast<int64_t>(m0) * lda;
-    auto a_ptr = [&](int r) { return ab + static_cast<int64_t>(r) * lda; };
-    kload<BM, NT>(pa[set], a_ptr, rows, k0);
+    // A rows [m0, mend) of the expert, K from k0: rows past mend read zeros
+    const bf16_t* abase = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
+                          static_cast<int64_t>(p_m0) * lda + k0;
+    const auto ra = rsrc_at(abase, ((p_mend - p_m0) * lda - k0) * 2);
+#pragma unroll
+    for (int i = 0; i < KA; ++i) pa[set].v[i] = bload(ra, voff_a[i]);
+    const int64_t wexp = static_cast<int64_t>(p_e) * E_fd;
     if constexpr (MODE == UP) {
-      const bf16_t* w1 = g.b0 + e * E_fd;
-      const bf16_t* w3 = g.b1 + e * E_fd;
-      auto b_ptr = [&](int r) {
-        return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
-                            : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
-      };
-      kload<BN, NT>(pb[set], b_ptr, BN, k0);
+      const int nb = (kUpHalf * d - k0) * 2;
+      const auto r1 = rsrc_at(g.b0 + wexp + static_cast<int64_t>(p_n0) * d + k0, nb);
+      const auto r3 = rsrc_at(g.b1 + wexp + static_cast<int64_t>(p_n0) * d + k0, nb);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) pb[set].v[i] = bload(i < KB / 2 ? r1 : r3, voff_b[i]);
     } else if constexpr (MODE == DOWN) {
-      const bf16_t* w2 = g.b0 + e * E_fd;
-      auto b_ptr = [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; };
-      kload<BN, NT>(pb[set], b_ptr, nvalid, k0);
-    } else if constexpr (MODE == DGRAD_DOWN) {
-      // W2[e] is [d][f]: element (k, n) at k * f + n
-      const bf16_t* base = g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0;
-      mload<BN, NT>(pm[set], base, f, BK, nvalid);
+      // W2[e] rows n0.. (over d), K = f; rows past d read zeros
+      const auto rb = rsrc_at(g.b0 + wexp + static_cast<int64_t>(p_n0) * f + k0,
+                              ((d - p_n0) * f - k0) * 2);
+#pragma unroll
+      for (int i = 0; i < KB; ++i) pb[set].v[i] = bload(rb, voff_b[i]);
     } else {
-      // W1/W3[e] are [f][d]: element (k, n) at k * d + n
-      const bf16_t* base = (half ? g.b1 : g.b0) + e * E_fd + static_cast<int64_t>(k0) * d + n0;
-      mload<BN, NT>(pm[set], base, d, BK, nvalid);
-    }
-  };
-  auto store_set = [&](const KPart<BM, NT>& a, const KPart<BN, NT>& b, const MPart<BN, NT>& m,
-                       int rows, int nvalid, bf16_t* As, bf16_t* Bs) {
-    kstore<BM, NT>(a, As, rows);
-    if constexpr (MODE == UP) {
-      kstore<BN, NT>(b, Bs, BN);
-    } else if constexpr (MODE == DOWN) {
-      kstore<BN, NT>(b, Bs, nvalid);
-    } else {
-      mstore<BN, NT>(m, Bs, BK, nvalid);
+      // DGRAD_DOWN: W2[e] [d][f], element (k, n) at k f + n;
+      // DGRAD_UP:   W1/W3[e] [f][d], element (k, n) at k d + n
+      const int krows = (MODE == DGRAD_DOWN) ? d : f;
+      const bf16_t* wb = ((MODE == DGRAD_UP && half) ? g.b1 : g.b0) + wexp;
+      const auto rm = rsrc_at(wb + static_cast<int64_t>(k0) * ldb + p_n0,
+                              ((krows - k0) * ldb - p_n0) * 2);
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pm[set].v[i][r] = bload(rm, voff_m[i] + r * ldb * 2);
     }
   };
   auto store = [&](auto set_c, bf16_t* As, bf16_t* Bs) {
     constexpr int set = decltype(set_c)::value;
-    store_set(pa[set], pb[set], pm[set], rows_s[set], nval_s[set], As, Bs);
+    kstore_raw<BM, NT>(pa[set], As);
+    if constexpr (MODE == UP || MODE == DOWN)
+      kstore_raw<BN, NT>(pb[set], Bs);
+    else
+      mstore_raw<BN, NT>(pm[set], Bs);
   };
 
   // Epilogue through the LDS buffer the last step consumed (free until the
   // next store into it; the final barrier keeps it so): the accumulators are
-  // rounded to bf16 and staged SR rows at a time as [SR][BN] with 16-byte
-  // chunks XOR-swizzled by row, then read back as whole rows and written in
-  // coalesced 16-byte chunks with the mode's elementwise work applied.
-  constexpr int SR = (BM + BN) * BK / BN;   // rows per pass: 128 in both configs
-  constexpr int CH = BN / 8;                // 16-byte chunks per staged row
+  // rounded to bf16 and staged as [BM][BN] with 16-byte chunks XOR-swizzled by
+  // row, then read back as whole rows and written in coalesced 16-byte chunks
+  // with the mode's elementwise work applied.  DGRAD_DOWN issues all of its
+  // saved-a/b loads before staging, so their latency overlaps the staging.
+  static_assert((BM + BN) * BK >= BM * BN, "one staging pass");
+  constexpr int CH = BN / 8;                 // 16-byte chunks per staged row
+  constexpr int kOutIt = BM * CH / NT;       // readback chunks per thread (N modes)
   auto epilogue = [&](int item, bf16_t* buf) {
     const int4 ds = sched.desc[item];
     const int m0 = ds.y, rows = min(BM, ds.z - m0);
+    const int n0 = ds.w * ((MODE == UP) ? kUpHalf : BN);
+    const int nch = (MODE == UP) ? kUpHalf / 8 : min(BN, Ndim - n0) / 8;
+    uint4 aux_a[(MODE == DGRAD_DOWN) ? kOutIt : 1], aux_b[(MODE == DGRAD_DOWN) ? kOutIt : 1];
+    if constexpr (MODE == DGRAD_DOWN) {
+#pragma unroll
+      for (int it = 0; it < kOutIt; ++it) {
+        const int v = threadIdx.x + NT * it;
+        const int r = min(v / CH, rows - 1), c = min(v % CH, nch - 1);   // clamped: in bounds
+        const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
+        aux_a[it] = *reinterpret_cast<const uint4*>(g.aux0 + o);
+        aux_b[it] = *reinterpret_cast<const uint4*>(g.aux1 + o);
+      }
+    }
     // The row swizzle key (r & 15 = lane & 15 for every fragment) goes through
     // an opaque move so that the staging addresses are formed here rather
     // than hoisted out of the step loop into registers held across it.
     int key;
     asm volatile("v_mov_b32 %0, %1" : "=v"(key) : "v"(static_cast<int>(threadIdx.x & 15)));
+    for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+      *reinterpret_cast<uint2*>(buf + m * BN + (((n >> 3) ^ key) << 3) + (n & 4)) =
+          pack4(v0, v1, v2, v3);
+    });
+    __syncthreads();
+    auto chunk = [&](int r, int c) {
+      return *reinterpret_cast<const uint4*>(buf + r * BN + ((c ^ (r & 15)) << 3));
+    };
+    if constexpr (MODE == UP) {
+      // staged columns [0, BN/2) hold a, [BN/2, BN) hold b of f columns n0 + c
+      constexpr int kCh = kUpHalf / 8;
 #pragma unroll
-    for (int p = 0; p < BM / SR; ++p) {
-      for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
-        if (m / SR != p) return;   // wavefront-uniform
-        const int r = m - p * SR;
-        *reinterpret_cast<uint2*>(buf + r * BN + (((n >> 3) ^ key) << 3) + (n & 4)) =
-            pack4(v0, v1, v2, v3);
-      });
-      __syncthreads();
-      auto chunk = [&](int r, int c) {
-        return *reinterpret_cast<const uint4*>(buf + r * BN + ((c ^ (r & 15)) << 3));
-      };
-      if constexpr (MODE == UP) {
-        // staged columns [0, BN/2) hold a, [BN/2, BN) hold b of f columns n0 + c
-        constexpr int kCh = kUpHalf / 8;
-#pragma unroll(BIG ? 1 : 4)
-        for (int v = threadIdx.x; v < SR * kCh; v += NT) {
-          const int r = v / kCh, c = v % kCh;
-          if (p * SR + r >= rows) continue;
-          const uint4 av = chunk(r, c), bv = chunk(r, c + kCh);
+      for (int it = 0; it < BM * kCh / NT; ++it) {
+        const int v = threadIdx.x + NT * it;
+        const int r = v / kCh, c = v % kCh;
+        if (r >= rows) continue;
+        const uint4 av = chunk(r, c), bv = chunk(r, c + kCh);
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+        uint32_t hw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+        const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c * 8;
+        *reinterpret_cast<uint4*>(g.c0 + o) = av;
+        *reinterpret_cast<uint4*>(g.c1 + o) = bv;
+        *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < kOutIt; ++it) {
+        const int v = threadIdx.x + NT * it;
+        const int r = v / CH, c = v % CH;
+        if (r >= rows || c >= nch) continue;
+        const uint4 hv = chunk(r, c);
+        const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
+        if constexpr (MODE == DGRAD_DOWN) {
+          // dh (rounded); da = dh b silu'(a), db = dh silu(a)
+          const uint4 av = aux_a[it], bv = aux_b[it];
+          const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
           const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-          uint32_t hw[4];
+          uint32_t daw[4], dbw[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
-          const int64_t o = static_cast<int64_t>(m0 + p * SR + r) * f + ds.w * kUpHalf + c * 8;
-          *reinterpret_cast<uint4*>(g.c0 + o) = av;
-          *reinterpret_cast<uint4*>(g.c1 + o) = bv;
-          *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        }
-      } else {
-        const int n0 = ds.w * BN;
-        const int nch = min(BN, Ndim - n0) / 8;
-#pragma unroll(BIG ? 1 : 4)
-        for (int v = threadIdx.x; v < SR * CH; v += NT) {
-          const int r = v / CH, c = v % CH;
-          if (p * SR + r >= rows || c >= nch) continue;
-          const uint4 hv = chunk(r, c);
-          const int64_t o = static_cast<int64_t>(m0 + p * SR + r) * Ndim + n0 + c * 8;
-          if constexpr (MODE == DGRAD_DOWN) {
-            // dh (rounded); da = dh b silu'(a), db = dh silu(a)
-            const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
-            const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
-            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-            const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-            uint32_t daw[4], dbw[4];
+          for (int q = 0; q < 4; ++q) {
+            float da2[2], db2[2];
+            const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
+            const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+            const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float da2[2], db2[2];
-              const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
-              const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
-              const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
-#pragma unroll
-              for (int u = 0; u < 2; ++u) {
-                const float sg = sigmoid_f(aa[u]);
-                da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
-                db2[u] = hh[u] * (aa[u] * sg);
-              }
-              daw[q] = bf_pack(da2[0], da2[1]);
-              dbw[q] = bf_pack(db2[0], db2[1]);
+            for (int u = 0; u < 2; ++u) {
+              const float sg = sigmoid_f(aa[u]);
+              da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+              db2[u] = hh[u] * (aa[u] * sg);
             }
-            *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
-            *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
-          } else {
-            *reinterpret_cast<uint4*>(g.c0 + o) = hv;
+            daw[q] = bf_pack(da2[0], da2[1]);
+            dbw[q] = bf_pack(db2[0], db2[1]);
           }
+          *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+          *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+        } else {
+          *reinterpret_cast<uint4*>(g.c0 + o) = hv;
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+  };
+  auto prep_if = [&](int item) {
+    if (item != p_item) {
+      prep(item);
+      p_item = item;
     }
   };
-  run_stream<BIG, NSETS>(acc, lds, n_items, nk, load, store, epilogue);
+  constexpr int kVmem = KA + ((MODE == UP || MODE == DOWN) ? KB : MB * 4);
+  constexpr int kDsw = KA + ((MODE == UP || MODE == DOWN) ? KB : MB * 8);
+  run_stream<BIG, NSETS, kVmem, kDsw>(acc, lds, n_items, n_items * nk, [nk](int) { return nk; },
+                                      prep_if, load, store, epilogue);
 }
 
 // expert and first row of row tile `tile` (tiles of BM rows; prefix sum of
@@ -967,6 +1176,203 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void wgrad_kernel(
   }
 }
 
+// Weight gradients with the small tile, persistent (same pipeline as the row
+// modes).  Items are (z, expert, tile, split), dealt like the row items; item
+// K ranges follow the expert's row count.  A workgroup first decodes its
+// items: those whose K range is empty write a zero tile (or zero partial)
+// straight away, the rest run through the stream.  Both operands are
+// m/n-contiguous ([rows p][M] and [rows p][N]) and go through buffer loads
+// (rows past the split's end and columns past the matrix edge read zeros) and
+// the in-register transpose.  splits == 1: the bf16 tile is staged through
+// the consumed LDS buffer and stored in 16-byte chunks; splits > 1: the fp32
+// partial tile goes out from the accumulators for wgrad_reduce_kernel.
+struct WgSched {
+  int4 d0[kMaxItems];   // z, e, m0, n0
+  int4 d1[kMaxItems];   // first row, end row, K steps, tile | split << 16
+  int n, S;
+};
+
+__global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
+    Args g, int32_t tiles_per_expert, int32_t splits, float* partial) {
+  constexpr bool BIG = false;
+  typedef Cfg<BIG> C;
+  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
+  constexpr int MA = BM * 2 / NT, MBn = BN * 2 / NT;   // 4 x 8 blocks per thread
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
+  __shared__ WgSched sched;
+  __shared__ int4 cand0[kMaxItems], cand1[kMaxItems];
+
+#ifdef MOE_TRACE
+  int tslot0 = 0;
+  MOE_TRACE_MARK(tslot0, 0);
+#endif
+  const int d = g.d, f = g.f, E = g.E;
+  const int G = gridDim.x, flat = flat_tile();
+  const int per_z = E * tiles_per_expert * splits;
+  const int total = 3 * per_z;
+  const int n_cand = flat < total ? min((total - flat + G - 1) / G, kMaxItems) : 0;
+  for (int t = threadIdx.x; t < n_cand; t += NT) {
+    const int it = flat + t * G;
+    const int z = it / per_z;
+    int rem = it - z * per_z;
+    const int e = rem / (tiles_per_expert * splits);
+    rem -= e * tiles_per_expert * splits;
+    const int tile = rem / splits, sp = rem - tile * splits;
+    const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
+    const int tiles_n = (Ndim + BN - 1) / BN;
+    const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+    const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
+    const int nk_all = (p1 - p0 + BK - 1) / BK;
+    const int per_split = (nk_all + splits - 1) / splits;
+    const int kt0 = min(nk_all, sp * per_split), kt1 = min(nk_all, kt0 + per_split);
+    // m0 >= Mdim: no such tile for this z (tiles_per_expert is the max over z)
+    cand0[t] = make_int4(m0 < Mdim ? z : -1, e, m0, n0);
+    cand1[t] = make_int4(p0 + kt0 * BK, min(p1, p0 + kt1 * BK), kt1 - kt0, tile | (sp << 16));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0, S = 0;
+    for (int t = 0; t < n_cand; ++t) {
+      if (cand0[t].x < 0 || cand1[t].z == 0) continue;
+      sched.d0[n] = cand0[t];
+      sched.d1[n] = cand1[t];
+      S += cand1[t].z;
+      ++n;
+    }
+    sched.n = n;
+    sched.S = S;
+  }
+  // items with an empty K range: zero output
+  for (int t = 0; t < n_cand; ++t) {
+    const int4 c0 = cand0[t], c1 = cand1[t];
+    if (c0.x < 0 || c1.z != 0) continue;
+    const int z = c0.x, e = c0.y, m0 = c0.z, n0 = c0.w;
+    const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
+    if (splits > 1) {
+      float* dst = partial +
+                   ((static_cast<int64_t>(z) * E + e) * tiles_per_expert + (c1.w & 0xFFFF)) *
+                       static_cast<int64_t>(splits) * (BM * BN) +
+                   static_cast<int64_t>(c1.w >> 16) * (BM * BN);
+      for (int v = threadIdx.x; v < BM * BN / 4; v += NT)
+        reinterpret_cast<float4*>(dst)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
+      const int mv = min(BM, Mdim - m0), nv8 = min(BN, Ndim - n0) / 8;
+      for (int v = threadIdx.x; v < BM * (BN / 8); v += NT) {
+        const int r = v / (BN / 8), c = v % (BN / 8);
+        if (r < mv && c < nv8)
+          *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8) =
+              make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  __syncthreads();
+#ifdef MOE_TRACE
+  MOE_TRACE_MARK(tslot0, 0);
+#endif
+  const int n_items = sched.n;
+  if (n_items == 0) return;
+
+  AccT<BIG> acc;
+  zero_acc<BIG>(acc);
+  constexpr int NSETS = kWgradSets;
+  MPart<BM, NT> pa[NSETS];
+  MPart<BN, NT> pb[NSETS];
+  uint32_t voff_a[MA], voff_b[MBn];
+  int p_item = -1, p_z = 0, p_e = 0, p_m0 = 0, p_n0 = 0, p_pb = 0, p_pe = 0;
+  auto prep = [&](int item) {
+    const int4 a = sched.d0[item], b = sched.d1[item];
+    p_z = __builtin_amdgcn_readfirstlane(a.x);
+    p_e = __builtin_amdgcn_readfirstlane(a.y);
+    p_m0 = __builtin_amdgcn_readfirstlane(a.z);
+    p_n0 = __builtin_amdgcn_readfirstlane(a.w);
+    p_pb = __builtin_amdgcn_readfirstlane(b.x);
+    p_pe = __builtin_amdgcn_readfirstlane(b.y);
+    const int Mdim = (p_z == 0) ? d : f, Ndim = (p_z == 0) ? f : d;
+#pragma unroll
+    for (int i = 0; i < MA; ++i) {
+      int jb, kq;
+      mblock<NT>(i, &jb, &kq);
+      voff_a[i] = (p_m0 + jb * 8 < Mdim) ? static_cast<uint32_t>((kq * 4 * Mdim + jb * 8) * 2)
+                                         : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < MBn; ++i) {
+      int jb, kq;
+      mblock<NT>(i, &jb, &kq);
+      voff_b[i] = (p_n0 + jb * 8 < Ndim) ? static_cast<uint32_t>((kq * 4 * Ndim + jb * 8) * 2)
+                                         : kOutOfRange;
+    }
+  };
+  auto nk_of = [&](int item) { return sched.d1[item].z; };
+  auto load = [&](int item, int kt, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+    const int Mdim = (p_z == 0) ? d : f, Ndim = (p_z == 0) ? f : d;
+    const bf16_t* Asrc = (p_z == 0) ? g.a0 : (p_z == 1 ? g.a1 : g.aux0);
+    const bf16_t* Bsrc = (p_z == 0) ? g.b0 : g.b1;
+    const int p = p_pb + kt * BK;
+    const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + p_m0,
+                            ((p_pe - p) * Mdim - p_m0) * 2);
+    const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + p_n0,
+                            ((p_pe - p) * Ndim - p_n0) * 2);
+#pragma unroll
+    for (int i = 0; i < MA; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pa[set].v[i][r] = bload(ra, voff_a[i] + r * Mdim * 2);
+#pragma unroll
+    for (int i = 0; i < MBn; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pb[set].v[i][r] = bload(rb, voff_b[i] + r * Ndim * 2);
+  };
+  auto store = [&](auto set_c, bf16_t* As, bf16_t* Bs) {
+    constexpr int set = decltype(set_c)::value;
+    mstore_raw<BM, NT>(pa[set], As);
+    mstore_raw<BN, NT>(pb[set], Bs);
+  };
+  auto epilogue = [&](int item, bf16_t* buf) {
+    const int4 a = sched.d0[item], b = sched.d1[item];
+    const int z = a.x, e = a.y, m0 = a.z, n0 = a.w;
+    const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
+    if (splits > 1) {
+      float* dst = partial +
+                   ((static_cast<int64_t>(z) * E + e) * tiles_per_expert + (b.w & 0xFFFF)) *
+                       static_cast<int64_t>(splits) * (BM * BN) +
+                   static_cast<int64_t>(b.w >> 16) * (BM * BN);
+      for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+        *reinterpret_cast<float4*>(dst + m * BN + n) = make_float4(v0, v1, v2, v3);
+      });
+      return;
+    }
+    int key;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(key) : "v"(static_cast<int>(threadIdx.x & 15)));
+    for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+      *reinterpret_cast<uint2*>(buf + m * BN + (((n >> 3) ^ key) << 3) + (n & 4)) =
+          pack4(v0, v1, v2, v3);
+    });
+    __syncthreads();
+    bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
+    const int mv = min(BM, Mdim - m0), nv8 = min(BN, Ndim - n0) / 8;
+    constexpr int CH = BN / 8;
+#pragma unroll
+    for (int it = 0; it < BM * CH / NT; ++it) {
+      const int v = threadIdx.x + NT * it;
+      const int r = v / CH, c = v % CH;
+      if (r >= mv || c >= nv8) continue;
+      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8) =
+          *reinterpret_cast<const uint4*>(buf + r * BN + ((c ^ (r & 15)) << 3));
+    }
+    __syncthreads();
+  };
+  auto prep_if = [&](int item) {
+    if (item != p_item) {
+      prep(item);
+      p_item = item;
+    }
+  };
+  run_stream<BIG, NSETS, (MA + MBn) * 4, (MA + MBn) * 8>(acc, lds, n_items, sched.S, nk_of,
+                                                         prep_if, load, store, epilogue);
+}
+
 // Adds the split-K partial tiles in split order and rounds once to bf16.
 // One thread per 8 consecutive outputs of a tile row (small tiles only).
 __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t tiles_per_expert,
@@ -1150,10 +1556,12 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   }
   const int tpe = wgrad_tiles_per_expert<false>(dm);
   const int splits = wgrad_splits_bf16(dm);
-  const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe * splits);
-  g.grid_pad = static_cast<int32_t>(grid);
-  hipLaunchKernelGGL(wgrad_kernel<false>, dim3(grid), dim3(Cfg<false>::THREADS), 0, s, g, tpe,
-                     splits, partial);
+  const int64_t items = static_cast<int64_t>(3) * dm.E * tpe * splits;
+  const int64_t grid = std::max(std::min(items, static_cast<int64_t>(2 * kCUs)),
+                                (items + kMaxItems - 1) / kMaxItems);
+  g.grid_pad = static_cast<int32_t>(pad8(grid));
+  hipLaunchKernelGGL(wgrad_stream_kernel, dim3(g.grid_pad), dim3(Cfg<false>::THREADS), 0, s, g,
+                     tpe, splits, partial);
   if (splits > 1) {
     const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (128 * 128 / 8);
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((chunks + kThreads - 1) / kThreads),
@@ -1162,13 +1570,15 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   return hipGetLastError();
 }
 
-// Split-K count for the (small-tile) weight gradients: enough workgroups to
-// fill the chip (about 4 per CU) when E x tiles alone would not, at most 8.
-// Big tiles never split.
+// Split-K count for the (small-tile) weight gradients: none when the tiles
+// alone give about two thirds of a workgroup per CU (the persistent kernel
+// streams long K ranges well); otherwise enough splits for about 320 items,
+// at most 8.  Big tiles never split.
 int wgrad_splits_bf16(const moe_dims& dm) {
   if (use_big_wgrad(dm)) return 1;
   const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm);
-  const int64_t want = 1024;
+  if (base >= MOE_WGRAD_NOSPLIT_ITEMS) return 1;
+  const int64_t want = 2 * MOE_WGRAD_NOSPLIT_ITEMS;
   int s = static_cast<int>((want + base - 1) / base);
   return std::max(1, std::min(s, 8));
 }
@@ -1181,3 +1591,14 @@ size_t wgrad_partial_bytes_bf16(const moe_dims& dm) {
 }
 
 }  // namespace moe
+
+#ifdef MOE_TRACE
+extern "C" int moe_debug_trace_copy(void* host, size_t bytes) {
+  const size_t n = std::min(bytes, sizeof(moe::moe_trace_data));
+  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::moe_trace_data), n));
+}
+extern "C" int moe_debug_trace_clear() {
+  static uint64_t zeros[moe::kTraceBlocks * moe::kTraceSlots];
+  return static_cast<int>(hipMemcpyToSymbol(HIP_SYMBOL(moe::moe_trace_data), zeros, sizeof(zeros)));
+}
+#endif
