@@ -5,7 +5,8 @@
 // Speed-Accuracy Comparisons" (Sec. 2.2: GShard dispatch, where a token's slot
 // inside an expert is the running count of earlier tokens that chose it).
 //
-// A stable counting sort in three small kernels plus one row mover:
+// A stable counting sort in three small kernels plus one row mover (for rows
+// of at most 1 KB, steps 2-4 run as one kernel, perm_scatter_gather_kernel):
 //   1. hist:    block b (256 tokens) counts its assignments per expert (LDS
 //               integer atomics, exact);
 //   2. scan:    one workgroup turns the [blocks, E] counts into expert counts,
@@ -133,6 +134,109 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
   }
 }
 
+// Scan, scatter and gather in one kernel (rows of at most 1 KB).  Workgroup
+// (b, q) (256 threads; q < kSgSplit) rebuilds, from the [nb, E] block counts,
+// the expert totals and block b's prefix (LDS integer atomics: exact,
+// order-free), scans the totals into expert offsets (workgroup (0, 0)
+// publishes counts and offsets), ranks the 256 tokens of block b with the LDS
+// bitmap like perm_scatter_kernel, writes pos/src for its quarter of them and
+// copies their rows once from X to each token's k rows of x_perm.  The
+// redundant scan and ranking are cheap; the split spreads the copy over 4 nb
+// workgroups.
+constexpr int kSgSplit = 4;
+constexpr int kSgTok = kPermBlock / kSgSplit;
+__global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
+    const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
+    const int32_t* __restrict__ hist, int32_t nb, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    const uint4* __restrict__ x, uint4* __restrict__ xp, int32_t vpr) {
+  __shared__ unsigned long long bits[kMaxKeys][kWords];
+  __shared__ int32_t tot[kMaxKeys], pre[kMaxKeys], base[kMaxKeys + 1];
+  __shared__ int32_t spos[kSgTok * 16];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / kSgSplit, q = blockIdx.x % kSgSplit;
+  for (int i = tid; i < E * kWords; i += kThreads) bits[i / kWords][i % kWords] = 0ull;
+  for (int e = tid; e < E; e += kThreads) {
+    tot[e] = 0;
+    pre[e] = 0;
+  }
+  __syncthreads();
+  {
+    const int n = nb * E;
+    constexpr int kU = 8;
+    for (int i0 = tid; i0 < n; i0 += kThreads * kU) {
+      int32_t v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + u * kThreads;
+        v[u] = (i < n) ? hist[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = i0 + u * kThreads;
+        if (i >= n || v[u] == 0) continue;
+        const int e = i % E;
+        atomicAdd(&tot[e], v[u]);
+        if (i / E < b) atomicAdd(&pre[e], v[u]);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t run = 0;
+    for (int e = 0; e < E; ++e) {
+      base[e] = run;
+      run += tot[e];
+    }
+    base[E] = run;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += kThreads) {
+      offsets[e] = base[e];
+      if (e < E && counts) counts[e] = tot[e];
+    }
+  }
+  const int64_t t = static_cast<int64_t>(b) * kPermBlock + tid;
+  const int w = tid >> 6, lane = tid & 63;
+  const bool live = t < T;
+  if (live) {
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      if (e >= 0 && e < E) atomicOr(&bits[e][w], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  if (live && w == q) {   // this workgroup's quarter: tokens 64 q ... 64 q + 63 of block b
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < k; ++j) {
+      const int32_t e = idx[t * k + j];
+      int32_t p = -1;
+      if (e >= 0 && e < E) {
+        int32_t rank = __popcll(bits[e][w] & below);
+        for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+        p = base[e] + pre[e] + rank;
+        src[p] = static_cast<int32_t>(t);
+      }
+      pos[t * k + j] = p;
+      spos[lane * k + j] = p;
+    }
+  }
+  __syncthreads();
+  if (!x || !xp) return;
+  const int64_t t0 = static_cast<int64_t>(b) * kPermBlock + q * kSgTok;
+  const int ntok = static_cast<int>(max<int64_t>(0, min<int64_t>(kSgTok, T - t0)));
+  const int total = ntok * vpr;
+  for (int i = tid; i < total; i += kThreads) {
+    const int tl = i / vpr, c = i - tl * vpr;
+    const uint4 val = x[(t0 + tl) * vpr + c];
+    for (int j = 0; j < k; ++j) {
+      const int32_t p = spos[tl * k + j];
+      if (p >= 0) xp[static_cast<int64_t>(p) * vpr + c] = val;
+    }
+  }
+}
+
 // x_perm[pos[t, j]] = x[t], moved as 16-byte pieces
 __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint4* __restrict__ x,
                                                                const int32_t* __restrict__ pos,
@@ -159,9 +263,18 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
                           int32_t* offsets, int32_t* pos, int32_t* src, const void* x,
                           void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s) {
   const int64_t nb = (dm.T + kPermBlock - 1) / kPermBlock;
+  const int elem = (dm.act == MOE_BF16) ? 2 : 4;
+  const int32_t vpr = dm.d * elem / 16;
   if (nb > 0) {
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
                        ws_hist);
+  }
+  // short rows: scan, scatter and gather fused
+  if (nb > 0 && dm.d * elem <= 1024 && dm.k <= 16) {
+    hipLaunchKernelGGL(perm_scatter_gather_kernel, dim3(nb * kSgSplit), dim3(kThreads), 0, s, idx, dm.T,
+                       dm.k, dm.E, ws_hist, static_cast<int32_t>(nb), counts, offsets, pos, src,
+                       static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(key_scan_kernel, dim3(1), dim3(256), 0, s, ws_hist,
                      static_cast<int32_t>(nb), dm.E, ws_base, counts, offsets);
@@ -170,8 +283,6 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
                        dm.E, ws_base, pos, src);
   }
   if (x && x_perm && dm.T > 0) {
-    const int elem = (dm.act == MOE_BF16) ? 2 : 4;
-    const int32_t vpr = dm.d * elem / 16;
     const int64_t total = dm.T * vpr;
     const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kThreads), 0, s,

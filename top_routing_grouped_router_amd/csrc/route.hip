@@ -226,6 +226,16 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 // experts 16j + l%16, so every token's E logits sit in one 16-lane group:
 // top-k, gates, margin and the full softmax run there with 16-lane shuffles.
 // ---------------------------------------------------------------------------
+#ifdef MOE_TRACE
+// Timing build only: router workgroup timelines (thread 0 writes the 100 MHz
+// wall clock at marked points).
+constexpr int kRtSlots = 16;
+__device__ uint64_t moe_route_trace[1024 * kRtSlots];
+#define MOE_RT_MARK(i) \
+  if (threadIdx.x == 0 && blockIdx.x < 1024) moe_route_trace[blockIdx.x * kRtSlots + (i)] = wall_clock64()
+#else
+#define MOE_RT_MARK(i) ((void)0)
+#endif
 constexpr int kMTile = 64;       // tokens per workgroup
 constexpr int kMBK = 32;         // k chunk
 constexpr int kMLd = kMBK + 8;   // LDS row stride (elements)
@@ -233,28 +243,155 @@ constexpr int kMLd = kMBK + 8;   // LDS row stride (elements)
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ Key group16_argmax(Key k) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) {
-    float v = __shfl_xor(k.v, off, 64);
-    int32_t i = __shfl_xor(k.i, off, 64);
-    if (better(v, i, k.v, k.i)) { k.v = v; k.i = i; }
+// Reductions over the 16 lanes of a DPP row: rotations by 8, 4, 2 and 1
+// lanes within the row (row_ror, a VALU operand modifier rather than an LDS
+// round trip).  At each level a lane combines the same two partial results as
+// its partner does, so all 16 lanes end bitwise identical.
+template <int CTRL>
+__device__ __forceinline__ int row_rot(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float row_rot(float v) {
+  return __int_as_float(row_rot<CTRL>(__float_as_int(v)));
+}
+constexpr int kRowRor8 = 0x128, kRowRor4 = 0x124, kRowRor2 = 0x122, kRowRor1 = 0x121;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_level(Key& k) {
+  const float v = row_rot<CTRL>(k.v);
+  const int32_t i = row_rot<CTRL>(k.i);
+  if (better(v, i, k.v, k.i)) {
+    k.v = v;
+    k.i = i;
   }
+}
+
+__device__ __forceinline__ Key group16_argmax(Key k) {
+  argmax_level<kRowRor8>(k);
+  argmax_level<kRowRor4>(k);
+  argmax_level<kRowRor2>(k);
+  argmax_level<kRowRor1>(k);
   return k;
 }
 
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += row_rot<kRowRor8>(v);
+  v += row_rot<kRowRor4>(v);
+  v += row_rot<kRowRor2>(v);
+  v += row_rot<kRowRor1>(v);
   return v;
+}
+
+// Per-token epilogue shared by the matrix-core router kernels: lane (g, c) of
+// wavefront `wave` holds the logits of tokens t0 + 16 wave + 4 g + q (q < 4)
+// for experts 16 j + c in acc[j][q].  Writes logits, top-k ids and gates,
+// margins, and the workgroup's LB partial sums (fixed-order folds).
+template <int NT>
+__device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f32x4_t (&acc)[NT],
+                                                    int64_t t0) {
+  __shared__ float psum_w[4][16 * NT];
+  __shared__ int32_t pcnt_w[4][16 * NT];
+  __shared__ int32_t tie_w[4];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int E = a.E, k = a.k;
+  float my_psum[NT];
+  int32_t my_cnt[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) { my_psum[j] = 0.f; my_cnt[j] = 0; }
+  int32_t ties = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tg = t0 + wave * 16 + g * 4 + q;
+    const bool live = tg < a.T;
+    float v[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + c;
+      v[j] = (e < E) ? acc[j][q] : -INFINITY;
+      if (live && e < E) a.logits[tg * E + e] = acc[j][q];
+    }
+    uint32_t taken = 0;
+    float my_v = -INFINITY, v_top = -INFINITY, v_km1 = 0.f, v_k = 0.f;
+    int32_t my_i = 0;
+    const int rounds = (k < E) ? k + 1 : k;
+    for (int r = 0; r < rounds; ++r) {
+      Key best{-INFINITY, 0x7fffffff};
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int e = 16 * j + c;
+        if (e < E && !(taken & (1u << j)) && better(v[j], e, best.v, best.i)) {
+          best.v = v[j];
+          best.i = e;
+        }
+      }
+      best = group16_argmax(best);
+      if (r == 0) v_top = best.v;
+      if (r == k - 1) v_km1 = best.v;
+      if (r == k) v_k = best.v;
+      if (c == r) { my_v = best.v; my_i = best.i; }
+      if (r < k && (best.i & 15) == c) taken |= 1u << (best.i >> 4);
+    }
+    float ex[NT];
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int e = 16 * j + c;
+      ex[j] = (e < E) ? __expf(v[j] - v_top) : 0.f;
+      part += ex[j];
+    }
+    const float inv = 1.0f / group16_sum(part);
+    const float my_e = (c < k) ? __expf(my_v - v_top) : 0.f;
+    const float z = group16_sum(my_e);
+    if (live) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        my_psum[j] += ex[j] * inv;
+        if (taken & (1u << j)) my_cnt[j] += 1;
+      }
+      if (c < k) {
+        a.idx[tg * k + c] = my_i;
+        a.gate[tg * k + c] = my_e / z;
+      }
+      const float m = (k < E) ? v_km1 - v_k : INFINITY;
+      if (c == 0) {
+        a.margin[tg] = m;
+        ties += (m < a.eps) ? 1 : 0;
+      }
+    }
+  }
+  // fold the 4 lane groups (fixed xor order), then the 4 waves (fixed order)
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    float s = my_psum[j];
+    int32_t n = my_cnt[j];
+    s += __shfl_xor(s, 16, 64);
+    n += __shfl_xor(n, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    n += __shfl_xor(n, 32, 64);
+    if (g == 0) {
+      psum_w[wave][16 * j + c] = s;
+      pcnt_w[wave][16 * j + c] = n;
+    }
+  }
+  ties += __shfl_xor(ties, 16, 64);
+  ties += __shfl_xor(ties, 32, 64);
+  if (lane == 0) tie_w[wave] = ties;
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
+    const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
+    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
+    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = n;
+  }
+  if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
 }
 
 template <int NT>   // 16-expert tiles: E <= 16 NT
 __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t wsh[3][16 * NT][kMLd];
-  __shared__ float psum_w[4][16 * NT];
-  __shared__ int32_t pcnt_w[4][16 * NT];
-  __shared__ int32_t tie_w[4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -349,147 +486,154 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  // ---------------- per-token epilogue: lane holds tokens 4g+q, experts 16j+c
-  float my_psum[NT];
-  int32_t my_cnt[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) { my_psum[j] = 0.f; my_cnt[j] = 0; }
-  int32_t ties = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t tg = t0 + wave * 16 + g * 4 + q;
-    const bool live = tg < a.T;
-    float v[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int e = 16 * j + c;
-      v[j] = (e < E) ? acc[j][q] : -INFINITY;
-      if (live && e < E) a.logits[tg * E + e] = acc[j][q];
-    }
-    uint32_t taken = 0;
-    float my_v = -INFINITY, v_top = -INFINITY, v_km1 = 0.f, v_k = 0.f;
-    int32_t my_i = 0;
-    const int rounds = (k < E) ? k + 1 : k;
-    for (int r = 0; r < rounds; ++r) {
-      Key best{-INFINITY, 0x7fffffff};
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int e = 16 * j + c;
-        if (e < E && !(taken & (1u << j)) && better(v[j], e, best.v, best.i)) {
-          best.v = v[j];
-          best.i = e;
-        }
-      }
-      best = group16_argmax(best);
-      if (r == 0) v_top = best.v;
-      if (r == k - 1) v_km1 = best.v;
-      if (r == k) v_k = best.v;
-      if (c == r) { my_v = best.v; my_i = best.i; }
-      if (r < k && (best.i & 15) == c) taken |= 1u << (best.i >> 4);
-    }
-    float ex[NT];
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int e = 16 * j + c;
-      ex[j] = (e < E) ? __expf(v[j] - v_top) : 0.f;
-      part += ex[j];
-    }
-    const float inv = 1.0f / group16_sum(part);
-    const float my_e = (c < k) ? __expf(my_v - v_top) : 0.f;
-    const float z = group16_sum(my_e);
-    if (live) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        my_psum[j] += ex[j] * inv;
-        if (taken & (1u << j)) my_cnt[j] += 1;
-      }
-      if (c < k) {
-        a.idx[tg * k + c] = my_i;
-        a.gate[tg * k + c] = my_e / z;
-      }
-      const float m = (k < E) ? v_km1 - v_k : INFINITY;
-      if (c == 0) {
-        a.margin[tg] = m;
-        ties += (m < a.eps) ? 1 : 0;
-      }
-    }
-  }
-  // fold the 4 lane groups (fixed xor order), then the 4 waves (fixed order)
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    float s = my_psum[j];
-    int32_t n = my_cnt[j];
-    s += __shfl_xor(s, 16, 64);
-    n += __shfl_xor(n, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    n += __shfl_xor(n, 32, 64);
-    if (g == 0) {
-      psum_w[wave][16 * j + c] = s;
-      pcnt_w[wave][16 * j + c] = n;
-    }
-  }
-  ties += __shfl_xor(ties, 16, 64);
-  ties += __shfl_xor(ties, 32, 64);
-  if (lane == 0) tie_w[wave] = ties;
-  __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
-    const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
-    const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
-    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
-    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = n;
-  }
-  if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+  route_tile_epilogue<NT>(a, acc, t0);
 }
 
-// One workgroup per balancing block r (grid G).  Per pass, 16 experts x 16
-// tile slices: thread (slice, e) sums tiles slice, slice + 16, ... of block r,
-// then the 16 slice sums are added in slice order.  Block 0 also totals the
-// near-tie counts (strided per thread, then a fixed tree).
-__global__ __launch_bounds__(kThreads) void route_finalize_kernel(
+// Matrix-core router for small E d (the split weight fits in LDS whole):
+// the workgroup splits fp32 Wr exactly into bf16 hi + mid + lo parts straight
+// into LDS (rounding to nearest even at each stage, so hi + mid + lo is the
+// fp32 weight and bf16 x bf16 products accumulated in fp32 give the fp32
+// logits), with one barrier; each wavefront holds its 16 tokens' X fragments
+// for the whole of K in registers (all loads issued at once) and runs the
+// MFMAs with B fragments from LDS.
+template <int NT, int NKC>   // NKC: K chunks of 32 (d = 32 NKC)
+__global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
+  constexpr int kLd = 32 * NKC + 8;
+  __shared__ __attribute__((aligned(16))) bf16_t wsh_dyn[3 * 16 * NT * kLd];   // [3][16 NT][kLd]
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int E = a.E, d = a.d;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMTile;
+  const bf16_t* x = static_cast<const bf16_t*>(a.x);
+  const int64_t my_row = t0 + wave * 16 + c;
+  const bool row_ok = my_row < a.T;
+  const bf16_t* xrow = x + (row_ok ? my_row : 0) * d + g * 8;
+  MOE_RT_MARK(0);
+  uint4 xa[NKC];
+#pragma unroll
+  for (int kt = 0; kt < NKC; ++kt) {
+    xa[kt] = *reinterpret_cast<const uint4*>(xrow + kt * 32);
+    if (!row_ok) xa[kt] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  // split Wr (E x d fp32; rows >= E are zero) into LDS, 4 weights per step
+  constexpr int kRowsP = 16 * NT;
+  const int nvec = kRowsP * d / 4;
+  for (int v = tid; v < nvec; v += kThreads) {
+    const int e = v / (d / 4), q = v % (d / 4);
+    const float4 w4 = (e < E) ? *reinterpret_cast<const float4*>(a.wr + static_cast<int64_t>(e) * d + q * 4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+    uint32_t hi[2], mi[2], lo[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      bf16_t h2[2], m2[2], l2[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float f0 = w[2 * u + z];
+        const bf16_t h = f32_to_bf16(f0);
+        const float r1 = f0 - bf16_to_f32(h);
+        const bf16_t m = f32_to_bf16(r1);
+        const float r2 = r1 - bf16_to_f32(m);
+        h2[z] = h;
+        m2[z] = m;
+        l2[z] = f32_to_bf16(r2);
+      }
+      hi[u] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+      mi[u] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+      lo[u] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+    }
+    bf16_t* row = wsh_dyn + e * kLd + q * 4;
+    *reinterpret_cast<uint2*>(row) = make_uint2(hi[0], hi[1]);
+    *reinterpret_cast<uint2*>(row + kRowsP * kLd) = make_uint2(mi[0], mi[1]);
+    *reinterpret_cast<uint2*>(row + 2 * kRowsP * kLd) = make_uint2(lo[0], lo[1]);
+  }
+  __syncthreads();
+  MOE_RT_MARK(1);
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < NKC; ++kt) {
+    const bf16x8_t af = __builtin_bit_cast(bf16x8_t, xa[kt]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(
+            wsh_dyn + (sp * kRowsP + 16 * j + c) * kLd + kt * 32 + g * 8);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
+      }
+  }
+#ifdef MOE_TRACE
+  if (acc[0][0] == 12345.f) acc[0][1] = 0.f;   // keep the mark after the MFMAs
+#endif
+  MOE_RT_MARK(2);
+  route_tile_epilogue<NT>(a, acc, t0);
+  MOE_RT_MARK(3);
+}
+
+// One workgroup (1024 threads) per balancing block r (grid G), all experts in
+// one pass: thread (slice, e) with slice < SL = 1024 / E_p (E_p: E rounded up
+// to a power of two, at least 16) adds tiles slice, slice + SL, ... of block r
+// in tile order (8 loads in flight), then thread e adds the SL slice sums in
+// slice order.  Block 0 also totals the near-tie counts (strided per thread,
+// then a fixed tree).
+constexpr int kFinThreads = 1024;
+__global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
     const float* psum, const int32_t* pcnt, const int32_t* ptie, int32_t n_tiles,
     int32_t tiles_per_group, int64_t T, int32_t E, int32_t k, int32_t* gcount, float* gprob,
     float* gaux, int32_t* tie_count) {
-  __shared__ float sp[16][17];
-  __shared__ int32_t sc[16][17];
+  __shared__ float sp[kFinThreads];
+  __shared__ int32_t sc[kFinThreads];
   __shared__ float fp[kMaxE];
-  __shared__ int32_t st[kThreads];
+  __shared__ int32_t st[kFinThreads];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int slice = tid >> 4, el = tid & 15;
+  const int Ep = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+  const int SL = kFinThreads / Ep;
+  const int slice = tid / Ep, e = tid % Ep;
   const int64_t G = gridDim.x;
   const double per_group = static_cast<double>(T) / static_cast<double>(G);
-  for (int e = tid; e < kMaxE; e += kThreads) fp[e] = 0.f;
-  for (int e0 = 0; e0 < E; e0 += 16) {
-    const int e = e0 + el;
-    float s = 0.f;
-    int32_t c = 0;
-    if (e < E) {
-      for (int i = slice; i < tiles_per_group; i += 16) {
+  for (int i = tid; i < kMaxE; i += kFinThreads) fp[i] = 0.f;
+  float s = 0.f;
+  int32_t c = 0;
+  if (e < E) {
+    for (int i0 = slice; i0 < tiles_per_group; i0 += SL * 8) {
+      float ps[8];
+      int32_t pc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(i0 + SL * u, tiles_per_group - 1);
         const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
-        s += psum[tile * E + e];
-        c += pcnt[tile * E + e];
+        ps[u] = psum[tile * E + e];
+        pc[u] = pcnt[tile * E + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + SL * u >= tiles_per_group) break;
+        s += ps[u];
+        c += pc[u];
       }
     }
-    sp[slice][el] = s;
-    sc[slice][el] = c;
-    __syncthreads();
-    if (tid < 16 && e0 + tid < E) {
-      float S = 0.f;
-      int32_t C = 0;
-      for (int q = 0; q < 16; ++q) {
-        S += sp[q][tid];
-        C += sc[q][tid];
-      }
-      const int ee = e0 + tid;
-      const float P = (per_group > 0) ? static_cast<float>(S / per_group) : 0.f;
-      const float fr = (per_group > 0) ? static_cast<float>(C / (per_group * k)) : 0.f;
-      if (gcount) gcount[static_cast<int64_t>(r) * E + ee] = C;
-      if (gprob) gprob[static_cast<int64_t>(r) * E + ee] = P;
-      fp[ee] = fr * P;
-    }
-    __syncthreads();
   }
+  sp[tid] = s;
+  sc[tid] = c;
+  __syncthreads();
+  if (tid < E) {
+    float S = 0.f;
+    int32_t C = 0;
+    for (int q = 0; q < SL; ++q) {
+      S += sp[q * Ep + tid];
+      C += sc[q * Ep + tid];
+    }
+    const float P = (per_group > 0) ? static_cast<float>(S / per_group) : 0.f;
+    const float fr = (per_group > 0) ? static_cast<float>(C / (per_group * k)) : 0.f;
+    if (gcount) gcount[static_cast<int64_t>(r) * E + tid] = C;
+    if (gprob) gprob[static_cast<int64_t>(r) * E + tid] = P;
+    fp[tid] = fr * P;
+  }
+  __syncthreads();
   // fixed-order tree over the (zero-padded) 256 products
   for (int w = kMaxE / 2; w >= 1; w >>= 1) {
     if (tid < w) fp[tid] += fp[tid + w];
@@ -497,11 +641,11 @@ __global__ __launch_bounds__(kThreads) void route_finalize_kernel(
   }
   if (tid == 0 && gaux) gaux[r] = static_cast<float>(E) * fp[0];
   if (r == 0 && tie_count) {
-    int32_t s = 0;
-    for (int i = tid; i < n_tiles; i += kThreads) s += ptie[i];
-    st[tid] = s;
+    int32_t t = 0;
+    for (int i = tid; i < n_tiles; i += kFinThreads) t += ptie[i];
+    st[tid] = t;
     __syncthreads();
-    for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    for (int w = kFinThreads / 2; w >= 1; w >>= 1) {
       if (tid < w) st[tid] += st[tid + w];
       __syncthreads();
     }
@@ -511,6 +655,11 @@ __global__ __launch_bounds__(kThreads) void route_finalize_kernel(
 
 }  // namespace
 
+// The LDS router holds the whole split weight of up to 64 experts for d <= 256.
+bool route_in_lds(const moe_dims& dm) {
+  return dm.act == MOE_BF16 && dm.E <= 64 && dm.d <= 256 && dm.d % 64 == 0;
+}
+
 hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
@@ -519,7 +668,22 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
   if (n_tiles > 0) {
     RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie,
                 dm.T, dm.d, dm.E, dm.k, tile, eps};
-    if (tile == kRouteMfmaTile) {
+    if (tile == kRouteMfmaTile && route_in_lds(dm)) {
+      const int nt = (dm.E + 15) / 16;
+      const int nt_p = nt <= 1 ? 1 : nt <= 2 ? 2 : 4;
+#define MOE_RL(N, K)                                                                          \
+  hipLaunchKernelGGL((route_lds_kernel<N, K>), dim3(n_tiles), dim3(kThreads), 0, s, a)
+#define MOE_RL_D(N)                              \
+  switch (dm.d / 32) {                           \
+    case 2: MOE_RL(N, 2); break;                 \
+    case 4: MOE_RL(N, 4); break;                 \
+    case 6: MOE_RL(N, 6); break;                 \
+    default: MOE_RL(N, 8); break;                \
+  }
+      if (nt_p == 1) { MOE_RL_D(1) } else if (nt_p == 2) { MOE_RL_D(2) } else { MOE_RL_D(4) }
+#undef MOE_RL_D
+#undef MOE_RL
+    } else if (tile == kRouteMfmaTile) {
       const int nt = (dm.E + 15) / 16;
 #define MOE_RM(N)                                                                        \
   case N:                                                                                \
@@ -542,10 +706,17 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
     if (e != hipSuccess) return e;
   }
   const int32_t tiles_per_group = static_cast<int32_t>(n_tiles / G);
-  hipLaunchKernelGGL(route_finalize_kernel, dim3(G), dim3(kThreads), 0, s, ws_psum, ws_pcnt,
+  hipLaunchKernelGGL(route_finalize_kernel, dim3(G), dim3(kFinThreads), 0, s, ws_psum, ws_pcnt,
                      ws_ptie, static_cast<int32_t>(n_tiles), tiles_per_group, dm.T, dm.E, dm.k,
                      gcount, gprob, gaux, tie_count);
   return hipGetLastError();
 }
 
 }  // namespace moe
+
+#ifdef MOE_TRACE
+extern "C" int moe_debug_route_trace_copy(void* host, size_t bytes) {
+  const size_t n = std::min(bytes, sizeof(moe::moe_route_trace));
+  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::moe_route_trace), n));
+}
+#endif
