@@ -1084,6 +1084,241 @@ __global__ __launch_bounds__(Cfg<true>::THREADS, 2) void tile_rows_kernel(Args g
   }
 }
 
+// ------------------------------------------------------------------ direct-to-LDS big tile
+// Row modes with k-contiguous operands (UP, DOWN) at the big tile, one tile
+// per workgroup: operand tiles go from HBM/L2 straight into a 4-stage LDS ring
+// (K step 32) by buffer loads with the LDS destination (no register staging),
+// issued three steps ahead.  Each wavefront instruction fills 1 KB of LDS:
+// 16 rows of 64 bytes, lane l taking row l / 4 and physical chunk l % 4; the
+// global address carries the swizzle (logical chunk = physical ^ key(row)), so
+// the fragment reads below are conflict-free.  The compiler does not track
+// these LDS writes, so the step waits on the vector-memory counter explicitly
+// and joins the workgroup with a plain s_barrier (a fenced barrier would also
+// drain the prefetch).
+namespace dma {
+constexpr int BM = 256, BN = 256, BKS = 32, NST = 4, NT = 512, WAVES_N = 4, FM = 4, FN = 2;
+constexpr int kStage = (BM + BN) * BKS;   // elements per stage
+// element offset of 16-byte chunk `chunk` (of 4) in row r of a 64-byte-row tile
+__device__ __forceinline__ int swz32(int r, int chunk) {
+  return r * BKS + ((chunk ^ ((r >> 2) & 3)) << 3);
+}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, static_cast<int>(voff), 0, 0, 0);
+}
+// s_waitcnt with vmcnt = N (N < 16), expcnt and lgkmcnt left free
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+}  // namespace dma
+
+template <int MODE>
+__global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
+  using namespace dma;
+  static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NST * kStage];   // 128 KB ring
+
+  const int flat = flat_tile();
+  const int row_tile = flat / g.n_tiles_n;
+  const int nt = flat - row_tile * g.n_tiles_n;
+  int e, m0, mend;
+  if (!find_row_tile<BM>(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  mend = __builtin_amdgcn_readfirstlane(mend);
+  const int rows = min(BM, mend - m0);
+  const int d = g.d, f = g.f;
+  constexpr int kUpHalf = BN / 2;
+  const int n0 = nt * ((MODE == UP) ? kUpHalf : BN);
+  const int K = (MODE == UP) ? d : f;
+  const int nk = K / BKS;
+  const int lda = (MODE == UP) ? d : f;
+  const int64_t E_fd = static_cast<int64_t>(f) * d;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // this wavefront's DMA instructions: A rows 32 wave + [0, 32) and B rows
+  // 32 wave + [0, 32), 16 rows per instruction
+  uint32_t voa[2], vob[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = wave * 32 + u * 16 + (lane >> 2);
+    const int logical = (lane & 3) ^ ((row >> 2) & 3);
+    voa[u] = (row * lda + logical * 8) * 2;
+    const int brow = (MODE == UP && row >= kUpHalf) ? row - kUpHalf : row;
+    vob[u] = (brow * ((MODE == UP) ? d : f) + logical * 8) * 2;
+  }
+  const bf16_t* abase = g.a0 + static_cast<int64_t>(m0) * lda;
+  const int a_rows_bytes = (mend - m0) * lda * 2;
+  const bf16_t* bbase;
+  int b_bytes;
+  if constexpr (MODE == UP) {
+    // wavefronts 0-3 fill B rows [0, 128) from W1, 4-7 rows [128, 256) from W3
+    bbase = (wave < 4 ? g.b0 : g.b1) + e * E_fd + static_cast<int64_t>(n0) * d;
+    b_bytes = kUpHalf * d * 2;
+  } else {
+    bbase = g.b0 + e * E_fd + static_cast<int64_t>(n0) * f;
+    b_bytes = (d - n0) * f * 2;
+  }
+  auto issue = [&](int kt) {   // step kt into stage kt % NST
+    bf16_t* As = lds + (kt % NST) * kStage;
+    bf16_t* Bs = As + BM * BKS;
+    const int k0 = kt * BKS;
+    const auto ra = rsrc_at(abase + k0, a_rows_bytes - k0 * 2);
+    const auto rb = rsrc_at(bbase + k0, b_bytes - k0 * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16(ra, As + (wave * 32 + u * 16) * BKS, voa[u]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16(rb, Bs + (wave * 32 + u * 16) * BKS, vob[u]);
+  };
+
+  AccT<true> acc;
+  zero_acc<true>(acc);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int r = lane & 31, gq = lane >> 5;
+  // byte addresses (within the stage) of this lane's fragment rows for the two
+  // 16-wide sub-steps; fragment i / j adds i * 32 / j * 128 rows (constant)
+  const int key = (r >> 2) & 3;
+  uint32_t a_addr[2], b_addr[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int pc = (2 * kk + gq) ^ key;
+    a_addr[kk] = ((wm * 32 * FM + r) * BKS + pc * 8) * 2;
+    b_addr[kk] = (BM * BKS + (wn * 32 + r) * BKS + pc * 8) * 2;
+  }
+  // LDS byte offset of the ring (an address-space-3 pointer is the offset)
+  const uint32_t lds_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)lds));
+  // Fragment reads overlap the MFMAs: per step kt two asm blocks, each six
+  // fragment reads interleaved with eight MFMAs and ending by waiting for its
+  // reads: block 1 reads the second 16-wide sub-step (kk = 1) of step kt while
+  // the kk = 0 MFMAs of step kt run; block 2, after the barrier that releases
+  // stage kt + 1, reads kk = 0 of step kt + 1 while the kk = 1 MFMAs of step kt
+  // run.  In flight: DMA of steps kt + 2 and kt + 3.
+  typedef float f32x16v __attribute__((ext_vector_type(16)));
+  f32x16v c00 = acc[0][0], c01 = acc[0][1], c10 = acc[1][0], c11 = acc[1][1];
+  f32x16v c20 = acc[2][0], c21 = acc[2][1], c30 = acc[3][0], c31 = acc[3][1];
+  bf16x8 p0[6], p1[6];   // sub-step fragments: a 0-3, b 4-5 (kk = 0 in p0, kk = 1 in p1)
+#define MOE_MF(c, b, a) "v_mfma_f32_32x32x16_bf16 " c ", " b ", " a ", " c "\n\t"
+#define MOE_RD(o, addr, off) "ds_read_b128 " o ", " addr " offset:" off "\n\t"
+  // reads six fragments at (aaddr, baddr) into `out` while running the eight
+  // MFMAs of the fragments `in`
+  auto half_asm = [&](const bf16x8 (&in)[6], bf16x8 (&out)[6], uint32_t aaddr, uint32_t baddr) {
+    asm volatile(
+        MOE_RD("%8", "%20", "0")      MOE_MF("%0", "%18", "%14")
+        MOE_RD("%9", "%20", "2048")   MOE_MF("%1", "%19", "%14")
+        MOE_RD("%10", "%20", "4096")  MOE_MF("%2", "%18", "%15")
+        MOE_RD("%11", "%20", "6144")  MOE_MF("%3", "%19", "%15")
+        MOE_RD("%12", "%21", "0")     MOE_MF("%4", "%18", "%16")
+        MOE_RD("%13", "%21", "8192")  MOE_MF("%5", "%19", "%16")
+                                      MOE_MF("%6", "%18", "%17")
+                                      MOE_MF("%7", "%19", "%17")
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11), "+v"(c20), "+v"(c21), "+v"(c30),
+          "+v"(c31), "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]),
+          "=&v"(out[4]), "=&v"(out[5])
+        : "v"(in[0]), "v"(in[1]), "v"(in[2]), "v"(in[3]), "v"(in[4]), "v"(in[5]), "v"(aaddr),
+          "v"(baddr)
+        : "memory");
+  };
+#undef MOE_MF
+#undef MOE_RD
+  auto read_p = [&](bf16x8 (&out)[6], uint32_t aaddr, uint32_t baddr) {
+    asm volatile(
+        "ds_read_b128 %0, %6 offset:0\n\t"
+        "ds_read_b128 %1, %6 offset:2048\n\t"
+        "ds_read_b128 %2, %6 offset:4096\n\t"
+        "ds_read_b128 %3, %6 offset:6144\n\t"
+        "ds_read_b128 %4, %7 offset:0\n\t"
+        "ds_read_b128 %5, %7 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
+          "=&v"(out[5])
+        : "v"(aaddr), "v"(baddr)
+        : "memory");
+  };
+  auto sbase = [&](int kt) { return lds_base + (kt % NST) * kStage * 2; };
+  // prologue: steps 0 .. 2 in flight (past-the-end steps reload the last);
+  // kk = 0 fragments of step 0 read once it has landed
+  issue(0);
+  issue(min(1, nk - 1));
+  issue(min(2, nk - 1));
+  dma::wait_vm<8>();
+  __builtin_amdgcn_s_barrier();
+  read_p(p0, sbase(0) + a_addr[0], sbase(0) + b_addr[0]);
+#ifdef MOE_TRACE
+  int tslot = 0;
+#endif
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t sc = sbase(kt), sn = sbase(kt + 1);
+    half_asm(p0, p1, sc + a_addr[1], sc + b_addr[1]);   // kk = 0 MFMAs; read kk = 1
+#ifdef MOE_TRACE
+    if (kt < 48) MOE_TRACE_MARK(tslot, 1ull << 60);
+#endif
+    dma::wait_vm<4>();              // this wavefront's loads of step kt + 1 have landed
+    __builtin_amdgcn_s_barrier();   // everyone's have; everyone is done with step kt - 1
+#ifdef MOE_TRACE
+    if (kt < 48) MOE_TRACE_MARK(tslot, 2ull << 60);
+#endif
+    issue(min(kt + 3, nk - 1));     // into stage (kt + 3) % 4, last read during step kt - 1
+    half_asm(p1, p0, sn + a_addr[0], sn + b_addr[0]);   // kk = 1 MFMAs; read next kk = 0
+#ifdef MOE_TRACE
+    if (kt < 48) MOE_TRACE_MARK(tslot, 3ull << 60);
+#endif
+  }
+  // the last MFMAs may still be writing: cover the longest MFMA-to-VALU
+  // read-after-write distance before the accumulators are read
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
+  acc[2][0] = c20; acc[2][1] = c21; acc[3][0] = c30; acc[3][1] = c31;
+  dma::wait_vm<0>();
+  __syncthreads();
+
+  // epilogue: the whole 256 x 256 tile staged as bf16 over the ring (128 KB),
+  // 16-byte chunks XOR-swizzled by row, then coalesced 16-byte stores
+  bf16_t* out = lds;
+  {
+    int skey;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(skey) : "v"(static_cast<int>(threadIdx.x & 15)));
+    for_each_quad<true>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+      *reinterpret_cast<uint2*>(out + m * BN + (((n >> 3) ^ skey) << 3) + (n & 4)) =
+          pack4(v0, v1, v2, v3);
+    });
+  }
+  __syncthreads();
+  auto chunk_at = [&](int rr, int c) {
+    return *reinterpret_cast<const uint4*>(out + rr * BN + ((c ^ (rr & 15)) << 3));
+  };
+  if constexpr (MODE == UP) {
+    constexpr int kCh = kUpHalf / 8;   // 16 chunks of a per row
+    for (int v = tid; v < BM * kCh; v += NT) {
+      const int rr = v / kCh, c = v % kCh;
+      if (rr >= rows) continue;
+      const uint4 av = chunk_at(rr, c), bv = chunk_at(rr, c + kCh);
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t hw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+      const int64_t o = static_cast<int64_t>(m0 + rr) * f + n0 + c * 8;
+      *reinterpret_cast<uint4*>(g.c0 + o) = av;
+      *reinterpret_cast<uint4*>(g.c1 + o) = bv;
+      *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+  } else {
+    constexpr int kCh = BN / 8;
+    const int nch = min(BN, d - n0) / 8;
+    for (int v = tid; v < BM * kCh; v += NT) {
+      const int rr = v / kCh, c = v % kCh;
+      if (rr >= rows || c >= nch) continue;
+      *reinterpret_cast<uint4*>(g.c0 + static_cast<int64_t>(m0 + rr) * d + n0 + c * 8) =
+          chunk_at(rr, c);
+    }
+  }
+}
+
 // Weight gradients: tile (e, m, n) of dW_z[e] = sum over the expert's rows p of
 // A[p][m] B[p][n]; z = 0: dW2 (A = dy, B = h), 1: dW1 (A = da, B = x),
 // 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
@@ -1460,6 +1695,12 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
   g.n_tiles_n = n_tiles_n;
   const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
   g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
+  if constexpr (MODE == UP || MODE == DOWN) {
+#ifndef MOE_NO_DMA
+    hipLaunchKernelGGL((dma_rows_kernel<MODE>), dim3(g.grid_pad), dim3(dma::NT), 0, s, g);
+    return hipGetLastError();
+#endif
+  }
   hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
                      g);
   return hipGetLastError();
