@@ -1506,6 +1506,229 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   }
 }
 
+// Input gradients with the big tile (DGRAD_DOWN: dh = dy_perm W2[e];
+// DGRAD_UP: dx_perm = da W1[e] + db W3[e]) on the LDS-DMA ring.  Stage = A
+// [256 rows][32 k] (64-byte rows, as in dma_rows_kernel, fragments read by an
+// asm block interleaved with the MFMAs) + B [32 k][256 n] (512-byte rows as
+// they lie in W, fragments from the transposing read, as in
+// wgrad_dma_kernel).  Four distinct stage arrays; the step count is padded to
+// a multiple of 4 with zero steps (empty resources).
+template <int MODE>
+__global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
+  using namespace dma;
+  static_assert(MODE == DGRAD_DOWN || MODE == DGRAD_UP, "dgrad modes");
+  constexpr int kAB = BM * BKS;   // A part of a stage (elements)
+  __shared__ __attribute__((aligned(16))) bf16_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st2[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st3[kStage];
+
+  const int flat = flat_tile();
+  const int row_tile = flat / g.n_tiles_n;
+  const int nt = flat - row_tile * g.n_tiles_n;
+  int e, m0, mend;
+  if (!find_row_tile<BM>(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  mend = __builtin_amdgcn_readfirstlane(mend);
+  const int rows = min(BM, mend - m0);
+  const int d = g.d, f = g.f;
+  const int n0 = nt * BN;
+  const int Ndim = (MODE == DGRAD_DOWN) ? f : d;   // output columns
+  const int lda = (MODE == DGRAD_DOWN) ? d : f;    // A row length
+  const int ldb = Ndim;                            // B row length (element (k, n) at k ldb + n)
+  const int Kh = (MODE == DGRAD_DOWN) ? d : f;     // K per half (DGRAD_UP: da then db)
+  const int nk = ((MODE == DGRAD_DOWN) ? d : 2 * f) / BKS;
+  const int64_t E_fd = static_cast<int64_t>(f) * d;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  uint32_t voa[2], vob[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = wave * 32 + u * 16 + (lane >> 2);   // A: 16 rows of 64 B
+    const int logical = (lane & 3) ^ ((row >> 2) & 3);
+    voa[u] = (row * lda + logical * 8) * 2;
+    const int brow = wave * 4 + u * 2 + (lane >> 5);    // B: 2 rows of 512 B
+    const int blog = (lane & 31) ^ (4 * (brow & 3));
+    vob[u] = (n0 + blog * 8 < Ndim) ? static_cast<uint32_t>((brow * ldb + blog * 8) * 2)
+                                    : kOutOfRange;
+  }
+  auto issue = [&](bf16_t* As, int kt) {
+    bf16_t* Bs = As + kAB;
+    const bool live = kt < nk;
+    int k0 = min(kt, nk - 1) * BKS;
+    int half = 0;
+    if (MODE == DGRAD_UP && k0 >= f) {
+      half = 1;
+      k0 -= f;
+    }
+    const bf16_t* abase = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
+                          static_cast<int64_t>(m0) * lda + k0;
+    const bf16_t* wbase = ((MODE == DGRAD_UP && half) ? g.b1 : g.b0) + e * E_fd +
+                          static_cast<int64_t>(k0) * ldb + n0;
+    const auto ra = rsrc_at(abase, live ? ((mend - m0) * lda - k0) * 2 : 0);
+    const auto rb = rsrc_at(wbase, live ? ((Kh - k0) * ldb - n0) * 2 : 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16(ra, As + (wave * 32 + u * 16) * BKS, voa[u]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma16(rb, Bs + (wave * 4 + u * 2) * BN, vob[u]);
+  };
+
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int r = lane & 31, gq = lane >> 5;
+  const int key = (r >> 2) & 3;
+  uint32_t a_addr[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    a_addr[kk] = ((wm * 32 * FM + r) * BKS + (((2 * kk + gq) ^ key) * 8)) * 2;
+  const int G = lane >> 4, sl = lane & 15;
+  const int row0 = 8 * (G >> 1) + (sl >> 2);
+  const int sw = 4 * (row0 & 3);
+  uint32_t tb[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = j * 128 + wn * 32 + 16 * (G & 1) + 4 * (sl & 3);
+    tb[j] = kAB * 2 + row0 * (BN * 2) + (((col >> 3) ^ sw) << 4) + ((col >> 2) & 1) * 8;
+  }
+  auto base_of = [](const bf16_t* st) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16_t*)st));
+  };
+  typedef float f32x16v __attribute__((ext_vector_type(16)));
+  f32x16v c00 = {}, c01 = {}, c10 = {}, c11 = {}, c20 = {}, c21 = {}, c30 = {}, c31 = {};
+  bf16x8 fa0[FM], fa1[FM], fb0[FN], fb1[FN];
+  auto read_b = [&](bf16x8 (&fb)[FN], const bf16_t* st, int kk) {
+    const uint32_t off = kk * 16 * (BN * 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = dmaw::tr_frag(st, tb[j] + off, tb[j] + off + 4 * (BN * 2));
+  };
+  auto read_a = [&](bf16x8 (&fa)[FM], uint32_t addr) {
+    asm volatile(
+        "ds_read_b128 %0, %4 offset:0\n\t"
+        "ds_read_b128 %1, %4 offset:2048\n\t"
+        "ds_read_b128 %2, %4 offset:4096\n\t"
+        "ds_read_b128 %3, %4 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3])
+        : "v"(addr)
+        : "memory");
+  };
+#define MOE_MF(c, b, a) "v_mfma_f32_32x32x16_bf16 " c ", " b ", " a ", " c "\n\t"
+#define MOE_RD(o, off) "ds_read_b128 " o ", %18 offset:" off "\n\t"
+  // the eight MFMAs of fragments (ain, bin) with four A fragment reads at
+  // `addr` into aout interleaved; ends by waiting for the reads
+  auto mma_read = [&](const bf16x8 (&ain)[FM], const bf16x8 (&bin)[FN], bf16x8 (&aout)[FM],
+                      uint32_t addr) {
+    asm volatile(
+        MOE_RD("%8", "0")     MOE_MF("%0", "%16", "%12")
+        MOE_RD("%9", "2048")  MOE_MF("%1", "%17", "%12")
+        MOE_RD("%10", "4096") MOE_MF("%2", "%16", "%13")
+        MOE_RD("%11", "6144") MOE_MF("%3", "%17", "%13")
+                              MOE_MF("%4", "%16", "%14")
+                              MOE_MF("%5", "%17", "%14")
+                              MOE_MF("%6", "%16", "%15")
+                              MOE_MF("%7", "%17", "%15")
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11), "+v"(c20), "+v"(c21), "+v"(c30),
+          "+v"(c31), "=&v"(aout[0]), "=&v"(aout[1]), "=&v"(aout[2]), "=&v"(aout[3])
+        : "v"(ain[0]), "v"(ain[1]), "v"(ain[2]), "v"(ain[3]), "v"(bin[0]), "v"(bin[1]),
+          "v"(addr)
+        : "memory");
+  };
+#undef MOE_MF
+#undef MOE_RD
+  auto sync_stage = [&]() {
+    dmaw::mem_fence_compiler();
+    wait_vm<4>();
+    __builtin_amdgcn_s_barrier();
+    dmaw::mem_fence_compiler();
+  };
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  dmaw::mem_fence_compiler();
+  wait_vm<8>();
+  __builtin_amdgcn_s_barrier();
+  dmaw::mem_fence_compiler();
+  read_b(fb0, st0, 0);
+  read_a(fa0, base_of(st0) + a_addr[0]);
+  auto step = [&](int kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
+    read_b(fb1, cur, 1);
+    mma_read(fa0, fb0, fa1, base_of(cur) + a_addr[1]);   // kk = 0 MFMAs; A of kk = 1
+    sync_stage();                                         // stage kt + 1 ready
+    issue(fill, kt + 3);                                  // into stage (kt - 1) % 4
+    read_b(fb0, nxt, 0);
+    mma_read(fa1, fb1, fa0, base_of(nxt) + a_addr[0]);   // kk = 1 MFMAs; A of next kk = 0
+  };
+  const int nk4 = (nk + 3) & ~3;
+  for (int kt = 0; kt < nk4; kt += 4) {
+    step(kt, st0, st1, st3);
+    step(kt + 1, st1, st2, st0);
+    step(kt + 2, st2, st3, st1);
+    step(kt + 3, st3, st0, st2);
+  }
+  dmaw::mem_fence_compiler();
+  wait_vm<0>();
+  // cover the longest MFMA-to-VALU read-after-write distance
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __syncthreads();
+  AccT<true> acc;
+  acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
+  acc[2][0] = c20; acc[2][1] = c21; acc[3][0] = c30; acc[3][1] = c31;
+
+  // epilogue: bf16 tile (dh or dx) staged over the ring, rows [64 q, 64 q + 64)
+  // in stage q, chunks XORed by row; DGRAD_DOWN then applies da = dh b silu'(a),
+  // db = dh silu(a) with the saved a, b
+  auto row_ptr = [&](int m) -> bf16_t* {
+    const int q = m >> 6;
+    bf16_t* base = (q == 0) ? st0 : (q == 1) ? st1 : (q == 2) ? st2 : st3;
+    return base + (m & 63) * BN;
+  };
+  {
+    int skey;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(skey) : "v"(static_cast<int>(threadIdx.x & 15)));
+    for_each_quad<true>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+      *reinterpret_cast<uint2*>(row_ptr(m) + (((n >> 3) ^ skey) << 3) + (n & 4)) =
+          pack4(v0, v1, v2, v3);
+    });
+  }
+  __syncthreads();
+  const int nch = min(BN, Ndim - n0) / 8;
+  for (int v = tid; v < BM * (BN / 8); v += NT) {
+    const int rr = v / (BN / 8), c = v % (BN / 8);
+    if (rr >= rows || c >= nch) continue;
+    const uint4 hv = *reinterpret_cast<const uint4*>(row_ptr(rr) + ((c ^ (rr & 15)) << 3));
+    const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
+    if constexpr (MODE == DGRAD_DOWN) {
+      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
+      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      uint32_t daw[4], dbw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float da2[2], db2[2];
+        const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
+        const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+        const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float sg = sigmoid_f(aa[u]);
+          da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+          db2[u] = hh[u] * (aa[u] * sg);
+        }
+        daw[q] = bf_pack(da2[0], da2[1]);
+        dbw[q] = bf_pack(db2[0], db2[1]);
+      }
+      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+    } else {
+      *reinterpret_cast<uint4*>(g.c0 + o) = hv;
+    }
+  }
+}
+
 // Weight gradients: tile (e, m, n) of dW_z[e] = sum over the expert's rows p of
 // A[p][m] B[p][n]; z = 0: dW2 (A = dy, B = h), 1: dW1 (A = da, B = x),
 // 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
@@ -1882,12 +2105,14 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
   g.n_tiles_n = n_tiles_n;
   const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
   g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
-  if constexpr (MODE == UP || MODE == DOWN) {
 #ifndef MOE_NO_DMA
+  if constexpr (MODE == UP || MODE == DOWN) {
     hipLaunchKernelGGL((dma_rows_kernel<MODE>), dim3(g.grid_pad), dim3(dma::NT), 0, s, g);
-    return hipGetLastError();
-#endif
+  } else {
+    hipLaunchKernelGGL((dgrad_dma_kernel<MODE>), dim3(g.grid_pad), dim3(dma::NT), 0, s, g);
   }
+  return hipGetLastError();
+#endif
   hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
                      g);
   return hipGetLastError();
