@@ -1729,6 +1729,164 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   }
 }
 
+// Weight gradients with the small tile (128 x 128, 4 wavefronts of 64 x 64) on
+// a 4-stage LDS-DMA ring, one tile per workgroup: the same scheme as
+// wgrad_dma_kernel at half the width (256-byte rows: a DMA instruction fills
+// four rows; the 16 chunks of a row are XORed with 4 (row & 3)).
+namespace dmas {
+constexpr int BM = 128, BN = 128, BKS = 32, NT = 256, WAVES_N = 2, FM = 2, FN = 2;
+constexpr int kHalf = BKS * BM;              // elements of the A (or B) part
+constexpr int kStage = 2 * kHalf;            // 16 KB
+constexpr int kRowBytes = BM * 2;            // 256
+}  // namespace dmas
+
+__global__ __launch_bounds__(dmas::NT, 2) void wgrad_dma_small_kernel(Args g,
+                                                                      int32_t tiles_per_expert) {
+  using namespace dmas;
+  __shared__ __attribute__((aligned(16))) bf16_t st0[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st1[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st2[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st3[kStage];
+
+  const int flat = flat_tile();
+  const int per_z = g.E * tiles_per_expert;
+  const int z = flat / per_z;
+  if (z >= 3) return;
+  const int rem = flat - z * per_z;
+  const int e = rem / tiles_per_expert, t = rem % tiles_per_expert;
+  const int d = g.d, f = g.f;
+  const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
+  const int tiles_n = (Ndim + BN - 1) / BN;
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  if (m0 >= Mdim) return;
+  const bf16_t* Asrc = (z == 0) ? g.a0 : (z == 1 ? g.a1 : g.aux0);
+  const bf16_t* Bsrc = (z == 0) ? g.b0 : g.b1;
+  bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
+  const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
+  const int nk = (p1 - p0 + BKS - 1) / BKS;
+  const int mvalid = min(BM, Mdim - m0), nvalid = min(BN, Ndim - n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (nk == 0) {
+    for (int v = tid; v < BM * (BN / 8); v += NT) {
+      const int r = v / (BN / 8), c = v % (BN / 8);
+      if (r < mvalid && c * 8 < nvalid)
+        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+    return;
+  }
+  // DMA: wavefront w fills rows 8 w .. 8 w + 7 of A and of B, four rows per
+  // instruction; lane l -> row + l / 16, physical chunk l % 16
+  uint32_t voa[2], vob[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = wave * 8 + u * 4 + (lane >> 4);
+    const int logical = (lane & 15) ^ (4 * (row & 3));
+    const int col = logical * 8;
+    voa[u] = (m0 + col < Mdim) ? static_cast<uint32_t>((row * Mdim + col) * 2) : kOutOfRange;
+    vob[u] = (n0 + col < Ndim) ? static_cast<uint32_t>((row * Ndim + col) * 2) : kOutOfRange;
+  }
+  auto issue = [&](bf16_t* As, int kt) {
+    bf16_t* Bs = As + kHalf;
+    const bool live = kt < nk;
+    const int p = p0 + min(kt, nk - 1) * BKS;
+    const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
+                            live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
+                            live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 8 + u * 4) * BM, voa[u]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 8 + u * 4) * BN, vob[u]);
+  };
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int G = lane >> 4, sl = lane & 15;
+  const int row0 = 8 * (G >> 1) + (sl >> 2);
+  const int sw = 4 * (row0 & 3);
+  uint32_t ta[FM], tb[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int col = wm * 64 + i * 32 + 16 * (G & 1) + 4 * (sl & 3);
+    ta[i] = row0 * kRowBytes + (((col >> 3) ^ sw) << 4) + ((col >> 2) & 1) * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = j * 64 + wn * 32 + 16 * (G & 1) + 4 * (sl & 3);
+    tb[j] = kHalf * 2 + row0 * kRowBytes + (((col >> 3) ^ sw) << 4) + ((col >> 2) & 1) * 8;
+  }
+  AccT<false> acc;
+  zero_acc<false>(acc);
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  auto read_sub = [&](bf16x8 (&fa)[FM], bf16x8 (&fb)[FN], const bf16_t* stage, int kk) {
+    const uint32_t off = kk * 16 * kRowBytes;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = dmaw::tr_frag(stage, ta[i] + off, ta[i] + off + 4 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[j] = dmaw::tr_frag(stage, tb[j] + off, tb[j] + off + 4 * kRowBytes);
+  };
+  auto mma_sub = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  auto sync_stage = [&]() {
+    dmaw::mem_fence_compiler();
+    dma::wait_vm<4>();
+    __builtin_amdgcn_s_barrier();
+    dmaw::mem_fence_compiler();
+  };
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  dmaw::mem_fence_compiler();
+  dma::wait_vm<8>();
+  __builtin_amdgcn_s_barrier();
+  dmaw::mem_fence_compiler();
+  read_sub(fa0, fb0, st0, 0);
+  auto step = [&](int kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
+    read_sub(fa1, fb1, cur, 1);
+    mma_sub(fa0, fb0);
+    sync_stage();
+    issue(fill, kt + 3);
+    read_sub(fa0, fb0, nxt, 0);
+    mma_sub(fa1, fb1);
+  };
+  const int nk4 = (nk + 3) & ~3;
+  for (int kt = 0; kt < nk4; kt += 4) {
+    step(kt, st0, st1, st3);
+    step(kt + 1, st1, st2, st0);
+    step(kt + 2, st2, st3, st1);
+    step(kt + 3, st3, st0, st2);
+  }
+  dmaw::mem_fence_compiler();
+  dma::wait_vm<0>();
+  __syncthreads();
+  // epilogue: bf16 tile staged over stages 0-1 (rows [64 q, 64 q + 64) in stage
+  // q), chunks XORed by row, then coalesced 16-byte stores of the valid part
+  auto row_ptr = [&](int m) -> bf16_t* { return ((m >> 6) ? st1 : st0) + (m & 63) * BN; };
+  {
+    int skey;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(skey) : "v"(static_cast<int>(threadIdx.x & 15)));
+    for_each_quad<false>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+      *reinterpret_cast<uint2*>(row_ptr(m) + (((n >> 3) ^ skey) << 3) + (n & 4)) =
+          pack4(v0, v1, v2, v3);
+    });
+  }
+  __syncthreads();
+  const int nch = nvalid / 8;
+  for (int v = tid; v < BM * (BN / 8); v += NT) {
+    const int r = v / (BN / 8), c = v % (BN / 8);
+    if (r >= mvalid || c >= nch) continue;
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8) =
+        *reinterpret_cast<const uint4*>(row_ptr(r) + ((c ^ (r & 15)) << 3));
+  }
+}
+
 // Weight gradients: tile (e, m, n) of dW_z[e] = sum over the expert's rows p of
 // A[p][m] B[p][n]; z = 0: dW2 (A = dy, B = h), 1: dW1 (A = da, B = x),
 // 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
@@ -2213,6 +2371,14 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   }
   const int tpe = wgrad_tiles_per_expert<false>(dm);
   const int splits = wgrad_splits_bf16(dm);
+#if !defined(MOE_NO_DMA) && !defined(MOE_NO_DMA_SMALL_WGRAD)
+  if (splits == 1) {
+    const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+    g.grid_pad = static_cast<int32_t>(grid);
+    hipLaunchKernelGGL(wgrad_dma_small_kernel, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
+    return hipGetLastError();
+  }
+#endif
   const int64_t items = static_cast<int64_t>(3) * dm.E * tpe * splits;
   const int64_t grid = std::max(std::min(items, static_cast<int64_t>(2 * kCUs)),
                                 (items + kMaxItems - 1) / kMaxItems);
