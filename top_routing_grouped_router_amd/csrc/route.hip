@@ -21,6 +21,17 @@
 namespace moe {
 namespace {
 
+#ifdef MOE_TRACE
+// Timing build only: router workgroup timelines (thread 0 writes the 100 MHz
+// wall clock at marked points).
+constexpr int kRtSlots = 16;
+__device__ uint64_t moe_route_trace[1024 * kRtSlots];
+#define MOE_RT_MARK(i) \
+  if (threadIdx.x == 0 && blockIdx.x < 1024) moe_route_trace[blockIdx.x * kRtSlots + (i)] = wall_clock64()
+#else
+#define MOE_RT_MARK(i) ((void)0)
+#endif
+
 constexpr int kThreads = 256;
 constexpr int kDChunk = 32;
 constexpr int kMaxE = 256;
@@ -226,16 +237,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 // experts 16j + l%16, so every token's E logits sit in one 16-lane group:
 // top-k, gates, margin and the full softmax run there with 16-lane shuffles.
 // ---------------------------------------------------------------------------
-#ifdef MOE_TRACE
-// Timing build only: router workgroup timelines (thread 0 writes the 100 MHz
-// wall clock at marked points).
-constexpr int kRtSlots = 16;
-__device__ uint64_t moe_route_trace[1024 * kRtSlots];
-#define MOE_RT_MARK(i) \
-  if (threadIdx.x == 0 && blockIdx.x < 1024) moe_route_trace[blockIdx.x * kRtSlots + (i)] = wall_clock64()
-#else
-#define MOE_RT_MARK(i) ((void)0)
-#endif
 constexpr int kMTile = 64;       // tokens per workgroup
 constexpr int kMBK = 32;         // k chunk
 constexpr int kMLd = kMBK + 8;   // LDS row stride (elements)
@@ -249,7 +250,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // its partner does, so all 16 lanes end bitwise identical.
 template <int CTRL>
 __device__ __forceinline__ int row_rot(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);   // every lane has a source
 }
 template <int CTRL>
 __device__ __forceinline__ float row_rot(float v) {
@@ -283,6 +284,34 @@ __device__ __forceinline__ float group16_sum(float v) {
   return v;
 }
 
+// Selection keys: one unsigned 64-bit integer per (logit, expert) whose
+// order is the selection order, larger logit first and, on equal logits, the
+// smaller expert id (the high word is the logit's bits made monotone: sign
+// bit set for non-negative values, all bits inverted for negative ones; the
+// low word is the inverted expert id).  -0 is folded into +0 first so that
+// equal logits give equal high words.  Key 0 lies below every real key and
+// marks experts already taken or absent.
+__device__ __forceinline__ uint64_t sel_key(float v, int32_t e) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(~e);
+}
+__device__ __forceinline__ float sel_key_value(uint64_t k) {
+  uint32_t u = static_cast<uint32_t>(k >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ int32_t sel_key_expert(uint64_t k) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(k));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t key_max_level(uint64_t k) {
+  const uint32_t lo = static_cast<uint32_t>(row_rot<CTRL>(static_cast<int>(static_cast<uint32_t>(k))));
+  const uint32_t hi = static_cast<uint32_t>(row_rot<CTRL>(static_cast<int>(static_cast<uint32_t>(k >> 32))));
+  const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+  return o > k ? o : k;
+}
+
 // Per-token epilogue shared by the matrix-core router kernels: lane (g, c) of
 // wavefront `wave` holds the logits of tokens t0 + 16 wave + 4 g + q (q < 4)
 // for experts 16 j + c in acc[j][q].  Writes logits, top-k ids and gates,
@@ -302,66 +331,124 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
 #pragma unroll
   for (int j = 0; j < NT; ++j) { my_psum[j] = 0.f; my_cnt[j] = 0; }
   int32_t ties = 0;
+  // the lane's 4 tokens go through every step together, so the 4 dependency
+  // chains of each cross-lane reduction interleave
+  float v[4][NT];
+  bool live[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t tg = t0 + wave * 16 + g * 4 + q;
-    const bool live = tg < a.T;
-    float v[NT];
+    live[q] = tg < a.T;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int e = 16 * j + c;
-      v[j] = (e < E) ? acc[j][q] : -INFINITY;
-      if (live && e < E) a.logits[tg * E + e] = acc[j][q];
+      v[q][j] = (e < E) ? acc[j][q] : -INFINITY;
+      if (live[q] && e < E) a.logits[tg * E + e] = acc[j][q];
     }
-    uint32_t taken = 0;
-    float my_v = -INFINITY, v_top = -INFINITY, v_km1 = 0.f, v_k = 0.f;
-    int32_t my_i = 0;
-    const int rounds = (k < E) ? k + 1 : k;
-    for (int r = 0; r < rounds; ++r) {
-      Key best{-INFINITY, 0x7fffffff};
+  }
+  MOE_RT_MARK(4);
+  uint64_t key[4][NT];
+  uint64_t my_key[4], k_top[4], k_km1[4], k_k[4];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int e = 16 * j + c;
-        if (e < E && !(taken & (1u << j)) && better(v[j], e, best.v, best.i)) {
-          best.v = v[j];
-          best.i = e;
-        }
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) key[q][j] = (16 * j + c < E) ? sel_key(v[q][j], 16 * j + c) : 0ull;
+    my_key[q] = k_top[q] = k_km1[q] = k_k[q] = 0ull;
+  }
+  // round r finds the r-th best key of each token (a max over the lane's own
+  // keys, then over the 16 lanes); rounds before k retire it
+  const int rounds = (k < E) ? k + 1 : k;
+  for (int r = 0; r < rounds; ++r) {
+    uint64_t best[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      best[q] = key[q][0];
+#pragma unroll
+      for (int j = 1; j < NT; ++j) best[q] = key[q][j] > best[q] ? key[q][j] : best[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) best[q] = key_max_level<kRowRor8>(best[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) best[q] = key_max_level<kRowRor4>(best[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) best[q] = key_max_level<kRowRor2>(best[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) best[q] = key_max_level<kRowRor1>(best[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (r == 0) k_top[q] = best[q];
+      if (r == k - 1) k_km1[q] = best[q];
+      if (r == k) k_k[q] = best[q];
+      if (c == r) my_key[q] = best[q];
+      if (r < k) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) key[q][j] = (key[q][j] == best[q]) ? 0ull : key[q][j];
       }
-      best = group16_argmax(best);
-      if (r == 0) v_top = best.v;
-      if (r == k - 1) v_km1 = best.v;
-      if (r == k) v_k = best.v;
-      if (c == r) { my_v = best.v; my_i = best.i; }
-      if (r < k && (best.i & 15) == c) taken |= 1u << (best.i >> 4);
     }
-    float ex[NT];
-    float part = 0.f;
+  }
+  // taken experts: the real keys retired by the first k rounds
+  uint32_t taken[4];
+  float my_v[4], v_top[4], v_km1[4], v_k[4];
+  int32_t my_i[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v_top[q] = sel_key_value(k_top[q]);
+    v_km1[q] = sel_key_value(k_km1[q]);
+    v_k[q] = sel_key_value(k_k[q]);
+    taken[q] = 0u;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (16 * j + c < E && key[q][j] == 0ull) taken[q] |= 1u << j;
+    my_v[q] = (c < k) ? sel_key_value(my_key[q]) : -INFINITY;
+    my_i[q] = (c < k) ? sel_key_expert(my_key[q]) : 0;
+  }
+  MOE_RT_MARK(5);
+  float ex[4][NT], part[4], my_e[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    part[q] = 0.f;
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int e = 16 * j + c;
-      ex[j] = (e < E) ? __expf(v[j] - v_top) : 0.f;
-      part += ex[j];
+      ex[q][j] = (e < E) ? __expf(v[q][j] - v_top[q]) : 0.f;
+      part[q] += ex[q][j];
     }
-    const float inv = 1.0f / group16_sum(part);
-    const float my_e = (c < k) ? __expf(my_v - v_top) : 0.f;
-    const float z = group16_sum(my_e);
-    if (live) {
+    my_e[q] = (c < k) ? __expf(my_v[q] - v_top[q]) : 0.f;
+  }
+  float z[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) z[q] = my_e[q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor8>(part[q]); z[q] += row_rot<kRowRor8>(z[q]); }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor4>(part[q]); z[q] += row_rot<kRowRor4>(z[q]); }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor2>(part[q]); z[q] += row_rot<kRowRor2>(z[q]); }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor1>(part[q]); z[q] += row_rot<kRowRor1>(z[q]); }
+  MOE_RT_MARK(6);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t tg = t0 + wave * 16 + g * 4 + q;
+    const float inv = 1.0f / part[q];
+    if (live[q]) {
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        my_psum[j] += ex[j] * inv;
-        if (taken & (1u << j)) my_cnt[j] += 1;
+        my_psum[j] += ex[q][j] * inv;
+        if (taken[q] & (1u << j)) my_cnt[j] += 1;
       }
       if (c < k) {
-        a.idx[tg * k + c] = my_i;
-        a.gate[tg * k + c] = my_e / z;
+        a.idx[tg * k + c] = my_i[q];
+        a.gate[tg * k + c] = my_e[q] / z[q];
       }
-      const float m = (k < E) ? v_km1 - v_k : INFINITY;
+      const float m = (k < E) ? v_km1[q] - v_k[q] : INFINITY;
       if (c == 0) {
         a.margin[tg] = m;
         ties += (m < a.eps) ? 1 : 0;
       }
     }
   }
+  MOE_RT_MARK(7);
   // fold the 4 lane groups (fixed xor order), then the 4 waves (fixed order)
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -380,6 +467,7 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
   ties += __shfl_xor(ties, 32, 64);
   if (lane == 0) tie_w[wave] = ties;
   __syncthreads();
+  MOE_RT_MARK(8);
   for (int e = tid; e < E; e += kThreads) {
     const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
     const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
@@ -430,11 +518,11 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
       const float w[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
       uint32_t hi[2], mi[2], lo[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int p = 0; p < 2; ++p) {
         bf16_t h2[2], m2[2], l2[2];
 #pragma unroll
         for (int z = 0; z < 2; ++z) {
-          const float f0 = w[2 * u + z];
+          const float f0 = w[2 * p + z];
           const bf16_t h = f32_to_bf16(f0);
           const float r1 = f0 - bf16_to_f32(h);
           const bf16_t m = f32_to_bf16(r1);
@@ -443,9 +531,9 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
           m2[z] = m;
           l2[z] = f32_to_bf16(r2);
         }
-        hi[u] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
-        mi[u] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
-        lo[u] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+        hi[p] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+        mi[p] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+        lo[p] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
       }
       *reinterpret_cast<uint2*>(&wsh[0][e][q * 4]) = make_uint2(hi[0], hi[1]);
       *reinterpret_cast<uint2*>(&wsh[1][e][q * 4]) = make_uint2(mi[0], mi[1]);
@@ -516,37 +604,54 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
     xa[kt] = *reinterpret_cast<const uint4*>(xrow + kt * 32);
     if (!row_ok) xa[kt] = make_uint4(0u, 0u, 0u, 0u);
   }
-  // split Wr (E x d fp32; rows >= E are zero) into LDS, 4 weights per step
+  // split Wr (E x d fp32; rows >= E are zero) into LDS, 4 weights per
+  // vector; the vectors of a thread are loaded in batches of 8 before any is
+  // split, so their latencies overlap
   constexpr int kRowsP = 16 * NT;
-  const int nvec = kRowsP * d / 4;
-  for (int v = tid; v < nvec; v += kThreads) {
-    const int e = v / (d / 4), q = v % (d / 4);
-    const float4 w4 = (e < E) ? *reinterpret_cast<const float4*>(a.wr + static_cast<int64_t>(e) * d + q * 4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float w[4] = {w4.x, w4.y, w4.z, w4.w};
-    uint32_t hi[2], mi[2], lo[2];
+  constexpr int kDv = 8 * NKC;                        // float4 vectors per row (d / 4)
+  constexpr int kPer = kRowsP * kDv / kThreads;       // vectors per thread
+  static_assert(kRowsP * kDv % kThreads == 0, "whole vectors per thread");
+  constexpr int kBatch = kPer < 8 ? kPer : 8;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16_t h2[2], m2[2], l2[2];
+  for (int b0 = 0; b0 < kPer; b0 += kBatch) {
+    float4 wb[kBatch];
 #pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const float f0 = w[2 * u + z];
-        const bf16_t h = f32_to_bf16(f0);
-        const float r1 = f0 - bf16_to_f32(h);
-        const bf16_t m = f32_to_bf16(r1);
-        const float r2 = r1 - bf16_to_f32(m);
-        h2[z] = h;
-        m2[z] = m;
-        l2[z] = f32_to_bf16(r2);
-      }
-      hi[u] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
-      mi[u] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
-      lo[u] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+    for (int u = 0; u < kBatch; ++u) {
+      const int v = tid + (b0 + u) * kThreads;
+      const int e = v / kDv, q = v % kDv;
+      wb[u] = (e < E) ? *reinterpret_cast<const float4*>(a.wr + static_cast<int64_t>(e) * d + q * 4)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    bf16_t* row = wsh_dyn + e * kLd + q * 4;
-    *reinterpret_cast<uint2*>(row) = make_uint2(hi[0], hi[1]);
-    *reinterpret_cast<uint2*>(row + kRowsP * kLd) = make_uint2(mi[0], mi[1]);
-    *reinterpret_cast<uint2*>(row + 2 * kRowsP * kLd) = make_uint2(lo[0], lo[1]);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int v = tid + (b0 + u) * kThreads;
+      const int e = v / kDv, q = v % kDv;
+      const float4 w4 = wb[u];
+      const float w[4] = {w4.x, w4.y, w4.z, w4.w};
+      uint32_t hi[2], mi[2], lo[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        bf16_t h2[2], m2[2], l2[2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+          const float f0 = w[2 * p + z];
+          const bf16_t h = f32_to_bf16(f0);
+          const float r1 = f0 - bf16_to_f32(h);
+          const bf16_t m = f32_to_bf16(r1);
+          const float r2 = r1 - bf16_to_f32(m);
+          h2[z] = h;
+          m2[z] = m;
+          l2[z] = f32_to_bf16(r2);
+        }
+        hi[p] = h2[0] | (static_cast<uint32_t>(h2[1]) << 16);
+        mi[p] = m2[0] | (static_cast<uint32_t>(m2[1]) << 16);
+        lo[p] = l2[0] | (static_cast<uint32_t>(l2[1]) << 16);
+      }
+      bf16_t* row = wsh_dyn + e * kLd + q * 4;
+      *reinterpret_cast<uint2*>(row) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2*>(row + kRowsP * kLd) = make_uint2(mi[0], mi[1]);
+      *reinterpret_cast<uint2*>(row + 2 * kRowsP * kLd) = make_uint2(lo[0], lo[1]);
+    }
   }
   __syncthreads();
   MOE_RT_MARK(1);
@@ -576,10 +681,13 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
 // One workgroup (1024 threads) per balancing block r (grid G), all experts in
 // one pass: thread (slice, e) with slice < SL = 1024 / E_p (E_p: E rounded up
 // to a power of two, at least 16) adds tiles slice, slice + SL, ... of block r
-// in tile order (8 loads in flight), then thread e adds the SL slice sums in
-// slice order.  Block 0 also totals the near-tie counts (strided per thread,
-// then a fixed tree).
+// in tile order (16 loads in flight); the slice sums are folded in a fixed
+// order, first across the slices inside a wavefront (lane xor 16, then 32),
+// then across wavefronts through LDS in wavefront order.  The expert products
+// f_e P_e and (block 0) the near-tie counts are reduced by wavefront 0 alone,
+// again in a fixed order.
 constexpr int kFinThreads = 1024;
+constexpr int kFinWaves = kFinThreads / 64;
 __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
     const float* psum, const int32_t* pcnt, const int32_t* ptie, int32_t n_tiles,
     int32_t tiles_per_group, int64_t T, int32_t E, int32_t k, int32_t* gcount, float* gprob,
@@ -587,9 +695,9 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
   __shared__ float sp[kFinThreads];
   __shared__ int32_t sc[kFinThreads];
   __shared__ float fp[kMaxE];
-  __shared__ int32_t st[kFinThreads];
+  __shared__ int32_t st[kFinWaves];
   const int r = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int Ep = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
   const int SL = kFinThreads / Ep;
   const int slice = tid / Ep, e = tid % Ep;
@@ -599,33 +707,45 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
   float s = 0.f;
   int32_t c = 0;
   if (e < E) {
-    for (int i0 = slice; i0 < tiles_per_group; i0 += SL * 8) {
-      float ps[8];
-      int32_t pc[8];
+    for (int i0 = slice; i0 < tiles_per_group; i0 += SL * 16) {
+      float ps[16];
+      int32_t pc[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int i = min(i0 + SL * u, tiles_per_group - 1);
         const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
         ps[u] = psum[tile * E + e];
         pc[u] = pcnt[tile * E + e];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         if (i0 + SL * u >= tiles_per_group) break;
         s += ps[u];
         c += pc[u];
       }
     }
   }
+  // slices inside one wavefront (E_p < 64): lanes e, e + E_p, ... of a wavefront
+  if (Ep <= 16) {
+    s += __shfl_xor(s, 16, 64);
+    c += __shfl_xor(c, 16, 64);
+  }
+  if (Ep <= 32) {
+    s += __shfl_xor(s, 32, 64);
+    c += __shfl_xor(c, 32, 64);
+  }
   sp[tid] = s;
   sc[tid] = c;
   __syncthreads();
   if (tid < E) {
+    // one partial per wavefront for E_p <= 64, else one per slice
+    const int step = Ep < 64 ? 64 : Ep;
+    const int n_part = kFinThreads / step;
     float S = 0.f;
     int32_t C = 0;
-    for (int q = 0; q < SL; ++q) {
-      S += sp[q * Ep + tid];
-      C += sc[q * Ep + tid];
+    for (int q = 0; q < n_part; ++q) {
+      S += sp[q * step + tid];
+      C += sc[q * step + tid];
     }
     const float P = (per_group > 0) ? static_cast<float>(S / per_group) : 0.f;
     const float fr = (per_group > 0) ? static_cast<float>(C / (per_group * k)) : 0.f;
@@ -633,23 +753,27 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
     if (gprob) gprob[static_cast<int64_t>(r) * E + tid] = P;
     fp[tid] = fr * P;
   }
-  __syncthreads();
-  // fixed-order tree over the (zero-padded) 256 products
-  for (int w = kMaxE / 2; w >= 1; w >>= 1) {
-    if (tid < w) fp[tid] += fp[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0 && gaux) gaux[r] = static_cast<float>(E) * fp[0];
+  int32_t t = 0;
   if (r == 0 && tie_count) {
-    int32_t t = 0;
     for (int i = tid; i < n_tiles; i += kFinThreads) t += ptie[i];
-    st[tid] = t;
-    __syncthreads();
-    for (int w = kFinThreads / 2; w >= 1; w >>= 1) {
-      if (tid < w) st[tid] += st[tid + w];
-      __syncthreads();
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) t += __shfl_xor(t, m, 64);
+    if (lane == 0) st[wave] = t;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // fixed order over the (zero-padded) 256 products: 4 per lane, then a
+    // lane xor tree
+    float v = ((fp[lane] + fp[lane + 64]) + fp[lane + 128]) + fp[lane + 192];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    if (lane == 0 && gaux) gaux[r] = static_cast<float>(E) * v;
+    if (r == 0 && tie_count) {
+      int32_t tt = lane < kFinWaves ? st[lane] : 0;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) tt += __shfl_xor(tt, m, 64);
+      if (lane == 0) *tie_count = tt;
     }
-    if (tid == 0) *tie_count = st[0];
   }
 }
 
