@@ -1106,11 +1106,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, static_cast<int>(voff), 0, 0, 0);
 }
-// s_waitcnt with vmcnt = N (N < 16), expcnt and lgkmcnt left free
+// s_waitcnt with vmcnt = N (N < 64: bits 3-0 and 15-14), expcnt and lgkmcnt left free
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 }  // namespace dma
 
