@@ -1740,13 +1740,22 @@ constexpr int kStage = 2 * kHalf;            // 16 KB
 constexpr int kRowBytes = BM * 2;            // 256
 }  // namespace dmas
 
-__global__ __launch_bounds__(dmas::NT, 2) void wgrad_dma_small_kernel(Args g,
-                                                                      int32_t tiles_per_expert) {
+// NST = 4 (64 KB, two workgroups per CU) or 8 (128 KB, one workgroup per CU,
+// for grids that give each CU at most one tile: twice the loads in flight).
+template <int NST>
+__global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args g,
+                                                                          int32_t tiles_per_expert) {
   using namespace dmas;
+  static_assert(NST == 4 || NST == 8, "4 or 8 stages");
+  constexpr int kX = NST == 8 ? kStage : 8;   // stages 4-7 exist only with NST = 8
   __shared__ __attribute__((aligned(16))) bf16_t st0[kStage];
   __shared__ __attribute__((aligned(16))) bf16_t st1[kStage];
   __shared__ __attribute__((aligned(16))) bf16_t st2[kStage];
   __shared__ __attribute__((aligned(16))) bf16_t st3[kStage];
+  __shared__ __attribute__((aligned(16))) bf16_t st4[kX];
+  __shared__ __attribute__((aligned(16))) bf16_t st5[kX];
+  __shared__ __attribute__((aligned(16))) bf16_t st6[kX];
+  __shared__ __attribute__((aligned(16))) bf16_t st7[kX];
 
   const int flat = flat_tile();
   const int per_z = g.E * tiles_per_expert;
@@ -1834,17 +1843,20 @@ __global__ __launch_bounds__(dmas::NT, 2) void wgrad_dma_small_kernel(Args g,
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
+  // each wavefront issues 4 loads per step.  At the barrier of step kt the
+  // loads of steps kt + 1 .. kt + NST - 2 are outstanding and step kt + 1 must
+  // have landed: NST - 3 steps may stay in flight
   auto sync_stage = [&]() {
     dmaw::mem_fence_compiler();
-    dma::wait_vm<4>();
+    dma::wait_vm<4 * (NST - 3)>();
     __builtin_amdgcn_s_barrier();
     dmaw::mem_fence_compiler();
   };
-  issue(st0, 0);
-  issue(st1, 1);
-  issue(st2, 2);
+  bf16_t* const stg[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+#pragma unroll
+  for (int q = 0; q < NST - 1; ++q) issue(stg[q], q);
   dmaw::mem_fence_compiler();
-  dma::wait_vm<8>();
+  dma::wait_vm<4 * (NST - 2)>();   // step 0 has landed
   __builtin_amdgcn_s_barrier();
   dmaw::mem_fence_compiler();
   read_sub(fa0, fb0, st0, 0);
@@ -1852,16 +1864,15 @@ __global__ __launch_bounds__(dmas::NT, 2) void wgrad_dma_small_kernel(Args g,
     read_sub(fa1, fb1, cur, 1);
     mma_sub(fa0, fb0);
     sync_stage();
-    issue(fill, kt + 3);
+    issue(fill, kt + NST - 1);
     read_sub(fa0, fb0, nxt, 0);
     mma_sub(fa1, fb1);
   };
-  const int nk4 = (nk + 3) & ~3;
-  for (int kt = 0; kt < nk4; kt += 4) {
-    step(kt, st0, st1, st3);
-    step(kt + 1, st1, st2, st0);
-    step(kt + 2, st2, st3, st1);
-    step(kt + 3, st3, st0, st2);
+  const int nkp = (nk + NST - 1) / NST * NST;
+  for (int kt = 0; kt < nkp; kt += NST) {
+#pragma unroll
+    for (int q = 0; q < NST; ++q)
+      step(kt + q, stg[q], stg[(q + 1) % NST], stg[(q + NST - 1) % NST]);
   }
   dmaw::mem_fence_compiler();
   dma::wait_vm<0>();
@@ -2375,7 +2386,10 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   if (splits == 1) {
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
-    hipLaunchKernelGGL(wgrad_dma_small_kernel, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
+    if (grid <= static_cast<unsigned>(kCUs))
+      hipLaunchKernelGGL(wgrad_dma_small_kernel<8>, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
+    else
+      hipLaunchKernelGGL(wgrad_dma_small_kernel<4>, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
     return hipGetLastError();
   }
 #endif
