@@ -62,17 +62,11 @@ GEMM_CALLS = ("moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
 
 
 def wgrad_kernels(dm):
-    """moe_expert_wgrad is one kernel unless it splits K (then it adds a reduce)."""
-    return 1 if wgrad_split_k(dm) <= 1 else 2
-
-
-def wgrad_split_k(dm):
-    # mirrors the library's split rule: ceil(1024 / (3 E tiles)), 1..8, bf16 only
-    if dm.act != 1:
-        return 1
-    tiles = ((dm.d + 127) // 128) * ((dm.f + 127) // 128)
-    base = 3 * dm.E * tiles
-    return max(1, min((1024 + base - 1) // base, 8))
+    """Kernels moe_expert_wgrad enqueues for these dims, as the library reports
+    (1, or 2 when it splits the expert rows and adds a reduction)."""
+    import ctypes
+    import top_routing_grouped_router_amd._lib as L
+    return int(L.lib().moe_expert_wgrad_launches(ctypes.byref(dm)))
 
 
 def roofline_entry(flops, nbytes, seconds, act):
@@ -86,7 +80,7 @@ def roofline_entry(flops, nbytes, seconds, act):
             "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "moe_expert_up": "gemm_bf16.hip", "moe_expert_down": "gemm_bf16.hip",
     "moe_expert_dgrad_down": "gemm_bf16.hip", "moe_expert_dgrad_up": "gemm_bf16.hip",

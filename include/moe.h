@@ -90,6 +90,13 @@ const char* moe_last_error(void);
  * are invalid. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups);
 
+/* [host] Kernels that moe_expert_wgrad enqueues for these dims: 1 (one
+ * kernel writes dW1, dW3, dW2), 2 (the expert rows are split into parts whose
+ * fp32 partial tiles a second kernel adds in a fixed order), or 0 when the
+ * dims are invalid.  For profilers and benchmarks that attribute time to
+ * kernels. */
+int32_t moe_expert_wgrad_launches(const moe_dims* dims);
+
 /*
  * moe_route -- router logits, top-k gating, margins, near-ties and
  * per-block load-balancing statistics.

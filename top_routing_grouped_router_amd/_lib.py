@@ -34,7 +34,7 @@ EXPORTED = (
     "moe_grouped_swiglu_fwd", "moe_combine", "moe_combine_bwd", "moe_grouped_swiglu_bwd",
     "moe_route_bwd", "moe_coselect", "moe_dispatch_plan", "moe_placement_greedy",
     "moe_check_placement", "moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
-    "moe_expert_dgrad_up", "moe_expert_wgrad",
+    "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_wgrad_launches",
 )
 
 
@@ -61,6 +61,7 @@ _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (_SZ, [_DIMS, _I32]),
+    "moe_expert_wgrad_launches": (_I32, [_DIMS]),
     "moe_route": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_swiglu_fwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

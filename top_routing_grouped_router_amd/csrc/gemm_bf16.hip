@@ -2245,7 +2245,10 @@ constexpr int kCUs = 256;
 // (and, for UP, f splits into 128-column halves); otherwise the small tile.
 bool use_big_rows(const moe_dims& dm, int n_big, int K) {
   const int64_t R = dm.T * dm.k;
-  return K >= 1024 && (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
+#ifndef MOE_BIG_ROWS_MIN_K
+#define MOE_BIG_ROWS_MIN_K 1024
+#endif
+  return K >= MOE_BIG_ROWS_MIN_K && (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
 }
 bool use_big_wgrad(const moe_dims& dm) {
   return 3LL * dm.E * wgrad_tiles_per_expert<true>(dm) >= 2 * kCUs;

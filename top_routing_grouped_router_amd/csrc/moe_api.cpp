@@ -242,6 +242,12 @@ size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups) {
   return workspace_needed(*dims, n_groups);
 }
 
+int32_t moe_expert_wgrad_launches(const moe_dims* dims) {
+  if (check_dims(dims, __func__) != MOE_OK) return 0;
+  if (dims->act != MOE_BF16) return 1;
+  return moe::wgrad_splits_bf16(*dims) > 1 ? 2 : 1;
+}
+
 moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router, float* logits,
                      int32_t* topk_idx, float* topk_gate, float* margin, float near_tie_eps,
                      int32_t* near_tie_count, int32_t n_groups, int32_t* group_count,
