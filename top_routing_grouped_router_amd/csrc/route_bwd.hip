@@ -96,9 +96,13 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
 
 // dWr[e] = sum over rows p of expert e (ascending token order) of
 // dl_perm[p] * x[src[p]].  The expert's rows are cut into `splits` contiguous
-// parts; workgroup (col block, split, e) sums its part (wave w takes rows
-// w, w+4, ..., four rows in flight; the four waves are combined in order), and
-// a second kernel adds the parts in split order.  Each lane owns 4 columns.
+// parts; workgroup (col block, split, e) sums its part: wavefront w takes the
+// runs of kRows rows w, w + 4, ... of it in order (a run's row ids and dl are
+// one vector load, then all kRows x rows are in flight), and the four
+// wavefronts are combined in order.  A second kernel adds the parts in split
+// order.  Each lane owns 4 columns.  (A last-workgroup-reduces variant needs a
+// device-scope release per workgroup, which on this multi-L2 part writes back
+// the XCD's L2 each time and cost more than the second launch.)
 
 __device__ __forceinline__ void load4(const float* p, float* v) {
   const float4 q = *reinterpret_cast<const float4*>(p);
@@ -110,6 +114,8 @@ __device__ __forceinline__ void load4(const bf16_t* p, float* v) {
   v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
 }
 
+constexpr int kRows = 8;   // rows per wavefront in flight
+
 template <typename TA>
 __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
     const TA* __restrict__ x, const int32_t* __restrict__ offsets,
@@ -117,32 +123,38 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
     float* __restrict__ partial, int32_t d, int32_t splits) {
   __shared__ float red[4][256];
   const int e = blockIdx.z, sp = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int col0 = blockIdx.x * 256 + lane * 4;
   const int32_t p0 = offsets[e], n = offsets[e + 1] - p0;
   const int32_t lo = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * sp) / splits);
   const int32_t hi = p0 + static_cast<int32_t>((static_cast<int64_t>(n) * (sp + 1)) / splits);
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (col0 < d) {
-    int32_t p = lo + wave;
-    for (; p + 12 < hi; p += 16) {
-      float g[4], v[4][4];
+  if (col0 < d) {   // lanes 0 .. kRows - 1 always pass (d % 64 == 0)
+    for (int32_t p = lo + wave * kRows; p < hi; p += 4 * kRows) {
+      // rows p .. p + kRows - 1: lanes 0 .. kRows - 1 load their ids and
+      // weights (one vector load each, clamped in bounds), then broadcast
+      const int32_t my_q = min(p + (lane & (kRows - 1)), hi - 1);
+      const int32_t my_s = src[my_q];
+      const float my_g = dl_perm[my_q];
+      int32_t s[kRows];
+      float g[kRows];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        g[u] = dl_perm[p + 4 * u];
-        load4(x + static_cast<int64_t>(src[p + 4 * u]) * d + col0, v[u]);
+      for (int u = 0; u < kRows; ++u) {
+        s[u] = __builtin_amdgcn_readlane(my_s, u);
+        g[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_g), u));
       }
+      float v[kRows][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kRows; ++u) load4(x + static_cast<int64_t>(s[u]) * d + col0, v[u]);
+      // branch-free: a branch here would let the compiler sink each load into
+      // its own block and serialise them; rows past hi weigh 0
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
-    }
-    for (; p < hi; p += 4) {
-      const float g = dl_perm[p];
-      float v[4];
-      load4(x + static_cast<int64_t>(src[p]) * d + col0, v);
+      for (int u = 0; u < kRows; ++u) {
+        const float w = (p + u < hi) ? g[u] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
+      }
     }
   }
 #pragma unroll
