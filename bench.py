@@ -7,6 +7,10 @@ tokens: moe_route -> moe_permute -> moe_expert_up -> moe_expert_down ->
 moe_combine -> moe_combine_bwd -> moe_expert_dgrad_down -> moe_expert_dgrad_up
 -> moe_expert_wgrad -> moe_route_bwd (the kernel-level phases of
 moe_grouped_swiglu_fwd/bwd, so each GEMM kernel can be timed on its own).
+By default the permutation is a plan only and moe_expert_up / moe_expert_wgrad
+read their input rows from X through src_token (the *_gather calls, reported
+as moe_permute_plan, moe_expert_up_gather, moe_expert_wgrad_gather);
+--no-gather materialises x_perm instead.  Both compute the same bits.
 Inputs and weights are resident in HBM before timing starts.  Prints one JSON
 line.
 
@@ -45,20 +49,27 @@ def algorithmic_work(cfg):
         "moe_route": (2 * T * d * E,
                       T * d * s + E * d * 4 + T * E * 4 + T * k * (i4 + 4) + T * 4, 2),
         "moe_permute": (0, T * k * i4 + T * d * s + R * d * s + 2 * R * i4 + (2 * E + 1) * i4, 4),
+        # plan only (gathered expert input): indices in, counts/offsets/pos/src out
+        "moe_permute_plan": (0, T * k * i4 + 2 * R * i4 + (2 * E + 1) * i4, 2),
         "moe_expert_up": (4 * R * d * f, R * d * s + 2 * Wf + 3 * R * f * s, 1),
+        "moe_expert_up_gather": (4 * R * d * f, R * d * s + R * i4 + 2 * Wf + 3 * R * f * s, 1),
         "moe_expert_down": (2 * R * d * f, R * f * s + Wf + R * d * s, 1),
         "moe_combine": (2 * R * d, R * d * s + T * d * s + T * k * (i4 + 4), 1),
         "moe_combine_bwd": (2 * R * d, T * d * s + 2 * R * d * s + T * k * (i4 + 8), 1),
         "moe_expert_dgrad_down": (2 * R * d * f, R * d * s + Wf + 4 * R * f * s, 1),
         "moe_expert_dgrad_up": (4 * R * d * f, 2 * R * f * s + 2 * Wf + R * d * s, 1),
         "moe_expert_wgrad": (6 * R * d * f, 2 * R * d * s + 3 * R * f * s + 3 * Wf, None),
+        "moe_expert_wgrad_gather": (6 * R * d * f, 2 * R * d * s + R * i4 + 3 * R * f * s + 3 * Wf,
+                                    None),
         "moe_route_bwd": (4 * R * d, T * d * s + E * d * 4 + R * d * s + T * d * s + E * d * 4
                           + T * k * 12 + R * 8, 4),
     }
 
 
 GEMM_CALLS = ("moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
-              "moe_expert_dgrad_up", "moe_expert_wgrad")
+              "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_up_gather",
+              "moe_expert_wgrad_gather")
+WGRAD_CALLS = ("moe_expert_wgrad", "moe_expert_wgrad_gather")
 
 
 def wgrad_kernels(dm):
@@ -83,6 +94,8 @@ def roofline_entry(flops, nbytes, seconds, act):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "moe_expert_up": "gemm_bf16.hip", "moe_expert_down": "gemm_bf16.hip",
+    "moe_expert_up_gather": "gemm_bf16.hip", "moe_expert_wgrad_gather": "gemm_bf16.hip",
+    "moe_permute_plan": "permute.hip",
     "moe_expert_dgrad_down": "gemm_bf16.hip", "moe_expert_dgrad_up": "gemm_bf16.hip",
     "moe_expert_wgrad": "gemm_bf16.hip", "moe_route": "route.hip", "moe_permute": "permute.hip",
     "moe_combine": "combine.hip", "moe_combine_bwd": "combine.hip",
@@ -160,6 +173,9 @@ def main():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-gather", action="store_true",
+                    help="materialise x_perm in moe_permute and run the expert GEMMs on it "
+                         "instead of gathering the expert input rows from X")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a "
                          "known-size kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -187,7 +203,8 @@ def main():
     wr = up(inp["wr"], torch.float32)
     w1, w3, w2 = up(inp["w1"], act), up(inp["w3"], act), up(inp["w2"], act)
     G = max(cfg.lb_groups)
-    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G)
+    gather = not args.no_gather
+    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=gather)
     dm = layer.dims
 
     da = torch.empty_like(layer.a)
@@ -199,6 +216,13 @@ def main():
                                               x, layer.x_perm, layer.workspace)),
         ("moe_expert_up", lambda: L.moe_expert_up(dm, layer.x_perm, layer.expert_offsets, w1, w3,
                                                   layer.a, layer.b, layer.h)),
+        # gathered expert input: the same two steps without x_perm
+        ("moe_permute_plan", lambda: L.moe_permute(dm, layer.topk_idx, layer.expert_counts,
+                                                   layer.expert_offsets, layer.pos,
+                                                   layer.src_token, None, None,
+                                                   layer.workspace)),
+        ("moe_expert_up_gather", lambda: L.moe_expert_up_gather(
+            dm, x, layer.src_token, layer.expert_offsets, w1, w3, layer.a, layer.b, layer.h)),
         ("moe_expert_down", lambda: L.moe_expert_down(dm, layer.h, layer.expert_offsets, w2,
                                                       layer.y_perm)),
         ("moe_combine", lambda: L.moe_combine(dm, layer.y_perm, layer.pos, layer.topk_gate,
@@ -213,11 +237,17 @@ def main():
         ("moe_expert_wgrad", lambda: L.moe_expert_wgrad(
             dm, layer.x_perm, layer.expert_offsets, layer.h, layer.dy_perm, da, db, layer.dw1,
             layer.dw3, layer.dw2, layer.workspace)),
+        ("moe_expert_wgrad_gather", lambda: L.moe_expert_wgrad_gather(
+            dm, x, layer.src_token, layer.expert_offsets, layer.h, layer.dy_perm, da, db,
+            layer.dw1, layer.dw3, layer.dw2, layer.workspace)),
         ("moe_route_bwd", lambda: L.moe_route_bwd(dm, x, wr, layer.topk_idx, layer.topk_gate,
                                                   layer.dgate, layer.expert_offsets, layer.pos,
                                                   layer.src_token, layer.dx_perm, layer.dx,
                                                   layer.dwr, layer.workspace)),
     ]
+    drop = (("moe_permute", "moe_expert_up", "moe_expert_wgrad") if gather else
+            ("moe_permute_plan", "moe_expert_up_gather", "moe_expert_wgrad_gather"))
+    calls = [c for c in calls if c[0] not in drop]
     if not cfg.backward:
         calls = calls[:5]
 
@@ -267,7 +297,7 @@ def main():
     work = algorithmic_work(cfg)
     # the dominant single-kernel call carries the roofline
     single = {n: t for n, t in per_call.items() if work[n][2] == 1 or
-              (n == "moe_expert_wgrad" and wgrad_kernels(dm) == 1)}
+              (n in WGRAD_CALLS and wgrad_kernels(dm) == 1)}
     dominant = max(single, key=single.get)
     fl, by, _ = work[dominant]
     roof = roofline_entry(fl, by, per_call[dominant] * 1e-3, cfg.act)
@@ -291,7 +321,9 @@ def main():
         "data": "synthetic (seeded generators; random-init weights)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} E={cfg.E} f={cfg.f} k={cfg.k} "
                                f"{cfg.act}, fp32 router, {'fwd+bwd' if cfg.backward else 'fwd'}",
-                   "tokens": cfg.T, "lb_groups": G},
+                   "tokens": cfg.T, "lb_groups": G,
+                   "expert_input": "gathered from X by src_token" if gather
+                                   else "materialised x_perm"},
         "grouped_gemm": {"tflops": round(gemm_tflops, 2),
                          "frac_of_peak": round(gemm_tflops / (PEAK_MFMA[cfg.act] / 1e12), 4)},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},

@@ -248,6 +248,42 @@ moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
                             void* stream);
 
 /*
+ * Gathered expert input ("Expert Coupling in MoE Pretraining", Fig. 5: the
+ * dispatch gathers each token's rows for its experts).  The same products as
+ * moe_grouped_swiglu_fwd/bwd, moe_expert_up and moe_expert_wgrad, with the
+ * expert input row p read as x[src_token[p]] instead of x_perm[p], so
+ * moe_permute can run as a plan only (x_perm = NULL) and the [T*k, d] copy
+ * of X is never written or read.  Results are bitwise those of the x_perm
+ * calls on x_perm[p] = x[src_token[p]].
+ * x [T,d] act; src_token [T*k] int32 in [0, T), as moe_permute writes it for
+ * the same routing (not checked on the device).  bf16: T*d*2 < 2^31 bytes,
+ * else MOE_ERR_UNSUPPORTED.  Other arguments, workspace and errors as in the
+ * calls they mirror.
+ */
+moe_status moe_grouped_swiglu_fwd_gather(const moe_dims* dims, const void* x,
+                                         const int32_t* src_token,
+                                         const int32_t* expert_offsets, const void* w1,
+                                         const void* w3, const void* w2, void* a_save,
+                                         void* b_save, void* h_save, void* y_perm,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+moe_status moe_grouped_swiglu_bwd_gather(const moe_dims* dims, const void* x,
+                                         const int32_t* src_token,
+                                         const int32_t* expert_offsets, const void* w1,
+                                         const void* w3, const void* w2, const void* a_save,
+                                         const void* b_save, const void* h_save,
+                                         const void* dy_perm, void* dx_perm, void* dw1,
+                                         void* dw3, void* dw2, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+moe_status moe_expert_up_gather(const moe_dims* dims, const void* x, const int32_t* src_token,
+                                const int32_t* expert_offsets, const void* w1, const void* w3,
+                                void* a_save, void* b_save, void* h_save, void* stream);
+moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
+                                   const int32_t* src_token, const int32_t* expert_offsets,
+                                   const void* h_save, const void* dy_perm, const void* da,
+                                   const void* db, void* dw1, void* dw3, void* dw2,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_route_bwd -- adjoint of the router (logits -> top-k -> renormalised
  * softmax), fused with the unpermute-and-sum of the expert input gradient.
  *

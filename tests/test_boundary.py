@@ -75,6 +75,25 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert st == INVALID and "x_perm" in L.last_error()
 
 
+def test_gathered_calls_check_their_table_and_x():
+    lib = L.lib()
+    dm = dims()
+    st = lib.moe_expert_up_gather(ctypes.byref(dm), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, None)
+    assert st == INVALID and "src_token" in L.last_error()
+    st = lib.moe_grouped_swiglu_fwd_gather(ctypes.byref(dm), None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == INVALID and "'x'" in L.last_error()
+    st = lib.moe_expert_wgrad_gather(ctypes.byref(dm), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == INVALID and "aligned" in L.last_error()
+    # bf16 offsets into X are 32-bit: X of 2 GiB or more is refused
+    big = dims(T=1 << 20, d=1024)
+    st = lib.moe_expert_up_gather(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, None)
+    assert st == UNSUP and "2 GiB" in L.last_error()
+
+
 def test_groups_must_divide_tokens():
     lib = L.lib()
     dm = dims(T=60)

@@ -35,6 +35,8 @@ EXPORTED = (
     "moe_route_bwd", "moe_coselect", "moe_dispatch_plan", "moe_placement_greedy",
     "moe_check_placement", "moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
     "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_wgrad_launches",
+    "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
+    "moe_expert_wgrad_gather",
 )
 
 
@@ -79,6 +81,13 @@ _SIGNATURES = {
     "moe_expert_dgrad_down": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_dgrad_up": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_wgrad": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_up_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_wgrad_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                       _P]),
+    "moe_grouped_swiglu_fwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _SZ, _P]),
+    "moe_grouped_swiglu_bwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
 }
 
@@ -324,3 +333,58 @@ def moe_check_placement(E, G, placement) -> None:
     pl = (ctypes.c_int32 * E)(*[int(v) for v in placement])
     st = lib().moe_check_placement(int(E), int(G), ctypes.cast(pl, ctypes.c_void_p))
     _check(st, "moe_check_placement")
+
+
+# ---------------------------------------------------------------- gathered expert input
+def moe_grouped_swiglu_fwd_gather(dims, x, src_token, expert_offsets, w1, w3, w2, a_save,
+                                  b_save, h_save, y_perm, workspace=None, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_grouped_swiglu_fwd_gather(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
+        _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
+        _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(y_perm, "y_perm", act),
+        _ptr(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_grouped_swiglu_fwd_gather")
+
+
+def moe_grouped_swiglu_bwd_gather(dims, x, src_token, expert_offsets, w1, w3, w2, a_save,
+                                  b_save, h_save, dy_perm, dx_perm, dw1, dw3, dw2, workspace,
+                                  stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_grouped_swiglu_bwd_gather(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
+        _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
+        _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(dy_perm, "dy_perm", act),
+        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act),
+        _ptr(dw2, "dw2", act), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_grouped_swiglu_bwd_gather")
+
+
+def moe_expert_up_gather(dims, x, src_token, expert_offsets, w1, w3, a_save, b_save, h_save,
+                         stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_up_gather(ctypes.byref(dims), _ptr(x, "x", act),
+                                    _ptr(src_token, "src_token", torch.int32),
+                                    _ptr(expert_offsets, "expert_offsets", torch.int32),
+                                    _ptr(w1, "w1", act), _ptr(w3, "w3", act),
+                                    _ptr(a_save, "a_save", act), _ptr(b_save, "b_save", act),
+                                    _ptr(h_save, "h_save", act), _stream(stream))
+    _check(st, "moe_expert_up_gather")
+
+
+def moe_expert_wgrad_gather(dims, x, src_token, expert_offsets, h_save, dy_perm, da, db, dw1,
+                            dw3, dw2, workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_wgrad_gather(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(h_save, "h_save", act),
+        _ptr(dy_perm, "dy_perm", act), _ptr(da, "da", act), _ptr(db, "db", act),
+        _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act), _ptr(dw2, "dw2", act),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_expert_wgrad_gather")

@@ -100,20 +100,22 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
 __global__ void key_scan_kernel(const int32_t* hist, int32_t nb, int32_t nkeys, int32_t* base,
                                 int32_t* counts, int32_t* offsets);
 
-// grouped GEMMs
-hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                             const void* w1, const void* w3, const void* w2, void* a, void* b,
-                             void* h, void* y, hipStream_t s);
-hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+// grouped GEMMs.  x_rows: NULL, or the gather table of the expert input: row p
+// of the expert input is then row x_rows[p] of x_perm (which is X [T,d])
+hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets, const void* w1, const void* w3,
+                             const void* w2, void* a, void* b, void* h, void* y, hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
                              float* ws_partial, hipStream_t s);
 
 // kernel-level phases of the expert GEMMs (dispatch on the activation type)
-hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                            const void* w1, const void* w3, void* a, void* b, void* h,
-                            hipStream_t s);
+hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                            const int32_t* offsets, const void* w1, const void* w3, void* a,
+                            void* b, void* h, hipStream_t s);
 hipError_t launch_expert_down(const moe_dims& dm, const void* h, const int32_t* offsets,
                               const void* w2, void* y, hipStream_t s);
 hipError_t launch_expert_dgrad_down(const moe_dims& dm, const void* dy_perm,
@@ -122,15 +124,15 @@ hipError_t launch_expert_dgrad_down(const moe_dims& dm, const void* dy_perm,
 hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void* db,
                                   const int32_t* offsets, const void* w1, const void* w3,
                                   void* dx_perm, hipStream_t s);
-hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                               const void* h, const void* dy_perm, const void* da,
-                               const void* db, void* dw1, void* dw3, void* dw2, float* partial,
-                               hipStream_t s);
+hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                               const int32_t* offsets, const void* h, const void* dy_perm,
+                               const void* da, const void* db, void* dw1, void* dw3, void* dw2,
+                               float* partial, hipStream_t s);
 
 // bf16 matrix-core implementations (gemm_bf16.hip)
-hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                          const void* w1, const void* w3, void* a, void* b, void* h,
-                          hipStream_t s);
+hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                          const int32_t* offsets, const void* w1, const void* w3, void* a,
+                          void* b, void* h, hipStream_t s);
 hipError_t launch_down_bf16(const moe_dims& dm, const void* h, const int32_t* offsets,
                             const void* w2, void* y, hipStream_t s);
 hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const int32_t* offsets,
@@ -139,9 +141,10 @@ hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const
 hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
                                 const int32_t* offsets, const void* w1, const void* w3,
                                 void* dx_perm, hipStream_t s);
-hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                             const void* h, const void* dy_perm, const void* da, const void* db,
-                             void* dw1, void* dw3, void* dw2, float* partial, hipStream_t s);
+hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets, const void* h, const void* dy_perm,
+                             const void* da, const void* db, void* dw1, void* dw3, void* dw2,
+                             float* partial, hipStream_t s);
 int wgrad_splits_bf16(const moe_dims& dm);           // split-K count of the weight gradients
 size_t wgrad_partial_bytes_bf16(const moe_dims& dm); // fp32 partial tiles it needs
 

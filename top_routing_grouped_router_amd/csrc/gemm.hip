@@ -44,6 +44,7 @@ struct GemmArgs {
   void* c1;
   void* c2;
   const int32_t* offsets;
+  const int32_t* x_rows;   // NULL, or: row p of the expert input is row x_rows[p] of X
   int32_t E, d, f;
 };
 
@@ -197,6 +198,22 @@ __device__ __forceinline__ void stage_mnmajor(T* lds, const T* base, int64_t ld,
   }
 }
 
+// As stage_mnmajor, with k row kr at row_ptr(kr) (mn offset applied by the caller)
+template <typename T, int BK, int LD, typename RowPtr>
+__device__ __forceinline__ void stage_mnmajor_rows(T* lds, RowPtr row_ptr, int kvalid,
+                                                   int mnvalid) {
+  constexpr int kVec = 16 / sizeof(T);
+  constexpr int kPerRow = 128 / kVec;
+  for (int v = threadIdx.x; v < BK * kPerRow; v += kThreads) {
+    const int kr = v / kPerRow, c = (v % kPerRow) * kVec;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (kr < kvalid && c < mnvalid) val = *reinterpret_cast<const uint4*>(row_ptr(kr) + c);
+    const T* e = reinterpret_cast<const T*>(&val);
+#pragma unroll
+    for (int i = 0; i < kVec; ++i) lds[(c + i) * LD + kr] = e[i];
+  }
+}
+
 template <typename TA>
 __device__ __forceinline__ void store_act(TA* p, float v) { *p = Act<TA>::from_f32(v); }
 
@@ -284,8 +301,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
       const int kvalid = min(BK, p1 - p);
       stage_mnmajor<TA, BK, LD>(As, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kvalid,
                                 Mdim - m0);
-      stage_mnmajor<TA, BK, LD>(Bs, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kvalid,
-                                Ndim - n0);
+      if (z != 0 && g.x_rows)   // B = X rows gathered by the table
+        stage_mnmajor_rows<TA, BK, LD>(
+            Bs, [&](int kr) { return Bsrc + static_cast<int64_t>(g.x_rows[p + kr]) * Ndim + n0; },
+            kvalid, Ndim - n0);
+      else
+        stage_mnmajor<TA, BK, LD>(Bs, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kvalid,
+                                  Ndim - n0);
       __syncthreads();
       core.compute(As, Bs);
       __syncthreads();
@@ -303,12 +325,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     const int n0 = blockIdx.y * ((MODE == UP) ? 64 : BN);
 
     if constexpr (MODE == UP) {
-      const TA* x = static_cast<const TA*>(g.a0) + static_cast<int64_t>(m0) * d;
+      const TA* x = static_cast<const TA*>(g.a0);
       const TA* w1 = static_cast<const TA*>(g.b0) + static_cast<int64_t>(e) * f * d;
       const TA* w3 = static_cast<const TA*>(g.b1) + static_cast<int64_t>(e) * f * d;
+      // input row r of the tile: expert row m0 + r, or the X row the table gives
+      auto x_row = [&](int r) {
+        const int64_t q = g.x_rows ? g.x_rows[m0 + r] : m0 + r;
+        return x + q * d;
+      };
       for (int k0 = 0; k0 < d; k0 += BK) {
-        stage_kmajor<TA, BK, LD>(As, [&](int r) { return x + static_cast<int64_t>(r) * d; },
-                                 rows, k0);
+        stage_kmajor<TA, BK, LD>(As, x_row, rows, k0);
         stage_kmajor<TA, BK, LD>(Bs, [&](int r) {
           const int q = r >> 5;
           const TA* w = (q & 1) ? w3 : w1;
@@ -428,13 +454,15 @@ unsigned row_tiles(const moe_dims& dm) {
 // Each phase dispatches on the activation type: bf16 runs on the matrix cores
 // (gemm_bf16.hip), fp32 on the vector ALUs (the kernel above).
 
-hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                            const void* w1, const void* w3, void* a, void* b, void* h,
-                            hipStream_t s) {
+hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                            const int32_t* offsets, const void* w1, const void* w3, void* a,
+                            void* b, void* h, hipStream_t s) {
   if (dm.T * dm.k == 0) return hipSuccess;
-  if (dm.act == MOE_BF16) return launch_up_bf16(dm, x_perm, offsets, w1, w3, a, b, h, s);
+  if (dm.act == MOE_BF16)
+    return launch_up_bf16(dm, x_perm, x_rows, offsets, w1, w3, a, b, h, s);
   GemmArgs g = base_args(dm, offsets);
   g.a0 = x_perm;
+  g.x_rows = x_rows;
   g.b0 = w1;
   g.b1 = w3;
   g.c0 = a;
@@ -483,12 +511,13 @@ hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void
   return launch_f32<DGRAD_UP>(dim3(row_tiles(dm), (dm.d + BN - 1) / BN), g, s);
 }
 
-hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                               const void* h, const void* dy_perm, const void* da,
-                               const void* db, void* dw1, void* dw3, void* dw2, float* partial,
-                               hipStream_t s) {
+hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                               const int32_t* offsets, const void* h, const void* dy_perm,
+                               const void* da, const void* db, void* dw1, void* dw3, void* dw2,
+                               float* partial, hipStream_t s) {
   if (dm.act == MOE_BF16)
-    return launch_wgrad_bf16(dm, x_perm, offsets, h, dy_perm, da, db, dw1, dw3, dw2, partial, s);
+    return launch_wgrad_bf16(dm, x_perm, x_rows, offsets, h, dy_perm, da, db, dw1, dw3, dw2,
+                             partial, s);
   // weight gradients (also for experts with no rows: they get zeros)
   GemmArgs g = base_args(dm, offsets);
   g.a0 = dy_perm;   // z = 0: A = dy (m over d), B = h (n over f)
@@ -496,6 +525,7 @@ hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int
   g.a1 = da;        // z = 1: A = da (m over f), B = x (n over d)
   g.aux0 = db;      // z = 2: A = db (m over f), B = x (n over d)
   g.b1 = x_perm;
+  g.x_rows = x_rows;
   g.c0 = dw2;
   g.c1 = dw1;
   g.c2 = dw3;
@@ -503,15 +533,16 @@ hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int
   return launch_f32<WGRAD>(dim3(tiles, dm.E, 3), g, s);
 }
 
-hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                             const void* w1, const void* w3, const void* w2, void* a, void* b,
-                             void* h, void* y, hipStream_t s) {
-  hipError_t e = launch_expert_up(dm, x_perm, offsets, w1, w3, a, b, h, s);
+hipError_t launch_swiglu_fwd(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets, const void* w1, const void* w3,
+                             const void* w2, void* a, void* b, void* h, void* y, hipStream_t s) {
+  hipError_t e = launch_expert_up(dm, x_perm, x_rows, offsets, w1, w3, a, b, h, s);
   if (e != hipSuccess) return e;
   return launch_expert_down(dm, h, offsets, w2, y, s);
 }
 
-hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
+hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
                              void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
@@ -520,8 +551,8 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
   if (e != hipSuccess) return e;
   e = launch_expert_dgrad_up(dm, ws_da, ws_db, offsets, w1, w3, dx_perm, s);
   if (e != hipSuccess) return e;
-  return launch_expert_wgrad(dm, x_perm, offsets, h, dy_perm, ws_da, ws_db, dw1, dw3, dw2,
-                             ws_partial, s);
+  return launch_expert_wgrad(dm, x_perm, x_rows, offsets, h, dy_perm, ws_da, ws_db, dw1, dw3,
+                             dw2, ws_partial, s);
 }
 
 }  // namespace moe

@@ -81,6 +81,10 @@ struct Args {
   bf16_t* c1;
   bf16_t* c2;
   const int32_t* offsets;
+  // NULL, or the gather table of the expert input (UP's A, WGRAD's x operand):
+  // row p is then row x_rows[p] of X [T, d] (x_bytes = T d 2 < 2^31)
+  const int32_t* x_rows;
+  int32_t x_bytes;
   int32_t E, d, f;
   int32_t n_tiles_n;     // row modes: tiles along n
   int32_t grid_pad;      // flat grid size (multiple of 8)
@@ -656,7 +660,8 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
 // ------------------------------------------------------------------ kernels
 // Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP), persistent: G workgroups
 // (at most what is resident at once) each run their item list.
-template <int MODE, bool BIG>
+// GATHER (UP only): the A rows come from X through the gather table x_rows.
+template <int MODE, bool BIG, bool GATHER = false>
 __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   typedef Cfg<BIG> C;
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
@@ -683,7 +688,7 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   AccT<BIG> acc;
   zero_acc<BIG>(acc);
 
-  constexpr int NSETS = (MODE == DGRAD_DOWN || MODE == DGRAD_UP) ? 2 : kRowSets;
+  constexpr int NSETS = (MODE == DGRAD_DOWN || MODE == DGRAD_UP || GATHER) ? 2 : kRowSets;
   constexpr int KA = BM * 8 / NT;   // A chunks per thread
   constexpr int KB = BN * 8 / NT;   // k-contiguous B chunks per thread (UP, DOWN)
   constexpr int MB = BN * 2 / NT;   // n-contiguous B blocks per thread (DGRAD modes)
@@ -696,6 +701,19 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   // per-item lane offsets (bytes from the item's base) and uniform item data
   uint32_t voff_a[KA], voff_b[KB], voff_m[MB];
   int p_item = -1, p_e = 0, p_m0 = 0, p_mend = 0, p_n0 = 0;
+  static_assert(!GATHER || MODE == UP, "gathered A rows in UP only");
+  // gather: xs holds the table entries of this lane's A rows for the item of
+  // the next load call (fetched one load call ahead, unconditionally, before
+  // that call's operand loads, so waiting for them never waits for operands)
+  int32_t xs[KA];
+  auto fetch_rows = [&](int item) {
+    const int4 ds = sched.desc[item];
+    const int m0 = __builtin_amdgcn_readfirstlane(ds.y);
+    const int mlast = __builtin_amdgcn_readfirstlane(ds.z) - 1;
+#pragma unroll
+    for (int i = 0; i < KA; ++i)
+      xs[i] = g.x_rows[min(m0 + static_cast<int>(threadIdx.x >> 3) + (NT / 8) * i, mlast)];
+  };
   auto prep = [&](int item) {
     const int4 ds = sched.desc[item];
     p_e = __builtin_amdgcn_readfirstlane(ds.x);
@@ -703,8 +721,18 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
     p_mend = __builtin_amdgcn_readfirstlane(ds.z);
     p_n0 = __builtin_amdgcn_readfirstlane(ds.w) * ((MODE == UP) ? kUpHalf : BN);
     const int t = threadIdx.x, c8 = (t & 7) * 8;
+    if constexpr (GATHER) {
 #pragma unroll
-    for (int i = 0; i < KA; ++i) voff_a[i] = (((t >> 3) + (NT / 8) * i) * lda + c8) * 2;
+      for (int i = 0; i < KA; ++i) {
+        const int r = (t >> 3) + (NT / 8) * i;
+        voff_a[i] = (p_m0 + r < p_mend)
+                        ? (static_cast<uint32_t>(xs[i]) * lda + c8) * 2
+                        : kOutOfRange;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KA; ++i) voff_a[i] = (((t >> 3) + (NT / 8) * i) * lda + c8) * 2;
+    }
     if constexpr (MODE == UP || MODE == DOWN) {
 #pragma unroll
       for (int i = 0; i < KB; ++i) {
@@ -732,9 +760,12 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
       k0 -= f;
     }
     // A rows [m0, mend) of the expert, K from k0: rows past mend read zeros
-    const bf16_t* abase = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
-                          static_cast<int64_t>(p_m0) * lda + k0;
-    const auto ra = rsrc_at(abase, ((p_mend - p_m0) * lda - k0) * 2);
+    // (gathered: X rows through the table, offsets in voff_a)
+    if constexpr (GATHER) fetch_rows((kt + 1 < nk) ? item : min(item + 1, n_items - 1));
+    const bf16_t* abase = GATHER ? g.a0 + k0
+                                 : ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
+                                       static_cast<int64_t>(p_m0) * lda + k0;
+    const auto ra = rsrc_at(abase, GATHER ? g.x_bytes - k0 * 2 : ((p_mend - p_m0) * lda - k0) * 2);
 #pragma unroll
     for (int i = 0; i < KA; ++i) pa[set].v[i] = bload(ra, voff_a[i]);
     const int64_t wexp = static_cast<int64_t>(p_e) * E_fd;
@@ -875,8 +906,9 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   };
   constexpr int kVmem = KA + ((MODE == UP || MODE == DOWN) ? KB : MB * 4);
   constexpr int kDsw = KA + ((MODE == UP || MODE == DOWN) ? KB : MB * 8);
-  run_stream<BIG, NSETS, kVmem, kDsw>(acc, lds, n_items, n_items * nk, [nk](int) { return nk; },
-                                      prep_if, load, store, epilogue);
+  if constexpr (GATHER) fetch_rows(0);
+  run_stream<BIG, NSETS, kVmem + (GATHER ? KA : 0), kDsw>(
+      acc, lds, n_items, n_items * nk, [nk](int) { return nk; }, prep_if, load, store, epilogue);
 }
 
 // expert and first row of row tile `tile` (tiles of BM rows; prefix sum of
@@ -1140,18 +1172,25 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // this wavefront's DMA instructions: A rows 32 wave + [0, 32) and B rows
-  // 32 wave + [0, 32), 16 rows per instruction
+  // 32 wave + [0, 32), 16 rows per instruction.  A row r is expert row m0 + r,
+  // or with a gather table X row x_rows[m0 + r] (rows past the expert read 0)
+  const bool gather = (MODE == UP) && g.x_rows != nullptr;
   uint32_t voa[2], vob[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = wave * 32 + u * 16 + (lane >> 2);
     const int logical = (lane & 3) ^ ((row >> 2) & 3);
-    voa[u] = (row * lda + logical * 8) * 2;
+    if (gather) {
+      const uint32_t src = static_cast<uint32_t>(g.x_rows[min(m0 + row, mend - 1)]);
+      voa[u] = (m0 + row < mend) ? (src * lda + logical * 8) * 2 : kOutOfRange;
+    } else {
+      voa[u] = (row * lda + logical * 8) * 2;
+    }
     const int brow = (MODE == UP && row >= kUpHalf) ? row - kUpHalf : row;
     vob[u] = (brow * ((MODE == UP) ? d : f) + logical * 8) * 2;
   }
-  const bf16_t* abase = g.a0 + static_cast<int64_t>(m0) * lda;
-  const int a_rows_bytes = (mend - m0) * lda * 2;
+  const bf16_t* abase = gather ? g.a0 : g.a0 + static_cast<int64_t>(m0) * lda;
+  const int a_rows_bytes = gather ? g.x_bytes : (mend - m0) * lda * 2;
   const bf16_t* bbase;
   int b_bytes;
   if constexpr (MODE == UP) {
@@ -1347,6 +1386,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* lds, uint32_t byte_lo, u
 __device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
 }  // namespace dmaw
 
+// GATHER: as in the small-tile kernel, the x operand of dW1 and dW3 comes from
+// X through the gather table, entries fetched NST - 1 = 3 steps ahead.
+template <bool GATHER>
 __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t tiles_per_expert) {
   using namespace dmaw;
   // four stage arrays (distinct objects: a transposing read of one stage is
@@ -1388,6 +1430,7 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   // DMA: wavefront w fills rows 4 w .. 4 w + 3 of the A and the B tile, two
   // rows (1 KB) per instruction; lane l -> row + l / 32, physical chunk l % 32
   uint32_t voa[2], vob[2];
+  int bcol[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = wave * 4 + u * 2 + (lane >> 5);
@@ -1395,21 +1438,47 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
     const int col = logical * 8;
     voa[u] = (m0 + col < Mdim) ? static_cast<uint32_t>((row * Mdim + col) * 2) : kOutOfRange;
     vob[u] = (n0 + col < Ndim) ? static_cast<uint32_t>((row * Ndim + col) * 2) : kOutOfRange;
+    bcol[u] = (n0 + col < Ndim) ? col : -1;
   }
+  const bool gz = GATHER && z != 0;   // B rows gathered from X
+  int32_t xs[NST][2];                 // table entries of the rows of step s in slot s % NST
+  auto fetch = [&](int slot, int kt) {
+    const int pb = p0 + kt * BKS;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      xs[slot][u] = g.x_rows[min(pb + wave * 4 + u * 2 + (lane >> 5), p1 - 1)];
+  };
   // step kt into the stage at As; steps at or past nk read through an empty
   // resource, so their stage is zero and adds nothing
-  auto issue = [&](bf16_t* As, int kt) {
+  auto issue = [&](bf16_t* As, int kt, int slot) {
     bf16_t* Bs = As + BKS * BM;
     const bool live = kt < nk;
     const int p = p0 + min(kt, nk - 1) * BKS;
     const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
                             live ? ((p1 - p) * Mdim - m0) * 2 : 0);
-    const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
-                            live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+    uint32_t vb[2] = {vob[0], vob[1]};
+    __amdgpu_buffer_rsrc_t rb;
+    if constexpr (GATHER) {
+      rb = gz ? rsrc_at(Bsrc + n0, live ? g.x_bytes - n0 * 2 : 0)
+              : rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
+                        live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+      if (gz) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = kt * BKS + wave * 4 + u * 2 + (lane >> 5);   // row of the expert
+          vb[u] = (p0 + q < p1 && bcol[u] >= 0)
+                      ? (static_cast<uint32_t>(xs[slot][u]) * Ndim + bcol[u]) * 2
+                      : kOutOfRange;
+        }
+      }
+    } else {
+      rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
+                   live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 4 + u * 2) * BM, voa[u]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 4 + u * 2) * BN, vob[u]);
+    for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 4 + u * 2) * BN, vb[u]);
   };
 
   // transposing-read addresses (bytes within a stage) for sub-step 0, half 0;
@@ -1446,36 +1515,49 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
+  // per step a wavefront issues 4 DMA loads (and, gathering, 2 table loads)
+  constexpr int kPerStep = GATHER ? 6 : 4;
   auto sync_stage = [&]() {   // the wave's DMA of the next stage landed, then everyone's
     mem_fence_compiler();
-    dma::wait_vm<4>();
+    dma::wait_vm<kPerStep>();
     __builtin_amdgcn_s_barrier();
     mem_fence_compiler();
   };
-  issue(st0, 0);
-  issue(st1, 1);
-  issue(st2, 2);
+  if constexpr (GATHER) {
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
+    fetch(3, 3);
+  }
+  issue(st0, 0, 0);
+  if constexpr (GATHER) fetch(0, 4);
+  issue(st1, 1, 1);
+  if constexpr (GATHER) fetch(1, 5);
+  issue(st2, 2, 2);
   mem_fence_compiler();
-  dma::wait_vm<8>();
+  dma::wait_vm<2 * kPerStep>();
   __builtin_amdgcn_s_barrier();
   mem_fence_compiler();
   read_sub(fa0, fb0, st0, 0);
   // step kt: stage kt % 4 current, (kt + 1) % 4 next, DMA into (kt + 3) % 4;
   // the step count is padded to a multiple of 4 with zero steps
-  auto step = [&](int kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
+  // (gathering: step s's table entries sit in slot s % 4; issuing step s
+  // first fetches those of step s + 3, whose slot step s - 1 has freed)
+  auto step = [&](int kt, int q, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
     read_sub(fa1, fb1, cur, 1);
     mma_sub(fa0, fb0);
     sync_stage();                   // stage kt + 1 ready; stage kt - 1 no longer read
-    issue(fill, kt + 3);
+    if constexpr (GATHER) fetch((q + 2) & 3, kt + 6);
+    issue(fill, kt + 3, (q + 3) & 3);
     read_sub(fa0, fb0, nxt, 0);
     mma_sub(fa1, fb1);
   };
   const int nk4 = (nk + 3) & ~3;
   for (int kt = 0; kt < nk4; kt += 4) {
-    step(kt, st0, st1, st3);
-    step(kt + 1, st1, st2, st0);
-    step(kt + 2, st2, st3, st1);
-    step(kt + 3, st3, st0, st2);
+    step(kt, 0, st0, st1, st3);
+    step(kt + 1, 1, st1, st2, st0);
+    step(kt + 2, 2, st2, st3, st1);
+    step(kt + 3, 3, st3, st0, st2);
   }
   mem_fence_compiler();
   dma::wait_vm<0>();
@@ -1742,7 +1824,11 @@ constexpr int kRowBytes = BM * 2;            // 256
 
 // NST = 4 (64 KB, two workgroups per CU) or 8 (128 KB, one workgroup per CU,
 // for grids that give each CU at most one tile: twice the loads in flight).
-template <int NST>
+// GATHER: the x operand of dW1 and dW3 (B of z = 1, 2) is read from X through
+// the gather table; the table entries of a step's rows are loaded NST - 1
+// steps before its DMA is issued (a register ring, one slot per stage), so
+// waiting for them never waits for DMA still meant to be in flight.
+template <int NST, bool GATHER>
 __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args g,
                                                                           int32_t tiles_per_expert) {
   using namespace dmas;
@@ -1788,6 +1874,7 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   // DMA: wavefront w fills rows 8 w .. 8 w + 7 of A and of B, four rows per
   // instruction; lane l -> row + l / 16, physical chunk l % 16
   uint32_t voa[2], vob[2];
+  int bcol[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = wave * 8 + u * 4 + (lane >> 4);
@@ -1795,19 +1882,45 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
     const int col = logical * 8;
     voa[u] = (m0 + col < Mdim) ? static_cast<uint32_t>((row * Mdim + col) * 2) : kOutOfRange;
     vob[u] = (n0 + col < Ndim) ? static_cast<uint32_t>((row * Ndim + col) * 2) : kOutOfRange;
+    bcol[u] = (n0 + col < Ndim) ? col : -1;
   }
-  auto issue = [&](bf16_t* As, int kt) {
+  const bool gz = GATHER && z != 0;   // B rows gathered from X
+  int32_t xs[NST][2];                 // table entries of the rows of step s in slot s % NST
+  auto fetch = [&](int slot, int kt) {
+    const int pb = p0 + kt * BKS;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      xs[slot][u] = g.x_rows[min(pb + wave * 8 + u * 4 + (lane >> 4), p1 - 1)];
+  };
+  auto issue = [&](bf16_t* As, int kt, int slot) {
     bf16_t* Bs = As + kHalf;
     const bool live = kt < nk;
     const int p = p0 + min(kt, nk - 1) * BKS;
     const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
                             live ? ((p1 - p) * Mdim - m0) * 2 : 0);
-    const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
-                            live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+    uint32_t vb[2] = {vob[0], vob[1]};
+    __amdgpu_buffer_rsrc_t rb;
+    if constexpr (GATHER) {
+      rb = gz ? rsrc_at(Bsrc + n0, live ? g.x_bytes - n0 * 2 : 0)
+              : rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
+                        live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+      if (gz) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = kt * BKS + wave * 8 + u * 4 + (lane >> 4);   // row of the expert
+          vb[u] = (p0 + q < p1 && bcol[u] >= 0)
+                      ? (static_cast<uint32_t>(xs[slot][u]) * Ndim + bcol[u]) * 2
+                      : kOutOfRange;
+        }
+      }
+    } else {
+      rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
+                   live ? ((p1 - p) * Ndim - n0) * 2 : 0);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 8 + u * 4) * BM, voa[u]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 8 + u * 4) * BN, vob[u]);
+    for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 8 + u * 4) * BN, vb[u]);
   };
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = lane >> 4, sl = lane & 15;
@@ -1848,23 +1961,34 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   // have landed: NST - 3 steps may stay in flight
   auto sync_stage = [&]() {
     dmaw::mem_fence_compiler();
-    dma::wait_vm<4 * (NST - 3)>();
+    dma::wait_vm<(4 + (GATHER ? 2 : 0)) * (NST - 3)>();
     __builtin_amdgcn_s_barrier();
     dmaw::mem_fence_compiler();
   };
   bf16_t* const stg[8] = {st0, st1, st2, st3, st4, st5, st6, st7};
+  if constexpr (GATHER) {
+    // table entries of steps 0 .. NST - 2 now; each issue of step s fetches
+    // those of step s + NST - 1 (before its own DMA)
 #pragma unroll
-  for (int q = 0; q < NST - 1; ++q) issue(stg[q], q);
+    for (int q = 0; q < NST - 1; ++q) fetch(q, q);
+  }
+#pragma unroll
+  for (int q = 0; q < NST - 1; ++q) {
+    if constexpr (GATHER) fetch((q + NST - 1) % NST, q + NST - 1);
+    issue(stg[q], q, q);
+  }
   dmaw::mem_fence_compiler();
-  dma::wait_vm<4 * (NST - 2)>();   // step 0 has landed
+  dma::wait_vm<(4 + (GATHER ? 2 : 0)) * (NST - 2)>();   // step 0 has landed
   __builtin_amdgcn_s_barrier();
   dmaw::mem_fence_compiler();
   read_sub(fa0, fb0, st0, 0);
-  auto step = [&](int kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
+  auto step = [&](int kt, int q, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
     read_sub(fa1, fb1, cur, 1);
     mma_sub(fa0, fb0);
     sync_stage();
-    issue(fill, kt + NST - 1);
+    const int t = kt + NST - 1;   // the step whose DMA this issues, slot (q + NST - 1) % NST
+    if constexpr (GATHER) fetch((q + NST - 2) % NST, t + NST - 1);
+    issue(fill, t, (q + NST - 1) % NST);
     read_sub(fa0, fb0, nxt, 0);
     mma_sub(fa1, fb1);
   };
@@ -1872,7 +1996,7 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   for (int kt = 0; kt < nkp; kt += NST) {
 #pragma unroll
     for (int q = 0; q < NST; ++q)
-      step(kt + q, stg[q], stg[(q + 1) % NST], stg[(q + NST - 1) % NST]);
+      step(kt + q, q, stg[q], stg[(q + 1) % NST], stg[(q + NST - 1) % NST]);
   }
   dmaw::mem_fence_compiler();
   dma::wait_vm<0>();
@@ -2006,6 +2130,10 @@ struct WgSched {
   int n, S;
 };
 
+// GATHER: the x operand of dW1 and dW3 (B of z = 1, 2) is read from X through
+// the gather table (each step loads the table entries of its rows first;
+// this kernel serves only the small tile counts that need split K).
+template <bool GATHER>
 __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
     Args g, int32_t tiles_per_expert, int32_t splits, float* partial) {
   constexpr bool BIG = false;
@@ -2127,16 +2255,37 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
     const int p = p_pb + kt * BK;
     const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + p_m0,
                             ((p_pe - p) * Mdim - p_m0) * 2);
-    const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + p_n0,
-                            ((p_pe - p) * Ndim - p_n0) * 2);
 #pragma unroll
     for (int i = 0; i < MA; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pa[set].v[i][r] = bload(ra, voff_a[i] + r * Mdim * 2);
+    if (GATHER && p_z != 0) {
+      // rows p + 4 kq + r of the expert are X rows x_rows[...]; past p_pe: zero
+      int kq, jb;
+      mblock<NT>(0, &jb, &kq);
+      int32_t xr[4];
 #pragma unroll
-    for (int i = 0; i < MBn; ++i)
+      for (int r = 0; r < 4; ++r) xr[r] = g.x_rows[min(p + 4 * kq + r, p_pe - 1)];
+      const auto rb = rsrc_at(Bsrc + p_n0, g.x_bytes - p_n0 * 2);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pb[set].v[i][r] = bload(rb, voff_b[i] + r * Ndim * 2);
+      for (int i = 0; i < MBn; ++i) {
+        mblock<NT>(i, &jb, &kq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t vo = (p + 4 * kq + r < p_pe && voff_b[i] != kOutOfRange)
+                                  ? (static_cast<uint32_t>(xr[r]) * Ndim + jb * 8) * 2
+                                  : kOutOfRange;
+          pb[set].v[i][r] = bload(rb, vo);
+        }
+      }
+    } else {
+      const auto rb = rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + p_n0,
+                              ((p_pe - p) * Ndim - p_n0) * 2);
+#pragma unroll
+      for (int i = 0; i < MBn; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[set].v[i][r] = bload(rb, voff_b[i] + r * Ndim * 2);
+    }
   };
   auto store = [&](auto set_c, bf16_t* As, bf16_t* Bs) {
     constexpr int set = decltype(set_c)::value;
@@ -2266,6 +2415,13 @@ hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, 
   const int64_t slots = 2 * static_cast<int64_t>(kCUs);
   const int64_t grid = std::max(std::min(items, slots), (items + kMaxItems - 1) / kMaxItems);
   g.grid_pad = static_cast<int32_t>(pad8(grid));
+  if constexpr (MODE == UP) {
+    if (g.x_rows) {
+      hipLaunchKernelGGL((rows_kernel<MODE, false, true>), dim3(g.grid_pad),
+                         dim3(Cfg<false>::THREADS), 0, s, g);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((rows_kernel<MODE, false>), dim3(g.grid_pad), dim3(Cfg<false>::THREADS), 0,
                      s, g);
   return hipGetLastError();
@@ -2285,6 +2441,7 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
   }
   return hipGetLastError();
 #endif
+  if (g.x_rows) return hipErrorNotSupported;   // the register-staged big tile has no gather
   hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
                      g);
   return hipGetLastError();
@@ -2312,11 +2469,13 @@ Args base_args(const moe_dims& dm, const int32_t* offsets) {
 
 }  // namespace
 
-hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                          const void* w1, const void* w3, void* a, void* b, void* h,
-                          hipStream_t s) {
+hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                          const int32_t* offsets, const void* w1, const void* w3, void* a,
+                          void* b, void* h, hipStream_t s) {
   Args g = base_args(dm, offsets);
   g.a0 = static_cast<const bf16_t*>(x_perm);
+  g.x_rows = x_rows;
+  g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
   g.b0 = static_cast<const bf16_t*>(w1);
   g.b1 = static_cast<const bf16_t*>(w3);
   g.c0 = static_cast<bf16_t*>(a);
@@ -2359,10 +2518,13 @@ hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* 
   return launch_rows<DGRAD_UP>(g, dm, dm.d, 2 * dm.f, s);
 }
 
-hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* offsets,
-                             const void* h, const void* dy_perm, const void* da, const void* db,
-                             void* dw1, void* dw3, void* dw2, float* partial, hipStream_t s) {
+hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
+                             const int32_t* offsets, const void* h, const void* dy_perm,
+                             const void* da, const void* db, void* dw1, void* dw3, void* dw2,
+                             float* partial, hipStream_t s) {
   Args g = base_args(dm, offsets);
+  g.x_rows = x_rows;
+  g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
   g.a0 = static_cast<const bf16_t*>(dy_perm);   // z = 0: A = dy (m over d), B = h (n over f)
   g.b0 = static_cast<const bf16_t*>(h);
   g.a1 = static_cast<const bf16_t*>(da);        // z = 1: A = da (m over f), B = x (n over d)
@@ -2376,8 +2538,12 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
 #ifndef MOE_NO_DMA
-    hipLaunchKernelGGL(wgrad_dma_kernel, dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
+    if (g.x_rows)
+      hipLaunchKernelGGL((wgrad_dma_kernel<true>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
+    else
+      hipLaunchKernelGGL((wgrad_dma_kernel<false>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
 #else
+    if (g.x_rows) return hipErrorNotSupported;   // the register-staged big tile has no gather
     hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(Cfg<true>::THREADS), 0, s, g, tpe, 1,
                        partial);
 #endif
@@ -2389,10 +2555,21 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   if (splits == 1) {
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
-    if (grid <= static_cast<unsigned>(kCUs))
-      hipLaunchKernelGGL(wgrad_dma_small_kernel<8>, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
-    else
-      hipLaunchKernelGGL(wgrad_dma_small_kernel<4>, dim3(grid), dim3(dmas::NT), 0, s, g, tpe);
+    const bool big = grid <= static_cast<unsigned>(kCUs);
+    if (g.x_rows) {
+      if (big)
+        hipLaunchKernelGGL((wgrad_dma_small_kernel<8, true>), dim3(grid), dim3(dmas::NT), 0, s,
+                           g, tpe);
+      else
+        hipLaunchKernelGGL((wgrad_dma_small_kernel<4, true>), dim3(grid), dim3(dmas::NT), 0, s,
+                           g, tpe);
+    } else if (big) {
+      hipLaunchKernelGGL((wgrad_dma_small_kernel<8, false>), dim3(grid), dim3(dmas::NT), 0, s, g,
+                         tpe);
+    } else {
+      hipLaunchKernelGGL((wgrad_dma_small_kernel<4, false>), dim3(grid), dim3(dmas::NT), 0, s, g,
+                         tpe);
+    }
     return hipGetLastError();
   }
 #endif
@@ -2400,8 +2577,12 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   const int64_t grid = std::max(std::min(items, static_cast<int64_t>(2 * kCUs)),
                                 (items + kMaxItems - 1) / kMaxItems);
   g.grid_pad = static_cast<int32_t>(pad8(grid));
-  hipLaunchKernelGGL(wgrad_stream_kernel, dim3(g.grid_pad), dim3(Cfg<false>::THREADS), 0, s, g,
-                     tpe, splits, partial);
+  if (g.x_rows)
+    hipLaunchKernelGGL((wgrad_stream_kernel<true>), dim3(g.grid_pad), dim3(Cfg<false>::THREADS),
+                       0, s, g, tpe, splits, partial);
+  else
+    hipLaunchKernelGGL((wgrad_stream_kernel<false>), dim3(g.grid_pad), dim3(Cfg<false>::THREADS),
+                       0, s, g, tpe, splits, partial);
   if (splits > 1) {
     const int64_t chunks = static_cast<int64_t>(3) * dm.E * tpe * (128 * 128 / 8);
     hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((chunks + kThreads - 1) / kThreads),

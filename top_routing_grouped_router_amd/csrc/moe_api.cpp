@@ -329,7 +329,7 @@ moe_status moe_grouped_swiglu_fwd(const moe_dims* dims, const void* x_perm,
   MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
   MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
   MOE_REQUIRE_PTR(y_perm, dm.T * dm.k * dm.d);
-  return hip_status(moe::launch_swiglu_fwd(dm, x_perm, expert_offsets, w1, w3, w2, a_save,
+  return hip_status(moe::launch_swiglu_fwd(dm, x_perm, nullptr, expert_offsets, w1, w3, w2, a_save,
                                            b_save, h_save, y_perm,
                                            static_cast<hipStream_t>(stream)),
                     __func__);
@@ -392,7 +392,7 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
   st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
   if (st != MOE_OK) return st;
   const BwdWs w = bwd_ws(dm, workspace);
-  return hip_status(moe::launch_swiglu_bwd(dm, x_perm, expert_offsets, w1, w3, w2, a_save, b_save,
+  return hip_status(moe::launch_swiglu_bwd(dm, x_perm, nullptr, expert_offsets, w1, w3, w2, a_save, b_save,
                                            h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da, w.db,
                                            w.partial, static_cast<hipStream_t>(stream)),
                     __func__);
@@ -411,7 +411,7 @@ moe_status moe_expert_up(const moe_dims* dims, const void* x_perm,
   MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
   MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
   MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
-  return hip_status(moe::launch_expert_up(dm, x_perm, expert_offsets, w1, w3, a_save, b_save,
+  return hip_status(moe::launch_expert_up(dm, x_perm, nullptr, expert_offsets, w1, w3, a_save, b_save,
                                           h_save, static_cast<hipStream_t>(stream)),
                     __func__);
 }
@@ -487,7 +487,7 @@ moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
   const size_t need = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
   st = check_ws(workspace, workspace_bytes, need, __func__);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_expert_wgrad(dm, x_perm, expert_offsets, h_save, dy_perm, da, db,
+  return hip_status(moe::launch_expert_wgrad(dm, x_perm, nullptr, expert_offsets, h_save, dy_perm, da, db,
                                              dw1, dw3, dw2, static_cast<float*>(workspace),
                                              static_cast<hipStream_t>(stream)),
                     __func__);
@@ -619,6 +619,132 @@ moe_status moe_placement_greedy(int32_t E, int32_t G, const int64_t* coselect,
     }
   }
   return ok();
+}
+
+
+// ---------------------------------------------------------------- gathered expert input
+// The expert input row p is X[src_token[p]] (the table moe_permute writes), so
+// x_perm is never materialised.  bf16 offsets into X are 32-bit.
+namespace {
+moe_status check_gather(const moe_dims& dm, const void* x, const int32_t* src_token,
+                        const char* fn) {
+  if (!x && dm.T > 0) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is NULL", fn);
+  if (x && !aligned16(x)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is not 16-byte aligned", fn);
+  if (!src_token && dm.T > 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'src_token' is NULL", fn);
+  if (dm.act == MOE_BF16 && dm.T * dm.d * 2 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: X must be under 2 GiB to be gathered", fn);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_expert_up_gather(const moe_dims* dims, const void* x, const int32_t* src_token,
+                                const int32_t* expert_offsets, const void* w1, const void* w3,
+                                void* a_save, void* b_save, void* h_save, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  return hip_status(moe::launch_expert_up(dm, x, src_token, expert_offsets, w1, w3, a_save,
+                                          b_save, h_save, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
+                                   const int32_t* src_token, const int32_t* expert_offsets,
+                                   const void* h_save, const void* dy_perm, const void* da,
+                                   const void* db, void* dw1, void* dw3, void* dw2,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
+  const size_t need = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
+  st = check_ws(workspace, workspace_bytes, need, __func__);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_expert_wgrad(dm, x, src_token, expert_offsets, h_save, dy_perm,
+                                             da, db, dw1, dw3, dw2,
+                                             static_cast<float*>(workspace),
+                                             static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_grouped_swiglu_fwd_gather(const moe_dims* dims, const void* x,
+                                         const int32_t* src_token,
+                                         const int32_t* expert_offsets, const void* w1,
+                                         const void* w3, const void* w2, void* a_save,
+                                         void* b_save, void* h_save, void* y_perm,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(y_perm, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_swiglu_fwd(dm, x, src_token, expert_offsets, w1, w3, w2, a_save,
+                                           b_save, h_save, y_perm,
+                                           static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_grouped_swiglu_bwd_gather(const moe_dims* dims, const void* x,
+                                         const int32_t* src_token,
+                                         const int32_t* expert_offsets, const void* w1,
+                                         const void* w3, const void* w2, const void* a_save,
+                                         const void* b_save, const void* h_save,
+                                         const void* dy_perm, void* dx_perm, void* dw1,
+                                         void* dw3, void* dw2, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(dx_perm, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
+  const BwdWs need = bwd_ws(dm, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const BwdWs w = bwd_ws(dm, workspace);
+  return hip_status(moe::launch_swiglu_bwd(dm, x, src_token, expert_offsets, w1, w3, w2, a_save,
+                                           b_save, h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da,
+                                           w.db, w.partial, static_cast<hipStream_t>(stream)),
+                    __func__);
 }
 
 }  // extern "C"

@@ -6,7 +6,10 @@ reused by each call, so a step enqueues kernels only.  The sequence is:
   forward:  moe_route -> moe_permute -> moe_grouped_swiglu_fwd -> moe_combine
   backward: moe_combine_bwd -> moe_grouped_swiglu_bwd -> moe_route_bwd
 
-(moe_route_bwd also unpermutes and sums the expert input gradients).
+(moe_route_bwd also unpermutes and sums the expert input gradients).  With
+gather=True the permutation is a plan only and the expert GEMMs read their
+input rows from X through src_token (moe_grouped_swiglu_fwd_gather /
+bwd_gather), so x_perm is never materialised; the results are identical.
 """
 from __future__ import annotations
 
@@ -17,9 +20,11 @@ from . import _lib as L
 
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, f: int, k: int, act: torch.dtype,
-                 n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda"):
+                 n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda",
+                 gather: bool = False):
         self.dims = L.make_dims(T, d, E, f, k, act)
         self.act = act
+        self.gather = gather
         self.n_groups = n_groups
         self.eps = near_tie_eps
         R = T * k
@@ -45,7 +50,7 @@ class MoELayer:
         self.expert_offsets = empty(E + 1, **i32)
         self.pos = empty(T, k, **i32)
         self.src_token = empty(R, **i32)
-        self.x_perm = empty(R, d, **ea)
+        self.x_perm = empty(0 if gather else R, d, **ea)
         self.a = empty(R, f, **ea)
         self.b = empty(R, f, **ea)
         self.h = empty(R, f, **ea)
@@ -68,10 +73,16 @@ class MoELayer:
                     self.group_mean_prob, self.group_aux, self.workspace)
 
     def forward_experts(self, x, w1, w3, w2):
-        L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
-                      self.pos, self.src_token, x, self.x_perm, self.workspace)
-        L.moe_grouped_swiglu_fwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
-                                 self.a, self.b, self.h, self.y_perm)
+        if self.gather:
+            L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
+                          self.pos, self.src_token, None, None, self.workspace)
+            L.moe_grouped_swiglu_fwd_gather(self.dims, x, self.src_token, self.expert_offsets,
+                                            w1, w3, w2, self.a, self.b, self.h, self.y_perm)
+        else:
+            L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
+                          self.pos, self.src_token, x, self.x_perm, self.workspace)
+            L.moe_grouped_swiglu_fwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
+                                     self.a, self.b, self.h, self.y_perm)
         L.moe_combine(self.dims, self.y_perm, self.pos, self.topk_gate, self.y)
 
     def forward(self, x, wr, w1, w3, w2, routing=None):
@@ -89,9 +100,15 @@ class MoELayer:
     def backward(self, dy, x, wr, w1, w3, w2):
         L.moe_combine_bwd(self.dims, dy, self.y_perm, self.pos, self.topk_gate, self.dy_perm,
                           self.dgate)
-        L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
-                                 self.a, self.b, self.h, self.dy_perm, self.dx_perm, self.dw1,
-                                 self.dw3, self.dw2, self.workspace)
+        if self.gather:
+            L.moe_grouped_swiglu_bwd_gather(self.dims, x, self.src_token, self.expert_offsets,
+                                            w1, w3, w2, self.a, self.b, self.h, self.dy_perm,
+                                            self.dx_perm, self.dw1, self.dw3, self.dw2,
+                                            self.workspace)
+        else:
+            L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
+                                     self.a, self.b, self.h, self.dy_perm, self.dx_perm,
+                                     self.dw1, self.dw3, self.dw2, self.workspace)
         L.moe_route_bwd(self.dims, x, wr, self.topk_idx, self.topk_gate, self.dgate,
                         self.expert_offsets, self.pos, self.src_token, self.dx_perm, self.dx,
                         self.dwr, self.workspace)
