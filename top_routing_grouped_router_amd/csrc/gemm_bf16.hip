@@ -1843,11 +1843,13 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   __shared__ __attribute__((aligned(16))) bf16_t st6[kX];
   __shared__ __attribute__((aligned(16))) bf16_t st7[kX];
 
+  // item order: the dW2 tiles, then the dW1 and dW3 tiles of each (e, tile) as
+  // adjacent items, so both read the same x rows on one XCD at the same time
   const int flat = flat_tile();
   const int per_z = g.E * tiles_per_expert;
-  const int z = flat / per_z;
-  if (z >= 3) return;
-  const int rem = flat - z * per_z;
+  if (flat >= 3 * per_z) return;
+  const int z = flat < per_z ? 0 : 1 + ((flat - per_z) & 1);
+  const int rem = flat < per_z ? flat : (flat - per_z) >> 1;
   const int e = rem / tiles_per_expert, t = rem % tiles_per_expert;
   const int d = g.d, f = g.f;
   const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
