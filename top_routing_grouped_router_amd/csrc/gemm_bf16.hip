@@ -915,9 +915,11 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
 // per-expert tile counts across wave 0, 4 experts per lane); false when there
 // is no such tile
 template <int BM>
-__device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_out, int* m0_out,
-                              int* mend_out) {
-  __shared__ int s_e, s_m0, s_mend;
+__device__ bool find_row_tile_at(int* scratch, const int32_t* offsets, int E, int tile, int* e_out,
+                                 int* m0_out, int* mend_out) {
+  int& s_e = scratch[0];
+  int& s_m0 = scratch[1];
+  int& s_mend = scratch[2];
   if (threadIdx.x == 0) s_e = -1;
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -959,6 +961,14 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
   *m0_out = s_m0;
   *mend_out = s_mend;
   return s_e >= 0;
+}
+
+// the same with its three results in static LDS
+template <int BM>
+__device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_out, int* m0_out,
+                              int* mend_out) {
+  __shared__ int s[3];
+  return find_row_tile_at<BM>(s, offsets, E, tile, e_out, m0_out, mend_out);
 }
 
 // Row-split modes with the big tile, one tile per workgroup (long K: the
@@ -1127,6 +1137,9 @@ __global__ __launch_bounds__(Cfg<true>::THREADS, 2) void tile_rows_kernel(Args g
 // these LDS writes, so the step waits on the vector-memory counter explicitly
 // and joins the workgroup with a plain s_barrier (a fenced barrier would also
 // drain the prefetch).
+#ifndef MOE_ROWS_NST
+#define MOE_ROWS_NST 4
+#endif
 namespace dma {
 constexpr int BM = 256, BN = 256, BKS = 32, NST = 4, NT = 512, WAVES_N = 4, FM = 4, FN = 2;
 constexpr int kStage = (BM + BN) * BKS;   // elements per stage
@@ -1150,13 +1163,27 @@ template <int MODE>
 __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   using namespace dma;
   static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
-  __shared__ __attribute__((aligned(16))) bf16_t lds[NST * kStage];   // 128 KB ring
+  // a ring of kNst stages (4: 128 KB, three steps in flight; 5 fills all
+  // 160 KB of LDS but measured slower, so the loads are not waiting on depth)
+  constexpr int kNst = MOE_ROWS_NST;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kNst * kStage];
 
+#ifdef MOE_TRACE
+#define MOE_TILE_MARK(i) \
+  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) moe_trace_data[blockIdx.x * kTraceSlots + 500 + (i)] = wall_clock64()
+#else
+#define MOE_TILE_MARK(i) ((void)0)
+#endif
+  MOE_TILE_MARK(0);
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
   const int nt = flat - row_tile * g.n_tiles_n;
   int e, m0, mend;
-  if (!find_row_tile<BM>(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  // the tile lookup's three results sit at the end of the last stage, which
+  // no DMA writes before every wavefront has passed two loop barriers
+  int* const scratch = reinterpret_cast<int*>(lds + kNst * kStage) - 4;
+  if (!find_row_tile_at<BM>(scratch, g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  MOE_TILE_MARK(1);
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   mend = __builtin_amdgcn_readfirstlane(mend);
@@ -1201,8 +1228,8 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
     bbase = g.b0 + e * E_fd + static_cast<int64_t>(n0) * f;
     b_bytes = (d - n0) * f * 2;
   }
-  auto issue = [&](int kt) {   // step kt into stage kt % NST
-    bf16_t* As = lds + (kt % NST) * kStage;
+  auto issue = [&](int kt) {   // step kt into stage kt % kNst
+    bf16_t* As = lds + (kt % kNst) * kStage;
     bf16_t* Bs = As + BM * BKS;
     const int k0 = kt * BKS;
     const auto ra = rsrc_at(abase + k0, a_rows_bytes - k0 * 2);
@@ -1278,15 +1305,15 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
         : "v"(aaddr), "v"(baddr)
         : "memory");
   };
-  auto sbase = [&](int kt) { return lds_base + (kt % NST) * kStage * 2; };
-  // prologue: steps 0 .. 2 in flight (past-the-end steps reload the last);
-  // kk = 0 fragments of step 0 read once it has landed
-  issue(0);
-  issue(min(1, nk - 1));
-  issue(min(2, nk - 1));
-  dma::wait_vm<8>();
+  auto sbase = [&](int kt) { return lds_base + (kt % kNst) * kStage * 2; };
+  // prologue: steps 0 .. kNst - 2 in flight (past-the-end steps reload the
+  // last); kk = 0 fragments of step 0 read once it has landed
+#pragma unroll
+  for (int q = 0; q < kNst - 1; ++q) issue(min(q, nk - 1));
+  dma::wait_vm<4 * (kNst - 2)>();
   __builtin_amdgcn_s_barrier();
   read_p(p0, sbase(0) + a_addr[0], sbase(0) + b_addr[0]);
+  MOE_TILE_MARK(2);
 #ifdef MOE_TRACE
   int tslot = 0;
 #endif
@@ -1296,12 +1323,12 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
 #ifdef MOE_TRACE
     if (kt < 48) MOE_TRACE_MARK(tslot, 1ull << 60);
 #endif
-    dma::wait_vm<4>();              // this wavefront's loads of step kt + 1 have landed
+    dma::wait_vm<4 * (kNst - 3)>();   // this wavefront's loads of step kt + 1 have landed
     __builtin_amdgcn_s_barrier();   // everyone's have; everyone is done with step kt - 1
 #ifdef MOE_TRACE
     if (kt < 48) MOE_TRACE_MARK(tslot, 2ull << 60);
 #endif
-    issue(min(kt + 3, nk - 1));     // into stage (kt + 3) % 4, last read during step kt - 1
+    issue(min(kt + kNst - 1, nk - 1));   // into the stage last read during step kt - 1
     half_asm(p1, p0, sn + a_addr[0], sn + b_addr[0]);   // kk = 1 MFMAs; read next kk = 0
 #ifdef MOE_TRACE
     if (kt < 48) MOE_TRACE_MARK(tslot, 3ull << 60);
@@ -1312,6 +1339,7 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
   acc[2][0] = c20; acc[2][1] = c21; acc[3][0] = c30; acc[3][1] = c31;
+  MOE_TILE_MARK(3);
   dma::wait_vm<0>();
   __syncthreads();
 
@@ -1356,6 +1384,8 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
           chunk_at(rr, c);
     }
   }
+  MOE_TILE_MARK(4);
+#undef MOE_TILE_MARK
 }
 
 // Weight gradients with the big tile on the same 4-stage LDS ring: both
