@@ -336,6 +336,30 @@ moe_status moe_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Expert-parallel dispatch emulated on one device ([COUPLING] Abstract: each
+ * token is sent to each GPU once; Fig. 5: dispatch, then every GPU runs its
+ * experts on the rows it received).
+ *
+ * moe_dispatch_pack: send[r] = x[row_token[r]] for r < group_offsets[G] (a
+ *   device value), with row_token and group_offsets from moe_dispatch_plan for
+ *   the same routing.  Rows are group-contiguous in (group, token) order, so
+ *   group g's slice [group_offsets[g], group_offsets[g+1]) is what GPU g
+ *   would receive.  x [T,d] act; send [T*k,d] act (capacity; rows past the
+ *   plan's total are left unchanged).  1 <= G <= 64.
+ * moe_dispatch_expand: x_perm[pos[t,j]] = recv[assign_row[t,j]] for every
+ *   (t, j): the receivers' expansion into expert-contiguous rows.  With recv
+ *   the send buffer (every slice received in place) and pos from moe_permute,
+ *   x_perm equals moe_permute's bit for bit.  recv [T*k,d] act; assign_row,
+ *   pos [T,k] int32; x_perm [T*k,d] act.
+ */
+moe_status moe_dispatch_pack(const moe_dims* dims, int32_t G, const void* x,
+                             const int32_t* group_offsets, const int32_t* row_token, void* send,
+                             void* stream);
+moe_status moe_dispatch_expand(const moe_dims* dims, const void* recv,
+                               const int32_t* assign_row, const int32_t* pos, void* x_perm,
+                               void* stream);
+
+/*
  * moe_placement_greedy -- [host] correlated expert placement ([COUPLING]
  * Abstract and Fig. 3: experts that are often selected together go to the
  * same GPU).  Deterministic, integer arithmetic only.  Fills one group at a

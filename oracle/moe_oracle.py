@@ -517,3 +517,35 @@ def dispatch_plan(idx, placement, G):
         "mean_destinations": rows_total / T,
         "dedup_fraction": (T * k - rows_total) / (T * k),
     }
+
+
+# ---------------------------------------------------------------------------
+# Expert-parallel dispatch emulated on one device ([COUPLING] Abstract: the
+# dispatcher sends each token to each GPU once; Fig. 5 steps 3-4: dispatch,
+# then the receiving GPU runs its experts on the rows it received)
+# ---------------------------------------------------------------------------
+
+def dispatch_pack(x, row_token, n_rows):
+    """Send buffer of the deduplicated plan: row r (group-contiguous, ordered
+    by (group, token)) is X[row_token[r]], for r < n_rows."""
+    x = np.asarray(x)
+    row_token = np.asarray(row_token, dtype=np.int64)
+    send = np.zeros((n_rows,) + x.shape[1:], dtype=x.dtype)
+    for r in range(n_rows):
+        send[r] = x[row_token[r]]
+    return send
+
+
+def dispatch_expand(recv, assign_row, pos):
+    """The receivers' re-expansion into expert-contiguous rows: the row of
+    assignment (t, j), pos[t, j], is the received row assign_row[t, j]."""
+    recv = np.asarray(recv)
+    assign_row = np.asarray(assign_row, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    T, k = pos.shape
+    out = np.zeros((T * k,) + recv.shape[1:], dtype=recv.dtype)
+    for t in range(T):
+        for j in range(k):
+            out[pos[t, j]] = recv[assign_row[t, j]]
+    return out
+

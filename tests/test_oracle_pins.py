@@ -387,6 +387,37 @@ def test_dispatch_plan_structure_and_edge_cases():
     assert p_1["rows_total"] == T and p_1["tokens_single_group"] == T
 
 
+@pytest.mark.parametrize("G,placement", [(4, "contiguous"), (4, "shuffled"), (16, "contiguous"),
+                                         (1, "contiguous")])
+def test_ep_dispatch_pack_then_expand_is_the_permutation(G, placement):
+    """Packing X by the dedup plan (one row per (group, token)) and then
+    re-expanding every (t, j) from its row gives exactly the expert-contiguous
+    rows of the permutation: x_perm[p] = X[src[p]].  This ties the two plans
+    together (assign_row must name a row that holds token t, in the group that
+    owns expert idx[t, j]), and a copy that dropped or swapped a row, or a plan
+    with a wrong assign_row, breaks the equality."""
+    T, E, k = 96, 16, 4
+    idx = make_routing(T, E, k, seed=50 + G)
+    pl = (O.placement_contiguous(E, G) if placement == "contiguous"
+          else np.array(stream(51, G).permutation(np.arange(E) % G)))
+    x = stream(52, G).standard_normal((T, 8))
+    plan = O.dispatch_plan(idx, pl, G)
+    send = O.dispatch_pack(x, plan["row_token"], plan["rows_total"])
+    assert send.shape[0] == plan["rows_total"] <= T * k
+    # the receive side of one GPU is its group's slice of the send buffer;
+    # here every group is received locally, so the buffer is passed through
+    perm = O.permute_plan(idx, E)
+    xp = O.dispatch_expand(send, plan["assign_row"], perm["pos"])
+    assert np.array_equal(xp, O.gather_rows(x, perm["src"]))
+    # and each group's slice holds only tokens routed to one of its experts
+    for g in range(G):
+        rows = range(plan["group_offsets"][g], plan["group_offsets"][g + 1])
+        for r in rows:
+            t = plan["row_token"][r]
+            assert np.array_equal(send[r], x[t])
+            assert g in {int(pl[e]) for e in idx[t]}
+
+
 def test_placement_checks():
     O.check_placement(O.placement_contiguous(16, 4), 16, 4)
     with pytest.raises(ValueError):

@@ -18,14 +18,20 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_combine_bwd,
     moe_coselect,
+    moe_dispatch_expand,
+    moe_dispatch_pack,
     moe_dispatch_plan,
     moe_expert_dgrad_down,
     moe_expert_dgrad_up,
     moe_expert_down,
     moe_expert_up,
+    moe_expert_up_gather,
     moe_expert_wgrad,
+    moe_expert_wgrad_gather,
     moe_grouped_swiglu_bwd,
+    moe_grouped_swiglu_bwd_gather,
     moe_grouped_swiglu_fwd,
+    moe_grouped_swiglu_fwd_gather,
     moe_permute,
     moe_placement_greedy,
     moe_route,

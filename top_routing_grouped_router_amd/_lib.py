@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_check_placement", "moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
     "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_wgrad_launches",
     "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
-    "moe_expert_wgrad_gather",
+    "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
 )
 
 
@@ -82,6 +82,8 @@ _SIGNATURES = {
     "moe_expert_dgrad_up": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_wgrad": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_up_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_pack": (_I32, [_DIMS, _I32, _P, _P, _P, _P, _P]),
+    "moe_dispatch_expand": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
     "moe_expert_wgrad_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
     "moe_grouped_swiglu_fwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -388,3 +390,23 @@ def moe_expert_wgrad_gather(dims, x, src_token, expert_offsets, h_save, dy_perm,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "moe_expert_wgrad_gather")
+
+
+# ---------------------------------------------------------------- EP dispatch on one device
+def moe_dispatch_pack(dims, G, x, group_offsets, row_token, send, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_dispatch_pack(ctypes.byref(dims), int(G), _ptr(x, "x", act),
+                                 _ptr(group_offsets, "group_offsets", torch.int32),
+                                 _ptr(row_token, "row_token", torch.int32),
+                                 _ptr(send, "send", act), _stream(stream))
+    _check(st, "moe_dispatch_pack")
+
+
+def moe_dispatch_expand(dims, recv, assign_row, pos, x_perm, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_dispatch_expand(ctypes.byref(dims), _ptr(recv, "recv", act),
+                                   _ptr(assign_row, "assign_row", torch.int32),
+                                   _ptr(pos, "pos", torch.int32), _ptr(x_perm, "x_perm", act),
+                                   _stream(stream))
+    _check(st, "moe_dispatch_expand")
+

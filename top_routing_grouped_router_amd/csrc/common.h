@@ -177,4 +177,11 @@ hipError_t launch_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G,
                                 int32_t* ws_hist, int32_t* ws_base, int32_t* ws_stat,
                                 hipStream_t s);
 
+// expert-parallel dispatch emulated on one device
+hipError_t launch_ep_pack(const moe_dims& dm, int32_t G, const void* x,
+                          const int32_t* group_offsets, const int32_t* row_token, void* send,
+                          hipStream_t s);
+hipError_t launch_ep_expand(const moe_dims& dm, const void* recv, const int32_t* assign_row,
+                            const int32_t* pos, void* x_perm, hipStream_t s);
+
 }  // namespace moe

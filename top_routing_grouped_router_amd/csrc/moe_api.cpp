@@ -747,4 +747,37 @@ moe_status moe_grouped_swiglu_bwd_gather(const moe_dims* dims, const void* x,
                     __func__);
 }
 
+// ---------------------------------------------------------------- EP dispatch on one device
+moe_status moe_dispatch_pack(const moe_dims* dims, int32_t G, const void* x,
+                             const int32_t* group_offsets, const int32_t* row_token, void* send,
+                             void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  if (G <= 0 || G > 64)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need 1 <= G <= 64", __func__);
+  MOE_REQUIRE_PTR(x, dm.T * dm.d);
+  MOE_REQUIRE_PTR(group_offsets, G + 1);
+  MOE_REQUIRE_PTR(row_token, dm.T * dm.k);
+  MOE_REQUIRE_PTR(send, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_ep_pack(dm, G, x, group_offsets, row_token, send,
+                                        static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_dispatch_expand(const moe_dims* dims, const void* recv,
+                               const int32_t* assign_row, const int32_t* pos, void* x_perm,
+                               void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(recv, dm.T * dm.k * dm.d);
+  MOE_REQUIRE_PTR(assign_row, dm.T * dm.k);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
+  return hip_status(moe::launch_ep_expand(dm, recv, assign_row, pos, x_perm,
+                                          static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
 }  // extern "C"
