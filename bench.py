@@ -165,6 +165,60 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
                       f"{'+bwd' if cfg.backward else ''}), fp64 numpy, {el:.1f} s"}
 
 
+def ep_dispatch(cfg, layer, x, steps):
+    """Expert-parallel dispatch emulated on one GPU for each placement group
+    count of the workload (contiguous placement): the dedup plan, the pack of
+    one row per (group, token) and the receivers' expansion into x_perm, each
+    timed with HIP events over `steps` launches.  Bytes per pack: rows read +
+    rows written (+ row ids); per expand: T k rows read + written (+ ids)."""
+    import torch
+    import top_routing_grouped_router_amd._lib as L
+    T, k, E, d = cfg.T, cfg.k, cfg.E, cfg.d
+    s = 2 if cfg.act == "bf16" else 4
+    dm = layer.dims
+    res = {}
+    for G in cfg.plan_groups:
+        pl = [e * G // E for e in range(E)]
+        i32 = dict(dtype=torch.int32, device="cuda")
+        out = {"n_dest": torch.empty(T, **i32), "group_rows": torch.empty(G, **i32),
+               "group_offsets": torch.empty(G + 1, **i32), "row_token": torch.empty(T * k, **i32),
+               "assign_row": torch.empty(T, k, **i32), "stats": torch.empty(4, **i32)}
+        ws = torch.empty(L.workspace_bytes(dm, G), dtype=torch.uint8, device="cuda")
+        send = torch.empty(T * k, d, dtype=x.dtype, device="cuda")
+        xp = torch.empty(T * k, d, dtype=x.dtype, device="cuda")
+        fns = {
+            "plan": lambda: L.moe_dispatch_plan(T, k, E, G, layer.topk_idx, pl, out["n_dest"],
+                                                out["group_rows"], out["group_offsets"],
+                                                out["row_token"], out["assign_row"],
+                                                out["stats"], ws),
+            "pack": lambda: L.moe_dispatch_pack(dm, G, x, out["group_offsets"], out["row_token"],
+                                                send),
+            "expand": lambda: L.moe_dispatch_expand(dm, send, out["assign_row"], layer.pos, xp),
+        }
+        times = {}
+        for name, fn in fns.items():
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times[name] = a.elapsed_time(b) / steps * 1e-3
+        rows = int(out["stats"][0].item())
+        pack_b = rows * d * s * 2 + rows * 4
+        exp_b = T * k * d * s * 2 + T * k * 8
+        res[f"G{G}_contiguous"] = {
+            "rows": rows, "rows_removed": T * k - rows,
+            "plan_us": round(times["plan"] * 1e6, 1),
+            "pack_us": round(times["pack"] * 1e6, 1),
+            "pack_GBps": round(pack_b / times["pack"] / 1e9, 1),
+            "expand_us": round(times["expand"] * 1e6, 1),
+            "expand_GBps": round(exp_b / times["expand"] / 1e9, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +230,10 @@ def main():
     ap.add_argument("--no-gather", action="store_true",
                     help="materialise x_perm in moe_permute and run the expert GEMMs on it "
                          "instead of gathering the expert input rows from X")
+    ap.add_argument("--ep", action="store_true",
+                    help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
+                         "expand) for the workload's placement group counts; adds an "
+                         "'ep_dispatch' object to the JSON line")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a "
                          "known-size kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -330,6 +388,8 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": roof,
     }
+    if args.ep and cfg.plan_groups:
+        out["ep_dispatch"] = ep_dispatch(cfg, layer, x, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)
