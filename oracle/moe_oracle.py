@@ -33,13 +33,22 @@ design notes of the repository):
     it is below eps (default 1e-3); the normalised margin of [LAYOUT] Finding 3
     (gap / spread of the token's logits) is reported beside it;
   * SwiGLU: h = silu(x W1^T) * (x W3^T), y = h W2^T, weights [E, out, in];
-  * dropless routing (no capacity);
+  * dropless routing in the main path; the capacity variant (capacity_keep)
+    gives each expert C = ceil(factor * (T/G) * k / E) places per block of T/G
+    tokens, filled slot-major (all first choices in token order, then all
+    second choices, ...); assignments past C are dropped (expert id -1, no
+    row, no output), gates are not renormalised after dropping;
+  * auxiliary losses: L_aux = mean over blocks of E * sum_e f_e P_e (f held
+    constant), L_z = mean over tokens of logsumexp(l)^2, each times its
+    coefficient;
   * LB statistics per contiguous token block: f = count / (block tokens * k),
     P = mean full-softmax probability, aux = E * sum_e f_e P_e;
   * dedup plan rows ordered by (group, token); all destinations count,
     including the token's home block.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -182,24 +191,29 @@ def lb_stats(logits, idx, E, G):
 def permute_plan(idx, E):
     """Stable counting sort of the T*k (token, slot) assignments by expert.
 
-    Inside one expert's segment the rows are in ascending token id.
+    Inside one expert's segment the rows are in ascending token id.  An
+    expert id of -1 marks a dropped assignment (capacity_keep): it gets no row
+    and pos -1.
     Returns counts [E], offsets [E+1], pos [T,k] (row of assignment (t, j)),
-    src [T*k] (token of each row), all int64.
+    src [T*k] (token of each row; -1 past offsets[E]), all int64.
     """
     T, k = idx.shape
     counts = np.zeros(E, dtype=np.int64)
     for t in range(T):
         for j in range(k):
-            counts[idx[t, j]] += 1
+            if idx[t, j] >= 0:
+                counts[idx[t, j]] += 1
     offsets = np.zeros(E + 1, dtype=np.int64)
     for e in range(E):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = offsets[:-1].copy()
-    pos = np.zeros((T, k), dtype=np.int64)
-    src = np.zeros(T * k, dtype=np.int64)
+    pos = np.full((T, k), -1, dtype=np.int64)
+    src = np.full(T * k, -1, dtype=np.int64)
     for t in range(T):
         for j in range(k):
             e = idx[t, j]
+            if e < 0:
+                continue
             pos[t, j] = fill[e]
             src[fill[e]] = t
             fill[e] += 1
@@ -291,18 +305,22 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm, act="f64"):
 # ---------------------------------------------------------------------------
 
 def combine(rows, pos, gates=None, act="f64"):
-    """y[t] = sum_j g[t, j] * rows[pos[t, j]]  (unit weights when gates is None)."""
+    """y[t] = sum_j g[t, j] * rows[pos[t, j]]  (unit weights when gates is None);
+    slots with pos -1 (dropped) add nothing."""
     rows = _f64(rows)
     T, k = pos.shape
     y = np.zeros((T, rows.shape[1]))
     for j in range(k):
         w = 1.0 if gates is None else _f64(gates)[:, j:j + 1]
-        y += w * rows[np.asarray(pos[:, j], dtype=np.int64)]
+        p = np.asarray(pos[:, j], dtype=np.int64)
+        live = (p >= 0)[:, None]
+        y += np.where(live, w * rows[np.maximum(p, 0)], 0.0)
     return storage(act)(y)
 
 
 def combine_bwd(dy, y_perm, pos, gates, act="f64"):
-    """dy_perm[pos[t,j]] = g[t,j] dY[t];  dgate[t,j] = <dY[t], y_perm[pos[t,j]]>.
+    """dy_perm[pos[t,j]] = g[t,j] dY[t];  dgate[t,j] = <dY[t], y_perm[pos[t,j]]>;
+    a dropped slot (pos -1) has no row and dgate 0.
     (act="bf16": dy_perm is stored as bfloat16; dgate is a router quantity.)"""
     st = storage(act)
     dy, y_perm, gates = _f64(dy), _f64(y_perm), _f64(gates)
@@ -311,8 +329,9 @@ def combine_bwd(dy, y_perm, pos, gates, act="f64"):
     dgate = np.zeros((T, k))
     for j in range(k):
         p = np.asarray(pos[:, j], dtype=np.int64)
-        dy_perm[p] = st(gates[:, j:j + 1] * dy)
-        dgate[:, j] = (dy * y_perm[p]).sum(axis=1)
+        live = p >= 0
+        dy_perm[p[live]] = st(gates[live, j:j + 1] * dy[live])
+        dgate[live, j] = (dy[live] * y_perm[p[live]]).sum(axis=1)
     return dy_perm, dgate
 
 
@@ -320,8 +339,10 @@ def combine_bwd(dy, y_perm, pos, gates, act="f64"):
 # Router backward (adjoint of logits -> top-k -> renormalised softmax)
 # ---------------------------------------------------------------------------
 
-def route_bwd(x, wr, idx, gates, dgate):
+def route_bwd(x, wr, idx, gates, dgate, logits=None, count=None, aux_coef=0.0, z_coef=0.0):
     """dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i), zero for unchosen experts;
+    plus aux_coef * dL_aux/dl and z_coef * dL_z/dl when those are non-zero
+    (logits [T,E] and, for L_aux, the block counts [G,E] of lb_stats);
     dX_router = dl Wr;  dWr = dl^T X."""
     x, wr, gates, dgate = _f64(x), _f64(wr), _f64(gates), _f64(dgate)
     T, k = idx.shape
@@ -331,19 +352,127 @@ def route_bwd(x, wr, idx, gates, dgate):
     dl = np.zeros((T, E))
     for j in range(k):
         dl[np.arange(T), idx[:, j]] += dsel[:, j]
+    if aux_coef != 0.0:
+        dl += aux_coef * aux_loss_grad(logits, count, k)
+    if z_coef != 0.0:
+        dl += z_coef * z_loss_grad(logits)
     return {"dlogits": dl, "dx_router": dl @ wr, "dwr": dl.T @ x}
+
+
+# ---------------------------------------------------------------------------
+# Definitional variants ([REVISIT] Sec. 2.1: Top-K routing with an expert
+# capacity, the GShard load-balancing loss and the ST-MoE router z-loss;
+# Sec. 4: a lower capacity for training than for evaluation; [LAYOUT] Two
+# Kinds of Layout Effects: capacity and balancing computed per machine, here
+# per contiguous block of T/G tokens)
+# ---------------------------------------------------------------------------
+
+def expert_capacity(T, k, E, G, factor):
+    """Places per expert in one block of n = T/G tokens: ceil(factor * (n k) / E),
+    the capacity factor times the block's mean load per expert."""
+    n = T // G
+    return int(math.ceil(factor * float(n * k) / E))
+
+
+def capacity_keep(idx, E, G, C):
+    """Per-block capacity with dropping.
+
+    Inside block r (tokens r n .. r n + n - 1) the assignments queue for their
+    experts slot-major, as GShard places second choices after all first
+    choices: slot 0 of every token in token order, then slot 1, and so on.
+    place[t, j] is the number of assignments ahead of (t, j) in its expert's
+    queue; the assignment is kept when place < C, else dropped.
+    Returns kept_idx [T,k] (expert id, or -1 when dropped), place [T,k] and
+    dropped [G] (dropped assignments per block).
+    """
+    T, k = idx.shape
+    n = T // G
+    kept = np.array(idx, dtype=np.int64)
+    place = np.zeros((T, k), dtype=np.int64)
+    dropped = np.zeros(G, dtype=np.int64)
+    for r in range(G):
+        load = np.zeros(E, dtype=np.int64)
+        for j in range(k):
+            for t in range(r * n, (r + 1) * n):
+                e = idx[t, j]
+                place[t, j] = load[e]
+                load[e] += 1
+                if place[t, j] >= C:
+                    kept[t, j] = -1
+                    dropped[r] += 1
+    return {"kept_idx": kept, "place": place, "dropped": dropped}
+
+
+def _logsumexp(logits):
+    logits = _f64(logits)
+    m = logits.max(axis=1)
+    return m + np.log(np.exp(logits - m[:, None]).sum(axis=1))
+
+
+def aux_loss(logits, count, k):
+    """L_aux = (1/G) sum_r E sum_e f[r,e] P[r,e] with f = count / (n k) (a
+    constant) and P[r] the mean full softmax over block r: the mean of
+    lb_stats' aux over the blocks."""
+    logits = _f64(logits)
+    G, E = count.shape
+    n = logits.shape[0] // G
+    p = full_softmax(logits)
+    total = 0.0
+    for r in range(G):
+        f = count[r] / float(n * k)
+        P = p[r * n:(r + 1) * n].mean(axis=0)
+        total += E * (f * P).sum()
+    return total / G
+
+
+def aux_loss_grad(logits, count, k):
+    """dL_aux/dl[t,i] = E / (G n) * p[t,i] (f[r,i] - sum_e f[r,e] p[t,e]),
+    the softmax Jacobian applied to f, for t in block r."""
+    logits = _f64(logits)
+    G, E = count.shape
+    T = logits.shape[0]
+    n = T // G
+    p = full_softmax(logits)
+    dl = np.zeros((T, E))
+    for r in range(G):
+        f = count[r] / float(n * k)
+        pr = p[r * n:(r + 1) * n]
+        fp = (pr * f[None, :]).sum(axis=1, keepdims=True)
+        dl[r * n:(r + 1) * n] = (E / float(G * n)) * pr * (f[None, :] - fp)
+    return dl
+
+
+def z_loss(logits):
+    """L_z = (1/T) sum_t (log sum_e exp l[t,e])^2."""
+    return float((_logsumexp(logits) ** 2).mean())
+
+
+def z_loss_groups(logits, G):
+    """Per block r: the mean over its tokens of logsumexp(l[t])^2."""
+    z = _logsumexp(logits) ** 2
+    return z.reshape(G, -1).mean(axis=1)
+
+
+def z_loss_grad(logits):
+    """dL_z/dl[t,i] = (2 / T) lse_t p[t,i]."""
+    logits = _f64(logits)
+    T = logits.shape[0]
+    return (2.0 / T) * _logsumexp(logits)[:, None] * full_softmax(logits)
 
 
 # ---------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------
 
-def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f64"):
+def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f64",
+                  capacity=None, lb_groups=1):
     """Router -> permute -> SwiGLU experts -> combine.
 
     routing, when given, is a (topk_idx, gates) pair that replaces the router's
     own decision (the logits, margins and near-ties are still reported).
     act: storage precision of the activations ("f64" or "bf16").
+    capacity, when given, is the per-block expert capacity C of capacity_keep
+    over lb_groups blocks; dropped assignments get no row and no output.
     """
     E = np.asarray(wr).shape[0]
     r = route(x, wr, k, near_tie_eps)
@@ -353,26 +482,40 @@ def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f6
         gates = _f64(gates)
     else:
         idx, gates = r["topk_idx"], r["gates"]
-    plan = permute_plan(idx, E)
+    kept = idx
+    cap = None
+    if capacity is not None:
+        cap = capacity_keep(idx, E, lb_groups, capacity)
+        kept = cap["kept_idx"]
+    plan = permute_plan(kept, E)
     x_perm = gather_rows(x, plan["src"])
     ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2, act)
     y = combine(ex["y_perm"], plan["pos"], gates, act)
     out = dict(r)
     out.update(plan)
     out.update(ex)
-    out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y, "act": act})
+    out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y, "act": act,
+                "kept_idx": kept, "lb_groups": lb_groups})
+    if cap is not None:
+        out["dropped"] = cap["dropped"]
     return out
 
 
-def layer_backward(x, wr, w1, w3, w2, fwd, dy):
+def layer_backward(x, wr, w1, w3, w2, fwd, dy, aux_coef=0.0, z_coef=0.0):
     """Backward of layer_forward for the upstream gradient dy [T, d], in the
-    forward's storage precision."""
+    forward's storage precision, plus the gradients of aux_coef * L_aux (over
+    the forward's lb_groups blocks) and z_coef * L_z when they are non-zero."""
     act = fwd.get("act", "f64")
     dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"], act)
     eb = swiglu_experts_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2,
                             fwd["a"], fwd["b"], dy_perm, act)
     dx_exp = combine(eb["dx_perm"], fwd["pos"], None)
-    rb = route_bwd(x, wr, fwd["topk_idx"], fwd["gates"], dgate)
+    count = None
+    if aux_coef != 0.0:
+        E = np.asarray(wr).shape[0]
+        count = lb_stats(fwd["logits"], fwd["topk_idx"], E, fwd.get("lb_groups", 1))["count"]
+    rb = route_bwd(x, wr, fwd["topk_idx"], fwd["gates"], dgate, fwd["logits"], count,
+                   aux_coef, z_coef)
     return {
         "dy_perm": dy_perm, "dgate": dgate,
         "dx_perm": eb["dx_perm"], "dh": eb["dh"], "da": eb["da"], "db": eb["db"],

@@ -521,3 +521,235 @@ def test_pins_catch_planted_mistakes(monkeypatch):
 
     rows = np.zeros((1, 4))
     assert list(topk_high_id(rows, 2)[0][0]) != brute_topk([0.0] * 4, 2)[0]
+
+
+# ---------------------------------------------------------------- capacity and dropping
+
+def test_capacity_worked_example():
+    with open(os.path.join(GOLDEN, "capacity_top2_worked.json")) as fh:
+        gold = json.load(fh)
+    idx = np.array(gold["topk_idx"], dtype=np.int32)
+    T, k = idx.shape
+    for case in gold["cases"]:
+        C = O.expert_capacity(T, k, gold["E"], case["G"], case["factor"])
+        assert C == case["C"]
+        cap = O.capacity_keep(idx, gold["E"], case["G"], C)
+        assert cap["place"].tolist() == case["place"]
+        assert cap["kept_idx"].tolist() == case["kept_idx"]
+        assert cap["dropped"].tolist() == case["dropped"]
+
+
+def _gshard_positions(idx, E, G):
+    """GShard's vectorised placement: per block and slot, one-hot masks, a
+    cumulative sum over tokens, offset by the block's totals of earlier slots."""
+    T, k = idx.shape
+    n = T // G
+    place = np.zeros((T, k), dtype=np.int64)
+    for r in range(G):
+        prior = np.zeros(E, dtype=np.int64)
+        for j in range(k):
+            mask = np.eye(E, dtype=np.int64)[idx[r * n:(r + 1) * n, j]]      # [n, E]
+            posn = (np.cumsum(mask, axis=0) - 1 + prior[None, :]) * mask
+            place[r * n:(r + 1) * n, j] = posn.sum(axis=1)
+            prior += mask.sum(axis=0)
+    return place
+
+
+@pytest.mark.parametrize("G,factor", [(1, 1.0), (2, 1.25), (4, 0.5), (4, 2.0)])
+def test_capacity_matches_gshard_cumsum_and_invariants(G, factor):
+    T, E, k = 96, 8, 3
+    g = stream(41, G)
+    logits = g.standard_normal((T, E)) + np.array([1.5, 1.0, 0.5, 0, 0, 0, 0, 0])
+    idx, _ = O.topk_select(logits, k)
+    C = O.expert_capacity(T, k, E, G, factor)
+    cap = O.capacity_keep(idx, E, G, C)
+    assert np.array_equal(cap["place"], _gshard_positions(idx, E, G))
+    n = T // G
+    for r in range(G):
+        blk = slice(r * n, (r + 1) * n)
+        load = np.bincount(idx[blk].ravel(), minlength=E)
+        kept = cap["kept_idx"][blk]
+        kept_load = np.bincount(kept[kept >= 0].ravel(), minlength=E)
+        assert np.array_equal(kept_load, np.minimum(load, C))
+        assert cap["dropped"][r] == np.maximum(load - C, 0).sum()
+    assert np.array_equal(cap["kept_idx"] >= 0, cap["place"] < C)
+
+
+def test_capacity_layer_matches_gshard_einsum_with_capacity_slots():
+    """Dispatch [T,E,C] and combine tensors built from the GShard positions; a
+    dropped assignment has no slot, so it adds nothing to the output."""
+    g = stream(43, 0)
+    T, d, E, f, k, G = 48, 8, 6, 5, 2, 2
+    x = g.standard_normal((T, d))
+    wr = g.standard_normal((E, d)) + 0.8 * np.eye(E, d)
+    w1 = g.standard_normal((E, f, d)) / 3
+    w3 = g.standard_normal((E, f, d)) / 3
+    w2 = g.standard_normal((E, d, f)) / 3
+    C = O.expert_capacity(T, k, E, G, 0.75)
+    out = O.layer_forward(x, wr, w1, w3, w2, k, capacity=C, lb_groups=G)
+    idx, gates = out["topk_idx"], out["gates"]
+    place = _gshard_positions(idx, E, G)
+    n = T // G
+    y = np.zeros((T, d))
+    dropped = 0
+    for r in range(G):
+        blk = slice(r * n, (r + 1) * n)
+        disp = np.zeros((n, E, C))
+        comb = np.zeros((n, E, C))
+        for tl in range(n):
+            for j in range(k):
+                c = place[r * n + tl, j]
+                if c < C:
+                    disp[tl, idx[r * n + tl, j], c] = 1.0
+                    comb[tl, idx[r * n + tl, j], c] = gates[r * n + tl, j]
+                else:
+                    dropped += 1
+        xin = np.einsum("tec,td->ecd", disp, x[blk])                         # [E, C, d]
+        a = np.einsum("ecd,efd->ecf", xin, w1)
+        b = np.einsum("ecd,efd->ecf", xin, w3)
+        hh = a / (1.0 + np.exp(-a)) * b
+        yout = np.einsum("ecf,edf->ecd", hh, w2)
+        y[blk] = np.einsum("tec,ecd->td", comb, yout)
+    assert dropped > 0 and dropped == out["dropped"].sum()
+    assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+
+
+def test_capacity_edge_cases():
+    g = stream(44, 0)
+    T, d, E, f, k = 32, 8, 4, 4, 2
+    x = g.standard_normal((T, d))
+    wr = g.standard_normal((E, d))
+    w1 = g.standard_normal((E, f, d))
+    w3 = g.standard_normal((E, f, d))
+    w2 = g.standard_normal((E, d, f))
+    base = O.layer_forward(x, wr, w1, w3, w2, k)
+    big = O.layer_forward(x, wr, w1, w3, w2, k, capacity=T * k, lb_groups=2)
+    assert np.array_equal(big["kept_idx"], base["topk_idx"])
+    assert np.array_equal(big["y"], base["y"])
+    none = O.layer_forward(x, wr, w1, w3, w2, k, capacity=0, lb_groups=4)
+    assert np.all(none["kept_idx"] == -1) and np.all(none["pos"] == -1)
+    assert none["offsets"][-1] == 0 and np.all(none["y"] == 0)
+    assert none["dropped"].sum() == T * k
+    dy = g.standard_normal((T, d))
+    bw = O.layer_backward(x, wr, w1, w3, w2, none, dy)
+    assert np.all(bw["dgate"] == 0) and np.all(bw["dx"] == 0) and np.all(bw["dwr"] == 0)
+
+
+# ---------------------------------------------------------------- auxiliary losses
+
+def _numeric_grad(fun, arr, h=1e-6):
+    num = np.zeros_like(arr)
+    it = np.nditer(arr, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = arr[i]
+        arr[i] = old + h
+        lp = fun(arr)
+        arr[i] = old - h
+        lm = fun(arr)
+        arr[i] = old
+        num[i] = (lp - lm) / (2 * h)
+    return num
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_aux_loss_grad_matches_finite_differences(G):
+    g = stream(45, G)
+    T, E, k = 16, 6, 2
+    logits = g.standard_normal((T, E))
+    idx, _ = O.topk_select(logits, k)
+    count = O.lb_stats(logits, idx, E, G)["count"]
+    # with the counts held fixed, the loss is the mean of lb_stats' aux
+    assert math.isclose(O.aux_loss(logits, count, k), O.lb_stats(logits, idx, E, G)["aux"].mean(),
+                        rel_tol=1e-14)
+    num = _numeric_grad(lambda l: O.aux_loss(l, count, k), logits.copy())
+    ana = O.aux_loss_grad(logits, count, k)
+    assert np.abs(num - ana).max() < 1e-8 * max(1.0, np.abs(num).max())
+
+
+def test_aux_loss_grad_vanishes_for_uniform_counts():
+    g = stream(46, 0)
+    T, E, k = 12, 4, 2
+    logits = g.standard_normal((T, E))
+    count = np.full((3, E), (T // 3) * k // E)          # every expert equally loaded
+    assert np.abs(O.aux_loss_grad(logits, count, k)).max() < 1e-15
+
+
+def test_z_loss_grad_matches_finite_differences_and_closed_form():
+    g = stream(47, 0)
+    T, E = 10, 7
+    logits = 3.0 * g.standard_normal((T, E))
+    num = _numeric_grad(O.z_loss, logits.copy())
+    ana = O.z_loss_grad(logits)
+    assert np.abs(num - ana).max() < 1e-8 * max(1.0, np.abs(num).max())
+    c = 0.375
+    flat = np.full((T, E), c)
+    lse = c + math.log(E)
+    assert math.isclose(O.z_loss(flat), lse * lse, rel_tol=1e-15)
+    assert np.allclose(O.z_loss_grad(flat), 2.0 / T * lse / E, rtol=1e-14, atol=0)
+    assert np.allclose(O.z_loss_groups(logits, 2).mean(), O.z_loss(logits), rtol=1e-14)
+
+
+@pytest.mark.parametrize("seed,cap", [(0, None), (1, 3), (2, 2)])
+def test_layer_backward_with_losses_and_capacity_matches_finite_differences(seed, cap):
+    """Loss = <dY, Y> + aux_coef L_aux + z_coef L_z, with per-block capacity
+    dropping some assignments: every gradient against central differences."""
+    T, d, E, f, k, G = 8, 6, 4, 4, 2, 2
+    aux_coef, z_coef = 0.3, 0.2
+    for attempt in range(1000):
+        g = stream(48 + seed, attempt)
+        x = g.standard_normal((T, d))
+        wr = g.standard_normal((E, d))
+        r = O.route(x, wr, k)
+        if r["margin"].min() >= 1e-2:
+            break
+    w1 = g.standard_normal((E, f, d)) / 2
+    w3 = g.standard_normal((E, f, d)) / 2
+    w2 = g.standard_normal((E, d, f)) / 2
+    dy = g.standard_normal((T, d))
+    fwd = O.layer_forward(x, wr, w1, w3, w2, k, capacity=cap, lb_groups=G)
+    if cap is not None:
+        assert fwd["dropped"].sum() > 0
+    count = O.lb_stats(fwd["logits"], fwd["topk_idx"], E, G)["count"]
+    bwd = O.layer_backward(x, wr, w1, w3, w2, fwd, dy, aux_coef, z_coef)
+    params = {"x": x, "wr": wr, "w1": w1, "w3": w3, "w2": w2}
+
+    def loss(p):
+        out = O.layer_forward(p["x"], p["wr"], p["w1"], p["w3"], p["w2"], k, capacity=cap,
+                              lb_groups=G)
+        assert np.array_equal(out["kept_idx"], fwd["kept_idx"])
+        return float((out["y"] * dy).sum() + aux_coef * O.aux_loss(out["logits"], count, k)
+                     + z_coef * O.z_loss(out["logits"]))
+
+    grads = {"x": bwd["dx"], "wr": bwd["dwr"], "w1": bwd["dw1"], "w3": bwd["dw3"], "w2": bwd["dw2"]}
+    for name, arr in params.items():
+        num = _numeric_grad(lambda a: loss(params), arr)
+        scale = max(np.abs(num).max(), 1e-3)
+        assert np.abs(num - grads[name]).max() / scale < 1e-6, name
+
+
+def test_new_pins_catch_planted_mistakes():
+    # token-major instead of slot-major queueing: the worked example disagrees
+    with open(os.path.join(GOLDEN, "capacity_top2_worked.json")) as fh:
+        gold = json.load(fh)
+    idx = np.array(gold["topk_idx"], dtype=np.int32)
+    load = np.zeros(gold["E"], dtype=np.int64)
+    place = np.zeros_like(idx)
+    for t in range(idx.shape[0]):
+        for j in range(idx.shape[1]):
+            place[t, j] = load[idx[t, j]]
+            load[idx[t, j]] += 1
+    assert place.tolist() != gold["cases"][0]["place"]
+    # the aux gradient without the softmax Jacobian's second term: differences disagree
+    g = stream(45, 1)
+    logits = g.standard_normal((16, 6))
+    idx2, _ = O.topk_select(logits, 2)
+    count = O.lb_stats(logits, idx2, 6, 2)["count"]
+    p = O.full_softmax(logits)
+    f = np.repeat(count / 16.0, 8, axis=0)
+    wrong = 6 / 16.0 * p * f
+    num = _numeric_grad(lambda l: O.aux_loss(l, count, 2), logits.copy())
+    assert np.abs(num - wrong).max() > 1e-3
+    # a z gradient missing the factor 2: differences disagree
+    num = _numeric_grad(O.z_loss, logits.copy())
+    assert np.abs(num - 0.5 * O.z_loss_grad(logits)).max() > 1e-3
