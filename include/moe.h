@@ -132,11 +132,14 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
  *   [REVISIT] Sec. 2.2 (GShard dispatch: a token's position inside its expert
  *   is the running count of earlier tokens that chose that expert).
  *
- * topk_idx [T,k] int32 in.
- * expert_counts [E], expert_offsets [E+1] (exclusive scan; offsets[E] = T*k).
+ * topk_idx [T,k] int32 in.  An id of -1 marks a dropped assignment (see
+ *   moe_capacity): it gets pos -1 and no row.
+ * expert_counts [E], expert_offsets [E+1] (exclusive scan; offsets[E] = the
+ *   number of kept assignments, T*k when nothing is dropped).
  * pos [T,k]: row of assignment (t, j) in the permuted order; rows of one
  *   expert are in ascending token id.
- * src_token [T*k]: token of each permuted row.
+ * src_token [T*k]: token of each permuted row (entries past offsets[E] are
+ *   left unchanged).
  * x [T,d] act and x_perm [T*k,d] act: x_perm[pos[t,j]] = x[t].  Pass both
  *   NULL to build the plan only.
  */
@@ -171,7 +174,8 @@ moe_status moe_grouped_swiglu_fwd(const moe_dims* dims, const void* x_perm,
  *   [REVISIT] Sec. 2.2 (GShard combine).
  *
  * out[t] = sum_{j<k} gate[t,j] * rows[pos[t,j]], accumulated in fp32 in slot
- * order j = 0..k-1, then stored as act.  gate == NULL means unit weights
+ * order j = 0..k-1, then stored as act; slots with pos -1 (dropped) add
+ * nothing.  gate == NULL means unit weights
  * (the plain unpermute-and-sum used for the input gradient).
  * rows [T*k,d] act; pos [T,k]; gate [T,k] fp32 or NULL; out [T,d] act.
  */
@@ -184,6 +188,7 @@ moe_status moe_combine(const moe_dims* dims, const void* rows, const int32_t* po
  *
  * dy_perm[pos[t,j]] = gate[t,j] * dy[t]           (act)
  * dgate[t,j]        = <dy[t], y_perm[pos[t,j]]>   (fp32 dot over d)
+ * A dropped slot (pos -1) writes no row and gets dgate 0.
  * dy [T,d] act; y_perm [T*k,d] act; pos [T,k]; gate [T,k] fp32;
  * dy_perm [T*k,d] act; dgate [T,k] fp32.
  */
@@ -296,6 +301,8 @@ moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
  * x [T,d] act; w_router [E,d]; topk_idx, topk_gate, dgate [T,k];
  * expert_offsets [E+1], pos [T,k], src_token [T*k] from moe_permute;
  * dx_perm [T*k,d] act or NULL; dx [T,d] act; dw_router [E,d] fp32.
+ * Every assignment must have a row (pos >= 0): with dropped assignments use
+ * moe_route_bwd_dense, which also carries the auxiliary losses.
  */
 moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_router,
                          const int32_t* topk_idx, const float* topk_gate, const float* dgate,
@@ -303,6 +310,70 @@ moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_rou
                          const int32_t* src_token, const void* dx_perm, void* dx,
                          float* dw_router, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * Definitional variants of the routing rules ([REVISIT] Sec. 2.1: Top-K
+ * routing with an expert capacity, the GShard load-balancing loss and the
+ * ST-MoE router z-loss; Sec. 4: capacity 1.25 for training and 2.0 for
+ * evaluation; [LAYOUT] Two Kinds of Layout Effects: capacity and balancing
+ * rules evaluated per machine, here per contiguous block of T/G tokens).
+ *
+ * moe_expert_capacity -- [host] places per expert in one block of
+ *   n = T / n_groups tokens: ceil(factor * (n * k) / E) in double precision,
+ *   the capacity factor times the block's mean load per expert.  -1 when the
+ *   arguments are invalid (n_groups not dividing T, factor negative or not
+ *   finite); saturates at INT32_MAX.
+ *
+ * moe_capacity -- per-block capacity with dropping.  Inside block r the
+ *   assignments queue for their experts slot-major, as GShard places second
+ *   choices after every first choice: slot 0 of each token in token order,
+ *   then slot 1, and so on.  An assignment is kept when fewer than `capacity`
+ *   assignments of its block are ahead of it in its expert's queue.
+ *   topk_idx [T,k] int32 in (ids outside [0,E) are written -1 and not
+ *   counted); kept_idx [T,k] int32 out: the expert id, or -1 when dropped
+ *   (a buffer of its own: moe_route_bwd_dense needs the original table);
+ *   group_dropped [G] int32 out: dropped assignments per block.  Gates are
+ *   not renormalised after dropping.  Feed kept_idx to moe_permute; the
+ *   combine and its backward skip dropped slots.  capacity >= 0; 1 <= G, G
+ *   divides T.
+ *
+ * moe_router_zloss -- group_z [G] fp32: the mean over block r of lse_t^2,
+ *   lse_t = log sum_e exp logits[t,e].  The z-loss is z_coef times the mean of
+ *   group_z (= the mean over all tokens).  The balancing loss is aux_coef
+ *   times the mean of moe_route's group_aux.
+ *
+ * moe_route_bwd_dense -- the router backward over the dense [T,E] logit
+ *   gradient, for dropped assignments and the auxiliary losses:
+ *     dl[t,e] = sum_{j : topk_idx[t,j] = e} g_j (dg_j - sum_i g_i dg_i)
+ *             + aux_coef * E / (G n) * p[t,e] (f[r,e] - sum_e' f[r,e'] p[t,e'])
+ *             + z_coef * 2 / T * lse_t * p[t,e]
+ *   with p the full softmax of logits[t], f = group_count / (n k) of the
+ *   token's block r (held constant), n = T / G;
+ *     dx[t]  = sum_e dl[t,e] w_router[e] + sum_{j : pos[t,j] >= 0} dx_perm[pos[t,j]]
+ *              (fp32, e ascending then slots in order, rounded once to act;
+ *              the second sum is skipped when dx_perm == NULL),
+ *     dw_router = dl^T x (fp32, tokens in a fixed order).
+ *   topk_idx is the router's selection (before dropping): a dropped slot
+ *   keeps its gate term, since its logit still sets the kept gates; moe_combine_bwd
+ *   gives it dgate 0.  logits [T,E] fp32 from moe_route; group_count [G,E]
+ *   from moe_route (required when aux_coef != 0); pos from moe_permute on the
+ *   kept table; dlogits [T,E] fp32 out, or NULL.  With aux_coef = z_coef = 0
+ *   and nothing dropped the result equals moe_route_bwd's up to summation
+ *   order.  Workspace: moe_workspace_bytes().
+ */
+int32_t moe_expert_capacity(int64_t T, int32_t k, int32_t E, int32_t n_groups, double factor);
+moe_status moe_capacity(const moe_dims* dims, int32_t n_groups, int32_t capacity,
+                        const int32_t* topk_idx, int32_t* kept_idx, int32_t* group_dropped,
+                        void* stream);
+moe_status moe_router_zloss(const moe_dims* dims, const float* logits, int32_t n_groups,
+                            float* group_z, void* stream);
+moe_status moe_route_bwd_dense(const moe_dims* dims, const void* x, const float* w_router,
+                               const float* logits, const int32_t* topk_idx,
+                               const float* topk_gate, const float* dgate, const int32_t* pos,
+                               const void* dx_perm, int32_t n_groups, const int32_t* group_count,
+                               float aux_coef, float z_coef, void* dx, float* dw_router,
+                               float* dlogits, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * moe_coselect -- co-selection counts ([COUPLING] Table III, Fig. 2):

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     alloc_workspace,
     lib,
     make_dims,
+    moe_capacity,
     moe_check_placement,
     moe_combine,
     moe_combine_bwd,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     moe_dispatch_plan,
     moe_expert_dgrad_down,
     moe_expert_dgrad_up,
+    moe_expert_capacity,
     moe_expert_down,
     moe_expert_up,
     moe_expert_up_gather,
@@ -36,6 +38,8 @@ from ._lib import (  # noqa: F401
     moe_placement_greedy,
     moe_route,
     moe_route_bwd,
+    moe_route_bwd_dense,
+    moe_router_zloss,
     workspace_bytes,
 )
 from .layer import MoELayer  # noqa: F401

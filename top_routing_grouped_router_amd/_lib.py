@@ -37,6 +37,7 @@ EXPORTED = (
     "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_wgrad_launches",
     "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
     "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
+    "moe_expert_capacity", "moe_capacity", "moe_router_zloss", "moe_route_bwd_dense",
 )
 
 
@@ -91,6 +92,11 @@ _SIGNATURES = {
     "moe_grouped_swiglu_bwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
+    "moe_expert_capacity": (_I32, [_I64, _I32, _I32, _I32, ctypes.c_double]),
+    "moe_capacity": (_I32, [_DIMS, _I32, _I32, _P, _P, _P, _P]),
+    "moe_router_zloss": (_I32, [_DIMS, _P, _I32, _P, _P]),
+    "moe_route_bwd_dense": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _F32, _F32,
+                                   _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -410,3 +416,42 @@ def moe_dispatch_expand(dims, recv, assign_row, pos, x_perm, stream=None):
                                    _stream(stream))
     _check(st, "moe_dispatch_expand")
 
+
+# ---------------------------------------------------------------- definitional variants
+def moe_expert_capacity(T, k, E, n_groups, factor) -> int:
+    c = int(lib().moe_expert_capacity(int(T), int(k), int(E), int(n_groups), float(factor)))
+    if c < 0:
+        raise MoEError(1, "moe_expert_capacity",
+                       f"invalid arguments T={T} k={k} E={E} n_groups={n_groups} factor={factor}")
+    return c
+
+
+def moe_capacity(dims, n_groups, capacity, topk_idx, kept_idx, group_dropped, stream=None):
+    st = lib().moe_capacity(ctypes.byref(dims), int(n_groups), int(capacity),
+                            _ptr(topk_idx, "topk_idx", torch.int32),
+                            _ptr(kept_idx, "kept_idx", torch.int32),
+                            _ptr(group_dropped, "group_dropped", torch.int32), _stream(stream))
+    _check(st, "moe_capacity")
+
+
+def moe_router_zloss(dims, logits, n_groups, group_z, stream=None):
+    st = lib().moe_router_zloss(ctypes.byref(dims), _ptr(logits, "logits", torch.float32),
+                                int(n_groups), _ptr(group_z, "group_z", torch.float32),
+                                _stream(stream))
+    _check(st, "moe_router_zloss")
+
+
+def moe_route_bwd_dense(dims, x, w_router, logits, topk_idx, topk_gate, dgate, pos, dx_perm,
+                        n_groups, group_count, aux_coef, z_coef, dx, dw_router, dlogits,
+                        workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_route_bwd_dense(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(w_router, "w_router", torch.float32),
+        _ptr(logits, "logits", torch.float32), _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(topk_gate, "topk_gate", torch.float32), _ptr(dgate, "dgate", torch.float32),
+        _ptr(pos, "pos", torch.int32), _ptr(dx_perm, "dx_perm", act), int(n_groups),
+        _ptr(group_count, "group_count", torch.int32), float(aux_coef), float(z_coef),
+        _ptr(dx, "dx", act), _ptr(dw_router, "dw_router", torch.float32),
+        _ptr(dlogits, "dlogits", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_route_bwd_dense")

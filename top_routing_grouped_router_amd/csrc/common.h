@@ -162,6 +162,20 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
                             float* ws_dl_sel, float* ws_partial, hipStream_t s);
 int route_bwd_splits(const moe_dims& dm);   // row splits per expert for the router weight gradient
+// dense form: dropped assignments and the auxiliary losses
+hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float* wr,
+                                  const float* logits, const int32_t* idx, const float* gate,
+                                  const float* dgate, const int32_t* pos, const void* dx_perm,
+                                  int32_t G, const int32_t* count, float aux_coef, float z_coef,
+                                  void* dx, float* dwr, float* dlogits, float* ws_dl,
+                                  float* ws_partial, hipStream_t s);
+int route_bwd_dense_splits(const moe_dims& dm);   // token splits of its weight gradient
+
+// per-block capacity with dropping; per-block mean of logsumexp^2
+hipError_t launch_capacity(int64_t T, int32_t k, int32_t E, int32_t G, int32_t C,
+                           const int32_t* idx, int32_t* kept, int32_t* dropped, hipStream_t s);
+hipError_t launch_router_z(int64_t T, int32_t E, int32_t G, const float* logits, float* group_z,
+                           hipStream_t s);
 
 // index products
 hipError_t launch_coselect(int64_t T, int32_t k, int32_t E, const int32_t* idx, int32_t* W,

@@ -162,6 +162,21 @@ RouteBwdWs route_bwd_ws(const moe_dims& dm, void* ws) {
   return r;
 }
 
+struct RouteBwdDenseWs {
+  float* dl;
+  float* partial;
+  size_t bytes;
+};
+RouteBwdDenseWs route_bwd_dense_ws(const moe_dims& dm, void* ws) {
+  Carver c;
+  RouteBwdDenseWs r;
+  r.dl = c.take<float>(ws, std::max<int64_t>(dm.T * dm.E, 1));
+  r.partial =
+      c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::route_bwd_dense_splits(dm) * dm.d);
+  r.bytes = c.off;
+  return r;
+}
+
 struct PlanWs {
   uint64_t* mask;
   int32_t* hist;
@@ -187,6 +202,7 @@ size_t workspace_needed(const moe_dims& dm, int32_t n_groups) {
   need = std::max(need, perm_ws(dm.T, dm.E, nullptr).bytes);
   need = std::max(need, bwd_ws(dm, nullptr).bytes);
   need = std::max(need, route_bwd_ws(dm, nullptr).bytes);
+  need = std::max(need, route_bwd_dense_ws(dm, nullptr).bytes);
   need = std::max(need, plan_ws(dm.T, std::max(G, 64), nullptr).bytes);
   return need;
 }
@@ -777,6 +793,98 @@ moe_status moe_dispatch_expand(const moe_dims* dims, const void* recv,
   MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
   return hip_status(moe::launch_ep_expand(dm, recv, assign_row, pos, x_perm,
                                           static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+// ---------------------------------------------------------------- definitional variants
+int32_t moe_expert_capacity(int64_t T, int32_t k, int32_t E, int32_t n_groups, double factor) {
+  if (T < 0 || k <= 0 || E <= 0 || n_groups <= 0 || T % n_groups || !std::isfinite(factor) ||
+      factor < 0.0)
+    return -1;
+  const int64_t n = T / n_groups;
+  const double c = std::ceil(factor * static_cast<double>(n * k) / E);
+  return c >= 2147483647.0 ? 2147483647 : static_cast<int32_t>(c);
+}
+
+static moe_status check_groups(const moe_dims& dm, int32_t n_groups, const char* fn) {
+  if (n_groups < 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d must be >= 1", fn, n_groups);
+  if (dm.T % n_groups)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d does not divide T=%lld", fn, n_groups,
+                static_cast<long long>(dm.T));
+  return MOE_OK;
+}
+
+moe_status moe_capacity(const moe_dims* dims, int32_t n_groups, int32_t capacity,
+                        const int32_t* topk_idx, int32_t* kept_idx, int32_t* group_dropped,
+                        void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_groups(dm, n_groups, __func__);
+  if (st != MOE_OK) return st;
+  if (capacity < 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: capacity=%d must be >= 0", __func__, capacity);
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(kept_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(group_dropped, n_groups);
+  return hip_status(moe::launch_capacity(dm.T, dm.k, dm.E, n_groups, capacity, topk_idx, kept_idx,
+                                         group_dropped, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_router_zloss(const moe_dims* dims, const float* logits, int32_t n_groups,
+                            float* group_z, void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_groups(dm, n_groups, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(logits, dm.T * dm.E);
+  MOE_REQUIRE_PTR(group_z, n_groups);
+  return hip_status(moe::launch_router_z(dm.T, dm.E, n_groups, logits, group_z,
+                                         static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_route_bwd_dense(const moe_dims* dims, const void* x, const float* w_router,
+                               const float* logits, const int32_t* topk_idx,
+                               const float* topk_gate, const float* dgate, const int32_t* pos,
+                               const void* dx_perm, int32_t n_groups, const int32_t* group_count,
+                               float aux_coef, float z_coef, void* dx, float* dw_router,
+                               float* dlogits, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_groups(dm, n_groups, __func__);
+  if (st != MOE_OK) return st;
+  if (!std::isfinite(aux_coef) || !std::isfinite(z_coef))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: aux_coef and z_coef must be finite", __func__);
+  MOE_REQUIRE_PTR(x, dm.T * dm.d);
+  MOE_REQUIRE_PTR(w_router, int64_t(dm.E) * dm.d);
+  MOE_REQUIRE_PTR(logits, dm.T * dm.E);
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dgate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_OPTIONAL_PTR(dx_perm);
+  if (aux_coef != 0.f) {
+    MOE_REQUIRE_PTR(group_count, int64_t(n_groups) * dm.E);
+  } else {
+    MOE_OPTIONAL_PTR(group_count);
+  }
+  MOE_REQUIRE_PTR(dx, dm.T * dm.d);
+  MOE_REQUIRE_PTR(dw_router, int64_t(dm.E) * dm.d);
+  MOE_OPTIONAL_PTR(dlogits);
+  const RouteBwdDenseWs need = route_bwd_dense_ws(dm, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const RouteBwdDenseWs w = route_bwd_dense_ws(dm, workspace);
+  return hip_status(moe::launch_route_bwd_dense(dm, x, w_router, logits, topk_idx, topk_gate,
+                                                dgate, pos, dx_perm, n_groups, group_count,
+                                                aux_coef, z_coef, dx, dw_router, dlogits, w.dl,
+                                                w.partial, static_cast<hipStream_t>(stream)),
                     __func__);
 }
 

@@ -210,6 +210,243 @@ __global__ __launch_bounds__(kThreads) void router_dwr_reduce_kernel(
   }
 }
 
+// ---------------------------------------------------------------- dense form
+// With dropped assignments (capacity) or the auxiliary losses the logit
+// gradient is no longer confined to the k chosen experts of a token that have
+// a permuted row, so the dense form is used:
+//   dl[t,e] = sum_{j : S_j(t) = e} g_j (dg_j - sum_i g_i dg_i)
+//           + aux_scale p[t,e] (f[r,e] - sum_e' f[r,e'] p[t,e'])   (GShard balancing)
+//           + z_scale lse_t p[t,e]                                  (ST-MoE z-loss)
+// with p the full softmax, f = count / (n k) of the token's block r, and
+//   dX[t] = sum_e dl[t,e] Wr[e] + sum_{j : pos >= 0} dx_perm[pos[t,j]],
+//   dWr   = dl^T X.
+// Dropped slots keep their gate term: the dropped expert's logit still sets
+// the renormalised gates of the kept ones.
+
+// One wavefront per token; lane l holds experts l, l + 64, ...  Wavefront
+// sums and maxima are xor butterflies, which leave the same bits in every lane.
+template <int EPL>
+__global__ __launch_bounds__(kThreads) void router_dl_dense_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gate, const float* __restrict__ dgate,
+    const int32_t* __restrict__ count, int32_t n, float f_scale, float aux_scale, float z_scale,
+    float* __restrict__ dl, float* __restrict__ dl_out, int64_t T, int32_t k, int32_t E) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;   // wavefront-uniform; no workgroup barrier below
+  float l[EPL], p[EPL], dv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    l[i] = (e < E) ? logits[t * E + e] : -INFINITY;
+    dv[i] = 0.f;
+  }
+  float m = l[0];
+#pragma unroll
+  for (int i = 1; i < EPL; ++i) m = fmaxf(m, l[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    p[i] = (lane + 64 * i < E) ? __expf(l[i] - m) : 0.f;
+    s += p[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+  const float inv = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) p[i] *= inv;
+  if (aux_scale != 0.f) {
+    const int32_t* cr = count + (t / n) * E;
+    float f[EPL];
+    float fp = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      f[i] = (e < E) ? static_cast<float>(cr[e]) * f_scale : 0.f;
+      fp = fmaf(f[i], p[i], fp);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) fp += __shfl_xor(fp, off, 64);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) dv[i] = aux_scale * p[i] * (f[i] - fp);
+  }
+  if (z_scale != 0.f) {
+    const float zl = z_scale * (m + __logf(s));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) dv[i] = fmaf(zl, p[i], dv[i]);
+  }
+  float inner = 0.f;
+  for (int j = 0; j < k; ++j) inner = fmaf(gate[t * k + j], dgate[t * k + j], inner);
+  for (int j = 0; j < k; ++j) {
+    const int32_t e = idx[t * k + j];
+    if (e < 0 || e >= E || (e & 63) != lane) continue;
+    const float v = gate[t * k + j] * (dgate[t * k + j] - inner);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if ((e >> 6) == i) dv[i] += v;
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e >= E) continue;
+    dl[t * E + e] = dv[i];
+    if (dl_out) dl_out[t * E + e] = dv[i];
+  }
+}
+
+__device__ __forceinline__ void store4(float* p, const float* v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store4(bf16_t* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+}
+
+// dX rows of the dense form: a wavefront computes kDxTok tokens x 256 columns
+// (4 per lane).  Its kDxTok x E block of dl is staged in LDS as [e][token],
+// so one broadcast read gives four tokens' weights of expert e; Wr rows come
+// from L2.  Per element: sum_e dl[t,e] Wr[e] (e ascending), then the kept
+// dx_perm rows in slot order, in fp32, rounded once.
+// K is the compile-time k (0: runtime k <= 16).
+constexpr int kDxTok = 16;
+template <typename TA, int K>
+__global__ __launch_bounds__(kThreads) void router_dx_dense_kernel(
+    const TA* __restrict__ dxp, const int32_t* __restrict__ pos, const float* __restrict__ dl,
+    const float* __restrict__ wr, TA* __restrict__ dx, int64_t T, int32_t d, int32_t k,
+    int32_t E) {
+  constexpr int KM = K > 0 ? K : 16;
+  constexpr int UT = (16 / KM) > 0 ? 16 / KM : 1;   // tokens whose rows are loaded together
+  static_assert(kDxTok % UT == 0, "token groups must tile the wavefront's tokens");
+  const int kk = K > 0 ? K : k;
+  extern __shared__ float sdl[];   // [4 waves][E][kDxTok]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ncb = (d + 255) / 256;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + w;
+  const int64_t t0 = (wid / ncb) * kDxTok;
+  const int cb = static_cast<int>(wid % ncb);
+  float* my = sdl + static_cast<int64_t>(w) * E * kDxTok;
+  for (int i = lane; i < kDxTok * E; i += 64) {
+    const int tl = i / E, e = i - tl * E;
+    my[e * kDxTok + tl] = (t0 + tl < T) ? dl[(t0 + tl) * E + e] : 0.f;
+  }
+  __syncthreads();
+  const int col = cb * 256 + lane * 4;
+  if (t0 >= T || col >= d) return;
+  float acc[kDxTok][4];
+#pragma unroll
+  for (int u = 0; u < kDxTok; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[u][i] = 0.f;
+  for (int e = 0; e < E; ++e) {
+    const float4 wv = *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * d + col);
+    const float4* dq = reinterpret_cast<const float4*>(my + e * kDxTok);
+#pragma unroll
+    for (int q = 0; q < kDxTok / 4; ++q) {
+      const float4 g = dq[q];
+      const float gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[4 * q + u][0] = fmaf(gg[u], wv.x, acc[4 * q + u][0]);
+        acc[4 * q + u][1] = fmaf(gg[u], wv.y, acc[4 * q + u][1]);
+        acc[4 * q + u][2] = fmaf(gg[u], wv.z, acc[4 * q + u][2]);
+        acc[4 * q + u][3] = fmaf(gg[u], wv.w, acc[4 * q + u][3]);
+      }
+    }
+  }
+  // kept expert rows in slot order; 16 / k tokens' loads in flight at a time
+  if (dxp) {
+#pragma unroll
+    for (int u0 = 0; u0 < kDxTok; u0 += UT) {
+      int32_t pp[UT][KM];
+      float v[UT][KM][4];
+#pragma unroll
+      for (int u = 0; u < UT; ++u) {
+        const int64_t t = min<int64_t>(t0 + u0 + u, T - 1);
+#pragma unroll
+        for (int j = 0; j < KM; ++j) pp[u][j] = pos[t * kk + min(j, kk - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < UT; ++u)
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          load4(dxp + static_cast<int64_t>(max(pp[u][j], 0)) * d + col, v[u][j]);
+#pragma unroll
+      for (int u = 0; u < UT; ++u)
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          if (j >= kk || pp[u][j] < 0) continue;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u0 + u][i] += v[u][j][i];
+        }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kDxTok; ++u)
+    if (t0 + u < T) store4(dx + (t0 + u) * d + col, acc[u]);
+}
+
+// dWr partial sums of the dense form: partial[e][sp][c] = sum over the
+// tokens of split sp of dl[t,e] x[t,c].  Workgroup (256-column block, block of
+// kDwEB experts, split sp): wavefront w takes tokens lo + w, lo + w + 4, ...
+// in order, four at a time in flight; the four wavefronts are added in order
+// through LDS, and router_dwr_reduce_kernel adds the splits in order.
+constexpr int kDwEB = 16;
+template <typename TA>
+__global__ __launch_bounds__(kThreads) void router_dwr_dense_partial_kernel(
+    const TA* __restrict__ x, const float* __restrict__ dl, float* __restrict__ partial,
+    int64_t T, int32_t d, int32_t E, int32_t splits) {
+  __shared__ float red[4][8][256];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int cb = blockIdx.x, e0 = blockIdx.y * kDwEB, sp = blockIdx.z;
+  const int col = cb * 256 + lane * 4;
+  const bool cok = col < d;
+  const int64_t lo = (T * sp) / splits, hi = (T * (sp + 1)) / splits;
+  float acc[kDwEB][4];
+#pragma unroll
+  for (int e = 0; e < kDwEB; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
+  constexpr int U = 4;
+  for (int64_t t = lo + w; t < hi; t += 4 * U) {
+    float xv[U][4];
+    float g[U][kDwEB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tt = t + 4 * u;
+      const int64_t tc = min<int64_t>(tt, hi - 1);
+      if (cok) load4(x + tc * d + col, xv[u]);
+      else xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
+#pragma unroll
+      for (int e = 0; e < kDwEB; ++e)
+        g[u][e] = (tt < hi && e0 + e < E) ? dl[tc * E + min(e0 + e, E - 1)] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < kDwEB; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(g[u][e], xv[u][i], acc[e][i]);
+  }
+#pragma unroll
+  for (int ec = 0; ec < kDwEB; ec += 8) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[w][e][lane * 4 + i] = acc[ec + e][i];
+    __syncthreads();
+    for (int v = threadIdx.x; v < 8 * 256; v += kThreads) {
+      const int e = v / 256, c = v % 256;
+      const int ee = e0 + ec + e, cc = cb * 256 + c;
+      if (ee < E && cc < d)
+        partial[(static_cast<int64_t>(ee) * splits + sp) * d + cc] =
+            ((red[0][e][c] + red[1][e][c]) + red[2][e][c]) + red[3][e][c];
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 // row splits per expert for the router weight gradient: about 2048 workgroups
@@ -265,6 +502,72 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     hipLaunchKernelGGL(router_dwr_partial_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d,
                        splits);
+  hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads), 0,
+                     s, ws_partial, dwr, dm.E, dm.d, splits);
+  return hipGetLastError();
+}
+
+// splits over tokens for the dense router weight gradient: about 2048 workgroups
+int route_bwd_dense_splits(const moe_dims& dm) {
+  const int64_t base = static_cast<int64_t>((dm.d + 255) / 256) * ((dm.E + kDwEB - 1) / kDwEB);
+  const int64_t s = (2048 + base - 1) / base;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+}
+
+hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float* wr,
+                                  const float* logits, const int32_t* idx, const float* gate,
+                                  const float* dgate, const int32_t* pos, const void* dx_perm,
+                                  int32_t G, const int32_t* count, float aux_coef, float z_coef,
+                                  void* dx, float* dwr, float* dlogits, float* ws_dl,
+                                  float* ws_partial, hipStream_t s) {
+  if (dm.T > 0) {
+    const int64_t n = dm.T / std::max(G, 1);
+    const float f_scale = static_cast<float>(1.0 / (static_cast<double>(n) * dm.k));
+    const float aux_scale =
+        static_cast<float>(aux_coef * static_cast<double>(dm.E) / (static_cast<double>(G) * n));
+    const float z_scale = static_cast<float>(z_coef * 2.0 / static_cast<double>(dm.T));
+    const dim3 g1((dm.T + 3) / 4);
+#define MOE_DL(EPL)                                                                            \
+  hipLaunchKernelGGL((router_dl_dense_kernel<EPL>), g1, dim3(kThreads), 0, s, logits, idx, gate, \
+                     dgate, count, static_cast<int32_t>(n), f_scale, aux_scale, z_scale, ws_dl,  \
+                     dlogits, dm.T, dm.k, dm.E)
+    if (dm.E <= 64) MOE_DL(1);
+    else if (dm.E <= 128) MOE_DL(2);
+    else MOE_DL(4);
+#undef MOE_DL
+    const int ncb = (dm.d + 255) / 256;
+    const int64_t waves = ((dm.T + kDxTok - 1) / kDxTok) * ncb;
+    const dim3 g2((waves + 3) / 4);
+    const size_t lds = static_cast<size_t>(4) * dm.E * kDxTok * sizeof(float);
+#define MOE_DXD(TA, KC)                                                                       \
+  hipLaunchKernelGGL((router_dx_dense_kernel<TA, KC>), g2, dim3(kThreads), lds, s,             \
+                     static_cast<const TA*>(dx_perm), pos, ws_dl, wr, static_cast<TA*>(dx),  \
+                     dm.T, dm.d, dm.k, dm.E)
+#define MOE_DXD_K(TA)                  \
+  switch (dm.k) {                      \
+    case 1: MOE_DXD(TA, 1); break;     \
+    case 2: MOE_DXD(TA, 2); break;     \
+    case 4: MOE_DXD(TA, 4); break;     \
+    case 6: MOE_DXD(TA, 6); break;     \
+    case 8: MOE_DXD(TA, 8); break;     \
+    default: MOE_DXD(TA, 0); break;    \
+  }
+    if (dm.act == MOE_BF16) {
+      MOE_DXD_K(bf16_t)
+    } else {
+      MOE_DXD_K(float)
+    }
+#undef MOE_DXD_K
+#undef MOE_DXD
+  }
+  const int splits = route_bwd_dense_splits(dm);
+  const dim3 g3((dm.d + 255) / 256, (dm.E + kDwEB - 1) / kDwEB, splits);
+  if (dm.act == MOE_BF16)
+    hipLaunchKernelGGL(router_dwr_dense_partial_kernel<bf16_t>, g3, dim3(kThreads), 0, s,
+                       static_cast<const bf16_t*>(x), ws_dl, ws_partial, dm.T, dm.d, dm.E, splits);
+  else
+    hipLaunchKernelGGL(router_dwr_dense_partial_kernel<float>, g3, dim3(kThreads), 0, s,
+                       static_cast<const float*>(x), ws_dl, ws_partial, dm.T, dm.d, dm.E, splits);
   hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads), 0,
                      s, ws_partial, dwr, dm.E, dm.d, splits);
   return hipGetLastError();

@@ -10,6 +10,12 @@ reused by each call, so a step enqueues kernels only.  The sequence is:
 gather=True the permutation is a plan only and the expert GEMMs read their
 input rows from X through src_token (moe_grouped_swiglu_fwd_gather /
 bwd_gather), so x_perm is never materialised; the results are identical.
+
+Definitional variants: capacity_factor enables per-block expert capacity
+(moe_capacity between the router and the permutation: dropped assignments get
+no row), and aux_coef / z_coef add the balancing and z-loss gradients.  Either
+switches the router backward to moe_route_bwd_dense; z_coef also computes the
+per-block z-loss values (moe_router_zloss) in the forward.
 """
 from __future__ import annotations
 
@@ -21,10 +27,16 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, f: int, k: int, act: torch.dtype,
                  n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda",
-                 gather: bool = False):
+                 gather: bool = False, capacity_factor=None, aux_coef: float = 0.0,
+                 z_coef: float = 0.0):
         self.dims = L.make_dims(T, d, E, f, k, act)
         self.act = act
         self.gather = gather
+        self.capacity = (None if capacity_factor is None else
+                         L.moe_expert_capacity(T, k, E, n_groups, capacity_factor))
+        self.aux_coef = float(aux_coef)
+        self.z_coef = float(z_coef)
+        self.dense_bwd = self.capacity is not None or self.aux_coef != 0.0 or self.z_coef != 0.0
         self.n_groups = n_groups
         self.eps = near_tie_eps
         R = T * k
@@ -64,6 +76,10 @@ class MoELayer:
         self.dw2 = empty(E, d, f, **ea)
         self.dx = empty(T, d, **ea)
         self.dwr = empty(E, d, **e32)
+        self.kept_idx = empty(T, k, **i32) if self.capacity is not None else None
+        self.group_dropped = empty(n_groups, **i32) if self.capacity is not None else None
+        self.group_z = empty(n_groups, **e32) if self.z_coef != 0.0 else None
+        self.dlogits = empty(T, E, **e32) if self.dense_bwd else None
         self.workspace = L.alloc_workspace(self.dims, n_groups, dev)
 
     # ------------------------------------------------------------------ forward
@@ -73,13 +89,20 @@ class MoELayer:
                     self.group_mean_prob, self.group_aux, self.workspace)
 
     def forward_experts(self, x, w1, w3, w2):
+        table = self.topk_idx
+        if self.capacity is not None:
+            L.moe_capacity(self.dims, self.n_groups, self.capacity, self.topk_idx, self.kept_idx,
+                           self.group_dropped)
+            table = self.kept_idx
+        if self.z_coef != 0.0:
+            L.moe_router_zloss(self.dims, self.logits, self.n_groups, self.group_z)
         if self.gather:
-            L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
+            L.moe_permute(self.dims, table, self.expert_counts, self.expert_offsets,
                           self.pos, self.src_token, None, None, self.workspace)
             L.moe_grouped_swiglu_fwd_gather(self.dims, x, self.src_token, self.expert_offsets,
                                             w1, w3, w2, self.a, self.b, self.h, self.y_perm)
         else:
-            L.moe_permute(self.dims, self.topk_idx, self.expert_counts, self.expert_offsets,
+            L.moe_permute(self.dims, table, self.expert_counts, self.expert_offsets,
                           self.pos, self.src_token, x, self.x_perm, self.workspace)
             L.moe_grouped_swiglu_fwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
                                      self.a, self.b, self.h, self.y_perm)
@@ -109,9 +132,15 @@ class MoELayer:
             L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
                                      self.a, self.b, self.h, self.dy_perm, self.dx_perm,
                                      self.dw1, self.dw3, self.dw2, self.workspace)
-        L.moe_route_bwd(self.dims, x, wr, self.topk_idx, self.topk_gate, self.dgate,
-                        self.expert_offsets, self.pos, self.src_token, self.dx_perm, self.dx,
-                        self.dwr, self.workspace)
+        if self.dense_bwd:
+            L.moe_route_bwd_dense(self.dims, x, wr, self.logits, self.topk_idx, self.topk_gate,
+                                  self.dgate, self.pos, self.dx_perm, self.n_groups,
+                                  self.group_count, self.aux_coef, self.z_coef, self.dx,
+                                  self.dwr, self.dlogits, self.workspace)
+        else:
+            L.moe_route_bwd(self.dims, x, wr, self.topk_idx, self.topk_gate, self.dgate,
+                            self.expert_offsets, self.pos, self.src_token, self.dx_perm, self.dx,
+                            self.dwr, self.workspace)
         return self.dx
 
     def step(self, x, wr, w1, w3, w2, dy):
