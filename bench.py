@@ -37,11 +37,12 @@ PEAK_HBM = 8.0e12          # bytes/s
 PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix peaks (fp32: vector/matrix fp32)
 
 
-def algorithmic_work(cfg):
+def algorithmic_work(cfg, R=None):
     """Per-call algorithmic (flops, bytes, kernels): what each call must compute
-    and move by its C-ABI contract (inputs read once, outputs written once)."""
+    and move by its C-ABI contract (inputs read once, outputs written once).
+    R: expert rows (T k, or fewer when a capacity drops assignments)."""
     T, d, E, f, k = cfg.T, cfg.d, cfg.E, cfg.f, cfg.k
-    R = T * k
+    R = T * k if R is None else R
     s = 2 if cfg.act == "bf16" else 4
     i4 = 4
     Wf = E * d * f * s          # one of W1, W3, W2
@@ -63,6 +64,11 @@ def algorithmic_work(cfg):
                                     None),
         "moe_route_bwd": (4 * R * d, T * d * s + E * d * 4 + R * d * s + T * d * s + E * d * 4
                           + T * k * 12 + R * 8, 4),
+        # definitional variants
+        "moe_capacity": (0, 2 * T * k * i4, 1),
+        "moe_router_zloss": (3 * T * E, T * E * 4, 1),
+        "moe_route_bwd_dense": (4 * T * E * d, T * d * s + E * d * 4 + T * E * 8 + T * k * 16
+                                + R * d * s + T * d * s + E * d * 4, 4),
     }
 
 
@@ -234,6 +240,13 @@ def main():
                     help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
                          "expand) for the workload's placement group counts; adds an "
                          "'ep_dispatch' object to the JSON line")
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="definitional variant: per-block expert capacity with dropping "
+                         "(moe_capacity before the permutation, moe_route_bwd_dense after)")
+    ap.add_argument("--aux-coef", type=float, default=0.0,
+                    help="definitional variant: GShard balancing-loss gradient coefficient")
+    ap.add_argument("--z-coef", type=float, default=0.0,
+                    help="definitional variant: router z-loss coefficient (values and gradient)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a "
                          "known-size kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -262,20 +275,28 @@ def main():
     w1, w3, w2 = up(inp["w1"], act), up(inp["w3"], act), up(inp["w2"], act)
     G = max(cfg.lb_groups)
     gather = not args.no_gather
-    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=gather)
+    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=gather,
+                     capacity_factor=args.capacity_factor, aux_coef=args.aux_coef,
+                     z_coef=args.z_coef)
     dm = layer.dims
+    table = layer.kept_idx if layer.capacity is not None else layer.topk_idx
 
     da = torch.empty_like(layer.a)
     db = torch.empty_like(layer.b)
     calls = [
         ("moe_route", lambda: layer.route(x, wr)),
-        ("moe_permute", lambda: L.moe_permute(dm, layer.topk_idx, layer.expert_counts,
+        ("moe_capacity", lambda: L.moe_capacity(dm, G, layer.capacity, layer.topk_idx,
+                                                layer.kept_idx, layer.group_dropped,
+                                                layer.workspace)),
+        ("moe_router_zloss", lambda: L.moe_router_zloss(dm, layer.logits, G, layer.group_z,
+                                                        layer.workspace)),
+        ("moe_permute", lambda: L.moe_permute(dm, table, layer.expert_counts,
                                               layer.expert_offsets, layer.pos, layer.src_token,
                                               x, layer.x_perm, layer.workspace)),
         ("moe_expert_up", lambda: L.moe_expert_up(dm, layer.x_perm, layer.expert_offsets, w1, w3,
                                                   layer.a, layer.b, layer.h)),
         # gathered expert input: the same two steps without x_perm
-        ("moe_permute_plan", lambda: L.moe_permute(dm, layer.topk_idx, layer.expert_counts,
+        ("moe_permute_plan", lambda: L.moe_permute(dm, table, layer.expert_counts,
                                                    layer.expert_offsets, layer.pos,
                                                    layer.src_token, None, None,
                                                    layer.workspace)),
@@ -302,12 +323,21 @@ def main():
                                                   layer.dgate, layer.expert_offsets, layer.pos,
                                                   layer.src_token, layer.dx_perm, layer.dx,
                                                   layer.dwr, layer.workspace)),
+        ("moe_route_bwd_dense", lambda: L.moe_route_bwd_dense(
+            dm, x, wr, layer.logits, layer.topk_idx, layer.topk_gate, layer.dgate, layer.pos,
+            layer.dx_perm, G, layer.group_count, layer.aux_coef, layer.z_coef, layer.dx,
+            layer.dwr, None, layer.workspace)),
     ]
     drop = (("moe_permute", "moe_expert_up", "moe_expert_wgrad") if gather else
             ("moe_permute_plan", "moe_expert_up_gather", "moe_expert_wgrad_gather"))
+    drop += ("moe_route_bwd",) if layer.dense_bwd else ("moe_route_bwd_dense",)
+    if layer.capacity is None:
+        drop += ("moe_capacity",)
+    if layer.z_coef == 0.0:
+        drop += ("moe_router_zloss",)
     calls = [c for c in calls if c[0] not in drop]
     if not cfg.backward:
-        calls = calls[:5]
+        calls = calls[:[c[0] for c in calls].index("moe_combine") + 1]
 
     if args.copy_calibration_mb > 0:
         nbytes = args.copy_calibration_mb << 20
@@ -352,7 +382,8 @@ def main():
                                      for s in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
 
-    work = algorithmic_work(cfg)
+    rows = int(layer.expert_offsets[cfg.E].item())   # expert rows (fewer when dropping)
+    work = algorithmic_work(cfg, rows)
     # the dominant single-kernel call carries the roofline
     single = {n: t for n, t in per_call.items() if work[n][2] == 1 or
               (n in WGRAD_CALLS and wgrad_kernels(dm) == 1)}
@@ -388,6 +419,12 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": roof,
     }
+    if layer.dense_bwd:
+        out["config"]["variant"] = {
+            "capacity_factor": args.capacity_factor, "capacity": layer.capacity,
+            "aux_coef": layer.aux_coef, "z_coef": layer.z_coef, "expert_rows": rows,
+            "dropped": (int(layer.group_dropped.sum().item())
+                        if layer.group_dropped is not None else 0)}
     if args.ep and cfg.plan_groups:
         out["ep_dispatch"] = ep_dispatch(cfg, layer, x, args.steps)
     if not args.no_cpu_baseline:

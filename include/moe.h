@@ -349,9 +349,9 @@ moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_rou
  *             + z_coef * 2 / T * lse_t * p[t,e]
  *   with p the full softmax of logits[t], f = group_count / (n k) of the
  *   token's block r (held constant), n = T / G;
- *     dx[t]  = sum_e dl[t,e] w_router[e] + sum_{j : pos[t,j] >= 0} dx_perm[pos[t,j]]
- *              (fp32, e ascending then slots in order, rounded once to act;
- *              the second sum is skipped when dx_perm == NULL),
+ *     dx[t]  = sum_{j : pos[t,j] >= 0} dx_perm[pos[t,j]] + sum_e dl[t,e] w_router[e]
+ *              (fp32, slots in order then e ascending, rounded once to act;
+ *              the first sum is skipped when dx_perm == NULL),
  *     dw_router = dl^T x (fp32, tokens in a fixed order).
  *   topk_idx is the router's selection (before dropping): a dropped slot
  *   keeps its gate term, since its logit still sets the kept gates; moe_combine_bwd
@@ -359,14 +359,17 @@ moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_rou
  *   from moe_route (required when aux_coef != 0); pos from moe_permute on the
  *   kept table; dlogits [T,E] fp32 out, or NULL.  With aux_coef = z_coef = 0
  *   and nothing dropped the result equals moe_route_bwd's up to summation
- *   order.  Workspace: moe_workspace_bytes().
+ *   order.
+ * moe_capacity, moe_router_zloss and moe_route_bwd_dense take a workspace of
+ * moe_workspace_bytes(dims, n_groups) bytes or more.
  */
 int32_t moe_expert_capacity(int64_t T, int32_t k, int32_t E, int32_t n_groups, double factor);
 moe_status moe_capacity(const moe_dims* dims, int32_t n_groups, int32_t capacity,
                         const int32_t* topk_idx, int32_t* kept_idx, int32_t* group_dropped,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 moe_status moe_router_zloss(const moe_dims* dims, const float* logits, int32_t n_groups,
-                            float* group_z, void* stream);
+                            float* group_z, void* workspace, size_t workspace_bytes,
+                            void* stream);
 moe_status moe_route_bwd_dense(const moe_dims* dims, const void* x, const float* w_router,
                                const float* logits, const int32_t* topk_idx,
                                const float* topk_gate, const float* dgate, const int32_t* pos,

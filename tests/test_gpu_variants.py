@@ -59,7 +59,7 @@ def test_capacity_kernel_bit_exact(case):
     dims = M.make_dims(T, 64, E, 64, k, torch.bfloat16)
     kept = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
     dropped = torch.full((G,), -7, dtype=torch.int32, device="cuda")
-    M.moe_capacity(dims, G, C, dev(idx, torch.int32), kept, dropped)
+    M.moe_capacity(dims, G, C, dev(idx, torch.int32), kept, dropped, M.alloc_workspace(dims, G))
     torch.cuda.synchronize()
     assert np.array_equal(host(kept), ref["kept_idx"])
     assert np.array_equal(host(dropped), ref["dropped"])
@@ -77,14 +77,14 @@ def test_capacity_then_permute_skips_dropped():
     dims = M.make_dims(T, 128, E, 64, k, torch.bfloat16)
     kept = torch.empty((T, k), dtype=torch.int32, device="cuda")
     dropped = torch.empty((G,), dtype=torch.int32, device="cuda")
-    M.moe_capacity(dims, G, C, dev(idx, torch.int32), kept, dropped)
+    ws = M.alloc_workspace(dims, G)
+    M.moe_capacity(dims, G, C, dev(idx, torch.int32), kept, dropped, ws)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     pos = torch.empty((T, k), dtype=torch.int32, device="cuda")
     src = torch.full((T * k,), -1, dtype=torch.int32, device="cuda")
     x = dev(stream(5, 1).standard_normal((T, 128)).astype(np.float32), torch.bfloat16)
     x_perm = torch.zeros((T * k, 128), dtype=torch.bfloat16, device="cuda")
-    ws = M.alloc_workspace(dims, G)
     M.moe_permute(dims, kept, counts, offsets, pos, src, x, x_perm, ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(counts), plan["counts"])
@@ -99,10 +99,13 @@ def test_capacity_rejects_bad_arguments():
     idx = torch.zeros((64, 2), dtype=torch.int32, device="cuda")
     kept = torch.empty_like(idx)
     dropped = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = M.alloc_workspace(dims, 4)
     with pytest.raises(M.MoEError):
-        M.moe_capacity(dims, 3, 4, idx, kept, dropped)      # 3 does not divide 64
+        M.moe_capacity(dims, 3, 4, idx, kept, dropped, ws)      # 3 does not divide 64
     with pytest.raises(M.MoEError):
-        M.moe_capacity(dims, 4, -1, idx, kept, dropped)     # negative capacity
+        M.moe_capacity(dims, 4, -1, idx, kept, dropped, ws)     # negative capacity
+    with pytest.raises(M.MoEError):
+        M.moe_capacity(dims, 4, 4, idx, kept, dropped, ws[:8])  # workspace too small
     with pytest.raises(M.MoEError):
         M.moe_expert_capacity(64, 2, 8, 3, 1.0)
     with pytest.raises(M.MoEError):
@@ -118,7 +121,7 @@ def test_router_zloss_values(T, E, G):
     dims = M.make_dims(T, 64, E, 64, 1, torch.float32)
     gz = torch.full((G,), float("nan"), dtype=torch.float32, device="cuda")
     lg = dev(logits, torch.float32) if T else torch.empty((1, E), device="cuda")[:0]
-    M.moe_router_zloss(dims, lg, G, gz)
+    M.moe_router_zloss(dims, lg, G, gz, M.alloc_workspace(dims, G))
     torch.cuda.synchronize()
     if T == 0:
         assert np.all(host(gz) == 0.0)

@@ -93,8 +93,8 @@ _SIGNATURES = {
                                              _P, _P, _P, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
     "moe_expert_capacity": (_I32, [_I64, _I32, _I32, _I32, ctypes.c_double]),
-    "moe_capacity": (_I32, [_DIMS, _I32, _I32, _P, _P, _P, _P]),
-    "moe_router_zloss": (_I32, [_DIMS, _P, _I32, _P, _P]),
+    "moe_capacity": (_I32, [_DIMS, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_router_zloss": (_I32, [_DIMS, _P, _I32, _P, _P, _SZ, _P]),
     "moe_route_bwd_dense": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _F32, _F32,
                                    _P, _P, _P, _P, _SZ, _P]),
 }
@@ -426,18 +426,22 @@ def moe_expert_capacity(T, k, E, n_groups, factor) -> int:
     return c
 
 
-def moe_capacity(dims, n_groups, capacity, topk_idx, kept_idx, group_dropped, stream=None):
+def moe_capacity(dims, n_groups, capacity, topk_idx, kept_idx, group_dropped, workspace,
+                 stream=None):
     st = lib().moe_capacity(ctypes.byref(dims), int(n_groups), int(capacity),
                             _ptr(topk_idx, "topk_idx", torch.int32),
                             _ptr(kept_idx, "kept_idx", torch.int32),
-                            _ptr(group_dropped, "group_dropped", torch.int32), _stream(stream))
+                            _ptr(group_dropped, "group_dropped", torch.int32),
+                            _ptr(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_capacity")
 
 
-def moe_router_zloss(dims, logits, n_groups, group_z, stream=None):
+def moe_router_zloss(dims, logits, n_groups, group_z, workspace, stream=None):
     st = lib().moe_router_zloss(ctypes.byref(dims), _ptr(logits, "logits", torch.float32),
                                 int(n_groups), _ptr(group_z, "group_z", torch.float32),
-                                _stream(stream))
+                                _ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_router_zloss")
 
 

@@ -173,9 +173,12 @@ int route_bwd_dense_splits(const moe_dims& dm);   // token splits of its weight 
 
 // per-block capacity with dropping; per-block mean of logsumexp^2
 hipError_t launch_capacity(int64_t T, int32_t k, int32_t E, int32_t G, int32_t C,
-                           const int32_t* idx, int32_t* kept, int32_t* dropped, hipStream_t s);
-hipError_t launch_router_z(int64_t T, int32_t E, int32_t G, const float* logits, float* group_z,
+                           const int32_t* idx, int32_t* kept, int32_t* dropped, int32_t* ws_hist,
                            hipStream_t s);
+int capacity_chunks(int64_t T, int32_t G);   // token chunks per block (workspace: G chunks k E ints)
+hipError_t launch_router_z(int64_t T, int32_t E, int32_t G, const float* logits, float* group_z,
+                           float* ws_partial, hipStream_t s);
+int zloss_chunks(int64_t T, int32_t G);      // token chunks per block (workspace: G chunks floats)
 
 // index products
 hipError_t launch_coselect(int64_t T, int32_t k, int32_t E, const int32_t* idx, int32_t* W,

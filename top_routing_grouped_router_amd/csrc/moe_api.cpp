@@ -170,9 +170,24 @@ struct RouteBwdDenseWs {
 RouteBwdDenseWs route_bwd_dense_ws(const moe_dims& dm, void* ws) {
   Carver c;
   RouteBwdDenseWs r;
-  r.dl = c.take<float>(ws, std::max<int64_t>(dm.T * dm.E, 1));
+  r.dl = c.take<float>(ws, dm.T * dm.E + 16);   // + the dWr kernel's read-ahead pad
   r.partial =
       c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::route_bwd_dense_splits(dm) * dm.d);
+  r.bytes = c.off;
+  return r;
+}
+
+struct VariantWs {
+  int32_t* hist;
+  float* zpart;
+  size_t bytes;
+};
+VariantWs variant_ws(const moe_dims& dm, int32_t G, void* ws) {
+  Carver c;
+  VariantWs r;
+  const int32_t g = std::max(G, 1);
+  r.hist = c.take<int32_t>(ws, static_cast<int64_t>(g) * moe::capacity_chunks(dm.T, g) * dm.k * dm.E);
+  r.zpart = c.take<float>(ws, static_cast<int64_t>(g) * moe::zloss_chunks(dm.T, g));
   r.bytes = c.off;
   return r;
 }
@@ -203,6 +218,7 @@ size_t workspace_needed(const moe_dims& dm, int32_t n_groups) {
   need = std::max(need, bwd_ws(dm, nullptr).bytes);
   need = std::max(need, route_bwd_ws(dm, nullptr).bytes);
   need = std::max(need, route_bwd_dense_ws(dm, nullptr).bytes);
+  need = std::max(need, variant_ws(dm, G, nullptr).bytes);
   need = std::max(need, plan_ws(dm.T, std::max(G, 64), nullptr).bytes);
   return need;
 }
@@ -817,7 +833,7 @@ static moe_status check_groups(const moe_dims& dm, int32_t n_groups, const char*
 
 moe_status moe_capacity(const moe_dims* dims, int32_t n_groups, int32_t capacity,
                         const int32_t* topk_idx, int32_t* kept_idx, int32_t* group_dropped,
-                        void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream) {
   moe_status st = check_dims(dims, __func__);
   if (st != MOE_OK) return st;
   const moe_dims& dm = *dims;
@@ -828,13 +844,18 @@ moe_status moe_capacity(const moe_dims* dims, int32_t n_groups, int32_t capacity
   MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
   MOE_REQUIRE_PTR(kept_idx, dm.T * dm.k);
   MOE_REQUIRE_PTR(group_dropped, n_groups);
+  const VariantWs need = variant_ws(dm, n_groups, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const VariantWs w = variant_ws(dm, n_groups, workspace);
   return hip_status(moe::launch_capacity(dm.T, dm.k, dm.E, n_groups, capacity, topk_idx, kept_idx,
-                                         group_dropped, static_cast<hipStream_t>(stream)),
+                                         group_dropped, w.hist, static_cast<hipStream_t>(stream)),
                     __func__);
 }
 
 moe_status moe_router_zloss(const moe_dims* dims, const float* logits, int32_t n_groups,
-                            float* group_z, void* stream) {
+                            float* group_z, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   moe_status st = check_dims(dims, __func__);
   if (st != MOE_OK) return st;
   const moe_dims& dm = *dims;
@@ -842,7 +863,11 @@ moe_status moe_router_zloss(const moe_dims* dims, const float* logits, int32_t n
   if (st != MOE_OK) return st;
   MOE_REQUIRE_PTR(logits, dm.T * dm.E);
   MOE_REQUIRE_PTR(group_z, n_groups);
-  return hip_status(moe::launch_router_z(dm.T, dm.E, n_groups, logits, group_z,
+  const VariantWs need = variant_ws(dm, n_groups, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const VariantWs w = variant_ws(dm, n_groups, workspace);
+  return hip_status(moe::launch_router_z(dm.T, dm.E, n_groups, logits, group_z, w.zpart,
                                          static_cast<hipStream_t>(stream)),
                     __func__);
 }

@@ -175,6 +175,7 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
 // splits sl, sl + 16, ... in order (all loads issued first), then thread
 // group sl = 0 adds the 16 lane sums in order: a fixed summation order, so
 // the result is reproducible, and one memory latency per thread.
+template <int kMaxPer>   // splits <= 16 kMaxPer
 __global__ __launch_bounds__(kThreads) void router_dwr_reduce_kernel(
     const float* __restrict__ partial, float* __restrict__ dwr, int32_t E, int32_t d,
     int32_t splits) {
@@ -185,7 +186,6 @@ __global__ __launch_bounds__(kThreads) void router_dwr_reduce_kernel(
   const bool ok = col < d;   // d is a multiple of 64; kept for safety
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (ok) {
-    constexpr int kMaxPer = 4;   // splits <= 64
     float4 v[kMaxPer];
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
@@ -304,57 +304,47 @@ __device__ __forceinline__ void store4(bf16_t* p, const float* v) {
 }
 
 // dX rows of the dense form: a wavefront computes kDxTok tokens x 256 columns
-// (4 per lane).  Its kDxTok x E block of dl is staged in LDS as [e][token],
-// so one broadcast read gives four tokens' weights of expert e; Wr rows come
-// from L2.  Per element: sum_e dl[t,e] Wr[e] (e ascending), then the kept
-// dx_perm rows in slot order, in fp32, rounded once.
+// (4 per lane).  Per element: the kept dx_perm rows in slot order, then
+// sum_e dl[t,e] Wr[e] (e ascending), in fp32, rounded once.  The rows of
+// several tokens are loaded together (UT tokens x k slots in flight); the
+// wavefront's kDxTok x E block of dl is staged in LDS as [e][token], so two
+// broadcast reads give the eight tokens' weights of expert e; Wr rows come
+// from L2, eight experts' loads issued before they are used.  Every address
+// is clamped in bounds, so no load sits behind a branch.
 // K is the compile-time k (0: runtime k <= 16).
-constexpr int kDxTok = 16;
+constexpr int kDxTok = 8;
 template <typename TA, int K>
 __global__ __launch_bounds__(kThreads) void router_dx_dense_kernel(
     const TA* __restrict__ dxp, const int32_t* __restrict__ pos, const float* __restrict__ dl,
     const float* __restrict__ wr, TA* __restrict__ dx, int64_t T, int32_t d, int32_t k,
     int32_t E) {
   constexpr int KM = K > 0 ? K : 16;
-  constexpr int UT = (16 / KM) > 0 ? 16 / KM : 1;   // tokens whose rows are loaded together
+  constexpr int kMaxRows = sizeof(TA) == 2 ? 32 : 8;          // row pieces in flight
+  constexpr int UT0 = kMaxRows / KM >= 8 ? 8 : kMaxRows / KM >= 4 ? 4 : kMaxRows / KM >= 2 ? 2 : 1;
+  constexpr int UT = UT0;                                      // tokens whose rows load together
   static_assert(kDxTok % UT == 0, "token groups must tile the wavefront's tokens");
   const int kk = K > 0 ? K : k;
-  extern __shared__ float sdl[];   // [4 waves][E][kDxTok]
+  extern __shared__ float sdl[];   // [4 waves][E8][kDxTok], E8 = E rounded up to 8
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int ncb = (d + 255) / 256;
+  const int E8 = (E + 7) & ~7;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + w;
   const int64_t t0 = (wid / ncb) * kDxTok;
   const int cb = static_cast<int>(wid % ncb);
-  float* my = sdl + static_cast<int64_t>(w) * E * kDxTok;
-  for (int i = lane; i < kDxTok * E; i += 64) {
-    const int tl = i / E, e = i - tl * E;
-    my[e * kDxTok + tl] = (t0 + tl < T) ? dl[(t0 + tl) * E + e] : 0.f;
+  float* my = sdl + static_cast<int64_t>(w) * E8 * kDxTok;
+  for (int i = lane; i < kDxTok * E8; i += 64) {   // padding experts weigh 0
+    const int tl = i / E8, e = i - tl * E8;
+    my[e * kDxTok + tl] = (t0 + tl < T && e < E) ? dl[(t0 + tl) * E + e] : 0.f;
   }
   __syncthreads();
+  if (t0 >= T) return;   // wavefront-uniform; no barrier below
   const int col = cb * 256 + lane * 4;
-  if (t0 >= T || col >= d) return;
+  const int colc = col < d ? col : 0;   // lanes past d compute on column 0 and store nothing
   float acc[kDxTok][4];
 #pragma unroll
   for (int u = 0; u < kDxTok; ++u)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[u][i] = 0.f;
-  for (int e = 0; e < E; ++e) {
-    const float4 wv = *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * d + col);
-    const float4* dq = reinterpret_cast<const float4*>(my + e * kDxTok);
-#pragma unroll
-    for (int q = 0; q < kDxTok / 4; ++q) {
-      const float4 g = dq[q];
-      const float gg[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[4 * q + u][0] = fmaf(gg[u], wv.x, acc[4 * q + u][0]);
-        acc[4 * q + u][1] = fmaf(gg[u], wv.y, acc[4 * q + u][1]);
-        acc[4 * q + u][2] = fmaf(gg[u], wv.z, acc[4 * q + u][2]);
-        acc[4 * q + u][3] = fmaf(gg[u], wv.w, acc[4 * q + u][3]);
-      }
-    }
-  }
-  // kept expert rows in slot order; 16 / k tokens' loads in flight at a time
   if (dxp) {
 #pragma unroll
     for (int u0 = 0; u0 < kDxTok; u0 += UT) {
@@ -370,17 +360,43 @@ __global__ __launch_bounds__(kThreads) void router_dx_dense_kernel(
       for (int u = 0; u < UT; ++u)
 #pragma unroll
         for (int j = 0; j < KM; ++j)
-          load4(dxp + static_cast<int64_t>(max(pp[u][j], 0)) * d + col, v[u][j]);
+          load4(dxp + static_cast<int64_t>(max(pp[u][j], 0)) * d + colc, v[u][j]);
 #pragma unroll
       for (int u = 0; u < UT; ++u)
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-          if (j >= kk || pp[u][j] < 0) continue;
+          const bool keep = j < kk && pp[u][j] >= 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[u0 + u][i] += v[u][j][i];
+          for (int i = 0; i < 4; ++i) acc[u0 + u][i] += keep ? v[u][j][i] : 0.f;
         }
+      // one group's loads in flight at a time (bounds the registers they hold)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    float4 wv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      wv[u] = *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(min(e0 + u, E - 1)) * d +
+                                              colc);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {   // experts past E: a clamped Wr row times weight 0
+      const float4* dq = reinterpret_cast<const float4*>(my + (e0 + u) * kDxTok);
+#pragma unroll
+      for (int q = 0; q < kDxTok / 4; ++q) {
+        const float4 g = dq[q];
+        const float gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          acc[4 * q + z][0] = fmaf(gg[z], wv[u].x, acc[4 * q + z][0]);
+          acc[4 * q + z][1] = fmaf(gg[z], wv[u].y, acc[4 * q + z][1]);
+          acc[4 * q + z][2] = fmaf(gg[z], wv[u].z, acc[4 * q + z][2]);
+          acc[4 * q + z][3] = fmaf(gg[z], wv[u].w, acc[4 * q + z][3]);
+        }
+      }
+    }
+  }
+  if (col >= d) return;
 #pragma unroll
   for (int u = 0; u < kDxTok; ++u)
     if (t0 + u < T) store4(dx + (t0 + u) * d + col, acc[u]);
@@ -409,25 +425,30 @@ __global__ __launch_bounds__(kThreads) void router_dwr_dense_partial_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[e][i] = 0.f;
   constexpr int U = 4;
+  const int colc = cok ? col : 0;   // lanes past d read column 0 and write nothing
   for (int64_t t = lo + w; t < hi; t += 4 * U) {
     float xv[U][4];
     float g[U][kDwEB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t tt = t + 4 * u;
-      const int64_t tc = min<int64_t>(tt, hi - 1);
-      if (cok) load4(x + tc * d + col, xv[u]);
-      else xv[u][0] = xv[u][1] = xv[u][2] = xv[u][3] = 0.f;
+      const int64_t tc = min<int64_t>(t + 4 * u, hi - 1);
+      load4(x + tc * d + colc, xv[u]);
+      // kDwEB consecutive values of the token's row (the buffer is padded by
+      // kDwEB floats, so the last row's tail stays in bounds; masked below)
+      const float* row = dl + tc * E + e0;
 #pragma unroll
-      for (int e = 0; e < kDwEB; ++e)
-        g[u][e] = (tt < hi && e0 + e < E) ? dl[tc * E + min(e0 + e, E - 1)] : 0.f;
+      for (int e = 0; e < kDwEB; ++e) g[u][e] = row[e];
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      const bool tok = t + 4 * u < hi;
 #pragma unroll
-      for (int e = 0; e < kDwEB; ++e)
+      for (int e = 0; e < kDwEB; ++e) {
+        const float ge = (tok && e0 + e < E) ? g[u][e] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(g[u][e], xv[u][i], acc[e][i]);
+        for (int i = 0; i < 4; ++i) acc[e][i] = fmaf(ge, xv[u][i], acc[e][i]);
+      }
+    }
   }
 #pragma unroll
   for (int ec = 0; ec < kDwEB; ec += 8) {
@@ -502,16 +523,18 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     hipLaunchKernelGGL(router_dwr_partial_kernel<float>, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(x), offsets, src, ws_dl_perm, ws_partial, dm.d,
                        splits);
-  hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads), 0,
-                     s, ws_partial, dwr, dm.E, dm.d, splits);
+  hipLaunchKernelGGL(router_dwr_reduce_kernel<4>, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads),
+                     0, s, ws_partial, dwr, dm.E, dm.d, splits);
   return hipGetLastError();
 }
 
-// splits over tokens for the dense router weight gradient: about 2048 workgroups
+// splits over tokens for the dense router weight gradient: about 2048
+// workgroups, at most 256 splits, at least 64 tokens per split
 int route_bwd_dense_splits(const moe_dims& dm) {
   const int64_t base = static_cast<int64_t>((dm.d + 255) / 256) * ((dm.E + kDwEB - 1) / kDwEB);
-  const int64_t s = (2048 + base - 1) / base;
-  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 64)));
+  int64_t s = (2048 + base - 1) / base;
+  s = std::min<int64_t>(s, std::max<int64_t>(dm.T / 64, 1));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s, 256)));
 }
 
 hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float* wr,
@@ -538,7 +561,7 @@ hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float
     const int ncb = (dm.d + 255) / 256;
     const int64_t waves = ((dm.T + kDxTok - 1) / kDxTok) * ncb;
     const dim3 g2((waves + 3) / 4);
-    const size_t lds = static_cast<size_t>(4) * dm.E * kDxTok * sizeof(float);
+    const size_t lds = static_cast<size_t>(4) * ((dm.E + 7) & ~7) * kDxTok * sizeof(float);
 #define MOE_DXD(TA, KC)                                                                       \
   hipLaunchKernelGGL((router_dx_dense_kernel<TA, KC>), g2, dim3(kThreads), lds, s,             \
                      static_cast<const TA*>(dx_perm), pos, ws_dl, wr, static_cast<TA*>(dx),  \
@@ -568,8 +591,8 @@ hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float
   else
     hipLaunchKernelGGL(router_dwr_dense_partial_kernel<float>, g3, dim3(kThreads), 0, s,
                        static_cast<const float*>(x), ws_dl, ws_partial, dm.T, dm.d, dm.E, splits);
-  hipLaunchKernelGGL(router_dwr_reduce_kernel, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads), 0,
-                     s, ws_partial, dwr, dm.E, dm.d, splits);
+  hipLaunchKernelGGL(router_dwr_reduce_kernel<16>, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads),
+                     0, s, ws_partial, dwr, dm.E, dm.d, splits);
   return hipGetLastError();
 }
 

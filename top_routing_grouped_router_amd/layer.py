@@ -92,10 +92,11 @@ class MoELayer:
         table = self.topk_idx
         if self.capacity is not None:
             L.moe_capacity(self.dims, self.n_groups, self.capacity, self.topk_idx, self.kept_idx,
-                           self.group_dropped)
+                           self.group_dropped, self.workspace)
             table = self.kept_idx
         if self.z_coef != 0.0:
-            L.moe_router_zloss(self.dims, self.logits, self.n_groups, self.group_z)
+            L.moe_router_zloss(self.dims, self.logits, self.n_groups, self.group_z,
+                               self.workspace)
         if self.gather:
             L.moe_permute(self.dims, table, self.expert_counts, self.expert_offsets,
                           self.pos, self.src_token, None, None, self.workspace)
