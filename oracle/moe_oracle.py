@@ -543,6 +543,59 @@ def coselect(idx, E):
     return W
 
 
+def coselect_cross(idx_cur, idx_next, E):
+    """Cross-layer co-selection ([COUPLING] Abstract: the experts a token picks
+    at one layer predict its picks at the next; Fig. 2(b)): W[e1, e2] = number
+    of tokens that select e1 at layer l (idx_cur) and e2 at layer l+1
+    (idx_next).  e1 == e2 counts too: the layers' experts are distinct."""
+    T, k = idx_cur.shape
+    W = np.zeros((E, E), dtype=np.int64)
+    for t in range(T):
+        for i in range(k):
+            for j in range(idx_next.shape[1]):
+                W[idx_cur[t, i], idx_next[t, j]] += 1
+    return W
+
+
+def shuffle_plan(idx_cur, W, placement_next, G):
+    """Token-shuffle planner ([COUPLING] Fig. 5 step 1, Fig. 6, Table I "token
+    moved"): each token goes to the group expected to hold most of its
+    next-layer experts, predicted from its current experts through the
+    cross-layer counts W (fit on other batches):
+        owner(t) = argmax_g sum_{e1 in S_cur(t)} sum_{e2 : placement(e2) = g} W[e1, e2],
+    ties to the lowest group id.  Returns owner [T] and the tokens per group."""
+    T, k = idx_cur.shape
+    E = W.shape[0]
+    owner = np.zeros(T, dtype=np.int64)
+    for t in range(T):
+        best, best_g = None, 0
+        for g in range(G):
+            score = 0
+            for i in range(k):
+                for e2 in range(E):
+                    if placement_next[e2] == g:
+                        score += int(W[idx_cur[t, i], e2])
+            if best is None or score > best:
+                best, best_g = score, g
+        owner[t] = best_g
+    return {"owner": owner, "group_tokens": np.bincount(owner, minlength=G)}
+
+
+def shuffle_local(owner, idx_next, placement_next, G):
+    """Table I "local experts": next-layer assignments served on the token's
+    own group, when it sits on the planned owner (moved) and when it stays on
+    its home group t // (T/G).  Returns (moved, stays) assignment counts."""
+    T, k = idx_next.shape
+    n = T // G
+    moved = stays = 0
+    for t in range(T):
+        for j in range(k):
+            g = placement_next[idx_next[t, j]]
+            moved += int(g == owner[t])
+            stays += int(g == t // n)
+    return moved, stays
+
+
 def placement_contiguous(E, G):
     """Expert e lives in group floor(e / (E/G))."""
     if E % G:

@@ -753,3 +753,73 @@ def test_new_pins_catch_planted_mistakes():
     # a z gradient missing the factor 2: differences disagree
     num = _numeric_grad(O.z_loss, logits.copy())
     assert np.abs(num - 0.5 * O.z_loss_grad(logits)).max() > 1e-3
+
+
+# ---------------------------------------------------------------- token-shuffle planner
+
+def test_coselect_cross_reduces_to_within_layer_counts():
+    T, E, k = 400, 10, 3
+    idx = make_routing(T, E, k, seed=8)
+    X = O.coselect_cross(idx, idx, E)
+    W = O.coselect(idx, E)
+    off = ~np.eye(E, dtype=bool)
+    assert np.array_equal(X[off], W[off])
+    assert np.array_equal(np.diag(X), np.bincount(idx.ravel(), minlength=E))
+    # another layer: row sums are the current layer's counts times k
+    nxt = make_routing(T, E, k, seed=9)
+    Y = O.coselect_cross(idx, nxt, E)
+    assert np.array_equal(Y.sum(1), k * np.bincount(idx.ravel(), minlength=E))
+    assert np.array_equal(Y.sum(0), k * np.bincount(nxt.ravel(), minlength=E))
+
+
+def test_shuffle_plan_matches_dense_scores():
+    """The planner's argmax against scores formed as one-hot(S_cur) W one-hot(placement)."""
+    T, E, k, G = 300, 12, 2, 4
+    cur = make_routing(T, E, k, seed=10)
+    nxt = make_routing(T, E, k, seed=11)
+    W = O.coselect_cross(make_routing(T, E, k, seed=12), make_routing(T, E, k, seed=13), E)
+    pl = O.placement_contiguous(E, G)
+    plan = O.shuffle_plan(cur, W, pl, G)
+    S = np.zeros((T, E), dtype=np.int64)
+    np.put_along_axis(S, cur.astype(np.int64), 1, axis=1)
+    P = np.eye(G, dtype=np.int64)[pl]                       # [E, G]
+    score = S @ W @ P
+    assert np.array_equal(plan["owner"], np.argmax(score, axis=1))   # first maximum = lowest id
+    assert plan["group_tokens"].sum() == T
+    moved, stays = O.shuffle_local(plan["owner"], nxt, pl, G)
+    G_of = P[nxt.ravel()].reshape(T, k, G)
+    assert moved == int(G_of[np.arange(T), :, plan["owner"]].sum())
+    assert stays == int(G_of[np.arange(T), :, np.arange(T) // (T // G)].sum())
+
+
+def test_shuffle_plan_planted_groups_are_all_local():
+    """Every token picks its k experts inside one group at both layers: the
+    counts never cross groups, so the planner finds that group and every
+    next-layer assignment is local; staying home is local only for the tokens
+    whose home is that group."""
+    T, E, k, G = 256, 16, 3, 4
+    g = stream(71, 0)
+    per = E // G
+    grp = g.integers(0, G, size=T)
+    def draw(seed):
+        gg = stream(72, seed)
+        return np.stack([grp[t] * per + gg.permutation(per)[:k] for t in range(T)]).astype(np.int32)
+    cur, nxt, fit_a, fit_b = draw(1), draw(2), draw(3), draw(4)
+    pl = O.placement_contiguous(E, G)
+    W = O.coselect_cross(fit_a, fit_b, E)
+    plan = O.shuffle_plan(cur, W, pl, G)
+    assert np.array_equal(plan["owner"], grp)
+    moved, stays = O.shuffle_local(plan["owner"], nxt, pl, G)
+    assert moved == T * k
+    assert stays == k * int((grp == np.arange(T) // (T // G)).sum())
+
+
+def test_shuffle_local_stays_is_one_over_g_for_independent_routing():
+    T, E, k, G = 4096, 16, 4, 8
+    nxt = make_routing(T, E, k, seed=14)
+    pl = O.placement_contiguous(E, G)
+    _, stays = O.shuffle_local(np.zeros(T, dtype=np.int64), nxt, pl, G)
+    # each assignment's group is uniform and independent of the home group
+    p = 1.0 / G
+    sd = math.sqrt(T * k * p * (1 - p))
+    assert abs(stays - T * k * p) < 5 * sd
