@@ -225,6 +225,75 @@ def ep_dispatch(cfg, layer, x, steps):
     return res
 
 
+def token_shuffle(cfg, layer, x, wr, steps):
+    """Token-shuffle planning on one GPU for each placement group count of the
+    workload: two layers' routes (the workload's router and a second router
+    drawn from another seed, on the same hidden states), cross-layer counts fit
+    on another batch of the workload, then the planner on this batch with the
+    next layer's experts placed contiguously or by greedy co-selection (itself
+    fit on the other batch).  Reports Table I's local next-layer assignments
+    when tokens are moved to the predicted owner versus when they stay home,
+    the spread of tokens per owner, and the planner's time (HIP events)."""
+    import torch
+    from synth import make_layer_inputs
+    import top_routing_grouped_router_amd._lib as L
+    T, k, E = cfg.T, cfg.k, cfg.E
+    dm = layer.dims
+    act = x.dtype
+    i32 = dict(dtype=torch.int32, device="cuda")
+    wr2 = torch.from_numpy(make_layer_inputs(cfg, seed=1, parts=("wr",))["wr"]).cuda()
+    x_fit = torch.from_numpy(make_layer_inputs(cfg, batch_seed=1, parts=("x",))["x"]).to(
+        "cuda", act)
+    ws = torch.empty(L.workspace_bytes(dm, max(cfg.plan_groups)), dtype=torch.uint8,
+                     device="cuda")
+
+    def route(xx, w):
+        lg = torch.empty(T, E, device="cuda")
+        idx = torch.empty(T, k, **i32)
+        gate = torch.empty(T, k, device="cuda")
+        mg = torch.empty(T, device="cuda")
+        ntc = torch.empty(1, **i32)
+        L.moe_route(dm, xx, w, lg, idx, gate, mg, 1e-3, ntc, 1, None, None, None, ws)
+        return idx
+
+    fit_cur, fit_nxt = route(x_fit, wr), route(x_fit, wr2)
+    cur, nxt = route(x, wr), route(x, wr2)
+    W = torch.empty(E, E, **i32)
+    L.moe_coselect_cross(T, k, E, fit_cur, fit_nxt, W)
+    Wn = torch.empty(E, E, **i32)
+    L.moe_coselect(T, k, E, fit_nxt, Wn)
+    torch.cuda.synchronize()
+    Wn_host = Wn.cpu().numpy().astype(np.int64)
+    cond = W.cpu().numpy() / np.maximum(W.cpu().numpy().sum(1, keepdims=True) / k, 1)
+    res = {"strong_pairs_pct": round(100.0 * float((cond > 0.3).mean()), 2)}
+    for G in cfg.plan_groups:
+        for name, pl in (("contiguous", [e * G // E for e in range(E)]),
+                         ("correlated", L.moe_placement_greedy(E, G, Wn_host))):
+            owner = torch.empty(T, **i32)
+            gt = torch.empty(G, **i32)
+            st = torch.empty(2, **i32)
+
+            def plan():
+                L.moe_shuffle_plan(T, k, E, G, cur, W, pl, nxt, owner, gt, st, ws)
+
+            plan()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                plan()
+            b.record()
+            torch.cuda.synchronize()
+            moved, stays = (int(v) for v in st.cpu().tolist())
+            tokens = gt.cpu().numpy()
+            res[f"G{G}_{name}"] = {
+                "local_moved_pct": round(100.0 * moved / (T * k), 1),
+                "local_stays_pct": round(100.0 * stays / (T * k), 1),
+                "owner_tokens_max_over_mean": round(float(tokens.max()) / (T / G), 2),
+                "plan_us": round(a.elapsed_time(b) / steps * 1e3, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +309,10 @@ def main():
                     help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
                          "expand) for the workload's placement group counts; adds an "
                          "'ep_dispatch' object to the JSON line")
+    ap.add_argument("--shuffle", action="store_true",
+                    help="also run the token-shuffle planner (cross-layer counts of two routers, "
+                         "owner prediction, local next-layer assignments) for the workload's "
+                         "placement group counts; adds a 'token_shuffle' object")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="definitional variant: per-block expert capacity with dropping "
                          "(moe_capacity before the permutation, moe_route_bwd_dense after)")
@@ -427,6 +500,8 @@ def main():
                         if layer.group_dropped is not None else 0)}
     if args.ep and cfg.plan_groups:
         out["ep_dispatch"] = ep_dispatch(cfg, layer, x, args.steps)
+    if args.shuffle and cfg.plan_groups:
+        out["token_shuffle"] = token_shuffle(cfg, layer, x, wr, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -434,6 +434,37 @@ moe_status moe_dispatch_expand(const moe_dims* dims, const void* recv,
                                void* stream);
 
 /*
+ * Token-shuffle planning ([COUPLING] Abstract: the experts a token selects at
+ * one layer predict those it selects at the next; Fig. 2(b); Fig. 5 step 1 and
+ * Fig. 6: a planner predicts each token's owner GPU from its previous-layer
+ * routes, and the reduce-scatter delivers the token there; Table I: local
+ * next-layer experts when moved versus when staying home).
+ *
+ * moe_coselect_cross -- W[e1,e2] = number of tokens that select e1 in
+ *   topk_idx_cur (layer l) and e2 in topk_idx_next (layer l+1); e1 == e2
+ *   counts.  topk_idx_cur, topk_idx_next [T,k]; coselect [E,E] int32.
+ *
+ * moe_shuffle_plan -- owner[t] = argmax over groups g of
+ *     sum_{e1 in S_cur(t)} sum_{e2 : placement_next[e2] = g} predictor[e1,e2]
+ *   (64-bit sums, ties to the lowest g), with predictor the cross-layer counts
+ *   of other batches (moe_coselect_cross).  group_tokens [G]: tokens per
+ *   owner.  stats [2] int32: next-layer assignments whose expert sits on the
+ *   token's owner group (moved) and on its home group t / (T/G) (stays), when
+ *   topk_idx_next [T,k] is given; zeros when it is NULL.
+ *   placement_next [host] [E]: a balanced partition of layer l+1's experts
+ *   over G groups (else MOE_ERR_INVALID_PLACEMENT); 1 <= G <= 64, G divides
+ *   T, E*G <= 8192 (else MOE_ERR_UNSUPPORTED).  Workspace: E*G*4 bytes
+ *   (moe_workspace_bytes covers it).
+ */
+moe_status moe_coselect_cross(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx_cur,
+                              const int32_t* topk_idx_next, int32_t* coselect, void* stream);
+moe_status moe_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G,
+                            const int32_t* topk_idx_cur, const int32_t* predictor,
+                            const int32_t* placement_next, const int32_t* topk_idx_next,
+                            int32_t* owner, int32_t* group_tokens, int32_t* stats,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_placement_greedy -- [host] correlated expert placement ([COUPLING]
  * Abstract and Fig. 3: experts that are often selected together go to the
  * same GPU).  Deterministic, integer arithmetic only.  Fills one group at a

@@ -1,0 +1,138 @@
+"""GPU parity of the token-shuffle planning calls against the oracle:
+moe_coselect_cross (cross-layer co-selection counts) and moe_shuffle_plan
+(owner prediction, tokens per owner, local next-layer assignments when moved
+or staying).  Integer outputs: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import get_config, make_layer_inputs, make_routing, stream
+import top_routing_grouped_router_amd as M
+
+from _util import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def _two_layer_routes(T, E, k, seed):
+    """Correlated routes of two layers: the next layer keeps each current
+    expert's group with probability 0.7 (a fixed expert map), else draws."""
+    g = stream(81, seed)
+    cur = make_routing(T, E, k, seed=seed)
+    remap = g.permutation(E)
+    nxt = np.empty_like(cur)
+    for t in range(T):
+        chosen = []
+        for j in range(k):
+            e = int(remap[cur[t, j]]) if g.random() < 0.7 else int(g.integers(0, E))
+            while e in chosen:
+                e = (e + 1) % E
+            chosen.append(e)
+        nxt[t] = chosen
+    return cur, nxt
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 8, 2), (3000, 64, 6), (517, 256, 16)])
+def test_coselect_cross_bit_exact(T, E, k):
+    _announce(f"coselect_cross T={T} E={E} k={k}")
+    cur, nxt = _two_layer_routes(T, E, k, seed=T)
+    W = torch.full((E, E), -1, dtype=torch.int32, device="cuda")
+    M.moe_coselect_cross(T, k, E, dev(cur, torch.int32), dev(nxt, torch.int32), W)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(W), O.coselect_cross(cur, nxt, E))
+
+
+@pytest.mark.parametrize("T,E,k,G,placement", [
+    (2048, 16, 4, 8, "contiguous"), (2048, 64, 6, 8, "greedy"), (1536, 64, 2, 16, "contiguous"),
+    (960, 12, 3, 4, "greedy")])
+def test_shuffle_plan_bit_exact(T, E, k, G, placement):
+    _announce(f"shuffle_plan T={T} E={E} k={k} G={G} {placement}")
+    fit_cur, fit_nxt = _two_layer_routes(T, E, k, seed=1)
+    cur, nxt = _two_layer_routes(T, E, k, seed=2)
+    W = O.coselect_cross(fit_cur, fit_nxt, E)
+    if placement == "contiguous":
+        pl = O.placement_contiguous(E, G)
+    else:
+        pl = O.placement_greedy(O.coselect(fit_nxt, E), G)
+    ref = O.shuffle_plan(cur, W, pl, G)
+    moved, stays = O.shuffle_local(ref["owner"], nxt, pl, G)
+    owner = torch.full((T,), -1, dtype=torch.int32, device="cuda")
+    gt = torch.full((G,), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(E * G * 4 + 256, dtype=torch.uint8, device="cuda")
+    M.moe_shuffle_plan(T, k, E, G, dev(cur, torch.int32), dev(W.astype(np.int32), torch.int32),
+                       list(pl), dev(nxt, torch.int32), owner, gt, st, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(owner), ref["owner"])
+    assert np.array_equal(host(gt), ref["group_tokens"])
+    assert host(st).tolist() == [moved, stays]
+    print(f"[shuffle] local when moved {moved / (T * k):.3f}, staying {stays / (T * k):.3f}",
+          flush=True)
+
+
+def test_shuffle_plan_full_size_routes_from_two_routers():
+    """16384 tokens of the mixture workload (2048 wide, 64 experts, top-6),
+    routed by two router weights on the same hidden states: owners against
+    the dense one-hot scores, local counts against their definition."""
+    _announce("shuffle_plan full size")
+    cfg = get_config("c5")
+    T, E, k, G = cfg.T, cfg.E, cfg.k, 8
+    inp = make_layer_inputs(cfg, parts=("x", "wr"))
+    wr2 = make_layer_inputs(cfg, seed=1, parts=("wr",))["wr"]
+    x = dev(inp["x"], torch.bfloat16)
+    dims = M.make_dims(T, cfg.d, E, cfg.f, k, torch.bfloat16)
+    ws = M.alloc_workspace(dims, G)
+    routes = []
+    for w in (inp["wr"], wr2):
+        lg = torch.empty((T, E), device="cuda")
+        idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        gate = torch.empty((T, k), device="cuda")
+        mg = torch.empty(T, device="cuda")
+        ntc = torch.empty(1, dtype=torch.int32, device="cuda")
+        M.moe_route(dims, x, dev(w, torch.float32), lg, idx, gate, mg, 1e-3, ntc, 1, None, None,
+                    None, ws)
+        routes.append(idx)
+    Wd = torch.empty((E, E), dtype=torch.int32, device="cuda")
+    M.moe_coselect_cross(T, k, E, routes[0], routes[1], Wd)
+    pl = O.placement_contiguous(E, G)
+    owner = torch.empty(T, dtype=torch.int32, device="cuda")
+    gt = torch.empty(G, dtype=torch.int32, device="cuda")
+    st = torch.empty(2, dtype=torch.int32, device="cuda")
+    M.moe_shuffle_plan(T, k, E, G, routes[0], Wd, list(pl), routes[1], owner, gt, st, ws)
+    torch.cuda.synchronize()
+    cur, nxt, W = host(routes[0]).astype(np.int64), host(routes[1]).astype(np.int64), host(Wd)
+    assert np.array_equal(W, O.coselect_cross(cur, nxt, E))
+    S = np.zeros((T, E), dtype=np.int64)
+    np.put_along_axis(S, cur, 1, axis=1)
+    score = S @ W.astype(np.int64) @ np.eye(G, dtype=np.int64)[pl]
+    own = np.argmax(score, axis=1)
+    assert np.array_equal(host(owner), own)
+    assert np.array_equal(host(gt), np.bincount(own, minlength=G))
+    grp = np.asarray(pl)[nxt]
+    moved = int((grp == own[:, None]).sum())
+    stays = int((grp == (np.arange(T) // (T // G))[:, None]).sum())
+    assert host(st).tolist() == [moved, stays]
+    print(f"[shuffle c5] local when moved {moved / (T * k):.3f}, staying {stays / (T * k):.3f}",
+          flush=True)
+
+
+def test_shuffle_plan_rejects_bad_arguments():
+    T, E, k, G = 64, 8, 2, 4
+    cur = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    W = torch.zeros((E, E), dtype=torch.int32, device="cuda")
+    owner = torch.empty(T, dtype=torch.int32, device="cuda")
+    gt = torch.empty(G, dtype=torch.int32, device="cuda")
+    st = torch.empty(2, dtype=torch.int32, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(M.MoEError):   # unbalanced placement
+        M.moe_shuffle_plan(T, k, E, G, cur, W, [0] * E, None, owner, gt, st, ws)
+    with pytest.raises(M.MoEError):   # G does not divide T
+        M.moe_shuffle_plan(T, k, E, 3, cur, W, [0, 0, 1, 1, 2, 2, 0, 1], None, owner, gt, st, ws)
+    with pytest.raises(M.MoEError):   # workspace too small
+        M.moe_shuffle_plan(T, k, E, G, cur, W, list(O.placement_contiguous(E, G)), None, owner,
+                           gt, st, ws[:16])

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_combine_bwd,
     moe_coselect,
+    moe_coselect_cross,
     moe_dispatch_expand,
     moe_dispatch_pack,
     moe_dispatch_plan,
@@ -40,6 +41,7 @@ from ._lib import (  # noqa: F401
     moe_route_bwd,
     moe_route_bwd_dense,
     moe_router_zloss,
+    moe_shuffle_plan,
     workspace_bytes,
 )
 from .layer import MoELayer  # noqa: F401

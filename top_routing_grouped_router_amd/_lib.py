@@ -38,6 +38,7 @@ EXPORTED = (
     "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
     "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
     "moe_expert_capacity", "moe_capacity", "moe_router_zloss", "moe_route_bwd_dense",
+    "moe_coselect_cross", "moe_shuffle_plan",
 )
 
 
@@ -97,6 +98,9 @@ _SIGNATURES = {
     "moe_router_zloss": (_I32, [_DIMS, _P, _I32, _P, _P, _SZ, _P]),
     "moe_route_bwd_dense": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _F32, _F32,
                                    _P, _P, _P, _P, _SZ, _P]),
+    "moe_coselect_cross": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_shuffle_plan": (_I32, [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -459,3 +463,27 @@ def moe_route_bwd_dense(dims, x, w_router, logits, topk_idx, topk_gate, dgate, p
         _ptr(dlogits, "dlogits", torch.float32), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_route_bwd_dense")
+
+
+# ---------------------------------------------------------------- token-shuffle planning
+def moe_coselect_cross(T, k, E, topk_idx_cur, topk_idx_next, coselect, stream=None):
+    st = lib().moe_coselect_cross(int(T), int(k), int(E),
+                                  _ptr(topk_idx_cur, "topk_idx_cur", torch.int32),
+                                  _ptr(topk_idx_next, "topk_idx_next", torch.int32),
+                                  _ptr(coselect, "coselect", torch.int32), _stream(stream))
+    _check(st, "moe_coselect_cross")
+
+
+def moe_shuffle_plan(T, k, E, G, topk_idx_cur, predictor, placement_next, topk_idx_next, owner,
+                     group_tokens, stats, workspace, stream=None):
+    pl = (ctypes.c_int32 * E)(*[int(v) for v in placement_next])
+    st = lib().moe_shuffle_plan(int(T), int(k), int(E), int(G),
+                                _ptr(topk_idx_cur, "topk_idx_cur", torch.int32),
+                                _ptr(predictor, "predictor", torch.int32),
+                                ctypes.cast(pl, ctypes.c_void_p),
+                                _ptr(topk_idx_next, "topk_idx_next", torch.int32),
+                                _ptr(owner, "owner", torch.int32),
+                                _ptr(group_tokens, "group_tokens", torch.int32),
+                                _ptr(stats, "stats", torch.int32), _ptr(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_shuffle_plan")

@@ -194,6 +194,14 @@ hipError_t launch_dispatch_plan(int64_t T, int32_t k, int32_t E, int32_t G,
                                 int32_t* ws_hist, int32_t* ws_base, int32_t* ws_stat,
                                 hipStream_t s);
 
+// token-shuffle planning: cross-layer co-selection and the owner prediction
+hipError_t launch_coselect_cross(int64_t T, int32_t k, int32_t E, const int32_t* cur,
+                                 const int32_t* nxt, int32_t* W, hipStream_t s);
+hipError_t launch_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G, const int32_t* cur,
+                               const int32_t* W, const PlacementArg& pl, const int32_t* nxt,
+                               int32_t* owner, int32_t* group_tokens, int32_t* stats,
+                               int32_t* ws_mass, hipStream_t s);
+
 // expert-parallel dispatch emulated on one device
 hipError_t launch_ep_pack(const moe_dims& dm, int32_t G, const void* x,
                           const int32_t* group_offsets, const int32_t* row_token, void* send,

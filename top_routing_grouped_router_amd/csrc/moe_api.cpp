@@ -219,6 +219,7 @@ size_t workspace_needed(const moe_dims& dm, int32_t n_groups) {
   need = std::max(need, route_bwd_ws(dm, nullptr).bytes);
   need = std::max(need, route_bwd_dense_ws(dm, nullptr).bytes);
   need = std::max(need, variant_ws(dm, G, nullptr).bytes);
+  need = std::max(need, moe::align256(static_cast<size_t>(dm.E) * std::max(G, 64) * 4));
   need = std::max(need, plan_ws(dm.T, std::max(G, 64), nullptr).bytes);
   return need;
 }
@@ -910,6 +911,61 @@ moe_status moe_route_bwd_dense(const moe_dims* dims, const void* x, const float*
                                                 dgate, pos, dx_perm, n_groups, group_count,
                                                 aux_coef, z_coef, dx, dw_router, dlogits, w.dl,
                                                 w.partial, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+// ---------------------------------------------------------------- token-shuffle planning
+static moe_status check_index_dims(int64_t T, int32_t k, int32_t E, const char* fn) {
+  if (T < 0 || k <= 0 || E <= 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need T >= 0 and k, E > 0", fn);
+  if (E > 256 || k > E || k > 16)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: need E <= 256 and k <= min(E, 16)", fn);
+  if (T * k >= (int64_t(1) << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k must be < 2^31", fn);
+  return MOE_OK;
+}
+
+moe_status moe_coselect_cross(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx_cur,
+                              const int32_t* topk_idx_next, int32_t* coselect, void* stream) {
+  moe_status st = check_index_dims(T, k, E, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(topk_idx_cur, T * k);
+  MOE_REQUIRE_PTR(topk_idx_next, T * k);
+  MOE_REQUIRE_PTR(coselect, int64_t(E) * E);
+  return hip_status(moe::launch_coselect_cross(T, k, E, topk_idx_cur, topk_idx_next, coselect,
+                                               static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G,
+                            const int32_t* topk_idx_cur, const int32_t* predictor,
+                            const int32_t* placement_next, const int32_t* topk_idx_next,
+                            int32_t* owner, int32_t* group_tokens, int32_t* stats,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_index_dims(T, k, E, __func__);
+  if (st != MOE_OK) return st;
+  if (G < 1 || G > 64)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: need 1 <= G <= 64", __func__);
+  if (T % G)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: G=%d does not divide T=%lld", __func__, G,
+                static_cast<long long>(T));
+  if (static_cast<int64_t>(E) * G > 8192)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E*G=%d exceeds 8192", __func__, E * G);
+  st = check_placement_impl(E, G, placement_next, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(topk_idx_cur, T * k);
+  MOE_REQUIRE_PTR(predictor, int64_t(E) * E);
+  MOE_OPTIONAL_PTR(topk_idx_next);
+  MOE_REQUIRE_PTR(owner, T);
+  MOE_REQUIRE_PTR(group_tokens, G);
+  MOE_REQUIRE_PTR(stats, 2);
+  st = check_ws(workspace, workspace_bytes, static_cast<size_t>(E) * G * 4, __func__);
+  if (st != MOE_OK) return st;
+  moe::PlacementArg pl{};
+  for (int32_t e = 0; e < E; ++e) pl.group_of[e] = placement_next[e];
+  return hip_status(moe::launch_shuffle_plan(T, k, E, G, topk_idx_cur, predictor, pl,
+                                             topk_idx_next, owner, group_tokens, stats,
+                                             static_cast<int32_t*>(workspace),
+                                             static_cast<hipStream_t>(stream)),
                     __func__);
 }
 
