@@ -294,6 +294,78 @@ def token_shuffle(cfg, layer, x, wr, steps):
     return res
 
 
+def fragility(cfg, layer, x, wr, steps):
+    """Routing-fragility probe: one router weight (a seeded expert, its
+    largest-magnitude input weight) moved by m units in the last place of fp32,
+    the router run again, and the tokens whose expert set changed
+    (moe_route_flips) set against their margins in the unmoved run.  Reports,
+    per m, the flip count, the largest logit shift |x[t,i] dw|, the share of
+    flips whose margin is within that shift, the median normalised margin of
+    flipped and kept tokens, and how much more often the 10% smallest margins
+    flip than the rest."""
+    import torch
+    import top_routing_grouped_router_amd._lib as L
+    T, k, E = cfg.T, cfg.k, cfg.E
+    dm = layer.dims
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ws = layer.workspace
+    rng = np.random.default_rng(7)
+    w_host = wr.cpu().numpy()
+    e = int(rng.integers(0, E))
+    i = int(np.argmax(np.abs(w_host[e])))
+
+    def route(w):
+        lg = torch.empty(T, E, device="cuda")
+        idx = torch.empty(T, k, **i32)
+        gate = torch.empty(T, k, device="cuda")
+        mg = torch.empty(T, device="cuda")
+        ntc = torch.empty(1, **i32)
+        L.moe_route(dm, x, w, lg, idx, gate, mg, 1e-3, ntc, 1, None, None, None, ws)
+        return idx, mg, lg
+
+    base_idx, base_margin, base_lg = route(wr)
+    lg = base_lg.cpu().numpy().astype(np.float64)
+    spread = lg.max(1) - lg.min(1)
+    margin = base_margin.cpu().numpy().astype(np.float64)
+    norm = np.where(spread > 0, margin / np.where(spread > 0, spread, 1.0), np.inf)
+    xcol = x[:, i].float().cpu().numpy().astype(np.float64)
+    res = {"weight": [e, i]}
+    flips = torch.empty(T, **i32)
+    n = torch.empty(1, **i32)
+    for m in (1, 1 << 10, 1 << 20):
+        v = np.float32(w_host[e, i])
+        bits = np.array([v], dtype=np.float32).view(np.int32)[0]
+        # toward +inf: the magnitude grows for positive values, shrinks for negative
+        bits = bits + m if v > 0 else bits - m
+        wn = w_host.copy()
+        wn[e, i] = np.array([bits], dtype=np.int32).view(np.float32)[0]
+        idx_n, _, _ = route(torch.from_numpy(wn).cuda())
+        L.moe_route_flips(T, k, E, base_idx, idx_n, flips, n)
+        torch.cuda.synchronize()
+        fl = flips.cpu().numpy().astype(bool)
+        shift = np.abs(xcol * (float(wn[e, i]) - float(v)))
+        small = norm <= np.quantile(norm, 0.1)
+        rate_small = fl[small].mean() if small.any() else 0.0
+        rate_rest = fl[~small].mean() if (~small).any() else 0.0
+        res[str(m)] = {
+            "flips": int(fl.sum()), "max_logit_shift": float(f"{shift.max():.3e}"),
+            "flips_within_shift_pct": (round(100.0 * float((margin[fl] <= shift[fl] + 1e-5).mean()),
+                                             1) if fl.any() else None),
+            "median_norm_margin_flipped": (float(f"{np.median(norm[fl]):.3e}") if fl.any()
+                                           else None),
+            "median_norm_margin_kept": float(f"{np.median(norm[~fl]):.3e}"),
+            "smallest_decile_flip_rate_ratio": (round(float(rate_small / rate_rest), 1)
+                                                if rate_rest > 0 else None)}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        L.moe_route_flips(T, k, E, base_idx, idx_n, flips, n)
+    b.record()
+    torch.cuda.synchronize()
+    res["route_flips_us"] = round(a.elapsed_time(b) / steps * 1e3, 1)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -309,6 +381,10 @@ def main():
                     help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
                          "expand) for the workload's placement group counts; adds an "
                          "'ep_dispatch' object to the JSON line")
+    ap.add_argument("--fragility", action="store_true",
+                    help="also run the routing-fragility probe (one router weight moved by "
+                         "1, 2^10 and 2^20 ulps; flips against margins); adds a 'fragility' "
+                         "object")
     ap.add_argument("--shuffle", action="store_true",
                     help="also run the token-shuffle planner (cross-layer counts of two routers, "
                          "owner prediction, local next-layer assignments) for the workload's "
@@ -500,6 +576,8 @@ def main():
                         if layer.group_dropped is not None else 0)}
     if args.ep and cfg.plan_groups:
         out["ep_dispatch"] = ep_dispatch(cfg, layer, x, args.steps)
+    if args.fragility:
+        out["fragility"] = fragility(cfg, layer, x, wr, args.steps)
     if args.shuffle and cfg.plan_groups:
         out["token_shuffle"] = token_shuffle(cfg, layer, x, wr, args.steps)
     if not args.no_cpu_baseline:

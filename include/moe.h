@@ -465,6 +465,18 @@ moe_status moe_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_flips -- routing decisions that differ between two runs ([LAYOUT]
+ * Finding 3: flipped decisions and their margins; Measurement Framework: a
+ * 1-ULP change to one weight as a yardstick).  flips [T] int32: 1 when token
+ * t's chosen expert set in topk_idx_a differs from that in topk_idx_b (slot
+ * order ignored), else 0; n_flips [1] int32: their number.  topk_idx_a,
+ * topk_idx_b [T,k] with ids in [0, E) (others are ignored).
+ */
+moe_status moe_route_flips(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx_a,
+                           const int32_t* topk_idx_b, int32_t* flips, int32_t* n_flips,
+                           void* stream);
+
+/*
  * moe_placement_greedy -- [host] correlated expert placement ([COUPLING]
  * Abstract and Fig. 3: experts that are often selected together go to the
  * same GPU).  Deterministic, integer arithmetic only.  Fills one group at a

@@ -596,6 +596,27 @@ def shuffle_local(owner, idx_next, placement_next, G):
     return moved, stays
 
 
+def route_flips(idx_a, idx_b):
+    """[LAYOUT] Finding 3 (routing decisions that change between two runs):
+    flips[t] is True when token t's chosen expert set differs (slot order
+    ignored)."""
+    return np.array([set(map(int, a)) != set(map(int, b)) for a, b in zip(idx_a, idx_b)],
+                    dtype=bool)
+
+
+def nudge_ulps(w, e, i, m):
+    """Router weight with element (e, i) moved m units in the last place of
+    fp32 (toward +inf for m > 0): [LAYOUT] Measurement Framework, the 1-ULP
+    change to a single weight (m = 1)."""
+    w = np.array(w, dtype=np.float32, copy=True)
+    v = w[e, i]
+    step = np.float32(np.inf) if m > 0 else np.float32(-np.inf)
+    for _ in range(abs(int(m))):
+        v = np.nextafter(v, step)
+    w[e, i] = v
+    return w
+
+
 def placement_contiguous(E, G):
     """Expert e lives in group floor(e / (E/G))."""
     if E % G:

@@ -823,3 +823,44 @@ def test_shuffle_local_stays_is_one_over_g_for_independent_routing():
     p = 1.0 / G
     sd = math.sqrt(T * k * p * (1 - p))
     assert abs(stays - T * k * p) < 5 * sd
+
+
+# ---------------------------------------------------------------- routing fragility probe
+
+def test_nudge_ulps_moves_by_units_in_the_last_place():
+    w = np.array([[1.0, -2.5], [3.0e-8, 0.0]], dtype=np.float32)
+    n = O.nudge_ulps(w, 0, 1, 1)
+    assert n[0, 1] == np.nextafter(np.float32(-2.5), np.float32(np.inf))
+    assert np.array_equal(np.delete(n.ravel(), 1), np.delete(w.ravel(), 1))
+    up = O.nudge_ulps(w, 0, 0, 8)
+    assert up.view(np.int32)[0, 0] - w.view(np.int32)[0, 0] == 8     # positive: ulps are ints
+    assert O.nudge_ulps(up, 0, 0, -8)[0, 0] == w[0, 0]
+
+
+def test_flips_of_a_single_weight_nudge_follow_the_logit_shift():
+    """Only expert e's logits move, each by exactly x[t,i] * dw; the oracle's
+    routing flips exactly where that shift carries e across the boundary
+    between chosen and unchosen experts (checked against the definition, away
+    from exact ties)."""
+    g = stream(91, 0)
+    T, d, E, k = 4000, 32, 8, 2
+    x = g.standard_normal((T, d)).astype(np.float32)
+    wr = g.standard_normal((E, d)).astype(np.float32)
+    e, i, m = 5, 7, 1 << 21
+    wn = O.nudge_ulps(wr, e, i, m)
+    la, lb = O.router_logits(x, wr), O.router_logits(x, wn)
+    dl = lb - la
+    assert np.abs(np.delete(dl, e, axis=1)).max() == 0.0
+    assert np.allclose(dl[:, e], x[:, i].astype(np.float64) * (float(wn[e, i]) - float(wr[e, i])),
+                       rtol=1e-12, atol=0)
+    ia, _ = O.topk_select(la, k)
+    ib, _ = O.topk_select(lb, k)
+    flips = O.route_flips(ia, ib)
+    assert 0 < flips.sum() < T
+    # predicted: e inside the set and now below the best excluded expert, or
+    # outside and now above the weakest chosen expert
+    srt = np.sort(np.delete(la, e, axis=1), axis=1)[:, ::-1]        # other experts, descending
+    inside = (ia == e).any(axis=1)
+    pred = np.where(inside, lb[:, e] < srt[:, k - 1], lb[:, e] > srt[:, k - 1])
+    clear = np.abs(lb[:, e] - srt[:, k - 1]) > 1e-12
+    assert np.array_equal(flips[clear], pred[clear])

@@ -40,6 +40,7 @@ from ._lib import (  # noqa: F401
     moe_route,
     moe_route_bwd,
     moe_route_bwd_dense,
+    moe_route_flips,
     moe_router_zloss,
     moe_shuffle_plan,
     workspace_bytes,

@@ -38,7 +38,7 @@ EXPORTED = (
     "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
     "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
     "moe_expert_capacity", "moe_capacity", "moe_router_zloss", "moe_route_bwd_dense",
-    "moe_coselect_cross", "moe_shuffle_plan",
+    "moe_coselect_cross", "moe_shuffle_plan", "moe_route_flips",
 )
 
 
@@ -99,6 +99,7 @@ _SIGNATURES = {
     "moe_route_bwd_dense": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _F32, _F32,
                                    _P, _P, _P, _P, _SZ, _P]),
     "moe_coselect_cross": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P]),
+    "moe_route_flips": (_I32, [_I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_shuffle_plan": (_I32, [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P]),
 }
@@ -487,3 +488,11 @@ def moe_shuffle_plan(T, k, E, G, topk_idx_cur, predictor, placement_next, topk_i
                                 _ptr(stats, "stats", torch.int32), _ptr(workspace, "workspace"),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_shuffle_plan")
+
+
+def moe_route_flips(T, k, E, topk_idx_a, topk_idx_b, flips, n_flips, stream=None):
+    st = lib().moe_route_flips(int(T), int(k), int(E), _ptr(topk_idx_a, "topk_idx_a", torch.int32),
+                               _ptr(topk_idx_b, "topk_idx_b", torch.int32),
+                               _ptr(flips, "flips", torch.int32),
+                               _ptr(n_flips, "n_flips", torch.int32), _stream(stream))
+    _check(st, "moe_route_flips")

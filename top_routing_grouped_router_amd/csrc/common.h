@@ -179,6 +179,8 @@ int capacity_chunks(int64_t T, int32_t G);   // token chunks per block (workspac
 hipError_t launch_router_z(int64_t T, int32_t E, int32_t G, const float* logits, float* group_z,
                            float* ws_partial, hipStream_t s);
 int zloss_chunks(int64_t T, int32_t G);      // token chunks per block (workspace: G chunks floats)
+hipError_t launch_route_flips(int64_t T, int32_t k, int32_t E, const int32_t* a, const int32_t* b,
+                              int32_t* flips, int32_t* n_flips, hipStream_t s);
 
 // index products
 hipError_t launch_coselect(int64_t T, int32_t k, int32_t E, const int32_t* idx, int32_t* W,

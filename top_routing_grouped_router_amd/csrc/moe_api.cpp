@@ -969,4 +969,18 @@ moe_status moe_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G,
                     __func__);
 }
 
+moe_status moe_route_flips(int64_t T, int32_t k, int32_t E, const int32_t* topk_idx_a,
+                           const int32_t* topk_idx_b, int32_t* flips, int32_t* n_flips,
+                           void* stream) {
+  moe_status st = check_index_dims(T, k, E, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(topk_idx_a, T * k);
+  MOE_REQUIRE_PTR(topk_idx_b, T * k);
+  MOE_REQUIRE_PTR(flips, T);
+  MOE_REQUIRE_PTR(n_flips, 1);
+  return hip_status(moe::launch_route_flips(T, k, E, topk_idx_a, topk_idx_b, flips, n_flips,
+                                            static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
 }  // extern "C"

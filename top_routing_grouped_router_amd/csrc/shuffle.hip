@@ -41,29 +41,33 @@ __global__ __launch_bounds__(kThreads) void coselect_cross_kernel(
   }
 }
 
-// M[e1][g] = sum over e2 placed on g of W[e1][e2] (workgroup e1, thread g
-// walks the experts in order); workgroup 0 also clears the outputs that the
+// M[e1][g] = sum over e2 placed on g of W[e1][e2]: workgroup e1, thread e2
+// reads its count (one coalesced row) and adds it to its group's LDS counter
+// (integer atomics: exact); workgroup 0 also clears the outputs that the
 // planner accumulates into.
 __global__ __launch_bounds__(kThreads) void shuffle_mass_kernel(
     const int32_t* __restrict__ W, int32_t E, int32_t G, PlacementArg pl, int32_t* __restrict__ M,
     int32_t* __restrict__ group_tokens, int32_t* __restrict__ stats) {
-  const int e1 = blockIdx.x, g = threadIdx.x;
-  if (g < G) {
-    int32_t s = 0;
-    for (int e2 = 0; e2 < E; ++e2)
-      if (pl.group_of[e2] == g) s += W[static_cast<int64_t>(e1) * E + e2];
-    M[e1 * G + g] = s;
-  }
+  __shared__ int32_t m[kMaxG];
+  const int e1 = blockIdx.x, tid = threadIdx.x;
+  if (tid < G) m[tid] = 0;
+  __syncthreads();
+  for (int e2 = tid; e2 < E; e2 += kThreads)
+    atomicAdd(&m[pl.group_of[e2]], W[static_cast<int64_t>(e1) * E + e2]);
+  __syncthreads();
+  if (tid < G) M[e1 * G + tid] = m[tid];
   if (e1 == 0) {
-    if (g < G) group_tokens[g] = 0;
-    if (g < 2) stats[g] = 0;
+    if (tid < G) group_tokens[tid] = 0;
+    if (tid < 2) stats[tid] = 0;
   }
 }
 
-// One thread per token: score(g) = sum_j M[S_j][g] (64-bit), owner = the first
-// g with the largest score; per-workgroup counts of owners and of local
-// next-layer assignments, then one integer atomic each.
-__global__ __launch_bounds__(kThreads) void shuffle_plan_kernel(
+// One thread per token, 64 tokens per workgroup (many workgroups for one
+// batch): score(g) = sum_j M[S_j][g] (64-bit), owner = the first g with the
+// largest score; per-workgroup counts of owners and of local next-layer
+// assignments, then one integer atomic each.
+constexpr int kPlanThreads = 64;
+__global__ __launch_bounds__(kPlanThreads) void shuffle_plan_kernel(
     const int32_t* __restrict__ cur, const int32_t* __restrict__ nxt,
     const int32_t* __restrict__ M, int64_t T, int32_t k, int32_t E, int32_t G, PlacementArg pl,
     int32_t* __restrict__ owner, int32_t* __restrict__ group_tokens,
@@ -72,11 +76,11 @@ __global__ __launch_bounds__(kThreads) void shuffle_plan_kernel(
   __shared__ int32_t cnt[kMaxG];
   __shared__ int32_t loc[2];
   const int tid = threadIdx.x;
-  for (int i = tid; i < E * G; i += kThreads) sM[i] = M[i];
+  for (int i = tid; i < E * G; i += kPlanThreads) sM[i] = M[i];
   if (tid < G) cnt[tid] = 0;
   if (tid < 2) loc[tid] = 0;
   __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + tid;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPlanThreads + tid;
   if (t < T) {
     int32_t ids[16];
 #pragma unroll
@@ -138,8 +142,9 @@ hipError_t launch_shuffle_plan(int64_t T, int32_t k, int32_t E, int32_t G, const
                      group_tokens, stats);
   if (T > 0) {
     const size_t lds = static_cast<size_t>(E) * G * sizeof(int32_t);
-    hipLaunchKernelGGL(shuffle_plan_kernel, dim3((T + kThreads - 1) / kThreads), dim3(kThreads),
-                       lds, s, cur, nxt, ws_mass, T, k, E, G, pl, owner, group_tokens, stats);
+    hipLaunchKernelGGL(shuffle_plan_kernel, dim3((T + kPlanThreads - 1) / kPlanThreads),
+                       dim3(kPlanThreads), lds, s, cur, nxt, ws_mass, T, k, E, G, pl, owner,
+                       group_tokens, stats);
   }
   return hipGetLastError();
 }

@@ -200,7 +200,53 @@ __global__ __launch_bounds__(256) void router_z_fold_kernel(const float* __restr
   }
 }
 
+// Routing flips between two runs ("MoE Pretraining: Parallelism Layout
+// Changes the Model, Not Quality", Finding 3): flips[t] = 1 when token t's
+// chosen expert sets differ (slot order ignored): each set becomes a 256-bit
+// mask.  The count is a workgroup sum plus one integer atomic (exact).
+__global__ __launch_bounds__(256) void route_flips_kernel(const int32_t* __restrict__ a,
+                                                          const int32_t* __restrict__ b,
+                                                          int64_t T, int32_t k, int32_t E,
+                                                          int32_t* __restrict__ flips,
+                                                          int32_t* __restrict__ n_flips) {
+  __shared__ int32_t wsum[4];
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  int32_t f = 0;
+  if (t < T) {
+    unsigned long long ma[4] = {0ull, 0ull, 0ull, 0ull}, mb[4] = {0ull, 0ull, 0ull, 0ull};
+    for (int j = 0; j < k; ++j) {
+      const int32_t ea = a[t * k + j], eb = b[t * k + j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (ea >= 0 && ea < E && (ea >> 6) == q) ma[q] |= 1ull << (ea & 63);
+        if (eb >= 0 && eb < E && (eb >> 6) == q) mb[q] |= 1ull << (eb & 63);
+      }
+    }
+    f = ((ma[0] ^ mb[0]) | (ma[1] ^ mb[1]) | (ma[2] ^ mb[2]) | (ma[3] ^ mb[3])) ? 1 : 0;
+    flips[t] = f;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int32_t c = __popcll(__ballot(f != 0));
+  if (lane == 0) wsum[w] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int32_t s = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    if (s) atomicAdd(n_flips, s);
+  }
+}
+
+__global__ void zero_one_kernel(int32_t* p) { *p = 0; }
+
 }  // namespace
+
+hipError_t launch_route_flips(int64_t T, int32_t k, int32_t E, const int32_t* a, const int32_t* b,
+                              int32_t* flips, int32_t* n_flips, hipStream_t s) {
+  hipLaunchKernelGGL(zero_one_kernel, dim3(1), dim3(1), 0, s, n_flips);
+  if (T > 0)
+    hipLaunchKernelGGL(route_flips_kernel, dim3((T + 255) / 256), dim3(256), 0, s, a, b, T, k, E,
+                       flips, n_flips);
+  return hipGetLastError();
+}
 
 int capacity_chunks(int64_t T, int32_t G) {
   const int64_t n = G > 0 ? T / G : 0;
