@@ -136,3 +136,21 @@ def test_shuffle_plan_rejects_bad_arguments():
     with pytest.raises(M.MoEError):   # workspace too small
         M.moe_shuffle_plan(T, k, E, G, cur, W, list(O.placement_contiguous(E, G)), None, owner,
                            gt, st, ws[:16])
+
+
+def test_shuffle_and_flips_on_an_empty_batch():
+    _announce("shuffle/flips T=0")
+    E, k, G = 8, 2, 4
+    e = torch.empty((1, k), dtype=torch.int32, device="cuda")[:0]
+    W = torch.full((E, E), -1, dtype=torch.int32, device="cuda")
+    M.moe_coselect_cross(0, k, E, e, e, W)
+    gt = torch.full((G,), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    owner = torch.empty(1, dtype=torch.int32, device="cuda")[:0]
+    ws = torch.empty(E * G * 4, dtype=torch.uint8, device="cuda")
+    M.moe_shuffle_plan(0, k, E, G, e, W, list(O.placement_contiguous(E, G)), e, owner, gt, st, ws)
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    M.moe_route_flips(0, k, E, e, e, owner, n)
+    torch.cuda.synchronize()
+    assert np.all(host(W) == 0) and np.all(host(gt) == 0) and np.all(host(st) == 0)
+    assert int(host(n)[0]) == 0

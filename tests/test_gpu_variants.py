@@ -285,3 +285,25 @@ def test_layer_step_with_capacity_and_losses(name):
         assert err <= tol, (key, err)
     # dropped slots: no gradient through the combine
     assert np.all(host(layer.dgate)[o_f["kept_idx"] < 0] == 0.0)
+
+
+def test_variants_on_an_empty_batch():
+    """T = 0: nothing dropped, zero z-loss values, a zero router weight gradient."""
+    _announce("variants T=0")
+    E, k, d, G = 8, 2, 64, 2
+    dims = M.make_dims(0, d, E, 64, k, torch.bfloat16)
+    ws = M.alloc_workspace(dims, G)
+    empty_i = torch.empty((1, k), dtype=torch.int32, device="cuda")[:0]
+    dropped = torch.full((G,), -1, dtype=torch.int32, device="cuda")
+    M.moe_capacity(dims, G, 4, empty_i, torch.empty_like(empty_i), dropped, ws)
+    dwr = torch.full((E, d), float("nan"), device="cuda")
+    e_f = torch.empty((1, k), device="cuda")[:0]
+    M.moe_route_bwd_dense(dims, torch.empty((1, d), dtype=torch.bfloat16, device="cuda")[:0],
+                          torch.zeros((E, d), device="cuda"),
+                          torch.empty((1, E), device="cuda")[:0], empty_i, e_f, e_f, empty_i,
+                          None, G, torch.zeros((G, E), dtype=torch.int32, device="cuda"), 0.01,
+                          0.001, torch.empty((1, d), dtype=torch.bfloat16, device="cuda")[:0],
+                          dwr, None, ws)
+    torch.cuda.synchronize()
+    assert np.all(host(dropped) == 0)
+    assert np.all(host(dwr) == 0.0)
