@@ -1127,26 +1127,15 @@ __global__ __launch_bounds__(Cfg<true>::THREADS, 2) void tile_rows_kernel(Args g
 }
 
 // ------------------------------------------------------------------ direct-to-LDS big tile
-// Row modes with k-contiguous operands (UP, DOWN) at the big tile, one tile
-// per workgroup: operand tiles go from HBM/L2 straight into a 4-stage LDS ring
-// (K step 32) by buffer loads with the LDS destination (no register staging),
-// issued three steps ahead.  Each wavefront instruction fills 1 KB of LDS:
-// 16 rows of 64 bytes, lane l taking row l / 4 and physical chunk l % 4; the
-// global address carries the swizzle (logical chunk = physical ^ key(row)), so
-// the fragment reads below are conflict-free.  The compiler does not track
-// these LDS writes, so the step waits on the vector-memory counter explicitly
-// and joins the workgroup with a plain s_barrier (a fenced barrier would also
-// drain the prefetch).
-#ifndef MOE_ROWS_NST
-#define MOE_ROWS_NST 4
-#endif
+// Row modes at the big tile, one tile per workgroup: operand tiles go from
+// HBM/L2 straight into LDS by buffer loads with the LDS destination (no
+// register staging).  Each wavefront instruction fills 1 KB of LDS; the global
+// addresses carry the swizzle of the LDS layout (logical chunk = physical ^
+// key(row)), so the fragment reads are conflict-free.  The compiler does not
+// track these LDS writes, so each step waits on the vector-memory counter
+// explicitly and joins the workgroup with a plain s_barrier (a fenced barrier
+// would also drain the prefetch).
 namespace dma {
-constexpr int BM = 256, BN = 256, BKS = 32, NST = 4, NT = 512, WAVES_N = 4, FM = 4, FN = 2;
-constexpr int kStage = (BM + BN) * BKS;   // elements per stage
-// element offset of 16-byte chunk `chunk` (of 4) in row r of a 64-byte-row tile
-__device__ __forceinline__ int swz32(int r, int chunk) {
-  return r * BKS + ((chunk ^ ((r >> 2) & 3)) << 3);
-}
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, static_cast<int>(voff), 0, 0, 0);
@@ -1159,31 +1148,29 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace dma
 
-template <int MODE>
-__global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
-  using namespace dma;
-  static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
-  // a ring of kNst stages (4: 128 KB, three steps in flight; 5 fills all
-  // 160 KB of LDS but measured slower, so the loads are not waiting on depth)
-  constexpr int kNst = MOE_ROWS_NST;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kNst * kStage];
+// The big UP/DOWN tile with 64-wide k steps: each row of a stage is 128 bytes,
+// a whole cache line, so every line of A and B is requested from L2 once (with
+// 32-wide steps each line is requested twice, half per step: measured 2.3x the
+// requests and 6% slower).  Two stages of 64 KB; the 16-byte chunks of a row
+// are XORed with (row >> 1) & 7, so any 16 consecutive rows read at one
+// logical chunk (a fragment read) hit distinct banks; the DMA writes carry
+// the same swizzle in their global addresses.
+namespace dma64 {
+constexpr int BM = 256, BN = 256, BKS = 64, NST = 2, NT = 512, WAVES_N = 4, FM = 4, FN = 2;
+constexpr int kStage = (BM + BN) * BKS;   // elements per stage (64 KB)
+}  // namespace dma64
 
-#ifdef MOE_TRACE
-#define MOE_TILE_MARK(i) \
-  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) moe_trace_data[blockIdx.x * kTraceSlots + 500 + (i)] = wall_clock64()
-#else
-#define MOE_TILE_MARK(i) ((void)0)
-#endif
-  MOE_TILE_MARK(0);
+template <int MODE>
+__global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
+  using namespace dma64;
+  static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[NST * kStage];
+  __shared__ int tile_info[3];
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
   const int nt = flat - row_tile * g.n_tiles_n;
   int e, m0, mend;
-  // the tile lookup's three results sit at the end of the last stage, which
-  // no DMA writes before every wavefront has passed two loop barriers
-  int* const scratch = reinterpret_cast<int*>(lds + kNst * kStage) - 4;
-  if (!find_row_tile_at<BM>(scratch, g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
-  MOE_TILE_MARK(1);
+  if (!find_row_tile_at<BM>(tile_info, g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   mend = __builtin_amdgcn_readfirstlane(mend);
@@ -1199,14 +1186,14 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // this wavefront's DMA instructions: A rows 32 wave + [0, 32) and B rows
-  // 32 wave + [0, 32), 16 rows per instruction.  A row r is expert row m0 + r,
-  // or with a gather table X row x_rows[m0 + r] (rows past the expert read 0)
+  // 32 wave + [0, 32), 8 rows of 128 bytes per instruction (lane l: row
+  // + l / 8, physical chunk l % 8, logical chunk (l % 8) ^ ((row >> 1) & 7))
   const bool gather = (MODE == UP) && g.x_rows != nullptr;
-  uint32_t voa[2], vob[2];
+  uint32_t voa[4], vob[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = wave * 32 + u * 16 + (lane >> 2);
-    const int logical = (lane & 3) ^ ((row >> 2) & 3);
+  for (int u = 0; u < 4; ++u) {
+    const int row = wave * 32 + u * 8 + (lane >> 3);
+    const int logical = (lane & 7) ^ ((row >> 1) & 7);
     if (gather) {
       const uint32_t src = static_cast<uint32_t>(g.x_rows[min(m0 + row, mend - 1)]);
       voa[u] = (m0 + row < mend) ? (src * lda + logical * 8) * 2 : kOutOfRange;
@@ -1221,66 +1208,58 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   const bf16_t* bbase;
   int b_bytes;
   if constexpr (MODE == UP) {
-    // wavefronts 0-3 fill B rows [0, 128) from W1, 4-7 rows [128, 256) from W3
     bbase = (wave < 4 ? g.b0 : g.b1) + e * E_fd + static_cast<int64_t>(n0) * d;
     b_bytes = kUpHalf * d * 2;
   } else {
     bbase = g.b0 + e * E_fd + static_cast<int64_t>(n0) * f;
     b_bytes = (d - n0) * f * 2;
   }
-  auto issue = [&](int kt) {   // step kt into stage kt % kNst
-    bf16_t* As = lds + (kt % kNst) * kStage;
+  auto issue = [&](int kt) {   // step kt into stage kt % 2
+    bf16_t* As = lds + (kt & 1) * kStage;
     bf16_t* Bs = As + BM * BKS;
     const int k0 = kt * BKS;
     const auto ra = rsrc_at(abase + k0, a_rows_bytes - k0 * 2);
     const auto rb = rsrc_at(bbase + k0, b_bytes - k0 * 2);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma16(ra, As + (wave * 32 + u * 16) * BKS, voa[u]);
+    for (int u = 0; u < 4; ++u) dma::dma16(ra, As + (wave * 32 + u * 8) * BKS, voa[u]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma16(rb, Bs + (wave * 32 + u * 16) * BKS, vob[u]);
+    for (int u = 0; u < 4; ++u) dma::dma16(rb, Bs + (wave * 32 + u * 8) * BKS, vob[u]);
   };
 
   AccT<true> acc;
   zero_acc<true>(acc);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int r = lane & 31, gq = lane >> 5;
-  // byte addresses (within the stage) of this lane's fragment rows for the two
-  // 16-wide sub-steps; fragment i / j adds i * 32 / j * 128 rows (constant)
-  const int key = (r >> 2) & 3;
-  uint32_t a_addr[2], b_addr[2];
+  // byte addresses (within the stage) of this lane's fragment rows for the
+  // four 16-wide sub-steps; fragment i / j adds i * 32 / j * 128 rows, which
+  // keeps (row >> 1) & 7 and so the swizzle
+  uint32_t a_addr[4], b_addr[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int pc = (2 * kk + gq) ^ key;
+  for (int kk = 0; kk < 4; ++kk) {
+    const int pc = (2 * kk + gq) ^ ((r >> 1) & 7);
     a_addr[kk] = ((wm * 32 * FM + r) * BKS + pc * 8) * 2;
     b_addr[kk] = (BM * BKS + (wn * 32 + r) * BKS + pc * 8) * 2;
   }
-  // LDS byte offset of the ring (an address-space-3 pointer is the offset)
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)lds));
-  // Fragment reads overlap the MFMAs: per step kt two asm blocks, each six
-  // fragment reads interleaved with eight MFMAs and ending by waiting for its
-  // reads: block 1 reads the second 16-wide sub-step (kk = 1) of step kt while
-  // the kk = 0 MFMAs of step kt run; block 2, after the barrier that releases
-  // stage kt + 1, reads kk = 0 of step kt + 1 while the kk = 1 MFMAs of step kt
-  // run.  In flight: DMA of steps kt + 2 and kt + 3.
   typedef float f32x16v __attribute__((ext_vector_type(16)));
   f32x16v c00 = acc[0][0], c01 = acc[0][1], c10 = acc[1][0], c11 = acc[1][1];
   f32x16v c20 = acc[2][0], c21 = acc[2][1], c30 = acc[3][0], c31 = acc[3][1];
-  bf16x8 p0[6], p1[6];   // sub-step fragments: a 0-3, b 4-5 (kk = 0 in p0, kk = 1 in p1)
+  bf16x8 p0[6], p1[6];
 #define MOE_MF(c, b, a) "v_mfma_f32_32x32x16_bf16 " c ", " b ", " a ", " c "\n\t"
 #define MOE_RD(o, addr, off) "ds_read_b128 " o ", " addr " offset:" off "\n\t"
   // reads six fragments at (aaddr, baddr) into `out` while running the eight
-  // MFMAs of the fragments `in`
+  // MFMAs of the fragments `in`, and waits for its reads
   auto half_asm = [&](const bf16x8 (&in)[6], bf16x8 (&out)[6], uint32_t aaddr, uint32_t baddr) {
     asm volatile(
-        MOE_RD("%8", "%20", "0")      MOE_MF("%0", "%18", "%14")
-        MOE_RD("%9", "%20", "2048")   MOE_MF("%1", "%19", "%14")
-        MOE_RD("%10", "%20", "4096")  MOE_MF("%2", "%18", "%15")
-        MOE_RD("%11", "%20", "6144")  MOE_MF("%3", "%19", "%15")
-        MOE_RD("%12", "%21", "0")     MOE_MF("%4", "%18", "%16")
-        MOE_RD("%13", "%21", "8192")  MOE_MF("%5", "%19", "%16")
-                                      MOE_MF("%6", "%18", "%17")
-                                      MOE_MF("%7", "%19", "%17")
+        MOE_RD("%8", "%20", "0")       MOE_MF("%0", "%18", "%14")
+        MOE_RD("%9", "%20", "4096")    MOE_MF("%1", "%19", "%14")
+        MOE_RD("%10", "%20", "8192")   MOE_MF("%2", "%18", "%15")
+        MOE_RD("%11", "%20", "12288")  MOE_MF("%3", "%19", "%15")
+        MOE_RD("%12", "%21", "0")      MOE_MF("%4", "%18", "%16")
+        MOE_RD("%13", "%21", "16384")  MOE_MF("%5", "%19", "%16")
+                                       MOE_MF("%6", "%18", "%17")
+                                       MOE_MF("%7", "%19", "%17")
         "s_waitcnt lgkmcnt(0)"
         : "+v"(c00), "+v"(c01), "+v"(c10), "+v"(c11), "+v"(c20), "+v"(c21), "+v"(c30),
           "+v"(c31), "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]),
@@ -1294,57 +1273,50 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
   auto read_p = [&](bf16x8 (&out)[6], uint32_t aaddr, uint32_t baddr) {
     asm volatile(
         "ds_read_b128 %0, %6 offset:0\n\t"
-        "ds_read_b128 %1, %6 offset:2048\n\t"
-        "ds_read_b128 %2, %6 offset:4096\n\t"
-        "ds_read_b128 %3, %6 offset:6144\n\t"
+        "ds_read_b128 %1, %6 offset:4096\n\t"
+        "ds_read_b128 %2, %6 offset:8192\n\t"
+        "ds_read_b128 %3, %6 offset:12288\n\t"
         "ds_read_b128 %4, %7 offset:0\n\t"
-        "ds_read_b128 %5, %7 offset:8192\n\t"
+        "ds_read_b128 %5, %7 offset:16384\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
           "=&v"(out[5])
         : "v"(aaddr), "v"(baddr)
         : "memory");
   };
-  auto sbase = [&](int kt) { return lds_base + (kt % kNst) * kStage * 2; };
-  // prologue: steps 0 .. kNst - 2 in flight (past-the-end steps reload the
-  // last); kk = 0 fragments of step 0 read once it has landed
-#pragma unroll
-  for (int q = 0; q < kNst - 1; ++q) issue(min(q, nk - 1));
-  dma::wait_vm<4 * (kNst - 2)>();
+  auto sbase = [&](int kt) { return lds_base + (kt & 1) * kStage * 2; };
+  // prologue: steps 0 and 1 in flight; kk = 0 fragments of step 0 once landed
+  issue(0);
+  if (nk > 1) {
+    issue(1);
+    dma::wait_vm<8>();
+  } else {
+    dma::wait_vm<0>();
+  }
   __builtin_amdgcn_s_barrier();
   read_p(p0, sbase(0) + a_addr[0], sbase(0) + b_addr[0]);
-  MOE_TILE_MARK(2);
-#ifdef MOE_TRACE
-  int tslot = 0;
-#endif
+  // step kt: sub-steps 0-2 of stage kt while reading 1-3; then the barrier
+  // that sees step kt + 1 landed everywhere and stage kt read by everyone,
+  // the DMA of step kt + 2 into stage kt, and sub-step 3 while reading
+  // sub-step 0 of step kt + 1
   for (int kt = 0; kt < nk; ++kt) {
     const uint32_t sc = sbase(kt), sn = sbase(kt + 1);
-    half_asm(p0, p1, sc + a_addr[1], sc + b_addr[1]);   // kk = 0 MFMAs; read kk = 1
-#ifdef MOE_TRACE
-    if (kt < 48) MOE_TRACE_MARK(tslot, 1ull << 60);
-#endif
-    dma::wait_vm<4 * (kNst - 3)>();   // this wavefront's loads of step kt + 1 have landed
-    __builtin_amdgcn_s_barrier();   // everyone's have; everyone is done with step kt - 1
-#ifdef MOE_TRACE
-    if (kt < 48) MOE_TRACE_MARK(tslot, 2ull << 60);
-#endif
-    issue(min(kt + kNst - 1, nk - 1));   // into the stage last read during step kt - 1
-    half_asm(p1, p0, sn + a_addr[0], sn + b_addr[0]);   // kk = 1 MFMAs; read next kk = 0
-#ifdef MOE_TRACE
-    if (kt < 48) MOE_TRACE_MARK(tslot, 3ull << 60);
-#endif
+    half_asm(p0, p1, sc + a_addr[1], sc + b_addr[1]);
+    half_asm(p1, p0, sc + a_addr[2], sc + b_addr[2]);
+    half_asm(p0, p1, sc + a_addr[3], sc + b_addr[3]);
+    dma::wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    half_asm(p1, p0, sn + a_addr[0], sn + b_addr[0]);
   }
-  // the last MFMAs may still be writing: cover the longest MFMA-to-VALU
-  // read-after-write distance before the accumulators are read
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
   acc[2][0] = c20; acc[2][1] = c21; acc[3][0] = c30; acc[3][1] = c31;
-  MOE_TILE_MARK(3);
   dma::wait_vm<0>();
   __syncthreads();
 
-  // epilogue: the whole 256 x 256 tile staged as bf16 over the ring (128 KB),
-  // 16-byte chunks XOR-swizzled by row, then coalesced 16-byte stores
+  // epilogue: the whole 256 x 256 tile staged as bf16 over the two stages
+  // (128 KB), 16-byte chunks XOR-swizzled by row, then coalesced stores
   bf16_t* out = lds;
   {
     int skey;
@@ -1359,7 +1331,7 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
     return *reinterpret_cast<const uint4*>(out + rr * BN + ((c ^ (rr & 15)) << 3));
   };
   if constexpr (MODE == UP) {
-    constexpr int kCh = kUpHalf / 8;   // 16 chunks of a per row
+    constexpr int kCh = kUpHalf / 8;
     for (int v = tid; v < BM * kCh; v += NT) {
       const int rr = v / kCh, c = v % kCh;
       if (rr >= rows) continue;
@@ -1384,11 +1356,9 @@ __global__ __launch_bounds__(dma::NT, 1) void dma_rows_kernel(Args g) {
           chunk_at(rr, c);
     }
   }
-  MOE_TILE_MARK(4);
-#undef MOE_TILE_MARK
 }
 
-// Weight gradients with the big tile on the same 4-stage LDS ring: both
+// Weight gradients with the big tile on a 4-stage LDS ring of 32-row steps: both
 // operands are row-major over the expert's rows p ([p][m] and [p][n]), so a
 // stage holds them as they lie in HBM, [32 rows][256 columns] (512-byte rows),
 // filled by buffer loads with the LDS destination, and the MFMA fragments
@@ -1618,22 +1588,20 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   }
 }
 
-// Input gradients with the big tile (DGRAD_DOWN: dh = dy_perm W2[e];
-// DGRAD_UP: dx_perm = da W1[e] + db W3[e]) on the LDS-DMA ring.  Stage = A
-// [256 rows][32 k] (64-byte rows, as in dma_rows_kernel, fragments read by an
-// asm block interleaved with the MFMAs) + B [32 k][256 n] (512-byte rows as
-// they lie in W, fragments from the transposing read, as in
-// wgrad_dma_kernel).  Four distinct stage arrays; the step count is padded to
-// a multiple of 4 with zero steps (empty resources).
+// Input gradients with the big tile and 64-wide k steps (whole 128-byte lines
+// of the k-contiguous A rows, as in dma_rows_kernel).  Stage = A [256 rows]
+// [64 k] (128-byte rows, chunks XORed with (row >> 1) & 7) + B [64 k][256 n]
+// (512-byte rows as they lie in W); two distinct stage arrays of 64 KB, the
+// step count padded to even with a zero step.
 template <int MODE>
-__global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
-  using namespace dma;
+__global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
+  using namespace dma64;
+  using dma::dma16;
+  using dma::wait_vm;
   static_assert(MODE == DGRAD_DOWN || MODE == DGRAD_UP, "dgrad modes");
   constexpr int kAB = BM * BKS;   // A part of a stage (elements)
   __shared__ __attribute__((aligned(16))) bf16_t st0[kStage];
   __shared__ __attribute__((aligned(16))) bf16_t st1[kStage];
-  __shared__ __attribute__((aligned(16))) bf16_t st2[kStage];
-  __shared__ __attribute__((aligned(16))) bf16_t st3[kStage];
 
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
@@ -1655,13 +1623,13 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  uint32_t voa[2], vob[2];
+  uint32_t voa[4], vob[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = wave * 32 + u * 16 + (lane >> 2);   // A: 16 rows of 64 B
-    const int logical = (lane & 3) ^ ((row >> 2) & 3);
+  for (int u = 0; u < 4; ++u) {
+    const int row = wave * 32 + u * 8 + (lane >> 3);    // A: 8 rows of 128 B
+    const int logical = (lane & 7) ^ ((row >> 1) & 7);
     voa[u] = (row * lda + logical * 8) * 2;
-    const int brow = wave * 4 + u * 2 + (lane >> 5);    // B: 2 rows of 512 B
+    const int brow = wave * 8 + u * 2 + (lane >> 5);    // B: 2 rows of 512 B
     const int blog = (lane & 31) ^ (4 * (brow & 3));
     vob[u] = (n0 + blog * 8 < Ndim) ? static_cast<uint32_t>((brow * ldb + blog * 8) * 2)
                                     : kOutOfRange;
@@ -1682,17 +1650,17 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
     const auto ra = rsrc_at(abase, live ? ((mend - m0) * lda - k0) * 2 : 0);
     const auto rb = rsrc_at(wbase, live ? ((Kh - k0) * ldb - n0) * 2 : 0);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma16(ra, As + (wave * 32 + u * 16) * BKS, voa[u]);
+    for (int u = 0; u < 4; ++u) dma16(ra, As + (wave * 32 + u * 8) * BKS, voa[u]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma16(rb, Bs + (wave * 4 + u * 2) * BN, vob[u]);
+    for (int u = 0; u < 4; ++u) dma16(rb, Bs + (wave * 8 + u * 2) * BN, vob[u]);
   };
 
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int r = lane & 31, gq = lane >> 5;
-  const int key = (r >> 2) & 3;
-  uint32_t a_addr[2];
+  const int key = (r >> 1) & 7;
+  uint32_t a_addr[4];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int kk = 0; kk < 4; ++kk)
     a_addr[kk] = ((wm * 32 * FM + r) * BKS + (((2 * kk + gq) ^ key) * 8)) * 2;
   const int G = lane >> 4, sl = lane & 15;
   const int row0 = 8 * (G >> 1) + (sl >> 2);
@@ -1718,9 +1686,9 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   auto read_a = [&](bf16x8 (&fa)[FM], uint32_t addr) {
     asm volatile(
         "ds_read_b128 %0, %4 offset:0\n\t"
-        "ds_read_b128 %1, %4 offset:2048\n\t"
-        "ds_read_b128 %2, %4 offset:4096\n\t"
-        "ds_read_b128 %3, %4 offset:6144\n\t"
+        "ds_read_b128 %1, %4 offset:4096\n\t"
+        "ds_read_b128 %2, %4 offset:8192\n\t"
+        "ds_read_b128 %3, %4 offset:12288\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(fa[0]), "=&v"(fa[1]), "=&v"(fa[2]), "=&v"(fa[3])
         : "v"(addr)
@@ -1733,10 +1701,10 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   auto mma_read = [&](const bf16x8 (&ain)[FM], const bf16x8 (&bin)[FN], bf16x8 (&aout)[FM],
                       uint32_t addr) {
     asm volatile(
-        MOE_RD("%8", "0")     MOE_MF("%0", "%16", "%12")
-        MOE_RD("%9", "2048")  MOE_MF("%1", "%17", "%12")
-        MOE_RD("%10", "4096") MOE_MF("%2", "%16", "%13")
-        MOE_RD("%11", "6144") MOE_MF("%3", "%17", "%13")
+        MOE_RD("%8", "0")      MOE_MF("%0", "%16", "%12")
+        MOE_RD("%9", "4096")   MOE_MF("%1", "%17", "%12")
+        MOE_RD("%10", "8192")  MOE_MF("%2", "%16", "%13")
+        MOE_RD("%11", "12288") MOE_MF("%3", "%17", "%13")
                               MOE_MF("%4", "%16", "%14")
                               MOE_MF("%5", "%17", "%14")
                               MOE_MF("%6", "%16", "%15")
@@ -1750,35 +1718,37 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   };
 #undef MOE_MF
 #undef MOE_RD
-  auto sync_stage = [&]() {
-    dmaw::mem_fence_compiler();
-    wait_vm<4>();
-    __builtin_amdgcn_s_barrier();
-    dmaw::mem_fence_compiler();
-  };
   issue(st0, 0);
   issue(st1, 1);
-  issue(st2, 2);
   dmaw::mem_fence_compiler();
   wait_vm<8>();
   __builtin_amdgcn_s_barrier();
   dmaw::mem_fence_compiler();
   read_b(fb0, st0, 0);
   read_a(fa0, base_of(st0) + a_addr[0]);
-  auto step = [&](int kt, const bf16_t* cur, const bf16_t* nxt, bf16_t* fill) {
+  // step kt: sub-steps 0-2 of stage kt while reading 1-3 (each asm block ends
+  // by waiting for every LDS read issued before it), the barrier that sees
+  // step kt + 1 landed and stage kt read by everyone, the DMA of step kt + 2
+  // into stage kt, then sub-step 3 while reading sub-step 0 of step kt + 1
+  auto step = [&](int kt, bf16_t* cur, const bf16_t* nxt) {
     read_b(fb1, cur, 1);
-    mma_read(fa0, fb0, fa1, base_of(cur) + a_addr[1]);   // kk = 0 MFMAs; A of kk = 1
-    sync_stage();                                         // stage kt + 1 ready
-    issue(fill, kt + 3);                                  // into stage (kt - 1) % 4
+    mma_read(fa0, fb0, fa1, base_of(cur) + a_addr[1]);
+    read_b(fb0, cur, 2);
+    mma_read(fa1, fb1, fa0, base_of(cur) + a_addr[2]);
+    read_b(fb1, cur, 3);
+    mma_read(fa0, fb0, fa1, base_of(cur) + a_addr[3]);
+    dmaw::mem_fence_compiler();
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    dmaw::mem_fence_compiler();
+    issue(cur, kt + 2);
     read_b(fb0, nxt, 0);
-    mma_read(fa1, fb1, fa0, base_of(nxt) + a_addr[0]);   // kk = 1 MFMAs; A of next kk = 0
+    mma_read(fa1, fb1, fa0, base_of(nxt) + a_addr[0]);
   };
-  const int nk4 = (nk + 3) & ~3;
-  for (int kt = 0; kt < nk4; kt += 4) {
-    step(kt, st0, st1, st3);
-    step(kt + 1, st1, st2, st0);
-    step(kt + 2, st2, st3, st1);
-    step(kt + 3, st3, st0, st2);
+  const int nk2 = (nk + 1) & ~1;
+  for (int kt = 0; kt < nk2; kt += 2) {
+    step(kt, st0, st1);
+    step(kt + 1, st1, st0);
   }
   dmaw::mem_fence_compiler();
   wait_vm<0>();
@@ -1789,14 +1759,10 @@ __global__ __launch_bounds__(dma::NT, 1) void dgrad_dma_kernel(Args g) {
   acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
   acc[2][0] = c20; acc[2][1] = c21; acc[3][0] = c30; acc[3][1] = c31;
 
-  // epilogue: bf16 tile (dh or dx) staged over the ring, rows [64 q, 64 q + 64)
-  // in stage q, chunks XORed by row; DGRAD_DOWN then applies da = dh b silu'(a),
-  // db = dh silu(a) with the saved a, b
-  auto row_ptr = [&](int m) -> bf16_t* {
-    const int q = m >> 6;
-    bf16_t* base = (q == 0) ? st0 : (q == 1) ? st1 : (q == 2) ? st2 : st3;
-    return base + (m & 63) * BN;
-  };
+  // epilogue: bf16 tile (dh or dx) staged over the two stages, rows
+  // [128 q, 128 q + 128) in stage q, chunks XORed by row; DGRAD_DOWN then
+  // applies da = dh b silu'(a), db = dh silu(a) with the saved a, b
+  auto row_ptr = [&](int m) -> bf16_t* { return ((m >> 7) ? st1 : st0) + (m & 127) * BN; };
   {
     int skey;
     asm volatile("v_mov_b32 %0, %1" : "=v"(skey) : "v"(static_cast<int>(threadIdx.x & 15)));
@@ -2467,9 +2433,9 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
   g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
 #ifndef MOE_NO_DMA
   if constexpr (MODE == UP || MODE == DOWN) {
-    hipLaunchKernelGGL((dma_rows_kernel<MODE>), dim3(g.grid_pad), dim3(dma::NT), 0, s, g);
+    hipLaunchKernelGGL((dma_rows_kernel<MODE>), dim3(g.grid_pad), dim3(dma64::NT), 0, s, g);
   } else {
-    hipLaunchKernelGGL((dgrad_dma_kernel<MODE>), dim3(g.grid_pad), dim3(dma::NT), 0, s, g);
+    hipLaunchKernelGGL((dgrad_dma_kernel<MODE>), dim3(g.grid_pad), dim3(dma64::NT), 0, s, g);
   }
   return hipGetLastError();
 #endif
