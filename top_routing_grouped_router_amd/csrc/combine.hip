@@ -16,30 +16,45 @@ namespace {
 constexpr int kThreads = 256;
 
 // out[t] = sum_j gate[t,j] * rows[pos[t,j]]; one thread per 16-byte piece.
-template <typename TA>
+// K is the compile-time k (0: runtime k <= 16); every load of a piece (its k
+// positions and gates, then its k rows, clamped in bounds) is issued before
+// any is used, so a piece costs one memory latency rather than one per slot.
+template <typename TA, int K>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restrict__ rows,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ gate,
                                                            uint4* __restrict__ out, int64_t T,
                                                            int32_t vpr, int32_t k) {
   constexpr int kPer = Act<TA>::kPer16B;
+  constexpr int KM = K > 0 ? K : 16;
+  const int kk = K > 0 ? K : k;
   const int64_t total = T * vpr;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total;
        v += stride) {
     const int64_t t = v / vpr;
     const int32_t c = static_cast<int32_t>(v - t * vpr);
+    int32_t p[KM];
+    float g[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int64_t q = t * kk + min(j, kk - 1);
+      p[j] = (j < kk) ? pos[q] : -1;
+      g[j] = gate ? gate[q] : 1.0f;
+    }
+    uint4 rv[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) rv[j] = rows[static_cast<int64_t>(max(p[j], 0)) * vpr + c];
     float acc[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = pos[t * k + j];
-      if (p < 0) continue;
-      const float g = gate ? gate[t * k + j] : 1.0f;
-      float r[kPer];
-      unpack16(rows[p * vpr + c], r, TA{});
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(g, r[i], acc[i]);
+    for (int j = 0; j < KM; ++j) {
+      if (p[j] < 0) continue;
+      float r[kPer];
+      unpack16(rv[j], r, TA{});
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(g[j], r[i], acc[i]);
     }
     out[v] = pack16(acc, TA{});
   }
@@ -110,14 +125,27 @@ hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* p
   const int32_t vpr = dm.d * elem / 16;
   const int64_t total = dm.T * vpr;
   const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
-  if (dm.act == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(kThreads), 0, s,
-                       static_cast<const uint4*>(rows), pos, gate, static_cast<uint4*>(out),
-                       dm.T, vpr, dm.k);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(kThreads), 0, s,
-                       static_cast<const uint4*>(rows), pos, gate, static_cast<uint4*>(out),
-                       dm.T, vpr, dm.k);
+  const uint4* rv = static_cast<const uint4*>(rows);
+  uint4* ov = static_cast<uint4*>(out);
+#define MOE_C(TA, KC)                                                                         \
+  hipLaunchKernelGGL((combine_kernel<TA, KC>), dim3(blocks), dim3(kThreads), 0, s, rv, pos, gate, \
+                     ov, dm.T, vpr, dm.k)
+#define MOE_C_K(TA)                  \
+  switch (dm.k) {                    \
+    case 1: MOE_C(TA, 1); break;     \
+    case 2: MOE_C(TA, 2); break;     \
+    case 4: MOE_C(TA, 4); break;     \
+    case 6: MOE_C(TA, 6); break;     \
+    case 8: MOE_C(TA, 8); break;     \
+    default: MOE_C(TA, 0); break;    \
+  }
+  if (dm.act == MOE_BF16) {
+    MOE_C_K(bf16_t)
+  } else {
+    MOE_C_K(float)
+  }
+#undef MOE_C_K
+#undef MOE_C
   return hipGetLastError();
 }
 
