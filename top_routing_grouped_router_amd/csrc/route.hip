@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 // top-k, gates, margin and the full softmax run there with 16-lane shuffles.
 // ---------------------------------------------------------------------------
 constexpr int kMTile = 64;       // tokens per workgroup
-constexpr int kMBK = 32;         // k chunk
+constexpr int kMBK = 64;         // k chunk (two 32-wide MFMA sub-steps)
 constexpr int kMLd = kMBK + 8;   // LDS row stride (elements)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
   const bool row_ok = my_row < a.T;
   const bf16_t* xrow = x + (row_ok ? my_row : 0) * d + g * 8;
 
-  // Wr staging: NT*16 rows x 32 k fp32 = NT*128 float4; split into 3 bf16 terms
+  // Wr staging: NT*16 rows x kMBK k fp32 (NT*16*kMBK/4 float4), split into 3 bf16 terms
   constexpr int kWVec = NT * 16 * (kMBK / 4);
   constexpr int kWPer = (kWVec + kThreads - 1) / kThreads;
   float4 wv[kWPer];
@@ -545,30 +545,47 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // X fragments two chunks ahead: lane (g, c) holds 8 k values of sub-step s
+  // of its token row
   constexpr int kAhead = 2;
-  uint4 xa[kAhead];
+  uint4 xa[kAhead][2];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i)
-    xa[i] = (row_ok && i < nk) ? *reinterpret_cast<const uint4*>(xrow + i * kMBK)
-                               : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      xa[i][s2] = (row_ok && i < nk)
+                      ? *reinterpret_cast<const uint4*>(xrow + i * kMBK + s2 * 32)
+                      : make_uint4(0u, 0u, 0u, 0u);
   wload(0);
   for (int kt = 0; kt < nk; ++kt) {
     wstore();
     __syncthreads();
     if (kt + 1 < nk) wload(kt + 1);
-    const uint4 cur = xa[0];
+    const uint4 cur0 = xa[0][0], cur1 = xa[0][1];
 #pragma unroll
-    for (int i = 0; i + 1 < kAhead; ++i) xa[i] = xa[i + 1];
-    xa[kAhead - 1] = (row_ok && kt + kAhead < nk)
-                         ? *reinterpret_cast<const uint4*>(xrow + (kt + kAhead) * kMBK)
-                         : make_uint4(0u, 0u, 0u, 0u);
-    const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&cur);
+    for (int i = 0; i + 1 < kAhead; ++i) {
+      xa[i][0] = xa[i + 1][0];
+      xa[i][1] = xa[i + 1][1];
+    }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int s2 = 0; s2 < 2; ++s2)
+      xa[kAhead - 1][s2] = (row_ok && kt + kAhead < nk)
+                               ? *reinterpret_cast<const uint4*>(xrow + (kt + kAhead) * kMBK +
+                                                                 s2 * 32)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    // sub-steps in k order, and per expert block hi, mid, lo: the fp32 sum
+    // runs in the same order as with 32-wide chunks
 #pragma unroll
-      for (int sp = 0; sp < 3; ++sp) {
-        const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t*>(&wsh[sp][16 * j + c][g * 8]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(s2 == 0 ? &cur0 : &cur1);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          const bf16x8_t bfr =
+              *reinterpret_cast<const bf16x8_t*>(&wsh[sp][16 * j + c][s2 * 32 + g * 8]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
