@@ -381,6 +381,9 @@ def main():
                     help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
                          "expand) for the workload's placement group counts; adds an "
                          "'ep_dispatch' object to the JSON line")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (per-call times "
+                         "still come from eager launches)")
     ap.add_argument("--fragility", action="store_true",
                     help="also run the routing-fragility probe (one router weight moved by "
                          "1, 2^10 and 2^20 ulps; flips against margins); adds a 'fragility' "
@@ -501,6 +504,30 @@ def main():
             fn()
     torch.cuda.synchronize()
 
+    def eager_step():
+        for _, fn in calls:
+            fn()
+
+    step = eager_step
+    if args.graph:
+        # one step captured in a HIP graph (the library allocates, frees and
+        # synchronises nothing, and launches on torch's current stream, which
+        # is the capture stream here); the timed region replays it
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            eager_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        step = graph.replay
+
     # Timed region: K whole steps back to back, bracketed by events on the
     # stream the library launches on (torch's current stream).
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -508,8 +535,7 @@ def main():
     wall0 = time.perf_counter()
     start.record()
     for _ in range(args.steps):
-        for _, fn in calls:
-            fn()
+        step()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -561,12 +587,18 @@ def main():
                                f"{cfg.act}, fp32 router, {'fwd+bwd' if cfg.backward else 'fwd'}",
                    "tokens": cfg.T, "lb_groups": G,
                    "expert_input": "gathered from X by src_token" if gather
-                                   else "materialised x_perm"},
+                                   else "materialised x_perm",
+                   "launch": "HIP graph replay" if args.graph else "eager launches"},
         "grouped_gemm": {"tflops": round(gemm_tflops, 2),
                          "frac_of_peak": round(gemm_tflops / (PEAK_MFMA[cfg.act] / 1e12), 4)},
         "per_call_ms": {k: round(v, 4) for k, v in per_call.items()},
         "wall_s": round(wall, 3),
         "roofline": roof,
+        # every call against its own bound (algorithmic work over its mean duration)
+        "per_call_roofline": {
+            n: {k2: v2 for k2, v2 in roofline_entry(work[n][0], work[n][1], t * 1e-3,
+                                                     cfg.act).items() if k2 in ("bound", "frac")}
+            for n, t in per_call.items()},
     }
     if layer.dense_bwd:
         out["config"]["variant"] = {
