@@ -405,7 +405,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of tokens; --gpus {args.gpus} is not "
-              "supported (this build runs on a single GPU).", file=sys.stderr)
+              "supported (the MoE layer path here runs on a single GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
