@@ -239,10 +239,12 @@ def silu(a):
     return a * _sigmoid(a)
 
 
-def swiglu_experts(x_perm, offsets, w1, w3, w2, act="f64"):
+def swiglu_experts(x_perm, offsets, w1, w3, w2, act="f64", row_scale=None):
     """Per expert e over rows [offsets[e], offsets[e+1]):
     a = X W1[e]^T, b = X W3[e]^T, h = silu(a) * b, y = h W2[e]^T.
-    (act="bf16": a, b, h and y are stored as bfloat16 values.)"""
+    (act="bf16": a, b, h and y are stored as bfloat16 values.)
+    row_scale [R], when given, multiplies h row by row before it is stored
+    (the gate folded onto the expert row: y then carries the gate)."""
     st = storage(act)
     x_perm = _f64(x_perm)
     w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
@@ -257,7 +259,10 @@ def swiglu_experts(x_perm, offsets, w1, w3, w2, act="f64"):
         xe = x_perm[s]
         a[s] = st(xe @ w1[e].T)
         b[s] = st(xe @ w3[e].T)
-        h[s] = st(silu(a[s]) * b[s])
+        hs = silu(a[s]) * b[s]
+        if row_scale is not None:
+            hs = hs * _f64(row_scale)[s, None]
+        h[s] = st(hs)
         y[s] = st(h[s] @ w2[e].T)
     return {"a": a, "b": b, "h": h, "y_perm": y}
 
@@ -297,6 +302,49 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm, act="f64"):
         dw3[e] = st(db[s].T @ x_perm[s])
     return {"dx_perm": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2,
             "dh": dh, "da": da, "db": db}
+
+
+def swiglu_experts_bwd_folded(x_perm, offsets, w1, w3, w2, a, b, hg, dy_rows, g_row,
+                              act="f64"):
+    """swiglu_experts_bwd with the gate folded onto the rows ([REVISIT] Sec. 2.1:
+    the combine weights each expert output by its gate, and the expert output
+    is linear in h, so the gate may sit on h).  For the upstream dY rows of
+    each expert row (dy_rows = dY[src]) and the row gates g_row:
+      u = dy_rows W2[e] (stored), dh = g u (not stored),
+      da = dh * b * silu'(a), db = dh * silu(a), dx = da W1[e] + db W3[e],
+      dgate_row = <u, silu(a) * b>  (= <dY, y_perm> of the unfolded layer),
+      dW2[e] = dy_rows^T hg with hg = g h the forward's stored rows,
+      dW1[e] = da^T x, dW3[e] = db^T x."""
+    st = storage(act)
+    x_perm, dy_rows = _f64(x_perm), _f64(dy_rows)
+    a, b, hg, g_row = _f64(a), _f64(b), _f64(hg), _f64(g_row)
+    w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
+    E, f, d = w1.shape
+    R = x_perm.shape[0]
+    dx = np.zeros((R, d))
+    u = np.zeros((R, f))
+    da = np.zeros((R, f))
+    db = np.zeros((R, f))
+    dgate_row = np.zeros(R)
+    dw1 = np.zeros_like(w1)
+    dw3 = np.zeros_like(w3)
+    dw2 = np.zeros_like(w2)
+    for e in range(E):
+        s = slice(int(offsets[e]), int(offsets[e + 1]))
+        sg = _sigmoid(a[s])
+        act_s = a[s] * sg
+        dact = sg * (1.0 + a[s] * (1.0 - sg))
+        u[s] = st(dy_rows[s] @ w2[e])
+        dh = g_row[s, None] * u[s]
+        dgate_row[s] = (u[s] * act_s * b[s]).sum(axis=1)
+        da[s] = st(dh * b[s] * dact)
+        db[s] = st(dh * act_s)
+        dx[s] = st(da[s] @ w1[e] + db[s] @ w3[e])
+        dw2[e] = st(dy_rows[s].T @ hg[s])
+        dw1[e] = st(da[s].T @ x_perm[s])
+        dw3[e] = st(db[s].T @ x_perm[s])
+    return {"dx_perm": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2, "u": u, "da": da, "db": db,
+            "dgate_row": dgate_row}
 
 
 # ---------------------------------------------------------------------------
@@ -465,7 +513,7 @@ def z_loss_grad(logits):
 # ---------------------------------------------------------------------------
 
 def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f64",
-                  capacity=None, lb_groups=1):
+                  capacity=None, lb_groups=1, fold_gate=False):
     """Router -> permute -> SwiGLU experts -> combine.
 
     routing, when given, is a (topk_idx, gates) pair that replaces the router's
@@ -473,6 +521,9 @@ def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f6
     act: storage precision of the activations ("f64" or "bf16").
     capacity, when given, is the per-block expert capacity C of capacity_keep
     over lb_groups blocks; dropped assignments get no row and no output.
+    fold_gate: the gate multiplies h of each expert row (h holds g h) and the
+    combine adds the rows unweighted; the same layer in exact arithmetic, with
+    the storage rounding at different points.
     """
     E = np.asarray(wr).shape[0]
     r = route(x, wr, k, near_tie_eps)
@@ -489,13 +540,19 @@ def layer_forward(x, wr, w1, w3, w2, k, near_tie_eps=1e-3, routing=None, act="f6
         kept = cap["kept_idx"]
     plan = permute_plan(kept, E)
     x_perm = gather_rows(x, plan["src"])
-    ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2, act)
-    y = combine(ex["y_perm"], plan["pos"], gates, act)
+    g_row = None
+    if fold_gate:
+        g_row = np.zeros(x_perm.shape[0])
+        live = plan["pos"] >= 0
+        g_row[plan["pos"][live]] = _f64(gates)[live]
+    ex = swiglu_experts(x_perm, plan["offsets"], w1, w3, w2, act, row_scale=g_row)
+    y = combine(ex["y_perm"], plan["pos"], None if fold_gate else gates, act)
     out = dict(r)
     out.update(plan)
     out.update(ex)
     out.update({"topk_idx": idx, "gates": gates, "x_perm": x_perm, "y": y, "act": act,
-                "kept_idx": kept, "lb_groups": lb_groups})
+                "kept_idx": kept, "lb_groups": lb_groups, "fold_gate": fold_gate,
+                "g_row": g_row})
     if cap is not None:
         out["dropped"] = cap["dropped"]
     return out
@@ -506,9 +563,20 @@ def layer_backward(x, wr, w1, w3, w2, fwd, dy, aux_coef=0.0, z_coef=0.0):
     forward's storage precision, plus the gradients of aux_coef * L_aux (over
     the forward's lb_groups blocks) and z_coef * L_z when they are non-zero."""
     act = fwd.get("act", "f64")
-    dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"], act)
-    eb = swiglu_experts_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2,
-                            fwd["a"], fwd["b"], dy_perm, act)
+    if fwd.get("fold_gate"):
+        # the gate sits on the rows: dY is read through src, dgate comes from
+        # the rows' <u, h> (a dropped slot has no row and dgate 0)
+        dy_perm = None
+        eb = swiglu_experts_bwd_folded(fwd["x_perm"], fwd["offsets"], w1, w3, w2, fwd["a"],
+                                       fwd["b"], fwd["h"], gather_rows(dy, fwd["src"]),
+                                       fwd["g_row"], act)
+        pos = fwd["pos"]
+        dgate = np.where(pos >= 0, eb["dgate_row"][np.maximum(pos, 0)], 0.0)
+        eb["dh"] = eb["u"] * _f64(fwd["g_row"])[:, None]
+    else:
+        dy_perm, dgate = combine_bwd(dy, fwd["y_perm"], fwd["pos"], fwd["gates"], act)
+        eb = swiglu_experts_bwd(fwd["x_perm"], fwd["offsets"], w1, w3, w2,
+                                fwd["a"], fwd["b"], dy_perm, act)
     dx_exp = combine(eb["dx_perm"], fwd["pos"], None)
     count = None
     if aux_coef != 0.0:

@@ -864,3 +864,34 @@ def test_flips_of_a_single_weight_nudge_follow_the_logit_shift():
     pred = np.where(inside, lb[:, e] < srt[:, k - 1], lb[:, e] > srt[:, k - 1])
     clear = np.abs(lb[:, e] - srt[:, k - 1]) > 1e-12
     assert np.array_equal(flips[clear], pred[clear])
+
+
+@pytest.mark.parametrize("cap", [None, 1.0])
+def test_folded_gate_layer_is_the_same_layer_in_exact_arithmetic(cap):
+    """[REVISIT] Sec. 2.1: y[t] = sum_j g_j E_j(x_t) with E(x) = W2 h linear in
+    h, so putting g on h (and reading dY through the rows) is the same layer.
+    In fp64 (no storage rounding) every output of the folded oracle equals the
+    unfolded one's to rounding level: a dropped gate, a wrong row index or a
+    missing dgate term breaks it."""
+    rng = np.random.default_rng(41)
+    T, d, E, f, k, G = 48, 16, 6, 12, 2, 4
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) * 0.5
+    w1 = rng.standard_normal((E, f, d)) * 0.3
+    w3 = rng.standard_normal((E, f, d)) * 0.3
+    w2 = rng.standard_normal((E, d, f)) * 0.3
+    dy = rng.standard_normal((T, d))
+    C = None if cap is None else O.expert_capacity(T, k, E, G, cap)
+    ref_f = O.layer_forward(x, wr, w1, w3, w2, k, capacity=C, lb_groups=G)
+    fol_f = O.layer_forward(x, wr, w1, w3, w2, k, capacity=C, lb_groups=G, fold_gate=True)
+    if C is not None:
+        assert ref_f["dropped"].sum() > 0
+    ref_b = O.layer_backward(x, wr, w1, w3, w2, ref_f, dy, 0.01, 0.001)
+    fol_b = O.layer_backward(x, wr, w1, w3, w2, fol_f, dy, 0.01, 0.001)
+    np.testing.assert_allclose(fol_f["y"], ref_f["y"], rtol=1e-10, atol=1e-12)
+    R = int(ref_f["offsets"][-1])
+    np.testing.assert_allclose(fol_f["h"][:R], ref_f["h"][:R] * fol_f["g_row"][:R, None],
+                               rtol=1e-12, atol=1e-14)
+    for key in ("dgate", "dx_perm", "dh", "da", "db", "dw1", "dw3", "dw2", "dx", "dwr",
+                "dlogits"):
+        np.testing.assert_allclose(fol_b[key], ref_b[key], rtol=1e-9, atol=1e-11, err_msg=key)
