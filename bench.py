@@ -11,6 +11,13 @@ By default the permutation is a plan only and moe_expert_up / moe_expert_wgrad
 read their input rows from X through src_token (the *_gather calls, reported
 as moe_permute_plan, moe_expert_up_gather, moe_expert_wgrad_gather);
 --no-gather materialises x_perm instead.  Both compute the same bits.
+Where the dims allow it (bf16, every expert GEMM on the 128 x 128 tile: C2,
+C3) the gate is folded onto the expert rows by default: moe_permute_gates ->
+moe_expert_up_folded -> moe_expert_down -> moe_combine (no gates) ->
+moe_expert_dgrad_down_folded -> moe_expert_dgrad_up -> moe_expert_wgrad_folded
+-> moe_route_bwd_folded (which sums the dgate parts), with no moe_combine_bwd
+and no dy_perm; --no-fold keeps the gate in the combine.  config.gate says
+which.
 Inputs and weights are resident in HBM before timing starts.  Prints one JSON
 line.
 
@@ -37,16 +44,32 @@ PEAK_HBM = 8.0e12          # bytes/s
 PEAK_MFMA = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix peaks (fp32: vector/matrix fp32)
 
 
-def algorithmic_work(cfg, R=None):
+def algorithmic_work(cfg, R=None, fold=False, parts=1):
     """Per-call algorithmic (flops, bytes, kernels): what each call must compute
     and move by its C-ABI contract (inputs read once, outputs written once).
-    R: expert rows (T k, or fewer when a capacity drops assignments)."""
+    R: expert rows (T k, or fewer when a capacity drops assignments).  fold:
+    the gate sits on the expert rows (the combine reads no gates); parts: the
+    dgate parts per row of the folded backward."""
     T, d, E, f, k = cfg.T, cfg.d, cfg.E, cfg.f, cfg.k
     R = T * k if R is None else R
     s = 2 if cfg.act == "bf16" else 4
     i4 = 4
     Wf = E * d * f * s          # one of W1, W3, W2
+    gates = 0 if fold else T * k * 4
     return {
+        # gate folded onto the expert rows: dY read through src_token, no dy_perm
+        "moe_permute_gates": (0, T * k * (i4 + 4) + 2 * R * i4 + R * 4 + (2 * E + 1) * i4, 2),
+        "moe_expert_up_folded": (4 * R * d * f,
+                                 R * d * s + R * (i4 + 4) + 2 * Wf + 3 * R * f * s, 1),
+        "moe_expert_dgrad_down_folded": (2 * R * d * f + 2 * R * f,
+                                         R * d * s + R * (i4 + 4) + Wf + 4 * R * f * s
+                                         + R * parts * 4, 1),
+        "moe_dgate_from_parts": (R * parts, R * parts * 4 + T * k * (i4 + 4), 1),
+        "moe_route_bwd_folded": (4 * R * d + R * parts,
+                                 T * d * s + E * d * 4 + R * d * s + T * d * s + E * d * 4
+                                 + T * k * 16 + R * parts * 4 + R * 8, 4),
+        "moe_expert_wgrad_folded": (6 * R * d * f,
+                                    2 * R * d * s + R * i4 + 3 * R * f * s + 3 * Wf, 1),
         "moe_route": (2 * T * d * E,
                       T * d * s + E * d * 4 + T * E * 4 + T * k * (i4 + 4) + T * 4, 2),
         "moe_permute": (0, T * k * i4 + T * d * s + R * d * s + 2 * R * i4 + (2 * E + 1) * i4, 4),
@@ -55,7 +78,7 @@ def algorithmic_work(cfg, R=None):
         "moe_expert_up": (4 * R * d * f, R * d * s + 2 * Wf + 3 * R * f * s, 1),
         "moe_expert_up_gather": (4 * R * d * f, R * d * s + R * i4 + 2 * Wf + 3 * R * f * s, 1),
         "moe_expert_down": (2 * R * d * f, R * f * s + Wf + R * d * s, 1),
-        "moe_combine": (2 * R * d, R * d * s + T * d * s + T * k * (i4 + 4), 1),
+        "moe_combine": (2 * R * d, R * d * s + T * d * s + T * k * i4 + gates, 1),
         "moe_combine_bwd": (2 * R * d, T * d * s + 2 * R * d * s + T * k * (i4 + 8), 1),
         "moe_expert_dgrad_down": (2 * R * d * f, R * d * s + Wf + 4 * R * f * s, 1),
         "moe_expert_dgrad_up": (4 * R * d * f, 2 * R * f * s + 2 * Wf + R * d * s, 1),
@@ -74,7 +97,8 @@ def algorithmic_work(cfg, R=None):
 
 GEMM_CALLS = ("moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
               "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_up_gather",
-              "moe_expert_wgrad_gather")
+              "moe_expert_wgrad_gather", "moe_expert_up_folded", "moe_expert_dgrad_down_folded",
+              "moe_expert_wgrad_folded")
 WGRAD_CALLS = ("moe_expert_wgrad", "moe_expert_wgrad_gather")
 
 
@@ -105,7 +129,10 @@ KERNEL_SOURCES = {
     "moe_expert_dgrad_down": "gemm_bf16.hip", "moe_expert_dgrad_up": "gemm_bf16.hip",
     "moe_expert_wgrad": "gemm_bf16.hip", "moe_route": "route.hip", "moe_permute": "permute.hip",
     "moe_combine": "combine.hip", "moe_combine_bwd": "combine.hip",
-    "moe_route_bwd": "route_bwd.hip",
+    "moe_route_bwd": "route_bwd.hip", "moe_permute_gates": "permute.hip",
+    "moe_expert_up_folded": "gemm_bf16.hip", "moe_expert_dgrad_down_folded": "gemm_bf16.hip",
+    "moe_expert_wgrad_folded": "gemm_bf16.hip", "moe_dgate_from_parts": "combine.hip",
+    "moe_route_bwd_folded": "route_bwd.hip",
 }
 
 
@@ -381,6 +408,9 @@ def main():
                     help="also time the expert-parallel dispatch emulation (dedup plan, pack, "
                          "expand) for the workload's placement group counts; adds an "
                          "'ep_dispatch' object to the JSON line")
+    ap.add_argument("--no-fold", action="store_true",
+                    help="keep the gate in the combine (moe_combine_bwd and dy_perm) even "
+                         "where the folded path is supported")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (per-call times "
                          "still come from eager launches)")
@@ -427,9 +457,11 @@ def main():
     w1, w3, w2 = up(inp["w1"], act), up(inp["w3"], act), up(inp["w2"], act)
     G = max(cfg.lb_groups)
     gather = not args.no_gather
+    fold = (gather and not args.no_fold and
+            L.moe_gate_folded_supported(L.make_dims(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act)))
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=gather,
                      capacity_factor=args.capacity_factor, aux_coef=args.aux_coef,
-                     z_coef=args.z_coef)
+                     z_coef=args.z_coef, fold_gate=fold)
     dm = layer.dims
     table = layer.kept_idx if layer.capacity is not None else layer.topk_idx
 
@@ -456,8 +488,8 @@ def main():
             dm, x, layer.src_token, layer.expert_offsets, w1, w3, layer.a, layer.b, layer.h)),
         ("moe_expert_down", lambda: L.moe_expert_down(dm, layer.h, layer.expert_offsets, w2,
                                                       layer.y_perm)),
-        ("moe_combine", lambda: L.moe_combine(dm, layer.y_perm, layer.pos, layer.topk_gate,
-                                              layer.y)),
+        ("moe_combine", lambda: L.moe_combine(dm, layer.y_perm, layer.pos,
+                                              None if fold else layer.topk_gate, layer.y)),
         ("moe_combine_bwd", lambda: L.moe_combine_bwd(dm, dy, layer.y_perm, layer.pos,
                                                       layer.topk_gate, layer.dy_perm,
                                                       layer.dgate)),
@@ -480,6 +512,37 @@ def main():
             layer.dx_perm, G, layer.group_count, layer.aux_coef, layer.z_coef, layer.dx,
             layer.dwr, None, layer.workspace)),
     ]
+    if fold:
+        calls += [
+            ("moe_permute_gates", lambda: L.moe_permute_gates(
+                dm, table, layer.topk_gate, layer.expert_counts, layer.expert_offsets, layer.pos,
+                layer.src_token, layer.gate_perm, layer.workspace)),
+            ("moe_expert_up_folded", lambda: L.moe_expert_up_folded(
+                dm, x, layer.src_token, layer.expert_offsets, layer.gate_perm, w1, w3, layer.a,
+                layer.b, layer.h)),
+            ("moe_expert_dgrad_down_folded", lambda: L.moe_expert_dgrad_down_folded(
+                dm, dy, layer.src_token, layer.expert_offsets, layer.gate_perm, w2, layer.a,
+                layer.b, da, db, layer.dgate_part)),
+            ("moe_dgate_from_parts", lambda: L.moe_dgate_from_parts(
+                dm, layer.dgate_part, layer.pos, layer.dgate)),
+            ("moe_route_bwd_folded", lambda: L.moe_route_bwd_folded(
+                dm, x, wr, layer.topk_idx, layer.topk_gate, layer.dgate_part,
+                layer.expert_offsets, layer.pos, layer.src_token, layer.dx_perm, layer.dgate,
+                layer.dx, layer.dwr, layer.workspace)),
+            ("moe_expert_wgrad_folded", lambda: L.moe_expert_wgrad_folded(
+                dm, x, dy, layer.src_token, layer.expert_offsets, layer.h, da, db, layer.dw1,
+                layer.dw3, layer.dw2)),
+        ]
+        order = ["moe_route", "moe_capacity", "moe_router_zloss", "moe_permute_gates",
+                 "moe_expert_up_folded", "moe_expert_down", "moe_combine",
+                 "moe_expert_dgrad_down_folded", "moe_dgate_from_parts", "moe_expert_dgrad_up",
+                 "moe_expert_wgrad_folded", "moe_route_bwd_folded", "moe_route_bwd_dense"]
+        if layer.dense_bwd:
+            order.remove("moe_route_bwd_folded")
+        else:   # the sparse router backward sums the dgate parts itself
+            order.remove("moe_dgate_from_parts")
+        by_name = dict(calls)
+        calls = [(n, by_name[n]) for n in order]
     drop = (("moe_permute", "moe_expert_up", "moe_expert_wgrad") if gather else
             ("moe_permute_plan", "moe_expert_up_gather", "moe_expert_wgrad_gather"))
     drop += ("moe_route_bwd",) if layer.dense_bwd else ("moe_route_bwd_dense",)
@@ -558,7 +621,7 @@ def main():
                 for i, (name, _) in enumerate(calls)}
 
     rows = int(layer.expert_offsets[cfg.E].item())   # expert rows (fewer when dropping)
-    work = algorithmic_work(cfg, rows)
+    work = algorithmic_work(cfg, rows, fold, L.moe_dgate_parts(dm))
     # the dominant single-kernel call carries the roofline
     single = {n: t for n, t in per_call.items() if work[n][2] == 1 or
               (n in WGRAD_CALLS and wgrad_kernels(dm) == 1)}
@@ -588,6 +651,7 @@ def main():
                    "tokens": cfg.T, "lb_groups": G,
                    "expert_input": "gathered from X by src_token" if gather
                                    else "materialised x_perm",
+                   "gate": "folded onto the expert rows" if fold else "applied in the combine",
                    "launch": "HIP graph replay" if args.graph else "eager launches"},
         "grouped_gemm": {"tflops": round(gemm_tflops, 2),
                          "frac_of_peak": round(gemm_tflops / (PEAK_MFMA[cfg.act] / 1e12), 4)},

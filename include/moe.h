@@ -289,6 +289,70 @@ moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Gate folded into the expert rows.  The combine is the gate-weighted sum
+ * y[t] = sum_j g_j E_{S_j}(x_t) ("Revisiting MoE and Dense Speed-Accuracy
+ * Comparisons", Sec. 2.1; "Expert Coupling in MoE Pretraining", Fig. 5 steps
+ * 3-4).  Since E(x) = W2 h is linear in h, these calls move g_j onto the
+ * expert row: the forward stores hg = g h (then moe_expert_down gives g E(x)
+ * and moe_combine with topk_gate = NULL sums the rows), and the backward
+ * reads dY [T,d] itself through src_token (no dy_perm):
+ *   u = dY[src] W2 (per row, over f; rounded to act), dh = g u,
+ *   da = dh b silu'(a), db = dh silu(a)            (as moe_expert_dgrad_down),
+ *   dgate[t,j] = <dY[t], W2 h> = <u, silu(a) b>     (per row, summed over f),
+ *   dW2 = sum_rows dY[src]^T hg, dW1 = da^T X[src], dW3 = db^T X[src].
+ * dgate comes out as parts, one per 128-column tile of f, in dgate_part
+ * [T*k, moe_dgate_parts(dims)] fp32; moe_dgate_from_parts adds them in tile
+ * order into dgate [T,k] (0 for a dropped slot, pos < 0).  The results match
+ * the unfolded calls up to rounding (one rounding of g h instead of one of
+ * h and one of g dY).
+ *
+ * Supported where every expert GEMM of the dims takes the 128 x 128 tile:
+ * bf16, and moe_gate_folded_supported(dims) == 1 (otherwise each call returns
+ * MOE_ERR_UNSUPPORTED).  The expert input is always X [T,d] through
+ * src_token; dY has the same shape and the same 2^31-byte bound.
+ *   moe_permute_gates:   moe_permute (no row copy) plus gate_perm [T*k] fp32,
+ *                        the gate of each expert row (its workspace);
+ *   moe_expert_up_folded: a, b, hg [T*k,f] from X, W1, W3 and gate_perm;
+ *   moe_expert_dgrad_down_folded: da, db [T*k,f] and dgate_part from dY,
+ *                        W2, a, b, gate_perm;
+ *   moe_dgate_from_parts: dgate [T,k] from dgate_part and pos;
+ *   moe_expert_wgrad_folded: dW1, dW3, dW2 from X, dY, hg, da, db.
+ * Rows past expert_offsets[E] (dropped slots) are never read or written.
+ */
+int32_t moe_gate_folded_supported(const moe_dims* dims);   /* [host] 1 or 0 */
+int32_t moe_dgate_parts(const moe_dims* dims);             /* [host] dgate parts per row */
+moe_status moe_permute_gates(const moe_dims* dims, const int32_t* topk_idx,
+                             const float* topk_gate, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* pos, int32_t* src_token,
+                             float* gate_perm, void* workspace, size_t workspace_bytes,
+                             void* stream);
+moe_status moe_expert_up_folded(const moe_dims* dims, const void* x, const int32_t* src_token,
+                                const int32_t* expert_offsets, const float* gate_perm,
+                                const void* w1, const void* w3, void* a_save, void* b_save,
+                                void* hg_save, void* stream);
+moe_status moe_expert_dgrad_down_folded(const moe_dims* dims, const void* dy,
+                                        const int32_t* src_token, const int32_t* expert_offsets,
+                                        const float* gate_perm, const void* w2, const void* a_save,
+                                        const void* b_save, void* da, void* db, float* dgate_part,
+                                        void* stream);
+moe_status moe_dgate_from_parts(const moe_dims* dims, const float* dgate_part,
+                                const int32_t* pos, float* dgate, void* stream);
+moe_status moe_expert_wgrad_folded(const moe_dims* dims, const void* x, const void* dy,
+                                   const int32_t* src_token, const int32_t* expert_offsets,
+                                   const void* hg_save, const void* da, const void* db,
+                                   void* dw1, void* dw3, void* dw2, void* stream);
+/* moe_route_bwd with the dgate parts in place of dgate: the same router
+ * backward (every assignment must have a row), its dgate [T,k] fp32 written
+ * as an output (the sum of each row's parts in tile order), so that
+ * moe_dgate_from_parts is not needed.  Same workspace as moe_route_bwd. */
+moe_status moe_route_bwd_folded(const moe_dims* dims, const void* x, const float* w_router,
+                                const int32_t* topk_idx, const float* topk_gate,
+                                const float* dgate_part, const int32_t* expert_offsets,
+                                const int32_t* pos, const int32_t* src_token,
+                                const void* dx_perm, float* dgate, void* dx, float* dw_router,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_route_bwd -- adjoint of the router (logits -> top-k -> renormalised
  * softmax), fused with the unpermute-and-sum of the expert input gradient.
  *

@@ -1,0 +1,124 @@
+"""GPU: the gate-folded layer (gate moved onto the expert rows; dY read
+through src_token, no dy_perm) against the oracle in its fold_gate mode, which
+stores bf16 values at the folded design's points (g h, u = dY W2) and is the
+unfolded oracle's layer in exact arithmetic (pinned on the CPU).
+
+The oracle's routing and block counts are copied into the layer, so integer
+outputs compare bit for bit and floats are held to the workload's tolerance.
+Cases: C2 and C3 at full size (the 8- and 4-stage weight-gradient rings), a
+ragged shape whose f = 192 leaves a partial column tile for the dgate parts,
+and C2 with capacity and both losses (dropped slots, dense router backward).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from synth import get_config, make_layer_inputs
+from top_routing_grouped_router_amd import MoELayer
+import top_routing_grouped_router_amd._lib as L
+
+from _util import TOL, TOL_ROUTER, act_torch, dev, host, per_slice_err, rel_err
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (config, overrides, G, capacity factor, aux_coef, z_coef)
+    "c2": ("c2", {}, 8, None, 0.0, 0.0),
+    "c3": ("c3", {}, 8, None, 0.0, 0.0),
+    "ragged_f192": ("c2", dict(T=1000, d=256, E=16, f=192, k=3), 4, None, 0.0, 0.0),
+    "c2_cap1_losses": ("c2", dict(T=4096), 4, 1.0, 0.01, 0.001),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_folded_layer_matches_oracle(name):
+    base, over, G, factor, aux_coef, z_coef = CASES[name]
+    print(f"\n[case] folded {name}", flush=True)
+    cfg = get_config(base, **over)
+    inp = make_layer_inputs(cfg, seed=23, with_dy=True)
+    act = act_torch(cfg.act)
+    C = None if factor is None else O.expert_capacity(cfg.T, cfg.k, cfg.E, G, factor)
+    o_f = O.layer_forward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], cfg.k,
+                          act="bf16", capacity=C, lb_groups=G, fold_gate=True)
+    o_b = O.layer_backward(inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"], o_f, inp["dy"],
+                           aux_coef, z_coef)
+    count = O.lb_stats(o_f["logits"], o_f["topk_idx"], cfg.E, G)["count"]
+
+    layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=True,
+                     capacity_factor=factor, aux_coef=aux_coef, z_coef=z_coef, fold_gate=True)
+    t = {key: dev(v, act) for key, v in inp.items() if key != "wr"}
+    t["wr"] = dev(inp["wr"], torch.float32)
+    layer.route(t["x"], t["wr"])
+    layer.topk_idx.copy_(dev(o_f["topk_idx"], torch.int32))
+    layer.topk_gate.copy_(dev(o_f["gates"].astype(np.float32), torch.float32))
+    layer.group_count.copy_(dev(count, torch.int32))
+    layer.forward_experts(t["x"], t["w1"], t["w3"], t["w2"])
+    layer.backward(t["dy"], t["x"], t["wr"], t["w1"], t["w3"], t["w2"])
+    torch.cuda.synchronize()
+
+    R = int(o_f["offsets"][-1])
+    kept = o_f["kept_idx"] if C is not None else o_f["topk_idx"]
+    assert np.array_equal(host(layer.expert_offsets), o_f["offsets"])
+    assert np.array_equal(host(layer.pos), o_f["pos"])
+    assert np.array_equal(host(layer.src_token)[:R], o_f["src"][:R])
+    # the gate of each expert row, exactly
+    gates32 = o_f["gates"].astype(np.float32)
+    live = kept >= 0
+    gp = host(layer.gate_perm)
+    assert np.array_equal(gp[o_f["pos"][live]], gates32[live])
+    errs = {}
+    for key in ("a", "b", "h", "y_perm"):   # h holds g h, y_perm g E(x)
+        errs[key] = rel_err(host(getattr(layer, key))[:R], o_f[key][:R])
+    errs["y"] = rel_err(host(layer.y), o_f["y"])
+    for key in ("da", "db", "dx_perm"):
+        errs[key] = rel_err(host(getattr(layer, key))[:R], o_b[key][:R])
+    for key in ("dgate", "dx"):
+        errs[key] = rel_err(host(getattr(layer, key)), o_b[key])
+    for key in ("dw1", "dw3", "dw2"):
+        errs[key] = per_slice_err(host(getattr(layer, key)), o_b[key])
+    errs["dwr"] = per_slice_err(host(layer.dwr), o_b["dwr"])
+    if layer.dlogits is not None:
+        errs["dlogits"] = rel_err(host(layer.dlogits), o_b["dlogits"])
+    print("[errors] " + " ".join(f"{k} {v:.1e}" for k, v in errs.items()), flush=True)
+    for key, err in errs.items():
+        assert err <= TOL["bf16"], (key, err)
+    if C is not None:
+        assert o_f["dropped"].sum() > 0
+        assert np.all(host(layer.dgate)[kept < 0] == 0.0)
+
+
+def test_folded_matches_unfolded_layer():
+    """Same inputs, same routing (the router runs in both): integer outputs
+    equal, floats a rounding step apart."""
+    print("\n[case] folded vs unfolded c2 T=4096", flush=True)
+    cfg = get_config("c2", T=4096)
+    inp = make_layer_inputs(cfg, seed=29, with_dy=True)
+    act = act_torch(cfg.act)
+    t = {key: dev(v, act) for key, v in inp.items() if key != "wr"}
+    t["wr"] = dev(inp["wr"], torch.float32)
+    a = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=4, gather=True)
+    b = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=4, gather=True,
+                 fold_gate=True)
+    for layer in (a, b):
+        layer.step(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], t["dy"])
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "pos", "src_token", "expert_offsets", "group_count"):
+        assert np.array_equal(host(getattr(a, key)), host(getattr(b, key))), key
+    for key in ("y", "dgate", "dx", "dw1", "dw3", "dw2", "dwr"):
+        e = rel_err(host(getattr(b, key)), host(getattr(a, key)))
+        print(f"[folded vs unfolded] {key} {e:.1e}", flush=True)
+        assert e <= TOL["bf16"], (key, e)
+
+
+def test_folded_calls_reject_unsupported_dims():
+    cfg = get_config("c5")
+    dims = L.make_dims(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, torch.bfloat16)
+    assert not L.moe_gate_folded_supported(dims)
+    z = torch.empty(16, dtype=torch.bfloat16, device="cuda")
+    zi = torch.empty(16, dtype=torch.int32, device="cuda")
+    zf = torch.empty(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(L.MoEError):
+        L.moe_expert_up_folded(dims, z, zi, zi, zf, z, z, z, z, z)
+    with pytest.raises(ValueError):
+        MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, torch.bfloat16, gather=True, fold_gate=True)

@@ -16,10 +16,10 @@ pytestmark = pytest.mark.gpu
 OUTPUTS = ("logits", "topk_idx", "topk_gate", "margin", "near_tie_count", "group_count",
            "group_mean_prob", "group_aux", "expert_counts", "expert_offsets", "pos", "src_token",
            "y_perm", "y", "dgate", "dx_perm", "dw1", "dw3", "dw2", "dx", "dwr", "kept_idx",
-           "group_dropped", "group_z", "dlogits")
+           "group_dropped", "group_z", "dlogits", "gate_perm", "dgate_part", "da", "db")
 
 
-@pytest.mark.parametrize("variant", ["default", "capacity_losses"])
+@pytest.mark.parametrize("variant", ["default", "capacity_losses", "gate_folded"])
 def test_layer_step_graph_replays_match_eager(variant):
     print(f"\n[case] graph {variant}", flush=True)
     cfg = get_config("c2", T=2048)
@@ -28,6 +28,8 @@ def test_layer_step_graph_replays_match_eager(variant):
     kw = dict(n_groups=4, gather=True)
     if variant == "capacity_losses":
         kw.update(capacity_factor=1.0, aux_coef=0.01, z_coef=0.001)
+    if variant == "gate_folded":
+        kw.update(fold_gate=True)
     layer = MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, **kw)
     t = {key: dev(v, act) for key, v in inp.items() if key != "wr"}
     t["wr"] = dev(inp["wr"], torch.float32)
@@ -42,7 +44,7 @@ def test_layer_step_graph_replays_match_eager(variant):
     kept = int(host(layer.expert_offsets)[-1])
     if variant == "capacity_losses":
         assert kept < cfg.T * cfg.k == kept + int(host(layer.group_dropped).sum())
-    rows = {"src_token", "y_perm", "dx_perm"}
+    rows = {"src_token", "y_perm", "dx_perm", "gate_perm", "dgate_part", "da", "db"}
 
     def defined(name):
         a = host(getattr(layer, name))

@@ -39,6 +39,9 @@ EXPORTED = (
     "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
     "moe_expert_capacity", "moe_capacity", "moe_router_zloss", "moe_route_bwd_dense",
     "moe_coselect_cross", "moe_shuffle_plan", "moe_route_flips",
+    "moe_gate_folded_supported", "moe_dgate_parts", "moe_permute_gates",
+    "moe_expert_up_folded", "moe_expert_dgrad_down_folded", "moe_dgate_from_parts",
+    "moe_expert_wgrad_folded", "moe_route_bwd_folded",
 )
 
 
@@ -94,6 +97,16 @@ _SIGNATURES = {
                                              _P, _P, _P, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
     "moe_expert_capacity": (_I32, [_I64, _I32, _I32, _I32, ctypes.c_double]),
+    "moe_gate_folded_supported": (_I32, [_DIMS]),
+    "moe_dgate_parts": (_I32, [_DIMS]),
+    "moe_permute_gates": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_up_folded": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_dgrad_down_folded": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P]),
+    "moe_dgate_from_parts": (_I32, [_DIMS, _P, _P, _P, _P]),
+    "moe_route_bwd_folded": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _SZ, _P]),
+    "moe_expert_wgrad_folded": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_capacity": (_I32, [_DIMS, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
     "moe_router_zloss": (_I32, [_DIMS, _P, _I32, _P, _P, _SZ, _P]),
     "moe_route_bwd_dense": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _F32, _F32,
@@ -401,6 +414,86 @@ def moe_expert_wgrad_gather(dims, x, src_token, expert_offsets, h_save, dy_perm,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "moe_expert_wgrad_gather")
+
+
+# ------------------------------------------------- gate folded into the expert rows
+def moe_gate_folded_supported(dims) -> bool:
+    return bool(lib().moe_gate_folded_supported(ctypes.byref(dims)))
+
+
+def moe_dgate_parts(dims) -> int:
+    return int(lib().moe_dgate_parts(ctypes.byref(dims)))
+
+
+def moe_permute_gates(dims, topk_idx, topk_gate, expert_counts, expert_offsets, pos, src_token,
+                      gate_perm, workspace, stream=None):
+    st = lib().moe_permute_gates(
+        ctypes.byref(dims), _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(topk_gate, "topk_gate", torch.float32),
+        _ptr(expert_counts, "expert_counts", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(pos, "pos", torch.int32),
+        _ptr(src_token, "src_token", torch.int32), _ptr(gate_perm, "gate_perm", torch.float32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "moe_permute_gates")
+
+
+def moe_expert_up_folded(dims, x, src_token, expert_offsets, gate_perm, w1, w3, a_save, b_save,
+                         hg_save, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_up_folded(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32),
+        _ptr(gate_perm, "gate_perm", torch.float32), _ptr(w1, "w1", act), _ptr(w3, "w3", act),
+        _ptr(a_save, "a_save", act), _ptr(b_save, "b_save", act), _ptr(hg_save, "hg_save", act),
+        _stream(stream))
+    _check(st, "moe_expert_up_folded")
+
+
+def moe_expert_dgrad_down_folded(dims, dy, src_token, expert_offsets, gate_perm, w2, a_save,
+                                 b_save, da, db, dgate_part, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_dgrad_down_folded(
+        ctypes.byref(dims), _ptr(dy, "dy", act), _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32),
+        _ptr(gate_perm, "gate_perm", torch.float32), _ptr(w2, "w2", act),
+        _ptr(a_save, "a_save", act), _ptr(b_save, "b_save", act), _ptr(da, "da", act),
+        _ptr(db, "db", act), _ptr(dgate_part, "dgate_part", torch.float32), _stream(stream))
+    _check(st, "moe_expert_dgrad_down_folded")
+
+
+def moe_dgate_from_parts(dims, dgate_part, pos, dgate, stream=None):
+    st = lib().moe_dgate_from_parts(
+        ctypes.byref(dims), _ptr(dgate_part, "dgate_part", torch.float32),
+        _ptr(pos, "pos", torch.int32), _ptr(dgate, "dgate", torch.float32), _stream(stream))
+    _check(st, "moe_dgate_from_parts")
+
+
+def moe_expert_wgrad_folded(dims, x, dy, src_token, expert_offsets, hg_save, da, db, dw1, dw3,
+                            dw2, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_expert_wgrad_folded(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(dy, "dy", act),
+        _ptr(src_token, "src_token", torch.int32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(hg_save, "hg_save", act),
+        _ptr(da, "da", act), _ptr(db, "db", act), _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act),
+        _ptr(dw2, "dw2", act), _stream(stream))
+    _check(st, "moe_expert_wgrad_folded")
+
+
+def moe_route_bwd_folded(dims, x, w_router, topk_idx, topk_gate, dgate_part, expert_offsets,
+                         pos, src_token, dx_perm, dgate, dx, dw_router, workspace, stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_route_bwd_folded(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(w_router, "w_router", torch.float32),
+        _ptr(topk_idx, "topk_idx", torch.int32), _ptr(topk_gate, "topk_gate", torch.float32),
+        _ptr(dgate_part, "dgate_part", torch.float32),
+        _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(pos, "pos", torch.int32),
+        _ptr(src_token, "src_token", torch.int32), _ptr(dx_perm, "dx_perm", act),
+        _ptr(dgate, "dgate", torch.float32), _ptr(dx, "dx", act),
+        _ptr(dw_router, "dw_router", torch.float32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_route_bwd_folded")
 
 
 # ---------------------------------------------------------------- EP dispatch on one device

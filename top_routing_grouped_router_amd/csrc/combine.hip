@@ -168,4 +168,29 @@ hipError_t launch_combine_bwd(const moe_dims& dm, const void* dy, const void* y_
                                      static_cast<uint4*>(dy_perm), dgate, dm.T, vpr, dm.k);
 }
 
+// Gate-folded backward: dgate[t, j] = the sum of the column-tile parts of
+// row pos[t, j] in tile order (0 for a dropped slot), one thread per slot.
+namespace {
+__global__ __launch_bounds__(kThreads) void dgate_from_parts_kernel(
+    const float* __restrict__ part, int32_t nparts, const int32_t* __restrict__ pos,
+    float* __restrict__ dgate, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const int32_t p = pos[i];
+  float s = 0.f;
+  if (p >= 0)
+    for (int q = 0; q < nparts; ++q) s += part[static_cast<int64_t>(p) * nparts + q];
+  dgate[i] = s;
+}
+}  // namespace
+
+hipError_t launch_dgate_from_parts(const moe_dims& dm, const float* part, int32_t nparts,
+                                   const int32_t* pos, float* dgate, hipStream_t s) {
+  const int64_t n = dm.T * dm.k;
+  if (n > 0)
+    hipLaunchKernelGGL(dgate_from_parts_kernel, dim3((n + kThreads - 1) / kThreads),
+                       dim3(kThreads), 0, s, part, nparts, pos, dgate, n);
+  return hipGetLastError();
+}
+
 }  // namespace moe

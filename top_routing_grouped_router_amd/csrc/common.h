@@ -94,7 +94,8 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
 constexpr int kPermBlock = 256;     // tokens per permutation block
 hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* pos, int32_t* src, const void* x,
-                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s);
+                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s,
+                          const float* gate = nullptr, float* gate_perm = nullptr);
 
 // shared by the permutation and the dispatch plan
 __global__ void key_scan_kernel(const int32_t* hist, int32_t nb, int32_t nkeys, int32_t* base,
@@ -145,12 +146,31 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
                              const int32_t* offsets, const void* h, const void* dy_perm,
                              const void* da, const void* db, void* dw1, void* dw3, void* dw2,
                              float* partial, hipStream_t s);
+// gate folded into the expert rows (small tiles, gathered expert input): UP
+// stores g h; DGRAD_DOWN reads dy through the table, scales dh by g and writes
+// per-row dgate parts; WGRAD reads dy through the table for dW2
+bool folded_bf16_ok(const moe_dims& dm);
+int dgate_parts_bf16(const moe_dims& dm);
+hipError_t launch_up_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
+                                 const int32_t* offsets, const float* gate_rows, const void* w1,
+                                 const void* w3, void* a, void* b, void* hg, hipStream_t s);
+hipError_t launch_dgrad_down_folded_bf16(const moe_dims& dm, const void* dy,
+                                         const int32_t* x_rows, const int32_t* offsets,
+                                         const float* gate_rows, const void* w2, const void* a,
+                                         const void* b, void* da, void* db, float* dgate_part,
+                                         hipStream_t s);
+hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
+                                    const int32_t* offsets, const void* hg, const void* dy,
+                                    const void* da, const void* db, void* dw1, void* dw3,
+                                    void* dw2, hipStream_t s);
 int wgrad_splits_bf16(const moe_dims& dm);           // split-K count of the weight gradients
 size_t wgrad_partial_bytes_bf16(const moe_dims& dm); // fp32 partial tiles it needs
 
 // combine
 hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* pos,
                           const float* gate, void* out, hipStream_t s);
+hipError_t launch_dgate_from_parts(const moe_dims& dm, const float* part, int32_t nparts,
+                                   const int32_t* pos, float* dgate, hipStream_t s);
 hipError_t launch_combine_bwd(const moe_dims& dm, const void* dy, const void* y_perm,
                               const int32_t* pos, const float* gate, void* dy_perm,
                               float* dgate, hipStream_t s);
@@ -160,7 +180,9 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const int32_t* idx, const float* gate, const float* dgate,
                             const int32_t* offsets, const int32_t* pos, const int32_t* src,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
-                            float* ws_dl_sel, float* ws_partial, hipStream_t s);
+                            float* ws_dl_sel, float* ws_partial, hipStream_t s,
+                            const float* dgate_part = nullptr, int32_t nparts = 0,
+                            float* dgate_out = nullptr);
 int route_bwd_splits(const moe_dims& dm);   // row splits per expert for the router weight gradient
 // dense form: dropped assignments and the auxiliary losses
 hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float* wr,

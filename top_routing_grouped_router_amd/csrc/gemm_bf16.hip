@@ -88,6 +88,13 @@ struct Args {
   int32_t E, d, f;
   int32_t n_tiles_n;     // row modes: tiles along n
   int32_t grid_pad;      // flat grid size (multiple of 8)
+  // Gate folded into the expert rows (NULL / 0 otherwise; small tiles only):
+  // UP stores g h; DGRAD_DOWN reads dy through x_rows, scales dh by g and
+  // writes <u, h> per row and column tile to dgate_part [rows][n_tiles_n];
+  // WGRAD reads the dy operand of dW2 through x_rows (a_gather).
+  const float* gate_rows;
+  float* dgate_part;
+  int32_t a_gather;
 };
 
 // LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r (128
@@ -701,7 +708,7 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   // per-item lane offsets (bytes from the item's base) and uniform item data
   uint32_t voff_a[KA], voff_b[KB], voff_m[MB];
   int p_item = -1, p_e = 0, p_m0 = 0, p_mend = 0, p_n0 = 0;
-  static_assert(!GATHER || MODE == UP, "gathered A rows in UP only");
+  static_assert(!GATHER || MODE == UP || MODE == DGRAD_DOWN, "gathered A rows: UP, DGRAD_DOWN");
   // gather: xs holds the table entries of this lane's A rows for the item of
   // the next load call (fetched one load call ahead, unconditionally, before
   // that call's operand loads, so waiting for them never waits for operands)
@@ -818,6 +825,18 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
     const int n0 = ds.w * ((MODE == UP) ? kUpHalf : BN);
     const int nch = (MODE == UP) ? kUpHalf / 8 : min(BN, Ndim - n0) / 8;
     uint4 aux_a[(MODE == DGRAD_DOWN) ? kOutIt : 1], aux_b[(MODE == DGRAD_DOWN) ? kOutIt : 1];
+    // folded gate of each readback row, loaded with the saved a/b (before staging)
+    constexpr int kGateIt = (MODE == UP) ? BM * (kUpHalf / 8) / NT
+                                         : ((MODE == DGRAD_DOWN && GATHER) ? kOutIt : 1);
+    float gate_r[kGateIt];
+    if constexpr (MODE == UP || (MODE == DGRAD_DOWN && GATHER)) {
+      constexpr int kRowCh = (MODE == UP) ? kUpHalf / 8 : CH;
+#pragma unroll
+      for (int it = 0; it < kGateIt; ++it) {
+        const int r = min((static_cast<int>(threadIdx.x) + NT * it) / kRowCh, rows - 1);
+        gate_r[it] = g.gate_rows ? g.gate_rows[m0 + r] : 1.0f;
+      }
+    }
     if constexpr (MODE == DGRAD_DOWN) {
 #pragma unroll
       for (int it = 0; it < kOutIt; ++it) {
@@ -851,14 +870,61 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
         if (r >= rows) continue;
         const uint4 av = chunk(r, c), bv = chunk(r, c + kCh);
         const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+        const float gr = gate_r[it];   // folded gate (1 when unfolded): g h
         uint32_t hw[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]) * gr,
+                          silu_f(bf_hi(aw[q])) * bf_hi(bw[q]) * gr);
         const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c * 8;
         *reinterpret_cast<uint4*>(g.c0 + o) = av;
         *reinterpret_cast<uint4*>(g.c1 + o) = bv;
         *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      }
+    } else if constexpr (MODE == DGRAD_DOWN && GATHER) {
+      // gate folded: the staged product is u = dy W2 (rounded); the row's
+      // dgate part is <u, silu(a) b> over this column tile (a 16-lane sum in a
+      // fixed order), dh = g u, then da = dh b silu'(a), db = dh silu(a)
+      static_assert(CH == 16, "one row per 16 lanes");
+#pragma unroll
+      for (int it = 0; it < kOutIt; ++it) {
+        const int v = threadIdx.x + NT * it;
+        const int r = v / CH, c = v % CH;
+        const bool ok = r < rows && c < nch;
+        const uint4 uv = chunk(r, c), av = aux_a[it], bv = aux_b[it];
+        const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+        const float gr = gate_r[it];
+        float part = 0.f;
+        uint32_t daw[4], dbw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float da2[2], db2[2];
+          const float uu[2] = {bf_lo(uw[q]), bf_hi(uw[q])};
+          const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+          const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float sg = sigmoid_f(aa[u]);
+            const float sa = aa[u] * sg;   // silu(a)
+            part = fmaf(uu[u], sa * bb[u], part);
+            const float dh = gr * uu[u];
+            da2[u] = dh * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+            db2[u] = dh * sa;
+          }
+          daw[q] = bf_pack(da2[0], da2[1]);
+          dbw[q] = bf_pack(db2[0], db2[1]);
+        }
+        part = ok ? part : 0.f;
+        part += __shfl_xor(part, 8, 64);
+        part += __shfl_xor(part, 4, 64);
+        part += __shfl_xor(part, 2, 64);
+        part += __shfl_xor(part, 1, 64);
+        if (!ok) continue;
+        if (c == 0) g.dgate_part[static_cast<int64_t>(m0 + r) * g.n_tiles_n + ds.w] = part;
+        const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
+        *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+        *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
       }
     } else {
 #pragma unroll
@@ -1872,7 +1938,7 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   // DMA: wavefront w fills rows 8 w .. 8 w + 7 of A and of B, four rows per
   // instruction; lane l -> row + l / 16, physical chunk l % 16
   uint32_t voa[2], vob[2];
-  int bcol[2];
+  int acol[2], bcol[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = wave * 8 + u * 4 + (lane >> 4);
@@ -1880,9 +1946,11 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
     const int col = logical * 8;
     voa[u] = (m0 + col < Mdim) ? static_cast<uint32_t>((row * Mdim + col) * 2) : kOutOfRange;
     vob[u] = (n0 + col < Ndim) ? static_cast<uint32_t>((row * Ndim + col) * 2) : kOutOfRange;
+    acol[u] = (m0 + col < Mdim) ? col : -1;
     bcol[u] = (n0 + col < Ndim) ? col : -1;
   }
-  const bool gz = GATHER && z != 0;   // B rows gathered from X
+  const bool gz = GATHER && z != 0;                 // B rows gathered from X
+  const bool ga = GATHER && g.a_gather && z == 0;   // A rows (dy) gathered from dY [T, d]
   int32_t xs[NST][2];                 // table entries of the rows of step s in slot s % NST
   auto fetch = [&](int slot, int kt) {
     const int pb = p0 + kt * BKS;
@@ -1894,11 +1962,22 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
     bf16_t* Bs = As + kHalf;
     const bool live = kt < nk;
     const int p = p0 + min(kt, nk - 1) * BKS;
-    const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
-                            live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    const auto ra = ga ? rsrc_at(Asrc + m0, live ? g.x_bytes - m0 * 2 : 0)
+                       : rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
+                                 live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    uint32_t va[2] = {voa[0], voa[1]};
     uint32_t vb[2] = {vob[0], vob[1]};
     __amdgpu_buffer_rsrc_t rb;
     if constexpr (GATHER) {
+      if (ga) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = kt * BKS + wave * 8 + u * 4 + (lane >> 4);   // row of the expert
+          va[u] = (p0 + q < p1 && acol[u] >= 0)
+                      ? (static_cast<uint32_t>(xs[slot][u]) * Mdim + acol[u]) * 2
+                      : kOutOfRange;
+        }
+      }
       rb = gz ? rsrc_at(Bsrc + n0, live ? g.x_bytes - n0 * 2 : 0)
               : rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
                         live ? ((p1 - p) * Ndim - n0) * 2 : 0);
@@ -1916,7 +1995,7 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
                    live ? ((p1 - p) * Ndim - n0) * 2 : 0);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 8 + u * 4) * BM, voa[u]);
+    for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 8 + u * 4) * BM, va[u]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 8 + u * 4) * BN, vb[u]);
   };
@@ -2413,7 +2492,7 @@ hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, 
   const int64_t slots = 2 * static_cast<int64_t>(kCUs);
   const int64_t grid = std::max(std::min(items, slots), (items + kMaxItems - 1) / kMaxItems);
   g.grid_pad = static_cast<int32_t>(pad8(grid));
-  if constexpr (MODE == UP) {
+  if constexpr (MODE == UP || MODE == DGRAD_DOWN) {
     if (g.x_rows) {
       hipLaunchKernelGGL((rows_kernel<MODE, false, true>), dim3(g.grid_pad),
                          dim3(Cfg<false>::THREADS), 0, s, g);
@@ -2427,6 +2506,9 @@ hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, 
 
 template <int MODE>
 hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
+  // the gate-folded epilogues and the gathered dgrad operand exist in the small tile only
+  if (base.gate_rows || base.dgate_part || (MODE == DGRAD_DOWN && base.x_rows))
+    return hipErrorNotSupported;
   Args g = base;
   g.n_tiles_n = n_tiles_n;
   const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
@@ -2587,6 +2669,91 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
                        dim3(kThreads), 0, s, g, tpe, splits, partial);
   }
   return hipGetLastError();
+}
+
+// The gate-folded path runs where every GEMM of the layer takes the small
+// tile and the weight gradients take the one-pass DMA kernel.
+bool folded_bf16_ok(const moe_dims& dm) {
+#if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
+  (void)dm;
+  return false;
+#else
+  return dm.act == MOE_BF16 && !use_big_rows(dm, dm.f / 128, dm.d) &&
+         !use_big_rows(dm, (dm.f + 255) / 256, dm.d) && !use_big_wgrad(dm) &&
+         wgrad_splits_bf16(dm) == 1;
+#endif
+}
+
+int dgate_parts_bf16(const moe_dims& dm) { return (dm.f + Cfg<false>::BN - 1) / Cfg<false>::BN; }
+
+hipError_t launch_up_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
+                                 const int32_t* offsets, const float* gate_rows, const void* w1,
+                                 const void* w3, void* a, void* b, void* hg, hipStream_t s) {
+  if (!folded_bf16_ok(dm) || !x_rows || !gate_rows) return hipErrorNotSupported;
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(x);
+  g.x_rows = x_rows;
+  g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
+  g.b0 = static_cast<const bf16_t*>(w1);
+  g.b1 = static_cast<const bf16_t*>(w3);
+  g.c0 = static_cast<bf16_t*>(a);
+  g.c1 = static_cast<bf16_t*>(b);
+  g.c2 = static_cast<bf16_t*>(hg);
+  g.gate_rows = gate_rows;
+  return launch_rows<UP>(g, dm, dm.f, dm.d, s);
+}
+
+hipError_t launch_dgrad_down_folded_bf16(const moe_dims& dm, const void* dy,
+                                         const int32_t* x_rows, const int32_t* offsets,
+                                         const float* gate_rows, const void* w2, const void* a,
+                                         const void* b, void* da, void* db, float* dgate_part,
+                                         hipStream_t s) {
+  if (!folded_bf16_ok(dm) || !x_rows || !gate_rows || !dgate_part) return hipErrorNotSupported;
+  Args g = base_args(dm, offsets);
+  g.a0 = static_cast<const bf16_t*>(dy);
+  g.x_rows = x_rows;
+  g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
+  g.b0 = static_cast<const bf16_t*>(w2);
+  g.aux0 = static_cast<const bf16_t*>(a);
+  g.aux1 = static_cast<const bf16_t*>(b);
+  g.c0 = static_cast<bf16_t*>(da);
+  g.c1 = static_cast<bf16_t*>(db);
+  g.gate_rows = gate_rows;
+  g.dgate_part = dgate_part;
+  return launch_rows<DGRAD_DOWN>(g, dm, dm.f, dm.d, s);
+}
+
+hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
+                                    const int32_t* offsets, const void* hg, const void* dy,
+                                    const void* da, const void* db, void* dw1, void* dw3,
+                                    void* dw2, hipStream_t s) {
+  if (!folded_bf16_ok(dm) || !x_rows) return hipErrorNotSupported;
+#if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
+  return hipErrorNotSupported;
+#else
+  Args g = base_args(dm, offsets);
+  g.x_rows = x_rows;
+  g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
+  g.a0 = static_cast<const bf16_t*>(dy);   // z = 0: A = dy through the table, B = g h
+  g.b0 = static_cast<const bf16_t*>(hg);
+  g.a1 = static_cast<const bf16_t*>(da);
+  g.aux0 = static_cast<const bf16_t*>(db);
+  g.b1 = static_cast<const bf16_t*>(x);
+  g.c0 = static_cast<bf16_t*>(dw2);
+  g.c1 = static_cast<bf16_t*>(dw1);
+  g.c2 = static_cast<bf16_t*>(dw3);
+  g.a_gather = 1;
+  const int tpe = wgrad_tiles_per_expert<false>(dm);
+  const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+  g.grid_pad = static_cast<int32_t>(grid);
+  if (grid <= static_cast<unsigned>(kCUs))
+    hipLaunchKernelGGL((wgrad_dma_small_kernel<8, true>), dim3(grid), dim3(dmas::NT), 0, s, g,
+                       tpe);
+  else
+    hipLaunchKernelGGL((wgrad_dma_small_kernel<4, true>), dim3(grid), dim3(dmas::NT), 0, s, g,
+                       tpe);
+  return hipGetLastError();
+#endif
 }
 
 // Split-K count for the (small-tile) weight gradients: none when the tiles

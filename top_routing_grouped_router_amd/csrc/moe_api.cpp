@@ -983,4 +983,171 @@ moe_status moe_route_flips(int64_t T, int32_t k, int32_t E, const int32_t* topk_
                     __func__);
 }
 
+// ------------------------------------------------ gate folded into the expert rows
+
+int32_t moe_gate_folded_supported(const moe_dims* dims) {
+  if (check_dims(dims, __func__) != MOE_OK) return 0;
+  return moe::folded_bf16_ok(*dims) ? 1 : 0;
+}
+
+int32_t moe_dgate_parts(const moe_dims* dims) {
+  if (check_dims(dims, __func__) != MOE_OK) return 0;
+  return moe::dgate_parts_bf16(*dims);
+}
+
+namespace {
+moe_status check_folded(const moe_dims* dims, const char* fn) {
+  moe_status st = check_dims(dims, fn);
+  if (st != MOE_OK) return st;
+  if (!moe::folded_bf16_ok(*dims))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: the gate-folded path needs bf16 and dims whose expert GEMMs all take the "
+                "128 x 128 tile (moe_gate_folded_supported)",
+                fn);
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_permute_gates(const moe_dims* dims, const int32_t* topk_idx,
+                             const float* topk_gate, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* pos, int32_t* src_token,
+                             float* gate_perm, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(expert_counts, dm.E);
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(src_token, dm.T * dm.k);
+  MOE_REQUIRE_PTR(gate_perm, dm.T * dm.k);
+  const PermWs need = perm_ws(dm.T, dm.E, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const PermWs w = perm_ws(dm.T, dm.E, workspace);
+  return hip_status(moe::launch_permute(dm, topk_idx, expert_counts, expert_offsets, pos,
+                                        src_token, nullptr, nullptr, w.hist, w.base,
+                                        static_cast<hipStream_t>(stream), topk_gate, gate_perm),
+                    __func__);
+}
+
+moe_status moe_expert_up_folded(const moe_dims* dims, const void* x, const int32_t* src_token,
+                                const int32_t* expert_offsets, const float* gate_perm,
+                                const void* w1, const void* w3, void* a_save, void* b_save,
+                                void* hg_save, void* stream) {
+  moe_status st = check_folded(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(gate_perm, dm.T * dm.k);
+  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(hg_save, dm.T * dm.k * dm.f);
+  return hip_status(moe::launch_up_folded_bf16(dm, x, src_token, expert_offsets, gate_perm, w1,
+                                               w3, a_save, b_save, hg_save,
+                                               static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_dgrad_down_folded(const moe_dims* dims, const void* dy,
+                                        const int32_t* src_token, const int32_t* expert_offsets,
+                                        const float* gate_perm, const void* w2, const void* a_save,
+                                        const void* b_save, void* da, void* db, float* dgate_part,
+                                        void* stream) {
+  moe_status st = check_folded(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, dy, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(gate_perm, dm.T * dm.k);
+  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dgate_part, dm.T * dm.k * moe::dgate_parts_bf16(dm));
+  return hip_status(moe::launch_dgrad_down_folded_bf16(dm, dy, src_token, expert_offsets,
+                                                       gate_perm, w2, a_save, b_save, da, db,
+                                                       dgate_part,
+                                                       static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_dgate_from_parts(const moe_dims* dims, const float* dgate_part,
+                                const int32_t* pos, float* dgate, void* stream) {
+  moe_status st = check_folded(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(dgate_part, dm.T * dm.k * moe::dgate_parts_bf16(dm));
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dgate, dm.T * dm.k);
+  return hip_status(moe::launch_dgate_from_parts(dm, dgate_part, moe::dgate_parts_bf16(dm), pos,
+                                                 dgate, static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_expert_wgrad_folded(const moe_dims* dims, const void* x, const void* dy,
+                                   const int32_t* src_token, const int32_t* expert_offsets,
+                                   const void* hg_save, const void* da, const void* db,
+                                   void* dw1, void* dw3, void* dw2, void* stream) {
+  moe_status st = check_folded(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  st = check_gather(dm, x, src_token, __func__);
+  if (st != MOE_OK) return st;
+  st = check_gather(dm, dy, src_token, __func__);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(hg_save, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
+  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
+  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
+  return hip_status(moe::launch_wgrad_folded_bf16(dm, x, src_token, expert_offsets, hg_save, dy,
+                                                  da, db, dw1, dw3, dw2,
+                                                  static_cast<hipStream_t>(stream)),
+                    __func__);
+}
+
+moe_status moe_route_bwd_folded(const moe_dims* dims, const void* x, const float* w_router,
+                                const int32_t* topk_idx, const float* topk_gate,
+                                const float* dgate_part, const int32_t* expert_offsets,
+                                const int32_t* pos, const int32_t* src_token,
+                                const void* dx_perm, float* dgate, void* dx, float* dw_router,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_folded(dims, __func__);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  MOE_REQUIRE_PTR(x, dm.T * dm.d);
+  MOE_REQUIRE_PTR(w_router, int64_t(dm.E) * dm.d);
+  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
+  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dgate_part, dm.T * dm.k * moe::dgate_parts_bf16(dm));
+  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
+  MOE_REQUIRE_PTR(pos, dm.T * dm.k);
+  MOE_REQUIRE_PTR(src_token, dm.T * dm.k);
+  MOE_OPTIONAL_PTR(dx_perm);
+  MOE_REQUIRE_PTR(dgate, dm.T * dm.k);
+  MOE_REQUIRE_PTR(dx, dm.T * dm.d);
+  MOE_REQUIRE_PTR(dw_router, int64_t(dm.E) * dm.d);
+  const RouteBwdWs need = route_bwd_ws(dm, nullptr);
+  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  if (st != MOE_OK) return st;
+  const RouteBwdWs w = route_bwd_ws(dm, workspace);
+  return hip_status(moe::launch_route_bwd(dm, x, w_router, topk_idx, topk_gate, nullptr,
+                                          expert_offsets, pos, src_token, dx_perm, dx, dw_router,
+                                          w.dl_perm, w.dl_sel, w.partial,
+                                          static_cast<hipStream_t>(stream), dgate_part,
+                                          moe::dgate_parts_bf16(dm), dgate),
+                    __func__);
+}
+
 }  // extern "C"

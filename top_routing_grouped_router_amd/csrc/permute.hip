@@ -103,7 +103,8 @@ namespace {
 
 __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
-    const int32_t* __restrict__ base, int32_t* __restrict__ pos, int32_t* __restrict__ src) {
+    const int32_t* __restrict__ base, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    const float* __restrict__ gate, float* __restrict__ gate_perm) {
   __shared__ unsigned long long bits[kMaxKeys][kWords];
   const int tid = threadIdx.x;
   for (int i = tid; i < E * kWords; i += kThreads) bits[i / kWords][i % kWords] = 0ull;
@@ -130,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
       const int32_t p = base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
       pos[t * k + j] = p;
       src[p] = static_cast<int32_t>(t);
+      if (gate_perm) gate_perm[p] = gate[t * k + j];
     }
   }
 }
@@ -149,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
     const int32_t* __restrict__ hist, int32_t nb, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
-    const uint4* __restrict__ x, uint4* __restrict__ xp, int32_t vpr) {
+    const uint4* __restrict__ x, uint4* __restrict__ xp, int32_t vpr,
+    const float* __restrict__ gate, float* __restrict__ gate_perm) {
   __shared__ unsigned long long bits[kMaxKeys][kWords];
   __shared__ int32_t tot[kMaxKeys], pre[kMaxKeys], base[kMaxKeys + 1];
   __shared__ int32_t spos[kSgTok * 16];
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
         for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
         p = base[e] + pre[e] + rank;
         src[p] = static_cast<int32_t>(t);
+        if (gate_perm) gate_perm[p] = gate[t * k + j];
       }
       pos[t * k + j] = p;
       spos[lane * k + j] = p;
@@ -261,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint4* __re
 
 hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* counts,
                           int32_t* offsets, int32_t* pos, int32_t* src, const void* x,
-                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s) {
+                          void* x_perm, int32_t* ws_hist, int32_t* ws_base, hipStream_t s,
+                          const float* gate, float* gate_perm) {
   const int64_t nb = (dm.T + kPermBlock - 1) / kPermBlock;
   const int elem = (dm.act == MOE_BF16) ? 2 : 4;
   const int32_t vpr = dm.d * elem / 16;
@@ -273,14 +278,15 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
   if (nb > 0 && dm.d * elem <= 1024 && dm.k <= 16) {
     hipLaunchKernelGGL(perm_scatter_gather_kernel, dim3(nb * kSgSplit), dim3(kThreads), 0, s, idx, dm.T,
                        dm.k, dm.E, ws_hist, static_cast<int32_t>(nb), counts, offsets, pos, src,
-                       static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr);
+                       static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr, gate,
+                       gate_perm);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(key_scan_kernel, dim3(1), dim3(256), 0, s, ws_hist,
                      static_cast<int32_t>(nb), dm.E, ws_base, counts, offsets);
   if (nb > 0) {
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k,
-                       dm.E, ws_base, pos, src);
+                       dm.E, ws_base, pos, src, gate, gate_perm);
   }
   if (x && x_perm && dm.T > 0) {
     const int64_t total = dm.T * vpr;

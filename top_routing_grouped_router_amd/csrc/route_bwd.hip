@@ -31,7 +31,8 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ dgate, const float* __restrict__ wr, uint4* __restrict__ dx,
-    float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E) {
+    float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E,
+    const float* __restrict__ dgate_part, int32_t nparts, float* __restrict__ dgate_out) {
   constexpr int kPer = Act<TA>::kPer16B;
   constexpr int KM = K > 0 ? K : 16;
   const int kk = K > 0 ? K : k;
@@ -47,9 +48,25 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     for (int j = 0; j < KM; ++j) {
       const int64_t q = t * kk + min(j, kk - 1);
       g[j] = gate[q];
-      dg[j] = dgate[q];
+      dg[j] = dgate_part ? 0.f : dgate[q];   // folded: from the parts below
       p[j] = pos[q];
       e[j] = idx[q];
+    }
+    if (dgate_part) {
+      // gate folded onto the rows: dg is the sum of the row's column-tile parts
+      // (tile order; 0 for a dropped slot), loaded beside the rows
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
+        float sum = 0.f;
+        for (int q = 0; q < nparts; ++q) sum += pp[q];
+        dg[j] = (p[j] >= 0) ? sum : 0.f;
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < kk) dgate_out[t * kk + j] = dg[j];
+      }
     }
     uint4 rows[KM];
     float w[KM][kPer];
@@ -481,7 +498,8 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const int32_t* idx, const float* gate, const float* dgate,
                             const int32_t* offsets, const int32_t* pos, const int32_t* src,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
-                            float* ws_dl_sel, float* ws_partial, hipStream_t s) {
+                            float* ws_dl_sel, float* ws_partial, hipStream_t s,
+                            const float* dgate_part, int32_t nparts, float* dgate_out) {
   if (dm.T > 0) {
     const int elem = (dm.act == MOE_BF16) ? 2 : 4;
     const int32_t vpr = dm.d * elem / 16;
@@ -491,7 +509,8 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     uint4* dxo = static_cast<uint4*>(dx);
 #define MOE_DX(TA, KC)                                                                        \
   hipLaunchKernelGGL((router_dx_kernel<TA, KC>), dim3(blocks), dim3(kThreads), 0, s, dxp, pos, \
-                     idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, dm.E)
+                     idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, dm.E,   \
+                     dgate_part, nparts, dgate_out)
     if (dm.act == MOE_BF16) {
       switch (dm.k) {
         case 1: MOE_DX(bf16_t, 1); break;

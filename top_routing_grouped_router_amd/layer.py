@@ -16,6 +16,16 @@ Definitional variants: capacity_factor enables per-block expert capacity
 no row), and aux_coef / z_coef add the balancing and z-loss gradients.  Either
 switches the router backward to moe_route_bwd_dense; z_coef also computes the
 per-block z-loss values (moe_router_zloss) in the forward.
+
+fold_gate=True (bf16, gathered input, dims that moe_gate_folded_supported
+accepts) moves the combine's gate onto the expert rows: the forward stores
+h = g silu(a) b (moe_permute_gates, moe_expert_up_folded, moe_expert_down,
+moe_combine without gates) and the backward reads dY through src_token
+(moe_expert_dgrad_down_folded, moe_expert_dgrad_up, moe_expert_wgrad_folded,
+moe_route_bwd_folded, which also sums the dgate parts; with the dense router
+backward moe_dgate_from_parts does that), so neither moe_combine_bwd nor
+dy_perm exists.
+The results equal the unfolded layer's up to rounding.
 """
 from __future__ import annotations
 
@@ -28,8 +38,12 @@ class MoELayer:
     def __init__(self, T: int, d: int, E: int, f: int, k: int, act: torch.dtype,
                  n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda",
                  gather: bool = False, capacity_factor=None, aux_coef: float = 0.0,
-                 z_coef: float = 0.0):
+                 z_coef: float = 0.0, fold_gate: bool = False):
         self.dims = L.make_dims(T, d, E, f, k, act)
+        if fold_gate and not (gather and L.moe_gate_folded_supported(self.dims)):
+            raise ValueError("fold_gate needs gather=True and dims that "
+                             "moe_gate_folded_supported accepts (bf16, 128 x 128 tiles)")
+        self.fold_gate = fold_gate
         self.act = act
         self.gather = gather
         self.capacity = (None if capacity_factor is None else
@@ -68,7 +82,12 @@ class MoELayer:
         self.h = empty(R, f, **ea)
         self.y_perm = empty(R, d, **ea)
         self.y = empty(T, d, **ea)
-        self.dy_perm = empty(R, d, **ea)
+        self.dy_perm = empty(0 if fold_gate else R, d, **ea)
+        self.gate_perm = empty(R, **e32) if fold_gate else None
+        self.dgate_part = (empty(R, L.moe_dgate_parts(self.dims), **e32) if fold_gate
+                           else None)
+        self.da = empty(R, f, **ea) if fold_gate else None
+        self.db = empty(R, f, **ea) if fold_gate else None
         self.dgate = empty(T, k, **e32)
         self.dx_perm = empty(R, d, **ea)
         self.dw1 = empty(E, f, d, **ea)
@@ -97,6 +116,15 @@ class MoELayer:
         if self.z_coef != 0.0:
             L.moe_router_zloss(self.dims, self.logits, self.n_groups, self.group_z,
                                self.workspace)
+        if self.fold_gate:
+            L.moe_permute_gates(self.dims, table, self.topk_gate, self.expert_counts,
+                                self.expert_offsets, self.pos, self.src_token, self.gate_perm,
+                                self.workspace)
+            L.moe_expert_up_folded(self.dims, x, self.src_token, self.expert_offsets,
+                                   self.gate_perm, w1, w3, self.a, self.b, self.h)
+            L.moe_expert_down(self.dims, self.h, self.expert_offsets, w2, self.y_perm)
+            L.moe_combine(self.dims, self.y_perm, self.pos, None, self.y)
+            return
         if self.gather:
             L.moe_permute(self.dims, table, self.expert_counts, self.expert_offsets,
                           self.pos, self.src_token, None, None, self.workspace)
@@ -122,6 +150,28 @@ class MoELayer:
 
     # ------------------------------------------------------------------ backward
     def backward(self, dy, x, wr, w1, w3, w2):
+        if self.fold_gate:
+            L.moe_expert_dgrad_down_folded(self.dims, dy, self.src_token, self.expert_offsets,
+                                           self.gate_perm, w2, self.a, self.b, self.da, self.db,
+                                           self.dgate_part)
+            if self.dense_bwd:
+                L.moe_dgate_from_parts(self.dims, self.dgate_part, self.pos, self.dgate)
+            L.moe_expert_dgrad_up(self.dims, self.da, self.db, self.expert_offsets, w1, w3,
+                                  self.dx_perm)
+            L.moe_expert_wgrad_folded(self.dims, x, dy, self.src_token, self.expert_offsets,
+                                      self.h, self.da, self.db, self.dw1, self.dw3, self.dw2)
+            if not self.dense_bwd:   # the router backward sums the parts into dgate itself
+                L.moe_route_bwd_folded(self.dims, x, wr, self.topk_idx, self.topk_gate,
+                                       self.dgate_part, self.expert_offsets, self.pos,
+                                       self.src_token, self.dx_perm, self.dgate, self.dx,
+                                       self.dwr, self.workspace)
+                return self.dx
+        else:
+            self._experts_bwd(dy, x, w1, w3, w2)
+        self._router_bwd(x, wr)
+        return self.dx
+
+    def _experts_bwd(self, dy, x, w1, w3, w2):
         L.moe_combine_bwd(self.dims, dy, self.y_perm, self.pos, self.topk_gate, self.dy_perm,
                           self.dgate)
         if self.gather:
@@ -133,6 +183,8 @@ class MoELayer:
             L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
                                      self.a, self.b, self.h, self.dy_perm, self.dx_perm,
                                      self.dw1, self.dw3, self.dw2, self.workspace)
+
+    def _router_bwd(self, x, wr):
         if self.dense_bwd:
             L.moe_route_bwd_dense(self.dims, x, wr, self.logits, self.topk_idx, self.topk_gate,
                                   self.dgate, self.pos, self.dx_perm, self.n_groups,
