@@ -88,13 +88,13 @@ struct Args {
   int32_t E, d, f;
   int32_t n_tiles_n;     // row modes: tiles along n
   int32_t grid_pad;      // flat grid size (multiple of 8)
-  // Gate folded into the expert rows (NULL / 0 otherwise; small tiles only):
-  // UP stores g h; DGRAD_DOWN reads dy through x_rows, scales dh by g and
-  // writes <u, h> per row and column tile to dgate_part [rows][n_tiles_n];
-  // WGRAD reads the dy operand of dW2 through x_rows (a_gather).
+  // Gate folded into the expert rows (NULL otherwise; small tiles only): UP
+  // stores g h; DGRAD_DOWN reads dy through x_rows, scales dh by g and writes
+  // <u, h> per row and column tile to dgate_part [rows][n_tiles_n].  (The
+  // folded weight gradients read dy through x_rows: wgrad_dma_small_kernel's
+  // FOLD_A instances.)
   const float* gate_rows;
   float* dgate_part;
-  int32_t a_gather;
 };
 
 // LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r (128
@@ -668,7 +668,7 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
 // Row-split modes (UP, DOWN, DGRAD_DOWN, DGRAD_UP), persistent: G workgroups
 // (at most what is resident at once) each run their item list.
 // GATHER (UP only): the A rows come from X through the gather table x_rows.
-template <int MODE, bool BIG, bool GATHER = false>
+template <int MODE, bool BIG, bool GATHER = false, bool FOLD = false>
 __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   typedef Cfg<BIG> C;
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
@@ -708,7 +708,10 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   // per-item lane offsets (bytes from the item's base) and uniform item data
   uint32_t voff_a[KA], voff_b[KB], voff_m[MB];
   int p_item = -1, p_e = 0, p_m0 = 0, p_mend = 0, p_n0 = 0;
-  static_assert(!GATHER || MODE == UP || MODE == DGRAD_DOWN, "gathered A rows: UP, DGRAD_DOWN");
+  static_assert(!GATHER || MODE == UP || (MODE == DGRAD_DOWN && FOLD),
+                "gathered A rows: UP, and DGRAD_DOWN with the gate folded");
+  static_assert(!FOLD || (GATHER && !BIG && (MODE == UP || MODE == DGRAD_DOWN)),
+                "gate folded: gathered small-tile UP and DGRAD_DOWN");
   // gather: xs holds the table entries of this lane's A rows for the item of
   // the next load call (fetched one load call ahead, unconditionally, before
   // that call's operand loads, so waiting for them never waits for operands)
@@ -826,15 +829,14 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
     const int nch = (MODE == UP) ? kUpHalf / 8 : min(BN, Ndim - n0) / 8;
     uint4 aux_a[(MODE == DGRAD_DOWN) ? kOutIt : 1], aux_b[(MODE == DGRAD_DOWN) ? kOutIt : 1];
     // folded gate of each readback row, loaded with the saved a/b (before staging)
-    constexpr int kGateIt = (MODE == UP) ? BM * (kUpHalf / 8) / NT
-                                         : ((MODE == DGRAD_DOWN && GATHER) ? kOutIt : 1);
+    constexpr int kGateIt = !FOLD ? 1 : (MODE == UP) ? BM * (kUpHalf / 8) / NT : kOutIt;
     float gate_r[kGateIt];
-    if constexpr (MODE == UP || (MODE == DGRAD_DOWN && GATHER)) {
+    if constexpr (FOLD) {
       constexpr int kRowCh = (MODE == UP) ? kUpHalf / 8 : CH;
 #pragma unroll
       for (int it = 0; it < kGateIt; ++it) {
         const int r = min((static_cast<int>(threadIdx.x) + NT * it) / kRowCh, rows - 1);
-        gate_r[it] = g.gate_rows ? g.gate_rows[m0 + r] : 1.0f;
+        gate_r[it] = g.gate_rows[m0 + r];
       }
     }
     if constexpr (MODE == DGRAD_DOWN) {
@@ -870,18 +872,25 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
         if (r >= rows) continue;
         const uint4 av = chunk(r, c), bv = chunk(r, c + kCh);
         const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-        const float gr = gate_r[it];   // folded gate (1 when unfolded): g h
         uint32_t hw[4];
+        if constexpr (FOLD) {   // the row's gate on h
+          const float gr = gate_r[it];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]) * gr,
-                          silu_f(bf_hi(aw[q])) * bf_hi(bw[q]) * gr);
+          for (int q = 0; q < 4; ++q)
+            hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]) * gr,
+                            silu_f(bf_hi(aw[q])) * bf_hi(bw[q]) * gr);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]),
+                            silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+        }
         const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c * 8;
         *reinterpret_cast<uint4*>(g.c0 + o) = av;
         *reinterpret_cast<uint4*>(g.c1 + o) = bv;
         *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       }
-    } else if constexpr (MODE == DGRAD_DOWN && GATHER) {
+    } else if constexpr (MODE == DGRAD_DOWN && FOLD) {
       // gate folded: the staged product is u = dy W2 (rounded); the row's
       // dgate part is <u, silu(a) b> over this column tile (a 16-lane sum in a
       // fixed order), dh = g u, then da = dh b silu'(a), db = dh silu(a)
@@ -1890,7 +1899,7 @@ constexpr int kRowBytes = BM * 2;            // 256
 // the gather table; the table entries of a step's rows are loaded NST - 1
 // steps before its DMA is issued (a register ring, one slot per stage), so
 // waiting for them never waits for DMA still meant to be in flight.
-template <int NST, bool GATHER>
+template <int NST, bool GATHER, bool FOLD_A = false>
 __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args g,
                                                                           int32_t tiles_per_expert) {
   using namespace dmas;
@@ -1950,7 +1959,7 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
     bcol[u] = (n0 + col < Ndim) ? col : -1;
   }
   const bool gz = GATHER && z != 0;                 // B rows gathered from X
-  const bool ga = GATHER && g.a_gather && z == 0;   // A rows (dy) gathered from dY [T, d]
+  const bool ga = FOLD_A && z == 0;   // A rows (dy) gathered from dY [T, d]
   int32_t xs[NST][2];                 // table entries of the rows of step s in slot s % NST
   auto fetch = [&](int slot, int kt) {
     const int pb = p0 + kt * BKS;
@@ -1962,14 +1971,14 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
     bf16_t* Bs = As + kHalf;
     const bool live = kt < nk;
     const int p = p0 + min(kt, nk - 1) * BKS;
-    const auto ra = ga ? rsrc_at(Asrc + m0, live ? g.x_bytes - m0 * 2 : 0)
-                       : rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
-                                 live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    const auto ra = (FOLD_A && ga) ? rsrc_at(Asrc + m0, live ? g.x_bytes - m0 * 2 : 0)
+                                   : rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
+                                             live ? ((p1 - p) * Mdim - m0) * 2 : 0);
     uint32_t va[2] = {voa[0], voa[1]};
     uint32_t vb[2] = {vob[0], vob[1]};
     __amdgpu_buffer_rsrc_t rb;
     if constexpr (GATHER) {
-      if (ga) {
+      if (FOLD_A && ga) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int q = kt * BKS + wave * 8 + u * 4 + (lane >> 4);   // row of the expert
@@ -2493,6 +2502,13 @@ hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, 
   const int64_t grid = std::max(std::min(items, slots), (items + kMaxItems - 1) / kMaxItems);
   g.grid_pad = static_cast<int32_t>(pad8(grid));
   if constexpr (MODE == UP || MODE == DGRAD_DOWN) {
+    if (g.gate_rows) {   // gate folded (gathered rows)
+      hipLaunchKernelGGL((rows_kernel<MODE, false, true, true>), dim3(g.grid_pad),
+                         dim3(Cfg<false>::THREADS), 0, s, g);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (MODE == UP) {
     if (g.x_rows) {
       hipLaunchKernelGGL((rows_kernel<MODE, false, true>), dim3(g.grid_pad),
                          dim3(Cfg<false>::THREADS), 0, s, g);
@@ -2742,16 +2758,15 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
   g.c0 = static_cast<bf16_t*>(dw2);
   g.c1 = static_cast<bf16_t*>(dw1);
   g.c2 = static_cast<bf16_t*>(dw3);
-  g.a_gather = 1;
   const int tpe = wgrad_tiles_per_expert<false>(dm);
   const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
   g.grid_pad = static_cast<int32_t>(grid);
   if (grid <= static_cast<unsigned>(kCUs))
-    hipLaunchKernelGGL((wgrad_dma_small_kernel<8, true>), dim3(grid), dim3(dmas::NT), 0, s, g,
-                       tpe);
+    hipLaunchKernelGGL((wgrad_dma_small_kernel<8, true, true>), dim3(grid), dim3(dmas::NT), 0, s,
+                       g, tpe);
   else
-    hipLaunchKernelGGL((wgrad_dma_small_kernel<4, true>), dim3(grid), dim3(dmas::NT), 0, s, g,
-                       tpe);
+    hipLaunchKernelGGL((wgrad_dma_small_kernel<4, true, true>), dim3(grid), dim3(dmas::NT), 0, s,
+                       g, tpe);
   return hipGetLastError();
 #endif
 }
