@@ -26,7 +26,7 @@ constexpr int kThreads = 256;
 // the compile-time k (0: runtime k <= 16); every load of a token is issued
 // before any is used (indices clamped, invalid slots masked), so a row costs
 // one memory latency rather than one per slot.
-template <typename TA, int K>
+template <typename TA, int K, bool FOLD>
 __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
@@ -48,25 +48,9 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     for (int j = 0; j < KM; ++j) {
       const int64_t q = t * kk + min(j, kk - 1);
       g[j] = gate[q];
-      dg[j] = dgate_part ? 0.f : dgate[q];   // folded: from the parts below
+      dg[j] = FOLD ? 0.f : dgate[q];   // folded: from the parts below
       p[j] = pos[q];
       e[j] = idx[q];
-    }
-    if (dgate_part) {
-      // gate folded onto the rows: dg is the sum of the row's column-tile parts
-      // (tile order; 0 for a dropped slot), loaded beside the rows
-#pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
-        float sum = 0.f;
-        for (int q = 0; q < nparts; ++q) sum += pp[q];
-        dg[j] = (p[j] >= 0) ? sum : 0.f;
-      }
-      if (c == 0) {
-#pragma unroll
-        for (int j = 0; j < KM; ++j)
-          if (j < kk) dgate_out[t * kk + j] = dg[j];
-      }
     }
     uint4 rows[KM];
     float w[KM][kPer];
@@ -77,6 +61,34 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
                         static_cast<int64_t>(c) * kPer;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) w[j][i] = wp[i];
+    }
+    if constexpr (FOLD) {
+      // gate folded onto the rows: dg is the sum of the row's column-tile parts
+      // in tile order (0 for a dropped slot); the first kPartsU parts of every
+      // slot are loaded after the rows, all at once, the rest (wide f) in a loop
+      constexpr int kPartsU = 4;
+      float pv[KM][kPartsU];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
+#pragma unroll
+        for (int q = 0; q < kPartsU; ++q) pv[j][q] = pp[min(q, nparts - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
+        float sum = pv[j][0];
+#pragma unroll
+        for (int q = 1; q < kPartsU; ++q)
+          if (q < nparts) sum += pv[j][q];
+        for (int q = kPartsU; q < nparts; ++q) sum += pp[q];
+        dg[j] = (p[j] >= 0) ? sum : 0.f;
+      }
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (j < kk) dgate_out[t * kk + j] = dg[j];
+      }
     }
     float inner = 0.f;
 #pragma unroll
@@ -508,7 +520,12 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     const uint4* dxp = static_cast<const uint4*>(dx_perm);
     uint4* dxo = static_cast<uint4*>(dx);
 #define MOE_DX(TA, KC)                                                                        \
-  hipLaunchKernelGGL((router_dx_kernel<TA, KC>), dim3(blocks), dim3(kThreads), 0, s, dxp, pos, \
+  if (dgate_part)                                                                             \
+    hipLaunchKernelGGL((router_dx_kernel<TA, KC, true>), dim3(blocks), dim3(kThreads), 0, s,   \
+                       dxp, pos, idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, \
+                       dm.E, dgate_part, nparts, dgate_out);                                   \
+  else                                                                                        \
+    hipLaunchKernelGGL((router_dx_kernel<TA, KC, false>), dim3(blocks), dim3(kThreads), 0, s, dxp, pos, \
                      idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, dm.E,   \
                      dgate_part, nparts, dgate_out)
     if (dm.act == MOE_BF16) {
