@@ -122,3 +122,23 @@ def test_folded_calls_reject_unsupported_dims():
         L.moe_expert_up_folded(dims, z, zi, zi, zf, z, z, z, z, z)
     with pytest.raises(ValueError):
         MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, torch.bfloat16, gather=True, fold_gate=True)
+
+
+def test_folded_layer_on_an_empty_batch():
+    """T = 0: every folded call runs, the weight gradients are zero."""
+    print("\n[case] folded T=0", flush=True)
+    T, d, E, f, k = 0, 256, 16, 256, 4
+    layer = MoELayer(T, d, E, f, k, torch.bfloat16, n_groups=1, gather=True, fold_gate=True)
+    x = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    wr = torch.randn((E, d), device="cuda")
+    w1 = torch.randn((E, f, d), device="cuda").to(torch.bfloat16)
+    w3 = torch.randn((E, f, d), device="cuda").to(torch.bfloat16)
+    w2 = torch.randn((E, d, f), device="cuda").to(torch.bfloat16)
+    for name in ("dw1", "dw3", "dw2", "dwr"):
+        getattr(layer, name).fill_(float("nan"))
+    layer.step(x, wr, w1, w3, w2, dy)
+    torch.cuda.synchronize()
+    for name in ("dw1", "dw3", "dw2", "dwr"):
+        assert torch.all(getattr(layer, name) == 0), name
+    assert int(layer.expert_offsets[E].item()) == 0

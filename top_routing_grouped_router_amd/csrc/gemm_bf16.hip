@@ -2705,6 +2705,7 @@ int dgate_parts_bf16(const moe_dims& dm) { return (dm.f + Cfg<false>::BN - 1) / 
 hipError_t launch_up_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
                                  const int32_t* offsets, const float* gate_rows, const void* w1,
                                  const void* w3, void* a, void* b, void* hg, hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;   // no expert rows
   if (!folded_bf16_ok(dm) || !x_rows || !gate_rows) return hipErrorNotSupported;
   Args g = base_args(dm, offsets);
   g.a0 = static_cast<const bf16_t*>(x);
@@ -2724,6 +2725,7 @@ hipError_t launch_dgrad_down_folded_bf16(const moe_dims& dm, const void* dy,
                                          const float* gate_rows, const void* w2, const void* a,
                                          const void* b, void* da, void* db, float* dgate_part,
                                          hipStream_t s) {
+  if (dm.T * dm.k == 0) return hipSuccess;   // no expert rows
   if (!folded_bf16_ok(dm) || !x_rows || !gate_rows || !dgate_part) return hipErrorNotSupported;
   Args g = base_args(dm, offsets);
   g.a0 = static_cast<const bf16_t*>(dy);
@@ -2743,6 +2745,9 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
                                     const int32_t* offsets, const void* hg, const void* dy,
                                     const void* da, const void* db, void* dw1, void* dw3,
                                     void* dw2, hipStream_t s) {
+  // no expert rows: every weight gradient is zero, as the unfolded call writes it
+  if (dm.T * dm.k == 0)
+    return launch_wgrad_bf16(dm, x, x_rows, offsets, hg, dy, da, db, dw1, dw3, dw2, nullptr, s);
   if (!folded_bf16_ok(dm) || !x_rows) return hipErrorNotSupported;
 #if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
   return hipErrorNotSupported;
