@@ -11,13 +11,14 @@ By default the permutation is a plan only and moe_expert_up / moe_expert_wgrad
 read their input rows from X through src_token (the *_gather calls, reported
 as moe_permute_plan, moe_expert_up_gather, moe_expert_wgrad_gather);
 --no-gather materialises x_perm instead.  Both compute the same bits.
-Where the dims allow it (bf16, every expert GEMM on the 128 x 128 tile: C2,
-C3) the gate is folded onto the expert rows by default: moe_permute_gates ->
+Where the dims allow it (bf16 with one-pass weight gradients: C2-C5) the
+gate is folded onto the expert rows by default: moe_permute_gates ->
 moe_expert_up_folded -> moe_expert_down -> moe_combine (no gates) ->
 moe_expert_dgrad_down_folded -> moe_expert_dgrad_up -> moe_expert_wgrad_folded
--> moe_route_bwd_folded (which sums the dgate parts), with no moe_combine_bwd
-and no dy_perm; --no-fold keeps the gate in the combine.  config.gate says
-which.
+-> moe_route_bwd_folded (which sums the dgate parts; with more than two parts
+per row moe_dgate_from_parts -> moe_route_bwd instead), with no
+moe_combine_bwd and no dy_perm; --no-fold keeps the gate in the combine.
+config.gate says which.
 Inputs and weights are resident in HBM before timing starts.  Prints one JSON
 line.
 
@@ -537,8 +538,12 @@ def main():
                  "moe_expert_up_folded", "moe_expert_down", "moe_combine",
                  "moe_expert_dgrad_down_folded", "moe_dgate_from_parts", "moe_expert_dgrad_up",
                  "moe_expert_wgrad_folded", "moe_route_bwd_folded", "moe_route_bwd_dense"]
-        if layer.dense_bwd:
+        if layer.dense_bwd or L.moe_dgate_parts(dm) > 2:
+            # the parts are summed once first (more than two per row would be
+            # reloaded by every dX thread of the router backward)
             order.remove("moe_route_bwd_folded")
+            if not layer.dense_bwd:
+                order.insert(order.index("moe_route_bwd_dense"), "moe_route_bwd")
         else:   # the sparse router backward sums the dgate parts itself
             order.remove("moe_dgate_from_parts")
         by_name = dict(calls)

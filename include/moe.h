@@ -300,14 +300,16 @@ moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
  *   da = dh b silu'(a), db = dh silu(a)            (as moe_expert_dgrad_down),
  *   dgate[t,j] = <dY[t], W2 h> = <u, silu(a) b>     (per row, summed over f),
  *   dW2 = sum_rows dY[src]^T hg, dW1 = da^T X[src], dW3 = db^T X[src].
- * dgate comes out as parts, one per 128-column tile of f, in dgate_part
+ * dgate comes out as parts, one per column tile of f (128 wide, 256 where the
+ * output-gradient GEMM takes the big tile), in dgate_part
  * [T*k, moe_dgate_parts(dims)] fp32; moe_dgate_from_parts adds them in tile
  * order into dgate [T,k] (0 for a dropped slot, pos < 0).  The results match
  * the unfolded calls up to rounding (one rounding of g h instead of one of
  * h and one of g dY).
  *
- * Supported where every expert GEMM of the dims takes the 128 x 128 tile:
- * bf16, and moe_gate_folded_supported(dims) == 1 (otherwise each call returns
+ * Supported for bf16 dims whose weight gradients take a one-pass kernel
+ * (not the split-K form used when E x output tiles are few):
+ * moe_gate_folded_supported(dims) == 1 (otherwise each call returns
  * MOE_ERR_UNSUPPORTED).  The expert input is always X [T,d] through
  * src_token; dY has the same shape and the same 2^31-byte bound.
  *   moe_permute_gates:   moe_permute (no row copy) plus gate_perm [T*k] fp32,

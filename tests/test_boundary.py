@@ -173,19 +173,20 @@ def test_greedy_placement_ties_and_zero_matrix():
 
 
 def test_gate_folded_support_query():
-    """The folded path is offered where every expert GEMM takes the 128 x 128
-    tile and the weight gradients the one-pass kernel (bf16 only)."""
+    """The folded path is offered on the LDS-DMA kernels (both tiles) where the
+    weight gradients take a one-pass kernel, bf16 only; one dgate part per
+    column tile of the output-gradient GEMM (128 wide, 256 on the big tile)."""
     lib = L.lib()
     for kw, ok, parts in [(dict(T=16384, d=256, E=16, f=256, k=4), 1, 2),      # C2
                           (dict(T=16384, d=256, E=64, f=64, k=4), 1, 1),       # C3
                           (dict(T=1000, d=256, E=16, f=192, k=3), 1, 2),
-                          (dict(T=16384, d=2048, E=64, f=1024, k=6), 0, 8),    # C5: big tiles
+                          (dict(T=16384, d=2048, E=64, f=1024, k=6), 1, 4),    # C5: big tiles
                           (dict(T=1000, d=256, E=8, f=192, k=3), 0, 2)]:       # split-K wgrad
         dm = dims(**kw)
         assert lib.moe_gate_folded_supported(ctypes.byref(dm)) == ok, kw
         assert lib.moe_dgate_parts(ctypes.byref(dm)) == parts, kw
     dm = dims(T=2048, d=256, E=16, f=256, k=4, act=0)   # fp32
     assert lib.moe_gate_folded_supported(ctypes.byref(dm)) == 0
-    big = dims(T=16384, d=2048, E=64, f=1024, k=6)
-    st = lib.moe_expert_up_folded(ctypes.byref(big), *([FAKE] * 9), None)
+    split = dims(T=1000, d=256, E=8, f=192, k=3)   # split-K weight gradients
+    st = lib.moe_expert_up_folded(ctypes.byref(split), *([FAKE] * 9), None)
     assert st == UNSUP and "moe_gate_folded_supported" in L.last_error()

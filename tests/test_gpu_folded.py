@@ -7,7 +7,8 @@ The oracle's routing and block counts are copied into the layer, so integer
 outputs compare bit for bit and floats are held to the workload's tolerance.
 Cases: C2 and C3 at full size (the 8- and 4-stage weight-gradient rings), a
 ragged shape whose f = 192 leaves a partial column tile for the dgate parts,
-and C2 with capacity and both losses (dropped slots, dense router backward).
+C2 with capacity and both losses (dropped slots, dense router backward), and
+a shape whose UP, dgrad_down and weight gradients all take the big tile.
 """
 import numpy as np
 import pytest
@@ -28,6 +29,8 @@ CASES = {
     "c3": ("c3", {}, 8, None, 0.0, 0.0),
     "ragged_f192": ("c2", dict(T=1000, d=256, E=16, f=192, k=3), 4, None, 0.0, 0.0),
     "c2_cap1_losses": ("c2", dict(T=4096), 4, 1.0, 0.01, 0.001),
+    # UP, dgrad_down and the weight gradients on the 256 x 256 tile
+    "big_tiles": ("c5", dict(T=8192, d=1024, E=16, f=1024, k=4), 4, None, 0.0, 0.0),
 }
 
 
@@ -112,7 +115,7 @@ def test_folded_matches_unfolded_layer():
 
 
 def test_folded_calls_reject_unsupported_dims():
-    cfg = get_config("c5")
+    cfg = get_config("c2", T=1000, d=256, E=8, f=192, k=3)   # split-K weight gradients
     dims = L.make_dims(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, torch.bfloat16)
     assert not L.moe_gate_folded_supported(dims)
     z = torch.empty(16, dtype=torch.bfloat16, device="cuda")

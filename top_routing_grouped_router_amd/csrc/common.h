@@ -146,7 +146,7 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
                              const int32_t* offsets, const void* h, const void* dy_perm,
                              const void* da, const void* db, void* dw1, void* dw3, void* dw2,
                              float* partial, hipStream_t s);
-// gate folded into the expert rows (small tiles, gathered expert input): UP
+// gate folded into the expert rows (gathered expert input): UP
 // stores g h; DGRAD_DOWN reads dy through the table, scales dh by g and writes
 // per-row dgate parts; WGRAD reads dy through the table for dW2
 bool folded_bf16_ok(const moe_dims& dm);

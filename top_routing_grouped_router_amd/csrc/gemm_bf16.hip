@@ -88,11 +88,10 @@ struct Args {
   int32_t E, d, f;
   int32_t n_tiles_n;     // row modes: tiles along n
   int32_t grid_pad;      // flat grid size (multiple of 8)
-  // Gate folded into the expert rows (NULL otherwise; small tiles only): UP
-  // stores g h; DGRAD_DOWN reads dy through x_rows, scales dh by g and writes
-  // <u, h> per row and column tile to dgate_part [rows][n_tiles_n].  (The
-  // folded weight gradients read dy through x_rows: wgrad_dma_small_kernel's
-  // FOLD_A instances.)
+  // Gate folded into the expert rows (NULL otherwise): UP stores g h;
+  // DGRAD_DOWN reads dy through x_rows, scales dh by g and writes <u, h> per
+  // row and column tile to dgate_part [rows][n_tiles_n].  (The folded weight
+  // gradients read dy through x_rows: the FOLD_A instances.)
   const float* gate_rows;
   float* dgate_part;
 };
@@ -1235,7 +1234,7 @@ constexpr int BM = 256, BN = 256, BKS = 64, NST = 2, NT = 512, WAVES_N = 4, FM =
 constexpr int kStage = (BM + BN) * BKS;   // elements per stage (64 KB)
 }  // namespace dma64
 
-template <int MODE>
+template <int MODE, bool FOLD = false>
 __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
   using namespace dma64;
   static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
@@ -1413,9 +1412,18 @@ __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
       const uint4 av = chunk_at(rr, c), bv = chunk_at(rr, c + kCh);
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
       uint32_t hw[4];
+      if constexpr (FOLD) {   // the row's gate on h
+        const float gr = g.gate_rows[m0 + rr];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]), silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+        for (int q = 0; q < 4; ++q)
+          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]) * gr,
+                          silu_f(bf_hi(aw[q])) * bf_hi(bw[q]) * gr);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]),
+                          silu_f(bf_hi(aw[q])) * bf_hi(bw[q]));
+      }
       const int64_t o = static_cast<int64_t>(m0 + rr) * f + n0 + c * 8;
       *reinterpret_cast<uint4*>(g.c0 + o) = av;
       *reinterpret_cast<uint4*>(g.c1 + o) = bv;
@@ -1463,7 +1471,7 @@ __device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memo
 
 // GATHER: as in the small-tile kernel, the x operand of dW1 and dW3 comes from
 // X through the gather table, entries fetched NST - 1 = 3 steps ahead.
-template <bool GATHER>
+template <bool GATHER, bool FOLD_A = false>
 __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t tiles_per_expert) {
   using namespace dmaw;
   // four stage arrays (distinct objects: a transposing read of one stage is
@@ -1505,7 +1513,7 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   // DMA: wavefront w fills rows 4 w .. 4 w + 3 of the A and the B tile, two
   // rows (1 KB) per instruction; lane l -> row + l / 32, physical chunk l % 32
   uint32_t voa[2], vob[2];
-  int bcol[2];
+  int acol[2], bcol[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = wave * 4 + u * 2 + (lane >> 5);
@@ -1513,9 +1521,11 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
     const int col = logical * 8;
     voa[u] = (m0 + col < Mdim) ? static_cast<uint32_t>((row * Mdim + col) * 2) : kOutOfRange;
     vob[u] = (n0 + col < Ndim) ? static_cast<uint32_t>((row * Ndim + col) * 2) : kOutOfRange;
+    acol[u] = (m0 + col < Mdim) ? col : -1;
     bcol[u] = (n0 + col < Ndim) ? col : -1;
   }
   const bool gz = GATHER && z != 0;   // B rows gathered from X
+  const bool ga = FOLD_A && z == 0;   // A rows (dy) gathered from dY [T, d]
   int32_t xs[NST][2];                 // table entries of the rows of step s in slot s % NST
   auto fetch = [&](int slot, int kt) {
     const int pb = p0 + kt * BKS;
@@ -1529,11 +1539,22 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
     bf16_t* Bs = As + BKS * BM;
     const bool live = kt < nk;
     const int p = p0 + min(kt, nk - 1) * BKS;
-    const auto ra = rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
-                            live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    const auto ra = (FOLD_A && ga) ? rsrc_at(Asrc + m0, live ? g.x_bytes - m0 * 2 : 0)
+                                   : rsrc_at(Asrc + static_cast<int64_t>(p) * Mdim + m0,
+                                             live ? ((p1 - p) * Mdim - m0) * 2 : 0);
+    uint32_t va[2] = {voa[0], voa[1]};
     uint32_t vb[2] = {vob[0], vob[1]};
     __amdgpu_buffer_rsrc_t rb;
     if constexpr (GATHER) {
+      if (FOLD_A && ga) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int q = kt * BKS + wave * 4 + u * 2 + (lane >> 5);   // row of the expert
+          va[u] = (p0 + q < p1 && acol[u] >= 0)
+                      ? (static_cast<uint32_t>(xs[slot][u]) * Mdim + acol[u]) * 2
+                      : kOutOfRange;
+        }
+      }
       rb = gz ? rsrc_at(Bsrc + n0, live ? g.x_bytes - n0 * 2 : 0)
               : rsrc_at(Bsrc + static_cast<int64_t>(p) * Ndim + n0,
                         live ? ((p1 - p) * Ndim - n0) * 2 : 0);
@@ -1551,7 +1572,7 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
                    live ? ((p1 - p) * Ndim - n0) * 2 : 0);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 4 + u * 2) * BM, voa[u]);
+    for (int u = 0; u < 2; ++u) dma::dma16(ra, As + (wave * 4 + u * 2) * BM, va[u]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) dma::dma16(rb, Bs + (wave * 4 + u * 2) * BN, vb[u]);
   };
@@ -1668,9 +1689,10 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
 // [64 k] (128-byte rows, chunks XORed with (row >> 1) & 7) + B [64 k][256 n]
 // (512-byte rows as they lie in W); two distinct stage arrays of 64 KB, the
 // step count padded to even with a zero step.
-template <int MODE>
+template <int MODE, bool FOLD = false>
 __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
   using namespace dma64;
+  static_assert(!FOLD || MODE == DGRAD_DOWN, "gate folded: DGRAD_DOWN");
   using dma::dma16;
   using dma::wait_vm;
   static_assert(MODE == DGRAD_DOWN || MODE == DGRAD_UP, "dgrad modes");
@@ -1703,7 +1725,12 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
   for (int u = 0; u < 4; ++u) {
     const int row = wave * 32 + u * 8 + (lane >> 3);    // A: 8 rows of 128 B
     const int logical = (lane & 7) ^ ((row >> 1) & 7);
-    voa[u] = (row * lda + logical * 8) * 2;
+    if constexpr (FOLD) {   // dy rows through the table (rows past the tile read zeros)
+      const uint32_t src = static_cast<uint32_t>(g.x_rows[min(m0 + row, mend - 1)]);
+      voa[u] = (m0 + row < mend) ? (src * lda + logical * 8) * 2 : kOutOfRange;
+    } else {
+      voa[u] = (row * lda + logical * 8) * 2;
+    }
     const int brow = wave * 8 + u * 2 + (lane >> 5);    // B: 2 rows of 512 B
     const int blog = (lane & 31) ^ (4 * (brow & 3));
     vob[u] = (n0 + blog * 8 < Ndim) ? static_cast<uint32_t>((brow * ldb + blog * 8) * 2)
@@ -1718,11 +1745,13 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
       half = 1;
       k0 -= f;
     }
-    const bf16_t* abase = ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
-                          static_cast<int64_t>(m0) * lda + k0;
+    const bf16_t* abase = FOLD ? g.a0 + k0
+                               : ((MODE == DGRAD_UP && half) ? g.a1 : g.a0) +
+                                     static_cast<int64_t>(m0) * lda + k0;
     const bf16_t* wbase = ((MODE == DGRAD_UP && half) ? g.b1 : g.b0) + e * E_fd +
                           static_cast<int64_t>(k0) * ldb + n0;
-    const auto ra = rsrc_at(abase, live ? ((mend - m0) * lda - k0) * 2 : 0);
+    const auto ra = rsrc_at(abase, !live ? 0 : FOLD ? g.x_bytes - k0 * 2
+                                                    : ((mend - m0) * lda - k0) * 2);
     const auto rb = rsrc_at(wbase, live ? ((Kh - k0) * ldb - n0) * 2 : 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma16(ra, As + (wave * 32 + u * 8) * BKS, voa[u]);
@@ -1848,6 +1877,56 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
   }
   __syncthreads();
   const int nch = min(BN, Ndim - n0) / 8;
+  if constexpr (FOLD) {
+    // gate folded: the staged product is u = dy W2 (rounded); the row's dgate
+    // part is <u, silu(a) b> over this column tile (a 32-lane sum in a fixed
+    // order: 32 lanes hold one row), dh = g u, da = dh b silu'(a), db = dh silu(a)
+    static_assert(BN / 8 == 32, "one row per 32 lanes");
+    for (int v = tid; v < BM * (BN / 8); v += NT) {
+      const int rr = v / (BN / 8), c = v % (BN / 8);
+      const bool ok = rr < rows && c < nch;
+      const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
+      const uint4 uv = *reinterpret_cast<const uint4*>(row_ptr(rr) + ((c ^ (rr & 15)) << 3));
+      const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
+      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + ol);
+      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + ol);
+      const float gr = g.gate_rows[m0 + rl];
+      const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
+      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      float part = 0.f;
+      uint32_t daw[4], dbw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float da2[2], db2[2];
+        const float uu[2] = {bf_lo(uw[q]), bf_hi(uw[q])};
+        const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+        const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float sg = sigmoid_f(aa[u]);
+          const float sa = aa[u] * sg;   // silu(a)
+          part = fmaf(uu[u], sa * bb[u], part);
+          const float dh = gr * uu[u];
+          da2[u] = dh * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+          db2[u] = dh * sa;
+        }
+        daw[q] = bf_pack(da2[0], da2[1]);
+        dbw[q] = bf_pack(db2[0], db2[1]);
+      }
+      part = ok ? part : 0.f;
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 8, 64);
+      part += __shfl_xor(part, 4, 64);
+      part += __shfl_xor(part, 2, 64);
+      part += __shfl_xor(part, 1, 64);
+      if (!ok) continue;
+      if (c == 0) g.dgate_part[static_cast<int64_t>(m0 + rr) * g.n_tiles_n + nt] = part;
+      const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
+      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+    }
+    return;
+  }
   for (int v = tid; v < BM * (BN / 8); v += NT) {
     const int rr = v / (BN / 8), c = v % (BN / 8);
     if (rr >= rows || c >= nch) continue;
@@ -2522,21 +2601,38 @@ hipError_t launch_rows_small(const Args& base, int64_t R, int E, int n_tiles_n, 
 
 template <int MODE>
 hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hipStream_t s) {
-  // the gate-folded epilogues and the gathered dgrad operand exist in the small tile only
-  if (base.gate_rows || base.dgate_part || (MODE == DGRAD_DOWN && base.x_rows))
-    return hipErrorNotSupported;
+  // gate folded (UP, DGRAD_DOWN): the FOLD instances; a gathered dgrad
+  // operand exists only with the gate folded
+  const bool fold = base.gate_rows != nullptr;
+  if (fold && !(MODE == UP || MODE == DGRAD_DOWN)) return hipErrorNotSupported;
+  if (!fold && MODE == DGRAD_DOWN && base.x_rows) return hipErrorNotSupported;
   Args g = base;
   g.n_tiles_n = n_tiles_n;
   const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
   g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
 #ifndef MOE_NO_DMA
   if constexpr (MODE == UP || MODE == DOWN) {
+    if constexpr (MODE == UP) {
+      if (fold) {
+        hipLaunchKernelGGL((dma_rows_kernel<MODE, true>), dim3(g.grid_pad), dim3(dma64::NT), 0,
+                           s, g);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((dma_rows_kernel<MODE>), dim3(g.grid_pad), dim3(dma64::NT), 0, s, g);
   } else {
+    if constexpr (MODE == DGRAD_DOWN) {
+      if (fold) {
+        hipLaunchKernelGGL((dgrad_dma_kernel<MODE, true>), dim3(g.grid_pad), dim3(dma64::NT), 0,
+                           s, g);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((dgrad_dma_kernel<MODE>), dim3(g.grid_pad), dim3(dma64::NT), 0, s, g);
   }
   return hipGetLastError();
 #endif
+  if (fold) return hipErrorNotSupported;
   if (g.x_rows) return hipErrorNotSupported;   // the register-staged big tile has no gather
   hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
                      g);
@@ -2687,20 +2783,24 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   return hipGetLastError();
 }
 
-// The gate-folded path runs where every GEMM of the layer takes the small
-// tile and the weight gradients take the one-pass DMA kernel.
+// The gate-folded path runs on the LDS-DMA kernels (small and big tiles) where
+// the weight gradients take a one-pass kernel (not the split-K stream).
 bool folded_bf16_ok(const moe_dims& dm) {
 #if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
   (void)dm;
   return false;
 #else
-  return dm.act == MOE_BF16 && !use_big_rows(dm, dm.f / 128, dm.d) &&
-         !use_big_rows(dm, (dm.f + 255) / 256, dm.d) && !use_big_wgrad(dm) &&
-         wgrad_splits_bf16(dm) == 1;
+  return dm.act == MOE_BF16 && (use_big_wgrad(dm) || wgrad_splits_bf16(dm) == 1);
 #endif
 }
 
-int dgate_parts_bf16(const moe_dims& dm) { return (dm.f + Cfg<false>::BN - 1) / Cfg<false>::BN; }
+// dgate parts per row: one per column tile of DGRAD_DOWN (256 wide on the big
+// tile, 128 on the small one)
+int dgate_parts_bf16(const moe_dims& dm) {
+  const int n_big = (dm.f + 255) / 256;
+  if (use_big_rows(dm, n_big, dm.d)) return n_big;
+  return (dm.f + Cfg<false>::BN - 1) / Cfg<false>::BN;
+}
 
 hipError_t launch_up_folded_bf16(const moe_dims& dm, const void* x, const int32_t* x_rows,
                                  const int32_t* offsets, const float* gate_rows, const void* w1,
@@ -2763,6 +2863,13 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
   g.c0 = static_cast<bf16_t*>(dw2);
   g.c1 = static_cast<bf16_t*>(dw1);
   g.c2 = static_cast<bf16_t*>(dw3);
+  if (use_big_wgrad(dm)) {
+    const int tpe = wgrad_tiles_per_expert<true>(dm);
+    const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+    g.grid_pad = static_cast<int32_t>(grid);
+    hipLaunchKernelGGL((wgrad_dma_kernel<true, true>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
+    return hipGetLastError();
+  }
   const int tpe = wgrad_tiles_per_expert<false>(dm);
   const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
   g.grid_pad = static_cast<int32_t>(grid);

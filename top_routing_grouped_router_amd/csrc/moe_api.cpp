@@ -1001,8 +1001,8 @@ moe_status check_folded(const moe_dims* dims, const char* fn) {
   if (st != MOE_OK) return st;
   if (!moe::folded_bf16_ok(*dims))
     return fail(MOE_ERR_UNSUPPORTED,
-                "%s: the gate-folded path needs bf16 and dims whose expert GEMMs all take the "
-                "128 x 128 tile (moe_gate_folded_supported)",
+                "%s: the gate-folded path needs bf16 and dims whose weight gradients take a "
+                "one-pass kernel (moe_gate_folded_supported)",
                 fn);
   return MOE_OK;
 }

@@ -23,8 +23,8 @@ h = g silu(a) b (moe_permute_gates, moe_expert_up_folded, moe_expert_down,
 moe_combine without gates) and the backward reads dY through src_token
 (moe_expert_dgrad_down_folded, moe_expert_dgrad_up, moe_expert_wgrad_folded,
 moe_route_bwd_folded, which also sums the dgate parts; with the dense router
-backward moe_dgate_from_parts does that), so neither moe_combine_bwd nor
-dy_perm exists.
+backward, or more than two parts per row, moe_dgate_from_parts sums them
+first), so neither moe_combine_bwd nor dy_perm exists.
 The results equal the unfolded layer's up to rounding.
 """
 from __future__ import annotations
@@ -42,7 +42,7 @@ class MoELayer:
         self.dims = L.make_dims(T, d, E, f, k, act)
         if fold_gate and not (gather and L.moe_gate_folded_supported(self.dims)):
             raise ValueError("fold_gate needs gather=True and dims that "
-                             "moe_gate_folded_supported accepts (bf16, 128 x 128 tiles)")
+                             "moe_gate_folded_supported accepts (bf16, one-pass weight gradients)")
         self.fold_gate = fold_gate
         self.act = act
         self.gather = gather
@@ -154,13 +154,16 @@ class MoELayer:
             L.moe_expert_dgrad_down_folded(self.dims, dy, self.src_token, self.expert_offsets,
                                            self.gate_perm, w2, self.a, self.b, self.da, self.db,
                                            self.dgate_part)
-            if self.dense_bwd:
+            # with more than two parts per row the router backward's dX threads
+            # would each reload them all: sum them once instead
+            parts_first = self.dense_bwd or L.moe_dgate_parts(self.dims) > 2
+            if parts_first:
                 L.moe_dgate_from_parts(self.dims, self.dgate_part, self.pos, self.dgate)
             L.moe_expert_dgrad_up(self.dims, self.da, self.db, self.expert_offsets, w1, w3,
                                   self.dx_perm)
             L.moe_expert_wgrad_folded(self.dims, x, dy, self.src_token, self.expert_offsets,
                                       self.h, self.da, self.db, self.dw1, self.dw3, self.dw2)
-            if not self.dense_bwd:   # the router backward sums the parts into dgate itself
+            if not parts_first:   # the router backward sums the parts into dgate itself
                 L.moe_route_bwd_folded(self.dims, x, wr, self.topk_idx, self.topk_gate,
                                        self.dgate_part, self.expert_offsets, self.pos,
                                        self.src_token, self.dx_perm, self.dgate, self.dx,
