@@ -894,8 +894,16 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
       // dgate part is <u, silu(a) b> over this column tile (a 16-lane sum in a
       // fixed order), dh = g u, then da = dh b silu'(a), db = dh silu(a)
       static_assert(CH == 16, "one row per 16 lanes");
+      // the da/db stores go out first; the parts of a group of iterations wait
+      // in registers and their 16-lane sums run together (xor 8, 4, 2, 1)
+      constexpr int kGrp = kOutIt < 4 ? kOutIt : 4;
+      static_assert(kOutIt % kGrp == 0, "whole groups");
 #pragma unroll
-      for (int it = 0; it < kOutIt; ++it) {
+      for (int i0 = 0; i0 < kOutIt; i0 += kGrp) {
+      float partv[kGrp];
+#pragma unroll
+      for (int ig = 0; ig < kGrp; ++ig) {
+        const int it = i0 + ig;
         const int v = threadIdx.x + NT * it;
         const int r = v / CH, c = v % CH;
         const bool ok = r < rows && c < nch;
@@ -923,16 +931,24 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
           daw[q] = bf_pack(da2[0], da2[1]);
           dbw[q] = bf_pack(db2[0], db2[1]);
         }
-        part = ok ? part : 0.f;
-        part += __shfl_xor(part, 8, 64);
-        part += __shfl_xor(part, 4, 64);
-        part += __shfl_xor(part, 2, 64);
-        part += __shfl_xor(part, 1, 64);
-        if (!ok) continue;
-        if (c == 0) g.dgate_part[static_cast<int64_t>(m0 + r) * g.n_tiles_n + ds.w] = part;
-        const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
-        *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
-        *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+        partv[ig] = ok ? part : 0.f;
+        if (ok) {
+          const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
+          *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+          *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+        }
+      }
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+        for (int ig = 0; ig < kGrp; ++ig) partv[ig] += __shfl_xor(partv[ig], m, 64);
+#pragma unroll
+      for (int ig = 0; ig < kGrp; ++ig) {
+        const int v = threadIdx.x + NT * (i0 + ig);
+        const int r = v / CH, c = v % CH;
+        if (c == 0 && r < rows)
+          g.dgate_part[static_cast<int64_t>(m0 + r) * g.n_tiles_n + ds.w] = partv[ig];
+      }
       }
     } else {
 #pragma unroll
@@ -1882,7 +1898,17 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
     // part is <u, silu(a) b> over this column tile (a 32-lane sum in a fixed
     // order: 32 lanes hold one row), dh = g u, da = dh b silu'(a), db = dh silu(a)
     static_assert(BN / 8 == 32, "one row per 32 lanes");
-    for (int v = tid; v < BM * (BN / 8); v += NT) {
+    // the da/db stores go out in the loop; the part of each iteration's row
+    // waits in a register and the 32-lane sums of all iterations run together
+    // after it (same order: xor 16, 8, 4, 2, 1)
+    constexpr int kIt = BM * (BN / 8) / NT;
+    constexpr int kGrp = 4;   // iterations whose sums run together
+    static_assert(kIt % kGrp == 0, "whole groups");
+    for (int i0 = 0; i0 < kIt; i0 += kGrp) {
+    float partv[kGrp];
+#pragma unroll
+    for (int ig = 0; ig < kGrp; ++ig) {
+      const int v = tid + NT * (i0 + ig);
       const int rr = v / (BN / 8), c = v % (BN / 8);
       const bool ok = rr < rows && c < nch;
       const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
@@ -1913,17 +1939,24 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
         daw[q] = bf_pack(da2[0], da2[1]);
         dbw[q] = bf_pack(db2[0], db2[1]);
       }
-      part = ok ? part : 0.f;
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 8, 64);
-      part += __shfl_xor(part, 4, 64);
-      part += __shfl_xor(part, 2, 64);
-      part += __shfl_xor(part, 1, 64);
-      if (!ok) continue;
-      if (c == 0) g.dgate_part[static_cast<int64_t>(m0 + rr) * g.n_tiles_n + nt] = part;
-      const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
-      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
-      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+      partv[ig] = ok ? part : 0.f;
+      if (ok) {
+        const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
+        *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+        *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+      }
+    }
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1)
+#pragma unroll
+      for (int ig = 0; ig < kGrp; ++ig) partv[ig] += __shfl_xor(partv[ig], m, 64);
+#pragma unroll
+    for (int ig = 0; ig < kGrp; ++ig) {
+      const int v = tid + NT * (i0 + ig);
+      const int rr = v / (BN / 8), c = v % (BN / 8);
+      if (c == 0 && rr < rows)
+        g.dgate_part[static_cast<int64_t>(m0 + rr) * g.n_tiles_n + nt] = partv[ig];
+    }
     }
     return;
   }
