@@ -594,6 +594,183 @@ def layer_backward(x, wr, w1, w3, w2, fwd, dy, aux_coef=0.0, z_coef=0.0):
 
 
 # ---------------------------------------------------------------------------
+# Forward error bounds of the layer's float outputs
+#
+# A GPU layer stores activations in a short format (bfloat16: 8 significant
+# bits, unit roundoff u = 2**-8) and accumulates in fp32 (unit roundoff
+# 2**-24).  Its outputs then differ from the exact layer above by rounding
+# alone, and that difference has a classical bound (Higham, "Accuracy and
+# Stability of Numerical Algorithms", Sec. 3.1: a computed dot product of n
+# terms is within gamma_n * sum |terms| of the exact one, gamma_n = n u /
+# (1 - n u)).  Carried through the layer to first order, every quantity q that
+# the layer forms gets a bound B(q) from the EXACT operands only:
+#   * a stored result adds u |q| (one rounding, wherever it happens);
+#   * a sum or dot product adds gamma_n(fp32) * sum |terms|, and passes on
+#     the bounds of its operands through |other operand|;
+#   * an elementwise function f(a) passes on |f'(a)| B(a).
+# The bound is written for the plain (unfolded) layer: quantities that a
+# computation may store are the named tensors of layer_forward/backward (a,
+# b, h, y_perm, y, dy_perm, dh, da, db, dx_perm, dx, dW); the router-side
+# quantities (gates, dgate, dlogits, dWr) are fp32.  A computation that
+# stores a rescaled tensor instead (g h in place of h, dY W2 in place of
+# g dY W2) has the same relative rounding, so the same bound covers it.
+# The check |gpu - exact| <= c B(q) is then independent of where a kernel
+# rounds, and a slip such as a dropped term, a wrong index or a wrong sign
+# is far outside it (an error of the size of the terms, not u times them).
+# ---------------------------------------------------------------------------
+
+U_BF16 = 2.0 ** -8
+U_F32 = 2.0 ** -24
+
+
+def gamma(n, u=U_F32):
+    """Higham's gamma_n = n u / (1 - n u)."""
+    return n * u / (1.0 - n * u)
+
+
+def _silu_derivs(a):
+    s = _sigmoid(a)
+    d1 = s * (1.0 + a * (1.0 - s))
+    d2 = s * (1.0 - s) * (2.0 + a * (1.0 - 2.0 * s))
+    return a * s, d1, d2
+
+
+def layer_error_bounds(x, wr, w1, w3, w2, fwd, bwd=None, dy=None, u=U_BF16,
+                       aux_coef=0.0, z_coef=0.0, ufn=8 * U_F32):
+    """First-order componentwise error bounds B(q) around the exact layer.
+
+    fwd, bwd come from layer_forward / layer_backward with act="f64" and no
+    gate folding (capacity and the auxiliary losses are allowed: pass the same
+    aux_coef and z_coef as to layer_backward).  u is the unit roundoff of the
+    stored activations (2**-8 for bfloat16, 2**-24 when they are fp32); ufn is
+    the relative error allowed for one evaluation of an exp-based function
+    (sigmoid, silu) in fp32.  Returns bounds shaped like the outputs: a, b, h,
+    y_perm, y and, with bwd, dy_perm, dgate, dh, da, db, dx_perm, dw1, dw3,
+    dw2, dlogits, dwr, dx.  Bounds are carried in float32: they are
+    magnitudes, and six significant digits are more than a tolerance needs."""
+    if fwd.get("fold_gate") or fwd.get("act", "f64") != "f64":
+        raise ValueError("bounds are taken around the exact, unfolded layer")
+    F = np.float32
+
+    def A(v):
+        return np.abs(np.asarray(v)).astype(F)
+
+    x, wr = _f64(x), _f64(wr)
+    w1, w3, w2 = _f64(w1), _f64(w3), _f64(w2)
+    E, f, d = w1.shape
+    off, pos, gates = fwd["offsets"], fwd["pos"], _f64(fwd["gates"])
+    T, k = pos.shape
+    xp, a, b, h, yp = fwd["x_perm"], fwd["a"], fwd["b"], fwd["h"], fwd["y_perm"]
+    u, uf = F(u), F(ufn)
+    g_d, g_f = F(gamma(d)), F(gamma(f))
+    act_a, d1, d2 = _silu_derivs(a)
+    act_a, d1, d2 = A(act_a), A(d1), A(d2)
+    aW1, aW3, aW2 = A(w1), A(w3), A(w2)
+    Ba = np.zeros(a.shape, F)
+    Bb = np.zeros(b.shape, F)
+    for e in range(E):
+        s = slice(int(off[e]), int(off[e + 1]))
+        ax = A(xp[s])
+        Ba[s] = u * A(a[s]) + g_d * (ax @ aW1[e].T)
+        Bb[s] = u * A(b[s]) + g_d * (ax @ aW3[e].T)
+    ab = A(b)
+    Bh = (u + uf) * A(h) + d1 * ab * Ba + act_a * Bb
+    Byp = np.zeros(yp.shape, F)
+    ah = A(h)
+    for e in range(E):
+        s = slice(int(off[e]), int(off[e + 1]))
+        Byp[s] = u * A(yp[s]) + (Bh[s] + g_f * ah[s]) @ aW2[e].T
+    live = pos >= 0
+    ayp = A(yp)
+    By = u * A(fwd["y"])
+    ay = np.zeros(By.shape, F)
+    for j in range(k):
+        p = np.maximum(pos[:, j], 0)
+        w = np.where(live[:, j], gates[:, j], 0.0).astype(F)[:, None]
+        By += w * Byp[p]
+        ay += w * ayp[p]
+    By += F(gamma(k + 1)) * ay
+    out = {"a": Ba, "b": Bb, "h": Bh, "y_perm": Byp, "y": By}
+    if bwd is None:
+        return out
+
+    ady = A(dy)
+    dyp, dh, da, db = bwd["dy_perm"], bwd["dh"], bwd["da"], bwd["db"]
+    dxp = bwd["dx_perm"]
+    # dy_perm = g dY (one rounding; g itself is an fp32 value)
+    adyp = A(dyp)
+    Bdyp = (u + F(U_F32)) * adyp
+    # dgate = <dY, y_perm> over d, in fp32
+    Bdg = np.zeros((T, k), F)
+    for j in range(k):
+        p = np.maximum(pos[:, j], 0)
+        v = (ady * (Byp[p] + g_d * ayp[p])).sum(axis=1)
+        Bdg[:, j] = np.where(live[:, j], v, 0.0)
+    adh = A(dh)
+    Bdh = np.zeros(dh.shape, F)
+    for e in range(E):
+        s = slice(int(off[e]), int(off[e + 1]))
+        Bdh[s] = u * adh[s] + (Bdyp[s] + g_d * adyp[s]) @ aW2[e]
+    ada, adb = A(da), A(db)
+    Bda = (u + uf) * ada + Bdh * ab * d1 + adh * Bb * d1 + adh * ab * d2 * Ba
+    Bdb = (u + uf) * adb + Bdh * act_a + adh * d1 * Ba
+    g2f = F(gamma(2 * f))
+    Bdxp = np.zeros(dxp.shape, F)
+    Bdw1 = np.zeros(w1.shape, F)
+    Bdw3 = np.zeros(w3.shape, F)
+    Bdw2 = np.zeros(w2.shape, F)
+    for e in range(E):
+        s = slice(int(off[e]), int(off[e + 1]))
+        n = int(off[e + 1] - off[e])
+        Bdxp[s] = (u * A(dxp[s]) + (Bda[s] + g2f * ada[s]) @ aW1[e]
+                   + (Bdb[s] + g2f * adb[s]) @ aW3[e])
+        gn = F(gamma(max(n, 1)))
+        ax = A(xp[s])
+        Bdw1[e] = u * A(bwd["dw1"][e]) + (Bda[s] + gn * ada[s]).T @ ax
+        Bdw3[e] = u * A(bwd["dw3"][e]) + (Bdb[s] + gn * adb[s]).T @ ax
+        Bdw2[e] = (u * A(bwd["dw2"][e]) + (Bdyp[s] + gn * adyp[s]).T @ ah[s]
+                   + adyp[s].T @ Bh[s])
+    # dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i) in fp32, plus the fp32 loss terms
+    adg = np.abs(_f64(bwd["dgate"]))
+    inner_b = (gates * Bdg).sum(axis=1, keepdims=True)
+    inner_a = (gates * adg).sum(axis=1, keepdims=True)
+    Bsel = gates * (Bdg + inner_b) + 8 * U_F32 * gates * (adg + inner_a)
+    Bdl = np.zeros((T, E))
+    for j in range(k):
+        Bdl[np.arange(T), fwd["topk_idx"][:, j]] += Bsel[:, j]
+    if aux_coef != 0.0 or z_coef != 0.0:
+        p = full_softmax(fwd["logits"])
+        if aux_coef != 0.0:
+            G = fwd.get("lb_groups", 1)
+            count = lb_stats(fwd["logits"], fwd["topk_idx"], E, G)["count"]
+            n = T // G
+            fr = np.repeat(count / float(n * fwd["topk_idx"].shape[1]), n, axis=0)
+            mag = (E / float(G * n)) * p * (fr + (fr * p).sum(axis=1, keepdims=True))
+            Bdl += 16 * U_F32 * abs(aux_coef) * mag
+        if z_coef != 0.0:
+            Bdl += 16 * U_F32 * abs(z_coef) * (2.0 / T) * np.abs(_logsumexp(fwd["logits"]))[:, None] * p
+    Bdl = Bdl.astype(F)
+    adl = A(bwd["dlogits"])
+    Bdwr = F(U_F32) * A(bwd["dwr"]) + (Bdl + F(gamma(T)) * adl).T @ A(x)
+    # dx = sum_j dx_perm[pos_j] + dl Wr, summed in fp32 and rounded once
+    adxp = A(dxp)
+    Bdx = u * A(bwd["dx"])
+    adx = np.zeros(Bdx.shape, F)
+    for j in range(k):
+        p = np.maximum(pos[:, j], 0)
+        m = live[:, j][:, None]
+        Bdx += np.where(m, Bdxp[p], F(0))
+        adx += np.where(m, adxp[p], F(0))
+    awr = A(wr)
+    adx += adl @ awr
+    Bdx += Bdl @ awr + F(gamma(k + E + 1)) * adx
+    out.update({"dy_perm": Bdyp, "dgate": Bdg, "dh": Bdh, "da": Bda, "db": Bdb,
+                "dx_perm": Bdxp, "dw1": Bdw1, "dw3": Bdw3, "dw2": Bdw2, "dlogits": Bdl,
+                "dwr": Bdwr, "dx": Bdx})
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Index products for expert-parallel layouts ([COUPLING] Table III notation,
 # Fig. 2 co-selection, Fig. 3 correlated placement, Abstract: a dispatcher that
 # sends each token to each GPU once, Table I statistics)

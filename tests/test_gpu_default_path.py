@@ -1,0 +1,71 @@
+"""GPU parity of the path bench.py times, on every workload at full size.
+
+The layer runs exactly as the benchmark launches it: the permutation as a
+plan only, expert input rows gathered from X through src_token, and (bf16
+workloads) the gate folded onto the expert rows with dY read through
+src_token.  The router is checked first (check_route); then the oracle's
+routing is uploaded (teacher forcing: near-tie tokens may legitimately pick
+another set) and every output is compared:
+  * counts, offsets, positions, source tokens and row gates: bit-exact;
+  * every element of every float output (a, b, g h, g y_perm, y, da, db,
+    dx_perm, dgate, dx, and all experts' dW1, dW3, dW2, and dWr): within
+    C_BOUND times its first-order error bound around the EXACT fp64 layer
+    (oracle.layer_error_bounds), and within the workload tolerance (1e-4
+    fp32, 2e-2 bf16, row-normwise) outside the weight gradients of the
+    clustered-input workloads.
+The reference is the plain fp64 oracle on identically rounded inputs: it
+rounds nothing where the kernels round.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import get_config, make_layer_inputs
+from top_routing_grouped_router_amd import MoELayer
+import top_routing_grouped_router_amd._lib as L
+
+from _parity import (bound_only_keys, check_plan, check_route, exact_reference, layer_floats,
+                     oracle_routing)
+from _util import TOL, act_torch, check_floats, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bench_layer(cfg, G):
+    """The layer in the benchmark's launch configuration."""
+    act = act_torch(cfg.act)
+    dims = L.make_dims(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act)
+    fold = bool(L.moe_gate_folded_supported(dims))
+    return MoELayer(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act, n_groups=G, gather=True,
+                    fold_gate=fold)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_default_path_full_size(name):
+    print(f"\n[case] default path {name}", flush=True)
+    cfg = get_config(name)
+    inp = make_layer_inputs(cfg, with_dy=cfg.backward)
+    G = max(cfg.lb_groups)
+    layer = bench_layer(cfg, G)
+    act = layer.act
+    print(f"[{name}] gate {'folded' if layer.fold_gate else 'in the combine'}", flush=True)
+    o_r, same = check_route(layer, inp["x"], inp["wr"], cfg.k, G=G)
+    print(f"[{name}] router ok: near-ties {o_r['near_tie_count']} / {cfg.T}, "
+          f"routing mismatches {int((~same).sum())}", flush=True)
+
+    routing = (o_r["topk_idx"], o_r["gates"].astype(np.float32))
+    t = {key: dev(v, act) for key, v in inp.items() if key != "wr"}
+    t["wr"] = dev(inp["wr"], torch.float32)
+    layer.forward(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], routing=oracle_routing(o_r))
+    if cfg.backward:
+        layer.backward(t["dy"], t["x"], t["wr"], t["w1"], t["w3"], t["w2"])
+    torch.cuda.synchronize()
+    del t
+
+    o_f, o_b, B = exact_reference(inp, cfg.k, routing, backward=cfg.backward, act=cfg.act)
+    print(f"[{name}] oracle done", flush=True)
+    check_plan(layer, o_f)
+    got, ex, bd = layer_floats(layer, o_f, o_b, B)
+    del o_f, o_b, B
+    check_floats(name, got, ex, bd, TOL[cfg.act], bound_only_keys(cfg))

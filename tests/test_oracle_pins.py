@@ -895,3 +895,141 @@ def test_folded_gate_layer_is_the_same_layer_in_exact_arithmetic(cap):
     for key in ("dgate", "dx_perm", "dh", "da", "db", "dw1", "dw3", "dw2", "dx", "dwr",
                 "dlogits"):
         np.testing.assert_allclose(fol_b[key], ref_b[key], rtol=1e-9, atol=1e-11, err_msg=key)
+
+
+# ---------------------------------------------------------------------------
+# Error bounds (oracle.layer_error_bounds).  Pinned by what they claim: any
+# computation that rounds the stored tensors with unit roundoff u stays inside
+# them, wherever it rounds (the unfolded and the gate-folded placements, round
+# to nearest and truncation, which doubles the rounding error), and a slip of
+# the kinds a kernel can make (a dropped term, a sign, a row index, a gate
+# applied twice) falls outside twice the bound.
+# ---------------------------------------------------------------------------
+
+BOUND_OUTPUTS = ("y", "dgate", "dx_perm", "dx", "dw1", "dw3", "dw2", "dwr")
+
+
+def _bound_case(seed, T=96, d=64, E=4, f=64, k=2, x_kind="normal"):
+    from synth import get_config, make_layer_inputs
+    over = dict(T=T, d=d, E=E, f=f, k=k, x_kind=x_kind)
+    if x_kind == "mixture":
+        over.update(n_centroids=4, noise_norm=0.3)
+    cfg = get_config("c2", **over)
+    inp = make_layer_inputs(cfg, seed=seed, with_dy=True)
+    r = O.route(inp["x"], inp["wr"], k)
+    routing = (r["topk_idx"], r["gates"].astype(np.float32))
+    w = (inp["x"], inp["wr"], inp["w1"], inp["w3"], inp["w2"])
+    ex_f = O.layer_forward(*w, k, routing=routing)
+    ex_b = O.layer_backward(*w, ex_f, inp["dy"])
+    B = O.layer_error_bounds(*w, ex_f, ex_b, inp["dy"])
+    return inp, w, routing, ex_f, ex_b, B
+
+
+def _rounded_layer(w, dy, k, routing, fold):
+    f = O.layer_forward(*w, k, routing=routing, act="bf16", fold_gate=fold)
+    b = O.layer_backward(*w, f, dy)
+    return f, b
+
+
+def _ratios(f, b, ex_f, ex_b, B):
+    out = {}
+    for key in BOUND_OUTPUTS:
+        got = f[key] if key == "y" else b[key]
+        ref = ex_f[key] if key == "y" else ex_b[key]
+        diff = np.abs(got - ref)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = np.where(diff == 0.0, 0.0, diff / B[key])
+        out[key] = float(np.nan_to_num(r, nan=np.inf, posinf=np.inf).max())
+    return out
+
+
+CASES_BOUND = [(0, dict()), (1, dict(T=200, E=8, k=3, f=96)),
+               (2, dict(x_kind="mixture", T=160, k=2)), (3, dict(E=1, k=1))]
+
+
+@pytest.mark.parametrize("seed,over", CASES_BOUND)
+def test_error_bounds_hold_for_rounded_layers(seed, over):
+    inp, w, routing, ex_f, ex_b, B = _bound_case(seed, **over)
+    k = routing[0].shape[1]
+    for fold in (False, True):
+        f, b = _rounded_layer(w, inp["dy"], k, routing, fold)
+        ratios = _ratios(f, b, ex_f, ex_b, B)
+        assert max(ratios.values()) <= 1.0, (fold, ratios)
+        # and the rounding is visible: the bound is not vacuous
+        assert max(ratios[k2] for k2 in ("y", "dx", "dw1")) > 1e-3, ratios
+
+
+def test_error_bounds_hold_for_truncation(monkeypatch):
+    """Rounding toward zero errs by up to 2u: inside twice the bound."""
+    def chop(v):
+        v = np.asarray(v, dtype=np.float64)
+        m, e = np.frexp(v)
+        return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+    inp, w, routing, ex_f, ex_b, B = _bound_case(5, T=128, E=4, k=2)
+    monkeypatch.setattr(O, "to_bf16", chop)
+    f, b = _rounded_layer(w, inp["dy"], 2, routing, False)
+    ratios = _ratios(f, b, ex_f, ex_b, B)
+    assert max(ratios.values()) <= 2.0, ratios
+    assert max(ratios.values()) > 0.3, ratios     # truncation errs one way: near the bound
+
+
+@pytest.mark.parametrize("x_kind", ["normal", "mixture"])
+def test_error_bounds_catch_planted_mistakes(x_kind):
+    """Each slip fails the GPU tests' float check: some element outside twice
+    its bound, or (outputs other than the expert weight gradients) a
+    row-normwise error over 2e-2.  The expert weight gradients, which
+    clustered workloads hold to the bound alone, must be caught by the bound
+    alone."""
+    inp, w, routing, ex_f, ex_b, B = _bound_case(7, T=256, E=4, k=2, x_kind=x_kind)
+    f, b = _rounded_layer(w, inp["dy"], 2, routing, False)
+    off, src, pos = ex_f["offsets"], ex_f["src"], ex_f["pos"]
+    x, dy = np.asarray(inp["x"], np.float64), np.asarray(inp["dy"], np.float64)
+
+    def rn(g, o):
+        g2, o2 = g.reshape(-1, o.shape[-1]), o.reshape(-1, o.shape[-1])
+        rms = np.sqrt(np.mean(o * o))
+        return float((np.abs(g2 - o2).max(1) / np.maximum(np.abs(o2).max(1), rms)).max())
+
+    def caught(key, got):
+        ref = ex_f[key] if key == "y" else ex_b[key]
+        out_of_bound = bool((np.abs(got - ref) > 2.0 * B[key]).any())
+        if key in ("dw1", "dw3", "dw2"):
+            return out_of_bound
+        return out_of_bound or rn(got, ref) > 2e-2
+
+    # unplanted: passes
+    for key in BOUND_OUTPUTS:
+        assert not caught(key, f[key] if key == "y" else b[key]), key
+    # a dropped term: expert 0's dW1 without its first row
+    r0 = int(off[0])
+    dw1 = b["dw1"].copy()
+    dw1[0] -= np.outer(b["da"][r0], x[src[r0]])
+    assert caught("dw1", dw1)
+    # a row index: dW2 of expert 1 pairing dy_perm rows with the next row's h
+    s = slice(int(off[1]), int(off[2]))
+    dw2 = b["dw2"].copy()
+    dw2[1] = b["dy_perm"][s].T @ np.roll(f["h"][s], 1, axis=0)
+    assert caught("dw2", dw2)
+    # a transposed operand: dW3 of expert 2 from db against dy_perm's columns
+    s = slice(int(off[2]), int(off[3]))
+    dw3 = b["dw3"].copy()
+    dw3[2] = b["db"][s].T @ x[src[s]][:, ::-1]
+    assert caught("dw3", dw3)
+    # dWr with one token's logit gradient sign flipped
+    dl = np.array(ex_b["dlogits"])
+    dl[11] = -dl[11]
+    assert caught("dwr", dl.T @ x)
+    # a sign: one token's dgate
+    dg = b["dgate"].copy()
+    dg[3, 1] = -dg[3, 1]
+    assert caught("dgate", dg)
+    # a gate applied twice in the combine
+    y2 = O.combine(f["y_perm"], pos, np.asarray(routing[1], np.float64) ** 2)
+    assert caught("y", y2)
+    # a slot left out of the unpermute-sum of dX
+    assert caught("dx", b["dx"] - b["dx_perm"][pos[:, 1]])
+    # one token's dY row taken from its neighbour in dgate
+    dg2 = b["dgate"].copy()
+    dg2[5, 0] = (dy[6] * f["y_perm"][pos[5, 0]]).sum()
+    assert caught("dgate", dg2)
