@@ -166,8 +166,19 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
     from a short probe.  Repeats until budget_s is spent (at least once)."""
     import threadpoolctl
     from oracle import moe_oracle as O
+    cores = len(os.sched_getaffinity(0))
+    threadpoolctl.threadpool_limits(cores)
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
 
     def step(n):
         sl = slice(0, n)
@@ -194,9 +205,111 @@ def cpu_baseline(cfg, inp, budget_s=20.0):
             break
     what = "full batch" if n == cfg.T else f"first {n} of {cfg.T} tokens"
     return {"value": round(n * steps / el, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "affinity_cores": cores,
             "sample": f"{steps} step(s) of {cfg.name} over the {what} (fwd"
                       f"{'+bwd' if cfg.backward else ''}), fp64 numpy, {el:.1f} s"}
+
+
+def workload_reports(steps):
+    """The index products the workloads are defined by, computed by the
+    library on each workload's own seeded inputs (the router's routing, not
+    the oracle's):
+      * C3: the near-tie share at margin 1e-3 ([LAYOUT] Finding 3) and the
+        share of normalised margins (gap / spread of the token's logits) under
+        0.01 (Finding 4's measure);
+      * C2: per-block balancing statistics for G = 1, 2, 4, 8 blocks
+        ([LAYOUT] Two Kinds of Layout Effects; [REVISIT] Sec. 2.2 outer
+        batches): aux per block and the largest and smallest E f and E P;
+      * C4 and C5: the deduplicated dispatch plan for each of the workload's
+        group counts under contiguous and correlated (greedy co-selection,
+        fit on another batch) placement ([COUPLING] Table I): share of tokens
+        whose experts sit in one group, distinct destinations per token, and
+        rows removed; plus C4's share of tokens whose top-2 pair is among the
+        20 most frequent pairs (about 1% of the pairs)."""
+    import torch
+    from synth import get_config, make_layer_inputs
+    import top_routing_grouped_router_amd._lib as L
+    i32 = dict(dtype=torch.int32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    rep = {}
+
+    def route(cfg, x_np, wr_np, G):
+        act = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+        dm = L.make_dims(cfg.T, cfg.d, cfg.E, cfg.f, cfg.k, act)
+        ws = L.alloc_workspace(dm, G)
+        x = torch.from_numpy(x_np).to("cuda", act)
+        wr = torch.from_numpy(wr_np).cuda()
+        T, E, k = cfg.T, cfg.E, cfg.k
+        o = {"logits": torch.empty(T, E, **f32), "idx": torch.empty(T, k, **i32),
+             "gate": torch.empty(T, k, **f32), "margin": torch.empty(T, **f32),
+             "ntc": torch.empty(1, **i32), "count": torch.empty(G, E, **i32),
+             "P": torch.empty(G, E, **f32), "aux": torch.empty(G, **f32)}
+        L.moe_route(dm, x, wr, o["logits"], o["idx"], o["gate"], o["margin"], 1e-3, o["ntc"], G,
+                    o["count"], o["P"], o["aux"], ws)
+        torch.cuda.synchronize()
+        return o
+
+    c3 = get_config("c3")
+    inp = make_layer_inputs(c3, parts=("x", "wr"))
+    r = route(c3, inp["x"], inp["wr"], 1)
+    lg = r["logits"].cpu().numpy().astype(np.float64)
+    mg = r["margin"].cpu().numpy().astype(np.float64)
+    spread = lg.max(1) - lg.min(1)
+    norm = mg / np.where(spread > 0, spread, 1.0)
+    rep["c3_near_ties"] = {"eps": 1e-3, "tokens": int(r["ntc"].item()), "of": c3.T,
+                           "fraction": round(int(r["ntc"].item()) / c3.T, 4),
+                           "normalised_margin_below_0.01": round(float((norm < 0.01).mean()), 4)}
+
+    c2 = get_config("c2")
+    inp = make_layer_inputs(c2, parts=("x", "wr"))
+    lb = {}
+    for G in c2.lb_groups:
+        r = route(c2, inp["x"], inp["wr"], G)
+        cnt = r["count"].cpu().numpy().astype(np.float64)
+        fE = cnt / (c2.T // G * c2.k) * c2.E
+        PE = r["P"].cpu().numpy().astype(np.float64) * c2.E
+        lb[f"G{G}"] = {"aux": [round(float(v), 5) for v in r["aux"].cpu().numpy()],
+                       "E_f_max": round(float(fE.max()), 4), "E_f_min": round(float(fE.min()), 4),
+                       "E_P_max": round(float(PE.max()), 4), "E_P_min": round(float(PE.min()), 4)}
+    rep["c2_lb_stats"] = lb
+
+    dd = {}
+    for name in ("c4", "c5"):
+        cfg = get_config(name)
+        inp = make_layer_inputs(cfg, parts=("x", "wr"))
+        fit = make_layer_inputs(cfg, batch_seed=1, parts=("x",))
+        idx = route(cfg, inp["x"], inp["wr"], 1)["idx"]
+        idx_fit = route(cfg, fit["x"], inp["wr"], 1)["idx"]
+        T, k, E = cfg.T, cfg.k, cfg.E
+        W = torch.empty(E, E, **i32)
+        L.moe_coselect(T, k, E, idx_fit, W)
+        torch.cuda.synchronize()
+        W_fit = W.cpu().numpy().astype(np.int64)
+        if k == 2:
+            pairs = np.sort(idx.cpu().numpy(), axis=1)
+            _, cnts = np.unique(pairs[:, 0] * E + pairs[:, 1], return_counts=True)
+            dd[f"{name}_top20_pair_token_share"] = round(float(np.sort(cnts)[::-1][:20].sum() / T),
+                                                         4)
+        for G in cfg.plan_groups:
+            dm = L.make_dims(T, 64, E, 64, k, torch.bfloat16)
+            ws = L.alloc_workspace(dm, G)
+            for kind, pl in (("contiguous", [e * G // E for e in range(E)]),
+                             ("correlated", L.moe_placement_greedy(E, G, W_fit))):
+                out = {"n_dest": torch.empty(T, **i32), "group_rows": torch.empty(G, **i32),
+                       "group_offsets": torch.empty(G + 1, **i32),
+                       "row_token": torch.empty(T * k, **i32),
+                       "assign_row": torch.empty(T, k, **i32), "stats": torch.empty(4, **i32)}
+                L.moe_dispatch_plan(T, k, E, G, idx, pl, out["n_dest"], out["group_rows"],
+                                    out["group_offsets"], out["row_token"], out["assign_row"],
+                                    out["stats"], ws)
+                torch.cuda.synchronize()
+                rows, removed, single, _ = (int(v) for v in out["stats"].cpu().tolist())
+                dd[f"{name}_G{G}_{kind}"] = {
+                    "same_group_share": round(single / T, 4),
+                    "destinations_per_token": round(rows / T, 4),
+                    "rows_removed_share": round(removed / (T * k), 4)}
+    rep["dedup_plans"] = dd
+    return rep
 
 
 def ep_dispatch(cfg, layer, x, steps):
@@ -399,7 +512,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"],
+                    help="c5 (the largest single-GPU workload) by default; the others are "
+                         "parity cases that can be timed too")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="bytes written before every timed step to evict L2 and MALL "
+                         "(outside the step's events); 0 disables the flushed headline")
+    ap.add_argument("--no-reports", action="store_true",
+                    help="skip the per-workload reports (C3 near-ties, C2 balancing "
+                         "statistics per group count, C4/C5 dedup plans)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-gather", action="store_true",
@@ -596,33 +717,48 @@ def main():
         torch.cuda.synchronize()
         step = graph.replay
 
-    # Timed region: K whole steps back to back, bracketed by events on the
-    # stream the library launches on (torch's current stream).
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Timed region (bracketed by synchronisations): K steps, each timed by its
+    # own pair of events on the stream the library launches on (torch's
+    # current stream).  Before each step a write of --flush-mb MiB evicts L2
+    # and the MALL, outside the step's events: the headline is the median of
+    # these cold-cache steps.  A second pass times K steps back to back with
+    # warm caches (the median again).
+    flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev)
+             if args.flush_mb > 0 else None)
+
+    def timed_steps(cold):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            if cold:
+                flush.fill_(1.0)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
+    cold_ms = timed_steps(True) if flush is not None else None
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    warm_ms = timed_steps(False)
+    ms_per_step = float(np.median(cold_ms if cold_ms is not None else warm_ms))
 
-    # Per-call durations (same stream, events around each call) in a second
-    # pass of the same K steps; they carry the roofline and the breakdown.
+    # Per-call durations (same stream, events around each call) in a third
+    # pass of K warm steps; they carry the roofline and the breakdown.
     n = len(calls)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in range(n)] for _ in range(args.steps)]
-    for s in range(args.steps):
+    for s_ in range(args.steps):
         for i, (_, fn) in enumerate(calls):
-            evs[s][i][0].record()
+            evs[s_][i][0].record()
             fn()
-            evs[s][i][1].record()
+            evs[s_][i][1].record()
     torch.cuda.synchronize()
-    per_call = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1])
-                                     for s in range(args.steps)]))
+    per_call = {name: float(np.mean([evs[s_][i][0].elapsed_time(evs[s_][i][1])
+                                     for s_ in range(args.steps)]))
                 for i, (name, _) in enumerate(calls)}
 
     rows = int(layer.expert_offsets[cfg.E].item())   # expert rows (fewer when dropping)
@@ -646,6 +782,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "timing": {"statistic": "median over the timed steps",
+                   "cold_cache": (f"{args.flush_mb} MiB written before every step, outside its "
+                                  "events" if cold_ms is not None else None),
+                   "ms_per_step_cold": (round(float(np.median(cold_ms)), 4)
+                                        if cold_ms is not None else None),
+                   "ms_per_step_warm": round(float(np.median(warm_ms)), 4),
+                   "tokens_per_s_warm": round(cfg.T / (float(np.median(warm_ms)) * 1e-3), 1)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -681,6 +824,8 @@ def main():
         out["fragility"] = fragility(cfg, layer, x, wr, args.steps)
     if args.shuffle and cfg.plan_groups:
         out["token_shuffle"] = token_shuffle(cfg, layer, x, wr, args.steps)
+    if not args.no_reports:
+        out["reports"] = workload_reports(args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -146,8 +146,12 @@ def layer_floats(layer, o_f, o_b, B):
 
 
 def bound_only_keys(cfg):
-    """Outputs held to the bound alone: the expert weight gradients of the
-    workloads with clustered hidden states, whose sums over many nearly
-    parallel rows cancel (a bf16-storage computation of them misses 2e-2 there
-    by rounding alone)."""
-    return ("dw1", "dw3", "dw2") if cfg.x_kind == "mixture" else ()
+    """Outputs held to the bound alone:
+      * the logit gradient dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i), whose
+        difference cancels wherever a token's dgate values are close, so that
+        the bf16 rounding of the expert path upstream of dgate reaches 3-5e-2
+        of it (row-normwise) in any bf16-storage computation;
+      * the expert weight gradients of the workloads with clustered hidden
+        states, whose sums over many nearly parallel rows cancel (2-4e-2 by
+        rounding alone there)."""
+    return ("dlogits",) + (("dw1", "dw3", "dw2") if cfg.x_kind == "mixture" else ())

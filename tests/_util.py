@@ -69,15 +69,16 @@ def per_slice_err(gpu, ref) -> float:
 # Sec. 3.1).  C_BOUND = 2 leaves room for the second-order terms that the
 # first-order bound drops.  Beside it, the workload tolerance (1e-4 fp32,
 # 2e-2 bf16) holds for the row-normwise error of every output outside
-# `bound_only`: the expert weight gradients of the clustered-input workloads,
-# whose sums over hundreds to thousands of nearly parallel rows cancel so much
-# that a bf16-storage computation misses 2e-2 there by rounding alone.
+# `bound_only` (outputs that cancel so much that a bf16-storage computation
+# misses 2e-2 there by rounding alone: the logit gradient, and the expert
+# weight gradients of the clustered-input workloads).  Rows are the last axis;
+# the expert weight gradients are taken per expert slice.
 # Both the elementwise error (|g-o| / max(|o|, rms)) and the row-normwise one
 # are printed.
 # ---------------------------------------------------------------------------
 
 C_BOUND = 2.0
-SLICED = ("dw1", "dw3", "dw2", "dwr")
+SLICED = ("dw1", "dw3", "dw2")   # per expert: [E, out, in] -> one [out, in] slice each
 
 
 def a13_err(gpu, ref) -> float:

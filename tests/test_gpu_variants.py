@@ -22,7 +22,7 @@ from top_routing_grouped_router_amd import MoELayer
 import top_routing_grouped_router_amd as M
 
 from _parity import bound_only_keys, exact_reference, layer_floats
-from _util import TOL, TOL_ROUTER, act_torch, check_floats, dev, host, rel_err
+from _util import TOL, TOL_ROUTER, act_torch, check_floats, dev, host, per_slice_err, rel_err
 
 pytestmark = pytest.mark.gpu
 
