@@ -46,7 +46,8 @@
  *    E <= 256, d % 64 == 0, f % 64 == 0, T * k < 2^31, act in {F32, BF16}.
  *  - topk_idx inputs must hold expert ids in [0, E) with no repeats within a
  *    token (moe_route produces such tables).  Out-of-range ids are ignored by
- *    the index kernels rather than written out of bounds.
+ *    the index kernels rather than written out of bounds; moe_permute sorts a
+ *    repeated id by the definition (each slot its own row, in slot order).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -133,7 +134,9 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
  *   is the running count of earlier tokens that chose that expert).
  *
  * topk_idx [T,k] int32 in.  An id of -1 marks a dropped assignment (see
- *   moe_capacity): it gets pos -1 and no row.
+ *   moe_capacity): it gets pos -1 and no row.  A token whose row repeats an
+ *   expert (outside the routing contract) gets one row per slot, the slots
+ *   in order, exactly as for distinct ids.
  * expert_counts [E], expert_offsets [E+1] (exclusive scan; offsets[E] = the
  *   number of kept assignments, T*k when nothing is dropped).
  * pos [T,k]: row of assignment (t, j) in the permuted order; rows of one

@@ -190,3 +190,4 @@ def test_gate_folded_support_query():
     split = dims(T=1000, d=256, E=8, f=192, k=3)   # split-K weight gradients
     st = lib.moe_expert_up_folded(ctypes.byref(split), *([FAKE] * 9), None)
     assert st == UNSUP and "moe_gate_folded_supported" in L.last_error()
+

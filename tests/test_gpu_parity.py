@@ -229,3 +229,38 @@ def test_dispatch_plan_and_coselect(name):
             print(f"[{name} G={G} {kind}] same-group {o['same_group_share']:.3f} "
                   f"destinations {o['mean_destinations']:.3f} dedup {o['dedup_fraction']:.3f}",
                   flush=True)
+
+
+# ---------------------------------------------------------------- permutation edge cases
+
+@pytest.mark.parametrize("T,E,k", [(1000, 8, 3), (40000, 16, 4)])
+def test_permute_follows_the_definition_with_repeated_ids(T, E, k):
+    """A token that lists an expert twice is outside the routing contract, but
+    the sort is still the definition's: every slot gets its own row, in slot
+    order, with x_perm[pos] = x bit for bit.  T = 1000 takes the fused
+    scan/scatter/gather kernel, T = 40000 (157 blocks) the separate kernels;
+    a clean table of the larger size is checked too."""
+    _announce(f"permute repeated ids T={T} E={E} k={k}")
+    from synth import make_routing
+    d = 64
+    idx = make_routing(T, E, k, seed=T).astype(np.int32)
+    clean = idx.copy()
+    g = stream(77, T)
+    rows = g.choice(T, size=max(3, T // 50), replace=False)
+    idx[rows, 1] = idx[rows, 0]                 # slot 1 repeats slot 0
+    x = g.standard_normal((T, d)).astype(np.float32)
+    for table in (idx, clean):
+        plan = O.permute_plan(table, E)
+        dims = M.make_dims(T, d, E, 64, k, torch.float32)
+        ws = M.alloc_workspace(dims, 1)
+        out = {n: torch.full(s, -7, dtype=torch.int32, device="cuda") for n, s in
+               (("counts", (E,)), ("offsets", (E + 1,)), ("pos", (T, k)), ("src", (T * k,)))}
+        xp = torch.zeros(T * k, d, device="cuda")
+        M.moe_permute(dims, dev(table, torch.int32), out["counts"], out["offsets"], out["pos"],
+                      out["src"], dev(x, torch.float32), xp, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out["counts"]), plan["counts"])
+        assert np.array_equal(host(out["offsets"]), plan["offsets"])
+        assert np.array_equal(host(out["pos"]), plan["pos"])
+        assert np.array_equal(host(out["src"]), plan["src"])
+        assert np.array_equal(host(xp), x[plan["src"]])

@@ -18,7 +18,7 @@
 // being written to LDS), so one compute core serves all modes:
 //   bf16: 16x16x32 bf16 MFMA, fp32 accumulators, 4 waves x (64x64) per
 //         128x128 tile;
-//   fp32: FMA on the vector ALUs, 8x8 outputs per thread.
+//   fp32: 16x16x4 fp32 MFMA on the same tiling.
 // A workgroup's (expert, row tile) comes from the expert offsets on the device,
 // so the host never reads the routing.  Each output element is produced by
 // exactly one workgroup with a fixed k order: results are reproducible.
@@ -116,53 +116,76 @@ template <> struct Core<bf16_t> {
   }
 };
 
-// ------------------------------------------------------------------ fp32 VALU core
+// ------------------------------------------------------------------ fp32 MFMA core
+// v_mfma_f32_16x16x4_f32 on the same 4-wave x (64x64) tiling as the bf16
+// core.  Within a BK = 32 tile, lane (g, r) of a 16-row block takes k = 8 g
+// ... 8 g + 7 of its row (two 16-byte LDS reads) and feeds k = 8 g + s at
+// step s; A and B use the same assignment, so each of the 8 steps sums k
+// = s, 8 + s, 16 + s, 24 + s and the 8 steps cover the tile.
 template <> struct Core<float> {
   static constexpr int BK = 32;
-  static constexpr int LD = BK + 4;     // 16-byte aligned rows for the staging stores
+  static constexpr int LD = BK + 4;     // 144-byte rows: 16-byte aligned staging and reads
   typedef float T;
-  float acc[8][8];
+  f32x4 acc[4][4];
 
   __device__ void zero() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __device__ void compute(const T* As, const T* Bs) {
-    const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
-#pragma unroll 4
-    for (int k = 0; k < BK; ++k) {
-      float a[8], b[8];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r = lane & 15, k0 = (lane >> 4) * 8;
+    float a[4][8], b[4][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = As[(tm + 16 * i) * LD + k];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) b[j] = Bs[(tn + 16 * j) * LD + k];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      const float4 lo = *reinterpret_cast<const float4*>(As + (wm * 64 + i * 16 + r) * LD + k0);
+      const float4 hi = *reinterpret_cast<const float4*>(As + (wm * 64 + i * 16 + r) * LD + k0 + 4);
+      a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
+      a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 lo = *reinterpret_cast<const float4*>(Bs + (wn * 64 + j * 16 + r) * LD + k0);
+      const float4 hi = *reinterpret_cast<const float4*>(Bs + (wn * 64 + j * 16 + r) * LD + k0 + 4);
+      b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
+      b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
+    }
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][st], b[j][st], acc[i][j], 0, 0, 0);
   }
   template <typename F>
   __device__ void for_each(F&& fn) const {
-    const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) fn(tm + 16 * i, tn + 16 * j, acc[i][j]);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          fn(wm * 64 + i * 16 + (lane >> 4) * 4 + q, wn * 64 + j * 16 + (lane & 15), acc[i][j][q]);
   }
-  // columns tn + 16 j: block of 32 = j / 2; pairs (j, j + 2) for j % 4 in {0, 1}
+  // pairs (a, b) whose B-tile rows are r and r + 32 inside one 64-row block
   template <typename F>
   __device__ void for_each_pair(F&& fn) const {
-    const int tm = threadIdx.x >> 4, tn = threadIdx.x & 15;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j = (jj & 1) + 4 * (jj >> 1);
-        fn(tm + 16 * i, tn + 16 * j, acc[i][j], acc[i][j + 2]);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          fn(wm * 64 + i * 16 + (lane >> 4) * 4 + q, wn * 64 + j * 16 + (lane & 15),
+             acc[i][j][q], acc[i][j + 2][q]);
   }
 };
 
@@ -451,8 +474,8 @@ unsigned row_tiles(const moe_dims& dm) {
 
 }  // namespace
 
-// Each phase dispatches on the activation type: bf16 runs on the matrix cores
-// (gemm_bf16.hip), fp32 on the vector ALUs (the kernel above).
+// Each phase dispatches on the activation type: bf16 runs on gemm_bf16.hip's
+// kernels, fp32 on the kernel above (fp32 matrix cores).
 
 hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
                             const int32_t* offsets, const void* w1, const void* w3, void* a,

@@ -45,6 +45,20 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
       return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is not 16-byte aligned", __func__, #p); \
   } while (0)
 
+#define MOE_REQUIRE_PTR_FN(p, n, fn)                                                         \
+  do {                                                                                       \
+    if (!(p) && (n) > 0)                                                                     \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is NULL", fn, #p);                     \
+    if (!aligned16(p))                                                                       \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is not 16-byte aligned", fn, #p);      \
+  } while (0)
+
+#define MOE_OPTIONAL_PTR_FN(p, fn)                                                           \
+  do {                                                                                       \
+    if ((p) && !aligned16(p))                                                                \
+      return fail(MOE_ERR_INVALID_ARGUMENT, "%s: '%s' is not 16-byte aligned", fn, #p);      \
+  } while (0)
+
 #define MOE_OPTIONAL_PTR(p)                                                                  \
   do {                                                                                       \
     if ((p) && !aligned16(p))                                                                \
@@ -96,6 +110,7 @@ int route_tile(int64_t T, int32_t G, int32_t act) {
 }
 
 struct RouteWs {
+  uint32_t* arrivals;
   float* psum;
   int32_t* pcnt;
   int32_t* ptie;
@@ -105,8 +120,10 @@ RouteWs route_ws(const moe_dims& dm, int tile, void* ws) {
   const int64_t n_tiles = (dm.T + tile - 1) / tile;
   Carver c;
   RouteWs r;
-  r.psum = c.take<float>(ws, n_tiles * dm.E);
-  r.pcnt = c.take<int32_t>(ws, n_tiles * dm.E);
+  r.arrivals = c.take<uint32_t>(ws, 1);
+  const int64_t ep4 = (dm.E + 3) & ~3;   // partial rows padded to 16 bytes
+  r.psum = c.take<float>(ws, n_tiles * ep4);
+  r.pcnt = c.take<int32_t>(ws, n_tiles * ep4);
   r.ptie = c.take<int32_t>(ws, std::max<int64_t>(n_tiles, 1));
   r.bytes = c.off;
   return r;
@@ -281,41 +298,56 @@ int32_t moe_expert_wgrad_launches(const moe_dims* dims) {
   return moe::wgrad_splits_bf16(*dims) > 1 ? 2 : 1;
 }
 
-moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router, float* logits,
+namespace {
+moe_status route_impl(const moe_dims* dims, const void* x, const float* w_router, float* logits,
                      int32_t* topk_idx, float* topk_gate, float* margin, float near_tie_eps,
                      int32_t* near_tie_count, int32_t n_groups, int32_t* group_count,
                      float* group_mean_prob, float* group_aux, void* workspace,
-                     size_t workspace_bytes, void* stream) {
-  moe_status st = check_dims(dims, __func__);
+                     size_t workspace_bytes, void* stream, const char* fn) {
+  moe_status st = check_dims(dims, fn);
   if (st != MOE_OK) return st;
   const moe_dims& dm = *dims;
-  MOE_REQUIRE_PTR(x, dm.T * dm.d);
-  MOE_REQUIRE_PTR(w_router, int64_t(dm.E) * dm.d);
-  MOE_REQUIRE_PTR(logits, dm.T * dm.E);
-  MOE_REQUIRE_PTR(topk_idx, dm.T * dm.k);
-  MOE_REQUIRE_PTR(topk_gate, dm.T * dm.k);
-  MOE_REQUIRE_PTR(margin, dm.T);
-  MOE_REQUIRE_PTR(near_tie_count, 1);
-  MOE_OPTIONAL_PTR(group_count);
-  MOE_OPTIONAL_PTR(group_mean_prob);
-  MOE_OPTIONAL_PTR(group_aux);
+  MOE_REQUIRE_PTR_FN(x, dm.T * dm.d, fn);
+  MOE_REQUIRE_PTR_FN(w_router, int64_t(dm.E) * dm.d, fn);
+  MOE_REQUIRE_PTR_FN(logits, dm.T * dm.E, fn);
+  MOE_REQUIRE_PTR_FN(topk_idx, dm.T * dm.k, fn);
+  MOE_REQUIRE_PTR_FN(topk_gate, dm.T * dm.k, fn);
+  MOE_REQUIRE_PTR_FN(margin, dm.T, fn);
+  MOE_REQUIRE_PTR_FN(near_tie_count, 1, fn);
+  MOE_OPTIONAL_PTR_FN(group_count, fn);
+  MOE_OPTIONAL_PTR_FN(group_mean_prob, fn);
+  MOE_OPTIONAL_PTR_FN(group_aux, fn);
   if (n_groups < 1)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d must be >= 1", __func__, n_groups);
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d must be >= 1", fn, n_groups);
   if (dm.T % n_groups)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d does not divide T=%lld", __func__,
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: n_groups=%d does not divide T=%lld", fn,
                 n_groups, static_cast<long long>(dm.T));
   if (!std::isfinite(near_tie_eps))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: near_tie_eps is not finite", __func__);
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: near_tie_eps is not finite", fn);
   const int tile = route_tile(dm.T, n_groups, dm.act);
+  if ((dm.T + tile - 1) / tile * int64_t((dm.E + 3) & ~3) * 4 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T=%lld with %d balancing groups needs over 2 GiB of "
+                "router partial sums", fn, static_cast<long long>(dm.T), n_groups);
   const RouteWs need = route_ws(dm, tile, nullptr);
-  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
+  st = check_ws(workspace, workspace_bytes, need.bytes, fn);
   if (st != MOE_OK) return st;
   const RouteWs w = route_ws(dm, tile, workspace);
   return hip_status(moe::launch_route(dm, x, w_router, logits, topk_idx, topk_gate, margin,
                                       near_tie_eps, near_tie_count, n_groups, group_count,
                                       group_mean_prob, group_aux, tile, w.psum, w.pcnt, w.ptie,
-                                      static_cast<hipStream_t>(stream)),
-                    __func__);
+                                      w.arrivals, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+}  // namespace
+
+moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router, float* logits,
+                     int32_t* topk_idx, float* topk_gate, float* margin, float near_tie_eps,
+                     int32_t* near_tie_count, int32_t n_groups, int32_t* group_count,
+                     float* group_mean_prob, float* group_aux, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return route_impl(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_eps,
+                    near_tie_count, n_groups, group_count, group_mean_prob, group_aux, workspace,
+                    workspace_bytes, stream, __func__);
 }
 
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_counts,

@@ -17,6 +17,12 @@
 //               expert come out in ascending token id;
 //   4. gather:  each 16-byte piece of X is read once and written to the k
 //               rows of its token (coalesced row moves).
+// A token whose row lists one expert twice is outside the routing contract
+// (a top-k never repeats an expert).  It is still sorted by the definition:
+// each of its slots gets a row, in slot order.  A block that holds such a
+// token ranks its assignments serially (one thread per expert walks the
+// block's tokens and slots in order) instead of by bitmap popcounts, which
+// count a token once per expert.
 #include "common.h"
 
 namespace moe {
@@ -101,23 +107,59 @@ __global__ __launch_bounds__(256) void key_scan_kernel(const int32_t* __restrict
 
 namespace {
 
+constexpr int kMaxK = 16;
+
+// slot j of a token's row repeats an expert of an earlier slot
+__device__ __forceinline__ bool repeats_earlier_slot(const int32_t* row, int j, int32_t e) {
+  for (int i = 0; i < j; ++i)
+    if (row[i] == e) return true;
+  return false;
+}
+
+// Ranks of every assignment of the block starting at token tb inside its
+// expert, by definition: thread e walks the block's tokens in order and each
+// token's slots in order (srank[local token * k + slot]).  Ends with a
+// workgroup barrier.
+__device__ void rank_serially(const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
+                              int64_t tb, int32_t* srank) {
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    int32_t r = 0;
+    for (int tl = 0; tl < kPermBlock && tb + tl < T; ++tl) {
+      int32_t row[kMaxK];   // the token's slots, loaded together
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j) row[j] = (j < k) ? idx[(tb + tl) * k + j] : -1;
+#pragma unroll
+      for (int j = 0; j < kMaxK; ++j)
+        if (j < k && row[j] == e) srank[tl * k + j] = r++;
+    }
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
     const int32_t* __restrict__ base, int32_t* __restrict__ pos, int32_t* __restrict__ src,
     const float* __restrict__ gate, float* __restrict__ gate_perm) {
   __shared__ unsigned long long bits[kMaxKeys][kWords];
+  __shared__ int32_t srank[kPermBlock * kMaxK];
+  __shared__ int dup;
   const int tid = threadIdx.x;
   for (int i = tid; i < E * kWords; i += kThreads) bits[i / kWords][i % kWords] = 0ull;
+  if (tid == 0) dup = 0;
   __syncthreads();
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + tid;
   const int w = tid >> 6, lane = tid & 63;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int32_t e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(&bits[e][w], 1ull << lane);
+      if (e >= 0 && e < E) {
+        atomicOr(&bits[e][w], 1ull << lane);
+        if (repeats_earlier_slot(idx + t * k, j, e)) dup = 1;
+      }
     }
   }
   __syncthreads();
+  if (dup) rank_serially(idx, T, k, E, static_cast<int64_t>(blockIdx.x) * kPermBlock, srank);
   if (t < T) {
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j = 0; j < k; ++j) {
@@ -126,8 +168,13 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
         pos[t * k + j] = -1;
         continue;
       }
-      int32_t rank = __popcll(bits[e][w] & below);
-      for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+      int32_t rank;
+      if (dup) {
+        rank = srank[tid * k + j];
+      } else {
+        rank = __popcll(bits[e][w] & below);
+        for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+      }
       const int32_t p = base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
       pos[t * k + j] = p;
       src[p] = static_cast<int32_t>(t);
@@ -147,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 // workgroups.
 constexpr int kSgSplit = 4;
 constexpr int kSgTok = kPermBlock / kSgSplit;
+constexpr int kSgMaxBlocks = 128;
 __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
     const int32_t* __restrict__ hist, int32_t nb, int32_t* __restrict__ counts,
@@ -155,7 +203,9 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     const float* __restrict__ gate, float* __restrict__ gate_perm) {
   __shared__ unsigned long long bits[kMaxKeys][kWords];
   __shared__ int32_t tot[kMaxKeys], pre[kMaxKeys], base[kMaxKeys + 1];
-  __shared__ int32_t spos[kSgTok * 16];
+  __shared__ int32_t spos[kSgTok * kMaxK];
+  __shared__ int32_t srank[kPermBlock * kMaxK];
+  __shared__ int dup;
   const int tid = threadIdx.x;
   const int b = blockIdx.x / kSgSplit, q = blockIdx.x % kSgSplit;
   for (int i = tid; i < E * kWords; i += kThreads) bits[i / kWords][i % kWords] = 0ull;
@@ -163,22 +213,23 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     tot[e] = 0;
     pre[e] = 0;
   }
+  if (tid == 0) dup = 0;
   __syncthreads();
   {
-    const int n = nb * E;
+    const int64_t n = static_cast<int64_t>(nb) * E;
     constexpr int kU = 8;
-    for (int i0 = tid; i0 < n; i0 += kThreads * kU) {
+    for (int64_t i0 = tid; i0 < n; i0 += kThreads * kU) {
       int32_t v[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int i = i0 + u * kThreads;
+        const int64_t i = i0 + u * kThreads;
         v[u] = (i < n) ? hist[i] : 0;
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const int i = i0 + u * kThreads;
+        const int64_t i = i0 + u * kThreads;
         if (i >= n || v[u] == 0) continue;
-        const int e = i % E;
+        const int e = static_cast<int>(i % E);
         atomicAdd(&tot[e], v[u]);
         if (i / E < b) atomicAdd(&pre[e], v[u]);
       }
@@ -206,18 +257,27 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
   if (live) {
     for (int j = 0; j < k; ++j) {
       const int32_t e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(&bits[e][w], 1ull << lane);
+      if (e >= 0 && e < E) {
+        atomicOr(&bits[e][w], 1ull << lane);
+        if (repeats_earlier_slot(idx + t * k, j, e)) dup = 1;
+      }
     }
   }
   __syncthreads();
+  if (dup) rank_serially(idx, T, k, E, static_cast<int64_t>(b) * kPermBlock, srank);
   if (live && w == q) {   // this workgroup's quarter: tokens 64 q ... 64 q + 63 of block b
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int j = 0; j < k; ++j) {
       const int32_t e = idx[t * k + j];
       int32_t p = -1;
       if (e >= 0 && e < E) {
-        int32_t rank = __popcll(bits[e][w] & below);
-        for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+        int32_t rank;
+        if (dup) {
+          rank = srank[tid * k + j];
+        } else {
+          rank = __popcll(bits[e][w] & below);
+          for (int ww = 0; ww < w; ++ww) rank += __popcll(bits[e][ww]);
+        }
         p = base[e] + pre[e] + rank;
         src[p] = static_cast<int32_t>(t);
         if (gate_perm) gate_perm[p] = gate[t * k + j];
@@ -274,8 +334,10 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
                        ws_hist);
   }
-  // short rows: scan, scatter and gather fused
-  if (nb > 0 && dm.d * elem <= 1024 && dm.k <= 16) {
+  // short rows and few blocks: scan, scatter and gather fused (every one of
+  // the 4 nb workgroups reads the whole [nb, E] block histogram, so the fused
+  // form is kept to nb <= 128, T <= 32768)
+  if (nb > 0 && nb <= kSgMaxBlocks && dm.d * elem <= 1024 && dm.k <= kMaxK) {
     hipLaunchKernelGGL(perm_scatter_gather_kernel, dim3(nb * kSgSplit), dim3(kThreads), 0, s, idx, dm.T,
                        dm.k, dm.E, ws_hist, static_cast<int32_t>(nb), counts, offsets, pos, src,
                        static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr, gate,

@@ -1,5 +1,5 @@
 // Router: logits, wavefront top-k, renormalised gates, margins, near-ties and
-// per-block load-balancing partial sums.
+// per-block load-balancing statistics.
 //
 // Method sources: "Expert Coupling in MoE Pretraining" (Abstract: each token
 // is routed to k of E experts); "Revisiting MoE and Dense Speed-Accuracy
@@ -8,29 +8,18 @@
 // Pretraining: Parallelism Layout Changes the Model" (Finding 3: the margin
 // between the k-th and (k+1)-th scores; balancing statistics per machine).
 //
-// One workgroup owns `tile` consecutive tokens (tile divides T/G, so a tile
-// never straddles two balancing blocks).  Phase 1 computes the tile's logits
-// with fp32 FMAs from LDS-staged chunks of X and Wr.  Phase 2 gives each token
-// to one wavefront: the E logits sit in registers (lane e holds experts e,
-// e+64, ...) and k+1 rounds of a wave-wide (value, lowest id) arg-max pick the
-// experts in order and the runner-up for the margin.  Per-tile partial sums of
-// the full softmax and the per-expert counts go to the workspace; a second
-// kernel reduces them per block in a fixed order (no floating-point atomics).
+// The main kernel gives each workgroup a tile of consecutive tokens (a tile
+// never straddles two balancing blocks): logits, then one 16-lane group (or
+// one wavefront) per token for top-k, gates, margin and the full softmax, and
+// per-tile partial sums of the balancing statistics, which are folded per
+// block in a fixed order (no floating-point atomics).  Two launches per call:
+// for d > 256 (bf16, E <= 64) a one-thread kernel clears an arrival counter
+// and the last workgroup of the streaming router folds the partials; on every
+// other path a second kernel folds them.
 #include "common.h"
 
 namespace moe {
 namespace {
-
-#ifdef MOE_TRACE
-// Timing build only: router workgroup timelines (thread 0 writes the 100 MHz
-// wall clock at marked points).
-constexpr int kRtSlots = 16;
-__device__ uint64_t moe_route_trace[1024 * kRtSlots];
-#define MOE_RT_MARK(i) \
-  if (threadIdx.x == 0 && blockIdx.x < 1024) moe_route_trace[blockIdx.x * kRtSlots + (i)] = wall_clock64()
-#else
-#define MOE_RT_MARK(i) ((void)0)
-#endif
 
 constexpr int kThreads = 256;
 constexpr int kDChunk = 32;
@@ -44,13 +33,158 @@ struct RouteArgs {
   int32_t* idx;
   float* gate;
   float* margin;
-  float* psum;      // [tiles, E]
-  int32_t* pcnt;    // [tiles, E]
-  int32_t* ptie;    // [tiles]
+  float* psum;            // [tiles, E] partial sums of the full softmax
+  int32_t* pcnt;          // [tiles, E] partial expert counts
+  int32_t* ptie;          // [tiles] partial near-tie counts
+  uint32_t* arrivals;     // workgroups done (cleared by route_prep_kernel)
+  int32_t* gcount;        // [G, E] or NULL
+  float* gprob;           // [G, E] or NULL
+  float* gaux;            // [G] or NULL
+  int32_t* tie_count;     // [1]
   int64_t T;
-  int32_t d, E, k, tile;
+  int32_t d, E, k, tile, G, n_tiles;
   float eps;
 };
+
+// Partial sums cross workgroups (and the XCDs' separate L2 caches) within
+// one kernel, so they are written and read with agent-scope atomics.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-block statistics from every tile's partials, by one 256-thread
+// workgroup.  Partials are laid out [tile][Ep4] (E rounded up to a multiple
+// of 4) and read as 16-byte vectors with the sc1 bit (coherent across the
+// XCDs' L2 caches, like the write-through stores that wrote them), all of a
+// thread's loads issued before any is used.  Fixed order throughout: thread
+// (pair, sl), pair = (block r, 4-expert column c4), adds tiles sl, sl + SLg,
+// ... of block r in tile order; the SLg sums of a pair are then added in sl
+// order; aux adds f_e P_e over e in order; the near-tie partials go through a
+// fixed thread-strided sum and lane tree.
+constexpr int kFinLoads = 16;   // loads in flight per thread
+__device__ __forceinline__ int ep4(int E) { return (E + 3) & ~3; }
+__device__ __forceinline__ float4 ld_sc1_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 16));
+}
+__device__ void route_finalize_block(const RouteArgs& a) {
+  __shared__ float4 s4[kThreads];
+  __shared__ int4 c4s[kThreads];
+  __shared__ float fpe[kThreads * 4];
+  __shared__ int32_t st[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, Ep = ep4(E), E4 = Ep / 4;
+  int E4p = 1;
+  while (E4p < E4) E4p <<= 1;
+  const int tpg = a.n_tiles / a.G;
+  const double per_group = static_cast<double>(a.T) / static_cast<double>(a.G);
+  const uint32_t pbytes = static_cast<uint32_t>(a.n_tiles) * Ep * 4;
+  const auto rp = __builtin_amdgcn_make_buffer_rsrc(a.psum, 0, pbytes, 0x00020000);
+  const auto rc = __builtin_amdgcn_make_buffer_rsrc(a.pcnt, 0, pbytes, 0x00020000);
+  // pairs (r, c4) processed 256 / SLg at a time
+  const int pairs = a.G * E4p;
+  const int SLg = pairs >= kThreads ? 1 : kThreads / pairs;
+  const int per_pass = kThreads / SLg;
+  for (int p0 = 0; p0 < pairs; p0 += per_pass) {
+    const int pair = p0 + tid / SLg, sl = tid % SLg;
+    const int r = pair / E4p, c4 = pair % E4p;
+    const bool on = pair < pairs && c4 < E4;
+    float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+    int4 C = make_int4(0, 0, 0, 0);
+    if (on) {
+      for (int i0 = sl; i0 < tpg; i0 += SLg * kFinLoads) {
+        float4 ps[kFinLoads];
+        float4 pc[kFinLoads];
+#pragma unroll
+        for (int u = 0; u < kFinLoads; ++u) {
+          const int i = min(i0 + SLg * u, tpg - 1);
+          const uint32_t o = static_cast<uint32_t>(((static_cast<int64_t>(r) * tpg + i) * Ep + 4 * c4) * 4);
+          ps[u] = ld_sc1_f4(rp, o);
+          pc[u] = ld_sc1_f4(rc, o);
+        }
+#pragma unroll
+        for (int u = 0; u < kFinLoads; ++u) {
+          if (i0 + SLg * u < tpg) {
+            S.x += ps[u].x; S.y += ps[u].y; S.z += ps[u].z; S.w += ps[u].w;
+            const int4 ci = __builtin_bit_cast(int4, pc[u]);
+            C.x += ci.x; C.y += ci.y; C.z += ci.z; C.w += ci.w;
+          }
+        }
+      }
+    }
+    s4[tid] = S;
+    c4s[tid] = C;
+    __syncthreads();
+    if (on && sl == 0) {
+      float4 T4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      int4 N4 = make_int4(0, 0, 0, 0);
+      for (int q = 0; q < SLg; ++q) {
+        const float4 v = s4[tid + q];
+        const int4 n = c4s[tid + q];
+        T4.x += v.x; T4.y += v.y; T4.z += v.z; T4.w += v.w;
+        N4.x += n.x; N4.y += n.y; N4.z += n.z; N4.w += n.w;
+      }
+      const float sv[4] = {T4.x, T4.y, T4.z, T4.w};
+      const int32_t nv[4] = {N4.x, N4.y, N4.z, N4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * c4 + q;
+        float prod = 0.f;
+        if (e < E) {
+          const float P = (per_group > 0) ? static_cast<float>(sv[q] / per_group) : 0.f;
+          const float fr = (per_group > 0) ? static_cast<float>(nv[q] / (per_group * a.k)) : 0.f;
+          if (a.gcount) a.gcount[static_cast<int64_t>(r) * E + e] = nv[q];
+          if (a.gprob) a.gprob[static_cast<int64_t>(r) * E + e] = P;
+          prod = fr * P;
+        }
+        fpe[(tid / SLg) * 4 + q] = prod;
+      }
+    }
+    __syncthreads();
+    // aux of the blocks in this pass (a pass holds whole blocks: per_pass is
+    // a multiple of E4p or covers every pair): one thread per block, e in order
+    const int rr = p0 / E4p + tid;
+    if (rr < a.G && (rr + 1) * E4p <= p0 + per_pass) {
+      float v = 0.f;
+      for (int e = 0; e < E; ++e) v += fpe[(rr * E4p - p0) * 4 + e];
+      if (a.gaux) a.gaux[rr] = static_cast<float>(E) * v;
+    }
+    __syncthreads();
+  }
+  int32_t t = 0;
+  for (int i = tid; i < a.n_tiles; i += kThreads) t += ld_agent(a.ptie + i);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) t += __shfl_xor(t, m, 64);
+  if (lane == 0) st[wave] = t;
+  __syncthreads();
+  if (tid == 0) *a.tie_count = st[0] + st[1] + st[2] + st[3];
+}
+
+// End of a tile: its partials were stored with write-through (agent-scope)
+// stores by the caller; each wavefront waits until its stores are
+// acknowledged, the workgroup counts itself in, and the last one to arrive
+// folds every tile's partials.
+__device__ __forceinline__ void route_arrive(const RouteArgs& a) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == static_cast<uint32_t>(a.n_tiles - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  route_finalize_block(a);
+}
 
 struct Key {
   float v;
@@ -99,16 +233,37 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 #pragma unroll
   for (int i = 0; i < kOutPerThread; ++i) acc[i] = 0.f;
 
-  for (int c0 = 0; c0 < d; c0 += kDChunk) {
-    for (int v = tid; v < tile * kDChunk; v += kThreads) {
-      const int t = v / kDChunk, c = v % kDChunk;
-      xs[t][c] = (t < ntok) ? Act<TX>::load(x + (t0 + t) * d + c0 + c) : 0.f;
+  // chunk c0 + kDChunk is loaded into registers while chunk c0 is summed,
+  // so a chunk costs one memory latency in total, not one each
+  constexpr int kXPer = kRouteTileMax * kDChunk / kThreads;   // 4
+  constexpr int kWPer = kMaxE * kDChunk / kThreads;           // 32
+  float xr[kXPer], wv[kWPer];
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) {
+      const int v = tid + u * kThreads, t = v / kDChunk, c = v % kDChunk;
+      xr[u] = (t < ntok && c0 < d) ? Act<TX>::load(x + (t0 + t) * d + c0 + c) : 0.f;
     }
-    for (int v = tid; v < E * kDChunk; v += kThreads) {
-      const int e = v / kDChunk, c = v % kDChunk;
-      wsh[e][c] = a.wr[static_cast<int64_t>(e) * d + c0 + c];
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u) {
+      const int v = tid + u * kThreads, e = v / kDChunk, c = v % kDChunk;
+      wv[u] = (e < E && c0 < d) ? a.wr[static_cast<int64_t>(e) * d + c0 + c] : 0.f;
+    }
+  };
+  load_chunk(0);
+  for (int c0 = 0; c0 < d; c0 += kDChunk) {
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) {
+      const int v = tid + u * kThreads;
+      if (v < tile * kDChunk) xs[v / kDChunk][v % kDChunk] = xr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kWPer; ++u) {
+      const int v = tid + u * kThreads;
+      if (v < E * kDChunk) wsh[v / kDChunk][v % kDChunk] = wv[u];
     }
     __syncthreads();
+    load_chunk(c0 + kDChunk);
 #pragma unroll
     for (int i = 0; i < kOutPerThread; ++i) {
       const int o = tid + i * kThreads;
@@ -217,8 +372,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
       s += psum_w[w][e];
       c += pcnt_w[w][e];
     }
-    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
-    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+    a.psum[static_cast<int64_t>(blockIdx.x) * ep4(E) + e] = s;
+    a.pcnt[static_cast<int64_t>(blockIdx.x) * ep4(E) + e] = c;
   }
   if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
 }
@@ -316,7 +471,7 @@ __device__ __forceinline__ uint64_t key_max_level(uint64_t k) {
 // wavefront `wave` holds the logits of tokens t0 + 16 wave + 4 g + q (q < 4)
 // for experts 16 j + c in acc[j][q].  Writes logits, top-k ids and gates,
 // margins, and the workgroup's LB partial sums (fixed-order folds).
-template <int NT>
+template <int NT, bool FUSED>
 __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f32x4_t (&acc)[NT],
                                                     int64_t t0) {
   __shared__ float psum_w[4][16 * NT];
@@ -346,7 +501,6 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
       if (live[q] && e < E) a.logits[tg * E + e] = acc[j][q];
     }
   }
-  MOE_RT_MARK(4);
   uint64_t key[4][NT];
   uint64_t my_key[4], k_top[4], k_km1[4], k_k[4];
 #pragma unroll
@@ -402,7 +556,6 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
     my_v[q] = (c < k) ? sel_key_value(my_key[q]) : -INFINITY;
     my_i[q] = (c < k) ? sel_key_expert(my_key[q]) : 0;
   }
-  MOE_RT_MARK(5);
   float ex[4][NT], part[4], my_e[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -426,7 +579,6 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
   for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor2>(part[q]); z[q] += row_rot<kRowRor2>(z[q]); }
 #pragma unroll
   for (int q = 0; q < 4; ++q) { part[q] += row_rot<kRowRor1>(part[q]); z[q] += row_rot<kRowRor1>(z[q]); }
-  MOE_RT_MARK(6);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t tg = t0 + wave * 16 + g * 4 + q;
@@ -448,7 +600,6 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
       }
     }
   }
-  MOE_RT_MARK(7);
   // fold the 4 lane groups (fixed xor order), then the 4 waves (fixed order)
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -467,14 +618,25 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
   ties += __shfl_xor(ties, 32, 64);
   if (lane == 0) tie_w[wave] = ties;
   __syncthreads();
-  MOE_RT_MARK(8);
   for (int e = tid; e < E; e += kThreads) {
     const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
     const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
-    a.psum[static_cast<int64_t>(blockIdx.x) * E + e] = s;
-    a.pcnt[static_cast<int64_t>(blockIdx.x) * E + e] = n;
+    const int64_t o = static_cast<int64_t>(blockIdx.x) * ep4(E) + e;
+    if (FUSED) {
+      st_agent(a.psum + o, s);
+      st_agent(a.pcnt + o, n);
+    } else {
+      a.psum[o] = s;
+      a.pcnt[o] = n;
+    }
   }
-  if (tid == 0) a.ptie[blockIdx.x] = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+  const int32_t tt = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+  if (FUSED) {
+    if (tid == 0) st_agent(a.ptie + blockIdx.x, tt);
+    route_arrive(a);
+  } else if (tid == 0) {
+    a.ptie[blockIdx.x] = tt;
+  }
 }
 
 template <int NT>   // 16-expert tiles: E <= 16 NT
@@ -591,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  route_tile_epilogue<NT>(a, acc, t0);
+  route_tile_epilogue<NT, false>(a, acc, t0);
 }
 
 // Matrix-core router for small E d (the split weight fits in LDS whole):
@@ -614,7 +776,6 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
   const int64_t my_row = t0 + wave * 16 + c;
   const bool row_ok = my_row < a.T;
   const bf16_t* xrow = x + (row_ok ? my_row : 0) * d + g * 8;
-  MOE_RT_MARK(0);
   uint4 xa[NKC];
 #pragma unroll
   for (int kt = 0; kt < NKC; ++kt) {
@@ -671,7 +832,6 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
     }
   }
   __syncthreads();
-  MOE_RT_MARK(1);
   f32x4_t acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -687,15 +847,11 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
       }
   }
-#ifdef MOE_TRACE
-  if (acc[0][0] == 12345.f) acc[0][1] = 0.f;   // keep the mark after the MFMAs
-#endif
-  MOE_RT_MARK(2);
-  route_tile_epilogue<NT>(a, acc, t0);
-  MOE_RT_MARK(3);
+  route_tile_epilogue<NT, false>(a, acc, t0);
 }
 
-// One workgroup (1024 threads) per balancing block r (grid G), all experts in
+// Second launch of the two-kernel paths (every path but the streaming one):
+// one workgroup (1024 threads) per balancing block r (grid G), all experts in
 // one pass: thread (slice, e) with slice < SL = 1024 / E_p (E_p: E rounded up
 // to a power of two, at least 16) adds tiles slice, slice + SL, ... of block r
 // in tile order (16 loads in flight); the slice sums are folded in a fixed
@@ -731,8 +887,8 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
       for (int u = 0; u < 16; ++u) {
         const int i = min(i0 + SL * u, tiles_per_group - 1);
         const int64_t tile = static_cast<int64_t>(r) * tiles_per_group + i;
-        ps[u] = psum[tile * E + e];
-        pc[u] = pcnt[tile * E + e];
+        ps[u] = psum[tile * ep4(E) + e];
+        pc[u] = pcnt[tile * ep4(E) + e];
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -794,21 +950,274 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router for bf16 hidden states, E <= 64 and d > 256: the weight streamed.
+//
+// The fp32 router weight is split exactly into three bf16 terms on the fly
+// (hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid), each remainder
+// exact in fp32, so hi + mid + lo = w); a bf16 x times a bf16 term is exact in
+// fp32, so three v_mfma_f32_16x16x32_bf16 passes into one fp32 accumulator give
+// an fp32-accumulated dot product with the fp32 weights.
+//
+// 64 tokens per workgroup, 4 wavefronts; wavefront w computes expert block
+// w % NT for the token blocks w / NT + (4 / NT) i.  The k loop runs in 64-wide
+// chunks, S - 1 chunks ahead: each wavefront moves its own 16 tokens' X chunk
+// into an LDS ring with direct-to-LDS loads, laid out as two A fragments, and
+// the fp32 weights of its own expert block in the B-fragment layout (lane
+// 16 g + c: expert 16 j + c, k = 8 g ... 8 g + 7 of each 32-wide half), which
+// it reads back and splits in registers.  Only direct-to-LDS loads fill the
+// ring: register-destination loads carried around the loop would make the
+// compiler drain the memory counter at the loop head.  Fragment reads from LDS are
+// inline-asm ds_read_b128 that wait for themselves, and each chunk waits for
+// its own loads with an explicit vmcnt plus a barrier (the compiler would
+// drain every direct-to-LDS load in flight before its own LDS reads).  The
+// logits then pass through LDS so that each wavefront holds its 16 tokens' E
+// logits in the epilogue's layout.  route_prep_kernel clears the arrival
+// counter first; the last workgroup folds the balancing statistics.
+// ---------------------------------------------------------------------------
+namespace rdma {
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nbytes, 0x00020000);
+}
+// The per-lane offset (voff) stays in one loop-invariant register; the
+// per-chunk offset goes in the scalar soff.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, static_cast<int>(voff),
+                                           static_cast<int>(soff), 0, 0);
+}
+__device__ __forceinline__ float4 ldf4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+// s_waitcnt with vmcnt = N (bits 3-0 and 15-14), expcnt and lgkmcnt left free
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+}  // namespace rdma
+
+// hi, mid, lo bf16 terms of 8 fp32 weights, packed as three B fragments
+__device__ __forceinline__ void split8(const float4& w0, const float4& w1, bf16x8_t& hi,
+                                       bf16x8_t& mid, bf16x8_t& lo) {
+  const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    h[p] = bf16x2_rne(w[2 * p], w[2 * p + 1]);
+    const float r0 = w[2 * p] - __uint_as_float(h[p] << 16);
+    const float r1 = w[2 * p + 1] - __uint_as_float(h[p] & 0xFFFF0000u);
+    m[p] = bf16x2_rne(r0, r1);
+    l[p] = bf16x2_rne(r0 - __uint_as_float(m[p] << 16), r1 - __uint_as_float(m[p] & 0xFFFF0000u));
+  }
+  hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+  mid = __builtin_bit_cast(bf16x8_t, make_uint4(m[0], m[1], m[2], m[3]));
+  lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
+}
+
+// Clears the arrival counter of the streaming router.
+__global__ __launch_bounds__(64) void route_prep_kernel(uint32_t* arrivals) {
+  if (threadIdx.x == 0) *arrivals = 0u;
+}
+
+// A fragments of one chunk from LDS: the wavefront's token blocks i and both
+// 32-wide halves, frag[i][h] at byte offset (2 (4 / NT) i + h) 1 KB from addr;
+// one wait for all of them, inside the same asm block.
+template <int NT>
+__device__ __forceinline__ void read_a(bf16x8_t (&f)[NT][2], uint32_t addr);
+template <>
+__device__ __forceinline__ void read_a<1>(bf16x8_t (&f)[1][2], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:0\n\t"
+      "ds_read_b128 %1, %2 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0][0]), "=&v"(f[0][1])
+      : "v"(addr)
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_a<2>(bf16x8_t (&f)[2][2], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:4096\n\t"
+      "ds_read_b128 %3, %4 offset:5120\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1])
+      : "v"(addr)
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_a<4>(bf16x8_t (&f)[4][2], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:0\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1]), "=&v"(f[2][0]),
+        "=&v"(f[2][1]), "=&v"(f[3][0]), "=&v"(f[3][1])
+      : "v"(addr)
+      : "memory");
+}
+
+// fp32 weights of one chunk from LDS: 4 x 16 bytes at (q) 1 KB from addr
+__device__ __forceinline__ void read_w4(float4 (&f)[4], uint32_t addr) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:0\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3])
+      : "v"(addr)
+      : "memory");
+}
+
+template <int NT, int S>   // NT: 16-expert blocks (E <= 16 NT); S: ring stages
+__global__ __launch_bounds__(kThreads, 1) void route_stream_kernel(RouteArgs a) {
+  // a stage: 8 A fragments (4 token blocks x 2 halves) of 1 KB, then per
+  // wavefront 4 KB of fp32 weights (lane-major: 1 KB per 16-byte quarter)
+  constexpr int kFrag = 512;                    // bf16 elements per KB
+  constexpr int kStage = (8 + 4 * 4) * kFrag;
+  constexpr int BSTEP = 4 / NT;                 // token-block stride of one wavefront
+  constexpr int kLdL = 68;                      // logit exchange row stride (floats)
+  static_assert(S >= 2 && 64 * kLdL * 4 <= S * kStage * 2, "exchange fits the ring");
+  __shared__ __attribute__((aligned(16))) bf16_t xs[S * kStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int d = a.d;
+  const int nk = d / 64;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMTile;
+  const int jw = wave % NT;
+  const int bw0 = wave / NT;
+
+  const int rows = static_cast<int>(min<int64_t>(kMTile, a.T - t0));
+  const bf16_t* xbase = static_cast<const bf16_t*>(a.x) + t0 * d;
+  const auto rx = rdma::rsrc(xbase, static_cast<uint32_t>(rows) * d * 2);
+  const auto rxz = rdma::rsrc(xbase, 0);
+  const auto rw = rdma::rsrc(a.wr, static_cast<uint32_t>(a.E) * d * 4);
+  const auto rwz = rdma::rsrc(a.wr, 0);
+  // per-lane offsets, loop invariant: X row 16 wave + c at k 8 g (bf16); the
+  // weights of expert 16 jw + c at k 8 g (fp32; rows past E read 0)
+  const uint32_t xvoff = static_cast<uint32_t>(((16 * wave + c) * d + 8 * g) * 2);
+  const uint32_t wvoff = static_cast<uint32_t>(((16 * jw + c) * d + 8 * g) * 4);
+
+  auto issue = [&](int kt, int slot) {
+    const bool on = kt < nk;
+    bf16_t* st = xs + slot * kStage;
+    const uint32_t sx = static_cast<uint32_t>(kt) * 128, sw = static_cast<uint32_t>(kt) * 256;
+    rdma::dma16(on ? rx : rxz, st + (2 * wave) * kFrag, xvoff, sx);
+    rdma::dma16(on ? rx : rxz, st + (2 * wave + 1) * kFrag, xvoff, sx + 64);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)   // half h = q / 2 at k + 32 h, + 4 weights for odd q
+      rdma::dma16(on ? rw : rwz, st + (8 + 4 * wave + q) * kFrag, wvoff,
+                  sw + (q >> 1) * 128 + (q & 1) * 16);
+  };
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t lds_x = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)xs));
+  const uint32_t a_addr = lds_x + bw0 * 2048 + lane * 16;
+  const uint32_t w_addr = lds_x + (8 + 4 * wave) * 1024 + lane * 16;
+
+#pragma unroll
+  for (int u = 0; u < S - 1; ++u) issue(u, u);
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nk) {
+        // this chunk's 6 loads done (the 6 of each of the S - 2 later chunks
+        // may still be in flight), and every wavefront past the previous
+        // chunk's reads, whose stage the next issue overwrites
+        rdma::wait_vm<6 * (S - 2)>();
+        __builtin_amdgcn_s_barrier();
+        issue(kt + S - 1, (u + S - 1) % S);
+        float4 wv[4];
+        read_w4(wv, w_addr + u * kStage * 2);
+        bf16x8_t af[NT][2];
+        read_a<NT>(af, a_addr + u * kStage * 2);
+        bf16x8_t bf[2][3];
+        split8(wv[0], wv[1], bf[0][0], bf[0][1], bf[0][2]);
+        split8(wv[2], wv[3], bf[1][0], bf[1][1], bf[1][2]);
+        // per token block: k order, then the hi, mid, lo terms
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < NT; ++i)
+#pragma unroll
+            for (int sp = 0; sp < 3; ++sp)
+              acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i][h], bf[h][sp], acc[i], 0, 0, 0);
+      }
+    }
+  }
+  rdma::wait_vm<0>();
+  __syncthreads();
+  // logits through LDS: wavefront w then holds tokens 16 w + 4 g + q, experts
+  // 16 j + c in acc_e[j][q]
+  float* L = reinterpret_cast<float*>(xs);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int b = bw0 + BSTEP * i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) L[(16 * b + 4 * g + q) * kLdL + 16 * jw + c] = acc[i][q];
+  }
+  __syncthreads();
+  f32x4_t acc_e[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc_e[j][q] = L[(16 * wave + 4 * g + q) * kLdL + 16 * j + c];
+  route_tile_epilogue<NT, true>(a, acc_e, t0);
+}
+
 }  // namespace
 
-// The LDS router holds the whole split weight of up to 64 experts for d <= 256.
+// bf16 hidden states with E <= 64: for d <= 256 the split weight sits in LDS
+// whole (route_lds_kernel); beyond, it is streamed (route_split_kernel).
 bool route_in_lds(const moe_dims& dm) {
   return dm.act == MOE_BF16 && dm.E <= 64 && dm.d <= 256 && dm.d % 64 == 0;
+}
+bool route_split_ok(const moe_dims& dm) {
+  return dm.act == MOE_BF16 && dm.E <= 64 && dm.d > 256 && dm.d % 64 == 0;
+}
+int route_split_nt(const moe_dims& dm) {
+  const int nt = (dm.E + 15) / 16;
+  return nt <= 1 ? 1 : nt <= 2 ? 2 : 4;
 }
 
 hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
-                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie, hipStream_t s) {
+                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie,
+                        uint32_t* ws_arrivals, hipStream_t s) {
   const int64_t n_tiles = (dm.T + tile - 1) / tile;
+  RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie, ws_arrivals,
+              gcount, gprob, gaux, tie_count, dm.T, dm.d, dm.E, dm.k, tile, G,
+              static_cast<int32_t>(n_tiles), eps};
+  if (n_tiles > 0 && tile == kRouteMfmaTile && route_split_ok(dm)) {
+    // streaming path: the split weight and the cleared counter first; the
+    // last workgroup of the main kernel folds the statistics
+    const int nt = route_split_nt(dm);
+    hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(64), 0, s, ws_arrivals);
+    switch (nt) {
+      case 1: hipLaunchKernelGGL((route_stream_kernel<1, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((route_stream_kernel<2, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL((route_stream_kernel<4, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   if (n_tiles > 0) {
-    RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie,
-                dm.T, dm.d, dm.E, dm.k, tile, eps};
     if (tile == kRouteMfmaTile && route_in_lds(dm)) {
       const int nt = (dm.E + 15) / 16;
       const int nt_p = nt <= 1 ? 1 : nt <= 2 ? 2 : 4;
@@ -825,12 +1234,12 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
 #undef MOE_RL_D
 #undef MOE_RL
     } else if (tile == kRouteMfmaTile) {
-      const int nt = (dm.E + 15) / 16;
+      const int ntm = (dm.E + 15) / 16;
 #define MOE_RM(N)                                                                        \
   case N:                                                                                \
     hipLaunchKernelGGL(route_mfma_kernel<N>, dim3(n_tiles), dim3(kThreads), 0, s, a);    \
     break;
-      switch (nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16) {
+      switch (ntm <= 1 ? 1 : ntm <= 2 ? 2 : ntm <= 4 ? 4 : ntm <= 8 ? 8 : 16) {
         MOE_RM(1)
         MOE_RM(2)
         MOE_RM(4)
@@ -854,10 +1263,3 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
 }
 
 }  // namespace moe
-
-#ifdef MOE_TRACE
-extern "C" int moe_debug_route_trace_copy(void* host, size_t bytes) {
-  const size_t n = std::min(bytes, sizeof(moe::moe_route_trace));
-  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::moe_route_trace), n));
-}
-#endif
