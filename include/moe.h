@@ -127,6 +127,27 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_route_noalloc -- moe_route for callers that cannot allocate device
+ * memory or hand over a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, outputs,
+ * kernels and bits as moe_route, without workspace and workspace_bytes: the
+ * scratch (per-tile partial sums and an arrival counter, cleared by the call
+ * itself where it must start at zero) lives in a static device array of
+ * moe_route_noalloc_max_bytes() = 4 MiB that the library holds on every GPU
+ * it runs on until the process ends.  Dims whose scratch exceeds it (about
+ * 2000 64-token tiles at E = 256, 8000 at E = 64) return MOE_ERR_UNSUPPORTED
+ * with nothing enqueued.  Every call on one GPU shares that GPU's array and
+ * leaves its last contents there: calls that overlap on one GPU (different
+ * streams without ordering between them) race and must not be issued.
+ */
+size_t moe_route_noalloc_max_bytes(void);   /* [host] */
+moe_status moe_route_noalloc(const moe_dims* dims, const void* x, const float* w_router,
+                             float* logits, int32_t* topk_idx, float* topk_gate, float* margin,
+                             float near_tie_eps, int32_t* near_tie_count, int32_t n_groups,
+                             int32_t* group_count, float* group_mean_prob, float* group_aux,
+                             void* stream);
+
+/*
  * moe_permute -- stable counting sort of the T*k (token, slot) assignments by
  * expert, and the row gather into expert-contiguous order.
  *   [COUPLING] Abstract and Fig. 5 step 3 (dispatch tokens to their experts);

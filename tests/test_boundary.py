@@ -191,3 +191,14 @@ def test_gate_folded_support_query():
     st = lib.moe_expert_up_folded(ctypes.byref(split), *([FAKE] * 9), None)
     assert st == UNSUP and "moe_gate_folded_supported" in L.last_error()
 
+
+def test_route_noalloc_rejects_dims_beyond_its_static_scratch():
+    """The allocation-free router refuses, on the host and before any device
+    call, dims whose scratch exceeds the static array (4 MiB)."""
+    lib = L.lib()
+    assert L.moe_route_noalloc_max_bytes() == 4 << 20
+    dm = dims(T=1 << 20, d=64, E=256, f=64, k=1)
+    st = lib.moe_route_noalloc(ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-3, FAKE,
+                               1, None, None, None, None)
+    assert st == UNSUP, L.last_error()
+    assert "static scratch" in L.last_error()

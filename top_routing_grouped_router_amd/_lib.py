@@ -41,7 +41,8 @@ EXPORTED = (
     "moe_coselect_cross", "moe_shuffle_plan", "moe_route_flips",
     "moe_gate_folded_supported", "moe_dgate_parts", "moe_permute_gates",
     "moe_expert_up_folded", "moe_expert_dgrad_down_folded", "moe_dgate_from_parts",
-    "moe_expert_wgrad_folded", "moe_route_bwd_folded",
+    "moe_expert_wgrad_folded", "moe_route_bwd_folded", "moe_route_noalloc",
+    "moe_route_noalloc_max_bytes",
 )
 
 
@@ -70,6 +71,8 @@ _SIGNATURES = {
     "moe_workspace_bytes": (_SZ, [_DIMS, _I32]),
     "moe_expert_wgrad_launches": (_I32, [_DIMS]),
     "moe_route": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _F32, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_noalloc": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _F32, _P, _I32, _P, _P, _P, _P]),
+    "moe_route_noalloc_max_bytes": (_SZ, []),
     "moe_permute": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_swiglu_fwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_combine": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
@@ -198,6 +201,25 @@ def moe_route(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_e
         _ptr(group_aux, "group_aux", torch.float32), _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_route")
+
+
+def moe_route_noalloc(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_eps,
+                      near_tie_count, n_groups, group_count, group_mean_prob, group_aux,
+                      stream=None):
+    act = act_dtype(dims)
+    st = lib().moe_route_noalloc(
+        ctypes.byref(dims), _ptr(x, "x", act), _ptr(w_router, "w_router", torch.float32),
+        _ptr(logits, "logits", torch.float32), _ptr(topk_idx, "topk_idx", torch.int32),
+        _ptr(topk_gate, "topk_gate", torch.float32), _ptr(margin, "margin", torch.float32),
+        float(near_tie_eps), _ptr(near_tie_count, "near_tie_count", torch.int32), int(n_groups),
+        _ptr(group_count, "group_count", torch.int32),
+        _ptr(group_mean_prob, "group_mean_prob", torch.float32),
+        _ptr(group_aux, "group_aux", torch.float32), _stream(stream))
+    _check(st, "moe_route_noalloc")
+
+
+def moe_route_noalloc_max_bytes() -> int:
+    return int(lib().moe_route_noalloc_max_bytes())
 
 
 def moe_permute(dims, topk_idx, expert_counts, expert_offsets, pos, src_token, x, x_perm,

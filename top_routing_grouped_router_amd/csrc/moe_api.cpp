@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -348,6 +349,68 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
   return route_impl(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_eps,
                     near_tie_count, n_groups, group_count, group_mean_prob, group_aux, workspace,
                     workspace_bytes, stream, __func__);
+}
+
+// ---------------------------------------------------------------- allocation-free router
+// moe_route with its scratch (arrival counter, per-tile partial sums) in a
+// file-scope device array instead of a caller workspace.  Each device holds
+// its own copy of the array; host code never passes the array's name (a host
+// stand-in, not a device address) but the address hipGetSymbolAddress gives
+// for the current device, looked up once per device and kept.
+namespace {
+constexpr size_t kScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status scratch_address(void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices the static scratch "
+                "table covers", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress returned NULL", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+size_t moe_route_noalloc_max_bytes(void) { return kScratchBytes; }
+
+moe_status moe_route_noalloc(const moe_dims* dims, const void* x, const float* w_router,
+                             float* logits, int32_t* topk_idx, float* topk_gate, float* margin,
+                             float near_tie_eps, int32_t* near_tie_count, int32_t n_groups,
+                             int32_t* group_count, float* group_mean_prob, float* group_aux,
+                             void* stream) {
+  moe_status st = check_dims(dims, __func__);
+  if (st != MOE_OK) return st;
+  if (n_groups >= 1 && dims->T % n_groups == 0) {
+    const int tile = route_tile(dims->T, n_groups, dims->act);
+    const size_t need = route_ws(*dims, tile, nullptr).bytes;
+    if (need > kScratchBytes)
+      return fail(MOE_ERR_UNSUPPORTED, "%s: these dims need %zu bytes of router scratch; the "
+                  "library's static scratch holds %zu (use moe_route with a workspace)",
+                  __func__, need, kScratchBytes);
+  }
+  void* ws = nullptr;
+  st = scratch_address(&ws, __func__);
+  if (st != MOE_OK) return st;
+  return route_impl(dims, x, w_router, logits, topk_idx, topk_gate, margin, near_tie_eps,
+                    near_tie_count, n_groups, group_count, group_mean_prob, group_aux, ws,
+                    kScratchBytes, stream, __func__);
 }
 
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_counts,
