@@ -13,12 +13,11 @@
 //   DGRAD_DOWN  dh = dy_perm W2; epilogue da, db from saved a, b (rows split by expert)
 //   DGRAD_UP    dx_perm = da W1 + db W3                         (rows split by expert)
 //   WGRAD       dW2 = dy^T h, dW1 = da^T x, dW3 = db^T x        (reduction over rows)
+// This file holds the fp32 path (bf16 runs on gemm_bf16.hip's kernels).
 // Tiles of A and B are staged through LDS in k-contiguous form whatever their
 // layout in HBM (operands stored with m or n contiguous are transposed while
-// being written to LDS), so one compute core serves all modes:
-//   bf16: 16x16x32 bf16 MFMA, fp32 accumulators, 4 waves x (64x64) per
-//         128x128 tile;
-//   fp32: 16x16x4 fp32 MFMA on the same tiling.
+// being written to LDS), so one compute core serves all modes: 16x16x4 fp32
+// MFMA, 4 waves x (64x64) per 128x128 tile.
 // A workgroup's (expert, row tile) comes from the expert offsets on the device,
 // so the host never reads the routing.  Each output element is produced by
 // exactly one workgroup with a fixed k order: results are reproducible.
@@ -48,77 +47,13 @@ struct GemmArgs {
   int32_t E, d, f;
 };
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <typename TA> struct Core;
 
-// ------------------------------------------------------------------ bf16 MFMA core
-template <> struct Core<bf16_t> {
-  static constexpr int BK = 64;
-  static constexpr int LD = BK + 8;     // LDS row stride in elements (144 bytes)
-  typedef bf16_t T;
-  f32x4 acc[4][4];
-
-  __device__ void zero() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __device__ void compute(const T* As, const T* Bs) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r = lane & 15, kq = (lane >> 4) * 8;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 16 + r) * LD + kk + kq);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 16 + r) * LD + kk + kq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-  // visit every accumulator as (tile row, tile col, value); for the SwiGLU
-  // pairing, columns c and c + 32 of the same 64-column wave slice pair up.
-  template <typename F>
-  __device__ void for_each(F&& fn) const {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          fn(wm * 64 + i * 16 + (lane >> 4) * 4 + q, wn * 64 + j * 16 + (lane & 15), acc[i][j][q]);
-  }
-  // pairs (a, b) whose B-tile rows are r and r + 32 inside one 64-row block
-  template <typename F>
-  __device__ void for_each_pair(F&& fn) const {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          fn(wm * 64 + i * 16 + (lane >> 4) * 4 + q, wn * 64 + j * 16 + (lane & 15),
-             acc[i][j][q], acc[i][j + 2][q]);
-  }
-};
-
 // ------------------------------------------------------------------ fp32 MFMA core
-// v_mfma_f32_16x16x4_f32 on the same 4-wave x (64x64) tiling as the bf16
-// core.  Within a BK = 32 tile, lane (g, r) of a 16-row block takes k = 8 g
+// v_mfma_f32_16x16x4_f32, 4 waves x (64x64) per 128x128 tile; accumulator
+// lane (g, r) of a 16x16 block holds rows 4 g + q, column r.  Within a BK = 32 tile, lane (g, r) of a 16-row block takes k = 8 g
 // ... 8 g + 7 of its row (two 16-byte LDS reads) and feeds k = 8 g + s at
 // step s; A and B use the same assignment, so each of the 8 steps sums k
 // = s, 8 + s, 16 + s, 24 + s and the 8 steps cover the tile.

@@ -61,13 +61,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 template <bool BIG> struct Cfg;
 template <> struct Cfg<false> {   // 128 x 128, 4 wavefronts of 64 x 64
   static constexpr int THREADS = 256, BM = 128, BN = 128, WAVES_N = 2, FM = 2, FN = 2;
-  static constexpr int kOutLd = BN + 8;
-  static constexpr int kLds = 2 * (BM + BN) * 64;
 };
 template <> struct Cfg<true> {    // 256 x 256, 8 wavefronts of 128 x 64
-  static constexpr int THREADS = 512, BM = 256, BN = 256, WAVES_N = 4, FM = 4, FN = 2;
-  static constexpr int kOutLd = BN + 8;
-  static constexpr int kLds = 256 * (BN + 8);   // >= 2 x (A + B) = 4 x 256 x 64
+  static constexpr int BM = 256, BN = 256, WAVES_N = 4, FM = 4, FN = 2;
 };
 
 struct Args {
@@ -105,50 +101,22 @@ struct Args {
 //    so the 16 lanes hit 16 distinct 16-byte bank groups;
 //  * k-contiguous stores (16 lanes = two whole rows): distinct by construction;
 //  * transposed 8-byte stores (32 lanes per clock = rows 8 j + 2 c + parity of j
-//    for 4 consecutive j, 4 chunks x 2 halves each, see mstore): rows 16
+//    for 4 consecutive j, 4 chunks x 2 halves each, see mstore_raw): rows 16
 //    apart get S values 4 apart, so their chunk sets are disjoint.
 __device__ __forceinline__ int swz(int r, int chunk) {
   return r * BK + ((chunk ^ (((r >> 1) ^ ((r >> 4) << 2)) & 7)) << 3);
 }
 
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
 // ------------------------------------------------------------------ staging
-// Loads never branch: an out-of-range row or column is read from a clamped,
-// valid address and zeroed when the registers are written to LDS, so all of a
-// step's global loads are in flight together (a guarded load would end in a
-// wait for the loads issued before it).
+// Loads never branch: an out-of-range row or column reads zeros through the
+// buffer resource (below), so all of a step's global loads are in flight
+// together (a guarded load would end in a wait for the loads issued before it).
 
 // k-contiguous operand: ROWS rows x 64 k = ROWS x 8 chunks, ROWS x 8 / NT per thread.
 template <int ROWS, int NT>
 struct KPart {
   uint4 v[ROWS * 8 / NT];
 };
-
-template <int ROWS, int NT, typename RowPtr>
-__device__ __forceinline__ void kload(KPart<ROWS, NT>& p, RowPtr row_ptr, int valid, int k0) {
-#pragma unroll
-  for (int i = 0; i < ROWS * 8 / NT; ++i) {
-    const int v = threadIdx.x + NT * i;
-    const int r = min(v >> 3, valid - 1), c = v & 7;
-    p.v[i] = *reinterpret_cast<const uint4*>(row_ptr(r) + k0 + c * 8);
-  }
-}
-
-__device__ __forceinline__ uint4 mask4(const uint4& v, bool keep) {
-  const uint32_t m = keep ? 0xFFFFFFFFu : 0u;
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
-
-template <int ROWS, int NT>
-__device__ __forceinline__ void kstore(const KPart<ROWS, NT>& p, bf16_t* lds, int valid) {
-#pragma unroll
-  for (int i = 0; i < ROWS * 8 / NT; ++i) {
-    const int v = threadIdx.x + NT * i;
-    const int r = v >> 3, c = v & 7;
-    *reinterpret_cast<uint4*>(lds + swz(r, c)) = mask4(p.v[i], r < valid);
-  }
-}
 
 // m/n-contiguous operand: element (k, j) at base[k * ld + j]; the 64 k x COLS j
 // tile is cut into 16 x (COLS / 8) blocks of 4 k x 8 j, COLS x 2 / NT per
@@ -166,56 +134,6 @@ __device__ __forceinline__ void mblock(int i, int* jb, int* kq) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   *kq = (wave & 1) * 8 + (lane & 7);
   *jb = i * (NT / 16) + (wave >> 1) * 8 + (lane >> 3);
-}
-
-// kvalid >= 1 and jvalid >= 8 (a multiple of 8) for every tile that runs
-template <int COLS, int NT>
-__device__ __forceinline__ void mload(MPart<COLS, NT>& p, const bf16_t* base, int64_t ld,
-                                      int kvalid, int jvalid) {
-#pragma unroll
-  for (int i = 0; i < COLS * 2 / NT; ++i) {
-    int jb, kq;
-    mblock<NT>(i, &jb, &kq);
-    const int j = min(jb * 8, jvalid - 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int k = min(kq * 4 + r, kvalid - 1);
-      p.v[i][r] = *reinterpret_cast<const uint4*>(base + k * ld + j);
-    }
-  }
-}
-
-// transpose each 4 x 8 block in registers: LDS row j receives its 4 k values
-// as one 8-byte piece (half of the swizzled 16-byte chunk kq / 2)
-template <int COLS, int NT>
-__device__ __forceinline__ void mstore(const MPart<COLS, NT>& p, bf16_t* lds, int kvalid,
-                                       int jvalid) {
-#pragma unroll
-  for (int i = 0; i < COLS * 2 / NT; ++i) {
-    int jb, kq;
-    mblock<NT>(i, &jb, &kq);
-    const bool jok = jb * 8 < jvalid;
-    uint4 in4[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) in4[r] = mask4(p.v[i][r], jok && (kq * 4 + r < kvalid));
-    const uint32_t in[4][4] = {{in4[0].x, in4[0].y, in4[0].z, in4[0].w},
-                               {in4[1].x, in4[1].y, in4[1].z, in4[1].w},
-                               {in4[2].x, in4[2].y, in4[2].z, in4[2].w},
-                               {in4[3].x, in4[3].y, in4[3].z, in4[3].w}};
-#pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
-      const uint32_t A0 = in[0][c2], A1 = in[1][c2], A2 = in[2][c2], A3 = in[3][c2];
-      const uint2 even = make_uint2((A0 & 0xFFFFu) | (A1 << 16), (A2 & 0xFFFFu) | (A3 << 16));
-      const uint2 odd =
-          make_uint2((A0 >> 16) | (A1 & 0xFFFF0000u), (A2 >> 16) | (A3 & 0xFFFF0000u));
-      // lanes of odd j blocks write the odd row first, so each store
-      // instruction covers both bank halves
-      const int p = jb & 1;
-      const int row = jb * 8 + 2 * c2;
-      *reinterpret_cast<uint2*>(lds + swz(row + p, kq >> 1) + 4 * (kq & 1)) = p ? odd : even;
-      *reinterpret_cast<uint2*>(lds + swz(row + 1 - p, kq >> 1) + 4 * (kq & 1)) = p ? even : odd;
-    }
-  }
 }
 
 // Buffer-resource loads (persistent kernel).  A resource covers
@@ -270,48 +188,9 @@ __device__ __forceinline__ void mstore_raw(const MPart<COLS, NT>& p, bf16_t* lds
 template <bool BIG>
 using AccT = f32x16[Cfg<BIG>::FM][Cfg<BIG>::FN];
 
-// K sub-steps [kk0, kk1) (16-wide pairs of chunks) of the wavefront's FM x FN
-// fragments.  Fragment (i, j) of wavefront (wm, wn) covers tile rows
-// wm 32 FM + 32 i + [0, 32) and columns j (BN / FN) + 32 wn + [0, 32), so the
-// FN fragments of a lane sit BN / FN columns apart (in UP: a and b of the same
-// f column).  The B fragment is the first MFMA source, so lane l ends up
-// owning C[m = l % 32][n = 8 (v / 4) + 4 (l / 32) + v % 4], v < 16, of each.
-template <bool BIG>
-__device__ __forceinline__ void mma_substeps(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
-                                             int kk0, int kk1) {
-  typedef Cfg<BIG> C;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int r = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int kk = kk0; kk < kk1; kk += 2) {
-    const int chunk = kk + g;
-    bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(As + swz(wm * 32 * C::FM + i * 32 + r, chunk));
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + swz(j * (C::BN / C::FN) + wn * 32 + r, chunk));
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-  }
-}
-
-// One K step (64 = 4 x k16) in two halves, so that LDS stores of the next step
-// can sit between them.
-template <bool BIG>
-__device__ __forceinline__ void mma_half(AccT<BIG>& acc, const bf16_t* As, const bf16_t* Bs,
-                                         int half) {
-  if (half == 0)
-    mma_substeps<BIG>(acc, As, Bs, 0, 4);
-  else
-    mma_substeps<BIG>(acc, As, Bs, 4, 8);
-}
-
+// Fragment (i, j) of wavefront (wm, wn) covers tile rows wm 32 FM + 32 i +
+// [0, 32) and columns j (BN / FN) + 32 wn + [0, 32), so the FN fragments of a
+// lane sit BN / FN columns apart (in UP: a and b of the same f column).
 // One K step with the fragments of sub-step ss + 1 read from LDS while the
 // MFMAs of sub-step ss run, and `mid` (the LDS store of the next step's
 // operands) placed before sub-step 2.  Scheduling groups then interleave, in
@@ -372,56 +251,6 @@ __device__ __forceinline__ void mma_step_pipe(AccT<BIG>& acc, const bf16_t* As, 
   }
 }
 
-// Software pipeline shared by the kernels: operand data for step j is loaded
-// into register set j & 1 two steps ahead, stored to LDS buffer j & 1 during
-// step j - 1 (between its two halves), and consumed at step j.  One barrier
-// per step.  `load(kt, set)` and `store(set, buf)` are the kernel's staging.
-template <bool BIG, bool TWO_SETS, typename Load, typename Store>
-__device__ __forceinline__ void run_pipeline(AccT<BIG>& acc, bf16_t* lds, int kt0, int nk,
-                                             Load&& load, Store&& store) {
-  constexpr int BM = Cfg<BIG>::BM, BN = Cfg<BIG>::BN;
-  bf16_t* As[2] = {lds, lds + (BM + BN) * BK};
-  bf16_t* Bs[2] = {lds + BM * BK, lds + (2 * BM + BN) * BK};
-  if (nk <= 0) return;
-  if constexpr (!TWO_SETS) {
-    // Without registers for a second staging set, loads for step j + 1 are
-    // issued before step j's MFMAs and stored after them.
-    load(kt0, 0);
-    store(0, As[0], Bs[0]);
-    __syncthreads();
-    for (int j = 0; j < nk; ++j) {
-      const int cur = j & 1;
-      if (j + 1 < nk) load(kt0 + j + 1, 0);
-      mma_substeps<BIG>(acc, cur ? As[1] : As[0], cur ? Bs[1] : Bs[0], 0, BK / 8);
-      if (j + 1 < nk) store(0, cur ? As[0] : As[1], cur ? Bs[0] : Bs[1]);
-      __syncthreads();
-    }
-    return;
-  }
-  // Loads are unconditional (a step past the end reloads the last one) so
-  // that the wait before each store covers only the older register set.
-  const int last = kt0 + nk - 1;
-  load(kt0, 0);
-  load(min(kt0 + 1, last), 1);
-  store(0, As[0], Bs[0]);
-  __syncthreads();
-  for (int j = 0; j < nk; j += 2) {
-    // step j (buffer 0); set 0 is free: load step j + 2 into it
-    load(min(kt0 + j + 2, last), 0);
-    mma_half<BIG>(acc, As[0], Bs[0], 0);
-    if (j + 1 < nk) store(1, As[1], Bs[1]);
-    mma_half<BIG>(acc, As[0], Bs[0], 1);
-    __syncthreads();
-    if (j + 1 >= nk) break;
-    // step j + 1 (buffer 1); set 1 is free: load step j + 3 into it
-    load(min(kt0 + j + 3, last), 1);
-    mma_half<BIG>(acc, As[1], Bs[1], 0);
-    if (j + 2 < nk) store(0, As[0], Bs[0]);
-    mma_half<BIG>(acc, As[1], Bs[1], 1);
-    __syncthreads();
-  }
-}
-
 template <bool BIG>
 __device__ __forceinline__ void zero_acc(AccT<BIG>& acc) {
 #pragma unroll
@@ -454,14 +283,6 @@ __device__ __forceinline__ void for_each_quad(const AccT<BIG>& acc, F&& fn) {
     }
 }
 
-// accumulators -> LDS tile [BM][kOutLd] of bf16 (rounded once)
-template <bool BIG>
-__device__ __forceinline__ void stage_out(const AccT<BIG>& acc, bf16_t* out) {
-  for_each_quad<BIG>(acc, [&](int m, int n, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2*>(out + m * Cfg<BIG>::kOutLd + n) = pack4(a, b, c, d);
-  });
-}
-
 // ------------------------------------------------------------------ tile lookup
 __device__ __forceinline__ int flat_tile() {
   const int per = gridDim.x / kXcd;            // the grid is a multiple of 8
@@ -481,34 +302,10 @@ __device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
 // each round of G items is one contiguous run, cut into one contiguous slice
 // per XCD: a row tile's column tiles share that XCD's L2.
 constexpr int kMaxItems = 64;
-#ifndef MOE_ROW_SETS
-#define MOE_ROW_SETS 3
-#endif
-constexpr int kRowSets = MOE_ROW_SETS;   // register staging sets of the persistent kernel
-#ifndef MOE_WGRAD_SETS
-#define MOE_WGRAD_SETS 2
-#endif
-constexpr int kWgradSets = MOE_WGRAD_SETS;
-#ifndef MOE_WGRAD_NOSPLIT_ITEMS
-#define MOE_WGRAD_NOSPLIT_ITEMS 160
-#endif
+constexpr int kRowSets = 3;     // register staging sets of the persistent row kernel
+constexpr int kWgradSets = 2;   // the same for the weight-gradient stream
+constexpr int kWgradNoSplitItems = 160;
 
-#ifdef MOE_TRACE
-// Timing build only: workgroup timelines of the persistent kernel (thread 0
-// writes the 100 MHz wall clock at its start, after its schedule, after each
-// step and, with the top bit set, after each epilogue).
-constexpr int kTraceSlots = 512;
-constexpr int kTraceBlocks = 1024;
-__device__ uint64_t moe_trace_data[kTraceBlocks * kTraceSlots];
-__device__ __forceinline__ void trace_mark(int& slot, uint64_t flag) {
-  if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks && slot < kTraceSlots)
-    moe_trace_data[blockIdx.x * kTraceSlots + slot] = wall_clock64() | flag;
-  ++slot;
-}
-#define MOE_TRACE_MARK(slot, flag) trace_mark(slot, flag)
-#else
-#define MOE_TRACE_MARK(slot, flag) ((void)0)
-#endif
 struct RowSched {
   int32_t pref[257];     // row tiles of the experts before e
   int32_t off[257];      // expert row offsets
@@ -616,9 +413,6 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
   };
   int ci = 0, ck = 0, cnk = lnk;   // compute cursor
   int j = 0;                       // step
-#ifdef MOE_TRACE
-  int tslot = 2;
-#endif
   auto step = [&](auto set) {
     constexpr int s = decltype(set)::value;
     const bool odd = j & 1;
@@ -634,7 +428,6 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
     mma_step_pipe<BIG, NVMEM, NDSW>(acc, ca, cb,
                                     [&] { store(IC<(s + 1) % NSETS>{}, na, nb); });
     __syncthreads();
-    MOE_TRACE_MARK(tslot, 0);
     advance();
     if (++ck == cnk) {
       epilogue(ci, ca);
@@ -642,7 +435,6 @@ __device__ __forceinline__ void run_stream(AccT<BIG>& acc, bf16_t* lds, int n_it
       ck = 0;
       ++ci;
       if (ci < n_items) cnk = nk_of(ci);
-      MOE_TRACE_MARK(tslot, 1ull << 63);
     }
     return ++j < S;
   };
@@ -673,14 +465,7 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
   constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
   __shared__ __attribute__((aligned(16))) bf16_t lds[2 * (BM + BN) * BK];
   __shared__ RowSched sched;
-#ifdef MOE_TRACE
-  int tslot0 = 0;
-  MOE_TRACE_MARK(tslot0, 0);
-#endif
   const int n_items = build_row_sched<BM, NT>(sched, g.offsets, g.E, g.n_tiles_n);
-#ifdef MOE_TRACE
-  MOE_TRACE_MARK(tslot0, 0);
-#endif
   if (n_items == 0) return;
   const int d = g.d, f = g.f;
   // UP covers BN/2 f columns of a and the same BN/2 of b per tile
@@ -1059,161 +844,6 @@ __device__ bool find_row_tile(const int32_t* offsets, int E, int tile, int* e_ou
                               int* mend_out) {
   __shared__ int s[3];
   return find_row_tile_at<BM>(s, offsets, E, tile, e_out, m0_out, mend_out);
-}
-
-// Row-split modes with the big tile, one tile per workgroup (long K: the
-// tile's own K loop hides the ramp, and the epilogue can stage the whole tile
-// through LDS).
-template <int MODE>
-__global__ __launch_bounds__(Cfg<true>::THREADS, 2) void tile_rows_kernel(Args g) {
-  constexpr bool BIG = true;
-  typedef Cfg<BIG> C;
-  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
-
-  const int flat = flat_tile();
-  const int row_tile = flat / g.n_tiles_n;
-  const int nt = flat - row_tile * g.n_tiles_n;
-  int e, m0, mend;
-  if (!find_row_tile<BM>(g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
-  const int rows = min(BM, mend - m0);
-  const int d = g.d, f = g.f;
-  // UP covers BN/2 f columns of a and the same BN/2 of b per tile
-  constexpr int kUpHalf = BN / 2;
-  const int n0 = nt * ((MODE == UP) ? kUpHalf : BN);
-  const int Ndim = (MODE == DOWN || MODE == DGRAD_UP) ? d : f;
-  const int nvalid = (MODE == UP) ? BN : min(BN, Ndim - n0);
-  const int K = (MODE == UP || MODE == DGRAD_DOWN) ? d : (MODE == DOWN ? f : 2 * f);
-  const int nk = K / BK;
-
-  const int64_t E_fd = static_cast<int64_t>(f) * d;
-  const int lda = (MODE == UP || MODE == DGRAD_DOWN) ? d : f;
-  auto a_row = [&](int half) {
-    const bf16_t* base = (MODE == DGRAD_UP && half) ? g.a1 : g.a0;
-    return base + static_cast<int64_t>(m0) * lda;
-  };
-
-  AccT<BIG> acc;
-  zero_acc<BIG>(acc);
-
-  KPart<BM, NT> pa[2];
-  KPart<BN, NT> pb[2];   // k-contiguous B (UP, DOWN)
-  MPart<BN, NT> pm[2];   // n-contiguous B (DGRAD_DOWN, DGRAD_UP)
-
-  auto load = [&](int kt, int set) {
-    int k0 = kt * BK;
-    int half = 0;
-    if (MODE == DGRAD_UP && k0 >= f) {
-      half = 1;
-      k0 -= f;
-    }
-    const bf16_t* ab = a_row(half);
-    auto a_ptr = [&](int r) { return ab + static_cast<int64_t>(r) * lda; };
-    if (set) kload<BM, NT>(pa[1], a_ptr, rows, k0); else kload<BM, NT>(pa[0], a_ptr, rows, k0);
-    if constexpr (MODE == UP) {
-      const bf16_t* w1 = g.b0 + e * E_fd;
-      const bf16_t* w3 = g.b1 + e * E_fd;
-      auto b_ptr = [&](int r) {
-        return (r < kUpHalf ? w1 + static_cast<int64_t>(n0 + r) * d
-                            : w3 + static_cast<int64_t>(n0 + r - kUpHalf) * d);
-      };
-      if (set) kload<BN, NT>(pb[1], b_ptr, BN, k0); else kload<BN, NT>(pb[0], b_ptr, BN, k0);
-    } else if constexpr (MODE == DOWN) {
-      const bf16_t* w2 = g.b0 + e * E_fd;
-      auto b_ptr = [&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; };
-      if (set) kload<BN, NT>(pb[1], b_ptr, nvalid, k0); else kload<BN, NT>(pb[0], b_ptr, nvalid, k0);
-    } else if constexpr (MODE == DGRAD_DOWN) {
-      // W2[e] is [d][f]: element (k, n) at k * f + n
-      const bf16_t* base = g.b0 + e * E_fd + static_cast<int64_t>(k0) * f + n0;
-      if (set) mload<BN, NT>(pm[1], base, f, BK, nvalid); else mload<BN, NT>(pm[0], base, f, BK, nvalid);
-    } else {
-      // W1/W3[e] are [f][d]: element (k, n) at k * d + n
-      const bf16_t* base = (half ? g.b1 : g.b0) + e * E_fd + static_cast<int64_t>(k0) * d + n0;
-      if (set) mload<BN, NT>(pm[1], base, d, BK, nvalid); else mload<BN, NT>(pm[0], base, d, BK, nvalid);
-    }
-  };
-  auto store_set = [&](const KPart<BM, NT>& a, const KPart<BN, NT>& b, const MPart<BN, NT>& m,
-                       bf16_t* As, bf16_t* Bs) {
-    kstore<BM, NT>(a, As, rows);
-    if constexpr (MODE == UP) {
-      kstore<BN, NT>(b, Bs, BN);
-    } else if constexpr (MODE == DOWN) {
-      kstore<BN, NT>(b, Bs, nvalid);
-    } else {
-      mstore<BN, NT>(m, Bs, BK, nvalid);
-    }
-  };
-  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
-    if (set) store_set(pa[1], pb[1], pm[1], As, Bs); else store_set(pa[0], pb[0], pm[0], As, Bs);
-  };
-  run_pipeline<BIG, !BIG && (MODE == UP || MODE == DOWN)>(acc, lds, 0, nk, load, store);
-
-  // epilogue: tile through LDS, then coalesced 16-byte chunks
-  constexpr int LO = C::kOutLd;
-  bf16_t* out = lds;
-  stage_out<BIG>(acc, out);
-  __syncthreads();
-  if constexpr (MODE == UP) {
-    // LDS columns [0, BN/2) hold a, [BN/2, BN) hold b for f columns n0 + c
-    constexpr int kChunks = kUpHalf / 8;
-    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
-      const int r = v / kChunks, c = (v % kChunks) * 8;
-      if (r >= rows) continue;
-      const uint4 av = *reinterpret_cast<const uint4*>(out + r * LO + c);
-      const uint4 bv = *reinterpret_cast<const uint4*>(out + r * LO + kUpHalf + c);
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-      uint32_t hw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a_lo = bf_lo(aw[q]), a_hi = bf_hi(aw[q]);
-        hw[q] = bf_pack(silu_f(a_lo) * bf_lo(bw[q]), silu_f(a_hi) * bf_hi(bw[q]));
-      }
-      const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c;
-      *reinterpret_cast<uint4*>(g.c0 + o) = av;
-      *reinterpret_cast<uint4*>(g.c1 + o) = bv;
-      *reinterpret_cast<uint4*>(g.c2 + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    }
-  } else if constexpr (MODE == DGRAD_DOWN) {
-    // dh (rounded) in LDS; da = dh b silu'(a), db = dh silu(a)
-    constexpr int kChunks = BN / 8;
-    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
-      const int r = v / kChunks, c = (v % kChunks) * 8;
-      if (r >= rows || c >= nvalid) continue;
-      const uint4 hv = *reinterpret_cast<const uint4*>(out + r * LO + c);
-      const int64_t o = static_cast<int64_t>(m0 + r) * f + n0 + c;
-      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
-      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
-      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-      uint32_t daw[4], dbw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float da2[2], db2[2];
-        const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
-        const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
-        const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float s = sigmoid_f(aa[u]);
-          da2[u] = hh[u] * bb[u] * (s * (1.0f + aa[u] * (1.0f - s)));
-          db2[u] = hh[u] * (aa[u] * s);
-        }
-        daw[q] = bf_pack(da2[0], da2[1]);
-        dbw[q] = bf_pack(db2[0], db2[1]);
-      }
-      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
-      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
-    }
-  } else {
-    // DOWN -> y_perm [R][d]; DGRAD_UP -> dx_perm [R][d]
-    constexpr int kChunks = BN / 8;
-    for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
-      const int r = v / kChunks, c = (v % kChunks) * 8;
-      if (r >= rows || c >= nvalid) continue;
-      *reinterpret_cast<uint4*>(g.c0 + static_cast<int64_t>(m0 + r) * d + n0 + c) =
-          *reinterpret_cast<const uint4*>(out + r * LO + c);
-    }
-  }
 }
 
 // ------------------------------------------------------------------ direct-to-LDS big tile
@@ -2220,98 +1850,6 @@ __global__ __launch_bounds__(dmas::NT, 8 / NST) void wgrad_dma_small_kernel(Args
   }
 }
 
-// Weight gradients: tile (e, m, n) of dW_z[e] = sum over the expert's rows p of
-// A[p][m] B[p][n]; z = 0: dW2 (A = dy, B = h), 1: dW1 (A = da, B = x),
-// 2: dW3 (A = db, B = x).  With splits > 1 the expert's K steps are cut into
-// `splits` contiguous runs; each workgroup writes its fp32 partial tile and
-// wgrad_reduce_kernel adds the runs in order (deterministic split-K).
-template <bool BIG>
-__global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void wgrad_kernel(
-    Args g, int32_t tiles_per_expert, int32_t splits, float* partial) {
-  typedef Cfg<BIG> C;
-  constexpr int BM = C::BM, BN = C::BN, NT = C::THREADS;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::kLds];
-
-  const int flat = flat_tile();
-  const int per_z = g.E * tiles_per_expert * splits;
-  const int z = flat / per_z;
-  if (z >= 3) return;
-  int rem = flat - z * per_z;
-  const int e = rem / (tiles_per_expert * splits);
-  rem -= e * tiles_per_expert * splits;
-  const int t = rem / splits;
-  const int sp = rem - t * splits;
-  const int d = g.d, f = g.f;
-  const int Mdim = (z == 0) ? d : f;
-  const int Ndim = (z == 0) ? f : d;
-  const int tiles_n = (Ndim + BN - 1) / BN;
-  const int m0 = (t / tiles_n) * BM;
-  const int n0 = (t % tiles_n) * BN;
-  if (m0 >= Mdim) return;
-  const bf16_t* Asrc = (z == 0) ? g.a0 : (z == 1 ? g.a1 : g.aux0);
-  const bf16_t* Bsrc = (z == 0) ? g.b0 : g.b1;
-  const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
-  const int nk_all = (p1 - p0 + BK - 1) / BK;
-  const int per_split = (nk_all + splits - 1) / splits;
-  const int kt0 = min(nk_all, sp * per_split);
-  const int kt1 = min(nk_all, kt0 + per_split);
-
-  AccT<BIG> acc;
-  zero_acc<BIG>(acc);
-
-  MPart<BM, NT> pa[2];
-  MPart<BN, NT> pb[2];
-  int kv[2] = {0, 0};
-  auto load = [&](int kt, int set) {
-    const int p = p0 + kt * BK;
-    const int kvalid = min(BK, p1 - p);
-    const bf16_t* a = Asrc + static_cast<int64_t>(p) * Mdim + m0;
-    const bf16_t* b = Bsrc + static_cast<int64_t>(p) * Ndim + n0;
-    if (set) {
-      kv[1] = kvalid;
-      mload<BM, NT>(pa[1], a, Mdim, kvalid, Mdim - m0);
-      mload<BN, NT>(pb[1], b, Ndim, kvalid, Ndim - n0);
-    } else {
-      kv[0] = kvalid;
-      mload<BM, NT>(pa[0], a, Mdim, kvalid, Mdim - m0);
-      mload<BN, NT>(pb[0], b, Ndim, kvalid, Ndim - n0);
-    }
-  };
-  auto store = [&](int set, bf16_t* As, bf16_t* Bs) {
-    if (set) {
-      mstore<BM, NT>(pa[1], As, kv[1], Mdim - m0);
-      mstore<BN, NT>(pb[1], Bs, kv[1], Ndim - n0);
-    } else {
-      mstore<BM, NT>(pa[0], As, kv[0], Mdim - m0);
-      mstore<BN, NT>(pb[0], Bs, kv[0], Ndim - n0);
-    }
-  };
-  run_pipeline<BIG, !BIG>(acc, lds, kt0, kt1 - kt0, load, store);
-  const int nvalid = min(BN, Ndim - n0), mvalid = min(BM, Mdim - m0);
-  if (splits > 1) {
-    // fp32 partial tile [BM][BN], n contiguous; runs of 4 consecutive n per lane
-    float* dst = partial + ((static_cast<int64_t>(z) * g.E + e) * tiles_per_expert + t) *
-                               static_cast<int64_t>(splits) * (BM * BN) +
-                 static_cast<int64_t>(sp) * (BM * BN);
-    for_each_quad<BIG>(acc, [&](int m, int n, float a, float b, float c, float dd) {
-      *reinterpret_cast<float4*>(dst + m * BN + n) = make_float4(a, b, c, dd);
-    });
-    return;
-  }
-  constexpr int LO = C::kOutLd;
-  bf16_t* out = lds;
-  stage_out<BIG>(acc, out);
-  __syncthreads();
-  bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
-  constexpr int kChunks = BN / 8;
-  for (int v = threadIdx.x; v < BM * kChunks; v += NT) {
-    const int r = v / kChunks, c = (v % kChunks) * 8;
-    if (r >= mvalid || c >= nvalid) continue;
-    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c) =
-        *reinterpret_cast<const uint4*>(out + r * LO + c);
-  }
-}
-
 // Weight gradients with the small tile, persistent (same pipeline as the row
 // modes).  Items are (z, expert, tile, split), dealt like the row items; item
 // K ranges follow the expert's row count.  A workgroup first decodes its
@@ -2342,10 +1880,6 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
   __shared__ WgSched sched;
   __shared__ int4 cand0[kMaxItems], cand1[kMaxItems];
 
-#ifdef MOE_TRACE
-  int tslot0 = 0;
-  MOE_TRACE_MARK(tslot0, 0);
-#endif
   const int d = g.d, f = g.f, E = g.E;
   const int G = gridDim.x, flat = flat_tile();
   const int per_z = E * tiles_per_expert * splits;
@@ -2407,9 +1941,6 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
     }
   }
   __syncthreads();
-#ifdef MOE_TRACE
-  MOE_TRACE_MARK(tslot0, 0);
-#endif
   const int n_items = sched.n;
   if (n_items == 0) return;
 
@@ -2419,11 +1950,10 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
   MPart<BM, NT> pa[NSETS];
   MPart<BN, NT> pb[NSETS];
   uint32_t voff_a[MA], voff_b[MBn];
-  int p_item = -1, p_z = 0, p_e = 0, p_m0 = 0, p_n0 = 0, p_pb = 0, p_pe = 0;
+  int p_item = -1, p_z = 0, p_m0 = 0, p_n0 = 0, p_pb = 0, p_pe = 0;
   auto prep = [&](int item) {
     const int4 a = sched.d0[item], b = sched.d1[item];
     p_z = __builtin_amdgcn_readfirstlane(a.x);
-    p_e = __builtin_amdgcn_readfirstlane(a.y);
     p_m0 = __builtin_amdgcn_readfirstlane(a.z);
     p_n0 = __builtin_amdgcn_readfirstlane(a.w);
     p_pb = __builtin_amdgcn_readfirstlane(b.x);
@@ -2592,10 +2122,7 @@ constexpr int kCUs = 256;
 // (and, for UP, f splits into 128-column halves); otherwise the small tile.
 bool use_big_rows(const moe_dims& dm, int n_big, int K) {
   const int64_t R = dm.T * dm.k;
-#ifndef MOE_BIG_ROWS_MIN_K
-#define MOE_BIG_ROWS_MIN_K 1024
-#endif
-  return K >= MOE_BIG_ROWS_MIN_K && (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
+  return K >= 1024 && (R / 256) * n_big >= 2 * kCUs && dm.f % 128 == 0;
 }
 bool use_big_wgrad(const moe_dims& dm) {
   return 3LL * dm.E * wgrad_tiles_per_expert<true>(dm) >= 2 * kCUs;
@@ -2643,7 +2170,6 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
   g.n_tiles_n = n_tiles_n;
   const int64_t row_tiles = (R + Cfg<true>::BM - 1) / Cfg<true>::BM + E;
   g.grid_pad = static_cast<int32_t>(pad8(row_tiles * n_tiles_n));
-#ifndef MOE_NO_DMA
   if constexpr (MODE == UP || MODE == DOWN) {
     if constexpr (MODE == UP) {
       if (fold) {
@@ -2663,12 +2189,6 @@ hipError_t launch_rows_big(const Args& base, int64_t R, int E, int n_tiles_n, hi
     }
     hipLaunchKernelGGL((dgrad_dma_kernel<MODE>), dim3(g.grid_pad), dim3(dma64::NT), 0, s, g);
   }
-  return hipGetLastError();
-#endif
-  if (fold) return hipErrorNotSupported;
-  if (g.x_rows) return hipErrorNotSupported;   // the register-staged big tile has no gather
-  hipLaunchKernelGGL((tile_rows_kernel<MODE>), dim3(g.grid_pad), dim3(Cfg<true>::THREADS), 0, s,
-                     g);
   return hipGetLastError();
 }
 
@@ -2762,21 +2282,14 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
     const int tpe = wgrad_tiles_per_expert<true>(dm);
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
-#ifndef MOE_NO_DMA
     if (g.x_rows)
       hipLaunchKernelGGL((wgrad_dma_kernel<true>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
     else
       hipLaunchKernelGGL((wgrad_dma_kernel<false>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
-#else
-    if (g.x_rows) return hipErrorNotSupported;   // the register-staged big tile has no gather
-    hipLaunchKernelGGL(wgrad_kernel<true>, dim3(grid), dim3(Cfg<true>::THREADS), 0, s, g, tpe, 1,
-                       partial);
-#endif
     return hipGetLastError();
   }
   const int tpe = wgrad_tiles_per_expert<false>(dm);
   const int splits = wgrad_splits_bf16(dm);
-#if !defined(MOE_NO_DMA) && !defined(MOE_NO_DMA_SMALL_WGRAD)
   if (splits == 1) {
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
@@ -2797,7 +2310,6 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
     }
     return hipGetLastError();
   }
-#endif
   const int64_t items = static_cast<int64_t>(3) * dm.E * tpe * splits;
   const int64_t grid = std::max(std::min(items, static_cast<int64_t>(2 * kCUs)),
                                 (items + kMaxItems - 1) / kMaxItems);
@@ -2819,12 +2331,7 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
 // The gate-folded path runs on the LDS-DMA kernels (small and big tiles) where
 // the weight gradients take a one-pass kernel (not the split-K stream).
 bool folded_bf16_ok(const moe_dims& dm) {
-#if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
-  (void)dm;
-  return false;
-#else
   return dm.act == MOE_BF16 && (use_big_wgrad(dm) || wgrad_splits_bf16(dm) == 1);
-#endif
 }
 
 // dgate parts per row: one per column tile of DGRAD_DOWN (256 wide on the big
@@ -2882,9 +2389,6 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
   if (dm.T * dm.k == 0)
     return launch_wgrad_bf16(dm, x, x_rows, offsets, hg, dy, da, db, dw1, dw3, dw2, nullptr, s);
   if (!folded_bf16_ok(dm) || !x_rows) return hipErrorNotSupported;
-#if defined(MOE_NO_DMA) || defined(MOE_NO_DMA_SMALL_WGRAD)
-  return hipErrorNotSupported;
-#else
   Args g = base_args(dm, offsets);
   g.x_rows = x_rows;
   g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
@@ -2913,7 +2417,6 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
     hipLaunchKernelGGL((wgrad_dma_small_kernel<4, true, true>), dim3(grid), dim3(dmas::NT), 0, s,
                        g, tpe);
   return hipGetLastError();
-#endif
 }
 
 // Split-K count for the (small-tile) weight gradients: none when the tiles
@@ -2923,8 +2426,8 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
 int wgrad_splits_bf16(const moe_dims& dm) {
   if (use_big_wgrad(dm)) return 1;
   const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm);
-  if (base >= MOE_WGRAD_NOSPLIT_ITEMS) return 1;
-  const int64_t want = 2 * MOE_WGRAD_NOSPLIT_ITEMS;
+  if (base >= kWgradNoSplitItems) return 1;
+  const int64_t want = 2 * kWgradNoSplitItems;
   int s = static_cast<int>((want + base - 1) / base);
   return std::max(1, std::min(s, 8));
 }
@@ -2938,13 +2441,3 @@ size_t wgrad_partial_bytes_bf16(const moe_dims& dm) {
 
 }  // namespace moe
 
-#ifdef MOE_TRACE
-extern "C" int moe_debug_trace_copy(void* host, size_t bytes) {
-  const size_t n = std::min(bytes, sizeof(moe::moe_trace_data));
-  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(moe::moe_trace_data), n));
-}
-extern "C" int moe_debug_trace_clear() {
-  static uint64_t zeros[moe::kTraceBlocks * moe::kTraceSlots];
-  return static_cast<int>(hipMemcpyToSymbol(HIP_SYMBOL(moe::moe_trace_data), zeros, sizeof(zeros)));
-}
-#endif
