@@ -91,7 +91,8 @@ const char* moe_last_error(void);
  * are invalid. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups);
 
-/* [host] Kernels that moe_expert_wgrad enqueues for these dims: 1 (one
+/* [host] Kernels that moe_expert_wgrad enqueues for these dims with
+ * wgrad_dtype = act: 1 (one
  * kernel writes dW1, dW3, dW2), 2 (the expert rows are split into parts whose
  * fp32 partial tiles a second kernel adds in a fixed order), or 0 when the
  * dims are invalid.  For profilers and benchmarks that attribute time to
@@ -230,16 +231,31 @@ moe_status moe_combine_bwd(const moe_dims* dims, const void* dy, const void* y_p
  * with silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + exp(-z)).
  * Inputs: x_perm [T*k,d], a_save, b_save, h_save [T*k,f], dy_perm [T*k,d]
  * (act); expert_offsets [E+1]; w1, w3 [E,f,d]; w2 [E,d,f] (act).
- * Outputs: dx_perm [T*k,d] act; dw1, dw3 [E,f,d] act; dw2 [E,d,f] act.
- * Each weight gradient is accumulated in fp32 over all rows of its expert in
- * a fixed order and rounded to act once.  Experts with no rows get zeros.
+ * a_save, b_save and h_save are either all given (as moe_grouped_swiglu_fwd
+ * wrote them) or all NULL: the call then recomputes them from x_perm, W1 and
+ * W3 with the forward kernel (activation recomputation), bit for bit what
+ * the forward pass stores, in workspace of
+ * moe_grouped_swiglu_bwd_workspace_bytes(dims, 1) bytes; a mix of NULL and
+ * non-NULL returns MOE_ERR_INVALID_ARGUMENT.
+ * Outputs: dx_perm [T*k,d] act; dw1, dw3 [E,f,d] and dw2 [E,d,f] of type
+ * wgrad_dtype: MOE_BF16 (bf16 layers only) or MOE_F32.  Each weight gradient
+ * is accumulated in fp32 over all rows of its expert in a fixed order and
+ * rounded once to bf16, or stored as the fp32 sum.  An fp32 layer takes
+ * MOE_F32 only (MOE_ERR_UNSUPPORTED otherwise).  Experts with no rows get
+ * zeros.
  */
 moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
                                   const int32_t* expert_offsets, const void* w1,
                                   const void* w3, const void* w2, const void* a_save,
                                   const void* b_save, const void* h_save, const void* dy_perm,
                                   void* dx_perm, void* dw1, void* dw3, void* dw2,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+                                  int32_t wgrad_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* [host] Workspace bytes moe_grouped_swiglu_bwd(_gather) needs with saved
+ * activations (recompute = 0: at most moe_workspace_bytes()) or recomputing
+ * them (recompute = 1: three more [T*k,f] act buffers).  0 for invalid dims. */
+size_t moe_grouped_swiglu_bwd_workspace_bytes(const moe_dims* dims, int32_t recompute);
 
 /*
  * Kernel-level phases of the two calls above, for callers that schedule the
@@ -255,6 +271,7 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
  *   moe_expert_dgrad_down: dh = dy_perm W2 (stored precision), da, db
  *   moe_expert_dgrad_up:   dx_perm = da W1 + db W3
  *   moe_expert_wgrad:      dW2 = dy_perm^T h, dW1 = da^T x_perm, dW3 = db^T x_perm
+ *                          (wgrad_dtype as in moe_grouped_swiglu_bwd)
  * moe_expert_wgrad's workspace: at least moe_workspace_bytes() bytes.
  */
 moe_status moe_expert_up(const moe_dims* dims, const void* x_perm,
@@ -273,8 +290,8 @@ moe_status moe_expert_dgrad_up(const moe_dims* dims, const void* da, const void*
 moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
                             const int32_t* expert_offsets, const void* h_save,
                             const void* dy_perm, const void* da, const void* db, void* dw1,
-                            void* dw3, void* dw2, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            void* dw3, void* dw2, int32_t wgrad_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Gathered expert input ("Expert Coupling in MoE Pretraining", Fig. 5: the
@@ -301,8 +318,8 @@ moe_status moe_grouped_swiglu_bwd_gather(const moe_dims* dims, const void* x,
                                          const void* w3, const void* w2, const void* a_save,
                                          const void* b_save, const void* h_save,
                                          const void* dy_perm, void* dx_perm, void* dw1,
-                                         void* dw3, void* dw2, void* workspace,
-                                         size_t workspace_bytes, void* stream);
+                                         void* dw3, void* dw2, int32_t wgrad_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 moe_status moe_expert_up_gather(const moe_dims* dims, const void* x, const int32_t* src_token,
                                 const int32_t* expert_offsets, const void* w1, const void* w3,
                                 void* a_save, void* b_save, void* h_save, void* stream);
@@ -310,7 +327,8 @@ moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
                                    const int32_t* src_token, const int32_t* expert_offsets,
                                    const void* h_save, const void* dy_perm, const void* da,
                                    const void* db, void* dw1, void* dw3, void* dw2,
-                                   void* workspace, size_t workspace_bytes, void* stream);
+                                   int32_t wgrad_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * Gate folded into the expert rows.  The combine is the gate-weighted sum

@@ -85,7 +85,7 @@ def test_gathered_calls_check_their_table_and_x():
                                            FAKE, FAKE, FAKE, FAKE, None, 0, None)
     assert st == INVALID and "'x'" in L.last_error()
     st = lib.moe_expert_wgrad_gather(ctypes.byref(dm), FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                     FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+                                     FAKE, FAKE, FAKE, FAKE, L.MOE_BF16, FAKE, 1 << 30, None)
     assert st == INVALID and "aligned" in L.last_error()
     # bf16 offsets into X are 32-bit: X of 2 GiB or more is refused
     big = dims(T=1 << 20, d=1024)
@@ -110,13 +110,55 @@ def test_small_workspace_is_rejected():
     dm = dims(T=4096, d=256, E=16, f=256, k=4)
     need = lib.moe_workspace_bytes(ctypes.byref(dm), 8)
     assert need > 0
-    st = lib.moe_grouped_swiglu_bwd(ctypes.byref(dm), *([FAKE] * 13), FAKE, 1024, None)
+    st = lib.moe_grouped_swiglu_bwd(ctypes.byref(dm), *([FAKE] * 13), L.MOE_BF16, FAKE, 1024,
+                                    None)
     assert st == WS and "needed" in L.last_error()
-    st = lib.moe_grouped_swiglu_bwd(ctypes.byref(dm), *([FAKE] * 13), None, need, None)
+    st = lib.moe_grouped_swiglu_bwd(ctypes.byref(dm), *([FAKE] * 13), L.MOE_BF16, None, need,
+                                    None)
     assert st == WS
     st = lib.moe_route(ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-3, FAKE, 8,
                        None, None, None, FAKE, 64, None)
     assert st == WS
+
+
+def _bwd(lib, dm, saved, wgrad_dtype, ws_bytes):
+    """moe_grouped_swiglu_bwd with fake pointers; saved = (a, b, h) pointers."""
+    return lib.moe_grouped_swiglu_bwd(ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, FAKE, *saved,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, wgrad_dtype, FAKE, ws_bytes,
+                                      None)
+
+
+def test_bwd_saved_activations_are_all_given_or_all_null():
+    lib = L.lib()
+    dm = dims(T=4096, d=256, E=16, f=256, k=4)
+    need = lib.moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dm), 1)
+    for saved in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None), (None, None, FAKE)):
+        assert _bwd(lib, dm, saved, L.MOE_BF16, need) == INVALID
+        assert "all NULL" in L.last_error()
+
+
+def test_bwd_recompute_needs_three_more_activation_buffers():
+    lib = L.lib()
+    dm = dims(T=4096, d=256, E=16, f=256, k=4)
+    saved_ws = lib.moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dm), 0)
+    recompute_ws = lib.moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dm), 1)
+    assert 0 < saved_ws <= lib.moe_workspace_bytes(ctypes.byref(dm), 1)
+    assert recompute_ws >= saved_ws + 3 * 4096 * 4 * 256 * 2
+    # the saved-activation size is too small once the call must recompute
+    assert _bwd(lib, dm, (None, None, None), L.MOE_BF16, saved_ws) == WS
+
+
+def test_bwd_wgrad_dtype_is_checked():
+    lib = L.lib()
+    dm = dims(T=4096, d=256, E=16, f=256, k=4)
+    need = lib.moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dm), 0)
+    assert _bwd(lib, dm, (FAKE, FAKE, FAKE), 7, need) == INVALID
+    assert "wgrad_dtype" in L.last_error()
+    dm32 = dims(T=4096, d=256, E=16, f=256, k=4, act=L.MOE_F32)
+    need32 = lib.moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dm32), 0)
+    assert _bwd(lib, dm32, (FAKE, FAKE, FAKE), L.MOE_BF16, need32) == UNSUP
+    st = lib.moe_expert_wgrad(ctypes.byref(dm32), *([FAKE] * 9), L.MOE_BF16, FAKE, need32, None)
+    assert st == UNSUP
 
 
 def test_workspace_covers_the_bwd_scratch():

@@ -35,6 +35,7 @@ EXPORTED = (
     "moe_route_bwd", "moe_coselect", "moe_dispatch_plan", "moe_placement_greedy",
     "moe_check_placement", "moe_expert_up", "moe_expert_down", "moe_expert_dgrad_down",
     "moe_expert_dgrad_up", "moe_expert_wgrad", "moe_expert_wgrad_launches",
+    "moe_grouped_swiglu_bwd_workspace_bytes",
     "moe_grouped_swiglu_fwd_gather", "moe_grouped_swiglu_bwd_gather", "moe_expert_up_gather",
     "moe_expert_wgrad_gather", "moe_dispatch_pack", "moe_dispatch_expand",
     "moe_expert_capacity", "moe_capacity", "moe_router_zloss", "moe_route_bwd_dense",
@@ -78,7 +79,8 @@ _SIGNATURES = {
     "moe_combine": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
     "moe_combine_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
     "moe_grouped_swiglu_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                      _P, _SZ, _P]),
+                                      _I32, _P, _SZ, _P]),
+    "moe_grouped_swiglu_bwd_workspace_bytes": (_SZ, [_DIMS, _I32]),
     "moe_route_bwd": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_coselect": (_I32, [_I64, _I32, _I32, _P, _P, _P]),
     "moe_dispatch_plan": (_I32, [_I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -88,16 +90,16 @@ _SIGNATURES = {
     "moe_expert_down": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
     "moe_expert_dgrad_down": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_dgrad_up": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
-    "moe_expert_wgrad": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_wgrad": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _SZ, _P]),
     "moe_expert_up_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_dispatch_pack": (_I32, [_DIMS, _I32, _P, _P, _P, _P, _P]),
     "moe_dispatch_expand": (_I32, [_DIMS, _P, _P, _P, _P, _P]),
-    "moe_expert_wgrad_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
-                                       _P]),
+    "moe_expert_wgrad_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                       _SZ, _P]),
     "moe_grouped_swiglu_fwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _SZ, _P]),
     "moe_grouped_swiglu_bwd_gather": (_I32, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                             _P, _P, _P, _P, _SZ, _P]),
+                                             _P, _P, _P, _I32, _P, _SZ, _P]),
     "moe_check_placement": (_I32, [_I32, _I32, _P]),
     "moe_expert_capacity": (_I32, [_I64, _I32, _I32, _I32, ctypes.c_double]),
     "moe_gate_folded_supported": (_I32, [_DIMS]),
@@ -266,16 +268,33 @@ def moe_combine_bwd(dims, dy, y_perm, pos, gate, dy_perm, dgate, stream=None):
     _check(st, "moe_combine_bwd")
 
 
+def _wgrad_dtype(dims, wgrad_dtype):
+    """(moe_dtype code, torch dtype) of the weight gradients; None: the act type."""
+    if wgrad_dtype is None:
+        wgrad_dtype = int(dims.act)
+    if wgrad_dtype in (torch.float32, MOE_F32):
+        return MOE_F32, torch.float32
+    if wgrad_dtype in (torch.bfloat16, MOE_BF16):
+        return MOE_BF16, torch.bfloat16
+    raise ValueError(f"wgrad_dtype must be MOE_F32 or MOE_BF16, got {wgrad_dtype!r}")
+
+
+def moe_grouped_swiglu_bwd_workspace_bytes(dims, recompute: bool) -> int:
+    return int(lib().moe_grouped_swiglu_bwd_workspace_bytes(ctypes.byref(dims), int(bool(recompute))))
+
+
 def moe_grouped_swiglu_bwd(dims, x_perm, expert_offsets, w1, w3, w2, a_save, b_save, h_save,
-                           dy_perm, dx_perm, dw1, dw3, dw2, workspace, stream=None):
+                           dy_perm, dx_perm, dw1, dw3, dw2, workspace, stream=None,
+                           wgrad_dtype=None):
     act = act_dtype(dims)
+    wcode, wdt = _wgrad_dtype(dims, wgrad_dtype)
     st = lib().moe_grouped_swiglu_bwd(
         ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
         _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
         _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
         _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(dy_perm, "dy_perm", act),
-        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act),
-        _ptr(dw2, "dw2", act), _ptr(workspace, "workspace"),
+        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", wdt), _ptr(dw3, "dw3", wdt),
+        _ptr(dw2, "dw2", wdt), wcode, _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_grouped_swiglu_bwd")
 
@@ -333,13 +352,14 @@ def moe_expert_dgrad_up(dims, da, db, expert_offsets, w1, w3, dx_perm, stream=No
 
 
 def moe_expert_wgrad(dims, x_perm, expert_offsets, h_save, dy_perm, da, db, dw1, dw3, dw2,
-                     workspace, stream=None):
+                     workspace, stream=None, wgrad_dtype=None):
     act = act_dtype(dims)
+    wcode, wdt = _wgrad_dtype(dims, wgrad_dtype)
     st = lib().moe_expert_wgrad(
         ctypes.byref(dims), _ptr(x_perm, "x_perm", act),
         _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(h_save, "h_save", act),
         _ptr(dy_perm, "dy_perm", act), _ptr(da, "da", act), _ptr(db, "db", act),
-        _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act), _ptr(dw2, "dw2", act),
+        _ptr(dw1, "dw1", wdt), _ptr(dw3, "dw3", wdt), _ptr(dw2, "dw2", wdt), wcode,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "moe_expert_wgrad")
@@ -400,15 +420,16 @@ def moe_grouped_swiglu_fwd_gather(dims, x, src_token, expert_offsets, w1, w3, w2
 
 def moe_grouped_swiglu_bwd_gather(dims, x, src_token, expert_offsets, w1, w3, w2, a_save,
                                   b_save, h_save, dy_perm, dx_perm, dw1, dw3, dw2, workspace,
-                                  stream=None):
+                                  stream=None, wgrad_dtype=None):
     act = act_dtype(dims)
+    wcode, wdt = _wgrad_dtype(dims, wgrad_dtype)
     st = lib().moe_grouped_swiglu_bwd_gather(
         ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
         _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(w1, "w1", act),
         _ptr(w3, "w3", act), _ptr(w2, "w2", act), _ptr(a_save, "a_save", act),
         _ptr(b_save, "b_save", act), _ptr(h_save, "h_save", act), _ptr(dy_perm, "dy_perm", act),
-        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act),
-        _ptr(dw2, "dw2", act), _ptr(workspace, "workspace"),
+        _ptr(dx_perm, "dx_perm", act), _ptr(dw1, "dw1", wdt), _ptr(dw3, "dw3", wdt),
+        _ptr(dw2, "dw2", wdt), wcode, _ptr(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_grouped_swiglu_bwd_gather")
 
@@ -426,13 +447,14 @@ def moe_expert_up_gather(dims, x, src_token, expert_offsets, w1, w3, a_save, b_s
 
 
 def moe_expert_wgrad_gather(dims, x, src_token, expert_offsets, h_save, dy_perm, da, db, dw1,
-                            dw3, dw2, workspace, stream=None):
+                            dw3, dw2, workspace, stream=None, wgrad_dtype=None):
     act = act_dtype(dims)
+    wcode, wdt = _wgrad_dtype(dims, wgrad_dtype)
     st = lib().moe_expert_wgrad_gather(
         ctypes.byref(dims), _ptr(x, "x", act), _ptr(src_token, "src_token", torch.int32),
         _ptr(expert_offsets, "expert_offsets", torch.int32), _ptr(h_save, "h_save", act),
         _ptr(dy_perm, "dy_perm", act), _ptr(da, "da", act), _ptr(db, "db", act),
-        _ptr(dw1, "dw1", act), _ptr(dw3, "dw3", act), _ptr(dw2, "dw2", act),
+        _ptr(dw1, "dw1", wdt), _ptr(dw3, "dw3", wdt), _ptr(dw2, "dw2", wdt), wcode,
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check(st, "moe_expert_wgrad_gather")

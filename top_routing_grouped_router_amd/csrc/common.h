@@ -111,8 +111,8 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
-                             void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
-                             float* ws_partial, hipStream_t s);
+                             void* dw1, void* dw3, void* dw2, bool wgrad_f32, void* ws_da,
+                             void* ws_db, float* ws_partial, hipStream_t s);
 
 // kernel-level phases of the expert GEMMs (dispatch on the activation type)
 hipError_t launch_expert_up(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
@@ -129,7 +129,7 @@ hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void
 hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
                                const int32_t* offsets, const void* h, const void* dy_perm,
                                const void* da, const void* db, void* dw1, void* dw3, void* dw2,
-                               float* partial, hipStream_t s);
+                               bool wgrad_f32, float* partial, hipStream_t s);
 
 // bf16 matrix-core implementations (gemm_bf16.hip)
 hipError_t launch_up_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
@@ -143,10 +143,11 @@ hipError_t launch_dgrad_down_bf16(const moe_dims& dm, const void* dy_perm, const
 hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* db,
                                 const int32_t* offsets, const void* w1, const void* w3,
                                 void* dx_perm, hipStream_t s);
+// out_f32: dW1, dW3, dW2 are fp32 (the fp32 accumulators stored unrounded)
 hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
                              const int32_t* offsets, const void* h, const void* dy_perm,
                              const void* da, const void* db, void* dw1, void* dw3, void* dw2,
-                             float* partial, hipStream_t s);
+                             bool out_f32, float* partial, hipStream_t s);
 // gate folded into the expert rows (gathered expert input): UP
 // stores g h; DGRAD_DOWN reads dy through the table, scales dh by g and writes
 // per-row dgate parts; WGRAD reads dy through the table for dW2
@@ -164,8 +165,9 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
                                     const int32_t* offsets, const void* hg, const void* dy,
                                     const void* da, const void* db, void* dw1, void* dw3,
                                     void* dw2, hipStream_t s);
-int wgrad_splits_bf16(const moe_dims& dm);           // split-K count of the weight gradients
-size_t wgrad_partial_bytes_bf16(const moe_dims& dm); // fp32 partial tiles it needs
+// split-K count of the weight gradients, and the fp32 partial tiles it needs
+int wgrad_splits_bf16(const moe_dims& dm, bool out_f32 = false);
+size_t wgrad_partial_bytes_bf16(const moe_dims& dm, bool out_f32 = false);
 
 // combine
 hipError_t launch_combine(const moe_dims& dm, const void* rows, const int32_t* pos,

@@ -472,10 +472,11 @@ hipError_t launch_expert_dgrad_up(const moe_dims& dm, const void* da, const void
 hipError_t launch_expert_wgrad(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
                                const int32_t* offsets, const void* h, const void* dy_perm,
                                const void* da, const void* db, void* dw1, void* dw3, void* dw2,
-                               float* partial, hipStream_t s) {
+                               bool wgrad_f32, float* partial, hipStream_t s) {
   if (dm.act == MOE_BF16)
     return launch_wgrad_bf16(dm, x_perm, x_rows, offsets, h, dy_perm, da, db, dw1, dw3, dw2,
-                             partial, s);
+                             wgrad_f32, partial, s);
+  if (!wgrad_f32) return hipErrorNotSupported;   // fp32 layers keep fp32 weight gradients
   // weight gradients (also for experts with no rows: they get zeros)
   GemmArgs g = base_args(dm, offsets);
   g.a0 = dy_perm;   // z = 0: A = dy (m over d), B = h (n over f)
@@ -503,14 +504,14 @@ hipError_t launch_swiglu_bwd(const moe_dims& dm, const void* x_perm, const int32
                              const int32_t* offsets,
                              const void* w1, const void* w3, const void* w2, const void* a,
                              const void* b, const void* h, const void* dy_perm, void* dx_perm,
-                             void* dw1, void* dw3, void* dw2, void* ws_da, void* ws_db,
-                             float* ws_partial, hipStream_t s) {
+                             void* dw1, void* dw3, void* dw2, bool wgrad_f32, void* ws_da,
+                             void* ws_db, float* ws_partial, hipStream_t s) {
   hipError_t e = launch_expert_dgrad_down(dm, dy_perm, offsets, w2, a, b, ws_da, ws_db, s);
   if (e != hipSuccess) return e;
   e = launch_expert_dgrad_up(dm, ws_da, ws_db, offsets, w1, w3, dx_perm, s);
   if (e != hipSuccess) return e;
   return launch_expert_wgrad(dm, x_perm, x_rows, offsets, h, dy_perm, ws_da, ws_db, dw1, dw3,
-                             dw2, ws_partial, s);
+                             dw2, wgrad_f32, ws_partial, s);
 }
 
 }  // namespace moe

@@ -90,6 +90,8 @@ struct Args {
   // gradients read dy through x_rows: the FOLD_A instances.)
   const float* gate_rows;
   float* dgate_part;
+  // weight gradients only: c0, c1, c2 hold fp32 (not bf16) elements
+  int32_t out_f32;
 };
 
 // LDS address (elements) of 16-byte chunk `chunk` of k-contiguous row r (128
@@ -1929,6 +1931,16 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
                    static_cast<int64_t>(c1.w >> 16) * (BM * BN);
       for (int v = threadIdx.x; v < BM * BN / 4; v += NT)
         reinterpret_cast<float4*>(dst)[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else if (g.out_f32) {
+      float* dst = reinterpret_cast<float*>((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) +
+                   static_cast<int64_t>(e) * d * f;
+      const int mv = min(BM, Mdim - m0), nv4 = min(BN, Ndim - n0) / 4;
+      for (int v = threadIdx.x; v < BM * (BN / 4); v += NT) {
+        const int r = v / (BN / 4), c = v % (BN / 4);
+        if (r < mv && c < nv4)
+          *reinterpret_cast<float4*>(dst + static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 4) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     } else {
       bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
       const int mv = min(BM, Mdim - m0), nv8 = min(BN, Ndim - n0) / 8;
@@ -2034,6 +2046,17 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
       });
       return;
     }
+    if (g.out_f32) {   // fp32 weight gradients: straight from the accumulators
+      float* dst = reinterpret_cast<float*>((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) +
+                   static_cast<int64_t>(e) * d * f;
+      const int mv = min(BM, Mdim - m0), nv = min(BN, Ndim - n0);
+      for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
+        if (m < mv && n < nv)
+          *reinterpret_cast<float4*>(dst + static_cast<int64_t>(m0 + m) * Ndim + n0 + n) =
+              make_float4(v0, v1, v2, v3);
+      });
+      return;
+    }
     int key;
     asm volatile("v_mov_b32 %0, %1" : "=v"(key) : "v"(static_cast<int>(threadIdx.x & 15)));
     for_each_quad<BIG>(acc, [&](int m, int n, float v0, float v1, float v2, float v3) {
@@ -2064,7 +2087,8 @@ __global__ __launch_bounds__(Cfg<false>::THREADS, 2) void wgrad_stream_kernel(
                                                          prep_if, load, store, epilogue);
 }
 
-// Adds the split-K partial tiles in split order and rounds once to bf16.
+// Adds the split-K partial tiles in split order and rounds once to bf16 (or
+// stores the fp32 sum when the weight gradients are fp32).
 // One thread per 8 consecutive outputs of a tile row (small tiles only).
 __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t tiles_per_expert,
                                                                 int32_t splits,
@@ -2099,9 +2123,15 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(Args g, int32_t 
     v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
     v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
   }
-  bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f +
-                static_cast<int64_t>(m0 + r) * Ndim + n0 + c;
-  *reinterpret_cast<uint4*>(dst) =
+  const int64_t at = static_cast<int64_t>(e) * d * f + static_cast<int64_t>(m0 + r) * Ndim + n0 + c;
+  bf16_t* const out = (z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2);
+  if (g.out_f32) {
+    float* dst = reinterpret_cast<float*>(out) + at;
+    reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    return;
+  }
+  *reinterpret_cast<uint4*>(out + at) =
       make_uint4(bf_pack(v[0], v[1]), bf_pack(v[2], v[3]), bf_pack(v[4], v[5]), bf_pack(v[6], v[7]));
 }
 
@@ -2266,8 +2296,9 @@ hipError_t launch_dgrad_up_bf16(const moe_dims& dm, const void* da, const void* 
 hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32_t* x_rows,
                              const int32_t* offsets, const void* h, const void* dy_perm,
                              const void* da, const void* db, void* dw1, void* dw3, void* dw2,
-                             float* partial, hipStream_t s) {
+                             bool out_f32, float* partial, hipStream_t s) {
   Args g = base_args(dm, offsets);
+  g.out_f32 = out_f32 ? 1 : 0;
   g.x_rows = x_rows;
   g.x_bytes = static_cast<int32_t>(dm.T * dm.d * 2);
   g.a0 = static_cast<const bf16_t*>(dy_perm);   // z = 0: A = dy (m over d), B = h (n over f)
@@ -2278,7 +2309,10 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   g.c0 = static_cast<bf16_t*>(dw2);
   g.c1 = static_cast<bf16_t*>(dw1);
   g.c2 = static_cast<bf16_t*>(dw3);
-  if (use_big_wgrad(dm)) {
+  // fp32 weight gradients go through the persistent stream kernel (its
+  // epilogue and the split-K reduction store fp32), never the one-pass
+  // direct-to-LDS kernels, whose epilogues stage bf16 tiles
+  if (!out_f32 && use_big_wgrad(dm)) {
     const int tpe = wgrad_tiles_per_expert<true>(dm);
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
@@ -2289,8 +2323,8 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
     return hipGetLastError();
   }
   const int tpe = wgrad_tiles_per_expert<false>(dm);
-  const int splits = wgrad_splits_bf16(dm);
-  if (splits == 1) {
+  const int splits = wgrad_splits_bf16(dm, out_f32);
+  if (splits == 1 && !out_f32) {
     const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
     g.grid_pad = static_cast<int32_t>(grid);
     const bool big = grid <= static_cast<unsigned>(kCUs);
@@ -2387,7 +2421,8 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
                                     void* dw2, hipStream_t s) {
   // no expert rows: every weight gradient is zero, as the unfolded call writes it
   if (dm.T * dm.k == 0)
-    return launch_wgrad_bf16(dm, x, x_rows, offsets, hg, dy, da, db, dw1, dw3, dw2, nullptr, s);
+    return launch_wgrad_bf16(dm, x, x_rows, offsets, hg, dy, da, db, dw1, dw3, dw2, false, nullptr,
+                             s);
   if (!folded_bf16_ok(dm) || !x_rows) return hipErrorNotSupported;
   Args g = base_args(dm, offsets);
   g.x_rows = x_rows;
@@ -2422,9 +2457,9 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
 // Split-K count for the (small-tile) weight gradients: none when the tiles
 // alone give about two thirds of a workgroup per CU (the persistent kernel
 // streams long K ranges well); otherwise enough splits for about 320 items,
-// at most 8.  Big tiles never split.
-int wgrad_splits_bf16(const moe_dims& dm) {
-  if (use_big_wgrad(dm)) return 1;
+// at most 8.  Big tiles (bf16 output only) never split.
+int wgrad_splits_bf16(const moe_dims& dm, bool out_f32) {
+  if (!out_f32 && use_big_wgrad(dm)) return 1;
   const int64_t base = static_cast<int64_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm);
   if (base >= kWgradNoSplitItems) return 1;
   const int64_t want = 2 * kWgradNoSplitItems;
@@ -2432,8 +2467,8 @@ int wgrad_splits_bf16(const moe_dims& dm) {
   return std::max(1, std::min(s, 8));
 }
 
-size_t wgrad_partial_bytes_bf16(const moe_dims& dm) {
-  const int s = wgrad_splits_bf16(dm);
+size_t wgrad_partial_bytes_bf16(const moe_dims& dm, bool out_f32) {
+  const int s = wgrad_splits_bf16(dm, out_f32);
   if (s <= 1) return 0;
   return static_cast<size_t>(3) * dm.E * wgrad_tiles_per_expert<false>(dm) * s * (128 * 128) *
          sizeof(float);

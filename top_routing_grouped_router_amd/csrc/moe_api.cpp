@@ -145,20 +145,35 @@ PermWs perm_ws(int64_t T, int32_t keys, void* ws) {
   return r;
 }
 
+// fp32 partial tiles of the split-K weight gradients
+size_t wgrad_ws_bytes(const moe_dims& dm, bool wgrad_f32) {
+  return dm.act == MOE_BF16 ? moe::wgrad_partial_bytes_bf16(dm, wgrad_f32) : 0;
+}
+
+// da, db and the weight-gradient partials; with `recompute` also a, b, h of
+// the forward pass, which the call then recomputes from the expert input
 struct BwdWs {
   void* da;
   void* db;
   float* partial;
+  void* a;
+  void* b;
+  void* h;
   size_t bytes;
 };
-BwdWs bwd_ws(const moe_dims& dm, void* ws) {
+BwdWs bwd_ws(const moe_dims& dm, void* ws, bool recompute = false, bool wgrad_f32 = false) {
   const int64_t R = dm.T * dm.k;
+  const size_t rf = R * dm.f * elem_size(dm);
   Carver c;
-  BwdWs r;
-  r.da = c.take<char>(ws, R * dm.f * elem_size(dm));
-  r.db = c.take<char>(ws, R * dm.f * elem_size(dm));
-  const size_t pbytes = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
-  r.partial = c.take<float>(ws, pbytes / sizeof(float));
+  BwdWs r{};
+  r.da = c.take<char>(ws, rf);
+  r.db = c.take<char>(ws, rf);
+  r.partial = c.take<float>(ws, wgrad_ws_bytes(dm, wgrad_f32) / sizeof(float));
+  if (recompute) {
+    r.a = c.take<char>(ws, rf);
+    r.b = c.take<char>(ws, rf);
+    r.h = c.take<char>(ws, rf);
+  }
   r.bytes = c.off;
   return r;
 }
@@ -233,7 +248,8 @@ size_t workspace_needed(const moe_dims& dm, int32_t n_groups) {
   const int32_t G = std::max(n_groups, 1);
   size_t need = route_ws(dm, 1, nullptr).bytes;  // tile 1 is the largest layout
   need = std::max(need, perm_ws(dm.T, dm.E, nullptr).bytes);
-  need = std::max(need, bwd_ws(dm, nullptr).bytes);
+  need = std::max(need, bwd_ws(dm, nullptr, false, false).bytes);
+  need = std::max(need, bwd_ws(dm, nullptr, false, true).bytes);
   need = std::max(need, route_bwd_ws(dm, nullptr).bytes);
   need = std::max(need, route_bwd_dense_ws(dm, nullptr).bytes);
   need = std::max(need, variant_ws(dm, G, nullptr).bytes);
@@ -270,6 +286,121 @@ moe_status check_placement_impl(int32_t E, int32_t G, const int32_t* placement, 
   return MOE_OK;
 }
 
+// Gathered expert input: bf16 offsets into X are 32-bit.
+moe_status check_gather(const moe_dims& dm, const void* x, const int32_t* src_token,
+                        const char* fn) {
+  if (!x && dm.T > 0) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is NULL", fn);
+  if (x && !aligned16(x)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is not 16-byte aligned", fn);
+  if (!src_token && dm.T > 0)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'src_token' is NULL", fn);
+  if (dm.act == MOE_BF16 && dm.T * dm.d * 2 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: X must be under 2 GiB to be gathered", fn);
+  return MOE_OK;
+}
+
+// wgrad_dtype: the type of dW1, dW3, dW2 (MOE_BF16 only for bf16 layers)
+moe_status check_wgrad_dtype(const moe_dims& dm, int32_t wgrad_dtype, bool* f32, const char* fn) {
+  if (wgrad_dtype != MOE_F32 && wgrad_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: wgrad_dtype=%d is neither MOE_F32 nor MOE_BF16", fn,
+                wgrad_dtype);
+  if (dm.act == MOE_F32 && wgrad_dtype != MOE_F32)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: an fp32 layer keeps fp32 weight gradients", fn);
+  *f32 = wgrad_dtype == MOE_F32;
+  return MOE_OK;
+}
+
+// moe_grouped_swiglu_bwd and its gathered form (x_rows != NULL: xin is X)
+moe_status swiglu_bwd_impl(const moe_dims* dims, const void* xin, const int32_t* x_rows,
+                           bool gather, const int32_t* expert_offsets, const void* w1,
+                           const void* w3, const void* w2, const void* a_save, const void* b_save,
+                           const void* h_save, const void* dy_perm, void* dx_perm, void* dw1,
+                           void* dw3, void* dw2, int32_t wgrad_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream, const char* fn) {
+  moe_status st = check_dims(dims, fn);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  const int64_t R = dm.T * dm.k, W = int64_t(dm.E) * dm.f * dm.d;
+  if (gather) {
+    st = check_gather(dm, xin, x_rows, fn);
+    if (st != MOE_OK) return st;
+  } else {
+    MOE_REQUIRE_PTR_FN(xin, R * dm.d, fn);
+  }
+  MOE_REQUIRE_PTR_FN(expert_offsets, dm.E + 1, fn);
+  MOE_REQUIRE_PTR_FN(w1, W, fn);
+  MOE_REQUIRE_PTR_FN(w3, W, fn);
+  MOE_REQUIRE_PTR_FN(w2, W, fn);
+  const int n_saved = (a_save != nullptr) + (b_save != nullptr) + (h_save != nullptr);
+  if (n_saved != 0 && n_saved != 3)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: a_save, b_save and h_save are all given, or all "
+                "NULL to recompute them", fn);
+  const bool recompute = n_saved == 0;
+  MOE_OPTIONAL_PTR_FN(a_save, fn);
+  MOE_OPTIONAL_PTR_FN(b_save, fn);
+  MOE_OPTIONAL_PTR_FN(h_save, fn);
+  MOE_REQUIRE_PTR_FN(dy_perm, R * dm.d, fn);
+  MOE_REQUIRE_PTR_FN(dx_perm, R * dm.d, fn);
+  MOE_REQUIRE_PTR_FN(dw1, W, fn);
+  MOE_REQUIRE_PTR_FN(dw3, W, fn);
+  MOE_REQUIRE_PTR_FN(dw2, W, fn);
+  bool f32 = false;
+  st = check_wgrad_dtype(dm, wgrad_dtype, &f32, fn);
+  if (st != MOE_OK) return st;
+  st = check_ws(workspace, workspace_bytes, bwd_ws(dm, nullptr, recompute, f32).bytes, fn);
+  if (st != MOE_OK) return st;
+  const BwdWs w = bwd_ws(dm, workspace, recompute, f32);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (recompute) {
+    st = hip_status(moe::launch_expert_up(dm, xin, x_rows, expert_offsets, w1, w3, w.a, w.b, w.h,
+                                          s),
+                    fn);
+    if (st != MOE_OK) return st;
+    a_save = w.a;
+    b_save = w.b;
+    h_save = w.h;
+  }
+  return hip_status(moe::launch_swiglu_bwd(dm, xin, x_rows, expert_offsets, w1, w3, w2, a_save,
+                                           b_save, h_save, dy_perm, dx_perm, dw1, dw3, dw2, f32,
+                                           w.da, w.db, w.partial, s),
+                    fn);
+}
+
+// moe_expert_wgrad and its gathered form
+moe_status expert_wgrad_impl(const moe_dims* dims, const void* xin, const int32_t* x_rows,
+                             bool gather, const int32_t* expert_offsets, const void* h_save,
+                             const void* dy_perm, const void* da, const void* db, void* dw1,
+                             void* dw3, void* dw2, int32_t wgrad_dtype, void* workspace,
+                             size_t workspace_bytes, void* stream, const char* fn) {
+  moe_status st = check_dims(dims, fn);
+  if (st != MOE_OK) return st;
+  const moe_dims& dm = *dims;
+  const int64_t R = dm.T * dm.k, W = int64_t(dm.E) * dm.f * dm.d;
+  if (gather) {
+    st = check_gather(dm, xin, x_rows, fn);
+    if (st != MOE_OK) return st;
+  } else {
+    MOE_REQUIRE_PTR_FN(xin, R * dm.d, fn);
+  }
+  MOE_REQUIRE_PTR_FN(expert_offsets, dm.E + 1, fn);
+  MOE_REQUIRE_PTR_FN(h_save, R * dm.f, fn);
+  MOE_REQUIRE_PTR_FN(dy_perm, R * dm.d, fn);
+  MOE_REQUIRE_PTR_FN(da, R * dm.f, fn);
+  MOE_REQUIRE_PTR_FN(db, R * dm.f, fn);
+  MOE_REQUIRE_PTR_FN(dw1, W, fn);
+  MOE_REQUIRE_PTR_FN(dw3, W, fn);
+  MOE_REQUIRE_PTR_FN(dw2, W, fn);
+  bool f32 = false;
+  st = check_wgrad_dtype(dm, wgrad_dtype, &f32, fn);
+  if (st != MOE_OK) return st;
+  st = check_ws(workspace, workspace_bytes, wgrad_ws_bytes(dm, f32), fn);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_expert_wgrad(dm, xin, x_rows, expert_offsets, h_save, dy_perm, da,
+                                             db, dw1, dw3, dw2, f32,
+                                             static_cast<float*>(workspace),
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,6 +422,12 @@ const char* moe_last_error(void) { return g_last_error; }
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t n_groups) {
   if (check_dims(dims, __func__) != MOE_OK) return 0;
   return workspace_needed(*dims, n_groups);
+}
+
+size_t moe_grouped_swiglu_bwd_workspace_bytes(const moe_dims* dims, int32_t recompute) {
+  if (check_dims(dims, __func__) != MOE_OK) return 0;
+  return std::max(bwd_ws(*dims, nullptr, recompute != 0, false).bytes,
+                  bwd_ws(*dims, nullptr, recompute != 0, true).bytes);
 }
 
 int32_t moe_expert_wgrad_launches(const moe_dims* dims) {
@@ -498,32 +635,11 @@ moe_status moe_grouped_swiglu_bwd(const moe_dims* dims, const void* x_perm,
                                   const int32_t* expert_offsets, const void* w1, const void* w3,
                                   const void* w2, const void* a_save, const void* b_save,
                                   const void* h_save, const void* dy_perm, void* dx_perm,
-                                  void* dw1, void* dw3, void* dw2, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  moe_status st = check_dims(dims, __func__);
-  if (st != MOE_OK) return st;
-  const moe_dims& dm = *dims;
-  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
-  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(dx_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
-  const BwdWs need = bwd_ws(dm, nullptr);
-  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
-  if (st != MOE_OK) return st;
-  const BwdWs w = bwd_ws(dm, workspace);
-  return hip_status(moe::launch_swiglu_bwd(dm, x_perm, nullptr, expert_offsets, w1, w3, w2, a_save, b_save,
-                                           h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da, w.db,
-                                           w.partial, static_cast<hipStream_t>(stream)),
-                    __func__);
+                                  void* dw1, void* dw3, void* dw2, int32_t wgrad_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return swiglu_bwd_impl(dims, x_perm, nullptr, false, expert_offsets, w1, w3, w2, a_save, b_save,
+                         h_save, dy_perm, dx_perm, dw1, dw3, dw2, wgrad_dtype, workspace,
+                         workspace_bytes, stream, __func__);
 }
 
 moe_status moe_expert_up(const moe_dims* dims, const void* x_perm,
@@ -598,27 +714,11 @@ moe_status moe_expert_dgrad_up(const moe_dims* dims, const void* da, const void*
 moe_status moe_expert_wgrad(const moe_dims* dims, const void* x_perm,
                             const int32_t* expert_offsets, const void* h_save,
                             const void* dy_perm, const void* da, const void* db, void* dw1,
-                            void* dw3, void* dw2, void* workspace, size_t workspace_bytes,
-                            void* stream) {
-  moe_status st = check_dims(dims, __func__);
-  if (st != MOE_OK) return st;
-  const moe_dims& dm = *dims;
-  MOE_REQUIRE_PTR(x_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
-  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
-  const size_t need = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
-  st = check_ws(workspace, workspace_bytes, need, __func__);
-  if (st != MOE_OK) return st;
-  return hip_status(moe::launch_expert_wgrad(dm, x_perm, nullptr, expert_offsets, h_save, dy_perm, da, db,
-                                             dw1, dw3, dw2, static_cast<float*>(workspace),
-                                             static_cast<hipStream_t>(stream)),
-                    __func__);
+                            void* dw3, void* dw2, int32_t wgrad_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return expert_wgrad_impl(dims, x_perm, nullptr, false, expert_offsets, h_save, dy_perm, da, db,
+                           dw1, dw3, dw2, wgrad_dtype, workspace, workspace_bytes, stream,
+                           __func__);
 }
 
 moe_status moe_route_bwd(const moe_dims* dims, const void* x, const float* w_router,
@@ -752,19 +852,7 @@ moe_status moe_placement_greedy(int32_t E, int32_t G, const int64_t* coselect,
 
 // ---------------------------------------------------------------- gathered expert input
 // The expert input row p is X[src_token[p]] (the table moe_permute writes), so
-// x_perm is never materialised.  bf16 offsets into X are 32-bit.
-namespace {
-moe_status check_gather(const moe_dims& dm, const void* x, const int32_t* src_token,
-                        const char* fn) {
-  if (!x && dm.T > 0) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is NULL", fn);
-  if (x && !aligned16(x)) return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'x' is not 16-byte aligned", fn);
-  if (!src_token && dm.T > 0)
-    return fail(MOE_ERR_INVALID_ARGUMENT, "%s: 'src_token' is NULL", fn);
-  if (dm.act == MOE_BF16 && dm.T * dm.d * 2 >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "%s: X must be under 2 GiB to be gathered", fn);
-  return MOE_OK;
-}
-}  // namespace
+// x_perm is never materialised (check_gather above holds the limits).
 
 moe_status moe_expert_up_gather(const moe_dims* dims, const void* x, const int32_t* src_token,
                                 const int32_t* expert_offsets, const void* w1, const void* w3,
@@ -789,28 +877,10 @@ moe_status moe_expert_wgrad_gather(const moe_dims* dims, const void* x,
                                    const int32_t* src_token, const int32_t* expert_offsets,
                                    const void* h_save, const void* dy_perm, const void* da,
                                    const void* db, void* dw1, void* dw3, void* dw2,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_dims(dims, __func__);
-  if (st != MOE_OK) return st;
-  const moe_dims& dm = *dims;
-  st = check_gather(dm, x, src_token, __func__);
-  if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
-  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(da, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(db, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
-  const size_t need = (dm.act == MOE_BF16) ? moe::wgrad_partial_bytes_bf16(dm) : 0;
-  st = check_ws(workspace, workspace_bytes, need, __func__);
-  if (st != MOE_OK) return st;
-  return hip_status(moe::launch_expert_wgrad(dm, x, src_token, expert_offsets, h_save, dy_perm,
-                                             da, db, dw1, dw3, dw2,
-                                             static_cast<float*>(workspace),
-                                             static_cast<hipStream_t>(stream)),
-                    __func__);
+                                   int32_t wgrad_dtype, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return expert_wgrad_impl(dims, x, src_token, true, expert_offsets, h_save, dy_perm, da, db, dw1,
+                           dw3, dw2, wgrad_dtype, workspace, workspace_bytes, stream, __func__);
 }
 
 moe_status moe_grouped_swiglu_fwd_gather(const moe_dims* dims, const void* x,
@@ -846,33 +916,11 @@ moe_status moe_grouped_swiglu_bwd_gather(const moe_dims* dims, const void* x,
                                          const void* w3, const void* w2, const void* a_save,
                                          const void* b_save, const void* h_save,
                                          const void* dy_perm, void* dx_perm, void* dw1,
-                                         void* dw3, void* dw2, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
-  moe_status st = check_dims(dims, __func__);
-  if (st != MOE_OK) return st;
-  const moe_dims& dm = *dims;
-  st = check_gather(dm, x, src_token, __func__);
-  if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(expert_offsets, dm.E + 1);
-  MOE_REQUIRE_PTR(w1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(w3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(w2, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(a_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(b_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(h_save, dm.T * dm.k * dm.f);
-  MOE_REQUIRE_PTR(dy_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(dx_perm, dm.T * dm.k * dm.d);
-  MOE_REQUIRE_PTR(dw1, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw3, int64_t(dm.E) * dm.f * dm.d);
-  MOE_REQUIRE_PTR(dw2, int64_t(dm.E) * dm.f * dm.d);
-  const BwdWs need = bwd_ws(dm, nullptr);
-  st = check_ws(workspace, workspace_bytes, need.bytes, __func__);
-  if (st != MOE_OK) return st;
-  const BwdWs w = bwd_ws(dm, workspace);
-  return hip_status(moe::launch_swiglu_bwd(dm, x, src_token, expert_offsets, w1, w3, w2, a_save,
-                                           b_save, h_save, dy_perm, dx_perm, dw1, dw3, dw2, w.da,
-                                           w.db, w.partial, static_cast<hipStream_t>(stream)),
-                    __func__);
+                                         void* dw3, void* dw2, int32_t wgrad_dtype,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return swiglu_bwd_impl(dims, x, src_token, true, expert_offsets, w1, w3, w2, a_save, b_save,
+                         h_save, dy_perm, dx_perm, dw1, dw3, dw2, wgrad_dtype, workspace,
+                         workspace_bytes, stream, __func__);
 }
 
 // ---------------------------------------------------------------- EP dispatch on one device

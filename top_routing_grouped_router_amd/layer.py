@@ -26,6 +26,12 @@ moe_route_bwd_folded, which also sums the dgate parts; with the dense router
 backward, or more than two parts per row, moe_dgate_from_parts sums them
 first), so neither moe_combine_bwd nor dy_perm exists.
 The results equal the unfolded layer's up to rounding.
+
+Backward options of the expert call: wgrad_dtype=torch.float32 on a bf16 layer
+keeps dW1, dW3, dW2 as the fp32 sums (not rounded to bf16), and
+recompute=True hands the backward no saved a, b, h, so that it recomputes
+them with the forward kernel (the forward still stores them here; the results
+are the same bits).  Neither combines with fold_gate.
 """
 from __future__ import annotations
 
@@ -38,8 +44,13 @@ class MoELayer:
     def __init__(self, T: int, d: int, E: int, f: int, k: int, act: torch.dtype,
                  n_groups: int = 1, near_tie_eps: float = 1e-3, device="cuda",
                  gather: bool = False, capacity_factor=None, aux_coef: float = 0.0,
-                 z_coef: float = 0.0, fold_gate: bool = False):
+                 z_coef: float = 0.0, fold_gate: bool = False, wgrad_dtype=None,
+                 recompute: bool = False):
         self.dims = L.make_dims(T, d, E, f, k, act)
+        self.wgrad_dtype = act if wgrad_dtype is None else wgrad_dtype
+        self.recompute = bool(recompute)
+        if fold_gate and (self.wgrad_dtype != act or self.recompute):
+            raise ValueError("fold_gate takes neither another wgrad_dtype nor recompute")
         if fold_gate and not (gather and L.moe_gate_folded_supported(self.dims)):
             raise ValueError("fold_gate needs gather=True and dims that "
                              "moe_gate_folded_supported accepts (bf16, one-pass weight gradients)")
@@ -90,9 +101,10 @@ class MoELayer:
         self.db = empty(R, f, **ea) if fold_gate else None
         self.dgate = empty(T, k, **e32)
         self.dx_perm = empty(R, d, **ea)
-        self.dw1 = empty(E, f, d, **ea)
-        self.dw3 = empty(E, f, d, **ea)
-        self.dw2 = empty(E, d, f, **ea)
+        ew = dict(dtype=self.wgrad_dtype, device=dev)
+        self.dw1 = empty(E, f, d, **ew)
+        self.dw3 = empty(E, f, d, **ew)
+        self.dw2 = empty(E, d, f, **ew)
         self.dx = empty(T, d, **ea)
         self.dwr = empty(E, d, **e32)
         self.kept_idx = empty(T, k, **i32) if self.capacity is not None else None
@@ -100,6 +112,10 @@ class MoELayer:
         self.group_z = empty(n_groups, **e32) if self.z_coef != 0.0 else None
         self.dlogits = empty(T, E, **e32) if self.dense_bwd else None
         self.workspace = L.alloc_workspace(self.dims, n_groups, dev)
+        if self.recompute:
+            need = L.moe_grouped_swiglu_bwd_workspace_bytes(self.dims, True)
+            if need > self.workspace.numel():
+                self.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------------ forward
     def route(self, x, wr):
@@ -177,15 +193,16 @@ class MoELayer:
     def _experts_bwd(self, dy, x, w1, w3, w2):
         L.moe_combine_bwd(self.dims, dy, self.y_perm, self.pos, self.topk_gate, self.dy_perm,
                           self.dgate)
+        saved = (None, None, None) if self.recompute else (self.a, self.b, self.h)
         if self.gather:
             L.moe_grouped_swiglu_bwd_gather(self.dims, x, self.src_token, self.expert_offsets,
-                                            w1, w3, w2, self.a, self.b, self.h, self.dy_perm,
-                                            self.dx_perm, self.dw1, self.dw3, self.dw2,
-                                            self.workspace)
+                                            w1, w3, w2, *saved, self.dy_perm, self.dx_perm,
+                                            self.dw1, self.dw3, self.dw2, self.workspace,
+                                            wgrad_dtype=self.wgrad_dtype)
         else:
             L.moe_grouped_swiglu_bwd(self.dims, self.x_perm, self.expert_offsets, w1, w3, w2,
-                                     self.a, self.b, self.h, self.dy_perm, self.dx_perm,
-                                     self.dw1, self.dw3, self.dw2, self.workspace)
+                                     *saved, self.dy_perm, self.dx_perm, self.dw1, self.dw3,
+                                     self.dw2, self.workspace, wgrad_dtype=self.wgrad_dtype)
 
     def _router_bwd(self, x, wr):
         if self.dense_bwd:
