@@ -1,8 +1,9 @@
 """GPU: expert-parallel dispatch emulated on one device.  The send buffer of
 the deduplicated plan (one row per (group, token)) against the oracle's, and
 its re-expansion into expert-contiguous rows against the permutation's x_perm,
-bit for bit, at a small ragged size and at the C5 size with both placements
-(contiguous and greedy co-selection) for 8 and 16 groups.
+bit for bit, at a small ragged size and at the C5 size (every row of the send
+buffer against the oracle's) with both placements (contiguous and greedy
+co-selection) for 8 and 16 groups.
 """
 import numpy as np
 import pytest
@@ -82,5 +83,5 @@ def test_ep_dispatch_c5():
         greedy = O.placement_greedy(W_fit, G)
         for kind, pl in (("contiguous", O.placement_contiguous(cfg.E, G)), ("correlated", greedy)):
             n = _check_case(cfg.T, cfg.d, cfg.E, cfg.k, cfg.act, inp["x"], idx, G, pl,
-                            oracle_send=None)
+                            oracle_send=True)
             print(f"[c5 G={G} {kind}] rows {n} of {cfg.T * cfg.k}", flush=True)
