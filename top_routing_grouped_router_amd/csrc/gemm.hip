@@ -124,51 +124,100 @@ template <> struct Core<float> {
   }
 };
 
-// ------------------------------------------------------------------ LDS staging
-// K-major source: tile row r (< 128) starts at row_ptr(r) + k0; rows >= valid are zero.
-template <typename T, int BK, int LD, typename RowPtr>
-__device__ __forceinline__ void stage_kmajor(T* lds, RowPtr row_ptr, int valid, int k0) {
-  constexpr int kVec = 16 / sizeof(T);
-  constexpr int kPerRow = BK / kVec;
-  for (int v = threadIdx.x; v < 128 * kPerRow; v += kThreads) {
-    const int r = v / kPerRow, c = (v % kPerRow) * kVec;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < valid) val = *reinterpret_cast<const uint4*>(row_ptr(r) + k0 + c);
-    *reinterpret_cast<uint4*>(lds + r * LD + c) = val;
-  }
-}
+// ------------------------------------------------------------------ staging
+// One operand stage (128 rows or columns x BK k) goes global -> registers ->
+// LDS in two calls, so that a step's loads can be issued before the previous
+// step's MFMAs and stored after them.  kVec elements per 16-byte vector,
+// kPer vectors per thread.
+template <typename T, int BK>
+struct Regs {
+  static constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  static constexpr int kPer = 128 * BK / kVec / kThreads;
+  uint4 v[kPer];
+};
 
-// MN-major source: element (k, mn) at base[k * ld + mn] for the tile's k rows
-// [0, BK) and mn columns [0, 128); k >= kvalid or mn >= mnvalid read as zero.
-// Written transposed so that LDS holds [mn][k].
+// K-major source: tile row r (< 128) starts at row_ptr(r); rows >= valid are
+// zero.  A thread's vectors sit in fixed rows, so their addresses (less k0)
+// are worked out once per tile (NULL for a zero row).
+template <typename T, int BK>
+struct KRows {
+  const T* p[Regs<T, BK>::kPer];
+};
+template <typename T, int BK, typename RowPtr>
+__device__ __forceinline__ KRows<T, BK> k_rows(RowPtr row_ptr, int valid) {
+  constexpr int kPerRow = BK / Regs<T, BK>::kVec;
+  KRows<T, BK> kr;
+#pragma unroll
+  for (int i = 0; i < Regs<T, BK>::kPer; ++i) {
+    const int v = threadIdx.x + i * kThreads;
+    const int r = v / kPerRow, c = (v % kPerRow) * Regs<T, BK>::kVec;
+    kr.p[i] = (r < valid) ? row_ptr(r) + c : nullptr;
+  }
+  return kr;
+}
+template <typename T, int BK>
+__device__ __forceinline__ void load_kmajor(Regs<T, BK>& rg, const KRows<T, BK>& kr, int k0) {
+#pragma unroll
+  for (int i = 0; i < Regs<T, BK>::kPer; ++i)
+    rg.v[i] = kr.p[i] ? *reinterpret_cast<const uint4*>(kr.p[i] + k0) : make_uint4(0, 0, 0, 0);
+}
 template <typename T, int BK, int LD>
-__device__ __forceinline__ void stage_mnmajor(T* lds, const T* base, int64_t ld, int kvalid,
-                                              int mnvalid) {
-  constexpr int kVec = 16 / sizeof(T);
-  constexpr int kPerRow = 128 / kVec;
-  for (int v = threadIdx.x; v < BK * kPerRow; v += kThreads) {
-    const int kr = v / kPerRow, c = (v % kPerRow) * kVec;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (kr < kvalid && c < mnvalid) val = *reinterpret_cast<const uint4*>(base + kr * ld + c);
-    const T* e = reinterpret_cast<const T*>(&val);
+__device__ __forceinline__ void store_kmajor(const Regs<T, BK>& rg, T* lds) {
+  constexpr int kPerRow = BK / Regs<T, BK>::kVec;
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) lds[(c + i) * LD + kr] = e[i];
+  for (int i = 0; i < Regs<T, BK>::kPer; ++i) {
+    const int v = threadIdx.x + i * kThreads;
+    const int r = v / kPerRow, c = (v % kPerRow) * Regs<T, BK>::kVec;
+    *reinterpret_cast<uint4*>(lds + r * LD + c) = rg.v[i];
   }
 }
 
-// As stage_mnmajor, with k row kr at row_ptr(kr) (mn offset applied by the caller)
-template <typename T, int BK, int LD, typename RowPtr>
-__device__ __forceinline__ void stage_mnmajor_rows(T* lds, RowPtr row_ptr, int kvalid,
-                                                   int mnvalid) {
-  constexpr int kVec = 16 / sizeof(T);
-  constexpr int kPerRow = 128 / kVec;
-  for (int v = threadIdx.x; v < BK * kPerRow; v += kThreads) {
-    const int kr = v / kPerRow, c = (v % kPerRow) * kVec;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (kr < kvalid && c < mnvalid) val = *reinterpret_cast<const uint4*>(row_ptr(kr) + c);
-    const T* e = reinterpret_cast<const T*>(&val);
+// MN-major source: element (k, mn) of k row kr at row_ptr(kr)[mn] for the
+// tile's k rows [0, BK) and mn columns [0, 128); k >= kvalid or mn >= mnvalid
+// read as zero.  Stored transposed, so that LDS holds [mn][k].
+template <typename T, int BK, typename RowPtr>
+__device__ __forceinline__ void load_mnmajor(Regs<T, BK>& rg, RowPtr row_ptr, int kvalid,
+                                             int mnvalid) {
+  constexpr int kPerRow = 128 / Regs<T, BK>::kVec;
 #pragma unroll
-    for (int i = 0; i < kVec; ++i) lds[(c + i) * LD + kr] = e[i];
+  for (int i = 0; i < Regs<T, BK>::kPer; ++i) {
+    const int v = threadIdx.x + i * kThreads;
+    const int kr = v / kPerRow, c = (v % kPerRow) * Regs<T, BK>::kVec;
+    rg.v[i] = (kr < kvalid && c < mnvalid) ? *reinterpret_cast<const uint4*>(row_ptr(kr) + c)
+                                           : make_uint4(0, 0, 0, 0);
+  }
+}
+template <typename T, int BK, int LD>
+__device__ __forceinline__ void store_mnmajor(const Regs<T, BK>& rg, T* lds) {
+  constexpr int kPerRow = 128 / Regs<T, BK>::kVec;
+#pragma unroll
+  for (int i = 0; i < Regs<T, BK>::kPer; ++i) {
+    const int v = threadIdx.x + i * kThreads;
+    const int kr = v / kPerRow, c = (v % kPerRow) * Regs<T, BK>::kVec;
+    const T* e = reinterpret_cast<const T*>(&rg.v[i]);
+#pragma unroll
+    for (int q = 0; q < Regs<T, BK>::kVec; ++q) lds[(c + q) * LD + kr] = e[q];
+  }
+}
+
+// The K loop: step j's operands are loaded into registers while step j - 1's
+// MFMAs run, then stored into LDS buffer j & 1; with two buffers one barrier
+// per step suffices (a buffer is rewritten only after every wavefront has
+// passed the barrier that follows its last use).  load(j) fills the
+// registers, store(As, Bs) writes them.
+template <typename C, typename T, int LD, typename Load, typename Store>
+__device__ __forceinline__ void run_steps(C& core, T* lds, int n, Load&& load, Store&& store) {
+  if (n <= 0) return;
+  load(0);
+  for (int j = 0; j < n; ++j) {
+    // buffer j & 1 by offset arithmetic on the LDS array (the compiler then
+    // keeps LDS addressing, not generic loads that would wait on the prefetch)
+    T* const A = lds + (j & 1) * ((BM + BN) * LD);
+    T* const B = A + BM * LD;
+    store(A, B);
+    __syncthreads();
+    if (j + 1 < n) load(j + 1);
+    core.compute(A, B);
   }
 }
 
@@ -235,12 +284,12 @@ template <typename TA, int MODE>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   typedef Core<TA> C;
   constexpr int BK = C::BK, LD = C::LD;
-  __shared__ __attribute__((aligned(16))) TA As[BM * LD];
-  __shared__ __attribute__((aligned(16))) TA Bs[BN * LD];
+  __shared__ __attribute__((aligned(16))) TA lds[2 * (BM + BN) * LD];
 
   const int d = g.d, f = g.f;
   C core;
   core.zero();
+  Regs<TA, BK> ra, rb;
 
   if constexpr (MODE == WGRAD) {
     // blockIdx.z: 0 -> dW2[e] [d, f] = dy^T h;  1 -> dW1[e] = da^T x;  2 -> dW3[e] = db^T x
@@ -255,21 +304,28 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     const TA* Asrc = static_cast<const TA*>(z == 0 ? g.a0 : (z == 1 ? g.a1 : g.aux0));
     const TA* Bsrc = static_cast<const TA*>(z == 0 ? g.b0 : g.b1);
     const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
-    for (int p = p0; p < p1; p += BK) {
-      const int kvalid = min(BK, p1 - p);
-      stage_mnmajor<TA, BK, LD>(As, Asrc + static_cast<int64_t>(p) * Mdim + m0, Mdim, kvalid,
-                                Mdim - m0);
-      if (z != 0 && g.x_rows)   // B = X rows gathered by the table
-        stage_mnmajor_rows<TA, BK, LD>(
-            Bs, [&](int kr) { return Bsrc + static_cast<int64_t>(g.x_rows[p + kr]) * Ndim + n0; },
-            kvalid, Ndim - n0);
-      else
-        stage_mnmajor<TA, BK, LD>(Bs, Bsrc + static_cast<int64_t>(p) * Ndim + n0, Ndim, kvalid,
-                                  Ndim - n0);
-      __syncthreads();
-      core.compute(As, Bs);
-      __syncthreads();
-    }
+    const bool gathered = z != 0 && g.x_rows;   // B = X rows gathered by the table
+    run_steps<C, TA, LD>(
+        core, lds, (p1 - p0 + BK - 1) / BK,
+        [&](int j) {
+          const int p = p0 + j * BK;
+          const int kvalid = min(BK, p1 - p);
+          load_mnmajor<TA, BK>(
+              ra, [&](int kr) { return Asrc + static_cast<int64_t>(p + kr) * Mdim + m0; },
+              kvalid, Mdim - m0);
+          if (gathered)
+            load_mnmajor<TA, BK>(
+                rb, [&](int kr) { return Bsrc + static_cast<int64_t>(g.x_rows[p + kr]) * Ndim + n0; },
+                kvalid, Ndim - n0);
+          else
+            load_mnmajor<TA, BK>(
+                rb, [&](int kr) { return Bsrc + static_cast<int64_t>(p + kr) * Ndim + n0; },
+                kvalid, Ndim - n0);
+        },
+        [&](TA* As, TA* Bs) {
+          store_mnmajor<TA, BK, LD>(ra, As);
+          store_mnmajor<TA, BK, LD>(rb, Bs);
+        });
     TA* out = static_cast<TA*>(z == 0 ? g.c0 : (z == 1 ? g.c1 : g.c2)) +
               static_cast<int64_t>(e) * d * f;
     core.for_each([&](int r, int c, float v) {
@@ -281,27 +337,55 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     if (!find_row_tile(g.offsets, g.E, blockIdx.x, &e, &m0, &mend)) return;
     const int rows = min(BM, mend - m0);
     const int n0 = blockIdx.y * ((MODE == UP) ? 64 : BN);
+    auto store_kk = [&](TA* As, TA* Bs) {   // both operands k-major
+      store_kmajor<TA, BK, LD>(ra, As);
+      store_kmajor<TA, BK, LD>(rb, Bs);
+    };
+    auto store_km = [&](TA* As, TA* Bs) {   // A k-major, B mn-major
+      store_kmajor<TA, BK, LD>(ra, As);
+      store_mnmajor<TA, BK, LD>(rb, Bs);
+    };
 
     if constexpr (MODE == UP) {
       const TA* x = static_cast<const TA*>(g.a0);
       const TA* w1 = static_cast<const TA*>(g.b0) + static_cast<int64_t>(e) * f * d;
       const TA* w3 = static_cast<const TA*>(g.b1) + static_cast<int64_t>(e) * f * d;
-      // input row r of the tile: expert row m0 + r, or the X row the table gives
-      auto x_row = [&](int r) {
-        const int64_t q = g.x_rows ? g.x_rows[m0 + r] : m0 + r;
-        return x + q * d;
-      };
-      for (int k0 = 0; k0 < d; k0 += BK) {
-        stage_kmajor<TA, BK, LD>(As, x_row, rows, k0);
-        stage_kmajor<TA, BK, LD>(Bs, [&](int r) {
-          const int q = r >> 5;
-          const TA* w = (q & 1) ? w3 : w1;
-          return w + static_cast<int64_t>(n0 + 32 * (q >> 1) + (r & 31)) * d;
-        }, BN, k0);
-        __syncthreads();
-        core.compute(As, Bs);
-        __syncthreads();
+      // input row r of the tile: expert row m0 + r, or the X row the table
+      // gives (the thread's table entries are loaded together, clamped to a
+      // valid row, before any is used)
+      int64_t xq[Regs<TA, BK>::kPer];
+      constexpr int kPerRowK = BK / Regs<TA, BK>::kVec;
+      if (g.x_rows) {
+#pragma unroll
+        for (int i = 0; i < Regs<TA, BK>::kPer; ++i)
+          xq[i] = g.x_rows[m0 + min((static_cast<int>(threadIdx.x) + i * kThreads) / kPerRowK,
+                                     rows - 1)];
+      } else {
+#pragma unroll
+        for (int i = 0; i < Regs<TA, BK>::kPer; ++i)
+          xq[i] = m0 + (threadIdx.x + i * kThreads) / kPerRowK;
       }
+      KRows<TA, BK> xa;
+#pragma unroll
+      for (int i = 0; i < Regs<TA, BK>::kPer; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        xa.p[i] = (v / kPerRowK < rows) ? x + xq[i] * d + (v % kPerRowK) * Regs<TA, BK>::kVec
+                                        : nullptr;
+      }
+      // B-tile row r: f row n0 + 32 (r / 64) + r % 32 of W1 (r % 64 < 32) or W3
+      auto w_row = [&](int r) {
+        const int q = r >> 5;
+        const TA* w = (q & 1) ? w3 : w1;
+        return w + static_cast<int64_t>(n0 + 32 * (q >> 1) + (r & 31)) * d;
+      };
+      const KRows<TA, BK> wb = k_rows<TA, BK>(w_row, BN);
+      run_steps<C, TA, LD>(
+          core, lds, d / BK,
+          [&](int j) {
+            load_kmajor<TA, BK>(ra, xa, j * BK);
+            load_kmajor<TA, BK>(rb, wb, j * BK);
+          },
+          store_kk);
       TA* ao = static_cast<TA*>(g.c0);
       TA* bo = static_cast<TA*>(g.c1);
       TA* ho = static_cast<TA*>(g.c2);
@@ -320,16 +404,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
       const TA* h = static_cast<const TA*>(g.a0) + static_cast<int64_t>(m0) * f;
       const TA* w2 = static_cast<const TA*>(g.b0) + static_cast<int64_t>(e) * d * f;
       const int nvalid = min(BN, d - n0);
-      for (int k0 = 0; k0 < f; k0 += BK) {
-        stage_kmajor<TA, BK, LD>(As, [&](int r) { return h + static_cast<int64_t>(r) * f; },
-                                 rows, k0);
-        stage_kmajor<TA, BK, LD>(Bs, [&](int r) {
-          return w2 + static_cast<int64_t>(n0 + min(r, nvalid - 1)) * f;
-        }, nvalid, k0);
-        __syncthreads();
-        core.compute(As, Bs);
-        __syncthreads();
-      }
+      const KRows<TA, BK> ha =
+          k_rows<TA, BK>([&](int r) { return h + static_cast<int64_t>(r) * f; }, rows);
+      const KRows<TA, BK> wb =
+          k_rows<TA, BK>([&](int r) { return w2 + static_cast<int64_t>(n0 + r) * f; }, nvalid);
+      run_steps<C, TA, LD>(
+          core, lds, f / BK,
+          [&](int j) {
+            load_kmajor<TA, BK>(ra, ha, j * BK);
+            load_kmajor<TA, BK>(rb, wb, j * BK);
+          },
+          store_kk);
       TA* yo = static_cast<TA*>(g.c0);
       core.for_each([&](int r, int c, float v) {
         if (r < rows && c < nvalid) store_act(yo + static_cast<int64_t>(m0 + r) * d + n0 + c, v);
@@ -339,14 +424,18 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
       const TA* dy = static_cast<const TA*>(g.a0) + static_cast<int64_t>(m0) * d;
       const TA* w2 = static_cast<const TA*>(g.b0) + static_cast<int64_t>(e) * d * f;
       const int nvalid = min(BN, f - n0);
-      for (int k0 = 0; k0 < d; k0 += BK) {
-        stage_kmajor<TA, BK, LD>(As, [&](int r) { return dy + static_cast<int64_t>(r) * d; },
-                                 rows, k0);
-        stage_mnmajor<TA, BK, LD>(Bs, w2 + static_cast<int64_t>(k0) * f + n0, f, BK, nvalid);
-        __syncthreads();
-        core.compute(As, Bs);
-        __syncthreads();
-      }
+      const KRows<TA, BK> dya =
+          k_rows<TA, BK>([&](int r) { return dy + static_cast<int64_t>(r) * d; }, rows);
+      run_steps<C, TA, LD>(
+          core, lds, d / BK,
+          [&](int j) {
+            const int k0 = j * BK;
+            load_kmajor<TA, BK>(ra, dya, k0);
+            load_mnmajor<TA, BK>(
+                rb, [&](int kr) { return w2 + static_cast<int64_t>(k0 + kr) * f + n0; }, BK,
+                nvalid);
+          },
+          store_km);
       const TA* sa = static_cast<const TA*>(g.aux0);
       const TA* sb = static_cast<const TA*>(g.aux1);
       TA* dao = static_cast<TA*>(g.c0);
@@ -368,18 +457,24 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
       const TA* w1 = static_cast<const TA*>(g.b0) + static_cast<int64_t>(e) * f * d;
       const TA* w3 = static_cast<const TA*>(g.b1) + static_cast<int64_t>(e) * f * d;
       const int nvalid = min(BN, d - n0);
-      for (int kk = 0; kk < 2 * f; kk += BK) {
-        const bool second = kk >= f;
-        const int k0 = second ? kk - f : kk;
-        const TA* asrc = second ? db : da;
-        const TA* bsrc = second ? w3 : w1;
-        stage_kmajor<TA, BK, LD>(As, [&](int r) { return asrc + static_cast<int64_t>(r) * f; },
-                                 rows, k0);
-        stage_mnmajor<TA, BK, LD>(Bs, bsrc + static_cast<int64_t>(k0) * d + n0, d, BK, nvalid);
-        __syncthreads();
-        core.compute(As, Bs);
-        __syncthreads();
-      }
+      // one K loop over 2f: da against W1, then db against W3
+      const KRows<TA, BK> daa =
+          k_rows<TA, BK>([&](int r) { return da + static_cast<int64_t>(r) * f; }, rows);
+      const KRows<TA, BK> dba =
+          k_rows<TA, BK>([&](int r) { return db + static_cast<int64_t>(r) * f; }, rows);
+      run_steps<C, TA, LD>(
+          core, lds, 2 * f / BK,
+          [&](int j) {
+            const int kk = j * BK;
+            const bool second = kk >= f;
+            const int k0 = second ? kk - f : kk;
+            const TA* bsrc = second ? w3 : w1;
+            load_kmajor<TA, BK>(ra, second ? dba : daa, k0);
+            load_mnmajor<TA, BK>(
+                rb, [&](int kr) { return bsrc + static_cast<int64_t>(k0 + kr) * d + n0; }, BK,
+                nvalid);
+          },
+          store_km);
       TA* dxo = static_cast<TA*>(g.c0);
       core.for_each([&](int r, int c, float v) {
         if (r < rows && c < nvalid) store_act(dxo + static_cast<int64_t>(m0 + r) * d + n0 + c, v);

@@ -98,11 +98,11 @@ struct Carver {
   }
 };
 
-// Tokens per router workgroup.  bf16 hidden states use the matrix-core router
-// (64-token tiles) when those tiles never straddle two balancing blocks.
+// Tokens per router workgroup: the matrix-core routers (64-token tiles) run
+// when those tiles never straddle two balancing blocks.
 int route_tile(int64_t T, int32_t G, int32_t act) {
-  if (act == MOE_BF16 && (G <= 1 || (T / G) % moe::kRouteMfmaTile == 0))
-    return moe::kRouteMfmaTile;
+  (void)act;
+  if (G <= 1 || (T / G) % moe::kRouteMfmaTile == 0) return moe::kRouteMfmaTile;
   if (G <= 1) return moe::kRouteTileMax;
   const int64_t per = T / G;
   int tile = moe::kRouteTileMax;

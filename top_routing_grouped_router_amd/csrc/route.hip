@@ -9,8 +9,10 @@
 // between the k-th and (k+1)-th scores; balancing statistics per machine).
 //
 // The main kernel gives each workgroup a tile of consecutive tokens (a tile
-// never straddles two balancing blocks): logits, then one 16-lane group (or
-// one wavefront) per token for top-k, gates, margin and the full softmax, and
+// never straddles two balancing blocks): logits (on the matrix cores, bf16 or
+// fp32, for 64-token tiles; on the vector ALUs for the smaller tiles that
+// balancing blocks of other sizes need), then one 16-lane group (or one
+// wavefront) per token for top-k, gates, margin and the full softmax, and
 // per-tile partial sums of the balancing statistics, which are folded per
 // block in a fixed order (no floating-point atomics).  Two launches per call:
 // for d > 256 (bf16, E <= 64) a one-thread kernel clears an arrival counter
@@ -850,6 +852,74 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
   route_tile_epilogue<NT, false>(a, acc, t0);
 }
 
+// fp32 hidden states on the fp32 matrix cores (v_mfma_f32_16x16x4_f32),
+// same 64-token tiles, C layout and epilogue as the bf16 routers.  For one
+// 16-wide k block lane (g, c) loads k = 4 g ... 4 g + 3 of its token row c and
+// of expert row 16 j + c as one float4 each, and MFMA step s takes element s
+// of both: A and B use the same k assignment, so the 4 steps cover the block.
+// Every wavefront reads X and Wr straight from global memory into registers,
+// KB blocks per batch (10 to 18 float4 per lane for both operands; blocks
+// past d read zeros), the next batch in flight while the current one runs.
+template <int NT>   // 16-expert tiles: E <= 16 NT
+__global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
+  constexpr int KB = NT == 1 ? 8 : NT == 2 ? 4 : NT <= 8 ? 2 : 1;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int E = a.E, d = a.d;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMTile;
+  const int64_t my_row = t0 + wave * 16 + c;
+  const bool row_ok = my_row < a.T;
+  const float* xrow = static_cast<const float*>(a.x) + (row_ok ? my_row : 0) * d + 4 * g;
+  const float* wrow[NT];
+  bool w_ok[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int e = 16 * j + c;
+    w_ok[j] = e < E;
+    wrow[j] = a.wr + static_cast<int64_t>(w_ok[j] ? e : 0) * d + 4 * g;
+  }
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 xc[KB], wc[KB][NT], xn[KB], wn[KB][NT];
+  auto load = [&](int bt, float4 (&xo)[KB], float4 (&wo)[KB][NT]) {
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const int k0 = (bt * KB + b) * 16;
+      const bool k_ok = k0 < d;
+      xo[b] = (row_ok && k_ok) ? *reinterpret_cast<const float4*>(xrow + k0) : zero4;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        wo[b][j] = (w_ok[j] && k_ok) ? *reinterpret_cast<const float4*>(wrow[j] + k0) : zero4;
+    }
+  };
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nb = (d + 16 * KB - 1) / (16 * KB);
+  load(0, xc, wc);
+  for (int bt = 0; bt < nb; ++bt) {
+    if (bt + 1 < nb) load(bt + 1, xn, wn);
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      const float xs[4] = {xc[b].x, xc[b].y, xc[b].z, xc[b].w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const float ws[4] = {wc[b][j].x, wc[b][j].y, wc[b][j].z, wc[b][j].w};
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[st], ws[st], acc[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+      xc[b] = xn[b];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) wc[b][j] = wn[b][j];
+    }
+  }
+  route_tile_epilogue<NT, false>(a, acc, t0);
+}
+
 // Second launch of the two-kernel paths (every path but the streaming one):
 // one workgroup (1024 threads) per balancing block r (grid G), all experts in
 // one pass: thread (slice, e) with slice < SL = 1024 / E_p (E_p: E rounded up
@@ -1233,6 +1303,20 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
       if (nt_p == 1) { MOE_RL_D(1) } else if (nt_p == 2) { MOE_RL_D(2) } else { MOE_RL_D(4) }
 #undef MOE_RL_D
 #undef MOE_RL
+    } else if (tile == kRouteMfmaTile && dm.act == MOE_F32) {
+      const int ntf = (dm.E + 15) / 16;
+#define MOE_RF(N)                                                                      \
+  case N:                                                                              \
+    hipLaunchKernelGGL(route_f32_kernel<N>, dim3(n_tiles), dim3(kThreads), 0, s, a);   \
+    break;
+      switch (ntf <= 1 ? 1 : ntf <= 2 ? 2 : ntf <= 4 ? 4 : ntf <= 8 ? 8 : 16) {
+        MOE_RF(1)
+        MOE_RF(2)
+        MOE_RF(4)
+        MOE_RF(8)
+        default: MOE_RF(16)
+      }
+#undef MOE_RF
     } else if (tile == kRouteMfmaTile) {
       const int ntm = (dm.E + 15) / 16;
 #define MOE_RM(N)                                                                        \
