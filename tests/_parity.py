@@ -155,3 +155,42 @@ def bound_only_keys(cfg):
         states, whose sums over many nearly parallel rows cancel (2-4e-2 by
         rounding alone there)."""
     return ("dlogits",) + (("dw1", "dw3", "dw2") if cfg.x_kind == "mixture" else ())
+
+
+def cancellation(o_f, o_b, keys):
+    """How much the exact sums of the bound-only outputs cancel: per row,
+    max_j sum|terms| / max(max_j |sum|, rms of the tensor), summarised as the
+    median and the largest over rows (the row-normwise error that a
+    relative perturbation u of every term can cause is u times this).
+    Returns {key: (median, max)} for the keys among dw1, dw3, dw2, dlogits."""
+    out = {}
+    off = o_f["offsets"]
+    E = len(off) - 1
+    pairs = {"dw1": ("da", o_f["x_perm"]), "dw3": ("db", o_f["x_perm"]),
+             "dw2": ("dy_perm", o_f["h"])}
+    for key in keys:
+        if key in pairs:
+            op, right = pairs[key]
+            ratios = []
+            ref = np.abs(o_b[key])
+            rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+            for e in range(E):
+                s = slice(int(off[e]), int(off[e + 1]))
+                if off[e + 1] == off[e]:
+                    continue
+                terms = np.abs(o_b[op][s]).T @ np.abs(right[s])
+                ratios.append(terms.max(axis=1) / np.maximum(ref[e].max(axis=1), rms))
+            r = np.concatenate(ratios) if ratios else np.zeros(1)
+        elif key == "dlogits":
+            # dl[t, S_j] = g_j (dg_j - sum_i g_i dg_i)
+            g, dg = o_f["gates"], o_b["dgate"]
+            inner = (g * np.abs(dg)).sum(axis=1, keepdims=True)
+            terms = (g * (np.abs(dg) + inner)).max(axis=1)
+            ref = np.abs(o_b["dlogits"])
+            rms = float(np.sqrt(np.mean(ref * ref))) or 1.0
+            r = terms / np.maximum(ref.max(axis=1), rms)
+        else:
+            continue
+        out[key] = (float(np.median(r)), float(r.max()))
+    return out
+

@@ -24,8 +24,8 @@ from synth import get_config, make_layer_inputs
 from top_routing_grouped_router_amd import MoELayer
 import top_routing_grouped_router_amd._lib as L
 
-from _parity import (bound_only_keys, check_plan, check_route, exact_reference, layer_floats,
-                     oracle_routing)
+from _parity import (bound_only_keys, cancellation, check_plan, check_route, exact_reference,
+                     layer_floats, oracle_routing)
 from _util import TOL, act_torch, check_floats, dev
 
 pytestmark = pytest.mark.gpu
@@ -67,5 +67,9 @@ def test_default_path_full_size(name):
     print(f"[{name}] oracle done", flush=True)
     check_plan(layer, o_f)
     got, ex, bd = layer_floats(layer, o_f, o_b, B)
+    if o_b is not None:
+        for key, (med, worst) in cancellation(o_f, o_b, bound_only_keys(cfg)).items():
+            print(f"[{name}] {key}: row sum|terms| / |sum|: median {med:.2f}, max {worst:.1f}",
+                  flush=True)
     del o_f, o_b, B
     check_floats(name, got, ex, bd, TOL[cfg.act], bound_only_keys(cfg))
