@@ -312,21 +312,37 @@ def workload_reports(steps):
     return rep
 
 
-def ep_dispatch(cfg, layer, x, steps):
+def ep_dispatch(cfg, layer, x, wr, steps):
     """Expert-parallel dispatch emulated on one GPU for each placement group
-    count of the workload (contiguous placement): the dedup plan, the pack of
-    one row per (group, token) and the receivers' expansion into x_perm, each
-    timed with HIP events over `steps` launches.  Bytes per pack: rows read +
-    rows written (+ row ids); per expand: T k rows read + written (+ ids)."""
+    count of the workload, under contiguous placement and under the greedy
+    correlated placement fitted on the co-selection of another batch: the
+    dedup plan, the pack of one row per (group, token) and the receivers'
+    expansion into x_perm, each timed with HIP events over `steps` launches.
+    Bytes per pack: rows read + rows written (+ row ids); per expand: T k rows
+    read + written (+ ids)."""
     import torch
     import top_routing_grouped_router_amd._lib as L
     T, k, E, d = cfg.T, cfg.k, cfg.E, cfg.d
     s = 2 if cfg.act == "bf16" else 4
     dm = layer.dims
+    from synth import make_layer_inputs
+    i32 = dict(dtype=torch.int32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    # route another batch with the same router to fit the correlated placement
+    x_fit = torch.from_numpy(make_layer_inputs(cfg, batch_seed=1, parts=("x",))["x"]).to(
+        "cuda", x.dtype)
+    idx_fit = torch.empty(T, k, **i32)
+    L.moe_route(dm, x_fit, wr, torch.empty(T, E, **f32), idx_fit, torch.empty(T, k, **f32),
+                torch.empty(T, **f32), 1e-3, torch.empty(1, **i32), 1, torch.empty(1, E, **i32),
+                torch.empty(1, E, **f32), torch.empty(1, **f32), layer.workspace)
+    W = torch.empty(E, E, **i32)
+    L.moe_coselect(T, k, E, idx_fit, W)
+    torch.cuda.synchronize()
+    W_fit = W.cpu().numpy().astype(np.int64)
     res = {}
-    for G in cfg.plan_groups:
-        pl = [e * G // E for e in range(E)]
-        i32 = dict(dtype=torch.int32, device="cuda")
+    for G, kind in [(G, kind) for G in cfg.plan_groups for kind in ("contiguous", "correlated")]:
+        pl = ([e * G // E for e in range(E)] if kind == "contiguous" else
+              L.moe_placement_greedy(E, G, W_fit))
         out = {"n_dest": torch.empty(T, **i32), "group_rows": torch.empty(G, **i32),
                "group_offsets": torch.empty(G + 1, **i32), "row_token": torch.empty(T * k, **i32),
                "assign_row": torch.empty(T, k, **i32), "stats": torch.empty(4, **i32)}
@@ -356,7 +372,7 @@ def ep_dispatch(cfg, layer, x, steps):
         rows = int(out["stats"][0].item())
         pack_b = rows * d * s * 2 + rows * 4
         exp_b = T * k * d * s * 2 + T * k * 8
-        res[f"G{G}_contiguous"] = {
+        res[f"G{G}_{kind}"] = {
             "rows": rows, "rows_removed": T * k - rows,
             "plan_us": round(times["plan"] * 1e6, 1),
             "pack_us": round(times["pack"] * 1e6, 1),
@@ -819,7 +835,7 @@ def main():
             "dropped": (int(layer.group_dropped.sum().item())
                         if layer.group_dropped is not None else 0)}
     if args.ep and cfg.plan_groups:
-        out["ep_dispatch"] = ep_dispatch(cfg, layer, x, args.steps)
+        out["ep_dispatch"] = ep_dispatch(cfg, layer, x, wr, args.steps)
     if args.fragility:
         out["fragility"] = fragility(cfg, layer, x, wr, args.steps)
     if args.shuffle and cfg.plan_groups:

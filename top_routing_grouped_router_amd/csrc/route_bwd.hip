@@ -18,11 +18,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per 16-byte chunk of a dX row (grid-stride):
+// dX rows:
 //   dl[t,j] = g_j (dg_j - sum_i g_i dg_i)          (the fp32 sum in slot order)
 //   dX[t]   = sum_j dx_perm[pos[t,j]] + sum_j dl[t,j] wr[idx[t,j]]
-// summed in fp32 in slot order and rounded once.  The thread holding chunk 0
-// of a row also scatters dl into permuted row order for the dWr kernel.  K is
+// summed in fp32 in slot order and rounded once.  Workgroup (column block,
+// token range): the block's bc columns of every router row (E x bc fp32) are
+// staged in LDS once, then each thread takes one 16-byte chunk of dX for
+// kThreads / (bc / kPer) tokens at a time, so the router rows come from LDS
+// rather than from L2 once per chunk and slot.  The threads holding chunk 0
+// of a row also scatter dl into permuted row order for the dWr kernel.  K is
 // the compile-time k (0: runtime k <= 16); every load of a token is issued
 // before any is used (indices clamped, invalid slots masked), so a row costs
 // one memory latency rather than one per slot.
@@ -32,16 +36,30 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gate,
     const float* __restrict__ dgate, const float* __restrict__ wr, uint4* __restrict__ dx,
     float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E,
-    const float* __restrict__ dgate_part, int32_t nparts, float* __restrict__ dgate_out) {
+    const float* __restrict__ dgate_part, int32_t nparts, float* __restrict__ dgate_out,
+    int32_t bc, int32_t tok_per_wg) {
+  extern __shared__ __attribute__((aligned(16))) float wl[];   // [E][bc]
   constexpr int kPer = Act<TA>::kPer16B;
   constexpr int KM = K > 0 ? K : 16;
   const int kk = K > 0 ? K : k;
-  const int64_t total = T * vpr;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total;
-       v += stride) {
-    const int64_t t = v / vpr;
-    const int32_t c = static_cast<int32_t>(v - t * vpr);
+  const int col0 = blockIdx.x * bc;
+  {
+    const int q4 = bc / 4;
+    for (int i = threadIdx.x; i < E * q4; i += kThreads) {
+      const int e = i / q4, q = i - e * q4;
+      *reinterpret_cast<float4*>(wl + e * bc + q * 4) =
+          *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * d + col0 + q * 4);
+    }
+  }
+  __syncthreads();
+  const int cpr = bc / kPer;                    // chunks of the block per row
+  const int tpp = kThreads / cpr;               // tokens per pass
+  const int cl = threadIdx.x % cpr;             // chunk within the block
+  const int32_t c = col0 / kPer + cl;           // chunk within the row
+  const int64_t t_end = min<int64_t>(T, static_cast<int64_t>(blockIdx.y + 1) * tok_per_wg);
+  for (int64_t t = static_cast<int64_t>(blockIdx.y) * tok_per_wg + threadIdx.x / cpr; t < t_end;
+       t += tpp) {
+    const int64_t v = t * vpr + c;
     float g[KM], dg[KM];
     int32_t p[KM], e[KM];
 #pragma unroll
@@ -53,15 +71,9 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
       e[j] = idx[q];
     }
     uint4 rows[KM];
-    float w[KM][kPer];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
+    for (int j = 0; j < KM; ++j)
       rows[j] = dxp ? dxp[static_cast<int64_t>(max(p[j], 0)) * vpr + c] : make_uint4(0u, 0u, 0u, 0u);
-      const float* wp = wr + static_cast<int64_t>(min(max(e[j], 0), E - 1)) * d +
-                        static_cast<int64_t>(c) * kPer;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) w[j][i] = wp[i];
-    }
     if constexpr (FOLD) {
       // gate folded onto the rows: dg is the sum of the row's column-tile parts
       // in tile order (0 for a dropped slot); the first kPartsU parts of every
@@ -116,12 +128,24 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j >= kk || e[j] < 0 || e[j] >= E) continue;
+      const float* wp = wl + e[j] * bc + cl * kPer;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(dl[j], w[j][i], acc[i]);
+      for (int i = 0; i < kPer; i += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wp + i);
+        acc[i] = fmaf(dl[j], w4.x, acc[i]);
+        acc[i + 1] = fmaf(dl[j], w4.y, acc[i + 1]);
+        acc[i + 2] = fmaf(dl[j], w4.z, acc[i + 2]);
+        acc[i + 3] = fmaf(dl[j], w4.w, acc[i + 3]);
+      }
     }
     dx[v] = pack16(acc, TA{});
   }
 }
+
+// Router-row columns per dX workgroup: 64, so that the staged block (E x 64
+// fp32: 16 KB at E = 64) leaves room for several workgroups per CU, whose
+// gathered row loads are what keeps HBM busy.
+constexpr int kDxCols = 64;
 
 // dWr[e] = sum over rows p of expert e (ascending token order) of
 // dl_perm[p] * x[src[p]].  The expert's rows are cut into `splits` contiguous
@@ -515,19 +539,25 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
   if (dm.T > 0) {
     const int elem = (dm.act == MOE_BF16) ? 2 : 4;
     const int32_t vpr = dm.d * elem / 16;
-    const int64_t total = dm.T * vpr;
-    const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
+    // column blocks x token ranges
+    const int bc = kDxCols;
+    const int ncb = dm.d / bc;
+    constexpr int kCUs = 256;   // MI355X: about 8 workgroups per CU
+    const int64_t want = std::max<int64_t>(1, (8 * kCUs + ncb - 1) / ncb);
+    const int64_t tpw = std::max<int64_t>((dm.T + want - 1) / want, 1);
+    const dim3 grid(ncb, static_cast<unsigned>((dm.T + tpw - 1) / tpw));
+    const size_t lds = static_cast<size_t>(dm.E) * bc * sizeof(float);
     const uint4* dxp = static_cast<const uint4*>(dx_perm);
     uint4* dxo = static_cast<uint4*>(dx);
 #define MOE_DX(TA, KC)                                                                        \
   if (dgate_part)                                                                             \
-    hipLaunchKernelGGL((router_dx_kernel<TA, KC, true>), dim3(blocks), dim3(kThreads), 0, s,   \
+    hipLaunchKernelGGL((router_dx_kernel<TA, KC, true>), grid, dim3(kThreads), lds, s,        \
                        dxp, pos, idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, \
-                       dm.E, dgate_part, nparts, dgate_out);                                   \
+                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw));    \
   else                                                                                        \
-    hipLaunchKernelGGL((router_dx_kernel<TA, KC, false>), dim3(blocks), dim3(kThreads), 0, s, dxp, pos, \
-                     idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, dm.E,   \
-                     dgate_part, nparts, dgate_out)
+    hipLaunchKernelGGL((router_dx_kernel<TA, KC, false>), grid, dim3(kThreads), lds, s, dxp,  \
+                       pos, idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k,     \
+                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw))
     if (dm.act == MOE_BF16) {
       switch (dm.k) {
         case 1: MOE_DX(bf16_t, 1); break;
