@@ -286,6 +286,30 @@ __device__ __forceinline__ void for_each_quad(const AccT<BIG>& acc, F&& fn) {
 }
 
 // ------------------------------------------------------------------ tile lookup
+// Sums across lanes through DPP operand modifiers (no LDS round trip).
+// row16_sum: rotations by 8, 4, 2 and 1 lanes within each 16-lane row; at
+// each level a lane adds the same two partial sums as its partner, so all 16
+// lanes end with the same bits.  row32_sum: then rows 1 and 3 add lane 15 of
+// rows 0 and 2 (row_bcast:15), so lanes 16-31 and 48-63 hold the sums of
+// lanes 0-31 and 32-63.
+template <int CTRL>
+__device__ __forceinline__ float dpp_rot(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_rot<0x128>(v);   // row_ror:8
+  v += dpp_rot<0x124>(v);   // row_ror:4
+  v += dpp_rot<0x122>(v);   // row_ror:2
+  v += dpp_rot<0x121>(v);   // row_ror:1
+  return v;
+}
+__device__ __forceinline__ float row32_sum(float v) {
+  v = row16_sum(v);
+  // rows 1 and 3 receive lane 15 of rows 0 and 2; rows 0 and 2 receive 0
+  return v + __int_as_float(
+                 __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+}
+
 __device__ __forceinline__ int flat_tile() {
   const int per = gridDim.x / kXcd;            // the grid is a multiple of 8
   return (blockIdx.x % kXcd) * per + blockIdx.x / kXcd;
@@ -725,10 +749,9 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
           *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
         }
       }
+      static_assert(CH == 16, "one row per 16 lanes");
 #pragma unroll
-      for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-        for (int ig = 0; ig < kGrp; ++ig) partv[ig] += __shfl_xor(partv[ig], m, 64);
+      for (int ig = 0; ig < kGrp; ++ig) partv[ig] = row16_sum(partv[ig]);
 #pragma unroll
       for (int ig = 0; ig < kGrp; ++ig) {
         const int v = threadIdx.x + NT * (i0 + ig);
@@ -1528,11 +1551,12 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
   if constexpr (FOLD) {
     // gate folded: the staged product is u = dy W2 (rounded); the row's dgate
     // part is <u, silu(a) b> over this column tile (a 32-lane sum in a fixed
-    // order: 32 lanes hold one row), dh = g u, da = dh b silu'(a), db = dh silu(a)
+    // order, row32_sum: 32 lanes hold one row), dh = g u, da = dh b silu'(a),
+    // db = dh silu(a)
     static_assert(BN / 8 == 32, "one row per 32 lanes");
     // the da/db stores go out in the loop; the part of each iteration's row
     // waits in a register and the 32-lane sums of all iterations run together
-    // after it (same order: xor 16, 8, 4, 2, 1)
+    // after it
     constexpr int kIt = BM * (BN / 8) / NT;
     constexpr int kGrp = 4;   // iterations whose sums run together
     static_assert(kIt % kGrp == 0, "whole groups");
@@ -1579,14 +1603,12 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
       }
     }
 #pragma unroll
-    for (int m = 16; m >= 1; m >>= 1)
-#pragma unroll
-      for (int ig = 0; ig < kGrp; ++ig) partv[ig] += __shfl_xor(partv[ig], m, 64);
+    for (int ig = 0; ig < kGrp; ++ig) partv[ig] = row32_sum(partv[ig]);
 #pragma unroll
     for (int ig = 0; ig < kGrp; ++ig) {
       const int v = tid + NT * (i0 + ig);
       const int rr = v / (BN / 8), c = v % (BN / 8);
-      if (c == 0 && rr < rows)
+      if (c == 16 && rr < rows)   // lanes 16-31 of the row's 32 hold its sum
         g.dgate_part[static_cast<int64_t>(m0 + rr) * g.n_tiles_n + nt] = partv[ig];
     }
     }
