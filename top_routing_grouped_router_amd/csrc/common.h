@@ -85,6 +85,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255);
 // route
 constexpr int kRouteTileMax = 32;   // tokens per workgroup of the vector-ALU router
 constexpr int kRouteMfmaTile = 64;  // tokens per workgroup of the matrix-core router (bf16 x)
+constexpr int kRouteF32Tile = 16;   // tokens per workgroup of the fp32 matrix-core router
 hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,

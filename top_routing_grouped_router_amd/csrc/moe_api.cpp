@@ -98,11 +98,12 @@ struct Carver {
   }
 };
 
-// Tokens per router workgroup: the matrix-core routers (64-token tiles) run
-// when those tiles never straddle two balancing blocks.
+// Tokens per router workgroup: the matrix-core routers (64-token tiles for
+// bf16, 16-token tiles for fp32) run when those tiles never straddle two
+// balancing blocks.
 int route_tile(int64_t T, int32_t G, int32_t act) {
-  (void)act;
-  if (G <= 1 || (T / G) % moe::kRouteMfmaTile == 0) return moe::kRouteMfmaTile;
+  const int mt = (act == MOE_F32) ? moe::kRouteF32Tile : moe::kRouteMfmaTile;
+  if (G <= 1 || (T / G) % mt == 0) return mt;
   if (G <= 1) return moe::kRouteTileMax;
   const int64_t per = T / G;
   int tile = moe::kRouteTileMax;

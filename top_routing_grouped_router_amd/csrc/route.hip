@@ -469,16 +469,17 @@ __device__ __forceinline__ uint64_t key_max_level(uint64_t k) {
   return o > k ? o : k;
 }
 
-// Per-token epilogue shared by the matrix-core router kernels: lane (g, c) of
-// wavefront `wave` holds the logits of tokens t0 + 16 wave + 4 g + q (q < 4)
-// for experts 16 j + c in acc[j][q].  Writes logits, top-k ids and gates,
-// margins, and the workgroup's LB partial sums (fixed-order folds).
-template <int NT, bool FUSED>
+// Per-token epilogue shared by the matrix-core router kernels (NW wavefronts
+// per workgroup): lane (g, c) of wavefront `wave` holds the logits of tokens
+// t0 + 16 wave + 4 g + q (q < 4) for experts 16 j + c in acc[j][q].  Writes
+// logits, top-k ids and gates, margins, and the workgroup's LB partial sums
+// (fixed-order folds).
+template <int NT, bool FUSED, int NW = 4>
 __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f32x4_t (&acc)[NT],
                                                     int64_t t0) {
-  __shared__ float psum_w[4][16 * NT];
-  __shared__ int32_t pcnt_w[4][16 * NT];
-  __shared__ int32_t tie_w[4];
+  __shared__ float psum_w[NW][16 * NT];
+  __shared__ int32_t pcnt_w[NW][16 * NT];
+  __shared__ int32_t tie_w[NW];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
@@ -620,9 +621,14 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
   ties += __shfl_xor(ties, 32, 64);
   if (lane == 0) tie_w[wave] = ties;
   __syncthreads();
-  for (int e = tid; e < E; e += kThreads) {
-    const float s = ((psum_w[0][e] + psum_w[1][e]) + psum_w[2][e]) + psum_w[3][e];
-    const int32_t n = pcnt_w[0][e] + pcnt_w[1][e] + pcnt_w[2][e] + pcnt_w[3][e];
+  for (int e = tid; e < E; e += 64 * NW) {
+    float s = psum_w[0][e];
+    int32_t n = pcnt_w[0][e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {   // wavefront order
+      s += psum_w[w][e];
+      n += pcnt_w[w][e];
+    }
     const int64_t o = static_cast<int64_t>(blockIdx.x) * ep4(E) + e;
     if (FUSED) {
       st_agent(a.psum + o, s);
@@ -632,7 +638,9 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
       a.pcnt[o] = n;
     }
   }
-  const int32_t tt = tie_w[0] + tie_w[1] + tie_w[2] + tie_w[3];
+  int32_t tt = tie_w[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) tt += tie_w[w];
   if (FUSED) {
     if (tid == 0) st_agent(a.ptie + blockIdx.x, tt);
     route_arrive(a);
@@ -852,8 +860,9 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
   route_tile_epilogue<NT, false>(a, acc, t0);
 }
 
-// fp32 hidden states on the fp32 matrix cores (v_mfma_f32_16x16x4_f32),
-// same 64-token tiles, C layout and epilogue as the bf16 routers.  For one
+// fp32 hidden states on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), one
+// wavefront of 16 tokens per workgroup (small fp32 batches then still spread
+// over every CU), with the C layout and epilogue of the bf16 routers.  For one
 // 16-wide k block lane (g, c) loads k = 4 g ... 4 g + 3 of its token row c and
 // of expert row 16 j + c as one float4 each, and MFMA step s takes element s
 // of both: A and B use the same k assignment, so the 4 steps cover the block.
@@ -861,13 +870,13 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
 // KB blocks per batch (10 to 18 float4 per lane for both operands; blocks
 // past d read zeros), the next batch in flight while the current one runs.
 template <int NT>   // 16-expert tiles: E <= 16 NT
-__global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
+__global__ __launch_bounds__(64) void route_f32_kernel(RouteArgs a) {
   constexpr int KB = NT == 1 ? 8 : NT == 2 ? 4 : NT <= 8 ? 2 : 1;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, c = lane & 15;
   const int E = a.E, d = a.d;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMTile;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kRouteF32Tile;
   const int64_t my_row = t0 + wave * 16 + c;
   const bool row_ok = my_row < a.T;
   const float* xrow = static_cast<const float*>(a.x) + (row_ok ? my_row : 0) * d + 4 * g;
@@ -917,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(RouteArgs a) {
       for (int j = 0; j < NT; ++j) wc[b][j] = wn[b][j];
     }
   }
-  route_tile_epilogue<NT, false>(a, acc, t0);
+  route_tile_epilogue<NT, false, 1>(a, acc, t0);
 }
 
 // Second launch of the two-kernel paths (every path but the streaming one):
@@ -1303,11 +1312,11 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
       if (nt_p == 1) { MOE_RL_D(1) } else if (nt_p == 2) { MOE_RL_D(2) } else { MOE_RL_D(4) }
 #undef MOE_RL_D
 #undef MOE_RL
-    } else if (tile == kRouteMfmaTile && dm.act == MOE_F32) {
+    } else if (tile == kRouteF32Tile && dm.act == MOE_F32) {
       const int ntf = (dm.E + 15) / 16;
 #define MOE_RF(N)                                                                      \
   case N:                                                                              \
-    hipLaunchKernelGGL(route_f32_kernel<N>, dim3(n_tiles), dim3(kThreads), 0, s, a);   \
+    hipLaunchKernelGGL(route_f32_kernel<N>, dim3(n_tiles), dim3(64), 0, s, a);         \
     break;
       switch (ntf <= 1 ? 1 : ntf <= 2 ? 2 : ntf <= 4 ? 4 : ntf <= 8 ? 8 : 16) {
         MOE_RF(1)
