@@ -132,9 +132,9 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
  * memory or hand over a workspace (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation).  Same arguments, outputs,
  * kernels and bits as moe_route, without workspace and workspace_bytes: the
- * scratch (per-tile partial sums and an arrival counter, cleared by the call
- * itself where it must start at zero) lives in a static device array of
- * moe_route_noalloc_max_bytes() = 4 MiB that the library holds on every GPU
+ * scratch (per-tile partial sums of the balancing statistics, each written
+ * before it is read, so nothing in it has to start at zero) lives in a static
+ * device array of moe_route_noalloc_max_bytes() = 4 MiB that the library holds on every GPU
  * it runs on until the process ends.  Dims whose scratch exceeds it (about
  * 2000 64-token tiles at E = 256, 8000 at E = 64) return MOE_ERR_UNSUPPORTED
  * with nothing enqueued.  Every call on one GPU shares that GPU's array and

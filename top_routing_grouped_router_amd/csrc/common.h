@@ -89,8 +89,7 @@ constexpr int kRouteF32Tile = 16;   // tokens per workgroup of the fp32 matrix-c
 hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, float* logits,
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
-                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie,
-                        uint32_t* ws_arrivals, hipStream_t s);
+                        float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie, hipStream_t s);
 
 // permutation (also used by the dispatch plan with "groups" as keys)
 constexpr int kPermBlock = 256;     // tokens per permutation block

@@ -112,7 +112,6 @@ int route_tile(int64_t T, int32_t G, int32_t act) {
 }
 
 struct RouteWs {
-  uint32_t* arrivals;
   float* psum;
   int32_t* pcnt;
   int32_t* ptie;
@@ -122,7 +121,6 @@ RouteWs route_ws(const moe_dims& dm, int tile, void* ws) {
   const int64_t n_tiles = (dm.T + tile - 1) / tile;
   Carver c;
   RouteWs r;
-  r.arrivals = c.take<uint32_t>(ws, 1);
   const int64_t ep4 = (dm.E + 3) & ~3;   // partial rows padded to 16 bytes
   r.psum = c.take<float>(ws, n_tiles * ep4);
   r.pcnt = c.take<int32_t>(ws, n_tiles * ep4);
@@ -474,7 +472,7 @@ moe_status route_impl(const moe_dims* dims, const void* x, const float* w_router
   return hip_status(moe::launch_route(dm, x, w_router, logits, topk_idx, topk_gate, margin,
                                       near_tie_eps, near_tie_count, n_groups, group_count,
                                       group_mean_prob, group_aux, tile, w.psum, w.pcnt, w.ptie,
-                                      w.arrivals, static_cast<hipStream_t>(stream)),
+                                      static_cast<hipStream_t>(stream)),
                     fn);
 }
 }  // namespace

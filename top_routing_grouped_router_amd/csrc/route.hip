@@ -13,11 +13,8 @@
 // fp32, for 64-token tiles; on the vector ALUs for the smaller tiles that
 // balancing blocks of other sizes need), then one 16-lane group (or one
 // wavefront) per token for top-k, gates, margin and the full softmax, and
-// per-tile partial sums of the balancing statistics, which are folded per
-// block in a fixed order (no floating-point atomics).  Two launches per call:
-// for d > 256 (bf16, E <= 64) a one-thread kernel clears an arrival counter
-// and the last workgroup of the streaming router folds the partials; on every
-// other path a second kernel folds them.
+// per-tile partial sums of the balancing statistics, which a second kernel
+// folds per block in a fixed order (no floating-point atomics).
 #include "common.h"
 
 namespace moe {
@@ -38,7 +35,6 @@ struct RouteArgs {
   float* psum;            // [tiles, E] partial sums of the full softmax
   int32_t* pcnt;          // [tiles, E] partial expert counts
   int32_t* ptie;          // [tiles] partial near-tie counts
-  uint32_t* arrivals;     // workgroups done (cleared by route_prep_kernel)
   int32_t* gcount;        // [G, E] or NULL
   float* gprob;           // [G, E] or NULL
   float* gaux;            // [G] or NULL
@@ -48,145 +44,7 @@ struct RouteArgs {
   float eps;
 };
 
-// Partial sums cross workgroups (and the XCDs' separate L2 caches) within
-// one kernel, so they are written and read with agent-scope atomics.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Per-block statistics from every tile's partials, by one 256-thread
-// workgroup.  Partials are laid out [tile][Ep4] (E rounded up to a multiple
-// of 4) and read as 16-byte vectors with the sc1 bit (coherent across the
-// XCDs' L2 caches, like the write-through stores that wrote them), all of a
-// thread's loads issued before any is used.  Fixed order throughout: thread
-// (pair, sl), pair = (block r, 4-expert column c4), adds tiles sl, sl + SLg,
-// ... of block r in tile order; the SLg sums of a pair are then added in sl
-// order; aux adds f_e P_e over e in order; the near-tie partials go through a
-// fixed thread-strided sum and lane tree.
-constexpr int kFinLoads = 16;   // loads in flight per thread
 __device__ __forceinline__ int ep4(int E) { return (E + 3) & ~3; }
-__device__ __forceinline__ float4 ld_sc1_f4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), 0, 16));
-}
-__device__ void route_finalize_block(const RouteArgs& a) {
-  __shared__ float4 s4[kThreads];
-  __shared__ int4 c4s[kThreads];
-  __shared__ float fpe[kThreads * 4];
-  __shared__ int32_t st[kThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int E = a.E, Ep = ep4(E), E4 = Ep / 4;
-  int E4p = 1;
-  while (E4p < E4) E4p <<= 1;
-  const int tpg = a.n_tiles / a.G;
-  const double per_group = static_cast<double>(a.T) / static_cast<double>(a.G);
-  const uint32_t pbytes = static_cast<uint32_t>(a.n_tiles) * Ep * 4;
-  const auto rp = __builtin_amdgcn_make_buffer_rsrc(a.psum, 0, pbytes, 0x00020000);
-  const auto rc = __builtin_amdgcn_make_buffer_rsrc(a.pcnt, 0, pbytes, 0x00020000);
-  // pairs (r, c4) processed 256 / SLg at a time
-  const int pairs = a.G * E4p;
-  const int SLg = pairs >= kThreads ? 1 : kThreads / pairs;
-  const int per_pass = kThreads / SLg;
-  for (int p0 = 0; p0 < pairs; p0 += per_pass) {
-    const int pair = p0 + tid / SLg, sl = tid % SLg;
-    const int r = pair / E4p, c4 = pair % E4p;
-    const bool on = pair < pairs && c4 < E4;
-    float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
-    int4 C = make_int4(0, 0, 0, 0);
-    if (on) {
-      for (int i0 = sl; i0 < tpg; i0 += SLg * kFinLoads) {
-        float4 ps[kFinLoads];
-        float4 pc[kFinLoads];
-#pragma unroll
-        for (int u = 0; u < kFinLoads; ++u) {
-          const int i = min(i0 + SLg * u, tpg - 1);
-          const uint32_t o = static_cast<uint32_t>(((static_cast<int64_t>(r) * tpg + i) * Ep + 4 * c4) * 4);
-          ps[u] = ld_sc1_f4(rp, o);
-          pc[u] = ld_sc1_f4(rc, o);
-        }
-#pragma unroll
-        for (int u = 0; u < kFinLoads; ++u) {
-          if (i0 + SLg * u < tpg) {
-            S.x += ps[u].x; S.y += ps[u].y; S.z += ps[u].z; S.w += ps[u].w;
-            const int4 ci = __builtin_bit_cast(int4, pc[u]);
-            C.x += ci.x; C.y += ci.y; C.z += ci.z; C.w += ci.w;
-          }
-        }
-      }
-    }
-    s4[tid] = S;
-    c4s[tid] = C;
-    __syncthreads();
-    if (on && sl == 0) {
-      float4 T4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      int4 N4 = make_int4(0, 0, 0, 0);
-      for (int q = 0; q < SLg; ++q) {
-        const float4 v = s4[tid + q];
-        const int4 n = c4s[tid + q];
-        T4.x += v.x; T4.y += v.y; T4.z += v.z; T4.w += v.w;
-        N4.x += n.x; N4.y += n.y; N4.z += n.z; N4.w += n.w;
-      }
-      const float sv[4] = {T4.x, T4.y, T4.z, T4.w};
-      const int32_t nv[4] = {N4.x, N4.y, N4.z, N4.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = 4 * c4 + q;
-        float prod = 0.f;
-        if (e < E) {
-          const float P = (per_group > 0) ? static_cast<float>(sv[q] / per_group) : 0.f;
-          const float fr = (per_group > 0) ? static_cast<float>(nv[q] / (per_group * a.k)) : 0.f;
-          if (a.gcount) a.gcount[static_cast<int64_t>(r) * E + e] = nv[q];
-          if (a.gprob) a.gprob[static_cast<int64_t>(r) * E + e] = P;
-          prod = fr * P;
-        }
-        fpe[(tid / SLg) * 4 + q] = prod;
-      }
-    }
-    __syncthreads();
-    // aux of the blocks in this pass (a pass holds whole blocks: per_pass is
-    // a multiple of E4p or covers every pair): one thread per block, e in order
-    const int rr = p0 / E4p + tid;
-    if (rr < a.G && (rr + 1) * E4p <= p0 + per_pass) {
-      float v = 0.f;
-      for (int e = 0; e < E; ++e) v += fpe[(rr * E4p - p0) * 4 + e];
-      if (a.gaux) a.gaux[rr] = static_cast<float>(E) * v;
-    }
-    __syncthreads();
-  }
-  int32_t t = 0;
-  for (int i = tid; i < a.n_tiles; i += kThreads) t += ld_agent(a.ptie + i);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) t += __shfl_xor(t, m, 64);
-  if (lane == 0) st[wave] = t;
-  __syncthreads();
-  if (tid == 0) *a.tie_count = st[0] + st[1] + st[2] + st[3];
-}
-
-// End of a tile: its partials were stored with write-through (agent-scope)
-// stores by the caller; each wavefront waits until its stores are
-// acknowledged, the workgroup counts itself in, and the last one to arrive
-// folds every tile's partials.
-__device__ __forceinline__ void route_arrive(const RouteArgs& a) {
-  __shared__ int last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev =
-        __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = prev == static_cast<uint32_t>(a.n_tiles - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  route_finalize_block(a);
-}
 
 struct Key {
   float v;
@@ -474,7 +332,7 @@ __device__ __forceinline__ uint64_t key_max_level(uint64_t k) {
 // t0 + 16 wave + 4 g + q (q < 4) for experts 16 j + c in acc[j][q].  Writes
 // logits, top-k ids and gates, margins, and the workgroup's LB partial sums
 // (fixed-order folds).
-template <int NT, bool FUSED, int NW = 4>
+template <int NT, int NW = 4>
 __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f32x4_t (&acc)[NT],
                                                     int64_t t0) {
   __shared__ float psum_w[NW][16 * NT];
@@ -630,23 +488,13 @@ __device__ __forceinline__ void route_tile_epilogue(const RouteArgs& a, const f3
       n += pcnt_w[w][e];
     }
     const int64_t o = static_cast<int64_t>(blockIdx.x) * ep4(E) + e;
-    if (FUSED) {
-      st_agent(a.psum + o, s);
-      st_agent(a.pcnt + o, n);
-    } else {
-      a.psum[o] = s;
-      a.pcnt[o] = n;
-    }
+    a.psum[o] = s;
+    a.pcnt[o] = n;
   }
   int32_t tt = tie_w[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) tt += tie_w[w];
-  if (FUSED) {
-    if (tid == 0) st_agent(a.ptie + blockIdx.x, tt);
-    route_arrive(a);
-  } else if (tid == 0) {
-    a.ptie[blockIdx.x] = tt;
-  }
+  if (tid == 0) a.ptie[blockIdx.x] = tt;
 }
 
 template <int NT>   // 16-expert tiles: E <= 16 NT
@@ -763,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void route_mfma_kernel(RouteArgs a) {
     __syncthreads();
   }
 
-  route_tile_epilogue<NT, false>(a, acc, t0);
+  route_tile_epilogue<NT>(a, acc, t0);
 }
 
 // Matrix-core router for small E d (the split weight fits in LDS whole):
@@ -857,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void route_lds_kernel(RouteArgs a) {
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr, acc[j], 0, 0, 0);
       }
   }
-  route_tile_epilogue<NT, false>(a, acc, t0);
+  route_tile_epilogue<NT>(a, acc, t0);
 }
 
 // fp32 hidden states on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), one
@@ -926,7 +774,7 @@ __global__ __launch_bounds__(64) void route_f32_kernel(RouteArgs a) {
       for (int j = 0; j < NT; ++j) wc[b][j] = wn[b][j];
     }
   }
-  route_tile_epilogue<NT, false, 1>(a, acc, t0);
+  route_tile_epilogue<NT, 1>(a, acc, t0);
 }
 
 // Second launch of the two-kernel paths (every path but the streaming one):
@@ -1051,8 +899,7 @@ __global__ __launch_bounds__(kFinThreads) void route_finalize_kernel(
 // its own loads with an explicit vmcnt plus a barrier (the compiler would
 // drain every direct-to-LDS load in flight before its own LDS reads).  The
 // logits then pass through LDS so that each wavefront holds its 16 tokens' E
-// logits in the epilogue's layout.  route_prep_kernel clears the arrival
-// counter first; the last workgroup folds the balancing statistics.
+// logits in the epilogue's layout.
 // ---------------------------------------------------------------------------
 namespace rdma {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -1094,11 +941,6 @@ __device__ __forceinline__ void split8(const float4& w0, const float4& w1, bf16x
   hi = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
   mid = __builtin_bit_cast(bf16x8_t, make_uint4(m[0], m[1], m[2], m[3]));
   lo = __builtin_bit_cast(bf16x8_t, make_uint4(l[0], l[1], l[2], l[3]));
-}
-
-// Clears the arrival counter of the streaming router.
-__global__ __launch_bounds__(64) void route_prep_kernel(uint32_t* arrivals) {
-  if (threadIdx.x == 0) *arrivals = 0u;
 }
 
 // A fragments of one chunk from LDS: the wavefront's token blocks i and both
@@ -1257,7 +1099,7 @@ __global__ __launch_bounds__(kThreads, 1) void route_stream_kernel(RouteArgs a) 
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc_e[j][q] = L[(16 * wave + 4 * g + q) * kLdL + 16 * j + c];
-  route_tile_epilogue<NT, true>(a, acc_e, t0);
+  route_tile_epilogue<NT>(a, acc_e, t0);
 }
 
 }  // namespace
@@ -1279,25 +1121,20 @@ hipError_t launch_route(const moe_dims& dm, const void* x, const float* wr, floa
                         int32_t* idx, float* gate, float* margin, float eps, int32_t* tie_count,
                         int32_t G, int32_t* gcount, float* gprob, float* gaux, int tile,
                         float* ws_psum, int32_t* ws_pcnt, int32_t* ws_ptie,
-                        uint32_t* ws_arrivals, hipStream_t s) {
+                        hipStream_t s) {
   const int64_t n_tiles = (dm.T + tile - 1) / tile;
-  RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie, ws_arrivals,
+  RouteArgs a{x, wr, logits, idx, gate, margin, ws_psum, ws_pcnt, ws_ptie,
               gcount, gprob, gaux, tie_count, dm.T, dm.d, dm.E, dm.k, tile, G,
               static_cast<int32_t>(n_tiles), eps};
-  if (n_tiles > 0 && tile == kRouteMfmaTile && route_split_ok(dm)) {
-    // streaming path: the split weight and the cleared counter first; the
-    // last workgroup of the main kernel folds the statistics
-    const int nt = route_split_nt(dm);
-    hipLaunchKernelGGL(route_prep_kernel, dim3(1), dim3(64), 0, s, ws_arrivals);
-    switch (nt) {
-      case 1: hipLaunchKernelGGL((route_stream_kernel<1, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((route_stream_kernel<2, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL((route_stream_kernel<4, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
-    }
-    return hipGetLastError();
-  }
   if (n_tiles > 0) {
-    if (tile == kRouteMfmaTile && route_in_lds(dm)) {
+    if (tile == kRouteMfmaTile && route_split_ok(dm)) {
+      // streaming path
+      switch (route_split_nt(dm)) {
+        case 1: hipLaunchKernelGGL((route_stream_kernel<1, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((route_stream_kernel<2, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((route_stream_kernel<4, 5>), dim3(n_tiles), dim3(kThreads), 0, s, a); break;
+      }
+    } else if (tile == kRouteMfmaTile && route_in_lds(dm)) {
       const int nt = (dm.E + 15) / 16;
       const int nt_p = nt <= 1 ? 1 : nt <= 2 ? 2 : 4;
 #define MOE_RL(N, K)                                                                          \
