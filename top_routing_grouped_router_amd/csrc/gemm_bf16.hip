@@ -1077,14 +1077,26 @@ __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
   };
   if constexpr (MODE == UP) {
     constexpr int kCh = kUpHalf / 8;
-    for (int v = tid; v < BM * kCh; v += NT) {
+    constexpr int kIt = BM * kCh / NT;
+    static_assert(BM * kCh % NT == 0, "whole iterations");
+    // the gates of the thread's rows are loaded first (clamped in bounds), so
+    // the epilogue waits for one latency, not one per row
+    float grs[kIt];
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int it = 0; it < kIt; ++it)
+        grs[it] = g.gate_rows[m0 + min((tid + NT * it) / kCh, rows - 1)];
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int v = tid + NT * it;
       const int rr = v / kCh, c = v % kCh;
       if (rr >= rows) continue;
       const uint4 av = chunk_at(rr, c), bv = chunk_at(rr, c + kCh);
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
       uint32_t hw[4];
       if constexpr (FOLD) {   // the row's gate on h
-        const float gr = g.gate_rows[m0 + rr];
+        const float gr = grs[it];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           hw[q] = bf_pack(silu_f(bf_lo(aw[q])) * bf_lo(bw[q]) * gr,
@@ -1554,27 +1566,36 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
     // order, row32_sum: 32 lanes hold one row), dh = g u, da = dh b silu'(a),
     // db = dh silu(a)
     static_assert(BN / 8 == 32, "one row per 32 lanes");
-    // the da/db stores go out in the loop; the part of each iteration's row
-    // waits in a register and the 32-lane sums of all iterations run together
-    // after it
+    // the a, b and gate loads of a group of kGrp iterations are issued before
+    // any is used (the accumulators are in LDS by now, so their registers
+    // hold them); the da/db stores go out in the loop, and the 32-lane sums
+    // of the group's parts run together after it
     constexpr int kIt = BM * (BN / 8) / NT;
-    constexpr int kGrp = 4;   // iterations whose sums run together
+    constexpr int kGrp = 8;   // two groups per tile (all 16 at once would spill)
     static_assert(kIt % kGrp == 0, "whole groups");
     for (int i0 = 0; i0 < kIt; i0 += kGrp) {
+    uint4 av[kGrp], bv[kGrp];
+    float gr[kGrp];
+#pragma unroll
+    for (int ig = 0; ig < kGrp; ++ig) {
+      const int v = tid + NT * (i0 + ig);
+      const int rr = v / (BN / 8), c = v % (BN / 8);
+      const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
+      const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
+      av[ig] = *reinterpret_cast<const uint4*>(g.aux0 + ol);
+      bv[ig] = *reinterpret_cast<const uint4*>(g.aux1 + ol);
+      gr[ig] = g.gate_rows[m0 + rl];
+    }
     float partv[kGrp];
 #pragma unroll
     for (int ig = 0; ig < kGrp; ++ig) {
       const int v = tid + NT * (i0 + ig);
       const int rr = v / (BN / 8), c = v % (BN / 8);
       const bool ok = rr < rows && c < nch;
-      const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
       const uint4 uv = *reinterpret_cast<const uint4*>(row_ptr(rr) + ((c ^ (rr & 15)) << 3));
-      const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
-      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + ol);
-      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + ol);
-      const float gr = g.gate_rows[m0 + rl];
       const uint32_t uw[4] = {uv.x, uv.y, uv.z, uv.w};
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      const uint32_t aw[4] = {av[ig].x, av[ig].y, av[ig].z, av[ig].w};
+      const uint32_t bw[4] = {bv[ig].x, bv[ig].y, bv[ig].z, bv[ig].w};
       float part = 0.f;
       uint32_t daw[4], dbw[4];
 #pragma unroll
@@ -1588,7 +1609,7 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
           const float sg = sigmoid_f(aa[u]);
           const float sa = aa[u] * sg;   // silu(a)
           part = fmaf(uu[u], sa * bb[u], part);
-          const float dh = gr * uu[u];
+          const float dh = gr[ig] * uu[u];
           da2[u] = dh * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
           db2[u] = dh * sa;
         }
@@ -1614,37 +1635,61 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
     }
     return;
   }
+  if constexpr (MODE == DGRAD_DOWN) {
+    // the saved a and b of a group of kGrp iterations are loaded before any
+    // is used (clamped in bounds), as in the gate-folded epilogue above
+    constexpr int kIt = BM * (BN / 8) / NT;
+    constexpr int kGrp = 8;
+    static_assert(kIt % kGrp == 0, "whole groups");
+    for (int i0 = 0; i0 < kIt; i0 += kGrp) {
+      uint4 av[kGrp], bv[kGrp];
+#pragma unroll
+      for (int ig = 0; ig < kGrp; ++ig) {
+        const int v = tid + NT * (i0 + ig);
+        const int rr = v / (BN / 8), c = v % (BN / 8);
+        const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
+        const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
+        av[ig] = *reinterpret_cast<const uint4*>(g.aux0 + ol);
+        bv[ig] = *reinterpret_cast<const uint4*>(g.aux1 + ol);
+      }
+#pragma unroll
+      for (int ig = 0; ig < kGrp; ++ig) {
+        const int v = tid + NT * (i0 + ig);
+        const int rr = v / (BN / 8), c = v % (BN / 8);
+        if (rr >= rows || c >= nch) continue;
+        const uint4 hv = *reinterpret_cast<const uint4*>(row_ptr(rr) + ((c ^ (rr & 15)) << 3));
+        const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
+        const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+        const uint32_t aw[4] = {av[ig].x, av[ig].y, av[ig].z, av[ig].w};
+        const uint32_t bw[4] = {bv[ig].x, bv[ig].y, bv[ig].z, bv[ig].w};
+        uint32_t daw[4], dbw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float da2[2], db2[2];
+          const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
+          const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
+          const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float sg = sigmoid_f(aa[u]);
+            da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
+            db2[u] = hh[u] * (aa[u] * sg);
+          }
+          daw[q] = bf_pack(da2[0], da2[1]);
+          dbw[q] = bf_pack(db2[0], db2[1]);
+        }
+        *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
+        *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
+      }
+    }
+    return;
+  }
   for (int v = tid; v < BM * (BN / 8); v += NT) {
     const int rr = v / (BN / 8), c = v % (BN / 8);
     if (rr >= rows || c >= nch) continue;
     const uint4 hv = *reinterpret_cast<const uint4*>(row_ptr(rr) + ((c ^ (rr & 15)) << 3));
     const int64_t o = static_cast<int64_t>(m0 + rr) * Ndim + n0 + c * 8;
-    if constexpr (MODE == DGRAD_DOWN) {
-      const uint4 av = *reinterpret_cast<const uint4*>(g.aux0 + o);
-      const uint4 bv = *reinterpret_cast<const uint4*>(g.aux1 + o);
-      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-      const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
-      uint32_t daw[4], dbw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float da2[2], db2[2];
-        const float hh[2] = {bf_lo(hw[q]), bf_hi(hw[q])};
-        const float aa[2] = {bf_lo(aw[q]), bf_hi(aw[q])};
-        const float bb[2] = {bf_lo(bw[q]), bf_hi(bw[q])};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const float sg = sigmoid_f(aa[u]);
-          da2[u] = hh[u] * bb[u] * (sg * (1.0f + aa[u] * (1.0f - sg)));
-          db2[u] = hh[u] * (aa[u] * sg);
-        }
-        daw[q] = bf_pack(da2[0], da2[1]);
-        dbw[q] = bf_pack(db2[0], db2[1]);
-      }
-      *reinterpret_cast<uint4*>(g.c0 + o) = make_uint4(daw[0], daw[1], daw[2], daw[3]);
-      *reinterpret_cast<uint4*>(g.c1 + o) = make_uint4(dbw[0], dbw[1], dbw[2], dbw[3]);
-    } else {
-      *reinterpret_cast<uint4*>(g.c0 + o) = hv;
-    }
+    *reinterpret_cast<uint4*>(g.c0 + o) = hv;
   }
 }
 
