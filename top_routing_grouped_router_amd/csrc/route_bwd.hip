@@ -23,13 +23,21 @@ constexpr int kThreads = 256;
 //   dX[t]   = sum_j dx_perm[pos[t,j]] + sum_j dl[t,j] wr[idx[t,j]]
 // summed in fp32 in slot order and rounded once.  Workgroup (column block,
 // token range): the block's bc columns of every router row (E x bc fp32) are
-// staged in LDS once, then each thread takes one 16-byte chunk of dX for
-// kThreads / (bc / kPer) tokens at a time, so the router rows come from LDS
-// rather than from L2 once per chunk and slot.  The threads holding chunk 0
-// of a row also scatter dl into permuted row order for the dWr kernel.  K is
-// the compile-time k (0: runtime k <= 16); every load of a token is issued
-// before any is used (indices clamped, invalid slots masked), so a row costs
-// one memory latency rather than one per slot.
+// staged in LDS once, so the router rows come from LDS rather than from L2
+// once per chunk and slot.  The token range goes in batches of kBatch tokens
+// (kThreads, or half of it for k > 8): first thread i reads the slots of token i of the batch (gates,
+// dgate or its column-tile parts, positions, ids: coalesced across the
+// threads, each once per column block), forms dl, and puts (position, id, dl)
+// of every slot in an LDS table; the workgroups of column block 0 also
+// scatter dl into permuted row order for the dWr kernel (and, gate folded,
+// write dgate).  Then each thread takes one 16-byte chunk of dX for
+// kThreads / (bc / kPer) tokens at a time, with the slots from the table; K
+// is the compile-time k (0: runtime k <= 16), and every row load of a token is
+// issued before any is used (positions clamped, invalid slots masked), so a
+// row costs one memory latency rather than one per slot.
+// tokens per slot-table batch (the table takes 12 KM kBatch bytes of LDS)
+constexpr int dx_batch(int km) { return km <= 8 ? kThreads : kThreads / 2; }
+
 template <typename TA, int K, bool FOLD>
 __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ pos,
@@ -38,11 +46,16 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E,
     const float* __restrict__ dgate_part, int32_t nparts, float* __restrict__ dgate_out,
     int32_t bc, int32_t tok_per_wg) {
-  extern __shared__ __attribute__((aligned(16))) float wl[];   // [E][bc]
+  // [E][bc] router block, then the batch's slot table [KM][kBatch] x 3
+  extern __shared__ __attribute__((aligned(16))) float wl[];
   constexpr int kPer = Act<TA>::kPer16B;
   constexpr int KM = K > 0 ? K : 16;
+  constexpr int kBatch = dx_batch(KM);
   const int kk = K > 0 ? K : k;
   const int col0 = blockIdx.x * bc;
+  int32_t* const tab_p = reinterpret_cast<int32_t*>(wl + E * bc);
+  int32_t* const tab_e = tab_p + KM * kBatch;
+  float* const tab_dl = reinterpret_cast<float*>(tab_e + KM * kBatch);
   {
     const int q4 = bc / 4;
     for (int i = threadIdx.x; i < E * q4; i += kThreads) {
@@ -51,98 +64,116 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
           *reinterpret_cast<const float4*>(wr + static_cast<int64_t>(e) * d + col0 + q * 4);
     }
   }
-  __syncthreads();
   const int cpr = bc / kPer;                    // chunks of the block per row
   const int tpp = kThreads / cpr;               // tokens per pass
   const int cl = threadIdx.x % cpr;             // chunk within the block
   const int32_t c = col0 / kPer + cl;           // chunk within the row
-  const int64_t t_end = min<int64_t>(T, static_cast<int64_t>(blockIdx.y + 1) * tok_per_wg);
-  for (int64_t t = static_cast<int64_t>(blockIdx.y) * tok_per_wg + threadIdx.x / cpr; t < t_end;
-       t += tpp) {
-    const int64_t v = t * vpr + c;
-    float g[KM], dg[KM];
-    int32_t p[KM], e[KM];
+  const bool first_block = blockIdx.x == 0;
+  const int64_t t_beg = static_cast<int64_t>(blockIdx.y) * tok_per_wg;
+  const int64_t t_end = min<int64_t>(T, t_beg + tok_per_wg);
+  for (int64_t b0 = t_beg; b0 < t_end; b0 += kBatch) {
+    __syncthreads();   // the router block is staged; the previous table is read
+    {
+      const int64_t t = b0 + threadIdx.x;
+      if (static_cast<int>(threadIdx.x) < kBatch && t < t_end) {
+        float g[KM], dg[KM];
+        int32_t p[KM], e[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const int64_t q = t * kk + min(j, kk - 1);
-      g[j] = gate[q];
-      dg[j] = FOLD ? 0.f : dgate[q];   // folded: from the parts below
-      p[j] = pos[q];
-      e[j] = idx[q];
-    }
-    uint4 rows[KM];
+        for (int j = 0; j < KM; ++j) {
+          const int64_t q = t * kk + min(j, kk - 1);
+          g[j] = gate[q];
+          dg[j] = FOLD ? 0.f : dgate[q];   // folded: from the parts below
+          p[j] = pos[q];
+          e[j] = idx[q];
+        }
+        if constexpr (FOLD) {
+          // gate folded onto the rows: dg is the sum of the row's column-tile
+          // parts in tile order (0 for a dropped slot); the first kPartsU
+          // parts of every slot are loaded at once, the rest (wide f) in a loop
+          constexpr int kPartsU = 4;
+          float pv[KM][kPartsU];
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      rows[j] = dxp ? dxp[static_cast<int64_t>(max(p[j], 0)) * vpr + c] : make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (FOLD) {
-      // gate folded onto the rows: dg is the sum of the row's column-tile parts
-      // in tile order (0 for a dropped slot); the first kPartsU parts of every
-      // slot are loaded after the rows, all at once, the rest (wide f) in a loop
-      constexpr int kPartsU = 4;
-      float pv[KM][kPartsU];
+          for (int j = 0; j < KM; ++j) {
+            const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
+            for (int q = 0; q < kPartsU; ++q) pv[j][q] = pp[min(q, nparts - 1)];
+          }
 #pragma unroll
-        for (int q = 0; q < kPartsU; ++q) pv[j][q] = pp[min(q, nparts - 1)];
-      }
+          for (int j = 0; j < KM; ++j) {
+            const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
+            float sum = pv[j][0];
 #pragma unroll
-      for (int j = 0; j < KM; ++j) {
-        const float* pp = dgate_part + static_cast<int64_t>(max(p[j], 0)) * nparts;
-        float sum = pv[j][0];
+            for (int q = 1; q < kPartsU; ++q)
+              if (q < nparts) sum += pv[j][q];
+            for (int q = kPartsU; q < nparts; ++q) sum += pp[q];
+            dg[j] = (p[j] >= 0) ? sum : 0.f;
+          }
+          if (first_block) {
 #pragma unroll
-        for (int q = 1; q < kPartsU; ++q)
-          if (q < nparts) sum += pv[j][q];
-        for (int q = kPartsU; q < nparts; ++q) sum += pp[q];
-        dg[j] = (p[j] >= 0) ? sum : 0.f;
-      }
-      if (c == 0) {
+            for (int j = 0; j < KM; ++j)
+              if (j < kk) dgate_out[t * kk + j] = dg[j];
+          }
+        }
+        float inner = 0.f;
 #pragma unroll
         for (int j = 0; j < KM; ++j)
-          if (j < kk) dgate_out[t * kk + j] = dg[j];
+          if (j < kk) inner = fmaf(g[j], dg[j], inner);
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+          const float dl = g[j] * (dg[j] - inner);
+          const bool live = j < kk;
+          if (first_block && live && p[j] >= 0) dl_perm[p[j]] = dl;
+          tab_p[j * kBatch + threadIdx.x] = live ? p[j] : -1;
+          tab_e[j * kBatch + threadIdx.x] = (live && e[j] >= 0 && e[j] < E) ? e[j] : -1;
+          tab_dl[j * kBatch + threadIdx.x] = dl;
+        }
       }
     }
-    float inner = 0.f;
+    __syncthreads();
+    const int nb = static_cast<int>(min<int64_t>(kBatch, t_end - b0));
+    for (int i = threadIdx.x / cpr; i < nb; i += tpp) {
+      int32_t p[KM], e[KM];
+      float dl[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j)
-      if (j < kk) inner = fmaf(g[j], dg[j], inner);
-    float dl[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) dl[j] = g[j] * (dg[j] - inner);
-    if (c == 0) {
+      for (int j = 0; j < KM; ++j) {
+        p[j] = tab_p[j * kBatch + i];
+        e[j] = tab_e[j * kBatch + i];
+        dl[j] = tab_dl[j * kBatch + i];
+      }
+      uint4 rows[KM];
 #pragma unroll
       for (int j = 0; j < KM; ++j)
-        if (j < kk && p[j] >= 0) dl_perm[p[j]] = dl[j];
-    }
-    float acc[kPer];
+        rows[j] = dxp ? dxp[static_cast<int64_t>(max(p[j], 0)) * vpr + c] : make_uint4(0u, 0u, 0u, 0u);
+      float acc[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+      for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (j >= kk || !dxp || p[j] < 0) continue;
-      float r[kPer];
-      unpack16(rows[j], r, TA{});
+      for (int j = 0; j < KM; ++j) {
+        if (!dxp || p[j] < 0) continue;
+        float r[kPer];
+        unpack16(rows[j], r, TA{});
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] += r[i];
-    }
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (j >= kk || e[j] < 0 || e[j] >= E) continue;
-      const float* wp = wl + e[j] * bc + cl * kPer;
-#pragma unroll
-      for (int i = 0; i < kPer; i += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wp + i);
-        acc[i] = fmaf(dl[j], w4.x, acc[i]);
-        acc[i + 1] = fmaf(dl[j], w4.y, acc[i + 1]);
-        acc[i + 2] = fmaf(dl[j], w4.z, acc[i + 2]);
-        acc[i + 3] = fmaf(dl[j], w4.w, acc[i + 3]);
+        for (int q = 0; q < kPer; ++q) acc[q] += r[q];
       }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (e[j] < 0) continue;
+        const float* wp = wl + e[j] * bc + cl * kPer;
+#pragma unroll
+        for (int q = 0; q < kPer; q += 4) {
+          const float4 w4 = *reinterpret_cast<const float4*>(wp + q);
+          acc[q] = fmaf(dl[j], w4.x, acc[q]);
+          acc[q + 1] = fmaf(dl[j], w4.y, acc[q + 1]);
+          acc[q + 2] = fmaf(dl[j], w4.z, acc[q + 2]);
+          acc[q + 3] = fmaf(dl[j], w4.w, acc[q + 3]);
+        }
+      }
+      dx[(b0 + i) * vpr + c] = pack16(acc, TA{});
     }
-    dx[v] = pack16(acc, TA{});
   }
 }
 
-// Router-row columns per dX workgroup: 64, so that the staged block (E x 64
+// Router-row columns per dX workgroup: 64 (32 past 128 experts), so that the staged block (E x 64
 // fp32: 16 KB at E = 64) leaves room for several workgroups per CU, whose
 // gathered row loads are what keeps HBM busy.
 constexpr int kDxCols = 64;
@@ -540,13 +571,17 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
     const int elem = (dm.act == MOE_BF16) ? 2 : 4;
     const int32_t vpr = dm.d * elem / 16;
     // column blocks x token ranges
-    const int bc = kDxCols;
+    const int bc = dm.E <= 128 ? kDxCols : kDxCols / 2;   // router block <= 32 KB
     const int ncb = dm.d / bc;
     constexpr int kCUs = 256;   // MI355X: about 8 workgroups per CU
     const int64_t want = std::max<int64_t>(1, (8 * kCUs + ncb - 1) / ncb);
     const int64_t tpw = std::max<int64_t>((dm.T + want - 1) / want, 1);
     const dim3 grid(ncb, static_cast<unsigned>((dm.T + tpw - 1) / tpw));
-    const size_t lds = static_cast<size_t>(dm.E) * bc * sizeof(float);
+    // the router block, then the slot table (3 words per slot of a batch):
+    // at most 32 KB + 24 KB
+    const int km = (dm.k == 1 || dm.k == 2 || dm.k == 4 || dm.k == 6 || dm.k == 8) ? dm.k : 16;
+    const size_t lds = (static_cast<size_t>(dm.E) * bc + 3 * static_cast<size_t>(km) * dx_batch(km)) *
+                       sizeof(float);
     const uint4* dxp = static_cast<const uint4*>(dx_perm);
     uint4* dxo = static_cast<uint4*>(dx);
 #define MOE_DX(TA, KC)                                                                        \
