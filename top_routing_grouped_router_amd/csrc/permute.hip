@@ -5,8 +5,9 @@
 // Speed-Accuracy Comparisons" (Sec. 2.2: GShard dispatch, where a token's slot
 // inside an expert is the running count of earlier tokens that chose it).
 //
-// A stable counting sort in three small kernels plus one row mover (for rows
-// of at most 1 KB, steps 2-4 run as one kernel, perm_scatter_gather_kernel):
+// A stable counting sort in three small kernels plus one row mover (with at
+// most 128 blocks, for rows of at most 1 KB or the plan alone, steps 2-4 run
+// as one kernel, perm_scatter_gather_kernel):
 //   1. hist:    block b (256 tokens) counts its assignments per expert (LDS
 //               integer atomics, exact);
 //   2. scan:    one workgroup turns the [blocks, E] counts into expert counts,
@@ -183,15 +184,15 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
   }
 }
 
-// Scan, scatter and gather in one kernel (rows of at most 1 KB).  Workgroup
-// (b, q) (256 threads; q < kSgSplit) rebuilds, from the [nb, E] block counts,
-// the expert totals and block b's prefix (LDS integer atomics: exact,
-// order-free), scans the totals into expert offsets (workgroup (0, 0)
-// publishes counts and offsets), ranks the 256 tokens of block b with the LDS
-// bitmap like perm_scatter_kernel, writes pos/src for its quarter of them and
-// copies their rows once from X to each token's k rows of x_perm.  The
-// redundant scan and ranking are cheap; the split spreads the copy over 4 nb
-// workgroups.
+// Scan, scatter and gather in one kernel (rows of at most 1 KB, or the plan
+// alone).  Workgroup (b, q) (256 threads; q < kSgSplit) rebuilds, from the
+// [nb, E] block counts, the expert totals and block b's prefix (LDS integer
+// atomics: exact, order-free), scans the totals into expert offsets
+// (workgroup (0, 0) publishes counts and offsets), ranks the 256 tokens of
+// block b with the LDS bitmap like perm_scatter_kernel, writes pos/src for its
+// quarter of them and copies their rows once from X to each token's k rows of
+// x_perm.  The redundant scan and ranking are cheap; the split spreads the
+// copy over 4 nb workgroups.
 constexpr int kSgSplit = 4;
 constexpr int kSgTok = kPermBlock / kSgSplit;
 constexpr int kSgMaxBlocks = 128;
@@ -236,13 +237,21 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t run = 0;
-    for (int e = 0; e < E; ++e) {
-      base[e] = run;
-      run += tot[e];
+  if (tid < 64) {   // exclusive scan of the totals by wavefront 0, 64 experts at a time
+    int32_t carry = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + tid;
+      const int32_t v = (e < E) ? tot[e] : 0;
+      int32_t incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off, 64);
+        if (tid >= off) incl += o;
+      }
+      if (e < E) base[e] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
     }
-    base[E] = run;
+    if (tid == 0) base[E] = carry;
   }
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -334,10 +343,12 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
     hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
                        ws_hist);
   }
-  // short rows and few blocks: scan, scatter and gather fused (every one of
-  // the 4 nb workgroups reads the whole [nb, E] block histogram, so the fused
-  // form is kept to nb <= 128, T <= 32768)
-  if (nb > 0 && nb <= kSgMaxBlocks && dm.d * elem <= 1024 && dm.k <= kMaxK) {
+  // few blocks, and short rows or no rows to move (the plan only): scan,
+  // scatter and gather fused (every one of the 4 nb workgroups reads the
+  // whole [nb, E] block histogram, so the fused form is kept to nb <= 128,
+  // T <= 32768)
+  const bool rows = x && x_perm;
+  if (nb > 0 && nb <= kSgMaxBlocks && (!rows || dm.d * elem <= 1024) && dm.k <= kMaxK) {
     hipLaunchKernelGGL(perm_scatter_gather_kernel, dim3(nb * kSgSplit), dim3(kThreads), 0, s, idx, dm.T,
                        dm.k, dm.E, ws_hist, static_cast<int32_t>(nb), counts, offsets, pos, src,
                        static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr, gate,
@@ -350,7 +361,7 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k,
                        dm.E, ws_base, pos, src, gate, gate_perm);
   }
-  if (x && x_perm && dm.T > 0) {
+  if (rows && dm.T > 0) {
     const int64_t total = dm.T * vpr;
     const int64_t blocks = std::min<int64_t>((total + kThreads - 1) / kThreads, 1 << 16);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(kThreads), 0, s,
