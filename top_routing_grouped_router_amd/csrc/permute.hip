@@ -7,7 +7,8 @@
 //
 // A stable counting sort in three small kernels plus one row mover (with at
 // most 128 blocks, for rows of at most 1 KB or the plan alone, steps 2-4 run
-// as one kernel, perm_scatter_gather_kernel):
+// as one kernel, perm_scatter_gather_kernel, which with at most 8192
+// assignments also does step 1 itself):
 //   1. hist:    block b (256 tokens) counts its assignments per expert (LDS
 //               integer atomics, exact);
 //   2. scan:    one workgroup turns the [blocks, E] counts into expert counts,
@@ -186,8 +187,8 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 
 // Scan, scatter and gather in one kernel (rows of at most 1 KB, or the plan
 // alone).  Workgroup (b, q) (256 threads; q < kSgSplit) rebuilds, from the
-// [nb, E] block counts, the expert totals and block b's prefix (LDS integer
-// atomics: exact, order-free), scans the totals into expert offsets
+// [nb, E] block counts (or, hist == NULL, from the ids themselves), the expert
+// totals and block b's prefix (LDS integer atomics: exact, order-free), scans the totals into expert offsets
 // (workgroup (0, 0) publishes counts and offsets), ranks the 256 tokens of
 // block b with the LDS bitmap like perm_scatter_kernel, writes pos/src for its
 // quarter of them and copies their rows once from X to each token's k rows of
@@ -196,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
 constexpr int kSgSplit = 4;
 constexpr int kSgTok = kPermBlock / kSgSplit;
 constexpr int kSgMaxBlocks = 128;
+constexpr int64_t kSgNoHist = 8192;   // assignments up to which no histogram kernel runs
 __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
     const int32_t* __restrict__ idx, int64_t T, int32_t k, int32_t E,
     const int32_t* __restrict__ hist, int32_t nb, int32_t* __restrict__ counts,
@@ -216,7 +218,26 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
   }
   if (tid == 0) dup = 0;
   __syncthreads();
-  {
+  if (!hist) {
+    // few assignments, no block counts: the totals and block b's prefix
+    // straight from the ids
+    const int64_t n = T * k, nb_pre = static_cast<int64_t>(b) * kPermBlock * k;
+    constexpr int kU = 8;
+    for (int64_t i0 = tid; i0 < n; i0 += kThreads * kU) {
+      int32_t v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kThreads;
+        v[u] = (i < n) ? idx[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (v[u] < 0 || v[u] >= E) continue;
+        atomicAdd(&tot[v[u]], 1);
+        if (i0 + u * kThreads < nb_pre) atomicAdd(&pre[v[u]], 1);
+      }
+    }
+  } else {
     const int64_t n = static_cast<int64_t>(nb) * E;
     constexpr int kU = 8;
     for (int64_t i0 = tid; i0 < n; i0 += kThreads * kU) {
@@ -339,18 +360,23 @@ hipError_t launch_permute(const moe_dims& dm, const int32_t* idx, int32_t* count
   const int64_t nb = (dm.T + kPermBlock - 1) / kPermBlock;
   const int elem = (dm.act == MOE_BF16) ? 2 : 4;
   const int32_t vpr = dm.d * elem / 16;
-  if (nb > 0) {
-    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
-                       ws_hist);
-  }
   // few blocks, and short rows or no rows to move (the plan only): scan,
   // scatter and gather fused (every one of the 4 nb workgroups reads the
   // whole [nb, E] block histogram, so the fused form is kept to nb <= 128,
-  // T <= 32768)
+  // T <= 32768); with at most kSgNoHist assignments each of them counts the
+  // ids itself and the histogram kernel is skipped
   const bool rows = x && x_perm;
-  if (nb > 0 && nb <= kSgMaxBlocks && (!rows || dm.d * elem <= 1024) && dm.k <= kMaxK) {
+  const bool fused = nb > 0 && nb <= kSgMaxBlocks && (!rows || dm.d * elem <= 1024) &&
+                     dm.k <= kMaxK;
+  const bool no_hist = fused && dm.T * dm.k <= kSgNoHist;
+  if (nb > 0 && !no_hist) {
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nb), dim3(kThreads), 0, s, idx, dm.T, dm.k, dm.E,
+                       ws_hist);
+  }
+  if (fused) {
     hipLaunchKernelGGL(perm_scatter_gather_kernel, dim3(nb * kSgSplit), dim3(kThreads), 0, s, idx, dm.T,
-                       dm.k, dm.E, ws_hist, static_cast<int32_t>(nb), counts, offsets, pos, src,
+                       dm.k, dm.E, no_hist ? nullptr : ws_hist, static_cast<int32_t>(nb), counts,
+                       offsets, pos, src,
                        static_cast<const uint4*>(x), static_cast<uint4*>(x_perm), vpr, gate,
                        gate_perm);
     return hipGetLastError();
