@@ -42,3 +42,43 @@ def test_route_paths(name):
     inp = make_layer_inputs(cfg, seed=400 + list(CASES).index(name), parts=("x", "wr"))
     layer = MoELayer(T, d, E, 64, k, act_torch("bf16"), n_groups=G)
     check_route(layer, inp["x"], inp["wr"], k, G=G)
+
+
+BWD_CASES = {
+    # name: (T, d, E, k)   -- bf16 X, d >= 1024: the router weight gradient on
+    # the matrix cores (16, 32 and 64 expert rows; k compiled and runtime)
+    "d1024_E5_k1": (777, 1024, 5, 1),
+    "d1024_E20_k3_ragged_T": (1000, 1024, 20, 3),
+    "d2048_E33_k8": (2048, 2048, 33, 8),
+    "d1280_E64_k10": (1500, 1280, 64, 10),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_router_backward_wide_rows(name):
+    """dWr and dX of a layer step on the oracle's routing, against the exact
+    fp64 oracle within the first-order error bounds and the bf16 tolerance."""
+    from _parity import exact_reference, layer_floats, oracle_routing
+    from _util import TOL, check_floats, dev
+    import numpy as np
+    import torch
+
+    T, d, E, k = BWD_CASES[name]
+    print(f"\n[case] router backward {name}", flush=True)
+    cfg = get_config("c2", T=T, d=d, E=E, f=64, k=k, act="bf16", x_kind="normal",
+                     backward=True)
+    inp = make_layer_inputs(cfg, seed=500 + list(BWD_CASES).index(name))
+    probe = MoELayer(T, d, E, 64, k, torch.bfloat16)
+    o_route, _ = check_route(probe, inp["x"], inp["wr"], k)
+    routing = (o_route["topk_idx"], o_route["gates"].astype(np.float32))
+    layer = MoELayer(T, d, E, 64, k, torch.bfloat16)
+    t = {key: dev(v, torch.bfloat16) for key, v in inp.items() if key != "wr"}
+    t["wr"] = dev(inp["wr"], torch.float32)
+    layer.forward(t["x"], t["wr"], t["w1"], t["w3"], t["w2"], routing=oracle_routing(o_route))
+    layer.backward(t["dy"], t["x"], t["wr"], t["w1"], t["w3"], t["w2"])
+    torch.cuda.synchronize()
+    o_f, o_b, B = exact_reference(inp, k, routing, act="bf16")
+    got, ex, bd = layer_floats(layer, o_f, o_b, B)
+    keys = ("dwr", "dx")
+    check_floats(f"route bwd {name}", {q: got[q] for q in keys}, {q: ex[q] for q in keys},
+                 {q: bd[q] for q in keys}, TOL["bf16"], ())

@@ -187,6 +187,12 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const float* dgate_part = nullptr, int32_t nparts = 0,
                             float* dgate_out = nullptr);
 int route_bwd_splits(const moe_dims& dm);   // row splits per expert for the router weight gradient
+// the router weight gradient on the matrix cores (dl in token-slot order in
+// ws_dl_sel, route_bwd_mfma_splits token splits: partials E x splits x d)
+bool route_bwd_mfma_ok(const moe_dims& dm);
+int route_bwd_mfma_ld(const moe_dims& dm);
+int64_t route_bwd_mfma_len(const moe_dims& dm);
+int route_bwd_mfma_splits(const moe_dims& dm);
 // dense form: dropped assignments and the auxiliary losses
 hipError_t launch_route_bwd_dense(const moe_dims& dm, const void* x, const float* wr,
                                   const float* logits, const int32_t* idx, const float* gate,

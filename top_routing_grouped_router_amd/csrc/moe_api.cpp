@@ -189,7 +189,9 @@ RouteBwdWs route_bwd_ws(const moe_dims& dm, void* ws) {
   RouteBwdWs r;
   r.dl_perm = c.take<float>(ws, std::max<int64_t>(R, 1));
   r.dl_sel = c.take<float>(ws, std::max<int64_t>(R, 1));
-  r.partial = c.take<float>(ws, static_cast<int64_t>(dm.E) * moe::route_bwd_splits(dm) * dm.d);
+  const bool mfma = moe::route_bwd_mfma_ok(dm);
+  const int64_t splits = mfma ? moe::route_bwd_mfma_splits(dm) : moe::route_bwd_splits(dm);
+  r.partial = c.take<float>(ws, static_cast<int64_t>(dm.E) * splits * dm.d);
   r.bytes = c.off;
   return r;
 }

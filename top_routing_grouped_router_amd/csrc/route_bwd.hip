@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
     const float* __restrict__ dgate, const float* __restrict__ wr, uint4* __restrict__ dx,
     float* __restrict__ dl_perm, int64_t T, int32_t vpr, int32_t d, int32_t k, int32_t E,
     const float* __restrict__ dgate_part, int32_t nparts, float* __restrict__ dgate_out,
-    int32_t bc, int32_t tok_per_wg) {
+    int32_t bc, int32_t tok_per_wg, float* __restrict__ dl_tok) {
   // [E][bc] router block, then the batch's slot table [KM][kBatch] x 3
   extern __shared__ __attribute__((aligned(16))) float wl[];
   constexpr int kPer = Act<TA>::kPer16B;
@@ -118,14 +118,21 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
 #pragma unroll
         for (int j = 0; j < KM; ++j)
           if (j < kk) inner = fmaf(g[j], dg[j], inner);
+        float dlv[KM];
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
           const float dl = g[j] * (dg[j] - inner);
           const bool live = j < kk;
+          dlv[j] = dl;
           if (first_block && live && p[j] >= 0) dl_perm[p[j]] = dl;
           tab_p[j * kBatch + threadIdx.x] = live ? p[j] : -1;
           tab_e[j * kBatch + threadIdx.x] = (live && e[j] >= 0 && e[j] < E) ? e[j] : -1;
           tab_dl[j * kBatch + threadIdx.x] = dl;
+        }
+        if (dl_tok && first_block) {   // dl in token-slot order, for the dWr kernel
+#pragma unroll
+          for (int j = 0; j < KM; ++j)
+            if (j < kk) dl_tok[t * kk + j] = dlv[j];
         }
       }
     }
@@ -252,6 +259,175 @@ __global__ __launch_bounds__(kThreads) void router_dwr_partial_kernel(
       out[i] = ((red[0][lane * 4 + i] + red[1][lane * 4 + i]) + red[2][lane * 4 + i]) +
                red[3][lane * 4 + i];
   }
+}
+
+// dWr on the matrix cores (bf16 X, E <= 64), from the logit gradient in
+// token-slot order (dl_tok [T][k] with the ids idx [T][k]):
+//   partial[e][s][c] = sum over the tokens t of split s of dl[t][e] X[t][c],
+// dl[t][e] the sum of dl_tok over the token's slots that chose e (zero for the
+// rest; a repeated id adds in slot order).  The thread of (token, 8-expert
+// piece) builds that piece of a chunk's dl rows in LDS, split exactly into
+// three bf16 parts (hi + mid + lo = dl), so every bf16 x bf16 product is exact
+// in fp32 and the three parts accumulate in fp32 (in chunk order, hi, mid, lo
+// within a chunk).  Workgroup (128-column
+// block, token split): the split's tokens go in chunks of 32 (the K of one
+// v_mfma_f32_16x16x32_bf16); a chunk's X rows and the three parts of its dl
+// rows sit in LDS token-major (rows padded by 16 bytes),
+// and the fragments (8 consecutive tokens of one column or one expert) come
+// from the gfx950 transposing LDS read: within each 16-lane group, lane s
+// reads 8 bytes of row s / 4 at column 4 (s % 4), and lane j receives column
+// j of the four rows.  Wavefront w owns columns 32 w ... 32 w + 31 and every
+// expert block.  The next chunk's global loads are in registers while the
+// current one runs (two LDS buffers, one barrier per chunk).
+constexpr int kDwBN = 128;                 // columns per workgroup
+constexpr int kDwChunk = 32;               // tokens per chunk
+constexpr int kDwXs = kDwBN * 2 + 16;      // X tile row stride (bytes)
+typedef short dw_v4s __attribute__((ext_vector_type(4)));
+typedef short dw_v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 dw_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float dw_f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dw_v4s* dw_lds_v4s_t;
+
+__device__ __forceinline__ dw_bf16x8 dw_tr_frag(const unsigned char* lds, uint32_t lo,
+                                                uint32_t hi) {
+  const dw_v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds_v4s_t)(lds + lo));
+  const dw_v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((dw_lds_v4s_t)(lds + hi));
+  const dw_v8s both = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(dw_bf16x8, both);
+}
+
+template <int NT, int K>   // E <= 16 NT; K = k (0: runtime k <= 16)
+__global__ __launch_bounds__(kThreads) void router_dwr_mfma_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ idx, const float* __restrict__ dl,
+    float* __restrict__ partial, int64_t T, int32_t d, int32_t n_experts, int32_t k, int32_t S,
+    int32_t L) {
+  constexpr int KM = K > 0 ? K : 16;
+  constexpr int kM = 16 * NT;                     // experts, zero-padded
+  constexpr int kAs = kM * 2 + 16;                // dl-part tile row stride (bytes)
+  constexpr int kXB = kDwChunk * kDwXs;
+  constexpr int kAB = kDwChunk * kAs;
+  constexpr int kBuf = kXB + 3 * kAB;
+  constexpr int kXv = kDwChunk * kDwBN / 8 / kThreads;         // 16-byte X pieces per thread (2)
+  constexpr int kPc = kM / 8;                                  // 8-expert pieces of a dl row
+  constexpr int kAct = kDwChunk * kPc;                         // threads building dl rows
+  const int kk = K > 0 ? K : k;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int n0 = blockIdx.x * kDwBN;
+  const int sp = blockIdx.y;
+  const int64_t t_lo = static_cast<int64_t>(sp) * L;
+  const int64_t t_hi = min<int64_t>(T, t_lo + L);
+  const int nch = static_cast<int>((t_hi - t_lo + kDwChunk - 1) / kDwChunk);
+
+  uint4 xr[kXv];
+  int32_t ir[KM];
+  float vr[KM];
+  auto load = [&](int ch) {   // rows past t_hi read as zeros, their ids as -1
+    const int64_t tb = t_lo + static_cast<int64_t>(ch) * kDwChunk;
+#pragma unroll
+    for (int i = 0; i < kXv; ++i) {
+      const int v = tid + i * kThreads;
+      const int64_t t = tb + v / (kDwBN / 8);
+      xr[i] = (t < t_hi) ? *reinterpret_cast<const uint4*>(x + t * d + n0 + (v % (kDwBN / 8)) * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const int64_t t = tb + tid / kPc;
+    const bool ok = tid < kAct && t < t_hi;
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      ir[j] = (ok && j < kk) ? idx[t * kk + j] : -1;
+      vr[j] = (ok && j < kk) ? dl[t * kk + j] : 0.f;
+    }
+  };
+  auto store = [&](unsigned char* buf) {
+#pragma unroll
+    for (int i = 0; i < kXv; ++i) {
+      const int v = tid + i * kThreads;
+      *reinterpret_cast<uint4*>(buf + (v / (kDwBN / 8)) * kDwXs + (v % (kDwBN / 8)) * 16) = xr[i];
+    }
+    if (tid < kAct) {
+      // experts 8 q ... 8 q + 7 of the chunk's token row: the sum of the
+      // slots that chose each (slot order), then its three bf16 parts
+      const int row = tid / kPc, q = tid % kPc;
+      float w[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (ir[j] == 8 * q + z) v += vr[j];
+        w[z] = v;
+      }
+      uint32_t h[4], m[4], l[4];
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        h[p2] = bf16x2_rne(w[2 * p2], w[2 * p2 + 1]);
+        const float r0 = w[2 * p2] - __uint_as_float(h[p2] << 16);
+        const float r1 = w[2 * p2 + 1] - __uint_as_float(h[p2] & 0xFFFF0000u);
+        m[p2] = bf16x2_rne(r0, r1);
+        l[p2] = bf16x2_rne(r0 - __uint_as_float(m[p2] << 16),
+                           r1 - __uint_as_float(m[p2] & 0xFFFF0000u));
+      }
+      unsigned char* a = buf + kXB + row * kAs + q * 16;
+      *reinterpret_cast<uint4*>(a) = make_uint4(h[0], h[1], h[2], h[3]);
+      *reinterpret_cast<uint4*>(a + kAB) = make_uint4(m[0], m[1], m[2], m[3]);
+      *reinterpret_cast<uint4*>(a + 2 * kAB) = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+  };
+  // transposing-read addresses within a buffer: rows 8 g + (c >> 2) (+ 4 for
+  // the second half), column 4 (c & 3) of the fragment's 16
+  const int r0 = 8 * g + (c >> 2);
+  uint32_t bx[2], ba[NT];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) bx[nb] = r0 * kDwXs + (32 * wave + 16 * nb + 4 * (c & 3)) * 2;
+#pragma unroll
+  for (int mb = 0; mb < NT; ++mb) ba[mb] = kXB + r0 * kAs + (16 * mb + 4 * (c & 3)) * 2;
+
+  dw_f32x4 acc[NT][2];
+#pragma unroll
+  for (int mb = 0; mb < NT; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = dw_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  store(lds);
+  if (nch > 1) load(1);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const unsigned char* cur = lds + (ch & 1) * kBuf;
+    if (ch + 1 < nch) {
+      store(lds + ((ch + 1) & 1) * kBuf);   // the other buffer: read two barriers ago
+      if (ch + 2 < nch) load(ch + 2);
+    }
+    dw_bf16x8 fb[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) fb[nb] = dw_tr_frag(cur, bx[nb], bx[nb] + 4 * kDwXs);
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+#pragma unroll
+      for (int mb = 0; mb < NT; ++mb) {
+        const uint32_t o = ba[mb] + part * kAB;
+        const dw_bf16x8 fa = dw_tr_frag(cur, o, o + 4 * kAs);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // lane (g, c) of block (mb, nb): experts 16 mb + 4 g + q, column 32 w + 16 nb + c
+#pragma unroll
+  for (int mb = 0; mb < NT; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 16 * mb + 4 * g + q;
+        if (e < n_experts)
+          partial[(static_cast<int64_t>(e) * S + sp) * d + n0 + 32 * wave + 16 * nb + c] =
+              acc[mb][nb][q];
+      }
 }
 
 // Adds the per-split partial sums of dWr.  Workgroup (column block of 64,
@@ -554,6 +730,33 @@ __global__ __launch_bounds__(kThreads) void router_dwr_dense_partial_kernel(
 
 }  // namespace
 
+// the router weight gradient on the matrix cores: bf16 X, E <= 64, d a
+// multiple of 128 from 1024 (on narrower rows the per-expert kernel's k-fold
+// reads of X cost less than this kernel's chunk loop and partial sums); dl
+// rows of route_bwd_mfma_ld experts, token splits of route_bwd_mfma_len tokens
+// (about 512 workgroups, and no more partial sums than X has bytes)
+bool route_bwd_mfma_ok(const moe_dims& dm) {
+  return dm.act == MOE_BF16 && dm.E <= 64 && dm.d % kDwBN == 0 && dm.d >= 1024 && dm.T > 0;
+}
+int route_bwd_mfma_ld(const moe_dims& dm) {
+  const int nt = (dm.E + 15) / 16;
+  return 16 * (nt <= 1 ? 1 : nt <= 2 ? 2 : 4);
+}
+int64_t route_bwd_mfma_len(const moe_dims& dm) {
+  const int64_t ncb = std::max(dm.d / kDwBN, 1);
+  int64_t s0 = std::max<int64_t>(1, (512 + ncb - 1) / ncb);
+  s0 = std::min<int64_t>(s0, std::max<int64_t>(1, dm.T / (2 * dm.E)));
+  int64_t len = (dm.T + s0 - 1) / s0;
+  len = std::max<int64_t>(kDwChunk, (len + kDwChunk - 1) / kDwChunk * kDwChunk);
+  // at most 256 splits (the reduction's limit)
+  const int64_t min_len = (dm.T + 255) / 256;
+  if (len < min_len) len = (min_len + kDwChunk - 1) / kDwChunk * kDwChunk;
+  return len;
+}
+int route_bwd_mfma_splits(const moe_dims& dm) {
+  return static_cast<int>((dm.T + route_bwd_mfma_len(dm) - 1) / route_bwd_mfma_len(dm));
+}
+
 // row splits per expert for the router weight gradient: about 2048 workgroups
 int route_bwd_splits(const moe_dims& dm) {
   const int64_t base = static_cast<int64_t>(dm.E) * ((dm.d + 255) / 256);
@@ -567,6 +770,9 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
                             const void* dx_perm, void* dx, float* dwr, float* ws_dl_perm,
                             float* ws_dl_sel, float* ws_partial, hipStream_t s,
                             const float* dgate_part, int32_t nparts, float* dgate_out) {
+  // the matrix-core weight gradient reads dl in token-slot order (ws_dl_sel)
+  const bool mfma = route_bwd_mfma_ok(dm);
+  float* const dl_tok = mfma ? ws_dl_sel : nullptr;
   if (dm.T > 0) {
     const int elem = (dm.act == MOE_BF16) ? 2 : 4;
     const int32_t vpr = dm.d * elem / 16;
@@ -588,11 +794,13 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
   if (dgate_part)                                                                             \
     hipLaunchKernelGGL((router_dx_kernel<TA, KC, true>), grid, dim3(kThreads), lds, s,        \
                        dxp, pos, idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k, \
-                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw));    \
+                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw),     \
+                       dl_tok);                                                                \
   else                                                                                        \
     hipLaunchKernelGGL((router_dx_kernel<TA, KC, false>), grid, dim3(kThreads), lds, s, dxp,  \
                        pos, idx, gate, dgate, wr, dxo, ws_dl_perm, dm.T, vpr, dm.d, dm.k,     \
-                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw))
+                       dm.E, dgate_part, nparts, dgate_out, bc, static_cast<int32_t>(tpw),     \
+                       dl_tok)
     if (dm.act == MOE_BF16) {
       switch (dm.k) {
         case 1: MOE_DX(bf16_t, 1); break;
@@ -613,6 +821,34 @@ hipError_t launch_route_bwd(const moe_dims& dm, const void* x, const float* wr,
       }
     }
 #undef MOE_DX
+  }
+  if (mfma) {
+    const int S = route_bwd_mfma_splits(dm);
+    const int32_t L = static_cast<int32_t>(route_bwd_mfma_len(dm));
+    const dim3 g1(dm.d / kDwBN, S);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+#define MOE_DW(N, KC)                                                                         \
+  hipLaunchKernelGGL((router_dwr_mfma_kernel<N, KC>), g1, dim3(kThreads), 0, s, xb, idx,       \
+                     dl_tok, ws_partial, dm.T, dm.d, dm.E, dm.k, S, L)
+#define MOE_DW_K(N)                                                  \
+  switch (dm.k) {                                                    \
+    case 1: MOE_DW(N, 1); break;                                     \
+    case 2: MOE_DW(N, 2); break;                                     \
+    case 4: MOE_DW(N, 4); break;                                     \
+    case 6: MOE_DW(N, 6); break;                                     \
+    case 8: MOE_DW(N, 8); break;                                     \
+    default: MOE_DW(N, 0); break;                                    \
+  }
+    switch (route_bwd_mfma_ld(dm)) {
+      case 16: MOE_DW_K(1) break;
+      case 32: MOE_DW_K(2) break;
+      default: MOE_DW_K(4) break;
+    }
+#undef MOE_DW_K
+#undef MOE_DW
+    hipLaunchKernelGGL(router_dwr_reduce_kernel<16>, dim3((dm.d + 63) / 64, dm.E), dim3(kThreads),
+                       0, s, ws_partial, dwr, dm.E, dm.d, S);
+    return hipGetLastError();
   }
   const int splits = route_bwd_splits(dm);
   const dim3 grid((dm.d + 255) / 256, splits, dm.E);
