@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
     }
     uint4 rv[KM];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) rv[j] = rows[static_cast<int64_t>(max(p[j], 0)) * vpr + c];
+    for (int j = 0; j < KM; ++j) rv[j] = ld_nt16(rows + static_cast<int64_t>(max(p[j], 0)) * vpr + c);
     float acc[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4* __restri
 #pragma unroll
       for (int i = 0; i < kPer; ++i) acc[i] = fmaf(g[j], r[i], acc[i]);
     }
-    out[v] = pack16(acc, TA{});
+    st_nt16(out + v, pack16(acc, TA{}));
   }
 }
 
@@ -80,8 +80,8 @@ __global__ __launch_bounds__(kThreads) void combine_bwd_kernel(
     if (p >= 0) {
       for (int c = lane_in; c < vpr; c += L) {
         float a[kPer], b[kPer];
-        unpack16(dy[t * vpr + c], a, TA{});
-        unpack16(yp[p * vpr + c], b, TA{});
+        unpack16(ld_nt16(dy + t * vpr + c), a, TA{});
+        unpack16(ld_nt16(yp + p * vpr + c), b, TA{});
         float s[kPer];
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {

@@ -69,6 +69,17 @@ __device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
                     bf16x2_rne(in[4], in[5]), bf16x2_rne(in[6], in[7]));
 }
 
+// 16-byte load with the nontemporal hint (data read once: streamed past the
+// caches' normal retention)
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt16(const uint4* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt16(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt*>(p));
+}
+
 // v_rcp_f32 instead of a full division (about 1 ulp); exp(-z) = inf gives 0
 __device__ __forceinline__ float sigmoid_f(float z) {
   return __builtin_amdgcn_rcpf(1.0f + __expf(-z));

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void gather_rows_kernel(const uint4* __re
        v += stride) {
     const int64_t t = v / vec_per_row;
     const int32_t c = static_cast<int32_t>(v - t * vec_per_row);
-    const uint4 val = x[v];
+    const uint4 val = ld_nt16(x + v);
     for (int j = 0; j < k; ++j) {
       const int64_t p = pos[t * k + j];
       if (p >= 0) xp[p * vec_per_row + c] = val;

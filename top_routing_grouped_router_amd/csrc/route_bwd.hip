@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
       uint4 rows[KM];
 #pragma unroll
       for (int j = 0; j < KM; ++j)
-        rows[j] = dxp ? dxp[static_cast<int64_t>(max(p[j], 0)) * vpr + c] : make_uint4(0u, 0u, 0u, 0u);
+        rows[j] = dxp ? ld_nt16(dxp + static_cast<int64_t>(max(p[j], 0)) * vpr + c)
+                      : make_uint4(0u, 0u, 0u, 0u);
       float acc[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) acc[q] = 0.f;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void router_dx_kernel(
           acc[q + 3] = fmaf(dl[j], w4.w, acc[q + 3]);
         }
       }
-      dx[(b0 + i) * vpr + c] = pack16(acc, TA{});
+      st_nt16(dx + (b0 + i) * vpr + c, pack16(acc, TA{}));
     }
   }
 }
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void router_dwr_mfma_kernel(
     for (int i = 0; i < kXv; ++i) {
       const int v = tid + i * kThreads;
       const int64_t t = tb + v / (kDwBN / 8);
-      xr[i] = (t < t_hi) ? *reinterpret_cast<const uint4*>(x + t * d + n0 + (v % (kDwBN / 8)) * 8)
+      xr[i] = (t < t_hi) ? ld_nt16(reinterpret_cast<const uint4*>(x + t * d + n0 + (v % (kDwBN / 8)) * 8))
                          : make_uint4(0u, 0u, 0u, 0u);
     }
     const int64_t t = tb + tid / kPc;
