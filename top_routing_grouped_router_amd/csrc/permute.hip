@@ -111,11 +111,25 @@ namespace {
 
 constexpr int kMaxK = 16;
 
-// slot j of a token's row repeats an expert of an earlier slot
-__device__ __forceinline__ bool repeats_earlier_slot(const int32_t* row, int j, int32_t e) {
-  for (int i = 0; i < j; ++i)
-    if (row[i] == e) return true;
-  return false;
+// the ids of token t (-1 past T and past slot k), all loads issued together
+__device__ __forceinline__ void load_row(const int32_t* __restrict__ idx, int64_t t, int64_t T,
+                                         int32_t k, int32_t (&row)[kMaxK]) {
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) row[j] = (t < T && j < k) ? idx[t * k + j] : -1;
+}
+// the token's bit in the LDS bitmap of each expert it chose; dup = 1 when a
+// slot repeats the expert of an earlier slot
+__device__ __forceinline__ void mark_row(const int32_t (&row)[kMaxK], int32_t k, int32_t E, int w,
+                                         int lane, unsigned long long (*bits)[kWords], int* dup) {
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    const int32_t e = row[j];
+    if (j >= k || e < 0 || e >= E) continue;
+    atomicOr(&bits[e][w], 1ull << lane);
+#pragma unroll
+    for (int i = 0; i < j; ++i)
+      if (row[i] == e) *dup = 1;
+  }
 }
 
 // Ranks of every assignment of the block starting at token tb inside its
@@ -151,21 +165,17 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_kernel(
   __syncthreads();
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermBlock + tid;
   const int w = tid >> 6, lane = tid & 63;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
-      if (e >= 0 && e < E) {
-        atomicOr(&bits[e][w], 1ull << lane);
-        if (repeats_earlier_slot(idx + t * k, j, e)) dup = 1;
-      }
-    }
-  }
+  int32_t row[kMaxK];   // the token's ids, loaded once
+  load_row(idx, t, T, k, row);
+  mark_row(row, k, E, w, lane, bits, &dup);
   __syncthreads();
   if (dup) rank_serially(idx, T, k, E, static_cast<int64_t>(blockIdx.x) * kPermBlock, srank);
   if (t < T) {
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int32_t e = row[j];
       if (e < 0 || e >= E) {
         pos[t * k + j] = -1;
         continue;
@@ -284,21 +294,17 @@ __global__ __launch_bounds__(kThreads) void perm_scatter_gather_kernel(
   const int64_t t = static_cast<int64_t>(b) * kPermBlock + tid;
   const int w = tid >> 6, lane = tid & 63;
   const bool live = t < T;
-  if (live) {
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
-      if (e >= 0 && e < E) {
-        atomicOr(&bits[e][w], 1ull << lane);
-        if (repeats_earlier_slot(idx + t * k, j, e)) dup = 1;
-      }
-    }
-  }
+  int32_t row[kMaxK];   // the token's ids, loaded once
+  load_row(idx, t, T, k, row);
+  mark_row(row, k, E, w, lane, bits, &dup);
   __syncthreads();
   if (dup) rank_serially(idx, T, k, E, static_cast<int64_t>(b) * kPermBlock, srank);
   if (live && w == q) {   // this workgroup's quarter: tokens 64 q ... 64 q + 63 of block b
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < k; ++j) {
-      const int32_t e = idx[t * k + j];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j >= k) break;
+      const int32_t e = row[j];
       int32_t p = -1;
       if (e >= 0 && e < E) {
         int32_t rank;
