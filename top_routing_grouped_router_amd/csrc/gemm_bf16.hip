@@ -655,8 +655,8 @@ __global__ __launch_bounds__(Cfg<BIG>::THREADS, 2) void rows_kernel(Args g) {
         const int v = threadIdx.x + NT * it;
         const int r = min(v / CH, rows - 1), c = min(v % CH, nch - 1);   // clamped: in bounds
         const int64_t o = static_cast<int64_t>(m0 + r) * Ndim + n0 + c * 8;
-        aux_a[it] = *reinterpret_cast<const uint4*>(g.aux0 + o);
-        aux_b[it] = *reinterpret_cast<const uint4*>(g.aux1 + o);
+        aux_a[it] = ld_nt16(reinterpret_cast<const uint4*>(g.aux0 + o));
+        aux_b[it] = ld_nt16(reinterpret_cast<const uint4*>(g.aux1 + o));
       }
     }
     // The row swizzle key (r & 15 = lane & 15 for every fragment) goes through
@@ -1582,8 +1582,8 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
       const int rr = v / (BN / 8), c = v % (BN / 8);
       const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
       const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
-      av[ig] = *reinterpret_cast<const uint4*>(g.aux0 + ol);
-      bv[ig] = *reinterpret_cast<const uint4*>(g.aux1 + ol);
+      av[ig] = ld_nt16(reinterpret_cast<const uint4*>(g.aux0 + ol));
+      bv[ig] = ld_nt16(reinterpret_cast<const uint4*>(g.aux1 + ol));
       gr[ig] = g.gate_rows[m0 + rl];
     }
     float partv[kGrp];
@@ -1649,8 +1649,8 @@ __global__ __launch_bounds__(dma64::NT, 1) void dgrad_dma_kernel(Args g) {
         const int rr = v / (BN / 8), c = v % (BN / 8);
         const int rl = min(rr, rows - 1), cl = min(c, nch - 1);   // clamped: in bounds
         const int64_t ol = static_cast<int64_t>(m0 + rl) * Ndim + n0 + cl * 8;
-        av[ig] = *reinterpret_cast<const uint4*>(g.aux0 + ol);
-        bv[ig] = *reinterpret_cast<const uint4*>(g.aux1 + ol);
+        av[ig] = ld_nt16(reinterpret_cast<const uint4*>(g.aux0 + ol));
+        bv[ig] = ld_nt16(reinterpret_cast<const uint4*>(g.aux1 + ol));
       }
 #pragma unroll
       for (int ig = 0; ig < kGrp; ++ig) {
