@@ -404,8 +404,12 @@ moe_status moe_route_bwd_folded(const moe_dims* dims, const void* x, const float
  * dx[t]  = sum_j dx_perm[pos[t,j]] + sum_j dl[t,S_j(t)] w_router[S_j(t)]
  *          (fp32, rounded once to act; the first sum is skipped when
  *          dx_perm == NULL);
- * dw_router[e] = sum over the rows p of expert e (ascending token order) of
- *          dl[src_token[p], e] * x[src_token[p]]   (fp32).
+ * dw_router[e] = sum over the tokens t that chose e of dl[t, e] * x[t]
+ *          (fp32; partial sums over fixed token ranges added in a fixed
+ *          order, so the result is reproducible: over each expert's rows
+ *          in ascending token order, or, for bf16 x with E <= 64 and d a
+ *          multiple of 128 from 1024, over 32-token chunks on the matrix
+ *          cores with dl split exactly into three bf16 parts).
  * x [T,d] act; w_router [E,d]; topk_idx, topk_gate, dgate [T,k];
  * expert_offsets [E+1], pos [T,k], src_token [T*k] from moe_permute;
  * dx_perm [T*k,d] act or NULL; dx [T,d] act; dw_router [E,d] fp32.
