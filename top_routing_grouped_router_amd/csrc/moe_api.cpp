@@ -490,7 +490,7 @@ moe_status moe_route(const moe_dims* dims, const void* x, const float* w_router,
 }
 
 // ---------------------------------------------------------------- allocation-free router
-// moe_route with its scratch (arrival counter, per-tile partial sums) in a
+// moe_route with its scratch (the per-tile partial sums) in a
 // file-scope device array instead of a caller workspace.  Each device holds
 // its own copy of the array; host code never passes the array's name (a host
 // stand-in, not a device address) but the address hipGetSymbolAddress gives
