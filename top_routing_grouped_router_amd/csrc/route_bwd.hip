@@ -8,9 +8,11 @@
 //   dWr[e]     = sum_t dl[t, e] X[t].
 // Three kernels: the dX rows (k expert-gradient rows plus k router rows,
 // summed in fp32 in slot order and rounded once; dl computed per token on the
-// way and scattered into permuted row order), dWr partial sums over contiguous
-// parts of each expert's rows (the permutation lists them in ascending token
-// order), and a fixed-order reduction of the parts.
+// way and written in permuted row order, or in token-slot order for the
+// matrix-core dWr), dWr partial sums (over contiguous parts of each expert's
+// rows, which the permutation lists in ascending token order; or, for bf16 X
+// with E <= 64 and d >= 1024, over token ranges on the matrix cores, reading X
+// once), and a fixed-order reduction of the parts.
 #include "common.h"
 
 namespace moe {
