@@ -233,6 +233,44 @@ def test_dispatch_plan_and_coselect(name):
 
 # ---------------------------------------------------------------- permutation edge cases
 
+@pytest.mark.parametrize("T,E,k,rep", [(2048, 8, 4, False), (2048, 8, 4, True), (2049, 8, 4, False),
+                                         (16384, 64, 6, False), (16384, 64, 6, True),
+                                         (32768, 64, 2, False), (40000, 16, 4, False)])
+def test_plan_with_gates_follows_the_definition(T, E, k, rep):
+    """moe_permute_gates (the plan alone, with the gates carried into row
+    order) on each of its kernel forms, bit for bit against the oracle's plan:
+    up to 8192 assignments one kernel counts the ids itself (T = 2048, k = 4),
+    above it a histogram kernel comes first (T = 2049), up to 128 blocks of 256
+    tokens the scan and scatter are one kernel (T = 16384, 32768), beyond
+    that they are separate (T = 40000).  rep: some tokens repeat an expert
+    (outside the routing contract; every slot still gets its own row)."""
+    _announce(f"plan with gates T={T} E={E} k={k} repeats={rep}")
+    from synth import make_routing
+    idx = make_routing(T, E, k, seed=T + k).astype(np.int32)
+    g = stream(78, T)
+    if rep:
+        rows = g.choice(T, size=max(3, T // 50), replace=False)
+        idx[rows, 1] = idx[rows, 0]
+    gate = g.random((T, k)).astype(np.float32)
+    plan = O.permute_plan(idx, E)
+    R = T * k
+    dims = M.make_dims(T, 64, E, 64, k, torch.bfloat16)
+    ws = M.alloc_workspace(dims, 1)
+    out = {n: torch.full(sh, -7, dtype=torch.int32, device="cuda") for n, sh in
+           (("counts", (E,)), ("offsets", (E + 1,)), ("pos", (T, k)), ("src", (R,)))}
+    gp = torch.full((R,), -1.0, device="cuda")
+    M.moe_permute_gates(dims, dev(idx, torch.int32), dev(gate, torch.float32), out["counts"],
+                        out["offsets"], out["pos"], out["src"], gp, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out["counts"]), plan["counts"])
+    assert np.array_equal(host(out["offsets"]), plan["offsets"])
+    assert np.array_equal(host(out["pos"]), plan["pos"])
+    assert np.array_equal(host(out["src"]), plan["src"])
+    want = np.zeros(R, np.float32)
+    want[plan["pos"].reshape(-1)] = gate.reshape(-1)
+    assert np.array_equal(host(gp), want)
+
+
 @pytest.mark.parametrize("T,E,k", [(1000, 8, 3), (40000, 16, 4)])
 def test_permute_follows_the_definition_with_repeated_ids(T, E, k):
     """A token that lists an expert twice is outside the routing contract, but

@@ -51,6 +51,8 @@ BWD_CASES = {
     "d1024_E20_k3_ragged_T": (1000, 1024, 20, 3),
     "d2048_E33_k8": (2048, 2048, 33, 8),
     "d1280_E64_k10": (1500, 1280, 64, 10),
+    "d1024_E8_one_token": (1, 1024, 8, 2),
+    "d2048_E64_31_tokens": (31, 2048, 64, 6),
 }
 
 
@@ -80,5 +82,9 @@ def test_router_backward_wide_rows(name):
     o_f, o_b, B = exact_reference(inp, k, routing, act="bf16")
     got, ex, bd = layer_floats(layer, o_f, o_b, B)
     keys = ("dwr", "dx")
+    # with only a few tokens per expert (T k < 64 E) each dWr row sums a few
+    # terms of random sign, and the bf16 rounding upstream of dl (dgate from
+    # bf16 rows) moves it by about 2e-2 of the row: held to the bound alone
+    bound_only = ("dwr",) if T * k < 64 * E else ()
     check_floats(f"route bwd {name}", {q: got[q] for q in keys}, {q: ex[q] for q in keys},
-                 {q: bd[q] for q in keys}, TOL["bf16"], ())
+                 {q: bd[q] for q in keys}, TOL["bf16"], bound_only)
