@@ -896,29 +896,38 @@ __device__ __forceinline__ void wait_vm() {
 // The big UP/DOWN tile with 64-wide k steps: each row of a stage is 128 bytes,
 // a whole cache line, so every line of A and B is requested from L2 once (with
 // 32-wide steps each line is requested twice, half per step: measured 2.3x the
-// requests and 6% slower).  Two stages of 64 KB; the 16-byte chunks of a row
-// are XORed with (row >> 1) & 7, so any 16 consecutive rows read at one
-// logical chunk (a fragment read) hit distinct banks; the DMA writes carry
-// the same swizzle in their global addresses.
+// requests and 6% slower).  A ring of five 32 KB slots, each holding the A or
+// the B operand of one step, keeps about a step and a half of fills in flight
+// across every barrier (two 64 KB stages drained the fills once per step: UP
+// measured 2-3% slower at C5).  The 16-byte chunks of a row are XORed with
+// (row >> 1) & 7, so any 16 consecutive rows read at one logical chunk (a
+// fragment read) hit distinct banks; the DMA writes carry the same swizzle in
+// their global addresses.
 namespace dma64 {
 constexpr int BM = 256, BN = 256, BKS = 64, NST = 2, NT = 512, WAVES_N = 4, FM = 4, FN = 2;
 constexpr int kStage = (BM + BN) * BKS;   // elements per stage (64 KB)
+constexpr int kSlot = BM * BKS;           // one operand of a step (32 KB)
+constexpr int kSlots = 5;                 // the ring of the UP/DOWN tile (160 KB)
 }  // namespace dma64
 
 template <int MODE, bool FOLD = false>
 __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
   using namespace dma64;
   static_assert(MODE == UP || MODE == DOWN, "k-contiguous modes only");
-  __shared__ __attribute__((aligned(16))) bf16_t lds[NST * kStage];
-  __shared__ int tile_info[3];
+  static_assert(BM == BN, "A and B parts of a step fill equal slots");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[kSlots * kSlot];
   const int flat = flat_tile();
   const int row_tile = flat / g.n_tiles_n;
   const int nt = flat - row_tile * g.n_tiles_n;
   int e, m0, mend;
-  if (!find_row_tile_at<BM>(tile_info, g.offsets, g.E, row_tile, &e, &m0, &mend)) return;
+  // the lookup's three results pass through the first bytes of the LDS
+  if (!find_row_tile_at<BM>(reinterpret_cast<int*>(lds), g.offsets, g.E, row_tile, &e, &m0,
+                            &mend))
+    return;
   e = __builtin_amdgcn_readfirstlane(e);
   m0 = __builtin_amdgcn_readfirstlane(m0);
   mend = __builtin_amdgcn_readfirstlane(mend);
+  __syncthreads();   // every lane holds them before the first fill lands there
   const int rows = min(BM, mend - m0);
   const int d = g.d, f = g.f;
   constexpr int kUpHalf = BN / 2;
@@ -959,23 +968,27 @@ __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
     bbase = g.b0 + e * E_fd + static_cast<int64_t>(n0) * f;
     b_bytes = (d - n0) * f * 2;
   }
-  auto issue = [&](int kt) {   // step kt into stage kt % 2
-    bf16_t* As = lds + (kt & 1) * kStage;
-    bf16_t* Bs = As + BM * BKS;
-    const int k0 = kt * BKS;
-    const auto ra = rsrc_at(abase + k0, a_rows_bytes - k0 * 2);
-    const auto rb = rsrc_at(bbase + k0, b_bytes - k0 * 2);
+  // half-step h: the A (h even) or B (h odd) operand of step h / 2, four
+  // instructions per wavefront, into ring slot `slot` (h mod 5)
+  auto issue_half = [&](int h, int slot) {
+    bf16_t* dst = lds + slot * kSlot + wave * 32 * BKS;
+    const int k0 = (h >> 1) * BKS;
+    if ((h & 1) == 0) {
+      const auto ra = rsrc_at(abase + k0, a_rows_bytes - k0 * 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma::dma16(ra, As + (wave * 32 + u * 8) * BKS, voa[u]);
+      for (int u = 0; u < 4; ++u) dma::dma16(ra, dst + u * 8 * BKS, voa[u]);
+    } else {
+      const auto rb = rsrc_at(bbase + k0, b_bytes - k0 * 2);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma::dma16(rb, Bs + (wave * 32 + u * 8) * BKS, vob[u]);
+      for (int u = 0; u < 4; ++u) dma::dma16(rb, dst + u * 8 * BKS, vob[u]);
+    }
   };
 
   AccT<true> acc;
   zero_acc<true>(acc);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int r = lane & 31, gq = lane >> 5;
-  // byte addresses (within the stage) of this lane's fragment rows for the
+  // byte addresses (within a slot) of this lane's fragment rows for the
   // four 16-wide sub-steps; fragment i / j adds i * 32 / j * 128 rows, which
   // keeps (row >> 1) & 7 and so the swizzle
   uint32_t a_addr[4], b_addr[4];
@@ -983,7 +996,7 @@ __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
   for (int kk = 0; kk < 4; ++kk) {
     const int pc = (2 * kk + gq) ^ ((r >> 1) & 7);
     a_addr[kk] = ((wm * 32 * FM + r) * BKS + pc * 8) * 2;
-    b_addr[kk] = (BM * BKS + (wn * 32 + r) * BKS + pc * 8) * 2;
+    b_addr[kk] = ((wn * 32 + r) * BKS + pc * 8) * 2;
   }
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) bf16_t*)lds));
@@ -1029,30 +1042,41 @@ __global__ __launch_bounds__(dma64::NT, 1) void dma_rows_kernel(Args g) {
         : "v"(aaddr), "v"(baddr)
         : "memory");
   };
-  auto sbase = [&](int kt) { return lds_base + (kt & 1) * kStage * 2; };
-  // prologue: steps 0 and 1 in flight; kk = 0 fragments of step 0 once landed
-  issue(0);
-  if (nk > 1) {
-    issue(1);
-    dma::wait_vm<8>();
-  } else {
-    dma::wait_vm<0>();
-  }
+  auto slot_addr = [&](int slot) { return lds_base + slot * kSlot * 2; };
+  // A ring of five 32 KB slots, one operand of one step each, so that the
+  // fills never drain: half-step h (the A or B operand of step h / 2) sits in
+  // slot h mod 5.  Prologue: half-steps 0-4 (steps 0 and 1, the A operand of
+  // step 2); the kk = 0 fragments of step 0 once it has landed.
+  const int nh = 2 * nk;
+#pragma unroll
+  for (int h = 0; h < kSlots; ++h)
+    if (h < nh) issue_half(h, h);
+  if (nk >= 3) dma::wait_vm<12>();
+  else if (nk == 2) dma::wait_vm<8>();
+  else dma::wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  read_p(p0, sbase(0) + a_addr[0], sbase(0) + b_addr[0]);
-  // step kt: sub-steps 0-2 of stage kt while reading 1-3; then the barrier
-  // that sees step kt + 1 landed everywhere and stage kt read by everyone,
-  // the DMA of step kt + 2 into stage kt, and sub-step 3 while reading
-  // sub-step 0 of step kt + 1
+  read_p(p0, slot_addr(0) + a_addr[0], slot_addr(1) + b_addr[0]);
+  // step kt (slots sa, sb): sub-steps 0-2 while reading 1-3; then the wait
+  // for step kt + 1 (the A operand of step kt + 2, issued last, may stay in
+  // flight), the barrier that sees step kt + 1 landed everywhere and step kt
+  // read by everyone, half-steps 2 kt + 5 and 2 kt + 6 into the freed slots,
+  // and sub-step 3 while reading sub-step 0 of step kt + 1
+  int sa = 0, sb = 1;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint32_t sc = sbase(kt), sn = sbase(kt + 1);
-    half_asm(p0, p1, sc + a_addr[1], sc + b_addr[1]);
-    half_asm(p1, p0, sc + a_addr[2], sc + b_addr[2]);
-    half_asm(p0, p1, sc + a_addr[3], sc + b_addr[3]);
-    dma::wait_vm<0>();
+    const uint32_t ca = slot_addr(sa), cb = slot_addr(sb);
+    const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;
+    const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
+    half_asm(p0, p1, ca + a_addr[1], cb + b_addr[1]);
+    half_asm(p1, p0, ca + a_addr[2], cb + b_addr[2]);
+    half_asm(p0, p1, ca + a_addr[3], cb + b_addr[3]);
+    if (kt + 2 < nk) dma::wait_vm<4>();
+    else dma::wait_vm<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < nk) issue(kt + 2);
-    half_asm(p1, p0, sn + a_addr[0], sn + b_addr[0]);
+    if (2 * kt + 5 < nh) issue_half(2 * kt + 5, sa);
+    if (2 * kt + 6 < nh) issue_half(2 * kt + 6, sb);
+    half_asm(p1, p0, slot_addr(na) + a_addr[0], slot_addr(nb) + b_addr[0]);
+    sa = na;
+    sb = nb;
   }
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   acc[0][0] = c00; acc[0][1] = c01; acc[1][0] = c10; acc[1][1] = c11;
