@@ -1176,6 +1176,62 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* lds, uint32_t byte_lo, u
 __device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
 }  // namespace dmaw
 
+// Tile order of the big weight-gradient kernel.  A tile's reduction runs over
+// its expert's rows, so its duration follows the expert's row count, which top-k
+// routing leaves uneven (at 16384 tokens, 64 experts and k = 6 the synthetic
+// routing gives 274 to 4216 rows).  The tiles of one product (dW2, dW1 or dW3)
+// of one expert form a group that stays on one XCD, where its tiles share the
+// expert's operand panels in L2.  Groups are ranked by their expert's row count,
+// largest first (equal counts: lower expert id first; an expert's three products
+// in the order dW2, dW1, dW3), and dealt to the 8 XCDs in a snake: round r goes
+// over XCDs 0..7 when r is even and 7..0 when it is odd.  Every XCD then gets
+// about the same number of rows and runs its largest groups first, where expert
+// order left one XCD with 16% more rows than the mean at that shape.  Workgroup
+// b runs on XCD b mod 8 as that XCD's (b / 8)-th; its round is (b / 8) / tpe.
+// The grid is 8 * ceil(3 E / 8) * tpe; a workgroup past the last group gets
+// false (uniform over the workgroup, before any barrier).  p0, p1: the expert's
+// row offsets.
+__device__ bool wgrad_snake_tile(const int32_t* offsets, int E, int tpe, int* z_out, int* e_out,
+                                 int* t_out, int* p0_out, int* p1_out) {
+  __shared__ int s_off[257];
+  __shared__ int s_rank[256];
+  __shared__ int s_e;
+  const int xcd = blockIdx.x % kXcd, j = blockIdx.x / kXcd;
+  const int r = j / tpe;
+  const int i = r * kXcd + ((r & 1) ? kXcd - 1 - xcd : xcd);
+  if (i >= 3 * E) return false;
+  const int q = i / 3;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int m = tid; m <= E; m += nt) {
+    s_off[m] = offsets[m];
+    if (m < E) s_rank[m] = 0;
+  }
+  __syncthreads();
+  // rank of expert u = the experts with more rows, or as many and a lower id;
+  // wavefront w counts over m = w, w + nw, ... and adds its count into LDS
+  const int lane = tid & 63, w = tid >> 6, nw = nt >> 6;
+  for (int u = lane; u < E; u += 64) {
+    const int cu = s_off[u + 1] - s_off[u];
+    int rk = 0;
+    for (int m = w; m < E; m += nw) {
+      const int cm = s_off[m + 1] - s_off[m];
+      rk += (cm > cu || (cm == cu && m < u)) ? 1 : 0;
+    }
+    if (rk) atomicAdd(&s_rank[u], rk);
+  }
+  __syncthreads();
+  for (int u = tid; u < E; u += nt)
+    if (s_rank[u] == q) s_e = u;   // the ranks are a permutation of 0 .. E - 1
+  __syncthreads();
+  const int e = s_e;
+  *z_out = i - 3 * q;
+  *e_out = e;
+  *t_out = j - r * tpe;
+  *p0_out = s_off[e];
+  *p1_out = s_off[e + 1];
+  return true;
+}
+
 // GATHER: as in the small-tile kernel, the x operand of dW1 and dW3 comes from
 // X through the gather table, entries fetched NST - 1 = 3 steps ahead.
 template <bool GATHER, bool FOLD_A = false>
@@ -1188,12 +1244,13 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   __shared__ __attribute__((aligned(16))) bf16_t st2[kStage];
   __shared__ __attribute__((aligned(16))) bf16_t st3[kStage];
 
-  const int flat = flat_tile();
-  const int per_z = g.E * tiles_per_expert;
-  const int z = flat / per_z;
-  if (z >= 3) return;
-  const int rem = flat - z * per_z;
-  const int e = rem / tiles_per_expert, t = rem % tiles_per_expert;
+  int z, e, t, p0, p1;
+  if (!wgrad_snake_tile(g.offsets, g.E, tiles_per_expert, &z, &e, &t, &p0, &p1)) return;
+  z = __builtin_amdgcn_readfirstlane(z);
+  e = __builtin_amdgcn_readfirstlane(e);
+  t = __builtin_amdgcn_readfirstlane(t);
+  p0 = __builtin_amdgcn_readfirstlane(p0);
+  p1 = __builtin_amdgcn_readfirstlane(p1);
   const int d = g.d, f = g.f;
   const int Mdim = (z == 0) ? d : f, Ndim = (z == 0) ? f : d;
   const int tiles_n = (Ndim + BN - 1) / BN;
@@ -1202,7 +1259,6 @@ __global__ __launch_bounds__(dmaw::NT, 1) void wgrad_dma_kernel(Args g, int32_t 
   const bf16_t* Asrc = (z == 0) ? g.a0 : (z == 1 ? g.a1 : g.aux0);
   const bf16_t* Bsrc = (z == 0) ? g.b0 : g.b1;
   bf16_t* dst = ((z == 0) ? g.c0 : (z == 1 ? g.c1 : g.c2)) + static_cast<int64_t>(e) * d * f;
-  const int p0 = g.offsets[e], p1 = g.offsets[e + 1];
   const int nk = (p1 - p0 + BKS - 1) / BKS;
   const int mvalid = min(BM, Mdim - m0), nvalid = min(BN, Ndim - n0);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -2236,6 +2292,12 @@ int wgrad_tiles_per_expert(const moe_dims& dm) {
 
 unsigned pad8(int64_t n) { return static_cast<unsigned>((n + kXcd - 1) / kXcd * kXcd); }
 
+// grid of the big weight-gradient kernel: ceil(3 E / 8) snake rounds of tpe
+// tiles on each of the 8 XCDs
+unsigned wgrad_snake_grid(int E, int tpe) {
+  return static_cast<unsigned>((3LL * E + kXcd - 1) / kXcd * kXcd * tpe);
+}
+
 constexpr int kCUs = 256;
 
 // Big tiles for long reductions (K >= 1024: the matrix cores, not the memory
@@ -2405,7 +2467,7 @@ hipError_t launch_wgrad_bf16(const moe_dims& dm, const void* x_perm, const int32
   // direct-to-LDS kernels, whose epilogues stage bf16 tiles
   if (!out_f32 && use_big_wgrad(dm)) {
     const int tpe = wgrad_tiles_per_expert<true>(dm);
-    const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+    const unsigned grid = wgrad_snake_grid(dm.E, tpe);
     g.grid_pad = static_cast<int32_t>(grid);
     if (g.x_rows)
       hipLaunchKernelGGL((wgrad_dma_kernel<true>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
@@ -2528,7 +2590,7 @@ hipError_t launch_wgrad_folded_bf16(const moe_dims& dm, const void* x, const int
   g.c2 = static_cast<bf16_t*>(dw3);
   if (use_big_wgrad(dm)) {
     const int tpe = wgrad_tiles_per_expert<true>(dm);
-    const unsigned grid = pad8(static_cast<int64_t>(3) * dm.E * tpe);
+    const unsigned grid = wgrad_snake_grid(dm.E, tpe);
     g.grid_pad = static_cast<int32_t>(grid);
     hipLaunchKernelGGL((wgrad_dma_kernel<true, true>), dim3(grid), dim3(dmaw::NT), 0, s, g, tpe);
     return hipGetLastError();
