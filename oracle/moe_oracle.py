@@ -285,9 +285,7 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm, act="f64"):
     dh = np.zeros((R, f))
     da = np.zeros((R, f))
     db = np.zeros((R, f))
-    dw1 = np.zeros_like(w1)
-    dw3 = np.zeros_like(w3)
-    dw2 = np.zeros_like(w2)
+    h = np.zeros((R, f))
     for e in range(E):
         s = slice(int(offsets[e]), int(offsets[e + 1]))
         sg = _sigmoid(a[s])
@@ -297,11 +295,31 @@ def swiglu_experts_bwd(x_perm, offsets, w1, w3, w2, a, b, dy_perm, act="f64"):
         da[s] = st(dh[s] * b[s] * dact)
         db[s] = st(dh[s] * act_s)
         dx[s] = st(da[s] @ w1[e] + db[s] @ w3[e])
-        dw2[e] = st(dy_perm[s].T @ st(act_s * b[s]))
+        h[s] = st(act_s * b[s])
+    wg = expert_weight_grads(x_perm, offsets, h, dy_perm, da, db, E, act)
+    return {"dx_perm": dx, "dw1": wg["dw1"], "dw3": wg["dw3"], "dw2": wg["dw2"],
+            "dh": dh, "da": da, "db": db}
+
+
+def expert_weight_grads(x_perm, offsets, h, dy_perm, da, db, E, act="f64"):
+    """The expert weight gradients as products over each expert's rows
+    [offsets[e], offsets[e+1]): dW2[e] = dy^T h, dW1[e] = da^T x, dW3[e] =
+    db^T x (zero for an expert without rows).  On absolute values of the
+    operands it gives the sums of |terms| of every entry.
+    (act="bf16": the weight gradients are stored as bfloat16.)"""
+    st = storage(act)
+    x_perm, h, dy_perm = _f64(x_perm), _f64(h), _f64(dy_perm)
+    da, db = _f64(da), _f64(db)
+    d, f = x_perm.shape[1], h.shape[1]
+    dw1 = np.zeros((E, f, d))
+    dw3 = np.zeros((E, f, d))
+    dw2 = np.zeros((E, d, f))
+    for e in range(E):
+        s = slice(int(offsets[e]), int(offsets[e + 1]))
+        dw2[e] = st(dy_perm[s].T @ h[s])
         dw1[e] = st(da[s].T @ x_perm[s])
         dw3[e] = st(db[s].T @ x_perm[s])
-    return {"dx_perm": dx, "dw1": dw1, "dw3": dw3, "dw2": dw2,
-            "dh": dh, "da": da, "db": db}
+    return {"dw1": dw1, "dw3": dw3, "dw2": dw2}
 
 
 def swiglu_experts_bwd_folded(x_perm, offsets, w1, w3, w2, a, b, hg, dy_rows, g_row,

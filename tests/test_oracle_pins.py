@@ -258,6 +258,29 @@ def _fd_check(oracle_module, seed=0, k=2, E=4):
     return worst
 
 
+def test_expert_weight_grads_are_sums_of_row_outer_products():
+    """The weight gradients of an expert are sums over its rows of outer
+    products ("Revisiting MoE...", Sec. 2.1, SwiGLU experts): one row gives one
+    outer product, an expert without rows gives zeros, and several rows give
+    the sum of theirs (brute force over rows)."""
+    rng = np.random.default_rng(5)
+    d, f, E = 5, 3, 3
+    off = np.array([0, 1, 1, 4])
+    x, dy = rng.standard_normal((4, d)), rng.standard_normal((4, d))
+    h, da, db = (rng.standard_normal((4, f)) for _ in range(3))
+    g = O.expert_weight_grads(x, off, h, dy, da, db, E)
+    np.testing.assert_allclose(g["dw1"][0], np.outer(da[0], x[0]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(g["dw2"][0], np.outer(dy[0], h[0]), rtol=0, atol=1e-14)
+    for key in ("dw1", "dw3", "dw2"):
+        assert not g[key][1].any()
+    bw1 = sum(np.outer(da[p], x[p]) for p in range(1, 4))
+    bw3 = sum(np.outer(db[p], x[p]) for p in range(1, 4))
+    bw2 = sum(np.outer(dy[p], h[p]) for p in range(1, 4))
+    np.testing.assert_allclose(g["dw1"][2], bw1, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g["dw3"][2], bw3, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g["dw2"][2], bw2, rtol=0, atol=1e-13)
+
+
 @pytest.mark.parametrize("seed,k,E", [(0, 2, 4), (1, 1, 4), (2, 3, 5), (3, 4, 4)])
 def test_backward_matches_finite_differences(seed, k, E):
     assert _fd_check(O, seed, k, E) < 1e-6
